@@ -1,0 +1,167 @@
+// C ABI of libisoquant: argument validation, split planning and launches.
+//
+// Every entry point validates its arguments on the host before touching the
+// HIP runtime, so argument errors are reported (and testable) without a GPU;
+// nothing is enqueued when a check fails.  No entry point synchronises the
+// host (FreeToken v0.2.0 release notes, Kernels #726).
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "../../include/isoquant.h"
+#include "iq_internal.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];
+
+int device_cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  int n = g_cu_count[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  g_cu_count[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+bool cache_ok(const iq_cache* c) {
+  return c && c->k_codes_dev && c->k_norms_dev && c->v_codes_dev && c->v_norms_dev &&
+         c->num_pages > 0 && c->n_kv_heads > 0;
+}
+
+iq::CacheView view(const iq_cache* c) {
+  return iq::CacheView{c->k_codes_dev, c->k_norms_dev, c->v_codes_dev, c->v_norms_dev,
+                       c->num_pages, c->n_kv_heads};
+}
+
+bool dtype_ok(int32_t d) { return d == IQ_F32 || d == IQ_BF16 || d == IQ_F16; }
+
+bool pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
+
+iq_status launch_status(hipError_t e) { return e == hipSuccess ? IQ_OK : IQ_ERR_LAUNCH; }
+
+float resolve_scale(float s) { return (s > 0.f && isfinite(s)) ? s : 1.0f / sqrtf(128.0f); }
+
+}  // namespace
+
+extern "C" {
+
+const char* iq_status_string(int32_t status) {
+  switch (status) {
+    case IQ_OK: return "ok";
+    case IQ_ERR_INVALID_ARG: return "invalid argument";
+    case IQ_ERR_UNSUPPORTED: return "unsupported configuration";
+    case IQ_ERR_WORKSPACE: return "workspace too small";
+    case IQ_ERR_LAUNCH: return "HIP copy or kernel launch failed";
+    case IQ_ERR_DEVICE: return "no usable HIP device";
+    default: return "unknown status";
+  }
+}
+
+int32_t iq_version(void) { return 10000; }
+
+size_t iq_rotation_bytes(int32_t n_kv_heads) {
+  return n_kv_heads > 0 ? iq::rotation_total_bytes(n_kv_heads) : 0;
+}
+
+iq_status iq_rotation_init(const float* quats_host, int32_t n_kv_heads, void* rot_dev,
+                           size_t rot_bytes, hipStream_t stream) {
+  if (!quats_host || !rot_dev || n_kv_heads < 1 || n_kv_heads > 65535) return IQ_ERR_INVALID_ARG;
+  if (rot_bytes < iq::rotation_total_bytes(n_kv_heads)) return IQ_ERR_INVALID_ARG;
+  for (int32_t i = 0; i < n_kv_heads * 32 * 2; ++i) {
+    double n = 0;
+    for (int k = 0; k < 4; ++k) {
+      const double v = quats_host[4 * i + k];
+      if (!isfinite(v)) return IQ_ERR_INVALID_ARG;
+      n += v * v;
+    }
+    if (!(n > 0) || !isfinite(n)) return IQ_ERR_INVALID_ARG;
+  }
+  float* mats = reinterpret_cast<float*>(rot_dev);
+  float* staging = reinterpret_cast<float*>(reinterpret_cast<char*>(rot_dev) +
+                                            iq::rotation_matrix_bytes(n_kv_heads));
+  const size_t qbytes = (size_t)n_kv_heads * 32 * 8 * sizeof(float);
+  if (hipMemcpyAsync(staging, quats_host, qbytes, hipMemcpyHostToDevice, stream) != hipSuccess)
+    return IQ_ERR_LAUNCH;
+  return launch_status(iq::launch_rotation_init(staging, n_kv_heads, mats, stream));
+}
+
+iq_status iq_quantize_append(const iq_cache* cache, const void* rot_dev, const void* k_dev,
+                             const void* v_dev, int32_t dtype, int32_t n_tokens,
+                             const int32_t* seq_idx_dev, const int32_t* pos_dev,
+                             const int32_t* block_table_dev, int32_t max_pages_per_seq,
+                             hipStream_t stream) {
+  if (!cache_ok(cache) || !rot_dev || !dtype_ok(dtype) || n_tokens < 0 || max_pages_per_seq < 1)
+    return IQ_ERR_INVALID_ARG;
+  if (n_tokens == 0) return IQ_OK;
+  if (!k_dev || !v_dev || !seq_idx_dev || !pos_dev || !block_table_dev) return IQ_ERR_INVALID_ARG;
+  return launch_status(iq::launch_quantize_append(view(cache), reinterpret_cast<const float*>(rot_dev),
+                                                  k_dev, v_dev, dtype, n_tokens, seq_idx_dev, pos_dev,
+                                                  block_table_dev, max_pages_per_seq, stream));
+}
+
+size_t iq_decode_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                                 int32_t max_seq_len) {
+  if (batch < 1 || n_q_heads < 1 || n_kv_heads < 1 || max_seq_len < 0) return 0;
+  const iq::DecodePlan plan = iq::plan_decode(batch, n_kv_heads, max_seq_len, device_cu_count());
+  return iq::decode_workspace_bytes(batch, n_q_heads, plan);
+}
+
+iq_status iq_decode_attention(const iq_cache* cache, const void* rot_dev, const void* q_dev,
+                              int32_t q_dtype, int32_t batch, int32_t n_q_heads,
+                              const int32_t* block_table_dev, int32_t max_pages_per_seq,
+                              const int32_t* seq_lens_dev, int32_t max_seq_len, float softmax_scale,
+                              float* out_dev, void* workspace_dev, size_t workspace_bytes,
+                              hipStream_t stream) {
+  if (!cache_ok(cache) || !rot_dev || !q_dev || !dtype_ok(q_dtype) || batch < 1 || batch > 65535 ||
+      n_q_heads < 1 || !block_table_dev || max_pages_per_seq < 1 || !seq_lens_dev ||
+      max_seq_len < 0 || !out_dev || !workspace_dev)
+    return IQ_ERR_INVALID_ARG;
+  if (n_q_heads % cache->n_kv_heads != 0) return IQ_ERR_INVALID_ARG;
+  if ((int64_t)max_seq_len > (int64_t)max_pages_per_seq * IQ_PAGE_TOKENS) return IQ_ERR_INVALID_ARG;
+  if (cache->n_kv_heads > 65535) return IQ_ERR_UNSUPPORTED;
+  if (n_q_heads / cache->n_kv_heads > IQ_MAX_GROUP) return IQ_ERR_UNSUPPORTED;
+  const iq::DecodePlan plan = iq::plan_decode(batch, cache->n_kv_heads, max_seq_len, device_cu_count());
+  if (workspace_bytes < iq::decode_workspace_bytes(batch, n_q_heads, plan)) return IQ_ERR_WORKSPACE;
+  return launch_status(iq::launch_decode(view(cache), reinterpret_cast<const float*>(rot_dev), q_dev,
+                                         q_dtype, batch, n_q_heads, block_table_dev, max_pages_per_seq,
+                                         seq_lens_dev, plan, resolve_scale(softmax_scale), out_dev,
+                                         workspace_dev, stream));
+}
+
+size_t iq_prefill_workspace_bytes(int32_t n_q, int32_t n_q_heads, int32_t n_kv_heads,
+                                  int32_t q_start_pos) {
+  if (n_q < 1 || n_q_heads < 1 || n_kv_heads < 1 || q_start_pos < 0) return 0;
+  const iq::PrefillPlan plan = iq::plan_prefill(n_q, n_q_heads, n_kv_heads, q_start_pos, device_cu_count());
+  return iq::prefill_workspace_bytes(n_q, n_q_heads, plan);
+}
+
+iq_status iq_prefill_attention(const iq_cache* cache, const void* rot_dev, const void* q_dev,
+                               int32_t q_dtype, int32_t n_q, int32_t n_q_heads, int32_t q_start_pos,
+                               const int32_t* block_table_dev, int32_t max_pages, float softmax_scale,
+                               float* out_dev, void* workspace_dev, size_t workspace_bytes,
+                               hipStream_t stream) {
+  if (!cache_ok(cache) || !rot_dev || !q_dev || !dtype_ok(q_dtype) || n_q < 0 || n_q_heads < 1 ||
+      q_start_pos < 0 || !block_table_dev || max_pages < 1 || !out_dev)
+    return IQ_ERR_INVALID_ARG;
+  if (n_q_heads % cache->n_kv_heads != 0) return IQ_ERR_INVALID_ARG;
+  if ((int64_t)q_start_pos + n_q > (int64_t)max_pages * IQ_PAGE_TOKENS) return IQ_ERR_INVALID_ARG;
+  if (n_q == 0) return IQ_OK;
+  const int group = n_q_heads / cache->n_kv_heads;
+  if (!pow2(group) || group > 128 || cache->n_kv_heads > 65535) return IQ_ERR_UNSUPPORTED;
+  const iq::PrefillPlan plan = iq::plan_prefill(n_q, n_q_heads, cache->n_kv_heads, q_start_pos, device_cu_count());
+  if (plan.row_tiles > 65535) return IQ_ERR_UNSUPPORTED;
+  const size_t need = iq::prefill_workspace_bytes(n_q, n_q_heads, plan);
+  if (need > 0 && (!workspace_dev || workspace_bytes < need)) return IQ_ERR_WORKSPACE;
+  return launch_status(iq::launch_prefill(view(cache), reinterpret_cast<const float*>(rot_dev), q_dev,
+                                          q_dtype, n_q, n_q_heads, q_start_pos, block_table_dev, max_pages,
+                                          plan, resolve_scale(softmax_scale), out_dev, workspace_dev,
+                                          stream));
+}
+
+}  // extern "C"

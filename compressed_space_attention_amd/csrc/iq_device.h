@@ -1,0 +1,204 @@
+// Device helpers shared by the IsoQuant HIP kernels (gfx950, wave64).
+//
+// Method ("RotaryQuant: Fitting 120B MoE Models on Consumer Hardware via Fused
+// Compressed-Space Attention", abstract): normalised Walsh-Hadamard transform,
+// then 32 block-diagonal SO(4) rotations, then 3-bit scalar quantisation; the
+// attention kernels read the packed codes directly.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace iq {
+
+constexpr int kD = 128;        // head dimension
+constexpr int kPage = 64;      // tokens per page
+constexpr int kRec = 48;       // code bytes per vector
+constexpr int kBlocks = 32;    // SO(4) blocks per head
+constexpr int kRotFloats = kBlocks * 16;  // fp32 4x4 matrices per kv head
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+
+struct __attribute__((aligned(4))) u3 {
+  uint32_t x, y, z;
+};
+
+// ---------------------------------------------------------------------------
+// Quantiser constants.  Decision thresholds = midpoints between adjacent
+// Gaussian Lloyd-Max levels (+-0.2451, +-0.7560, +-1.3440, +-2.1520), as fp32.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t code_of(float u) {
+  uint32_t c = (u >= -1.748f);
+  c += (u >= -1.05f);
+  c += (u >= -0.50055f);
+  c += (u >= 0.0f);
+  c += (u >= 0.50055f);
+  c += (u >= 1.05f);
+  c += (u >= 1.748f);
+  return c;
+}
+
+// The matrix-core kernels consume the levels as f16 operands.  They carry
+// alpha * level with alpha = 1.7670845, chosen so that all four magnitudes
+// land within 1.7e-5 (relative) of an f16 value (plain f16 levels are off by
+// up to 1.9e-4); 1/alpha is folded into the per-token norm factor.
+constexpr float kLevelScale = 1.7670845f;
+constexpr uint16_t kLevelF16[8] = {0xC39B, 0xC0C0, 0xBD58, 0xB6EE,   // codes 0..3 (negative)
+                                   0x36EE, 0x3D58, 0x40C0, 0x439B};  // codes 4..7
+constexpr uint32_t bytes4(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  return a | (b << 8) | (c << 16) | (d << 24);
+}
+constexpr uint32_t kLo0123 = bytes4(kLevelF16[0] & 255, kLevelF16[1] & 255, kLevelF16[2] & 255,
+                                    kLevelF16[3] & 255);
+constexpr uint32_t kLo4567 = bytes4(kLevelF16[4] & 255, kLevelF16[5] & 255, kLevelF16[6] & 255,
+                                    kLevelF16[7] & 255);
+constexpr uint32_t kHi0123 = bytes4(kLevelF16[0] >> 8, kLevelF16[1] >> 8, kLevelF16[2] >> 8,
+                                    kLevelF16[3] >> 8);
+constexpr uint32_t kHi4567 = bytes4(kLevelF16[4] >> 8, kLevelF16[5] >> 8, kLevelF16[6] >> 8,
+                                    kLevelF16[7] >> 8);
+
+// ---------------------------------------------------------------------------
+// Packed record layout.  A 48-byte record is four 12-byte groups (group g =
+// coordinates 32g..32g+31), each three little-endian dwords w0, w1, w2.  Byte
+// lane b (byte b of w0, w1, w2) is a 24-bit integer holding the codes of
+// coordinates 32g + 4s + b at bits 3s..3s+2, s = 0..7.
+//
+// "Selector" z_s = the four codes of coordinates 4s..4s+3 of the group, one
+// per byte: exactly the byte-select operand v_perm_b32 takes, so a selector
+// turns into four f16 levels with four v_perm_b32.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void group_to_selectors(uint32_t w0, uint32_t w1, uint32_t w2,
+                                                   uint32_t z[8]) {
+  z[0] = w0 & 0x07070707u;
+  z[1] = (w0 >> 3) & 0x07070707u;
+  z[2] = ((w0 >> 6) & 0x03030303u) | ((w1 << 2) & 0x04040404u);
+  z[3] = (w1 >> 1) & 0x07070707u;
+  z[4] = (w1 >> 4) & 0x07070707u;
+  z[5] = ((w1 >> 7) & 0x01010101u) | ((w2 << 1) & 0x06060606u);
+  z[6] = (w2 >> 2) & 0x07070707u;
+  z[7] = (w2 >> 5) & 0x07070707u;
+}
+
+__device__ __forceinline__ void selectors_to_group(const uint32_t z[8], uint32_t& w0,
+                                                   uint32_t& w1, uint32_t& w2) {
+  w0 = z[0] | (z[1] << 3) | ((z[2] & 0x03030303u) << 6);
+  w1 = ((z[2] >> 2) & 0x01010101u) | (z[3] << 1) | (z[4] << 4) | ((z[5] & 0x01010101u) << 7);
+  w2 = ((z[5] >> 1) & 0x03030303u) | (z[6] << 2) | (z[7] << 5);
+}
+
+// Four codes (one selector) -> four f16 levels (alpha-scaled) in two dwords:
+// the first holds coordinates 4s, 4s+1 and the second 4s+2, 4s+3.
+__device__ __forceinline__ u2 selector_to_f16(uint32_t z) {
+  const uint32_t l = __builtin_amdgcn_perm(kLo4567, kLo0123, z);  // low bytes of 4 levels
+  const uint32_t h = __builtin_amdgcn_perm(kHi4567, kHi0123, z);  // high bytes
+  return u2{__builtin_amdgcn_perm(h, l, 0x05010400u), __builtin_amdgcn_perm(h, l, 0x07030602u)};
+}
+
+// ---------------------------------------------------------------------------
+// Small numeric helpers.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float half_bits_to_float(uint32_t bits16) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+}
+
+// fp32 -> fp16 bits, round to nearest even, saturating finite values at 65504.
+__device__ __forceinline__ uint16_t float_to_half_sat(float x) {
+  _Float16 h = (_Float16)x;
+  uint16_t b = __builtin_bit_cast(uint16_t, h);
+  if ((b & 0x7FFFu) == 0x7C00u) b = (b & 0x8000u) | 0x7BFFu;
+  return b;
+}
+
+__device__ __forceinline__ float load_as_float(const void* base, size_t idx, int dtype) {
+  if (dtype == 0) return reinterpret_cast<const float*>(base)[idx];
+  if (dtype == 1) {
+    const uint32_t b = reinterpret_cast<const uint16_t*>(base)[idx];
+    return __builtin_bit_cast(float, b << 16);
+  }
+  return (float)reinterpret_cast<const _Float16*>(base)[idx];
+}
+
+// Load 32 consecutive elements (128-bit aligned) as fp32.
+__device__ __forceinline__ void load32(const void* base, size_t idx, int dtype, float x[32]) {
+  if (dtype == 0) {
+    const f4* p = reinterpret_cast<const f4*>(reinterpret_cast<const float*>(base) + idx);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      f4 v = p[i];
+      x[4 * i] = v[0]; x[4 * i + 1] = v[1]; x[4 * i + 2] = v[2]; x[4 * i + 3] = v[3];
+    }
+  } else {
+    const u4* p = reinterpret_cast<const u4*>(reinterpret_cast<const uint16_t*>(base) + idx);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      u4 v = p[i];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t w = v[k];
+        if (dtype == 1) {
+          x[8 * i + 2 * k] = __builtin_bit_cast(float, w << 16);
+          x[8 * i + 2 * k + 1] = __builtin_bit_cast(float, w & 0xFFFF0000u);
+        } else {
+          x[8 * i + 2 * k] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
+          x[8 * i + 2 * k + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Unnormalised Walsh-Hadamard transform (Sylvester order) of a 128-vector held
+// by four lanes, 32 consecutive coordinates each: lane quarter j holds
+// coordinates 32j..32j+31.  XOR_A / XOR_B are the lane-xor distances of the
+// quarters j^1 and j^2.  Coordinate distances 1..16 are in-register
+// butterflies; 32 and 64 cross lanes.
+// ---------------------------------------------------------------------------
+template <int XOR_A, int XOR_B>
+__device__ __forceinline__ void wht128_quad(float x[32], int j) {
+#pragma unroll
+  for (int h = 1; h < 32; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      if ((i & h) == 0) {
+        const float a = x[i], b = x[i + h];
+        x[i] = a + b;
+        x[i + h] = a - b;
+      }
+    }
+  }
+  const float s1 = (j & 1) ? -1.0f : 1.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const float p = __shfl_xor(x[i], XOR_A);
+    x[i] = fmaf(s1, x[i], p);  // low quarter: x + p; high quarter: p - x
+  }
+  const float s2 = (j & 2) ? -1.0f : 1.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const float p = __shfl_xor(x[i], XOR_B);
+    x[i] = fmaf(s2, x[i], p);
+  }
+}
+
+// z = M_b y for the 8 blocks of quarter j (blocks 8j..8j+7); rot = one kv
+// head's [32][4][4] row-major fp32 matrices.
+__device__ __forceinline__ void so4_forward_quarter(const float* __restrict__ rot, int j,
+                                                    const float y[32], float z[32]) {
+#pragma unroll
+  for (int bb = 0; bb < 8; ++bb) {
+    const f4* m = reinterpret_cast<const f4*>(rot + (8 * j + bb) * 16);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const f4 row = m[r];
+      z[4 * bb + r] = row[0] * y[4 * bb] + row[1] * y[4 * bb + 1] + row[2] * y[4 * bb + 2] +
+                      row[3] * y[4 * bb + 3];
+    }
+  }
+}
+
+}  // namespace iq

@@ -1,0 +1,57 @@
+// Internal interface between the C-ABI host code (api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace iq {
+
+struct CacheView {
+  uint8_t* k_codes;
+  uint16_t* k_norms;
+  uint8_t* v_codes;
+  uint16_t* v_norms;
+  int32_t num_pages;
+  int32_t hkv;
+};
+
+// Rotation buffer: fp32 matrices [hkv][32][4][4], then fp32 quaternion staging
+// [hkv][32][2][4].
+inline size_t rotation_matrix_bytes(int hkv) { return (size_t)hkv * 32 * 16 * sizeof(float); }
+inline size_t rotation_total_bytes(int hkv) {
+  return rotation_matrix_bytes(hkv) + (size_t)hkv * 32 * 8 * sizeof(float);
+}
+
+hipError_t launch_rotation_init(const float* quats_dev, int hkv, float* rot_dev,
+                                hipStream_t stream);
+
+hipError_t launch_quantize_append(const CacheView& c, const float* rot, const void* k,
+                                  const void* v, int dtype, int n_tokens, const int32_t* seq_idx,
+                                  const int32_t* pos, const int32_t* block_table, int max_pages,
+                                  hipStream_t stream);
+
+struct DecodePlan {
+  int splits;           // workgroups per (sequence, kv head)
+  int pages_per_split;
+};
+DecodePlan plan_decode(int batch, int hkv, int max_seq_len, int num_cus);
+size_t decode_workspace_bytes(int batch, int hq, const DecodePlan& plan);
+
+hipError_t launch_decode(const CacheView& c, const float* rot, const void* q, int q_dtype,
+                         int batch, int hq, const int32_t* block_table, int max_pages,
+                         const int32_t* seq_lens, const DecodePlan& plan, float softmax_scale,
+                         float* out, void* workspace, hipStream_t stream);
+
+struct PrefillPlan {
+  int row_tiles;        // workgroups per kv head along the query rows
+  int kv_splits;        // workgroups along the key range
+};
+PrefillPlan plan_prefill(int n_q, int hq, int hkv, int q_start, int num_cus);
+size_t prefill_workspace_bytes(int n_q, int hq, const PrefillPlan& plan);
+hipError_t launch_prefill(const CacheView& c, const float* rot, const void* q, int q_dtype,
+                          int n_q, int hq, int q_start, const int32_t* block_table,
+                          int max_pages, const PrefillPlan& plan, float softmax_scale,
+                          float* out, void* workspace, hipStream_t stream);
+
+}  // namespace iq

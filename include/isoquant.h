@@ -1,0 +1,184 @@
+/*
+ * libisoquant — IsoQuant compressed-space attention for AMD Instinct MI355X
+ * (gfx950).  C ABI: plain pointers and sizes, no C++ or framework types.
+ *
+ * The method ("RotaryQuant: Fitting 120B MoE Models on Consumer Hardware via
+ * Fused Compressed-Space Attention", abstract): each key/value head vector
+ * (d = 128) is put through a normalised Walsh-Hadamard transform and then 32
+ * block-diagonal SO(4) rotations, each given by a pair of unit quaternions
+ * (256 stored parameters per head), and is then scalar-quantised to 3 bits;
+ * attention runs on the packed tensors without materialising full-precision
+ * K/V.  The query is rotated into the same orthogonal space and the value
+ * accumulator is rotated back once at the end.
+ *
+ * Quantiser: n = ||x||_2 (stored as fp16), u = (T x) sqrt(d) / n, code =
+ * number of the seven nearest-centroid thresholds that u reaches; centroids
+ * are the 8 Gaussian Lloyd-Max levels +-0.2451, +-0.7560, +-1.3440, +-2.1520
+ * scaled by n / sqrt(d).  One record = 48 bytes of codes + 2 bytes of norm.
+ *
+ * Conventions for every entry point
+ *   - Pointers named *_dev are device memory on the current HIP device; the
+ *     caller allocates and owns all of them (cache, rotation, inputs,
+ *     outputs, workspace).  The library never allocates or frees device
+ *     memory and keeps no pointer after returning.
+ *   - Every call is asynchronous on `stream` (0 = the null stream) and does
+ *     not synchronise the host (FreeToken v0.2.0 release notes, Kernels:
+ *     attention metadata must not block the host, #726).
+ *   - Arguments are validated on the host before anything is enqueued; a
+ *     failed check returns a negative iq_status and enqueues nothing.  A
+ *     failed kernel launch returns IQ_ERR_LAUNCH.
+ *   - Device-side contract (not checked): block-table entries lie in
+ *     [0, num_pages); sequence lengths and positions fit the block table;
+ *     each cache slot is written by at most one token of a call.
+ *   - Byte offsets are computed in 64 bits (caches larger than 2^31 bytes
+ *     are supported; FreeToken v0.2.0 release notes, GGUF Support #699:
+ *     kernels must not run past 32-bit offsets).
+ *   - Functions are re-entrant; calls that write the same cache slots or the
+ *     same workspace on overlapping streams race.
+ */
+#ifndef ISOQUANT_H
+#define ISOQUANT_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  IQ_OK = 0,
+  IQ_ERR_INVALID_ARG = -1,   /* null pointer, bad size, bad dtype, bad quaternion */
+  IQ_ERR_UNSUPPORTED = -2,   /* valid but outside what the kernels handle     */
+  IQ_ERR_WORKSPACE = -3,     /* workspace smaller than the *_workspace_bytes   */
+  IQ_ERR_LAUNCH = -4,        /* HIP reported an error for a copy or launch     */
+  IQ_ERR_DEVICE = -5         /* no usable HIP device                           */
+} iq_status;
+
+typedef enum { IQ_F32 = 0, IQ_BF16 = 1, IQ_F16 = 2 } iq_dtype;
+
+enum {
+  IQ_HEAD_DIM = 128,         /* d                                               */
+  IQ_PAGE_TOKENS = 64,       /* tokens per cache page                           */
+  IQ_CODE_BYTES = 48,        /* 128 codes x 3 bits                              */
+  IQ_ROT_PARAMS = 256,       /* stored rotation parameters per kv head          */
+  IQ_MAX_GROUP = 16          /* query heads per kv head handled by decode       */
+};
+
+/*
+ * One layer's paged cache, in four caller-owned device arrays:
+ *   k_codes, v_codes : uint8  [num_pages][n_kv_heads][64][48]
+ *   k_norms, v_norms : uint16 [num_pages][n_kv_heads][64]   (fp16 bit patterns)
+ * Token t of a sequence lives in page block_table[seq][t / 64], slot t % 64
+ * (FreeToken v0.1.3 release notes, Engine #367: paged KV reserved at allocation
+ * granularity).
+ * Code record layout (48 bytes, coordinates 0..127): four 12-byte groups, group
+ * g holding coordinates 32g..32g+31.  In a group, the bytes at offsets b, 4+b
+ * and 8+b (b = 0..3) form a 24-bit little-endian integer ("byte lane" b); the
+ * 3-bit code of coordinate 32g + 4s + b is at bits 3s..3s+2 of byte lane b.
+ * The struct is read during the call only.
+ */
+typedef struct {
+  uint8_t *k_codes_dev;
+  uint16_t *k_norms_dev;
+  uint8_t *v_codes_dev;
+  uint16_t *v_norms_dev;
+  int32_t num_pages;
+  int32_t n_kv_heads;
+} iq_cache;
+
+/* Human-readable text for a status code (static storage). */
+const char *iq_status_string(int32_t status);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int32_t iq_version(void);
+
+/*
+ * Rotation setup ("RotaryQuant ...", abstract: WHT followed by block-diagonal
+ * SO(4) rotations; FreeToken issue #141, Proposed Solution: quaternion
+ * rotations).  One rotation per kv head, shared by K, V and that head's query
+ * group.
+ *
+ * quats_host : host float[n_kv_heads][32][2][4]; [h][b][0] = q_L, [h][b][1] = q_R,
+ *              components (w, x, y, z) with w real.  Need not be unit: each is
+ *              normalised.  Block b maps coordinates 4b..4b+3, read as the
+ *              quaternion v = v0 + v1 i + v2 j + v3 k, to q_L * v * conj(q_R).
+ * rot_dev    : device buffer of at least iq_rotation_bytes(n_kv_heads) bytes,
+ *              written by this call; pass it unchanged to the other calls.
+ * Errors     : IQ_ERR_INVALID_ARG for null pointers, n_kv_heads < 1, a buffer
+ *              that is too small, or a quaternion of zero or non-finite norm.
+ */
+size_t iq_rotation_bytes(int32_t n_kv_heads);
+iq_status iq_rotation_init(const float *quats_host, int32_t n_kv_heads, void *rot_dev,
+                           size_t rot_bytes, hipStream_t stream);
+
+/*
+ * Quantise and append ("RotaryQuant ...", abstract: 3-bit scalar quantisation
+ * after the rotation).  For every token i and kv head h, quantises K[i][h] and
+ * V[i][h] and stores the records in slot pos[i] % 64 of page
+ * block_table[seq_idx[i]][pos[i] / 64].
+ *
+ * k_dev, v_dev     : [n_tokens][n_kv_heads][128] of `dtype` (IQ_F32/IQ_BF16/IQ_F16).
+ * seq_idx_dev      : int32[n_tokens], row of the block table of each token.
+ * pos_dev          : int32[n_tokens], absolute position of each token.
+ * block_table_dev  : int32[*][max_pages_per_seq], row-major.
+ * n_tokens == 0 is a no-op.  Inputs with non-finite values give unspecified codes.
+ */
+iq_status iq_quantize_append(const iq_cache *cache, const void *rot_dev, const void *k_dev,
+                             const void *v_dev, int32_t dtype, int32_t n_tokens,
+                             const int32_t *seq_idx_dev, const int32_t *pos_dev,
+                             const int32_t *block_table_dev, int32_t max_pages_per_seq,
+                             hipStream_t stream);
+
+/*
+ * Decode attention on the packed cache ("RotaryQuant ...", abstract; the
+ * context is split across workgroups as in FreeToken v0.2.0 release notes,
+ * Kernels #729, and an all -inf chunk yields no NaN, #654).  Every query head
+ * h of sequence b attends all seq_lens[b] cached tokens of kv head
+ * h / (n_q_heads / n_kv_heads); the caller appends the current token first.
+ *
+ * q_dev          : [batch][n_q_heads][128] of q_dtype.
+ * block_table_dev: int32[batch][max_pages_per_seq].
+ * seq_lens_dev   : int32[batch], each in [0, max_seq_len].
+ * max_seq_len    : host-side upper bound of seq_lens, used to plan the splits.
+ * softmax_scale  : <= 0 selects 1/sqrt(128).
+ * out_dev        : float[batch][n_q_heads][128], in the original (unrotated) space.
+ *                  A sequence of length 0 gives zeros.
+ * workspace_dev  : at least iq_decode_workspace_bytes(...) bytes, any contents.
+ * Unsupported: n_q_heads / n_kv_heads > IQ_MAX_GROUP.
+ */
+size_t iq_decode_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                                 int32_t max_seq_len);
+iq_status iq_decode_attention(const iq_cache *cache, const void *rot_dev, const void *q_dev,
+                              int32_t q_dtype, int32_t batch, int32_t n_q_heads,
+                              const int32_t *block_table_dev, int32_t max_pages_per_seq,
+                              const int32_t *seq_lens_dev, int32_t max_seq_len,
+                              float softmax_scale, float *out_dev, void *workspace_dev,
+                              size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Chunked causal prefill attention of one sequence on the packed cache
+ * ("RotaryQuant ...", abstract; FreeToken issue #141, Proposed Solution:
+ * faster prefill with GQA).  Query i sits at position q_start_pos + i and
+ * attends cached keys 0 .. q_start_pos + i.  The GQA-grouped QK^T and PV are
+ * dense contractions and run on the matrix cores (f16 inputs, fp32 accumulate).
+ *
+ * q_dev          : [n_q][n_q_heads][128] of q_dtype.
+ * block_table_dev: int32[max_pages] of this sequence.
+ * out_dev        : float[n_q][n_q_heads][128], original space.
+ * workspace_dev  : at least iq_prefill_workspace_bytes(...) bytes.
+ */
+size_t iq_prefill_workspace_bytes(int32_t n_q, int32_t n_q_heads, int32_t n_kv_heads,
+                                  int32_t q_start_pos);
+iq_status iq_prefill_attention(const iq_cache *cache, const void *rot_dev, const void *q_dev,
+                               int32_t q_dtype, int32_t n_q, int32_t n_q_heads,
+                               int32_t q_start_pos, const int32_t *block_table_dev,
+                               int32_t max_pages, float softmax_scale, float *out_dev,
+                               void *workspace_dev, size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ISOQUANT_H */

@@ -190,7 +190,8 @@ def fp16_midpoint_near(n, rel_eps: float = NEAR_EPS) -> np.ndarray:
     when computed in fp32 instead of fp64 (R6/R17)."""
     n = np.asarray(n, dtype=np.float64)
     h = np.minimum(n, FP16_MAX).astype(np.float16)
-    up = np.nextafter(h, np.float16(np.inf)).astype(np.float64)
+    with np.errstate(over="ignore"):
+        up = np.nextafter(h, np.float16(np.inf)).astype(np.float64)
     dn = np.nextafter(h, np.float16(0)).astype(np.float64)
     hv = h.astype(np.float64)
     mids = np.stack([(hv + up) / 2.0, (hv + dn) / 2.0])

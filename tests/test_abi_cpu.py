@@ -1,0 +1,105 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/isoquant.h declares, and rejects bad arguments on the host before
+anything is enqueued (no compute call is made here)."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "isoquant.h")
+
+iq = pytest.importorskip("compressed_space_attention_amd.isoquant",
+                         reason="libisoquant.so not built")
+L = iq.lib
+FAKE = 0x1000  # never dereferenced: every call below fails validation first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(iq_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declarations_are_exported_and_bound():
+    names = declared_functions()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(L, n), n                    # dlsym succeeds
+    assert sorted(iq.EXPORTED) == names
+
+
+def test_status_strings_and_sizes():
+    for code, text in [(0, "ok"), (-1, "invalid argument"), (-2, "unsupported configuration"),
+                       (-3, "workspace too small"), (-4, "HIP copy or kernel launch failed"),
+                       (-5, "no usable HIP device")]:
+        assert iq.status_string(code) == text
+    assert iq.status_string(7) == "unknown status"
+    assert L.iq_version() == 10000
+    assert iq.rotation_bytes(8) == 8 * (32 * 16 + 32 * 8) * 4
+    assert iq.rotation_bytes(0) == 0
+    assert iq.decode_workspace_bytes(0, 32, 4, 1024) == 0
+
+
+def _cache(hkv=4, pages=8):
+    return ctypes.byref(iq.IqCacheStruct(FAKE, FAKE, FAKE, FAKE, pages, hkv))
+
+
+def test_rotation_init_validation():
+    q = np.ones((2, 32, 2, 4), np.float32)
+    assert L.iq_rotation_init(None, 2, FAKE, 10 ** 6, None) == -1
+    assert L.iq_rotation_init(q.ctypes.data, 0, FAKE, 10 ** 6, None) == -1
+    assert L.iq_rotation_init(q.ctypes.data, 2, FAKE, 100, None) == -1       # buffer too small
+    bad = q.copy()
+    bad[1, 5, 1] = 0.0                                                        # zero quaternion
+    assert L.iq_rotation_init(bad.ctypes.data, 2, FAKE, 10 ** 6, None) == -1
+    bad = q.copy()
+    bad[0, 0, 0, 2] = np.nan
+    assert L.iq_rotation_init(bad.ctypes.data, 2, FAKE, 10 ** 6, None) == -1
+
+
+def test_quantize_append_validation():
+    c = _cache()
+    assert L.iq_quantize_append(None, FAKE, FAKE, FAKE, 1, 4, FAKE, FAKE, FAKE, 8, None) == -1
+    assert L.iq_quantize_append(c, FAKE, FAKE, FAKE, 7, 4, FAKE, FAKE, FAKE, 8, None) == -1  # dtype
+    assert L.iq_quantize_append(c, FAKE, FAKE, FAKE, 1, -1, FAKE, FAKE, FAKE, 8, None) == -1
+    assert L.iq_quantize_append(c, FAKE, None, FAKE, 1, 4, FAKE, FAKE, FAKE, 8, None) == -1
+    assert L.iq_quantize_append(c, FAKE, FAKE, FAKE, 1, 0, FAKE, FAKE, FAKE, 8, None) == 0   # no-op
+    empty = ctypes.byref(iq.IqCacheStruct(FAKE, FAKE, FAKE, FAKE, 0, 4))
+    assert L.iq_quantize_append(empty, FAKE, FAKE, FAKE, 1, 4, FAKE, FAKE, FAKE, 8, None) == -1
+
+
+def _decode(c, hq=32, ws=10 ** 9, dtype=1, max_len=1024, max_pages=16, batch=1):
+    return L.iq_decode_attention(c, FAKE, FAKE, dtype, batch, hq, FAKE, max_pages, FAKE, max_len,
+                                 0.0, FAKE, FAKE, ws, None)
+
+
+def test_decode_validation():
+    c = _cache(hkv=4)
+    assert _decode(c, hq=30) == -1                  # Hq not a multiple of Hkv
+    assert _decode(c, dtype=5) == -1
+    assert _decode(c, max_len=2000, max_pages=16) == -1   # lengths exceed the block table
+    assert _decode(c, hq=4 * 17) == -2              # group above IQ_MAX_GROUP
+    assert _decode(c, ws=16) == -3                  # workspace too small
+    assert _decode(c, batch=0) == -1
+    assert L.iq_decode_attention(c, FAKE, FAKE, 1, 1, 32, None, 16, FAKE, 1024, 0.0, FAKE, FAKE,
+                                 10 ** 9, None) == -1
+
+
+def test_decode_workspace_is_monotone_in_context():
+    a = iq.decode_workspace_bytes(1, 32, 4, 4096)
+    b = iq.decode_workspace_bytes(1, 32, 4, 32768)
+    assert 0 < a <= b
+
+
+def test_prefill_validation():
+    c = _cache(hkv=8)
+    args = dict()
+    assert L.iq_prefill_attention(c, FAKE, FAKE, 1, 16, 60, 0, FAKE, 8, 0.0, FAKE, FAKE, 0, None) == -1
+    assert L.iq_prefill_attention(c, FAKE, FAKE, 1, 16, 24, 0, FAKE, 8, 0.0, FAKE, FAKE, 0, None) == -2
+    assert L.iq_prefill_attention(c, FAKE, FAKE, 1, 16, 64, 500, FAKE, 8, 0.0, FAKE, FAKE, 0, None) == -1
+    assert L.iq_prefill_attention(c, FAKE, FAKE, 1, 0, 64, 0, FAKE, 8, 0.0, FAKE, FAKE, 0, None) == 0
+    assert L.iq_prefill_attention(c, FAKE, FAKE, 9, 16, 64, 0, FAKE, 8, 0.0, FAKE, FAKE, 0, None) == -1

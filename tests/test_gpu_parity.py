@@ -1,0 +1,172 @@
+"""HIP path vs CPU oracle, element by element, through the C-ABI.
+
+Codes must match bit for bit except coordinates within 1e-6 of a decision
+boundary (their count is reported and must stay below 1e-5 of all codes);
+norms bit for bit except values within 1e-6 of an fp16 rounding midpoint.
+Attention outputs must satisfy max_rows max|gpu - oracle| / max|oracle| <= 1e-3,
+with the oracle attending over the GPU-written cache.
+"""
+
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from compressed_space_attention_amd import synth
+from oracle import isoquant_oracle as O
+from tests.gpu_cases import Scenario, code_parity, max_row_error, tol
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def test_rotation_matrices_match_oracle():
+    from compressed_space_attention_amd import isoquant as iq
+    quats = synth.quaternions(11, 5) * 3.0
+    rot = iq.rotation_init(quats)
+    torch.cuda.synchronize()
+    mats = rot[: 5 * 32 * 16 * 4].view(torch.float32).cpu().numpy().reshape(5, 32, 4, 4)
+    want = O.rotation_matrices(quats)
+    assert np.max(np.abs(mats - want)) < 1e-6
+
+
+@pytest.mark.parametrize("dtype,outliers", [("f32", False), ("bf16", True), ("f16", False)])
+def test_quantize_append_codes_and_norms(dtype, outliers):
+    _say(f"quantize parity dtype={dtype} outliers={outliers}")
+    s = Scenario(21, [1, 100, 700, 64], hkv=4, dtype=dtype, outliers=outliers)
+    ref, info = s.oracle_cache()
+    st = code_parity(s.host_cache(), ref, info, s)
+    _say(st)
+    assert st["mismatch"] <= st["near"]
+    assert st["mismatch"] < 1e-5 * st["codes"] + 1
+
+
+def test_quantize_special_vectors():
+    """Zero vectors, a huge norm (fp16 saturation), identity rotation with a
+    Hadamard column and a basis vector (closed-form codes)."""
+    n = 6
+    k = torch.zeros((n, 1, 128), dtype=torch.float32)
+    k[1, 0, 0] = 3.0                                  # e_0 -> all codes 5
+    k[2, 0] = torch.from_numpy(O.sylvester_hadamard()[:, 37] * 0.25)  # -> code 7 at 37, else 4
+    k[3, 0] = 1e5                                     # norm 1.13e6 -> saturates at 65504
+    k[4, 0, 5] = -2.0                                 # -e_5 -> u = -1 or +1 by Hadamard sign
+    k[5] = torch.from_numpy(synth.normal(3, (1, 128)))
+    v = k.clone()
+    s = Scenario(31, [n], hkv=1, dtype="f32", identity=True, kv_override=(k, v))
+    ref, info = s.oracle_cache()
+    code_parity(s.host_cache(), ref, info, s)
+    g = s.host_cache()
+    codes = O.unpack_codes(g.k_codes[s.block_table[0, 0], 0, :n])
+    assert np.all(codes[0] == 4) and g.k_norms[s.block_table[0, 0], 0, 0] == 0
+    assert np.all(codes[1] == 5)
+    want = np.full(128, 4)
+    want[37] = 7
+    assert np.array_equal(codes[2], want)
+    assert g.k_norms[s.block_table[0, 0], 0, 3] == 0x7BFF
+
+
+DECODE_CASES = [
+    # (lens, hkv, hq, dtype, outliers)
+    ([2048], 1, 1, "f32", False),
+    ([1, 63, 64, 65, 700], 2, 4, "bf16", True),
+    ([130, 1000, 2100], 4, 32, "bf16", True),
+    ([640, 33], 2, 32, "f16", False),
+]
+
+
+@pytest.mark.parametrize("case", range(len(DECODE_CASES)))
+def test_decode_matches_oracle_on_gpu_cache(case):
+    lens, hkv, hq, dtype, outl = DECODE_CASES[case]
+    _say(f"decode parity lens={lens} hkv={hkv} hq={hq} dtype={dtype}")
+    s = Scenario(100 + case, lens, hkv=hkv, dtype=dtype, outliers=outl)
+    q = s.queries(200 + case, len(lens), hq)
+    out = s.iq.decode_attention(s.cache, s.rot, q.cuda(), s.bt_dev, s.lens_dev, max(lens))
+    torch.cuda.synchronize()
+    ref = O.decode_attention(s.host_cache(), s.blocks, q.double().numpy(), s.block_table, lens)
+    err = max_row_error(out.cpu().numpy(), ref)
+    _say(f"  max row error {err:.3e}")
+    assert np.all(np.isfinite(out.cpu().numpy()))
+    assert err <= tol()
+
+
+def test_decode_edge_lengths_and_empty_sequence():
+    lens = [0, 1, 64, 129]
+    s = Scenario(300, lens, hkv=2, dtype="bf16")
+    q = s.queries(301, len(lens), 16)
+    out = s.iq.decode_attention(s.cache, s.rot, q.cuda(), s.bt_dev, s.lens_dev, max(lens)).cpu().numpy()
+    ref = O.decode_attention(s.host_cache(), s.blocks, q.double().numpy(), s.block_table, lens)
+    assert np.all(out[0] == 0)
+    assert max_row_error(out, ref) <= tol()
+    # context 1: the output is the dequantised value of token 0
+    hc = s.host_cache()
+    vc, vn = hc.gather(s.block_table, 1, 1, 0, "v")
+    v0 = O.dequantize(vc, vn, s.blocks[0])[0]
+    assert np.max(np.abs(out[1, :8] - v0)) <= 1e-3 * np.max(np.abs(v0))
+
+
+def test_decode_split_plans_agree_and_are_deterministic():
+    lens = [3000, 1500]
+    s = Scenario(400, lens, hkv=2, dtype="bf16", outliers=True)
+    q = s.queries(401, 2, 16).cuda()
+    outs = []
+    old = os.environ.get("IQ_DECODE_TARGET_WGS")
+    try:
+        for target in ("1", "7", "64", "100000"):
+            os.environ["IQ_DECODE_TARGET_WGS"] = target
+            outs.append(s.iq.decode_attention(s.cache, s.rot, q, s.bt_dev, s.lens_dev, 3000).cpu().numpy())
+        again = s.iq.decode_attention(s.cache, s.rot, q, s.bt_dev, s.lens_dev, 3000).cpu().numpy()
+    finally:
+        if old is None:
+            os.environ.pop("IQ_DECODE_TARGET_WGS", None)
+        else:
+            os.environ["IQ_DECODE_TARGET_WGS"] = old
+    assert np.array_equal(again, outs[-1])           # fixed plan: bit-identical
+    # Each plan is within the oracle tolerance; plans differ only by where P~ is
+    # rounded to f16 (relative to each split's running max), about 2^-11 per weight.
+    ref = O.decode_attention(s.host_cache(), s.blocks, q.double().cpu().numpy(), s.block_table, lens)
+    for o in outs:
+        assert max_row_error(o, ref) <= tol()
+        assert max_row_error(o, outs[0]) <= 0.5 * tol()
+
+
+def test_decode_shuffled_equals_contiguous_block_table():
+    lens = [777]
+    k = synth.kv_vectors(5, 777, 2, "bf16")
+    v = synth.kv_vectors(6, 777, 2, "bf16")
+    a = Scenario(500, lens, hkv=2, dtype="bf16", shuffle=False, kv_override=(k, v))
+    b = Scenario(500, lens, hkv=2, dtype="bf16", shuffle=True, kv_override=(k, v))
+    q = a.queries(501, 1, 8).cuda()
+    oa = a.iq.decode_attention(a.cache, a.rot, q, a.bt_dev, a.lens_dev, 777).cpu().numpy()
+    ob = b.iq.decode_attention(b.cache, b.rot, q, b.bt_dev, b.lens_dev, 777).cpu().numpy()
+    assert np.array_equal(oa, ob)
+
+
+PREFILL_CASES = [
+    # (cache length, n_q, hkv, hq)
+    (1000, 200, 2, 16),
+    (300, 300, 1, 1),
+    (700, 77, 2, 8),
+]
+
+
+@pytest.mark.parametrize("case", range(len(PREFILL_CASES)))
+def test_prefill_matches_oracle(case):
+    total, n_q, hkv, hq = PREFILL_CASES[case]
+    _say(f"prefill parity total={total} n_q={n_q} hkv={hkv} hq={hq}")
+    s = Scenario(600 + case, [total], hkv=hkv, dtype="bf16")
+    q = synth.to_dtype(synth.normal(601 + case, (n_q, hq, 128)), "bf16")
+    q_start = total - n_q
+    out = s.iq.prefill_attention(s.cache, s.rot, q.cuda(), q_start, s.bt_dev[0]).cpu().numpy()
+    rows = np.unique(np.linspace(0, n_q - 1, min(n_q, 24)).astype(int))
+    ref = O.prefill_attention(s.host_cache(), s.blocks, q.double().numpy(), q_start, s.block_table[0],
+                              rows=rows)
+    err = max_row_error(out[rows], ref)
+    _say(f"  max row error {err:.3e}")
+    assert err <= tol()
