@@ -1,0 +1,279 @@
+#!/usr/bin/env python3
+"""Benchmark of the IsoQuant packed-KV attention path on one MI355X.
+
+Default workload: GQA decode at 32K context (batch 1, 32 query / 4 kv heads,
+d = 128, bf16 inputs, 64-token pages, shuffled page table).  One step = one
+layer's decode step: quantise-append the current token's K/V into the packed
+cache, then decode attention of all query heads over the 32,768 cached tokens.
+Steps walk a ring of layer caches (>= 1 GB in total, above the 256 MB
+Infinity Cache) so every step reads its packed KV from HBM.  The steps are
+recorded once into a HIP graph (torch.cuda.CUDAGraph) and replayed, so the
+host's launch rate does not pace the GPU.
+
+Prints one JSON line: metric/value (packed-KV GB/s), the roofline of the
+dominant kernel (measured live with HIP events on the launch stream) and the
+CPU oracle timed on a bounded sample on the host.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
+MFMA_F16_PEAK_TFLOPS = 2500.0    # MI355X dense f16 matrix peak, published
+METRIC = "packed-KV decode attention GB/s (% of HBM peak) + tokens/s at 32K ctx"
+REC_BYTES = 100                  # K + V records per (token, kv head): 2 x (48 + 2)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=160)
+    ap.add_argument("--workload", default="gqa_decode_32k_32q4kv")
+    ap.add_argument("--ring-bytes", type=float, default=1.0e9,
+                    help="minimum bytes of distinct layer caches cycled by the steps")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="launch eagerly (profiling runs)")
+    return ap.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class DecodeLayer:
+    """One layer: rotation, packed cache holding context-1 tokens, and the
+    current token's q/k/v."""
+
+    def __init__(self, iq, synth, w, idx, block_table, num_pages, device):
+        import torch
+        self.idx = idx
+        seed = w.seed * 1000 + idx
+        self.rot = iq.rotation_init(synth.quaternions(seed, w.n_kv_heads), device=device)
+        self.cache = iq.PagedCache(num_pages, w.n_kv_heads, device=device)
+        lens = w.seq_lens()
+        n_prev = [int(n) - 1 for n in lens]
+        total = sum(n_prev)
+        outl = synth.outlier_channels(seed + 1, w.n_kv_heads) if w.k_outliers else None
+        dt = {"bf16": torch.bfloat16, "f32": torch.float32}[w.dtype]
+        scale = torch.ones(w.n_kv_heads, 128, device=device)
+        if outl is not None:
+            for h in range(w.n_kv_heads):
+                scale[h, torch.from_numpy(outl[h]).to(device)] = 10.0
+        seq_idx = torch.cat([torch.full((n,), b, dtype=torch.int32) for b, n in enumerate(n_prev)]).to(device)
+        pos = torch.cat([torch.arange(n, dtype=torch.int32) for n in n_prev]).to(device)
+        chunk = 1 << 16
+        for s in range(0, total, chunk):
+            e = min(total, s + chunk)
+            k = (synth.draw_normal_device(seed * 7 + s, (e - s, w.n_kv_heads, 128), torch.float32, device)
+                 * scale).to(dt)
+            v = synth.draw_normal_device(seed * 11 + s, (e - s, w.n_kv_heads, 128), dt, device)
+            iq.quantize_append(self.cache, self.rot, k, v, seq_idx[s:e], pos[s:e], block_table)
+        # the current token of every sequence (position len-1) and the queries
+        b = w.batch
+        self.k_new = (synth.draw_normal_device(seed * 13, (b, w.n_kv_heads, 128), torch.float32, device)
+                      * scale).to(dt)
+        self.v_new = synth.draw_normal_device(seed * 17, (b, w.n_kv_heads, 128), dt, device)
+        self.q = synth.draw_normal_device(seed * 19, (b, w.n_q_heads, 128), dt, device)
+        self.seq_new = torch.arange(b, dtype=torch.int32, device=device)
+        self.pos_new = torch.tensor(n_prev, dtype=torch.int32, device=device)
+        self.out = torch.empty((b, w.n_q_heads, 128), dtype=torch.float32, device=device)
+
+
+def run_decode(args):
+    import torch
+
+    from compressed_space_attention_amd import isoquant as iq
+    from compressed_space_attention_amd import synth, workloads
+
+    w = workloads.DECODE_WORKLOADS[args.workload]
+    device = "cuda"
+    torch.cuda.set_device(0)
+    lens = w.seq_lens()
+    pages = [-(-int(n) // 64) for n in lens]
+    bt_np, num_pages = synth.block_table(w.seed + 5, pages, shuffle=w.shuffle_pages)
+    block_table = torch.from_numpy(bt_np).to(device)
+    seq_lens = torch.from_numpy(lens).to(device)
+    max_len = int(lens.max())
+    kv_bytes = REC_BYTES * int(lens.sum()) * w.n_kv_heads            # read by one decode call
+    layer_bytes = num_pages * w.n_kv_heads * 64 * REC_BYTES
+    ring = max(1, math.ceil(args.ring_bytes / layer_bytes))
+    log(f"[bench] workload {w.name}: {kv_bytes / 1e6:.1f} MB packed KV per call, ring of {ring} layers "
+        f"({ring * layer_bytes / 1e9:.2f} GB)")
+    t0 = time.time()
+    layers = [DecodeLayer(iq, synth, w, i, block_table, num_pages, device) for i in range(ring)]
+    torch.cuda.synchronize()
+    log(f"[bench] caches built in {time.time() - t0:.1f} s")
+    ws = torch.empty(max(16, iq.decode_workspace_bytes(w.batch, w.n_q_heads, w.n_kv_heads, max_len)),
+                     dtype=torch.uint8, device=device)
+
+    def step(layer, with_append=True):
+        if with_append:
+            iq.quantize_append(layer.cache, layer.rot, layer.k_new, layer.v_new, layer.seq_new,
+                               layer.pos_new, block_table)
+        iq.decode_attention(layer.cache, layer.rot, layer.q, block_table, seq_lens, max_len,
+                            out=layer.out, workspace=ws)
+
+    def run_steps(n, start, with_append=True):
+        for i in range(n):
+            step(layers[(start + i) % ring], with_append)
+
+    # warmup (eager)
+    run_steps(args.warmup, 0)
+    torch.cuda.synchronize()
+
+    def make_graph(n, with_append):
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                run_steps(n, 0, with_append)
+        torch.cuda.current_stream().wait_stream(s)
+        return g
+
+    def timed(n_steps, with_append):
+        """Time exactly n_steps steps; returns seconds measured by HIP events."""
+        stream = torch.cuda.current_stream()
+        if args.no_graph:
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            run_steps(n_steps, 0, with_append)
+            b.record(stream)
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) / 1e3
+        full, rem = divmod(n_steps, ring)
+        g_full = make_graph(ring, with_append) if full else None
+        g_rem = make_graph(rem, with_append) if rem else None
+        if g_full:
+            g_full.replay()      # one untimed replay: the graph's first launch uploads it
+        if g_rem:
+            g_rem.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(full):
+            g_full.replay()
+        if g_rem:
+            g_rem.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / 1e3
+
+    t_step = timed(args.steps, True) / args.steps
+    t_decode = timed(args.steps, False) / args.steps
+    gbs = kv_bytes / t_step / 1e9
+    dec_gbs = kv_bytes / t_decode / 1e9
+    log(f"[bench] step {t_step * 1e6:.2f} us ({gbs:.0f} GB/s), decode call {t_decode * 1e6:.2f} us "
+        f"({dec_gbs:.0f} GB/s)")
+
+    result = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t_step * 1e3, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": ("synthetic: seeded N(0,1) bf16 K/V/Q"
+                 + (", 4 outlier key channels x10 per kv head" if w.k_outliers else "")
+                 + ", seeded random quaternion rotations, "
+                 + ("shuffled" if w.shuffle_pages else "contiguous") + " 64-token page table"),
+        "config": {
+            "workload": w.name, "batch": w.batch, "context": max_len, "n_q_heads": w.n_q_heads,
+            "n_kv_heads": w.n_kv_heads, "head_dim": 128, "page_tokens": 64,
+            "packed_kv_bytes_per_step": kv_bytes, "layer_ring": ring,
+            "step": "quantise-append current token + decode attention, one layer",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "decode attention call (decode_split_kernel + decode_merge_kernel)",
+            "achieved": round(dec_gbs, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+            "traffic": None,
+        },
+        "detail": {
+            "pct_hbm_peak_step": round(100 * gbs / HBM_PEAK_GBS, 2),
+            "decode_call_us": round(t_decode * 1e6, 3),
+            "step_us": round(t_step * 1e6, 3),
+            "tokens_per_s_per_layer": round(w.batch / t_step, 1),
+        },
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_decode(args, w, layers[0], bt_np, lens)
+    return result
+
+
+def cpu_baseline_decode(args, w, layer, bt_np, lens):
+    """The CPU oracle, as it stands, on a bounded sample of the same step:
+    quantise-append the current token, then decode over the layer's cache."""
+    import threadpoolctl
+
+    from oracle import isoquant_oracle as O
+
+    host = O.PagedCache.from_arrays(*layer.cache.to_host())
+    quats = None
+    from compressed_space_attention_amd import synth
+    quats = synth.quaternions(w.seed * 1000 + layer.idx, w.n_kv_heads)
+    blocks = O.rotation_matrices(quats)
+    q = layer.q.float().cpu().numpy().astype(np.float64)
+    k_new = layer.k_new.float().cpu().numpy().astype(np.float64)
+    v_new = layer.v_new.float().cpu().numpy().astype(np.float64)
+    pos_new = layer.pos_new.cpu().numpy()
+    seq_new = layer.seq_new.cpu().numpy()
+    kv_bytes = REC_BYTES * int(lens.sum()) * w.n_kv_heads
+    info = threadpoolctl.threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+    steps, t0 = 0, time.perf_counter()
+    while True:
+        O.quantize_append(host, blocks, k_new, v_new, seq_new, pos_new, bt_np)
+        O.decode_attention(host, blocks, q, bt_np, lens)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= args.cpu_seconds or el * (steps + 1) / steps > 30.0:
+            break
+    return {
+        "value": round(kv_bytes * steps / el / 1e9, 5),
+        "unit": "GB/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{steps} oracle steps of one layer (append 1 token + decode over "
+                  f"{int(lens.max())} tokens, {w.n_q_heads}q/{w.n_kv_heads}kv) in {el:.1f} s; "
+                  f"host has {os.cpu_count()} logical CPUs",
+    }
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this benchmark measures one GPU; the path has no multi-GPU "
+                                   "collective (each GPU would own its own sequences/kv heads)",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    res = run_decode(args)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

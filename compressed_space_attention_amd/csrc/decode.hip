@@ -16,14 +16,18 @@
 //   one partial (m, l, acc[128]) per query head is written to the workspace.
 //   A second kernel merges the partials of all splits and applies T^T.
 //
-// Per page and wave, the G query heads of the group are the 16 columns of
-// 16x16 matrix-core tiles (padded with zero queries):
+// Per page and wave, the G query heads of the group are the columns of 16x16
+// matrix-core tiles (zero queries pad the group to 16 columns):
 //   S^T[token][head] = K^[token][:] . Q'[head][:]   v_mfma_f32_16x16x32_f16, with
 //       Q' split into an f16 high and low part (two MFMAs, ~2^-22 relative);
-//       the K operand row of lane l is token l%16 and its 32 coordinates come
-//       straight from one 12-byte group of the token's record.
-//   V^ is transposed with an identity MFMA (exact) so that the contraction
-//   index is the token, then O'^T[dim][head] += V^T . P~ (16x16x16).
+//       lane l's K operand is token l%16 and its coordinates come straight from
+//       one 12-byte group of the token's record.
+//   O'^T[dim][head] += V^T[dim][token] . P~^T[token][head]   (16x16x32); the V
+//       pages are stored so that lane l's 48-byte region is exactly its V
+//       operand for the page, so no transpose is needed.
+// With G <= 8 two 16-token score tiles share one set of registers (columns
+// 0-7 and 8-15), which halves the softmax work; the shared layout is also the
+// B operand of the PV product after one row shift.
 // Levels enter as alpha-scaled f16 (see iq_device.h); the key norm, 1/alpha,
 // the softmax scale and log2(e) are one fp32 factor per score.  The value
 // norm is folded into P~ relative to a per-page power-of-two frame so that P~
@@ -56,22 +60,50 @@ struct DecodeArgs {
   float* out;          // [B][Hq][128]
 };
 
+// DPP controls (gfx9): shifts and rotation inside rows of 16 lanes.
+constexpr int kRowShl8 = 0x108, kRowShr8 = 0x118, kRowRor8 = 0x128;
+
+template <int CTRL, int BANK_MASK>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t old, uint32_t src) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)src, CTRL, 0xF, BANK_MASK, false);
+}
+template <int CTRL, int BANK_MASK>
+__device__ __forceinline__ float dpp_f(float old, float src) {
+  return __builtin_bit_cast(float, dpp_u<CTRL, BANK_MASK>(__builtin_bit_cast(uint32_t, old),
+                                                          __builtin_bit_cast(uint32_t, src)));
+}
+
+// Score tiles held by one lane: with PACK8 (G <= 8) tile t covers token block
+// 2t + (lane%16 >= 8); otherwise tile t is token block t.
+template <bool PACK8>
 struct PageRegs {
-  u3 kc[4], vc[4];  // 12 code bytes of token 16*rb + (lane%16), group lane/16
-  u2 kn[4], vn[4];  // fp16 norms of tokens 16*rb + 4*(lane/16) + 0..3
+  static constexpr int NT = PACK8 ? 2 : 4;
+  u3 kc[4];       // K: 12 code bytes of token 16*rb + lane%16, group lane/16
+  u4 vr[3];       // V: the lane's 48-byte region (chunks c = 0..3, dwords 3c..3c+2)
+  u2 kn[NT], vn[NT];  // fp16 norms of the lane's four score tokens per tile
 };
 
-__device__ __forceinline__ void load_page(const DecodeArgs& a, int b, int g, int pg, int t, int jq,
-                                          PageRegs& r) {
-  const int page = a.block_table[(size_t)b * a.max_pages + pg];
+template <bool PACK8>
+__device__ __forceinline__ int tile_block(int t, int col) {
+  return PACK8 ? 2 * t + (col >> 3) : t;
+}
+
+template <bool PACK8>
+__device__ __forceinline__ void load_page(const DecodeArgs& a, int page, int g, int lane,
+                                          PageRegs<PACK8>& r) {
+  const int col = lane & 15, jq = lane >> 4;
   const size_t base = ((size_t)page * a.hkv + g) * kPage;  // record index of slot 0
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb) {
-    const size_t rec = base + 16 * rb + t;
-    r.kc[rb] = *reinterpret_cast<const u3*>(a.k_codes + rec * kRec + 12 * jq);
-    r.vc[rb] = *reinterpret_cast<const u3*>(a.v_codes + rec * kRec + 12 * jq);
-    r.kn[rb] = *reinterpret_cast<const u2*>(a.k_norms + base + 16 * rb + 4 * jq);
-    r.vn[rb] = *reinterpret_cast<const u2*>(a.v_norms + base + 16 * rb + 4 * jq);
+  for (int rb = 0; rb < 4; ++rb)
+    r.kc[rb] = *reinterpret_cast<const u3*>(a.k_codes + (base + 16 * rb + col) * kRec + 12 * jq);
+  const u4* vreg = reinterpret_cast<const u4*>(a.v_codes + (base + lane) * kRec);
+#pragma unroll
+  for (int i = 0; i < 3; ++i) r.vr[i] = vreg[i];
+#pragma unroll
+  for (int t = 0; t < PageRegs<PACK8>::NT; ++t) {
+    const size_t nb = base + 16 * tile_block<PACK8>(t, col) + 4 * jq;
+    r.kn[t] = *reinterpret_cast<const u2*>(a.k_norms + nb);
+    r.vn[t] = *reinterpret_cast<const u2*>(a.v_norms + nb);
   }
 }
 
@@ -80,13 +112,154 @@ __device__ __forceinline__ float norm_at(const u2& n, int r) {
   return half_bits_to_float((r & 1) ? (w >> 16) : (w & 0xFFFFu));
 }
 
+struct PageState {
+  float m_run, l_run, rho;  // running max (log2 units), partial sum, value-norm frame
+  f4 acc[8];                // O'^T tiles: coordinates 32*(lane/16) + 4m + r, head lane%16
+};
+
+// Power-of-two frame for the value norms of a page: returns 2^(15 - e) for
+// the largest fp16 norm bits with biased exponent e, so that vn * frame < 2.
+__device__ __forceinline__ float norm_frame(uint32_t max_bits, float current) {
+  if (max_bits == 0) return current;
+  const int e16 = (int)((max_bits >> 10) & 0x1Fu);
+  return __builtin_bit_cast(float, (uint32_t)(15 - e16 + 127) << 23);
+}
+
+template <bool PACK8>
+__device__ __forceinline__ float column_max(float v) {
+  if (PACK8) v = fmaxf(v, dpp_f<kRowRor8, 0xF>(v, v));
+  v = fmaxf(v, __shfl_xor(v, 16));
+  return fmaxf(v, __shfl_xor(v, 32));
+}
+
+// One page for one wave: scores on the matrix cores, online-softmax update,
+// P~ V^ accumulation.  MASKED pages hold tokens at or beyond the length L.
+template <bool PACK8, bool MASKED>
+__device__ __forceinline__ void process_page(const PageRegs<PACK8>& cur, PageState& st, int tok0,
+                                             int L, int lane, float fac, const h8 qhi[4],
+                                             const h8 qlo[4]) {
+  constexpr int NT = PageRegs<PACK8>::NT;
+  const int col = lane & 15, jq = lane >> 4;
+  f4 s[4];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) {
+    uint32_t z[8];
+    group_to_selectors(cur.kc[rb].x, cur.kc[rb].y, cur.kc[rb].z, z);
+    f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const u2 d0 = selector_to_f16(z[2 * kk]), d1 = selector_to_f16(z[2 * kk + 1]);
+      const h8 av = __builtin_bit_cast(h8, u4{d0[0], d0[1], d1[0], d1[1]});
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, qhi[kk], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, qlo[kk], acc, 0, 0, 0);
+    }
+    s[rb] = acc;
+  }
+
+  float sc[NT][4];
+  float mp = -INFINITY;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int tok = tok0 + 16 * tile_block<PACK8>(t, col) + 4 * jq;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      // with PACK8, columns 8-15 take the scores of the odd token block
+      const float raw = PACK8 ? dpp_f<kRowShr8, 0xC>(s[2 * t][r], s[2 * t + 1][r]) : s[t][r];
+      const float v = raw * (norm_at(cur.kn[t], r) * fac);
+      sc[t][r] = (!MASKED || tok + r < L) ? v : -INFINITY;
+      mp = fmaxf(mp, sc[t][r]);
+    }
+  }
+  u2 vn[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    vn[t] = cur.vn[t];
+    if (MASKED) {  // zero the norms of tokens at or beyond L
+      const int t0 = tok0 + 16 * tile_block<PACK8>(t, col) + 4 * jq;
+      vn[t][0] &= (t0 < L ? 0xFFFFu : 0u) | (t0 + 1 < L ? 0xFFFF0000u : 0u);
+      vn[t][1] &= (t0 + 2 < L ? 0xFFFFu : 0u) | (t0 + 3 < L ? 0xFFFF0000u : 0u);
+    }
+  }
+  uint32_t vbits = PACK8 ? max_half_bits(vn[0], vn[1])
+                         : max(max_half_bits(vn[0], vn[1]), max_half_bits(vn[NT - 2], vn[NT - 1]));
+  mp = column_max<PACK8>(mp);
+  if (PACK8) vbits = max(vbits, dpp_u<kRowRor8, 0xF>(vbits, vbits));
+  vbits = max(vbits, (uint32_t)__shfl_xor((int)vbits, 16));
+  vbits = max(vbits, (uint32_t)__shfl_xor((int)vbits, 32));
+  const float m_new = fmaxf(st.m_run, mp);        // finite: the page has a valid token
+  const float corr = fast_exp2(st.m_run - m_new);  // 0 on the first page
+  const float rho_new = norm_frame(vbits, st.rho);
+  const float rescale = corr * (rho_new / st.rho);
+  if (__any(rescale != 1.0f)) {
+#pragma unroll
+    for (int m = 0; m < 8; ++m) st.acc[m] *= rescale;
+    st.l_run *= corr;
+  }
+  st.m_run = m_new;
+  st.rho = rho_new;
+
+  uint32_t pw[NT][2];  // P~ as f16 pairs: tokens r = 0,1 and r = 2,3 of each tile
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    float p[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      p[r] = fast_exp2(sc[t][r] - m_new);  // masked tokens: 2^-inf = 0
+      st.l_run += p[r];
+      p[r] *= norm_at(vn[t], r) * rho_new;
+    }
+    // round to nearest even (round-toward-zero would bias every weight down)
+    typedef _Float16 hh2 __attribute__((ext_vector_type(2)));
+    pw[t][0] = __builtin_bit_cast(uint32_t, hh2{(_Float16)p[0], (_Float16)p[1]});
+    pw[t][1] = __builtin_bit_cast(uint32_t, hh2{(_Float16)p[2], (_Float16)p[3]});
+  }
+  h8 pb[2];  // B operand of token blocks (2th, 2th+1)
+#pragma unroll
+  for (int th = 0; th < 2; ++th) {
+    u4 w;
+    if (PACK8) {
+      w[0] = pw[th][0];
+      w[1] = pw[th][1];
+      w[2] = dpp_u<kRowShl8, 0x3>(pw[th][0], pw[th][0]);
+      w[3] = dpp_u<kRowShl8, 0x3>(pw[th][1], pw[th][1]);
+    } else {
+      w[0] = pw[2 * th][0];
+      w[1] = pw[2 * th][1];
+      w[2] = pw[2 * th + 1][0];
+      w[3] = pw[2 * th + 1][1];
+    }
+    pb[th] = __builtin_bit_cast(h8, w);
+  }
+
+  uint32_t zv[4][8];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int d = 3 * c;
+    group_to_selectors(cur.vr[d / 4][d % 4], cur.vr[(d + 1) / 4][(d + 1) % 4],
+                       cur.vr[(d + 2) / 4][(d + 2) % 4], zv[c]);
+  }
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+#pragma unroll
+    for (int th = 0; th < 2; ++th) {
+      const u2 d0 = selector_to_f16(zv[2 * th][m]), d1 = selector_to_f16(zv[2 * th + 1][m]);
+      const h8 av = __builtin_bit_cast(h8, u4{d0[0], d0[1], d1[0], d1[1]});
+      st.acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pb[th], st.acc[m], 0, 0, 0);
+    }
+  }
+}
+
+template <bool PACK8>
 __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int col = lane & 15, jq = lane >> 4;
+  const int pg_begin = split * a.pages_per_split;
+  int pg = pg_begin + wave;
+  // The page id of the wave's first page is fetched together with the length.
+  const int first_page = (pg < a.max_pages) ? a.block_table[(size_t)b * a.max_pages + pg] : 0;
   const int L = a.seq_lens[b];
   const int n_pages = (L + kPage - 1) / kPage;
-  const int pg_begin = split * a.pages_per_split;
   if (pg_begin >= n_pages) return;  // uniform for the workgroup
   const int pg_end = min(n_pages, pg_begin + a.pages_per_split);
 
@@ -95,21 +268,22 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
   __shared__ float s_acc[4][32][64];
   __shared__ float s_m[4][16], s_l[4][16];
 
-  // Issue the first page's loads before anything else.
-  PageRegs cur;
-  int pg = pg_begin + wave;
-  if (pg < pg_end) load_page(a, b, g, pg, col, jq, cur);
-
-  // Wave 0 rotates the group's queries: lane (head col, quarter jq) holds
-  // coordinates 32jq..32jq+31, which is exactly the B-operand layout below.
+  // Wave 0 loads the group's queries before its first page.
+  float x[32];
   if (wave == 0) {
-    float x[32];
     if (col < a.group) {
       load32(a.q, ((size_t)b * a.hq + (size_t)g * a.group + col) * kD + 32 * jq, a.q_dtype, x);
     } else {
 #pragma unroll
       for (int i = 0; i < 32; ++i) x[i] = 0.f;
     }
+  }
+  PageRegs<PACK8> cur;
+  if (pg < pg_end) load_page<PACK8>(a, first_page, g, lane, cur);
+
+  // Wave 0 rotates the queries: lane (head col, quarter jq) holds coordinates
+  // 32jq..32jq+31, which is exactly the B-operand layout of the score MFMA.
+  if (wave == 0) {
     wht128_quad<16, 32>(x, jq);
     float z[32];
     so4_forward_quarter(a.rot + (size_t)g * kRotFloats, jq, x, z);
@@ -150,104 +324,37 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
     qhi[kk] = __builtin_bit_cast(h8, dh);
     qlo[kk] = __builtin_bit_cast(h8, dl);
   }
-  const float fac = a.score_factor * s_qinv[col];
-  h4 ident;
-#pragma unroll
-  for (int s = 0; s < 4; ++s) ident[s] = (4 * jq + s == col) ? (_Float16)1.0f : (_Float16)0.0f;
+  // per-lane score factor of the lane's head column
+  const float fac = a.score_factor * s_qinv[PACK8 ? (col & 7) : col];
 
-  float m_run = -INFINITY, l_run = 0.f, rho = 1.0f;
-  f4 acc[8];
+  PageState st;
+  st.m_run = -INFINITY;
+  st.l_run = 0.f;
+  st.rho = 1.0f;
 #pragma unroll
-  for (int m = 0; m < 8; ++m) acc[m] = f4{0.f, 0.f, 0.f, 0.f};
+  for (int m = 0; m < 8; ++m) st.acc[m] = f4{0.f, 0.f, 0.f, 0.f};
 
   for (; pg < pg_end; pg += 4) {
-    PageRegs nxt;
+    PageRegs<PACK8> nxt;
     const bool more = pg + 4 < pg_end;
-    if (more) load_page(a, b, g, pg + 4, col, jq, nxt);
-    const int tok_base = pg * kPage + 4 * jq;
-
-    // ---- scores (log2 units) ----
-    float sc[4][4];
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      uint32_t z[8];
-      group_to_selectors(cur.kc[rb].x, cur.kc[rb].y, cur.kc[rb].z, z);
-      f4 s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const u2 d0 = selector_to_f16(z[2 * kk]), d1 = selector_to_f16(z[2 * kk + 1]);
-        const h8 av = __builtin_bit_cast(h8, u4{d0[0], d0[1], d1[0], d1[1]});
-        s = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, qhi[kk], s, 0, 0, 0);
-        s = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, qlo[kk], s, 0, 0, 0);
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int tok = tok_base + 16 * rb + r;
-        const float v = s[r] * norm_at(cur.kn[rb], r) * fac;
-        sc[rb][r] = (tok < L) ? v : -INFINITY;
-      }
-    }
-
-    // ---- online softmax update ----
-    float mp = -INFINITY, vmax = 0.f;
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        mp = fmaxf(mp, sc[rb][r]);
-        if (tok_base + 16 * rb + r < L) vmax = fmaxf(vmax, norm_at(cur.vn[rb], r));
-      }
-    mp = fmaxf(mp, __shfl_xor(mp, 16));
-    mp = fmaxf(mp, __shfl_xor(mp, 32));
-    vmax = fmaxf(vmax, __shfl_xor(vmax, 16));
-    vmax = fmaxf(vmax, __shfl_xor(vmax, 32));
-    const float m_new = fmaxf(m_run, mp);            // finite: the page has a valid token
-    const float corr = exp2f(m_run - m_new);         // 0 on the first page
-    int e = 0;
-    frexpf(vmax, &e);
-    const float rho_new = (vmax > 0.f) ? ldexpf(1.0f, 1 - e) : rho;
-    const float rescale = corr * (rho_new / rho);
-#pragma unroll
-    for (int m = 0; m < 8; ++m) acc[m] *= rescale;
-    l_run *= corr;
-    m_run = m_new;
-    rho = rho_new;
-
-    h4 pb[4];
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float p = exp2f(sc[rb][r] - m_new);  // masked tokens: exp2(-inf) = 0
-        l_run += p;
-        const bool valid = tok_base + 16 * rb + r < L;
-        pb[rb][r] = (_Float16)(valid ? p * norm_at(cur.vn[rb], r) * rho : 0.f);
-      }
-
-    // ---- P~ V^ on the matrix cores ----
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      uint32_t z[8];
-      group_to_selectors(cur.vc[rb].x, cur.vc[rb].y, cur.vc[rb].z, z);
-#pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        const h4 av = __builtin_bit_cast(h4, selector_to_f16(z[m]));
-        const f4 t = __builtin_amdgcn_mfma_f32_16x16x16f16(av, ident, f4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-        const h4 tv = {(_Float16)t[0], (_Float16)t[1], (_Float16)t[2], (_Float16)t[3]};
-        acc[m] = __builtin_amdgcn_mfma_f32_16x16x16f16(tv, pb[rb], acc[m], 0, 0, 0);
-      }
-    }
+    if (more) load_page<PACK8>(a, a.block_table[(size_t)b * a.max_pages + pg + 4], g, lane, nxt);
+    if ((pg + 1) * kPage <= L)
+      process_page<PACK8, false>(cur, st, pg * kPage, L, lane, fac, qhi, qlo);
+    else
+      process_page<PACK8, true>(cur, st, pg * kPage, L, lane, fac, qhi, qlo);
     if (more) cur = nxt;
   }
 
   // ---- merge the four waves ----
-  float l_col = l_run + __shfl_xor(l_run, 16);
+  float l_col = st.l_run;
+  if (PACK8) l_col += dpp_f<kRowRor8, 0xF>(l_col, l_col);
+  l_col += __shfl_xor(l_col, 16);
   l_col += __shfl_xor(l_col, 32);
-  const float fin = a.out_factor / rho;
+  const float fin = a.out_factor / st.rho;
 #pragma unroll
-  for (int k = 0; k < 32; ++k) s_acc[wave][k][lane] = acc[k >> 2][k & 3] * fin;
+  for (int k = 0; k < 32; ++k) s_acc[wave][k][lane] = st.acc[k >> 2][k & 3] * fin;
   if (jq == 0) {
-    s_m[wave][col] = m_run;
+    s_m[wave][col] = st.m_run;
     s_l[wave][col] = l_col;
   }
   __syncthreads();
@@ -262,7 +369,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
     float wt[4], Ls = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      wt[w] = (mw[w] == -INFINITY) ? 0.f : exp2f(mw[w] - M);
+      wt[w] = (mw[w] == -INFINITY) ? 0.f : fast_exp2(mw[w] - M);
       Ls += wt[w] * s_l[w][col];
     }
     if (col < a.group) {
@@ -290,32 +397,67 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
   }
 }
 
-// One wave per (query head, sequence): merge the split partials, normalise,
-// and rotate back: o = (H / sqrt(d)) B^T o'.  Lane l owns coordinates 2l, 2l+1.
-__global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
-  const int hq = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
+// One workgroup per (query head, sequence): merge the split partials with all
+// loads in flight at once, normalise, and rotate back: o = (H / sqrt(d)) B^T o'.
+// Thread t adds coordinates 4*(t%32)..+3 over the splits s = t/32 (mod 8).
+__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
+  const int hq = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int L = a.seq_lens[b];
   const int n_pages = (L + kPage - 1) / kPage;
   // A length above the planned maximum is outside the contract; never read
   // partials that the split kernel did not plan for.
   const int ns = min(a.splits, (n_pages + a.pages_per_split - 1) / a.pages_per_split);
-  float* out = a.out + ((size_t)b * a.hq + hq) * kD + 2 * lane;
+  float* out = a.out + ((size_t)b * a.hq + hq) * kD;
   if (ns == 0) {
-    out[0] = 0.f;
-    out[1] = 0.f;
+    if (tid < 32) reinterpret_cast<f4*>(out)[tid] = f4{0.f, 0.f, 0.f, 0.f};
     return;
   }
+  __shared__ float s_w[1024];
+  __shared__ float s_red[8];
+  __shared__ f4 s_part[8][32];
   const size_t row0 = ((size_t)b * a.hq + hq) * a.splits;
+  const float2* ml = reinterpret_cast<const float2*>(a.ws_ml) + row0;
+
+  // maximum over splits
   float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, a.ws_ml[2 * (row0 + s)]);
-  float Ls = 0.f, o0 = 0.f, o1 = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const float m = a.ws_ml[2 * (row0 + s)], l = a.ws_ml[2 * (row0 + s) + 1];
-    const float w = exp2f(m - M);
-    const float2 v = *reinterpret_cast<const float2*>(a.ws_acc + (row0 + s) * kD + 2 * lane);
-    Ls += w * l;
-    o0 += w * v.x;
-    o1 += w * v.y;
+  for (int s = tid; s < ns; s += 256) M = fmaxf(M, ml[s].x);
+  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  if ((tid & 63) == 0) s_red[tid >> 6] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+  // split weights and the normaliser
+  float Ls = 0.f;
+  for (int s = tid; s < ns; s += 256) {
+    const float2 v = ml[s];
+    const float w = fast_exp2(v.x - M);
+    if (s < 1024) s_w[s] = w;
+    Ls += w * v.y;
+  }
+  for (int o = 32; o > 0; o >>= 1) Ls += __shfl_xor(Ls, o);
+  __syncthreads();
+  if ((tid & 63) == 0) s_red[4 + (tid >> 6)] = Ls;
+  __syncthreads();
+  Ls = (s_red[4] + s_red[5]) + (s_red[6] + s_red[7]);
+
+  const int quad = tid & 31, grp = tid >> 5;
+  f4 acc = {0.f, 0.f, 0.f, 0.f};
+  const f4* src = reinterpret_cast<const f4*>(a.ws_acc + row0 * kD) + quad;
+#pragma unroll 8
+  for (int s = grp; s < ns; s += 8) {
+    const float w = (s < 1024) ? s_w[s] : fast_exp2(ml[s].x - M);
+    acc += w * src[(size_t)s * (kD / 4)];
+  }
+  s_part[grp][quad] = acc;
+  __syncthreads();
+  if (tid >= 64) return;
+  // lane l owns coordinates 2l, 2l+1
+  const int lane = tid;
+  float o0 = 0.f, o1 = 0.f;
+#pragma unroll
+  for (int gq = 0; gq < 8; ++gq) {
+    const f4 v = s_part[gq][lane >> 1];
+    o0 += (lane & 1) ? v[2] : v[0];
+    o1 += (lane & 1) ? v[3] : v[1];
   }
   const float inv = 1.0f / Ls;
   o0 *= inv;
@@ -342,7 +484,7 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
     y1 = fmaf(sgn, y1, p1);
   }
   const float nrm = 0.08838834764831845f;  // 1/sqrt(128)
-  *reinterpret_cast<float2*>(out) = make_float2(y0 * nrm, y1 * nrm);
+  *reinterpret_cast<float2*>(out + 2 * lane) = make_float2(y0 * nrm, y1 * nrm);
 }
 
 DecodePlan plan_decode(int batch, int hkv, int max_seq_len, int num_cus) {
@@ -394,10 +536,13 @@ hipError_t launch_decode(const CacheView& c, const float* rot, const void* q, in
   a.ws_acc = reinterpret_cast<float*>(workspace);
   a.ws_ml = a.ws_acc + rows * kD;
   a.out = out;
-  hipLaunchKernelGGL(decode_split_kernel, dim3(plan.splits, c.hkv, batch), dim3(256), 0, stream, a);
+  if (a.group <= 8)
+    hipLaunchKernelGGL(decode_split_kernel<true>, dim3(plan.splits, c.hkv, batch), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(decode_split_kernel<false>, dim3(plan.splits, c.hkv, batch), dim3(256), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_merge_kernel, dim3(hq, batch), dim3(64), 0, stream, a);
+  hipLaunchKernelGGL(decode_merge_kernel, dim3(hq, batch), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -122,33 +122,53 @@ __device__ __forceinline__ float load_as_float(const void* base, size_t idx, int
   return (float)reinterpret_cast<const _Float16*>(base)[idx];
 }
 
-// Load 32 consecutive elements (128-bit aligned) as fp32.
+// Load 32 consecutive elements (128-bit aligned) as fp32.  The dtype branch
+// is taken once, outside the element loops.
 __device__ __forceinline__ void load32(const void* base, size_t idx, int dtype, float x[32]) {
   if (dtype == 0) {
     const f4* p = reinterpret_cast<const f4*>(reinterpret_cast<const float*>(base) + idx);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      f4 v = p[i];
+      const f4 v = p[i];
       x[4 * i] = v[0]; x[4 * i + 1] = v[1]; x[4 * i + 2] = v[2]; x[4 * i + 3] = v[3];
     }
-  } else {
-    const u4* p = reinterpret_cast<const u4*>(reinterpret_cast<const uint16_t*>(base) + idx);
+    return;
+  }
+  const u4* p = reinterpret_cast<const u4*>(reinterpret_cast<const uint16_t*>(base) + idx);
+  u4 v[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      u4 v = p[i];
+  for (int i = 0; i < 4; ++i) v[i] = p[i];
+  if (dtype == 1) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const uint32_t w = v[k];
-        if (dtype == 1) {
-          x[8 * i + 2 * k] = __builtin_bit_cast(float, w << 16);
-          x[8 * i + 2 * k + 1] = __builtin_bit_cast(float, w & 0xFFFF0000u);
-        } else {
-          x[8 * i + 2 * k] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
-          x[8 * i + 2 * k + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
-        }
+        x[8 * i + 2 * k] = __builtin_bit_cast(float, v[i][k] << 16);
+        x[8 * i + 2 * k + 1] = __builtin_bit_cast(float, v[i][k] & 0xFFFF0000u);
       }
-    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        x[8 * i + 2 * k] = (float)__builtin_bit_cast(_Float16, (uint16_t)(v[i][k] & 0xFFFFu));
+        x[8 * i + 2 * k + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(v[i][k] >> 16));
+      }
   }
+}
+
+// 2^x on the transcendental unit (v_exp_f32).  Results below 2^-126 flush to
+// zero, which is harmless for softmax weights relative to a running maximum.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Largest of the eight non-negative fp16 values held in two u2 pairs, as
+// fp16 bits (non-negative fp16 bit patterns order like the values).
+typedef uint16_t us2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t max_half_bits(const u2& a, const u2& b) {
+  const us2 m0 = __builtin_elementwise_max(__builtin_bit_cast(us2, a[0]), __builtin_bit_cast(us2, a[1]));
+  const us2 m1 = __builtin_elementwise_max(__builtin_bit_cast(us2, b[0]), __builtin_bit_cast(us2, b[1]));
+  const us2 m = __builtin_elementwise_max(m0, m1);
+  return m[0] > m[1] ? m[0] : m[1];
 }
 
 // ---------------------------------------------------------------------------

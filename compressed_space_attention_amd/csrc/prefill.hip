@@ -12,9 +12,9 @@
 //   O'^T[dim][row] += V^T[dim][token] P~[row][token]   (16x16x32)
 // A workgroup (4 waves, 32 rows each) owns 128 rows of one kv head and walks
 // the pages up to its causal limit.  Each page is unpacked once per workgroup
-// into LDS as f16: K^ token-major (rows of 128 coordinates) and V^ transposed
-// by an identity MFMA into [coordinate][token], so every wave reads ready
-// matrix-core operands.  Grid x is the kv head, so on an 8-XCD part the tiles
+// into LDS as f16: K^ token-major (rows of 128 coordinates) and V^ as
+// [coordinate][token], so every wave reads ready matrix-core operands.  V pages are stored in matrix-core order, so each
+// thread converts one 12-byte chunk straight into four LDS rows.  Grid x is the kv head, so on an 8-XCD part the tiles
 // of one kv head share an XCD's L2 when there are 8 kv heads.
 #include <math.h>
 
@@ -107,10 +107,6 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(PrefillArgs a) {
     }
   }
 
-  h4 ident;
-#pragma unroll
-  for (int s = 0; s < 4; ++s) ident[s] = (4 * jq + s == col) ? (_Float16)1.0f : (_Float16)0.0f;
-
   float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f}, rho = 1.0f;
   f4 acc[2][8];
 #pragma unroll
@@ -118,13 +114,16 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
     for (int m = 0; m < 8; ++m) acc[cb][m] = f4{0.f, 0.f, 0.f, 0.f};
 
-  // Codes of the wave's 16 tokens of a page: lane (token col, group jq).
+  // Per page, thread (lane, wave) loads K group jq of token 16*wave + col and
+  // chunk `wave` of V region `lane` (V pages are stored in matrix-core order:
+  // that chunk holds tokens 16*wave + 4*jq + r for coordinates 32*(col/4) +
+  // 4m + col%4, m = 0..7).
   u3 kc, vc;
   auto load_codes = [&](int pg) {
     const int page = a.block_table[pg];
-    const size_t rec = ((size_t)page * a.hkv + g) * kPage + 16 * wave + col;
-    kc = *reinterpret_cast<const u3*>(a.k_codes + rec * kRec + 12 * jq);
-    vc = *reinterpret_cast<const u3*>(a.v_codes + rec * kRec + 12 * jq);
+    const size_t base = ((size_t)page * a.hkv + g) * kPage;
+    kc = *reinterpret_cast<const u3*>(a.k_codes + (base + 16 * wave + col) * kRec + 12 * jq);
+    vc = *reinterpret_cast<const u3*>(a.v_codes + (base + lane) * kRec + 12 * wave);
   };
   if (n_pages > 0) load_codes(0);
 
@@ -141,12 +140,8 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(PrefillArgs a) {
       }
       group_to_selectors(vc.x, vc.y, vc.z, z);
 #pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        const f4 t = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(h4, selector_to_f16(z[m])), ident,
-                                                            f4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-        const h4 tv = {(_Float16)t[0], (_Float16)t[1], (_Float16)t[2], (_Float16)t[3]};
-        *reinterpret_cast<h4*>(s_v + (16 * m + col) * kVStride + 16 * wave + 4 * jq) = tv;
-      }
+      for (int m = 0; m < 8; ++m)
+        *reinterpret_cast<u2*>(s_v + (16 * m + col) * kVStride + 16 * wave + 4 * jq) = selector_to_f16(z[m]);
     }
     __syncthreads();
     if (pg + 1 < n_pages) load_codes(pg + 1);

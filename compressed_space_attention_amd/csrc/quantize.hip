@@ -68,10 +68,26 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(
 
   const int p = pos[tok];
   const int page = block_table[(size_t)seq_idx[tok] * max_pages + (p >> 6)];
-  const size_t rec = ((size_t)page * hkv + head) * kPage + (p & 63);
-  uint8_t* codes = which ? v_codes : k_codes;
-  *reinterpret_cast<u3*>(codes + rec * kRec + 12 * j) = w;
-  if (j == 0) (which ? v_norms : k_norms)[rec] = float_to_half_sat(n);
+  const int slot = p & 63;
+  const size_t rec = ((size_t)page * hkv + head) * kPage + slot;
+  if (!which) {
+    *reinterpret_cast<u3*>(k_codes + rec * kRec + 12 * j) = w;
+    if (j == 0) k_norms[rec] = float_to_half_sat(n);
+    return;
+  }
+  // V: byte lane b of this group goes to region n = 4j + b (quad q of the
+  // slot), chunk c = slot / 16, byte lane r = slot % 4 -- the order in which
+  // the decode matrix cores consume V (see the cache layout in isoquant.h).
+  uint8_t* blk = v_codes + ((size_t)page * hkv + head) * (kPage * kRec);
+  const int c = slot >> 4, q = (slot >> 2) & 3, r = slot & 3;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    uint8_t* dst = blk + (4 * j + b + 16 * q) * kRec + 12 * c + r;
+    dst[0] = (uint8_t)(w.x >> (8 * b));
+    dst[4] = (uint8_t)(w.y >> (8 * b));
+    dst[8] = (uint8_t)(w.z >> (8 * b));
+  }
+  if (j == 0) v_norms[rec] = float_to_half_sat(n);
 }
 
 hipError_t launch_quantize_append(const CacheView& c, const float* rot, const void* k, const void* v,

@@ -294,11 +294,31 @@ def dequantize(codes, norm16, blocks) -> np.ndarray:
 
 
 # ----------------------------------------------------------------------------
-# Paged cache (R9): pages of 64 tokens; per (page, kv head) the 64 records are
-# contiguous, codes [num_pages][Hkv][64][48] and fp16 norms [num_pages][Hkv][64],
-# separately for K and V; token t of sequence s lives in page
-# block_table[s][t // 64], slot t % 64.
+# Paged cache (R9): pages of 64 tokens; per (page, kv head) a 3072-byte block
+# of codes and 64 fp16 norms, separately for K and V; token t of sequence s
+# lives in page block_table[s][t // 64], slot t % 64.
+#
+# K blocks hold the 64 records in slot order (slot t at bytes 48t..48t+47).
+# V blocks hold the same 48-byte records with their bytes permuted into the
+# order the decode matrix cores read them (reading R9b): the block is 64
+# regions of 48 bytes; region n + 16q (n = 0..15, q = 0..3) is four 12-byte
+# chunks c = 0..3; byte lane r (bytes r, 4+r, 8+r) of chunk c of region
+# (n, q) is the 24-bit byte lane n % 4 of group n // 4 of the record in slot
+# 16c + 4q + r.  Nothing is lost or added: it is a fixed byte permutation.
 # ----------------------------------------------------------------------------
+def v_block_offsets() -> np.ndarray:
+    """int[64][48]: physical byte offset in a V block of (slot, record byte)."""
+    off = np.empty((PAGE_TOKENS, CODE_BYTES), dtype=np.int64)
+    for t in range(PAGE_TOKENS):
+        c, q, r = t // 16, (t % 16) // 4, t % 4
+        for j in range(CODE_BYTES):
+            g, k = divmod(j, 12)          # group and byte within the group
+            i, b = divmod(k, 4)           # dword w_i of the group, byte lane b
+            n = 4 * g + b
+            off[t, j] = (n + 16 * q) * 48 + 12 * c + 4 * i + r
+    return off
+
+
 class PagedCache:
     def __init__(self, num_pages: int, n_kv_heads: int):
         self.num_pages = num_pages
@@ -321,10 +341,28 @@ class PagedCache:
         pos = np.asarray(pos)
         return np.asarray(block_table)[seq, pos // PAGE_TOKENS], pos % PAGE_TOKENS
 
+    def records(self, which: str, page, head: int, slot) -> np.ndarray:
+        """48-byte records (K-format byte order) of the given slots."""
+        page, slot = np.asarray(page), np.asarray(slot)
+        if which == "k":
+            return self.k_codes[page, head, slot]
+        blocks = self.v_codes[page, head].reshape(np.shape(page) + (PAGE_TOKENS * CODE_BYTES,))
+        return np.take_along_axis(blocks, v_block_offsets()[slot], axis=-1)
+
+    def store(self, which: str, page, head: int, slot, recs):
+        page, slot = np.asarray(page), np.asarray(slot)
+        if which == "k":
+            self.k_codes[page, head, slot] = recs
+            return
+        flat = self.v_codes.reshape(self.num_pages, self.n_kv_heads, PAGE_TOKENS * CODE_BYTES)
+        offs = v_block_offsets()[slot]
+        for i in range(len(page)):
+            flat[page[i], head, offs[i]] = recs[i]
+
     def gather(self, block_table, seq: int, length: int, head: int, which: str):
         """(codes uint8[length][128], norm16 uint16[length]) of tokens 0..length-1."""
         page, slot = self.locate(block_table, seq, np.arange(length))
-        codes = getattr(self, which + "_codes")[page, head, slot]
+        codes = self.records(which, page, head, slot)
         norms = getattr(self, which + "_norms")[page, head, slot]
         return unpack_codes(codes), norms
 
@@ -347,7 +385,7 @@ def quantize_append(cache: PagedCache, blocks_all, k, v, seq_idx, pos, block_tab
             page = np.asarray(block_table)[np.asarray(seq_idx, dtype=np.int64),
                                            pos_a // PAGE_TOKENS]
             slot = pos_a % PAGE_TOKENS
-            getattr(cache, name + "_codes")[page, h, slot] = packed
+            cache.store(name, page, h, slot, packed)
             getattr(cache, name + "_norms")[page, h, slot] = q["norm16"]
         info[name] = per_head
     return info

@@ -69,8 +69,8 @@ def code_parity(gpu: O.PagedCache, ref: O.PagedCache, info, scen: Scenario):
     stats = {"codes": 0, "mismatch": 0, "near": 0, "norm_mismatch": 0}
     for name in ("k", "v"):
         for h in range(scen.hkv):
-            g_rec = getattr(gpu, name + "_codes")[page, h, slot]
-            r_rec = getattr(ref, name + "_codes")[page, h, slot]
+            g_rec = gpu.records(name, page, h, slot)
+            r_rec = ref.records(name, page, h, slot)
             g_codes, r_codes = O.unpack_codes(g_rec), O.unpack_codes(r_rec)
             near = info[name][h]["near"]
             bad = g_codes != r_codes
@@ -81,9 +81,12 @@ def code_parity(gpu: O.PagedCache, ref: O.PagedCache, info, scen: Scenario):
                 i, j = np.argwhere(bad & ~near)[0]
                 raise AssertionError(f"{name} head {h} vector {i} coord {j}: gpu {g_codes[i, j]} "
                                      f"oracle {r_codes[i, j]} u={info[name][h]['u'][i, j]!r}")
-            # records whose codes agree must agree byte for byte
+            # records whose codes agree must agree byte for byte (in place, too)
             same = ~bad.any(axis=1)
             assert np.array_equal(g_rec[same], r_rec[same]), f"{name} packing differs"
+            if name == "v" and np.all(same):
+                pg = np.unique(page)
+                assert np.array_equal(gpu.v_codes[pg, h], ref.v_codes[pg, h]) or len(pg) == 0
             gn = getattr(gpu, name + "_norms")[page, h, slot]
             rn = getattr(ref, name + "_norms")[page, h, slot]
             nb = gn != rn

@@ -1,0 +1,190 @@
+"""Parity at the full sizes of the named workloads, in the launch configuration
+the benchmark uses (same entry points, same split planning).
+
+Large inputs are drawn on the GPU by a seeded torch generator; the oracle gets
+the sampled inputs copied to the host.  Attention parity uses the GPU-written
+cache; code parity re-quantises sampled vectors with the oracle.  The cosine
+similarity of compressed vs uncompressed fp64 attention is reported."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from compressed_space_attention_amd import synth, workloads
+from oracle import isoquant_oracle as O
+from tests.gpu_cases import max_row_error, tol
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+from compressed_space_attention_amd import isoquant as iq  # noqa: E402
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+class Built:
+    """A workload's cache quantised by the GPU, inputs kept on the device."""
+
+    def __init__(self, w, lens, device="cuda"):
+        self.w = w
+        self.lens = np.asarray(lens, dtype=np.int64)
+        self.quats = synth.quaternions(w.seed, w.n_kv_heads)
+        self.blocks = O.rotation_matrices(self.quats)
+        pages = [-(-int(n) // 64) for n in self.lens]
+        self.bt, self.num_pages = synth.block_table(w.seed + 5, pages, shuffle=w.shuffle_pages)
+        self.bt_dev = torch.from_numpy(self.bt).to(device)
+        self.lens_dev = torch.from_numpy(self.lens.astype(np.int32)).to(device)
+        self.rot = iq.rotation_init(self.quats, device=device)
+        self.cache = iq.PagedCache(self.num_pages, w.n_kv_heads, device=device, zero=True)
+        dt = {"bf16": torch.bfloat16, "f32": torch.float32}[w.dtype]
+        total = int(self.lens.sum())
+        scale = torch.ones(w.n_kv_heads, 128, device=device)
+        if w.k_outliers:
+            ch = synth.outlier_channels(w.seed + 1, w.n_kv_heads)
+            for h in range(w.n_kv_heads):
+                scale[h, torch.from_numpy(ch[h]).to(device)] = 10.0
+        self.k = (synth.draw_normal_device(w.seed + 2, (total, w.n_kv_heads, 128), torch.float32, device)
+                  * scale).to(dt)
+        self.v = synth.draw_normal_device(w.seed + 3, (total, w.n_kv_heads, 128), dt, device)
+        self.seq_idx = np.concatenate([np.full(n, b, np.int32) for b, n in enumerate(self.lens)])
+        self.pos = np.concatenate([np.arange(n, dtype=np.int32) for n in self.lens])
+        iq.quantize_append(self.cache, self.rot, self.k, self.v, torch.from_numpy(self.seq_idx).to(device),
+                           torch.from_numpy(self.pos).to(device), self.bt_dev)
+        self.q = synth.draw_normal_device(w.seed + 4, (len(self.lens), w.n_q_heads, 128), dt, device)
+        torch.cuda.synchronize()
+
+    def sampled_code_parity(self, n_sample, seed):
+        rng = np.random.default_rng(seed)
+        idx = np.unique(rng.integers(0, len(self.pos), size=n_sample))
+        idx = np.unique(np.concatenate([idx, [0, len(self.pos) - 1]]))
+        page = self.bt[self.seq_idx[idx], self.pos[idx] // 64]
+        slot = self.pos[idx] % 64
+        codes = mism = near = 0
+        host = O.PagedCache.from_arrays(*self.cache.to_host())
+        for name, x in (("k", self.k), ("v", self.v)):
+            xs = x[torch.from_numpy(idx).cuda()].double().cpu().numpy()
+            for h in range(self.w.n_kv_heads):
+                q = O.quantize(xs[:, h], self.blocks[h])
+                gc = O.unpack_codes(host.records(name, page, h, slot))
+                gn = getattr(host, name + "_norms")[page, h, slot]
+                bad = gc != q["codes"]
+                assert not np.any(bad & ~q["near"]), f"{name} head {h}: code mismatch off-boundary"
+                nb = gn != q["norm16"]
+                assert not np.any(nb & ~q["norm_near"]), f"{name} head {h}: norm mismatch"
+                codes += gc.size
+                mism += int(bad.sum())
+                near += int(q["near"].sum())
+        _say(f"  sampled codes {codes}: mismatches {mism}, near-boundary {near}")
+        assert mism < 1e-5 * codes + 1
+        return mism, near, codes
+
+    def decode(self):
+        return iq.decode_attention(self.cache, self.rot, self.q, self.bt_dev, self.lens_dev,
+                                   int(self.lens.max()))
+
+    def oracle_decode(self, seqs):
+        host = O.PagedCache.from_arrays(*self.cache.to_host())
+        q = self.q.double().cpu().numpy()
+        bt = self.bt[seqs]
+        return O.decode_attention(host, self.blocks, q[seqs], bt, self.lens[seqs])
+
+    def cosine_vs_uncompressed(self, seq, heads, out):
+        grp = self.w.group
+        n = int(self.lens[seq])
+        start = int(self.lens[:seq].sum())
+        cos = []
+        for h in heads:
+            g = h // grp
+            k = self.k[start:start + n, g].double().cpu().numpy()
+            v = self.v[start:start + n, g].double().cpu().numpy()
+            q = self.q[seq, h:h + 1].double().cpu().numpy()
+            ref = O.reference_attention(q, k, v)
+            cos.append(float(O.row_cosine(out[seq, h:h + 1], ref)[0]))
+        return cos
+
+
+def test_tiny_decode_full():
+    w = workloads.TINY_DECODE
+    b = Built(w, w.seq_lens())
+    b.sampled_code_parity(4096, 1)
+    out = b.decode().cpu().numpy()
+    ref = b.oracle_decode(np.arange(w.batch))
+    err = max_row_error(out, ref)
+    cos = b.cosine_vs_uncompressed(0, range(w.n_q_heads), out)
+    _say(f"  {w.name}: max row error {err:.3e}, cosine vs uncompressed {np.round(cos, 4)}")
+    assert err <= tol()
+
+
+def test_gqa_decode_32k_full():
+    w = workloads.GQA_DECODE_32K
+    b = Built(w, w.seq_lens())
+    b.sampled_code_parity(8192, 2)
+    out = b.decode().cpu().numpy()
+    ref = b.oracle_decode(np.arange(w.batch))
+    err = max_row_error(out, ref)
+    cos = b.cosine_vs_uncompressed(0, range(0, w.n_q_heads, 4), out)
+    _say(f"  {w.name}: max row error {err:.3e}, cosine min {min(cos):.4f} mean {np.mean(cos):.4f}")
+    assert err <= tol()
+
+
+def test_ragged_decode_sampled_sequences():
+    w = workloads.RAGGED_DECODE
+    lens = w.seq_lens()
+    b = Built(w, lens)
+    b.sampled_code_parity(8192, 3)
+    out = b.decode().cpu().numpy()
+    pick = np.unique([int(np.argmin(lens)), int(np.argmax(lens)), 5])
+    ref = b.oracle_decode(pick)
+    err = max_row_error(out[pick], ref)
+    _say(f"  {w.name}: lens {lens.tolist()}, checked {pick.tolist()}, max row error {err:.3e}")
+    assert err <= tol()
+
+
+def test_long_decode_128k_sampled_sequence():
+    w = workloads.LONG_DECODE_128K
+    b = Built(w, w.seq_lens())
+    b.sampled_code_parity(4096, 4)
+    out = b.decode().cpu().numpy()
+    ref = b.oracle_decode(np.array([w.batch - 1]))
+    err = max_row_error(out[w.batch - 1:], ref)
+    _say(f"  {w.name}: max row error {err:.3e} (last sequence, all heads)")
+    assert err <= tol()
+    assert np.all(np.isfinite(out))
+
+
+def test_chunked_prefill_full_shape_sampled_rows():
+    p = workloads.CHUNKED_PREFILL
+    w = workloads.DecodeWorkload(p.name, 1, p.n_q_heads, p.n_kv_heads, p.dtype, False, True,
+                                 p.seed, context=p.total)
+    # cache: the first `cached` tokens, then the appended chunk in a second call
+    b = Built(w, [p.cached])
+    k2 = synth.draw_normal_device(p.seed + 7, (p.appended, p.n_kv_heads, 128), torch.bfloat16)
+    v2 = synth.draw_normal_device(p.seed + 8, (p.appended, p.n_kv_heads, 128), torch.bfloat16)
+    pages = -(-p.total // 64)
+    bt, num_pages = synth.block_table(p.seed + 9, [pages], shuffle=True)
+    b.bt, b.bt_dev = bt, torch.from_numpy(bt).cuda()
+    b.cache = iq.PagedCache(num_pages, p.n_kv_heads, zero=True)
+    pos1 = torch.arange(p.cached, dtype=torch.int32, device="cuda")
+    pos2 = torch.arange(p.cached, p.total, dtype=torch.int32, device="cuda")
+    iq.quantize_append(b.cache, b.rot, b.k, b.v, torch.zeros_like(pos1), pos1, b.bt_dev)
+    iq.quantize_append(b.cache, b.rot, k2, v2, torch.zeros_like(pos2), pos2, b.bt_dev)
+    b.k = torch.cat([b.k, k2])
+    b.v = torch.cat([b.v, v2])
+    b.seq_idx = np.zeros(p.total, np.int32)
+    b.pos = np.arange(p.total, dtype=np.int32)
+    b.lens = np.array([p.total])
+    b.sampled_code_parity(4096, 5)
+    q = synth.draw_normal_device(p.seed + 10, (p.n_queries, p.n_q_heads, 128), torch.bfloat16)
+    out = iq.prefill_attention(b.cache, b.rot, q, p.q_start, b.bt_dev[0]).cpu().numpy()
+    rows = np.array([0, 1, 100, 255, 256, 400, p.n_queries - 2, p.n_queries - 1])
+    host = O.PagedCache.from_arrays(*b.cache.to_host())
+    ref = O.prefill_attention(host, b.blocks, q.double().cpu().numpy(), p.q_start, bt[0], rows=rows)
+    err = max_row_error(out[rows], ref)
+    _say(f"  {p.name}: max row error {err:.3e} over rows {rows.tolist()}")
+    assert err <= tol()

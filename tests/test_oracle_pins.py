@@ -248,6 +248,30 @@ def test_pack_round_trip_and_saturation():
     assert np.all(O.pack_codes(np.full((1, 128), 7, np.uint8)) == 0xFF)
 
 
+def test_v_block_permutation():
+    """V blocks are a fixed byte permutation of the 64 records (reading R9b).
+    Hand-derived offsets: slot 5 (chunk 0, quad 1, lane 1), record byte 0
+    (group 0, dword 0, byte lane 0 -> region 0 + 16) -> 16*48 + 1 = 769;
+    slot 63, byte 47 (group 3, dword 2, byte lane 3 -> region 15 + 48) ->
+    63*48 + 12*3 + 8 + 3 = 3071; slot 16 (chunk 1), byte 13 (group 1, dword 0,
+    byte lane 1 -> region 5) -> 5*48 + 12 = 252."""
+    off = O.v_block_offsets()
+    assert sorted(off.ravel().tolist()) == list(range(3072))
+    assert off[5, 0] == 769 and off[63, 47] == 3071 and off[16, 13] == 252 and off[0, 0] == 0
+    c = O.PagedCache(3, 2)
+    recs = np.random.default_rng(4).integers(0, 256, (70, 48), dtype=np.uint8)
+    page = np.array([1] * 64 + [2] * 6)
+    slot = np.concatenate([np.arange(64), np.arange(6)])
+    c.store("v", page, 1, slot, recs)
+    assert np.array_equal(c.records("v", page, 1, slot), recs)
+    assert np.all(c.v_codes[0] == 0) and np.all(c.v_codes[:, 0] == 0)
+    # region (n=6, q=2) chunk 1 byte lane 3 holds slot 16+8+3=27's byte lane 2 of group 1
+    blk = c.v_codes[1, 1].reshape(3072)
+    region = blk[(6 + 32) * 48:(6 + 32) * 48 + 48]
+    for i in range(3):
+        assert region[12 * 1 + 4 * i + 3] == recs[27, 12 * 1 + 4 * i + 2]
+
+
 # --------------------------------------------------------------- attention --
 def _small_cache(seed, lens, hkv, pages_extra=3):
     pages = [-(-int(n) // 64) for n in lens]
