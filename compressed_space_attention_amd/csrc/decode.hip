@@ -88,22 +88,59 @@ __device__ __forceinline__ int tile_block(int t, int col) {
   return PACK8 ? 2 * t + (col >> 3) : t;
 }
 
-template <bool PACK8>
-__device__ __forceinline__ void load_page(const DecodeArgs& a, int page, int g, int lane,
-                                          PageRegs<PACK8>& r) {
-  const int col = lane & 15, jq = lane >> 4;
+// ---- LDS page ring -------------------------------------------------------
+// Each wave streams its pages through two LDS slots of 6,400 bytes (the
+// packed page of one kv head: K codes 3,072 | V codes 3,072 | K norms 128 |
+// V norms 128), filled by direct global->LDS loads (7 per page).  Two pages are
+// in flight while the wave computes a third from registers.
+constexpr int kSlotBytes = 6400;
+constexpr int kMaxPagesPerSplit = 256;  // the planner keeps splits within this
+#define IQ_MAX_GROUP_BYTES (16 * 128 * 4)  // up to 16 query heads of fp32
+constexpr int kDmaPerPage = 7;
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+__device__ __forceinline__ void lds_dma16(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_ptr)lds, 16, 0, 0);
+}
+__device__ __forceinline__ void lds_dma4(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_ptr)lds, 4, 0, 0);
+}
+// s_waitcnt immediates (gfx9 encoding: vmcnt [3:0] and [15:14], expcnt [6:4],
+// lgkmcnt [11:8]); issued through the builtin so the compiler's own counter
+// tracking knows which loads have landed.
+constexpr int wait_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+constexpr int kWaitLgkm0 = 0xF | (0x3 << 14) | (0x7 << 4);
+
+// Issue the 7 loads of one page into `slot` (wave-uniform pointer).
+__device__ __forceinline__ void issue_page(const DecodeArgs& a, int page, int g, int lane,
+                                           uint8_t* slot) {
   const size_t base = ((size_t)page * a.hkv + g) * kPage;  // record index of slot 0
+  const uint8_t* kb = a.k_codes + base * kRec + 16 * lane;
+  const uint8_t* vb = a.v_codes + base * kRec + 16 * lane;
+#pragma unroll
+  for (int i = 0; i < 3; ++i) lds_dma16(kb + 1024 * i, slot + 1024 * i);
+#pragma unroll
+  for (int i = 0; i < 3; ++i) lds_dma16(vb + 1024 * i, slot + 3072 + 1024 * i);
+  // lanes 0-31 bring the K norms (two per lane), lanes 32-63 the V norms
+  const uint16_t* nb = (lane < 32 ? a.k_norms : a.v_norms) + base + 2 * (lane & 31);
+  lds_dma4(nb, slot + 6144);
+}
+
+template <bool PACK8>
+__device__ __forceinline__ void read_page(const uint8_t* slot, int lane, PageRegs<PACK8>& r) {
+  const int col = lane & 15, jq = lane >> 4;
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb)
-    r.kc[rb] = *reinterpret_cast<const u3*>(a.k_codes + (base + 16 * rb + col) * kRec + 12 * jq);
-  const u4* vreg = reinterpret_cast<const u4*>(a.v_codes + (base + lane) * kRec);
+    r.kc[rb] = *reinterpret_cast<const u3*>(slot + (16 * rb + col) * kRec + 12 * jq);
+  const u4* vreg = reinterpret_cast<const u4*>(slot + 3072 + lane * kRec);
 #pragma unroll
   for (int i = 0; i < 3; ++i) r.vr[i] = vreg[i];
+  const uint16_t* kn = reinterpret_cast<const uint16_t*>(slot + 6144);
 #pragma unroll
   for (int t = 0; t < PageRegs<PACK8>::NT; ++t) {
-    const size_t nb = base + 16 * tile_block<PACK8>(t, col) + 4 * jq;
-    r.kn[t] = *reinterpret_cast<const u2*>(a.k_norms + nb);
-    r.vn[t] = *reinterpret_cast<const u2*>(a.v_norms + nb);
+    const int tok = 16 * tile_block<PACK8>(t, col) + 4 * jq;
+    r.kn[t] = *reinterpret_cast<const u2*>(kn + tok);
+    r.vn[t] = *reinterpret_cast<const u2*>(kn + 64 + tok);
   }
 }
 
@@ -128,8 +165,7 @@ __device__ __forceinline__ float norm_frame(uint32_t max_bits, float current) {
 template <bool PACK8>
 __device__ __forceinline__ float column_max(float v) {
   if (PACK8) v = fmaxf(v, dpp_f<kRowRor8, 0xF>(v, v));
-  v = fmaxf(v, __shfl_xor(v, 16));
-  return fmaxf(v, __shfl_xor(v, 32));
+  return max_xor32(max_xor16(v));
 }
 
 // One page for one wave: scores on the matrix cores, online-softmax update,
@@ -184,8 +220,7 @@ __device__ __forceinline__ void process_page(const PageRegs<PACK8>& cur, PageSta
                          : max(max_half_bits(vn[0], vn[1]), max_half_bits(vn[NT - 2], vn[NT - 1]));
   mp = column_max<PACK8>(mp);
   if (PACK8) vbits = max(vbits, dpp_u<kRowRor8, 0xF>(vbits, vbits));
-  vbits = max(vbits, (uint32_t)__shfl_xor((int)vbits, 16));
-  vbits = max(vbits, (uint32_t)__shfl_xor((int)vbits, 32));
+  vbits = umax_xor32(umax_xor16(vbits));
   const float m_new = fmaxf(st.m_run, mp);        // finite: the page has a valid token
   const float corr = fast_exp2(st.m_run - m_new);  // 0 on the first page
   const float rho_new = norm_frame(vbits, st.rho);
@@ -252,49 +287,91 @@ __device__ __forceinline__ void process_page(const PageRegs<PACK8>& cur, PageSta
 template <bool PACK8>
 __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // wave-uniform: keeps the wave's page bookkeeping in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, jq = lane >> 4;
   const int pg_begin = split * a.pages_per_split;
-  int pg = pg_begin + wave;
-  // The page id of the wave's first page is fetched together with the length.
-  const int first_page = (pg < a.max_pages) ? a.block_table[(size_t)b * a.max_pages + pg] : 0;
+  const int pg_first = pg_begin + wave;
+  // Page ids of the wave's first two pages are fetched together with the length.
+  const int* bt = a.block_table + (size_t)b * a.max_pages;
+  const int page0 = (pg_first < a.max_pages) ? bt[pg_first] : 0;
+  const int page1 = (pg_first + 4 < a.max_pages) ? bt[pg_first + 4] : 0;
   const int L = a.seq_lens[b];
-  const int n_pages = (L + kPage - 1) / kPage;
+  // (a length beyond the block table breaks the contract; never read past it)
+  const int n_pages = min((L + kPage - 1) / kPage, a.max_pages);
   if (pg_begin >= n_pages) return;  // uniform for the workgroup
   const int pg_end = min(n_pages, pg_begin + a.pages_per_split);
+  const int n_mine = pg_first < pg_end ? (pg_end - pg_first + 3) / 4 : 0;  // this wave's pages
 
+  __shared__ __attribute__((aligned(16))) uint8_t s_ring[4][2][kSlotBytes];  // 51,200 B
+  __shared__ __attribute__((aligned(16))) float s_rot[kRotFloats];           // 2,048 B
   __shared__ uint32_t s_q[32 * 64];  // Q' operands: [kstep*8 + dword][lane]
+  __shared__ int s_pages[kMaxPagesPerSplit];  // the split's page ids
+  __shared__ __attribute__((aligned(16))) uint8_t s_qraw[IQ_MAX_GROUP_BYTES];  // the group's queries
   __shared__ float s_qinv[16];
-  __shared__ float s_acc[4][32][64];
   __shared__ float s_m[4][16], s_l[4][16];
 
-  // Wave 0 loads the group's queries before its first page.
-  float x[32];
+  // Everything the prologue needs arrives by direct-to-LDS loads issued before
+  // the pages (lane-predicated): the split's page ids (a quarter per wave), and
+  // in wave 0 the rotation blocks and the group's queries.  No load that the
+  // compiler tracks in registers precedes the page loads, so no implicit wait
+  // ever drains them.
+  const int n_split = pg_end - pg_begin;
+  int n_pre = 0;  // direct-to-LDS loads issued by this wave before its pages
+  if (64 * wave < n_split) {
+    if (64 * wave + lane < n_split) lds_dma4(bt + pg_begin + 64 * wave + lane, &s_pages[64 * wave]);
+    ++n_pre;
+  }
+  const int qbytes = a.group * kD * (a.q_dtype == 0 ? 4 : 2);
   if (wave == 0) {
-    if (col < a.group) {
-      load32(a.q, ((size_t)b * a.hq + (size_t)g * a.group + col) * kD + 32 * jq, a.q_dtype, x);
+    const uint8_t* rg = reinterpret_cast<const uint8_t*>(a.rot + (size_t)g * kRotFloats) + 16 * lane;
+    lds_dma16(rg, s_rot);
+    lds_dma16(rg + 1024, reinterpret_cast<uint8_t*>(s_rot) + 1024);
+    const uint8_t* qg = reinterpret_cast<const uint8_t*>(a.q) +
+                        ((size_t)b * a.hq + (size_t)g * a.group) * kD * (a.q_dtype == 0 ? 4 : 2);
+    for (int i = 0; 1024 * i < qbytes; ++i) {
+      if (1024 * i + 16 * lane < qbytes) lds_dma16(qg + 1024 * i + 16 * lane, s_qraw + 1024 * i);
+      ++n_pre;
+    }
+    n_pre += 2;
+  }
+  (void)n_pre;
+  if (n_mine > 0) issue_page(a, page0, g, lane, s_ring[wave][0]);
+  if (n_mine > 1) issue_page(a, page1, g, lane, s_ring[wave][1]);
+  // The prologue loads have landed once at most the page loads are outstanding.
+  if (n_mine > 1)
+    __builtin_amdgcn_s_waitcnt(wait_vm(2 * kDmaPerPage));
+  else if (n_mine == 1)
+    __builtin_amdgcn_s_waitcnt(wait_vm(kDmaPerPage));
+  else
+    __builtin_amdgcn_s_waitcnt(wait_vm(0));
+
+  // Wave 0 rotates the queries with the four quarters of a head on adjacent
+  // lanes (lane = 4h + j), so the cross-lane butterflies are DPP quad moves,
+  // and writes Q' to LDS in the B-operand layout of the score MFMA: lane
+  // h + 16j holds coordinates 32j..32j+31 of head h.
+  if (wave == 0) {
+    const int h = lane >> 2, j = lane & 3;
+    float x[32];
+    if (h < a.group) {
+      lds_to_float32(s_qraw, h * kD + 32 * j, a.q_dtype, x);
     } else {
 #pragma unroll
       for (int i = 0; i < 32; ++i) x[i] = 0.f;
     }
-  }
-  PageRegs<PACK8> cur;
-  if (pg < pg_end) load_page<PACK8>(a, first_page, g, lane, cur);
-
-  // Wave 0 rotates the queries: lane (head col, quarter jq) holds coordinates
-  // 32jq..32jq+31, which is exactly the B-operand layout of the score MFMA.
-  if (wave == 0) {
-    wht128_quad<16, 32>(x, jq);
+    wht128_quad(x, j);
     float z[32];
-    so4_forward_quarter(a.rot + (size_t)g * kRotFloats, jq, x, z);
+    so4_forward_quarter(s_rot, j, x, z);
     float mx = 0.f;
 #pragma unroll
     for (int i = 0; i < 32; ++i) mx = fmaxf(mx, fabsf(z[i]));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = fmaxf(mx, quad_xor1(mx));
+    mx = fmaxf(mx, quad_xor2(mx));
     int e = 0;
     frexpf(mx, &e);
     const float sc = (mx > 0.f) ? ldexpf(1.0f, 1 - e) : 1.0f;  // max |z*sc| in [1, 2)
+    const int dst = h + 16 * j;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
@@ -302,15 +379,18 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
         const float v0 = z[8 * kk + 2 * d] * sc, v1 = z[8 * kk + 2 * d + 1] * sc;
         const _Float16 h0 = (_Float16)v0, h1 = (_Float16)v1;
         const _Float16 l0 = (_Float16)(v0 - (float)h0), l1 = (_Float16)(v1 - (float)h1);
-        s_q[(kk * 8 + d) * 64 + lane] =
+        s_q[(kk * 8 + d) * 64 + dst] =
             (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-        s_q[(kk * 8 + 4 + d) * 64 + lane] =
+        s_q[(kk * 8 + 4 + d) * 64 + dst] =
             (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
       }
     }
-    if (jq == 0) s_qinv[col] = 1.0f / sc;
+    if (j == 0) s_qinv[h] = 1.0f / sc;
   }
-  __syncthreads();
+  // LDS writes visible to the workgroup; unlike __syncthreads this does not
+  // wait for the page loads still in flight.
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  __builtin_amdgcn_s_barrier();
 
   h8 qhi[4], qlo[4];
 #pragma unroll
@@ -334,25 +414,39 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
   for (int m = 0; m < 8; ++m) st.acc[m] = f4{0.f, 0.f, 0.f, 0.f};
 
-  for (; pg < pg_end; pg += 4) {
-    PageRegs<PACK8> nxt;
-    const bool more = pg + 4 < pg_end;
-    if (more) load_page<PACK8>(a, a.block_table[(size_t)b * a.max_pages + pg + 4], g, lane, nxt);
+  for (int i = 0; i < n_mine; ++i) {
+    uint8_t* slot = s_ring[wave][i & 1];
+    const int pg = pg_first + 4 * i;
+    // page i has landed once at most the other slot's loads are outstanding
+    if (i + 1 < n_mine)
+      __builtin_amdgcn_s_waitcnt(wait_vm(kDmaPerPage));
+    else
+      __builtin_amdgcn_s_waitcnt(wait_vm(0));
+    PageRegs<PACK8> cur;
+    read_page<PACK8>(slot, lane, cur);
+    if (i + 2 < n_mine) {
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // slot read before it is refilled
+      issue_page(a, s_pages[wave + 4 * (i + 2)], g, lane, slot);
+    }
     if ((pg + 1) * kPage <= L)
       process_page<PACK8, false>(cur, st, pg * kPage, L, lane, fac, qhi, qlo);
     else
       process_page<PACK8, true>(cur, st, pg * kPage, L, lane, fac, qhi, qlo);
-    if (more) cur = nxt;
   }
 
   // ---- merge the four waves ----
   float l_col = st.l_run;
   if (PACK8) l_col += dpp_f<kRowRor8, 0xF>(l_col, l_col);
-  l_col += __shfl_xor(l_col, 16);
-  l_col += __shfl_xor(l_col, 32);
+  l_col = sum_xor32(sum_xor16(l_col));
   const float fin = a.out_factor / st.rho;
+  // The wave's own two slots hold its accumulator now (all its loads have
+  // landed): values 0-15 in slot 0, 16-31 in slot 1.
+  static_assert(kSlotBytes >= 16 * 64 * 4, "a slot holds half an accumulator");
+  float* acc_lo = reinterpret_cast<float*>(s_ring[wave][0]);
+  float* acc_hi = reinterpret_cast<float*>(s_ring[wave][1]);
 #pragma unroll
-  for (int k = 0; k < 32; ++k) s_acc[wave][k][lane] = st.acc[k >> 2][k & 3] * fin;
+  for (int k = 0; k < 32; ++k)
+    (k < 16 ? acc_lo : acc_hi)[(k & 15) * 64 + lane] = st.acc[k >> 2][k & 3] * fin;
   if (jq == 0) {
     s_m[wave][col] = st.m_run;
     s_l[wave][col] = l_col;
@@ -380,8 +474,10 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
         float s0 = 0.f, s1 = 0.f;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          s0 += wt[w] * s_acc[w][8 * part + k][lane];
-          s1 += wt[w] * s_acc[w][8 * part + 4 + k][lane];
+          // values 8*part + k and 8*part + 4 + k (slot 0 holds 0-15, slot 1 16-31)
+          const float* wacc = reinterpret_cast<const float*>(s_ring[w][part < 2 ? 0 : 1]);
+          s0 += wt[w] * wacc[((8 * part + k) & 15) * 64 + lane];
+          s1 += wt[w] * wacc[((8 * part + 4 + k) & 15) * 64 + lane];
         }
         o0[k] = s0;
         o1[k] = s1;
@@ -497,7 +593,8 @@ DecodePlan plan_decode(int batch, int hkv, int max_seq_len, int num_cus) {
   }
   long long splits = (target + units - 1) / units;
   splits = splits < 1 ? 1 : (splits > max_pages ? max_pages : splits);
-  const int pps = (int)((max_pages + splits - 1) / splits);
+  int pps = (int)((max_pages + splits - 1) / splits);
+  if (pps > kMaxPagesPerSplit) pps = kMaxPagesPerSplit;
   DecodePlan p;
   p.pages_per_split = pps;
   p.splits = (max_pages + pps - 1) / pps;

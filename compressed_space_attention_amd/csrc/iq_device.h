@@ -157,6 +157,41 @@ __device__ __forceinline__ void load32(const void* base, size_t idx, int dtype, 
   }
 }
 
+// 32 consecutive elements starting at element `idx` of an LDS buffer, as
+// fp32 (each dtype converted in its own straight-line branch).
+__device__ __forceinline__ void lds_to_float32(const uint8_t* buf, int idx, int dtype, float x[32]) {
+  if (dtype == 0) {
+    const f4* p = reinterpret_cast<const f4*>(buf + 4 * idx);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const f4 v = p[i];
+      x[4 * i] = v[0]; x[4 * i + 1] = v[1]; x[4 * i + 2] = v[2]; x[4 * i + 3] = v[3];
+    }
+  } else if (dtype == 1) {
+    const u4* p = reinterpret_cast<const u4*>(buf + 2 * idx);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const u4 v = p[i];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        x[8 * i + 2 * k] = __builtin_bit_cast(float, v[k] << 16);
+        x[8 * i + 2 * k + 1] = __builtin_bit_cast(float, v[k] & 0xFFFF0000u);
+      }
+    }
+  } else {
+    const u4* p = reinterpret_cast<const u4*>(buf + 2 * idx);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const u4 v = p[i];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        x[8 * i + 2 * k] = (float)__builtin_bit_cast(_Float16, (uint16_t)(v[k] & 0xFFFFu));
+        x[8 * i + 2 * k + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(v[k] >> 16));
+      }
+    }
+  }
+}
+
 // 2^x on the transcendental unit (v_exp_f32).  Results below 2^-126 flush to
 // zero, which is harmless for softmax weights relative to a running maximum.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -165,20 +200,73 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // fp16 bits (non-negative fp16 bit patterns order like the values).
 typedef uint16_t us2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t max_half_bits(const u2& a, const u2& b) {
-  const us2 m0 = __builtin_elementwise_max(__builtin_bit_cast(us2, a[0]), __builtin_bit_cast(us2, a[1]));
-  const us2 m1 = __builtin_elementwise_max(__builtin_bit_cast(us2, b[0]), __builtin_bit_cast(us2, b[1]));
+  const us2 m0 = __builtin_elementwise_max(__builtin_bit_cast(us2, (uint32_t)a[0]),
+                                            __builtin_bit_cast(us2, (uint32_t)a[1]));
+  const us2 m1 = __builtin_elementwise_max(__builtin_bit_cast(us2, (uint32_t)b[0]),
+                                            __builtin_bit_cast(us2, (uint32_t)b[1]));
   const us2 m = __builtin_elementwise_max(m0, m1);
   return m[0] > m[1] ? m[0] : m[1];
 }
 
 // ---------------------------------------------------------------------------
-// Unnormalised Walsh-Hadamard transform (Sylvester order) of a 128-vector held
-// by four lanes, 32 consecutive coordinates each: lane quarter j holds
-// coordinates 32j..32j+31.  XOR_A / XOR_B are the lane-xor distances of the
-// quarters j^1 and j^2.  Coordinate distances 1..16 are in-register
-// butterflies; 32 and 64 cross lanes.
+// Lane exchanges inside a quad of lanes, on the DPP path (full-rate VALU, no
+// LDS crossbar): xor 1 = quad_perm [1,0,3,2], xor 2 = quad_perm [2,3,0,1].
 // ---------------------------------------------------------------------------
-template <int XOR_A, int XOR_B>
+template <int QUAD_PERM>
+__device__ __forceinline__ float quad_swap(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), QUAD_PERM,
+                                                            0xF, 0xF, true));
+}
+__device__ __forceinline__ float quad_xor1(float v) { return quad_swap<0xB1>(v); }
+__device__ __forceinline__ float quad_xor2(float v) { return quad_swap<0x4E>(v); }
+
+// Exchanges across rows (16 lanes) and halves (32 lanes) with the gfx950
+// permlane swaps: with both operands equal to v, lane l of the two results
+// holds v[l] and v[l ^ 16] (resp. v[l ^ 32]) in some order, so any
+// symmetric combination of the pair is a butterfly reduction step.
+//
+// Note on bit casts: clang lowers __builtin_bit_cast of an ext_vector element
+// lvalue (v[1], v.y) as a load from the vector's first element, so every bit
+// cast here and elsewhere takes a converted rvalue ((uint32_t)v[1]).
+__device__ __forceinline__ u2 pair_xor16(uint32_t v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return u2{(uint32_t)r[0], (uint32_t)r[1]};
+}
+__device__ __forceinline__ u2 pair_xor32(uint32_t v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return u2{(uint32_t)r[0], (uint32_t)r[1]};
+}
+__device__ __forceinline__ float max_xor16(float v) {
+  const u2 p = pair_xor16(__builtin_bit_cast(uint32_t, v));
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)p[0]), __builtin_bit_cast(float, (uint32_t)p[1]));
+}
+__device__ __forceinline__ float max_xor32(float v) {
+  const u2 p = pair_xor32(__builtin_bit_cast(uint32_t, v));
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)p[0]), __builtin_bit_cast(float, (uint32_t)p[1]));
+}
+__device__ __forceinline__ float sum_xor16(float v) {
+  const u2 p = pair_xor16(__builtin_bit_cast(uint32_t, v));
+  return __builtin_bit_cast(float, (uint32_t)p[0]) + __builtin_bit_cast(float, (uint32_t)p[1]);
+}
+__device__ __forceinline__ float sum_xor32(float v) {
+  const u2 p = pair_xor32(__builtin_bit_cast(uint32_t, v));
+  return __builtin_bit_cast(float, (uint32_t)p[0]) + __builtin_bit_cast(float, (uint32_t)p[1]);
+}
+__device__ __forceinline__ uint32_t umax_xor16(uint32_t v) {
+  const u2 p = pair_xor16(v);
+  return max(p[0], p[1]);
+}
+__device__ __forceinline__ uint32_t umax_xor32(uint32_t v) {
+  const u2 p = pair_xor32(v);
+  return max(p[0], p[1]);
+}
+
+// ---------------------------------------------------------------------------
+// Unnormalised Walsh-Hadamard transform (Sylvester order) of a 128-vector held
+// by the four lanes of a quad, 32 consecutive coordinates each: lane quarter
+// j = lane % 4 holds coordinates 32j..32j+31.  Coordinate distances 1..16 are
+// in-register butterflies; 32 and 64 are DPP exchanges within the quad.
+// ---------------------------------------------------------------------------
 __device__ __forceinline__ void wht128_quad(float x[32], int j) {
 #pragma unroll
   for (int h = 1; h < 32; h <<= 1) {
@@ -193,16 +281,34 @@ __device__ __forceinline__ void wht128_quad(float x[32], int j) {
   }
   const float s1 = (j & 1) ? -1.0f : 1.0f;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    const float p = __shfl_xor(x[i], XOR_A);
-    x[i] = fmaf(s1, x[i], p);  // low quarter: x + p; high quarter: p - x
-  }
+  for (int i = 0; i < 32; ++i) x[i] = fmaf(s1, x[i], quad_xor1(x[i]));  // low: x + p, high: p - x
   const float s2 = (j & 2) ? -1.0f : 1.0f;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    const float p = __shfl_xor(x[i], XOR_B);
-    x[i] = fmaf(s2, x[i], p);
+  for (int i = 0; i < 32; ++i) x[i] = fmaf(s2, x[i], quad_xor2(x[i]));
+}
+
+// The same transform with the quarters on lanes l, l^XOR_A (j^1) and
+// l^XOR_B (j^2) of a wave (generic lane exchange; used where the quarters of
+// a vector must sit 16 lanes apart).
+template <int XOR_A, int XOR_B>
+__device__ __forceinline__ void wht128_spread(float x[32], int j) {
+#pragma unroll
+  for (int h = 1; h < 32; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      if ((i & h) == 0) {
+        const float a = x[i], b = x[i + h];
+        x[i] = a + b;
+        x[i + h] = a - b;
+      }
+    }
   }
+  const float s1 = (j & 1) ? -1.0f : 1.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) x[i] = fmaf(s1, x[i], __shfl_xor(x[i], XOR_A));
+  const float s2 = (j & 2) ? -1.0f : 1.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) x[i] = fmaf(s2, x[i], __shfl_xor(x[i], XOR_B));
 }
 
 // z = M_b y for the 8 blocks of quarter j (blocks 8j..8j+7); rot = one kv

@@ -80,14 +80,13 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
       for (int i = 0; i < 32; ++i) x[i] = 0.f;
     }
-    wht128_quad<16, 32>(x, jq);
+    wht128_spread<16, 32>(x, jq);
     float z[32];
     so4_forward_quarter(a.rot + (size_t)g * kRotFloats, jq, x, z);
     float mx = 0.f;
 #pragma unroll
     for (int i = 0; i < 32; ++i) mx = fmaxf(mx, fabsf(z[i]));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = max_xor32(max_xor16(mx));
     int e = 0;
     frexpf(mx, &e);
     const float sc = (mx > 0.f) ? ldexpf(1.0f, 1 - e) : 1.0f;
@@ -180,8 +179,7 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         if (tok_base + 16 * tb + r < kv_end) vmax = fmaxf(vmax, norm_at2(vn[tb], r));
-    vmax = fmaxf(vmax, __shfl_xor(vmax, 16));
-    vmax = fmaxf(vmax, __shfl_xor(vmax, 32));
+    vmax = max_xor32(max_xor16(vmax));
     int e = 0;
     frexpf(vmax, &e);
     const float rho_new = (vmax > 0.f) ? ldexpf(1.0f, 1 - e) : rho;
@@ -200,8 +198,7 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(PrefillArgs a) {
           sv[tb][r] = (tok <= qpos[cb] && tok < kv_end) ? v : -INFINITY;
           mp = fmaxf(mp, sv[tb][r]);
         }
-      mp = fmaxf(mp, __shfl_xor(mp, 16));
-      mp = fmaxf(mp, __shfl_xor(mp, 32));
+      mp = max_xor32(max_xor16(mp));
       const float m_new = fmaxf(m_run[cb], mp);
       // A row whose keys on this page are all masked keeps its state.
       const bool live = m_new != -INFINITY;
@@ -244,8 +241,7 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(PrefillArgs a) {
   const float* rot = a.rot + (size_t)g * kRotFloats;
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
-    float l = l_run[cb] + __shfl_xor(l_run[cb], 16);
-    l += __shfl_xor(l, 32);
+    const float l = sum_xor32(sum_xor16(l_run[cb]));
     const float scale = (l > 0.f) ? a.out_factor / (rho * l) : 0.f;
     float o[32], y[32];
 #pragma unroll
@@ -259,7 +255,7 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(PrefillArgs a) {
         y[4 * bb + c] = r0[c] * o[4 * bb] + r1[c] * o[4 * bb + 1] + r2[c] * o[4 * bb + 2] +
                         r3[c] * o[4 * bb + 3];
     }
-    wht128_quad<16, 32>(y, jq);
+    wht128_spread<16, 32>(y, jq);
     if (qi_of[cb] < a.n_q) {
       f4* dst = reinterpret_cast<f4*>(a.out + ((size_t)qi_of[cb] * a.hq + (size_t)g * a.group + head_of[cb]) * kD + 32 * jq);
       const float nrm = 0.08838834764831845f;  // 1/sqrt(128)

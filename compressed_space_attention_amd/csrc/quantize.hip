@@ -43,11 +43,11 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(
     ss3 = fmaf(x[i + 3], x[i + 3], ss3);
   }
   float ss = (ss0 + ss1) + (ss2 + ss3);
-  ss += __shfl_xor(ss, 1);
-  ss += __shfl_xor(ss, 2);
+  ss += quad_xor1(ss);
+  ss += quad_xor2(ss);
   const float n = sqrtf(ss);
 
-  wht128_quad<1, 2>(x, j);
+  wht128_quad(x, j);
   float z[32];
   so4_forward_quarter(rot + (size_t)head * kRotFloats, j, x, z);
 

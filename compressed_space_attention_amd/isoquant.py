@@ -15,7 +15,8 @@ import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libisoquant.so")
+# ISOQUANT_LIB may name another build of the same library (e.g. a profiling build).
+LIB_PATH = os.environ.get("ISOQUANT_LIB") or os.path.join(_HERE, "libisoquant.so")
 
 HEAD_DIM = 128
 PAGE_TOKENS = 64
