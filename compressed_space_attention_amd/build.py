@@ -24,6 +24,10 @@ FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     # Packed-fp32 instructions stay disabled on this target.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # The leading scalar arguments of the kernels (up to 14 dwords) arrive in
+    # SGPRs at wave launch: no kernel-argument load on the prologue's
+    # critical path.
+    "-mllvm", "-amdgpu-kernarg-preload-count=14",
     "-I", os.path.join(ROOT, "include"),
 ]
 

@@ -44,14 +44,10 @@ struct DecodeArgs {
   const uint16_t* k_norms;
   const uint8_t* v_codes;
   const uint16_t* v_norms;
-  int hkv;
-  const float* rot;
-  const void* q;
+  int num_pages, hkv;
   int q_dtype;
   int hq, group;
-  const int32_t* block_table;
   int max_pages;
-  const int32_t* seq_lens;
   int pages_per_split, splits;
   float score_factor;  // softmax_scale * log2(e) / (128 * alpha)
   float out_factor;    // 1 / (sqrt(128) * alpha)
@@ -95,6 +91,7 @@ __device__ __forceinline__ int tile_block(int t, int col) {
 // in flight while the wave computes a third from registers.
 constexpr int kSlotBytes = 6400;
 constexpr int kMaxPagesPerSplit = 256;  // the planner keeps splits within this
+constexpr int kDefaultPagesPerSplit = 32;  // many-page regime: 8 pages per wave
 #define IQ_MAX_GROUP_BYTES (16 * 128 * 4)  // up to 16 query heads of fp32
 constexpr int kDmaPerPage = 7;
 
@@ -150,16 +147,17 @@ __device__ __forceinline__ float norm_at(const u2& n, int r) {
 }
 
 struct PageState {
-  float m_run, l_run, rho;  // running max (log2 units), partial sum, value-norm frame
-  f4 acc[8];                // O'^T tiles: coordinates 32*(lane/16) + 4m + r, head lane%16
+  float m_run, l_run;  // running max (log2 units) and partial sum
+  int rho_e;           // value-norm frame 2^rho_e
+  f4 acc[8];           // O'^T tiles: coordinates 32*(lane/16) + 4m + r, head lane%16
 };
 
-// Power-of-two frame for the value norms of a page: returns 2^(15 - e) for
-// the largest fp16 norm bits with biased exponent e, so that vn * frame < 2.
-__device__ __forceinline__ float norm_frame(uint32_t max_bits, float current) {
+// Power-of-two frame for the value norms of a page: the exponent 15 - e of
+// 2^(15 - e), e the biased exponent of the largest fp16 norm bits, so that
+// vn * frame < 2.  A page without a nonzero norm keeps the current frame.
+__device__ __forceinline__ int frame_exp(uint32_t max_bits, int current) {
   if (max_bits == 0) return current;
-  const int e16 = (int)((max_bits >> 10) & 0x1Fu);
-  return __builtin_bit_cast(float, (uint32_t)(15 - e16 + 127) << 23);
+  return 15 - (int)((max_bits >> 10) & 0x1Fu);
 }
 
 template <bool PACK8>
@@ -223,15 +221,16 @@ __device__ __forceinline__ void process_page(const PageRegs<PACK8>& cur, PageSta
   vbits = umax_xor32(umax_xor16(vbits));
   const float m_new = fmaxf(st.m_run, mp);        // finite: the page has a valid token
   const float corr = fast_exp2(st.m_run - m_new);  // 0 on the first page
-  const float rho_new = norm_frame(vbits, st.rho);
-  const float rescale = corr * (rho_new / st.rho);
+  const int rho_new = frame_exp(vbits, st.rho_e);
+  const float rescale = __builtin_amdgcn_ldexpf(corr, rho_new - st.rho_e);
+  const float frame = __builtin_amdgcn_ldexpf(1.0f, rho_new);
   if (__any(rescale != 1.0f)) {
 #pragma unroll
     for (int m = 0; m < 8; ++m) st.acc[m] *= rescale;
     st.l_run *= corr;
   }
   st.m_run = m_new;
-  st.rho = rho_new;
+  st.rho_e = rho_new;
 
   uint32_t pw[NT][2];  // P~ as f16 pairs: tokens r = 0,1 and r = 2,3 of each tile
 #pragma unroll
@@ -241,7 +240,7 @@ __device__ __forceinline__ void process_page(const PageRegs<PACK8>& cur, PageSta
     for (int r = 0; r < 4; ++r) {
       p[r] = fast_exp2(sc[t][r] - m_new);  // masked tokens: 2^-inf = 0
       st.l_run += p[r];
-      p[r] *= norm_at(vn[t], r) * rho_new;
+      p[r] *= norm_at(vn[t], r) * frame;
     }
     // round to nearest even (round-toward-zero would bias every weight down)
     typedef _Float16 hh2 __attribute__((ext_vector_type(2)));
@@ -284,25 +283,123 @@ __device__ __forceinline__ void process_page(const PageRegs<PACK8>& cur, PageSta
   }
 }
 
+// Exchange with lane ^ 4 inside rows: two row shifts, each writing the banks
+// (groups of four lanes) that read in its direction.
+__device__ __forceinline__ float lane_xor4(float v) {
+  const float t = dpp_f<0x104, 0x5>(v, v);  // row_shl:4 into banks 0 and 2
+  return dpp_f<0x114, 0xA>(t, v);           // row_shr:4 into banks 1 and 3
+}
+
+// Q' for the heads of one pass: wave w rotates head hb + 2w + lane/32, lane
+// r = lane % 32 holding coordinates 4r..4r+3 (SO(4) block r), and stores the
+// f16 high and low parts in the B-operand layout of the score MFMA (head h,
+// quarter j at lane h + 16j).  The Walsh-Hadamard butterflies at coordinate
+// distance 1 and 2 are in-register, 4..64 are lane exchanges 1..16.
+__device__ __forceinline__ void rotate_queries(int group, int q_dtype, const uint8_t* s_qraw,
+                                               const float* s_rot, uint32_t* s_q, float* s_qinv,
+                                               int hb, int wave, int lane) {
+  const int r = lane & 31;
+  const int h = hb + 2 * wave + (lane >> 5);
+  float x0 = 0.f, x1 = 0.f, x2 = 0.f, x3 = 0.f;
+  if (h < group) {
+    const int idx = h * kD + 4 * r;
+    if (q_dtype == 0) {
+      const f4 v = *reinterpret_cast<const f4*>(s_qraw + 4 * idx);
+      x0 = v[0]; x1 = v[1]; x2 = v[2]; x3 = v[3];
+    } else {
+      const u2 v = *reinterpret_cast<const u2*>(s_qraw + 2 * idx);
+      const uint32_t w0 = v[0], w1 = v[1];
+      if (q_dtype == 1) {
+        x0 = __builtin_bit_cast(float, w0 << 16);
+        x1 = __builtin_bit_cast(float, w0 & 0xFFFF0000u);
+        x2 = __builtin_bit_cast(float, w1 << 16);
+        x3 = __builtin_bit_cast(float, w1 & 0xFFFF0000u);
+      } else {
+        x0 = half_bits_to_float(w0 & 0xFFFFu);
+        x1 = half_bits_to_float(w0 >> 16);
+        x2 = half_bits_to_float(w1 & 0xFFFFu);
+        x3 = half_bits_to_float(w1 >> 16);
+      }
+    }
+  }
+  {
+    const float a0 = x0 + x1, a1 = x0 - x1, a2 = x2 + x3, a3 = x2 - x3;
+    x0 = a0 + a2; x2 = a0 - a2; x1 = a1 + a3; x3 = a1 - a3;
+  }
+  float s;
+  s = (r & 1) ? -1.0f : 1.0f;
+  x0 = fmaf(s, x0, quad_xor1(x0)); x1 = fmaf(s, x1, quad_xor1(x1));
+  x2 = fmaf(s, x2, quad_xor1(x2)); x3 = fmaf(s, x3, quad_xor1(x3));
+  s = (r & 2) ? -1.0f : 1.0f;
+  x0 = fmaf(s, x0, quad_xor2(x0)); x1 = fmaf(s, x1, quad_xor2(x1));
+  x2 = fmaf(s, x2, quad_xor2(x2)); x3 = fmaf(s, x3, quad_xor2(x3));
+  s = (r & 4) ? -1.0f : 1.0f;
+  x0 = fmaf(s, x0, lane_xor4(x0)); x1 = fmaf(s, x1, lane_xor4(x1));
+  x2 = fmaf(s, x2, lane_xor4(x2)); x3 = fmaf(s, x3, lane_xor4(x3));
+  s = (r & 8) ? -1.0f : 1.0f;
+  x0 = fmaf(s, x0, dpp_f<kRowRor8, 0xF>(x0, x0)); x1 = fmaf(s, x1, dpp_f<kRowRor8, 0xF>(x1, x1));
+  x2 = fmaf(s, x2, dpp_f<kRowRor8, 0xF>(x2, x2)); x3 = fmaf(s, x3, dpp_f<kRowRor8, 0xF>(x3, x3));
+  {
+    // swap pair (A, B) = (own, partner) on the lower row, (partner, own) on
+    // the upper one: the butterfly is A + (+-1) B on both
+    s = (r & 16) ? -1.0f : 1.0f;
+    float* xs[4] = {&x0, &x1, &x2, &x3};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const u2 p = pair_xor16(__builtin_bit_cast(uint32_t, *xs[i]));
+      *xs[i] = fmaf(s, __builtin_bit_cast(float, (uint32_t)p[1]), __builtin_bit_cast(float, (uint32_t)p[0]));
+    }
+  }
+  // SO(4) block r
+  const f4* m = reinterpret_cast<const f4*>(s_rot + 16 * r);
+  float z[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f4 row = m[i];
+    z[i] = row[0] * x0 + row[1] * x1 + row[2] * x2 + row[3] * x3;
+  }
+  // per-head power-of-two scale: max |z * sc| in [1, 2)
+  float mx = fmaxf(fmaxf(fabsf(z[0]), fabsf(z[1])), fmaxf(fabsf(z[2]), fabsf(z[3])));
+  mx = fmaxf(mx, quad_xor1(mx));
+  mx = fmaxf(mx, quad_xor2(mx));
+  mx = fmaxf(mx, lane_xor4(mx));
+  mx = fmaxf(mx, dpp_f<kRowRor8, 0xF>(mx, mx));
+  mx = max_xor16(mx);
+  int e = 0;
+  frexpf(mx, &e);
+  const float sc = (mx > 0.f) ? ldexpf(1.0f, 1 - e) : 1.0f;
+  if (h < 16) {
+    const int j = r >> 3, kk = (r & 7) >> 1, d = 2 * (r & 1);
+    const int dst = h + 16 * j;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const float v0 = z[2 * t] * sc, v1 = z[2 * t + 1] * sc;
+      const _Float16 h0 = (_Float16)v0, h1 = (_Float16)v1;
+      const _Float16 l0 = (_Float16)(v0 - (float)h0), l1 = (_Float16)(v1 - (float)h1);
+      s_q[(kk * 8 + d + t) * 64 + dst] =
+          (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+      s_q[(kk * 8 + 4 + d + t) * 64 + dst] =
+          (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+    }
+    if (r == 0) s_qinv[h] = 1.0f / sc;
+  }
+}
+
 template <bool PACK8>
-__global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256, 2) void decode_split_kernel(const int32_t* __restrict__ block_table,
+                                                              const int32_t* __restrict__ seq_lens,
+                                                              const uint8_t* __restrict__ q_bytes,
+                                                              const float* __restrict__ rot_all,
+                                                              int max_pages, int pages_per_split,
+                                                              int hq, int group, int q_dtype,
+                                                              int splits, DecodeArgs a) {
+  // The leading arguments are preloaded into SGPRs (14 dwords): everything
+  // the first loads need.  The rest come from the argument struct.
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
   // wave-uniform: keeps the wave's page bookkeeping in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, jq = lane >> 4;
-  const int pg_begin = split * a.pages_per_split;
-  const int pg_first = pg_begin + wave;
-  // Page ids of the wave's first two pages are fetched together with the length.
-  const int* bt = a.block_table + (size_t)b * a.max_pages;
-  const int page0 = (pg_first < a.max_pages) ? bt[pg_first] : 0;
-  const int page1 = (pg_first + 4 < a.max_pages) ? bt[pg_first + 4] : 0;
-  const int L = a.seq_lens[b];
-  // (a length beyond the block table breaks the contract; never read past it)
-  const int n_pages = min((L + kPage - 1) / kPage, a.max_pages);
-  if (pg_begin >= n_pages) return;  // uniform for the workgroup
-  const int pg_end = min(n_pages, pg_begin + a.pages_per_split);
-  const int n_mine = pg_first < pg_end ? (pg_end - pg_first + 3) / 4 : 0;  // this wave's pages
 
   __shared__ __attribute__((aligned(16))) uint8_t s_ring[4][2][kSlotBytes];  // 51,200 B
   __shared__ __attribute__((aligned(16))) float s_rot[kRotFloats];           // 2,048 B
@@ -312,81 +409,71 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
   __shared__ float s_qinv[16];
   __shared__ float s_m[4][16], s_l[4][16];
 
-  // Everything the prologue needs arrives by direct-to-LDS loads issued before
-  // the pages (lane-predicated): the split's page ids (a quarter per wave), and
-  // in wave 0 the rotation blocks and the group's queries.  No load that the
-  // compiler tracks in registers precedes the page loads, so no implicit wait
-  // ever drains them.
-  const int n_split = pg_end - pg_begin;
-  int n_pre = 0;  // direct-to-LDS loads issued by this wave before its pages
-  if (64 * wave < n_split) {
-    if (64 * wave + lane < n_split) lds_dma4(bt + pg_begin + 64 * wave + lane, &s_pages[64 * wave]);
-    ++n_pre;
-  }
-  const int qbytes = a.group * kD * (a.q_dtype == 0 ? 4 : 2);
-  if (wave == 0) {
-    const uint8_t* rg = reinterpret_cast<const uint8_t*>(a.rot + (size_t)g * kRotFloats) + 16 * lane;
+  // ---- prologue: every load that needs only the arguments goes out first ----
+  // The split's page ids (a quarter per wave) and, in wave 0, the rotation
+  // blocks and the group's queries arrive by direct-to-LDS loads; the length
+  // and the wave's first two page ids are scalar loads.  The first two pages
+  // are requested before the length is known: their block-table entries lie
+  // inside the table and their ids are clamped into the cache, so the loads
+  // stay in bounds even where the table holds no page yet, and a page beyond
+  // the length is never used.
+  const int pg_begin = split * pages_per_split;
+  const int pg_first = pg_begin + wave;
+  const int* bt = block_table + (size_t)b * max_pages;
+  // scalar loads first: after the first direct-to-LDS load the compiler no
+  // longer proves the table unmodified and would use vector loads + full waits
+  const int L = seq_lens[b];
+  const int last_entry = max_pages - 1;
+  const uint32_t last_page = (uint32_t)a.num_pages - 1u;
+  const uint32_t bt0 = (uint32_t)bt[min(pg_first, last_entry)];
+  const uint32_t bt1 = (uint32_t)bt[min(pg_first + 4, last_entry)];
+  const int n_alloc = min(pages_per_split, max_pages - pg_begin);  // readable table entries
+  if (64 * wave < n_alloc && 64 * wave + lane < n_alloc)
+    lds_dma4(bt + pg_begin + 64 * wave + lane, &s_pages[64 * wave]);
+  // Each wave loads the rotation blocks (the same bytes into the same place)
+  // and the rows of the query heads it rotates: 2w, 2w+1 (and 8+2w, 9+2w
+  // for groups above 8).
+  const int esize = q_dtype == 0 ? 4 : 2;
+  const int n_pass = group > 8 ? 2 : 1;
+  {
+    const uint8_t* rg = reinterpret_cast<const uint8_t*>(rot_all + (size_t)g * kRotFloats) + 16 * lane;
     lds_dma16(rg, s_rot);
     lds_dma16(rg + 1024, reinterpret_cast<uint8_t*>(s_rot) + 1024);
-    const uint8_t* qg = reinterpret_cast<const uint8_t*>(a.q) +
-                        ((size_t)b * a.hq + (size_t)g * a.group) * kD * (a.q_dtype == 0 ? 4 : 2);
-    for (int i = 0; 1024 * i < qbytes; ++i) {
-      if (1024 * i + 16 * lane < qbytes) lds_dma16(qg + 1024 * i + 16 * lane, s_qraw + 1024 * i);
-      ++n_pre;
+    const size_t row_bytes = (size_t)kD * esize;
+    const uint8_t* qg = q_bytes + ((size_t)b * hq + (size_t)g * group) * row_bytes;
+    for (int p = 0; p < n_pass; ++p) {
+      const int h0 = 8 * p + 2 * wave;
+      const int nbytes = max(0, min(2, group - h0)) * (int)row_bytes;
+      if (16 * lane < nbytes) lds_dma16(qg + h0 * row_bytes + 16 * lane, s_qraw + h0 * row_bytes);
     }
-    n_pre += 2;
   }
-  (void)n_pre;
-  if (n_mine > 0) issue_page(a, page0, g, lane, s_ring[wave][0]);
-  if (n_mine > 1) issue_page(a, page1, g, lane, s_ring[wave][1]);
-  // The prologue loads have landed once at most the page loads are outstanding.
-  if (n_mine > 1)
-    __builtin_amdgcn_s_waitcnt(wait_vm(2 * kDmaPerPage));
-  else if (n_mine == 1)
-    __builtin_amdgcn_s_waitcnt(wait_vm(kDmaPerPage));
-  else
-    __builtin_amdgcn_s_waitcnt(wait_vm(0));
+  const uint32_t id0 = min(bt0, last_page);
+  const uint32_t id1 = min(bt1, last_page);
+  issue_page(a, (int)id0, g, lane, s_ring[wave][0]);
+  issue_page(a, (int)id1, g, lane, s_ring[wave][1]);
 
-  // Wave 0 rotates the queries with the four quarters of a head on adjacent
-  // lanes (lane = 4h + j), so the cross-lane butterflies are DPP quad moves,
-  // and writes Q' to LDS in the B-operand layout of the score MFMA: lane
-  // h + 16j holds coordinates 32j..32j+31 of head h.
-  if (wave == 0) {
-    const int h = lane >> 2, j = lane & 3;
-    float x[32];
-    if (h < a.group) {
-      lds_to_float32(s_qraw, h * kD + 32 * j, a.q_dtype, x);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 32; ++i) x[i] = 0.f;
+  // (a length beyond the block table breaks the contract; never read past it)
+  const int n_pages = min((L + kPage - 1) / kPage, max_pages);
+  if (pg_begin >= n_pages) {  // uniform for the workgroup
+    // an empty split still leaves its mark: zero weight in the merge
+    if (tid < group) {
+      const size_t row = ((size_t)b * hq + (size_t)g * group + tid) * splits + split;
+      a.ws_ml[2 * row] = -INFINITY;
+      a.ws_ml[2 * row + 1] = 0.f;
     }
-    wht128_quad(x, j);
-    float z[32];
-    so4_forward_quarter(s_rot, j, x, z);
-    float mx = 0.f;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) mx = fmaxf(mx, fabsf(z[i]));
-    mx = fmaxf(mx, quad_xor1(mx));
-    mx = fmaxf(mx, quad_xor2(mx));
-    int e = 0;
-    frexpf(mx, &e);
-    const float sc = (mx > 0.f) ? ldexpf(1.0f, 1 - e) : 1.0f;  // max |z*sc| in [1, 2)
-    const int dst = h + 16 * j;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const float v0 = z[8 * kk + 2 * d] * sc, v1 = z[8 * kk + 2 * d + 1] * sc;
-        const _Float16 h0 = (_Float16)v0, h1 = (_Float16)v1;
-        const _Float16 l0 = (_Float16)(v0 - (float)h0), l1 = (_Float16)(v1 - (float)h1);
-        s_q[(kk * 8 + d) * 64 + dst] =
-            (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-        s_q[(kk * 8 + 4 + d) * 64 + dst] =
-            (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
-      }
-    }
-    if (j == 0) s_qinv[h] = 1.0f / sc;
+    __builtin_amdgcn_s_waitcnt(wait_vm(0));  // no load may still target this LDS
+    return;
   }
+  const int pg_end = min(n_pages, pg_begin + pages_per_split);
+  const int n_mine = pg_first < pg_end ? (pg_end - pg_first + 3) / 4 : 0;  // this wave's pages
+
+  // Everything but the two pages has landed once at most their loads are
+  // outstanding (loads complete in issue order).
+  __builtin_amdgcn_s_waitcnt(wait_vm(2 * kDmaPerPage));
+
+  // All four waves rotate the queries (each its own heads).
+  for (int p = 0; p < n_pass; ++p)
+    rotate_queries(group, q_dtype, s_qraw, s_rot, s_q, s_qinv, 8 * p, wave, lane);
   // LDS writes visible to the workgroup; unlike __syncthreads this does not
   // wait for the page loads still in flight.
   __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
@@ -410,35 +497,45 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
   PageState st;
   st.m_run = -INFINITY;
   st.l_run = 0.f;
-  st.rho = 1.0f;
+  st.rho_e = 0;
 #pragma unroll
   for (int m = 0; m < 8; ++m) st.acc[m] = f4{0.f, 0.f, 0.f, 0.f};
 
-  for (int i = 0; i < n_mine; ++i) {
+  // Page i of the wave: wait for its loads, read it into registers and reuse
+  // its slot for page i + 2.  Page 1 is always in flight behind page 0.
+  auto stage = [&](int i, PageRegs<PACK8>& cur) {
     uint8_t* slot = s_ring[wave][i & 1];
-    const int pg = pg_first + 4 * i;
-    // page i has landed once at most the other slot's loads are outstanding
-    if (i + 1 < n_mine)
+    if (i == 0 || i + 1 < n_mine)
       __builtin_amdgcn_s_waitcnt(wait_vm(kDmaPerPage));
     else
       __builtin_amdgcn_s_waitcnt(wait_vm(0));
-    PageRegs<PACK8> cur;
     read_page<PACK8>(slot, lane, cur);
     if (i + 2 < n_mine) {
+      const uint32_t id = min((uint32_t)s_pages[wave + 4 * (i + 2)], last_page);
       __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // slot read before it is refilled
-      issue_page(a, s_pages[wave + 4 * (i + 2)], g, lane, slot);
+      issue_page(a, (int)__builtin_amdgcn_readfirstlane(id), g, lane, slot);
     }
-    if ((pg + 1) * kPage <= L)
-      process_page<PACK8, false>(cur, st, pg * kPage, L, lane, fac, qhi, qlo);
-    else
-      process_page<PACK8, true>(cur, st, pg * kPage, L, lane, fac, qhi, qlo);
+  };
+  // Only the wave's last page can hold the end of the sequence: the loop runs
+  // unmasked and the last page goes through the masked variant.
+  int i = 0;
+  for (; i + 1 < n_mine; ++i) {
+    PageRegs<PACK8> cur;
+    stage(i, cur);
+    process_page<PACK8, false>(cur, st, (pg_first + 4 * i) * kPage, L, lane, fac, qhi, qlo);
   }
+  if (i < n_mine) {
+    PageRegs<PACK8> cur;
+    stage(i, cur);
+    process_page<PACK8, true>(cur, st, (pg_first + 4 * i) * kPage, L, lane, fac, qhi, qlo);
+  }
+  __builtin_amdgcn_s_waitcnt(wait_vm(0));  // a page requested but not used may still be landing
 
   // ---- merge the four waves ----
   float l_col = st.l_run;
   if (PACK8) l_col += dpp_f<kRowRor8, 0xF>(l_col, l_col);
   l_col = sum_xor32(sum_xor16(l_col));
-  const float fin = a.out_factor / st.rho;
+  const float fin = __builtin_amdgcn_ldexpf(a.out_factor, -st.rho_e);
   // The wave's own two slots hold its accumulator now (all its loads have
   // landed): values 0-15 in slot 0, 16-31 in slot 1.
   static_assert(kSlotBytes >= 16 * 64 * 4, "a slot holds half an accumulator");
@@ -466,8 +563,8 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
       wt[w] = (mw[w] == -INFINITY) ? 0.f : fast_exp2(mw[w] - M);
       Ls += wt[w] * s_l[w][col];
     }
-    if (col < a.group) {
-      const size_t row = ((size_t)b * a.hq + (size_t)g * a.group + col) * a.splits + split;
+    if (col < group) {
+      const size_t row = ((size_t)b * hq + (size_t)g * group + col) * splits + split;
       f4 o0, o1;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -493,111 +590,195 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
   }
 }
 
-// One workgroup per (query head, sequence): merge the split partials with all
-// loads in flight at once, normalise, and rotate back: o = (H / sqrt(d)) B^T o'.
-// Thread t adds coordinates 4*(t%32)..+3 over the splits s = t/32 (mod 8).
-__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
+// One workgroup per (query head, sequence): merge the split partials,
+// normalise, and rotate back: o = (H / sqrt(d)) B^T o'.  Thread t keeps an
+// online merge of coordinates 4*(t%32)..+3 over the splits s = t/32 (mod 8),
+// with all of its loads issued before any result is used; the eight groups
+// then combine through LDS.
+constexpr int kMergeChunk = 16;
+__global__ __launch_bounds__(256, 1) void decode_merge_kernel(const float* __restrict__ rot_all,
+                                                           const float* __restrict__ ws_acc,
+                                                           const float* __restrict__ ws_ml,
+                                                           int splits, int hq_n, int group,
+                                                           float* __restrict__ out_all) {
+  // All arguments arrive preloaded in SGPRs and every load is issued at once.
+  // Each planned split has written its row (an empty one only m = -inf,
+  // l = 0), so no length is needed here; zero-weight rows never touch the sums.
   const int hq = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  const int L = a.seq_lens[b];
-  const int n_pages = (L + kPage - 1) / kPage;
-  // A length above the planned maximum is outside the contract; never read
-  // partials that the split kernel did not plan for.
-  const int ns = min(a.splits, (n_pages + a.pages_per_split - 1) / a.pages_per_split);
-  float* out = a.out + ((size_t)b * a.hq + hq) * kD;
-  if (ns == 0) {
-    if (tid < 32) reinterpret_cast<f4*>(out)[tid] = f4{0.f, 0.f, 0.f, 0.f};
-    return;
-  }
-  __shared__ float s_w[1024];
-  __shared__ float s_red[8];
-  __shared__ f4 s_part[8][32];
-  const size_t row0 = ((size_t)b * a.hq + hq) * a.splits;
-  const float2* ml = reinterpret_cast<const float2*>(a.ws_ml) + row0;
-
-  // maximum over splits
-  float M = -INFINITY;
-  for (int s = tid; s < ns; s += 256) M = fmaxf(M, ml[s].x);
-  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-  if ((tid & 63) == 0) s_red[tid >> 6] = M;
-  __syncthreads();
-  M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
-  // split weights and the normaliser
-  float Ls = 0.f;
-  for (int s = tid; s < ns; s += 256) {
-    const float2 v = ml[s];
-    const float w = fast_exp2(v.x - M);
-    if (s < 1024) s_w[s] = w;
-    Ls += w * v.y;
-  }
-  for (int o = 32; o > 0; o >>= 1) Ls += __shfl_xor(Ls, o);
-  __syncthreads();
-  if ((tid & 63) == 0) s_red[4 + (tid >> 6)] = Ls;
-  __syncthreads();
-  Ls = (s_red[4] + s_red[5]) + (s_red[6] + s_red[7]);
-
   const int quad = tid & 31, grp = tid >> 5;
-  f4 acc = {0.f, 0.f, 0.f, 0.f};
-  const f4* src = reinterpret_cast<const f4*>(a.ws_acc + row0 * kD) + quad;
-#pragma unroll 8
-  for (int s = grp; s < ns; s += 8) {
-    const float w = (s < 1024) ? s_w[s] : fast_exp2(ml[s].x - M);
-    acc += w * src[(size_t)s * (kD / 4)];
+  __shared__ float s_m[8], s_l[8];
+  __shared__ f4 s_part[8][32];
+  const size_t row0 = ((size_t)b * hq_n + hq) * splits;
+  const float2* ml = reinterpret_cast<const float2*>(ws_ml) + row0;
+  const f4* accp = reinterpret_cast<const f4*>(ws_acc + row0 * kD) + quad;
+
+  // this lane's rotation block (wave 0 applies B^T); every thread loads one
+  // so that no branch separates these loads from the others
+  f4 mt[4];
+  {
+    const f4* src = reinterpret_cast<const f4*>(rot_all + (size_t)(hq / group) * kRotFloats +
+                                                 ((tid & 63) >> 1) * 16);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) mt[r] = src[r];
   }
-  s_part[grp][quad] = acc;
+  float m_t = -INFINITY, l_t = 0.f;
+  f4 acc_t = {0.f, 0.f, 0.f, 0.f};
+  // splits s0, s0 + 8, ..., s0 + 8 (kMergeChunk - 1): loads first, then an
+  // online merge into (m_t, l_t, acc_t)
+  auto merge_chunk = [&](int s0) {
+    float2 mv[kMergeChunk];
+    f4 av[kMergeChunk];
+#pragma unroll
+    for (int k = 0; k < kMergeChunk; ++k) {  // rows past the end repeat the last one
+      const int s = min(s0 + 8 * k, splits - 1);
+      mv[k] = ml[s];
+      av[k] = accp[(size_t)s * (kD / 4)];
+    }
+    __builtin_amdgcn_sched_barrier(0);  // every load above issues before any use
+#pragma unroll
+    for (int k = 0; k < kMergeChunk; ++k)
+      if (s0 + 8 * k >= splits) mv[k].x = -INFINITY;  // ... with zero weight
+    float cm = m_t;
+#pragma unroll
+    for (int k = 0; k < kMergeChunk; ++k) cm = fmaxf(cm, mv[k].x);
+    // branch-free (a branch here would sink the loads behind it)
+    const float keep = (m_t == -INFINITY) ? 0.f : fast_exp2(m_t - cm);
+    acc_t *= keep;
+    l_t *= keep;
+#pragma unroll
+    for (int k = 0; k < kMergeChunk; ++k) {
+      // an empty row's accumulator is selected away, never multiplied
+      const bool live = mv[k].x > -INFINITY;
+      const float w = live ? fast_exp2(mv[k].x - cm) : 0.f;
+      const f4 c = w * av[k];
+      acc_t[0] += live ? c[0] : 0.f;
+      acc_t[1] += live ? c[1] : 0.f;
+      acc_t[2] += live ? c[2] : 0.f;
+      acc_t[3] += live ? c[3] : 0.f;
+      l_t += w * mv[k].y;
+    }
+    m_t = cm;
+  };
+  merge_chunk(grp);  // no loop before the first chunk: its loads follow the ones above
+  for (int s0 = grp + 8 * kMergeChunk; s0 < splits; s0 += 8 * kMergeChunk) merge_chunk(s0);
+  s_part[grp][quad] = acc_t;
+  if (quad == 0) {
+    s_m[grp] = m_t;
+    s_l[grp] = l_t;
+  }
   __syncthreads();
   if (tid >= 64) return;
   // lane l owns coordinates 2l, 2l+1
   const int lane = tid;
-  float o0 = 0.f, o1 = 0.f;
+  float M = -INFINITY;
 #pragma unroll
-  for (int gq = 0; gq < 8; ++gq) {
-    const f4 v = s_part[gq][lane >> 1];
-    o0 += (lane & 1) ? v[2] : v[0];
-    o1 += (lane & 1) ? v[3] : v[1];
+  for (int gq = 0; gq < 8; ++gq) M = fmaxf(M, s_m[gq]);
+  float o0 = 0.f, o1 = 0.f, Ls = 0.f;
+  if (M > -INFINITY) {
+#pragma unroll
+    for (int gq = 0; gq < 8; ++gq) {
+      const float w = (s_m[gq] == -INFINITY) ? 0.f : fast_exp2(s_m[gq] - M);
+      const f4 v = s_part[gq][lane >> 1];
+      o0 += w * ((lane & 1) ? v[2] : v[0]);
+      o1 += w * ((lane & 1) ? v[3] : v[1]);
+      Ls += w * s_l[gq];
+    }
   }
-  const float inv = 1.0f / Ls;
+  const float inv = (Ls > 0.f) ? 1.0f / Ls : 0.f;  // an empty sequence gives zeros
   o0 *= inv;
   o1 *= inv;
   // B^T on block lane/2: this lane holds block coordinates c0 = 2*(lane&1), c0+1.
-  const float* mt = a.rot + (size_t)(hq / a.group) * kRotFloats + (lane >> 1) * 16;
-  const float n0 = __shfl_xor(o0, 1), n1 = __shfl_xor(o1, 1);
+  const float n0 = quad_xor1(o0), n1 = quad_xor1(o1);
   const bool odd = lane & 1;
   const float v0 = odd ? n0 : o0, v1 = odd ? n1 : o1, v2 = odd ? o0 : n0, v3 = odd ? o1 : n1;
   const int c0 = odd ? 2 : 0;
-  float y0 = mt[c0] * v0 + mt[4 + c0] * v1 + mt[8 + c0] * v2 + mt[12 + c0] * v3;
-  float y1 = mt[c0 + 1] * v0 + mt[5 + c0] * v1 + mt[9 + c0] * v2 + mt[13 + c0] * v3;
-  // Walsh-Hadamard: coordinate distance 1 in-lane, 2..64 across lanes.
+  float y0 = mt[0][c0] * v0 + mt[1][c0] * v1 + mt[2][c0] * v2 + mt[3][c0] * v3;
+  float y1 = mt[0][c0 + 1] * v0 + mt[1][c0 + 1] * v1 + mt[2][c0 + 1] * v2 + mt[3][c0 + 1] * v3;
+  // Walsh-Hadamard: coordinate distance 1 in-lane, 2..64 across lanes (lane
+  // distance 1..32): a butterfly keeps y + partner on the lower lane and
+  // partner - y on the upper one.
   {
     const float t0 = y0 + y1, t1 = y0 - y1;
     y0 = t0;
     y1 = t1;
   }
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) {
-    const float p0 = __shfl_xor(y0, m), p1 = __shfl_xor(y1, m);
-    const float sgn = (lane & m) ? -1.0f : 1.0f;
-    y0 = fmaf(sgn, y0, p0);
-    y1 = fmaf(sgn, y1, p1);
+  {
+    const float s = (lane & 1) ? -1.0f : 1.0f;
+    y0 = fmaf(s, y0, quad_xor1(y0));
+    y1 = fmaf(s, y1, quad_xor1(y1));
+  }
+  {
+    const float s = (lane & 2) ? -1.0f : 1.0f;
+    y0 = fmaf(s, y0, quad_xor2(y0));
+    y1 = fmaf(s, y1, quad_xor2(y1));
+  }
+  {
+    const float s = (lane & 4) ? -1.0f : 1.0f;
+    y0 = fmaf(s, y0, lane_xor4(y0));
+    y1 = fmaf(s, y1, lane_xor4(y1));
+  }
+  {
+    const float s = (lane & 8) ? -1.0f : 1.0f;
+    y0 = fmaf(s, y0, dpp_f<kRowRor8, 0xF>(y0, y0));
+    y1 = fmaf(s, y1, dpp_f<kRowRor8, 0xF>(y1, y1));
+  }
+  {
+    // the swap pair (A, B): (own, partner) on the lower lanes, (partner, own)
+    // on the upper ones, so both results are A + (+-1) B
+    const float s = (lane & 16) ? -1.0f : 1.0f;
+    const u2 p0 = pair_xor16(__builtin_bit_cast(uint32_t, y0));
+    const u2 p1 = pair_xor16(__builtin_bit_cast(uint32_t, y1));
+    y0 = fmaf(s, __builtin_bit_cast(float, (uint32_t)p0[1]), __builtin_bit_cast(float, (uint32_t)p0[0]));
+    y1 = fmaf(s, __builtin_bit_cast(float, (uint32_t)p1[1]), __builtin_bit_cast(float, (uint32_t)p1[0]));
+  }
+  {
+    const float s = (lane & 32) ? -1.0f : 1.0f;
+    const u2 p0 = pair_xor32(__builtin_bit_cast(uint32_t, y0));
+    const u2 p1 = pair_xor32(__builtin_bit_cast(uint32_t, y1));
+    y0 = fmaf(s, __builtin_bit_cast(float, (uint32_t)p0[1]), __builtin_bit_cast(float, (uint32_t)p0[0]));
+    y1 = fmaf(s, __builtin_bit_cast(float, (uint32_t)p1[1]), __builtin_bit_cast(float, (uint32_t)p1[0]));
   }
   const float nrm = 0.08838834764831845f;  // 1/sqrt(128)
+  float* out = out_all + ((size_t)b * hq_n + hq) * kD;
   *reinterpret_cast<float2*>(out + 2 * lane) = make_float2(y0 * nrm, y1 * nrm);
 }
 
+// Split planning.  Few pages per kv head (short or single sequences): one
+// wave of workgroups (two per CU, the LDS limit) so the whole call is a
+// single pass with the shortest critical path.  Many pages: more, shorter
+// splits than the CUs can hold at once, so that workgroups that finish early
+// (the second workgroup on a CU runs behind the first, and ragged batches
+// give splits of unequal length) are replaced by the hardware dispatcher.
 DecodePlan plan_decode(int batch, int hkv, int max_seq_len, int num_cus) {
   const int max_pages = max(1, (max_seq_len + kPage - 1) / kPage);
   const long long units = (long long)max(1, batch) * max(1, hkv);
-  long long target = 2LL * max(1, num_cus);
-  if (const char* env = getenv("IQ_DECODE_TARGET_WGS")) {
+  // One workgroup per CU (two pages per wave at 32K context) beats two (one
+  // page per wave): half the query rotations and split partials, and each
+  // wave's second page loads while it computes the first.
+  long long per_cu = 1;
+  if (const char* env = getenv("IQ_DECODE_WGS_PER_CU")) {
     const long long v = atoll(env);
-    if (v > 0) target = v;
+    if (v > 0) per_cu = v;
   }
-  long long splits = (target + units - 1) / units;
-  splits = splits < 1 ? 1 : (splits > max_pages ? max_pages : splits);
-  int pps = (int)((max_pages + splits - 1) / splits);
+  const long long slots = per_cu * max(1, num_cus);
+  long long pps;
+  if (units * max_pages <= slots * 4 * 2) {
+    // latency regime: at most two pages per wave
+    long long splits = (slots + units - 1) / units;
+    if (splits > max_pages) splits = max_pages;
+    pps = (max_pages + splits - 1) / splits;
+  } else {
+    pps = kDefaultPagesPerSplit;
+  }
+  if (const char* env = getenv("IQ_DECODE_PAGES_PER_SPLIT")) {
+    const long long v = atoll(env);
+    if (v > 0) pps = v;
+  }
   if (pps > kMaxPagesPerSplit) pps = kMaxPagesPerSplit;
+  if (pps < 1) pps = 1;
   DecodePlan p;
-  p.pages_per_split = pps;
-  p.splits = (max_pages + pps - 1) / pps;
+  p.pages_per_split = (int)pps;
+  p.splits = (int)((max_pages + pps - 1) / pps);
   return p;
 }
 
@@ -615,15 +796,12 @@ hipError_t launch_decode(const CacheView& c, const float* rot, const void* q, in
   a.k_norms = c.k_norms;
   a.v_codes = c.v_codes;
   a.v_norms = c.v_norms;
+  a.num_pages = c.num_pages;
   a.hkv = c.hkv;
-  a.rot = rot;
-  a.q = q;
   a.q_dtype = q_dtype;
   a.hq = hq;
   a.group = hq / c.hkv;
-  a.block_table = block_table;
   a.max_pages = max_pages;
-  a.seq_lens = seq_lens;
   a.pages_per_split = plan.pages_per_split;
   a.splits = plan.splits;
   const double log2e = 1.4426950408889634;
@@ -633,13 +811,20 @@ hipError_t launch_decode(const CacheView& c, const float* rot, const void* q, in
   a.ws_acc = reinterpret_cast<float*>(workspace);
   a.ws_ml = a.ws_acc + rows * kD;
   a.out = out;
+  const uint8_t* qb = static_cast<const uint8_t*>(q);
+  const dim3 grid(plan.splits, c.hkv, batch);
   if (a.group <= 8)
-    hipLaunchKernelGGL(decode_split_kernel<true>, dim3(plan.splits, c.hkv, batch), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(decode_split_kernel<true>, grid, dim3(256), 0, stream, block_table, seq_lens,
+                       qb, rot, a.max_pages, a.pages_per_split, a.hq, a.group, a.q_dtype,
+                       a.splits, a);
   else
-    hipLaunchKernelGGL(decode_split_kernel<false>, dim3(plan.splits, c.hkv, batch), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(decode_split_kernel<false>, grid, dim3(256), 0, stream, block_table, seq_lens,
+                       qb, rot, a.max_pages, a.pages_per_split, a.hq, a.group, a.q_dtype,
+                       a.splits, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_merge_kernel, dim3(hq, batch), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(decode_merge_kernel, dim3(hq, batch), dim3(256), 0, stream, rot, a.ws_acc,
+                     a.ws_ml, a.splits, a.hq, a.group, a.out);
   return hipGetLastError();
 }
 

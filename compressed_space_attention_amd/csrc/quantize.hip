@@ -17,10 +17,17 @@
 
 namespace iq {
 
+// Appends of at most this many vectors (K and V together) take the
+// latency-oriented kernel.
+constexpr long long kSmallAppendVectors = 16384;
+
+// The first 14 argument dwords (everything the first loads need) are
+// preloaded into SGPRs; the cache pointers follow from the argument segment.
+template <int DT>
 __global__ __launch_bounds__(256) void quantize_append_kernel(
-    const void* __restrict__ k, const void* __restrict__ v, int dtype, long long n_vec,
-    int hkv, const int32_t* __restrict__ seq_idx, const int32_t* __restrict__ pos,
-    const int32_t* __restrict__ block_table, int max_pages, const float* __restrict__ rot,
+    const void* __restrict__ k, const void* __restrict__ v, const int32_t* __restrict__ seq_idx,
+    const int32_t* __restrict__ pos, const int32_t* __restrict__ block_table, long long n_vec,
+    int hkv, int max_pages, const float* __restrict__ rot, int num_pages,
     uint8_t* __restrict__ k_codes, uint16_t* __restrict__ k_norms, uint8_t* __restrict__ v_codes,
     uint16_t* __restrict__ v_norms) {
   const long long gv = (long long)blockIdx.x * 64 + (threadIdx.x >> 2);
@@ -31,8 +38,15 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(
   const int tok = (int)(vi / hkv);
   const int head = (int)(vi - (long long)tok * hkv);
 
+  // The destination is looked up while the vector is transformed: position
+  // and sequence first, then the page id, all before the arithmetic.
+  const int p = pos[tok];
+  const int si = seq_idx[tok];
   float x[32];
-  load32(which ? v : k, (size_t)vi * kD + 32 * j, dtype, x);
+  load32(which ? v : k, (size_t)vi * kD + 32 * j, DT, x);
+  // a position outside the table or a page id outside the cache is skipped
+  const bool in_table = (unsigned)p < (unsigned)max_pages * kPage;
+  const int page = in_table ? block_table[(size_t)si * max_pages + (p >> 6)] : -1;
 
   float ss0 = 0.f, ss1 = 0.f, ss2 = 0.f, ss3 = 0.f;
 #pragma unroll
@@ -66,8 +80,7 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(
   u3 w;
   selectors_to_group(sel, w.x, w.y, w.z);
 
-  const int p = pos[tok];
-  const int page = block_table[(size_t)seq_idx[tok] * max_pages + (p >> 6)];
+  if ((unsigned)page >= (unsigned)num_pages) return;
   const int slot = p & 63;
   const size_t rec = ((size_t)page * hkv + head) * kPage + slot;
   if (!which) {
@@ -90,15 +103,201 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(
   if (j == 0) v_norms[rec] = float_to_half_sat(n);
 }
 
+// Few vectors (a decode step appends one token per sequence): the latency
+// of one vector is what counts.  Here 32 lanes share a vector, lane r holding
+// coordinates 4r..4r+3 and SO(4) block r, so the transform is a handful of
+// register and lane-exchange steps per lane; lane r's four codes are selector
+// r % 8 of group r / 8, and the eight lanes of a group OR their bit fields
+// into the group's three dwords.  Loads of the position, the rotation block
+// and the vector go out together, the page id as soon as the position lands.
+__device__ __forceinline__ uint32_t or_xor1(uint32_t v) {
+  return v | (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true);
+}
+__device__ __forceinline__ uint32_t or_xor2(uint32_t v) {
+  return v | (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true);
+}
+__device__ __forceinline__ uint32_t or_xor4(uint32_t v) {
+  const uint32_t t = (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x104, 0xF, 0x5, false);
+  return v | (uint32_t)__builtin_amdgcn_update_dpp((int)t, (int)v, 0x114, 0xF, 0xA, false);
+}
+__device__ __forceinline__ float add_xor4(float v) {
+  const int iv = __builtin_bit_cast(int, v);
+  const int t = __builtin_amdgcn_update_dpp(iv, iv, 0x104, 0xF, 0x5, false);
+  return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(t, iv, 0x114, 0xF, 0xA, false));
+}
+__device__ __forceinline__ float lane_xor4_f(float v) {
+  const int iv = __builtin_bit_cast(int, v);
+  const int t = __builtin_amdgcn_update_dpp(iv, iv, 0x104, 0xF, 0x5, false);
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(t, iv, 0x114, 0xF, 0xA, false));
+}
+__device__ __forceinline__ float lane_xor8_f(float v) {
+  const int iv = __builtin_bit_cast(int, v);
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(iv, iv, 0x128, 0xF, 0xF, false));
+}
+
+template <int DT>
+__global__ __launch_bounds__(256) void quantize_small_kernel(
+    const void* __restrict__ k, const void* __restrict__ v, const int32_t* __restrict__ seq_idx,
+    const int32_t* __restrict__ pos, const int32_t* __restrict__ block_table,
+    const float* __restrict__ rot, int n_vec, int hkv, int max_pages, int num_pages,
+    uint8_t* __restrict__ k_codes, uint16_t* __restrict__ k_norms, uint8_t* __restrict__ v_codes,
+    uint16_t* __restrict__ v_norms) {
+  const int gv = blockIdx.x * 8 + (threadIdx.x >> 5);  // K vectors first, then V
+  const int r = threadIdx.x & 31;
+  if (gv >= 2 * n_vec) return;  // whole half-waves leave together
+  const int which = gv >= n_vec;
+  const int vi = gv - (which ? n_vec : 0);  // token * hkv + head
+  const int tok = vi / hkv;
+  const int head = vi - tok * hkv;
+
+  const int p = pos[tok];
+  const int si = seq_idx[tok];
+  const f4* mrow = reinterpret_cast<const f4*>(rot + (size_t)head * kRotFloats + 16 * r);
+  const f4 m0 = mrow[0], m1 = mrow[1], m2 = mrow[2], m3 = mrow[3];
+  float x0, x1, x2, x3;
+  {
+    const size_t idx = (size_t)vi * kD + 4 * r;
+    if (DT == 0) {
+      const f4 a = *reinterpret_cast<const f4*>(reinterpret_cast<const float*>(which ? v : k) + idx);
+      x0 = a[0]; x1 = a[1]; x2 = a[2]; x3 = a[3];
+    } else {
+      const u2 a = *reinterpret_cast<const u2*>(reinterpret_cast<const uint16_t*>(which ? v : k) + idx);
+      const uint32_t w0 = a[0], w1 = a[1];
+      if (DT == 1) {
+        x0 = __builtin_bit_cast(float, w0 << 16);
+        x1 = __builtin_bit_cast(float, w0 & 0xFFFF0000u);
+        x2 = __builtin_bit_cast(float, w1 << 16);
+        x3 = __builtin_bit_cast(float, w1 & 0xFFFF0000u);
+      } else {
+        x0 = half_bits_to_float(w0 & 0xFFFFu);
+        x1 = half_bits_to_float(w0 >> 16);
+        x2 = half_bits_to_float(w1 & 0xFFFFu);
+        x3 = half_bits_to_float(w1 >> 16);
+      }
+    }
+  }
+  // a position outside the table or a page id outside the cache is skipped
+  const bool in_table = (unsigned)p < (unsigned)max_pages * kPage;
+  const int page = in_table ? block_table[(size_t)si * max_pages + (p >> 6)] : -1;
+
+  // norm: sum of squares over the 32 lanes of the vector
+  float ss = fmaf(x3, x3, fmaf(x2, x2, fmaf(x1, x1, x0 * x0)));
+  ss += quad_xor1(ss);
+  ss += quad_xor2(ss);
+  ss = add_xor4(ss);
+  ss += lane_xor8_f(ss);
+  ss = sum_xor16(ss);
+  const float n = sqrtf(ss);
+
+  // Walsh-Hadamard (unnormalised, Sylvester order): distances 1, 2 in
+  // registers, 4..64 across lanes 1..16 (lower lane keeps y + partner)
+  {
+    const float a0 = x0 + x1, a1 = x0 - x1, a2 = x2 + x3, a3 = x2 - x3;
+    x0 = a0 + a2; x2 = a0 - a2; x1 = a1 + a3; x3 = a1 - a3;
+  }
+  float sg = (r & 1) ? -1.0f : 1.0f;
+  x0 = fmaf(sg, x0, quad_xor1(x0)); x1 = fmaf(sg, x1, quad_xor1(x1));
+  x2 = fmaf(sg, x2, quad_xor1(x2)); x3 = fmaf(sg, x3, quad_xor1(x3));
+  sg = (r & 2) ? -1.0f : 1.0f;
+  x0 = fmaf(sg, x0, quad_xor2(x0)); x1 = fmaf(sg, x1, quad_xor2(x1));
+  x2 = fmaf(sg, x2, quad_xor2(x2)); x3 = fmaf(sg, x3, quad_xor2(x3));
+  sg = (r & 4) ? -1.0f : 1.0f;
+  x0 = fmaf(sg, x0, lane_xor4_f(x0)); x1 = fmaf(sg, x1, lane_xor4_f(x1));
+  x2 = fmaf(sg, x2, lane_xor4_f(x2)); x3 = fmaf(sg, x3, lane_xor4_f(x3));
+  sg = (r & 8) ? -1.0f : 1.0f;
+  x0 = fmaf(sg, x0, lane_xor8_f(x0)); x1 = fmaf(sg, x1, lane_xor8_f(x1));
+  x2 = fmaf(sg, x2, lane_xor8_f(x2)); x3 = fmaf(sg, x3, lane_xor8_f(x3));
+  {
+    // swap pair (A, B) = (own, partner) on the lower row, (partner, own) on
+    // the upper one: the butterfly is A + (+-1) B on both
+    sg = (r & 16) ? -1.0f : 1.0f;
+    u2 q;
+    q = pair_xor16(__builtin_bit_cast(uint32_t, x0));
+    x0 = fmaf(sg, __builtin_bit_cast(float, (uint32_t)q[1]), __builtin_bit_cast(float, (uint32_t)q[0]));
+    q = pair_xor16(__builtin_bit_cast(uint32_t, x1));
+    x1 = fmaf(sg, __builtin_bit_cast(float, (uint32_t)q[1]), __builtin_bit_cast(float, (uint32_t)q[0]));
+    q = pair_xor16(__builtin_bit_cast(uint32_t, x2));
+    x2 = fmaf(sg, __builtin_bit_cast(float, (uint32_t)q[1]), __builtin_bit_cast(float, (uint32_t)q[0]));
+    q = pair_xor16(__builtin_bit_cast(uint32_t, x3));
+    x3 = fmaf(sg, __builtin_bit_cast(float, (uint32_t)q[1]), __builtin_bit_cast(float, (uint32_t)q[0]));
+  }
+  // SO(4) block r, then the scalar quantiser on u = z / n
+  const float z0 = m0[0] * x0 + m0[1] * x1 + m0[2] * x2 + m0[3] * x3;
+  const float z1 = m1[0] * x0 + m1[1] * x1 + m1[2] * x2 + m1[3] * x3;
+  const float z2 = m2[0] * x0 + m2[1] * x1 + m2[2] * x2 + m2[3] * x3;
+  const float z3 = m3[0] * x0 + m3[1] * x1 + m3[2] * x2 + m3[3] * x3;
+  uint32_t sel = 0x04040404u;  // zero vector: level +0.2451 * 0
+  if (n > 0.f) {
+    const float inv_n = 1.0f / n;
+    sel = code_of(z0 * inv_n) | (code_of(z1 * inv_n) << 8) | (code_of(z2 * inv_n) << 16) |
+          (code_of(z3 * inv_n) << 24);
+  }
+  // selector s of group g: its bit fields in the group's three dwords
+  const int s = r & 7, g = r >> 3;
+  uint32_t w0 = 0, w1 = 0, w2 = 0;
+  switch (s) {
+    case 0: w0 = sel; break;
+    case 1: w0 = sel << 3; break;
+    case 2: w0 = (sel & 0x03030303u) << 6; w1 = (sel >> 2) & 0x01010101u; break;
+    case 3: w1 = sel << 1; break;
+    case 4: w1 = sel << 4; break;
+    case 5: w1 = (sel & 0x01010101u) << 7; w2 = (sel >> 1) & 0x03030303u; break;
+    case 6: w2 = sel << 2; break;
+    default: w2 = sel << 5; break;
+  }
+  w0 = or_xor4(or_xor2(or_xor1(w0)));
+  w1 = or_xor4(or_xor2(or_xor1(w1)));
+  w2 = or_xor4(or_xor2(or_xor1(w2)));
+
+  if ((unsigned)page >= (unsigned)num_pages) return;
+  const int slot = p & 63;
+  const size_t rec = ((size_t)page * hkv + head) * kPage + slot;
+  if (!which) {
+    if (s == 0) *reinterpret_cast<u3*>(k_codes + rec * kRec + 12 * g) = u3{w0, w1, w2};
+    if (r == 0) k_norms[rec] = float_to_half_sat(n);
+    return;
+  }
+  // V: byte lane b of group g goes to region 4g + b (quad q of the slot),
+  // chunk c = slot / 16, byte lane slot % 4 -- lane 8g + b stores it
+  if (s < 4) {
+    uint8_t* blk = v_codes + ((size_t)page * hkv + head) * (kPage * kRec);
+    const int c = slot >> 4, q = (slot >> 2) & 3, rr = slot & 3;
+    uint8_t* dst = blk + (4 * g + s + 16 * q) * kRec + 12 * c + rr;
+    dst[0] = (uint8_t)(w0 >> (8 * s));
+    dst[4] = (uint8_t)(w1 >> (8 * s));
+    dst[8] = (uint8_t)(w2 >> (8 * s));
+  }
+  if (r == 0) v_norms[rec] = float_to_half_sat(n);
+}
+
 hipError_t launch_quantize_append(const CacheView& c, const float* rot, const void* k, const void* v,
                                   int dtype, int n_tokens, const int32_t* seq_idx,
                                   const int32_t* pos, const int32_t* block_table, int max_pages,
                                   hipStream_t stream) {
   const long long n_vec = (long long)n_tokens * c.hkv;
+  if (2 * n_vec <= kSmallAppendVectors) {
+    const unsigned blocks = (unsigned)((2 * n_vec + 7) / 8);
+#define IQ_SMALL(DT)                                                                          \
+  hipLaunchKernelGGL(quantize_small_kernel<DT>, dim3(blocks), dim3(256), 0, stream, k, v,     \
+                     seq_idx, pos, block_table, rot, (int)n_vec, c.hkv, max_pages,            \
+                     c.num_pages, c.k_codes,                                                  \
+                     c.k_norms, c.v_codes, c.v_norms)
+    if (dtype == 0) IQ_SMALL(0);
+    else if (dtype == 1) IQ_SMALL(1);
+    else IQ_SMALL(2);
+#undef IQ_SMALL
+    return hipGetLastError();
+  }
   const long long blocks = (2 * n_vec + 63) / 64;
-  hipLaunchKernelGGL(quantize_append_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, k, v,
-                     dtype, n_vec, c.hkv, seq_idx, pos, block_table, max_pages, rot, c.k_codes,
-                     c.k_norms, c.v_codes, c.v_norms);
+#define IQ_QUADS(DT)                                                                             \
+  hipLaunchKernelGGL(quantize_append_kernel<DT>, dim3((unsigned)blocks), dim3(256), 0, stream, k, \
+                     v, seq_idx, pos, block_table, n_vec, c.hkv, max_pages, rot, c.num_pages,     \
+                     c.k_codes,                                                                   \
+                     c.k_norms, c.v_codes, c.v_norms)
+  if (dtype == 0) IQ_QUADS(0);
+  else if (dtype == 1) IQ_QUADS(1);
+  else IQ_QUADS(2);
+#undef IQ_QUADS
   return hipGetLastError();
 }
 

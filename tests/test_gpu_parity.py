@@ -37,10 +37,17 @@ def test_rotation_matrices_match_oracle():
     assert np.max(np.abs(mats - want)) < 1e-6
 
 
+# Up to 16384 vectors (K and V together) an append takes the 32-lanes-per-vector
+# kernel, above it the 4-lanes-per-vector one: both are covered.
+SMALL_LENS = [1, 100, 700, 64]     # 865 tokens x 4 heads x 2 = 6920 vectors
+LARGE_LENS = [2100, 77, 64]        # 2241 tokens x 4 heads x 2 = 17928 vectors
+
+
+@pytest.mark.parametrize("lens", [SMALL_LENS, LARGE_LENS], ids=["lanes32", "quads"])
 @pytest.mark.parametrize("dtype,outliers", [("f32", False), ("bf16", True), ("f16", False)])
-def test_quantize_append_codes_and_norms(dtype, outliers):
-    _say(f"quantize parity dtype={dtype} outliers={outliers}")
-    s = Scenario(21, [1, 100, 700, 64], hkv=4, dtype=dtype, outliers=outliers)
+def test_quantize_append_codes_and_norms(dtype, outliers, lens):
+    _say(f"quantize parity dtype={dtype} outliers={outliers} tokens={sum(lens)}")
+    s = Scenario(21, lens, hkv=4, dtype=dtype, outliers=outliers)
     ref, info = s.oracle_cache()
     st = code_parity(s.host_cache(), ref, info, s)
     _say(st)
@@ -70,6 +77,27 @@ def test_quantize_special_vectors():
     want[37] = 7
     assert np.array_equal(codes[2], want)
     assert g.k_norms[s.block_table[0, 0], 0, 3] == 0x7BFF
+
+
+@pytest.mark.parametrize("n_tok", [3, 5000], ids=["lanes32", "quads"])
+def test_quantize_skips_positions_outside_the_table(n_tok):
+    """A position past the block table, or a table entry that is no page of the
+    cache, writes nothing (and reads nothing out of bounds)."""
+    from compressed_space_attention_amd import isoquant as iq
+    s = Scenario(41, [64], hkv=2, dtype="f32")
+    before = [t.clone() for t in (s.cache.k_codes, s.cache.v_codes, s.cache.k_norms, s.cache.v_norms)]
+    k = torch.from_numpy(synth.normal(42, (n_tok, 2, 128))).float().cuda()
+    max_pages = s.bt_dev.shape[1]
+    pos = torch.full((n_tok,), max_pages * 64 + 5, dtype=torch.int32, device="cuda")
+    seq = torch.zeros(n_tok, dtype=torch.int32, device="cuda")
+    iq.quantize_append(s.cache, s.rot, k, k, seq, pos, s.bt_dev)
+    bad_bt = torch.full_like(s.bt_dev, s.num_pages + 7)
+    pos2 = torch.zeros(n_tok, dtype=torch.int32, device="cuda")
+    iq.quantize_append(s.cache, s.rot, k, k, seq, pos2, bad_bt)
+    torch.cuda.synchronize()
+    after = (s.cache.k_codes, s.cache.v_codes, s.cache.k_norms, s.cache.v_norms)
+    for a, b in zip(before, after):
+        assert torch.equal(a, b)
 
 
 DECODE_CASES = [
