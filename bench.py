@@ -47,6 +47,11 @@ def parse():
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly (profiling runs)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (20 times): the known-size "
+                         "reference that scales the HBM byte counters")
+    ap.add_argument("--no-aux", action="store_true",
+                    help="skip the chunked-prefill side measurements (append, prefill)")
     return ap.parse_args()
 
 
@@ -224,6 +229,66 @@ def run_decode(args):
     return result
 
 
+def run_prefill_aux(iters=30):
+    """The chunked-prefill workload (8192-token quantise-append into a 32,768-token
+    cache, then causal attention of the last 512 positions x 64 query heads):
+    append tokens/s and prefill TFLOP/s against the f16 matrix-core peak."""
+    import torch
+
+    from compressed_space_attention_amd import isoquant as iq
+    from compressed_space_attention_amd import synth, workloads
+
+    p = workloads.CHUNKED_PREFILL
+    dev = "cuda"
+    pages = -(-p.total // 64)
+    bt_np, num_pages = synth.block_table(p.seed + 9, [pages], shuffle=True)
+    bt = torch.from_numpy(bt_np).to(dev)
+    rot = iq.rotation_init(synth.quaternions(p.seed, p.n_kv_heads), device=dev)
+    cache = iq.PagedCache(num_pages, p.n_kv_heads, device=dev, zero=True)
+    k = synth.draw_normal_device(p.seed + 2, (p.total, p.n_kv_heads, 128), torch.bfloat16, dev)
+    v = synth.draw_normal_device(p.seed + 3, (p.total, p.n_kv_heads, 128), torch.bfloat16, dev)
+    pos = torch.arange(p.total, dtype=torch.int32, device=dev)
+    seq = torch.zeros(p.total, dtype=torch.int32, device=dev)
+    iq.quantize_append(cache, rot, k[:p.cached], v[:p.cached], seq[:p.cached], pos[:p.cached], bt)
+    k2, v2 = k[p.cached:].contiguous(), v[p.cached:].contiguous()
+    s2, p2 = seq[p.cached:].contiguous(), pos[p.cached:].contiguous()
+    q = synth.draw_normal_device(p.seed + 10, (p.n_queries, p.n_q_heads, 128), torch.bfloat16, dev)
+    out = torch.empty((p.n_queries, p.n_q_heads, 128), dtype=torch.float32, device=dev)
+    ws_n = iq.prefill_workspace_bytes(p.n_queries, p.n_q_heads, p.n_kv_heads, p.q_start)
+    ws = torch.empty(max(16, ws_n), dtype=torch.uint8, device=dev)
+
+    def timeit(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(iters):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / 1e3 / iters
+
+    t_app = timeit(lambda: iq.quantize_append(cache, rot, k2, v2, s2, p2, bt))
+    t_pre = timeit(lambda: iq.prefill_attention(cache, rot, q, p.q_start, bt[0], out=out,
+                                                 workspace=ws))
+    # algorithmic flops: 2 d for q.k and 2 d for p.v per (query head, key) pair
+    keys = sum(p.q_start + i + 1 for i in range(p.n_queries))
+    flops = 4.0 * 128 * p.n_q_heads * keys
+    moved = p.appended * p.n_kv_heads * 2 * (128 * 2 + 50)  # bf16 in, packed record out
+    tf = flops / t_pre / 1e12
+    return {
+        "workload": p.name,
+        "append_us": round(t_app * 1e6, 2),
+        "append_tokens_per_s": round(p.appended / t_app, 1),
+        "append_gbs": round(moved / t_app / 1e9, 1),
+        "prefill_us": round(t_pre * 1e6, 2),
+        "prefill_tflops": round(tf, 2),
+        "prefill_frac_of_f16_peak": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
+        "prefill_mfma_tflops_issued": round(1.5 * tf, 2),  # q.k runs as two f16 products
+    }
+
+
 def cpu_baseline_decode(args, w, layer, bt_np, lens):
     """The CPU oracle, as it stands, on a bounded sample of the same step:
     quantise-append the current token, then decode over the layer's cache."""
@@ -263,8 +328,24 @@ def cpu_baseline_decode(args, w, layer, bt_np, lens):
     }
 
 
+def copy_calibration(mib: int, reps: int = 20):
+    """A plain device-to-device copy of known size, for scaling FETCH_SIZE and
+    WRITE_SIZE: each launch reads and writes exactly mib MiB."""
+    import torch
+    n = mib * (1 << 20)
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_per_launch": n, "launches": reps}), flush=True)
+
+
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(json.dumps({"error": "this benchmark measures one GPU; the path has no multi-GPU "
@@ -272,6 +353,8 @@ def main():
                           "n_gpus": args.gpus}))
         sys.exit(2)
     res = run_decode(args)
+    if not args.no_aux:
+        res["detail"]["prefill"] = run_prefill_aux()
     print(json.dumps(res), flush=True)
 
 
