@@ -154,6 +154,8 @@ iq_status iq_prefill_attention(const iq_cache* cache, const void* rot_dev, const
   if (n_q == 0) return IQ_OK;
   const int group = n_q_heads / cache->n_kv_heads;
   if (!pow2(group) || group > 128 || cache->n_kv_heads > 65535) return IQ_ERR_UNSUPPORTED;
+  if ((int64_t)q_start_pos + n_q > (int64_t)iq::kPrefillMaxPages * IQ_PAGE_TOKENS)
+    return IQ_ERR_UNSUPPORTED;
   const iq::PrefillPlan plan = iq::plan_prefill(n_q, n_q_heads, cache->n_kv_heads, q_start_pos, device_cu_count());
   if (plan.row_tiles > 65535) return IQ_ERR_UNSUPPORTED;
   const size_t need = iq::prefill_workspace_bytes(n_q, n_q_heads, plan);

@@ -43,6 +43,10 @@ hipError_t launch_decode(const CacheView& c, const float* rot, const void* q, in
                          const int32_t* seq_lens, const DecodePlan& plan, float softmax_scale,
                          float* out, void* workspace, hipStream_t stream);
 
+// Longest causal key range of one prefill call, in pages (the page ids of the
+// range are staged in LDS): 4096 pages = 262,144 tokens.
+constexpr int kPrefillMaxPages = 4096;
+
 struct PrefillPlan {
   int row_tiles;        // workgroups per kv head along the query rows
   int kv_splits;        // workgroups along the key range

@@ -177,10 +177,14 @@ def test_decode_shuffled_equals_contiguous_block_table():
 
 
 PREFILL_CASES = [
-    # (cache length, n_q, hkv, hq)
+    # (cache length, n_q, hkv, hq): groups 1..128 (1..128 queries per 128-row
+    # tile), ragged last tiles, a page-aligned chunk start, a single query
     (1000, 200, 2, 16),
     (300, 300, 1, 1),
     (700, 77, 2, 8),
+    (1024, 128, 1, 32),
+    (640, 1, 2, 4),
+    (200, 70, 1, 128),
 ]
 
 
