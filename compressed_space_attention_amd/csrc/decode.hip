@@ -90,8 +90,7 @@ __device__ __forceinline__ int tile_block(int t, int col) {
 // V norms 128), filled by direct global->LDS loads (7 per page).  Two pages are
 // in flight while the wave computes a third from registers.
 constexpr int kSlotBytes = 6400;
-constexpr int kMaxPagesPerSplit = 256;  // the planner keeps splits within this
-constexpr int kDefaultPagesPerSplit = 32;  // many-page regime: 8 pages per wave
+constexpr int kMaxPagesPerSplit = 512;   // the planner keeps splits within this (64 per wave)
 #define IQ_MAX_GROUP_BYTES (16 * 128 * 4)  // up to 16 query heads of fp32
 constexpr int kDmaPerPage = 7;
 
@@ -385,14 +384,14 @@ __device__ __forceinline__ void rotate_queries(int group, int q_dtype, const uin
   }
 }
 
-template <bool PACK8>
-__global__ __launch_bounds__(256, 2) void decode_split_kernel(const int32_t* __restrict__ block_table,
-                                                              const int32_t* __restrict__ seq_lens,
-                                                              const uint8_t* __restrict__ q_bytes,
-                                                              const float* __restrict__ rot_all,
-                                                              int max_pages, int pages_per_split,
-                                                              int hq, int group, int q_dtype,
-                                                              int splits, DecodeArgs a) {
+template <bool PACK8, int kDecWaves>
+__global__ __launch_bounds__(64 * kDecWaves, 1) void decode_split_kernel(const int32_t* __restrict__ block_table,
+                                                                      const int32_t* __restrict__ seq_lens,
+                                                                      const uint8_t* __restrict__ q_bytes,
+                                                                      const float* __restrict__ rot_all,
+                                                                      int max_pages, int pages_per_split,
+                                                                      int hq, int group, int q_dtype,
+                                                                      int splits, DecodeArgs a) {
   // The leading arguments are preloaded into SGPRs (14 dwords): everything
   // the first loads need.  The rest come from the argument struct.
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
@@ -400,41 +399,44 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const int32_t* __r
   // wave-uniform: keeps the wave's page bookkeeping in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, jq = lane >> 4;
+  constexpr int kLastWave = kDecWaves - 1;
 
-  __shared__ __attribute__((aligned(16))) uint8_t s_ring[4][2][kSlotBytes];  // 51,200 B
-  __shared__ __attribute__((aligned(16))) float s_rot[kRotFloats];           // 2,048 B
+  __shared__ __attribute__((aligned(16))) uint8_t s_ring[kDecWaves][2][kSlotBytes];  // 102,400 B
+  __shared__ __attribute__((aligned(16))) uint8_t s_tail[kSlotBytes];  // the sequence's partial last page
+  __shared__ __attribute__((aligned(16))) float s_rot[kRotFloats];     // 2,048 B
   __shared__ uint32_t s_q[32 * 64];  // Q' operands: [kstep*8 + dword][lane]
-  __shared__ int s_pages[kMaxPagesPerSplit];  // the split's page ids
+  __shared__ int s_pages[64 * kDecWaves];  // the split's page ids
   __shared__ __attribute__((aligned(16))) uint8_t s_qraw[IQ_MAX_GROUP_BYTES];  // the group's queries
   __shared__ float s_qinv[16];
-  __shared__ float s_m[4][16], s_l[4][16];
+  __shared__ float s_m[kDecWaves][16], s_l[kDecWaves][16];
+  __shared__ int s_next;  // next unclaimed page of the split (waves claim pages as they go)
 
   // ---- prologue: every load that needs only the arguments goes out first ----
-  // The split's page ids (a quarter per wave) and, in wave 0, the rotation
-  // blocks and the group's queries arrive by direct-to-LDS loads; the length
-  // and the wave's first two page ids are scalar loads.  The first two pages
-  // are requested before the length is known: their block-table entries lie
-  // inside the table and their ids are clamped into the cache, so the loads
-  // stay in bounds even where the table holds no page yet, and a page beyond
-  // the length is never used.
+  // The split's page ids (an eighth per wave), the rotation blocks and the
+  // group's queries arrive by direct-to-LDS loads; the length and the wave's
+  // first two page ids are scalar loads.  The first two pages are requested
+  // before the length is known: their block-table entries lie inside the table
+  // and their ids are clamped into the cache, so the loads stay in bounds even
+  // where the table holds no page yet, and a page beyond the length is never
+  // used.
   const int pg_begin = split * pages_per_split;
-  const int pg_first = pg_begin + wave;
   const int* bt = block_table + (size_t)b * max_pages;
   // scalar loads first: after the first direct-to-LDS load the compiler no
   // longer proves the table unmodified and would use vector loads + full waits
   const int L = seq_lens[b];
   const int last_entry = max_pages - 1;
+  const uint32_t bt0 = (uint32_t)bt[min(pg_begin + wave, last_entry)];
+  const uint32_t bt1 = (uint32_t)bt[min(pg_begin + wave + kDecWaves, last_entry)];
   const uint32_t last_page = (uint32_t)a.num_pages - 1u;
-  const uint32_t bt0 = (uint32_t)bt[min(pg_first, last_entry)];
-  const uint32_t bt1 = (uint32_t)bt[min(pg_first + 4, last_entry)];
   const int n_alloc = min(pages_per_split, max_pages - pg_begin);  // readable table entries
   if (64 * wave < n_alloc && 64 * wave + lane < n_alloc)
     lds_dma4(bt + pg_begin + 64 * wave + lane, &s_pages[64 * wave]);
   // Each wave loads the rotation blocks (the same bytes into the same place)
-  // and the rows of the query heads it rotates: 2w, 2w+1 (and 8+2w, 9+2w
-  // for groups above 8).
+  // and the rows of the query heads it rotates: 2w, 2w+1 (+ 2W, 2W+1 for
+  // the second pass of a four-wave workgroup with a group above 8).
   const int esize = q_dtype == 0 ? 4 : 2;
-  const int n_pass = group > 8 ? 2 : 1;
+  constexpr int kHeadsPerPass = 2 * kDecWaves;
+  const int n_pass = (group + kHeadsPerPass - 1) / kHeadsPerPass;
   {
     const uint8_t* rg = reinterpret_cast<const uint8_t*>(rot_all + (size_t)g * kRotFloats) + 16 * lane;
     lds_dma16(rg, s_rot);
@@ -442,15 +444,13 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const int32_t* __r
     const size_t row_bytes = (size_t)kD * esize;
     const uint8_t* qg = q_bytes + ((size_t)b * hq + (size_t)g * group) * row_bytes;
     for (int p = 0; p < n_pass; ++p) {
-      const int h0 = 8 * p + 2 * wave;
+      const int h0 = kHeadsPerPass * p + 2 * wave;
       const int nbytes = max(0, min(2, group - h0)) * (int)row_bytes;
       if (16 * lane < nbytes) lds_dma16(qg + h0 * row_bytes + 16 * lane, s_qraw + h0 * row_bytes);
     }
   }
-  const uint32_t id0 = min(bt0, last_page);
-  const uint32_t id1 = min(bt1, last_page);
-  issue_page(a, (int)id0, g, lane, s_ring[wave][0]);
-  issue_page(a, (int)id1, g, lane, s_ring[wave][1]);
+  issue_page(a, (int)min(bt0, last_page), g, lane, s_ring[wave][0]);
+  issue_page(a, (int)min(bt1, last_page), g, lane, s_ring[wave][1]);
 
   // (a length beyond the block table breaks the contract; never read past it)
   const int n_pages = min((L + kPage - 1) / kPage, max_pages);
@@ -465,15 +465,20 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const int32_t* __r
     return;
   }
   const int pg_end = min(n_pages, pg_begin + pages_per_split);
-  const int n_mine = pg_first < pg_end ? (pg_end - pg_first + 3) / 4 : 0;  // this wave's pages
+  // The partial last page of the sequence, if it falls in this split, is kept
+  // out of the shared pool and handled (masked) by the last wave.
+  const bool has_tail = (L % kPage) != 0 && n_pages * kPage > L && pg_end == n_pages;
+  const int n_pool = (pg_end - pg_begin) - (has_tail ? 1 : 0);  // full pages to share
+  if (tid == 0) s_next = 2 * kDecWaves;  // pool pages w and w + 8 are each wave's first two
 
   // Everything but the two pages has landed once at most their loads are
   // outstanding (loads complete in issue order).
   __builtin_amdgcn_s_waitcnt(wait_vm(2 * kDmaPerPage));
 
-  // All four waves rotate the queries (each its own heads).
+  // Every wave rotates its query heads (rotate_queries: lane r of a half
+  // wave holds coordinates 4r..4r+3).
   for (int p = 0; p < n_pass; ++p)
-    rotate_queries(group, q_dtype, s_qraw, s_rot, s_q, s_qinv, 8 * p, wave, lane);
+    rotate_queries(group, q_dtype, s_qraw, s_rot, s_q, s_qinv, kHeadsPerPass * p, wave, lane);
   // LDS writes visible to the workgroup; unlike __syncthreads this does not
   // wait for the page loads still in flight.
   __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
@@ -494,6 +499,10 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const int32_t* __r
   // per-lane score factor of the lane's head column
   const float fac = a.score_factor * s_qinv[PACK8 ? (col & 7) : col];
 
+  // the last wave brings the partial page now; it is used after its stream
+  const bool tail_mine = has_tail && wave == kLastWave;
+  if (tail_mine) issue_page(a, (int)min((uint32_t)s_pages[n_pages - 1 - pg_begin], last_page), g, lane, s_tail);
+
   PageState st;
   st.m_run = -INFINITY;
   st.l_run = 0.f;
@@ -501,44 +510,71 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const int32_t* __r
 #pragma unroll
   for (int m = 0; m < 8; ++m) st.acc[m] = f4{0.f, 0.f, 0.f, 0.f};
 
-  // Page i of the wave: wait for its loads, read it into registers and reuse
-  // its slot for page i + 2.  Page 1 is always in flight behind page 0.
-  auto stage = [&](int i, PageRegs<PACK8>& cur) {
-    uint8_t* slot = s_ring[wave][i & 1];
-    if (i == 0 || i + 1 < n_mine)
-      __builtin_amdgcn_s_waitcnt(wait_vm(kDmaPerPage));
-    else
-      __builtin_amdgcn_s_waitcnt(wait_vm(0));
+  // ---- the wave's stream of full pages ----
+  // Slots 0 and 1 start with pool pages w and w + W; each processed slot is
+  // refilled with the next unclaimed pool page (an LDS counter), so the waves
+  // of the workgroup finish within about a page of each other.  seq[] counts
+  // page loads in issue order, to know how many may still be outstanding.
+  bool have0 = wave < n_pool, have1 = wave + kDecWaves < n_pool;
+  int pg0 = pg_begin + wave, pg1 = pg_begin + wave + kDecWaves;
+  int seq0 = 0, seq1 = 1, issued = 2;
+  int head = 0;
+  bool pool_open = true;
+  while (head == 0 ? have0 : have1) {
+    uint8_t* slot = s_ring[wave][head];
+    const int seq_h = head == 0 ? seq0 : seq1;
+    // loads issued after this page's: the other slot (and the tail's, which
+    // went out after the first two pages)
+    const int after = issued - 1 - seq_h + ((tail_mine && seq_h < 2) ? 1 : 0);
+    if (after <= 0) __builtin_amdgcn_s_waitcnt(wait_vm(0));
+    else if (after == 1) __builtin_amdgcn_s_waitcnt(wait_vm(kDmaPerPage));
+    else __builtin_amdgcn_s_waitcnt(wait_vm(2 * kDmaPerPage));
+    PageRegs<PACK8> cur;
     read_page<PACK8>(slot, lane, cur);
-    if (i + 2 < n_mine) {
-      const uint32_t id = min((uint32_t)s_pages[wave + 4 * (i + 2)], last_page);
+    const int pg = head == 0 ? pg0 : pg1;
+    // claim the next page and reuse this slot for it (claims only grow: a
+    // failed claim ends the stream)
+    int claim = n_pool;
+    if (pool_open) {
+      int c = 0;
+      if (lane == 0) c = atomicAdd(&s_next, 1);
+      claim = __builtin_amdgcn_readfirstlane(c);
+    }
+    const bool got = claim < n_pool;
+    pool_open = got;
+    if (got) {
+      const uint32_t id = min((uint32_t)s_pages[claim], last_page);
       __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // slot read before it is refilled
       issue_page(a, (int)__builtin_amdgcn_readfirstlane(id), g, lane, slot);
     }
-  };
-  // Only the wave's last page can hold the end of the sequence: the loop runs
-  // unmasked and the last page goes through the masked variant.
-  int i = 0;
-  for (; i + 1 < n_mine; ++i) {
-    PageRegs<PACK8> cur;
-    stage(i, cur);
-    process_page<PACK8, false>(cur, st, (pg_first + 4 * i) * kPage, L, lane, fac, qhi, qlo);
+    if (head == 0) {
+      have0 = got; pg0 = pg_begin + claim; seq0 = issued;
+    } else {
+      have1 = got; pg1 = pg_begin + claim; seq1 = issued;
+    }
+    issued += got ? 1 : 0;
+    process_page<PACK8, false>(cur, st, pg * kPage, L, lane, fac, qhi, qlo);
+    // the other slot's page is older than the refill, if it holds one
+    if (head == 0 ? have1 : have0) head ^= 1;
   }
-  if (i < n_mine) {
+  if (tail_mine) {
+    __builtin_amdgcn_s_waitcnt(wait_vm(0));
     PageRegs<PACK8> cur;
-    stage(i, cur);
-    process_page<PACK8, true>(cur, st, (pg_first + 4 * i) * kPage, L, lane, fac, qhi, qlo);
+    read_page<PACK8>(s_tail, lane, cur);
+    process_page<PACK8, true>(cur, st, (n_pages - 1) * kPage, L, lane, fac, qhi, qlo);
   }
   __builtin_amdgcn_s_waitcnt(wait_vm(0));  // a page requested but not used may still be landing
 
-  // ---- merge the four waves ----
+  // ---- merge the eight waves ----
   float l_col = st.l_run;
   if (PACK8) l_col += dpp_f<kRowRor8, 0xF>(l_col, l_col);
   l_col = sum_xor32(sum_xor16(l_col));
   const float fin = __builtin_amdgcn_ldexpf(a.out_factor, -st.rho_e);
   // The wave's own two slots hold its accumulator now (all its loads have
-  // landed): values 0-15 in slot 0, 16-31 in slot 1.
+  // landed and its reads of them are done): values 0-15 in slot 0, 16-31 in
+  // slot 1.
   static_assert(kSlotBytes >= 16 * 64 * 4, "a slot holds half an accumulator");
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
   float* acc_lo = reinterpret_cast<float*>(s_ring[wave][0]);
   float* acc_hi = reinterpret_cast<float*>(s_ring[wave][1]);
 #pragma unroll
@@ -550,39 +586,40 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const int32_t* __r
   }
   __syncthreads();
   {
-    const int part = wave;  // this thread merges values 8*part .. 8*part+7 of `lane`
-    float mw[4], M = -INFINITY;
+    // this thread merges values V w .. V w + V - 1 of `lane` (coordinates
+    // 32 jq + k), V = 32 / waves
+    constexpr int V = 32 / kDecWaves;
+    float mw[kDecWaves], M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < kDecWaves; ++w) {
       mw[w] = s_m[w][col];
       M = fmaxf(M, mw[w]);
     }
-    float wt[4], Ls = 0.f;
+    float wt[kDecWaves], Ls = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < kDecWaves; ++w) {
       wt[w] = (mw[w] == -INFINITY) ? 0.f : fast_exp2(mw[w] - M);
       Ls += wt[w] * s_l[w][col];
     }
     if (col < group) {
       const size_t row = ((size_t)b * hq + (size_t)g * group + col) * splits + split;
-      f4 o0, o1;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        float s0 = 0.f, s1 = 0.f;
+      for (int v4 = 0; v4 < V / 4; ++v4) {
+        f4 o;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          // values 8*part + k and 8*part + 4 + k (slot 0 holds 0-15, slot 1 16-31)
-          const float* wacc = reinterpret_cast<const float*>(s_ring[w][part < 2 ? 0 : 1]);
-          s0 += wt[w] * wacc[((8 * part + k) & 15) * 64 + lane];
-          s1 += wt[w] * wacc[((8 * part + 4 + k) & 15) * 64 + lane];
+        for (int r = 0; r < 4; ++r) {
+          const int k = V * wave + 4 * v4 + r;  // value index; slot 0 holds 0-15, slot 1 16-31
+          float sum = 0.f;
+#pragma unroll
+          for (int w = 0; w < kDecWaves; ++w) {
+            const float* wacc = reinterpret_cast<const float*>(s_ring[w][k < 16 ? 0 : 1]);
+            sum += wt[w] * wacc[(k & 15) * 64 + lane];
+          }
+          o[r] = sum;
         }
-        o0[k] = s0;
-        o1[k] = s1;
+        *reinterpret_cast<f4*>(a.ws_acc + row * kD + 32 * jq + V * wave + 4 * v4) = o;
       }
-      f4* dst = reinterpret_cast<f4*>(a.ws_acc + row * kD + 32 * jq + 8 * part);
-      dst[0] = o0;
-      dst[1] = o1;
-      if (jq == 0 && part == 0) {
+      if (jq == 0 && wave == 0) {
         a.ws_ml[2 * row] = M;
         a.ws_ml[2 * row + 1] = Ls;
       }
@@ -743,40 +780,37 @@ __global__ __launch_bounds__(256, 1) void decode_merge_kernel(const float* __res
   *reinterpret_cast<float2*>(out + 2 * lane) = make_float2(y0 * nrm, y1 * nrm);
 }
 
-// Split planning.  Few pages per kv head (short or single sequences): one
-// wave of workgroups (two per CU, the LDS limit) so the whole call is a
-// single pass with the shortest critical path.  Many pages: more, shorter
-// splits than the CUs can hold at once, so that workgroups that finish early
-// (the second workgroup on a CU runs behind the first, and ragged batches
-// give splits of unequal length) are replaced by the hardware dispatcher.
+// Split planning: one workgroup per CU.  Few pages per kv head (short or
+// single sequences, at most two pages per wave): four waves, one pass over the
+// chip, the shortest critical path.  Many pages: eight waves (two per SIMD;
+// the LDS holds one such workgroup), a unit (sequence, kv head) getting
+// ceil(CUs / units) splits of equal page ranges inside which the waves claim
+// pages dynamically, so the waves of a CU finish together.  One workgroup
+// per CU also keeps two workgroups from competing for the same SIMDs (the
+// older would win the issue arbitration and the younger finish late).
+// Ragged batches may ask for more rounds of shorter splits
+// (IQ_DECODE_ROUNDS), which the hardware dispatcher balances.
 DecodePlan plan_decode(int batch, int hkv, int max_seq_len, int num_cus) {
   const int max_pages = max(1, (max_seq_len + kPage - 1) / kPage);
   const long long units = (long long)max(1, batch) * max(1, hkv);
-  // One workgroup per CU (two pages per wave at 32K context) beats two (one
-  // page per wave): half the query rotations and split partials, and each
-  // wave's second page loads while it computes the first.
-  long long per_cu = 1;
-  if (const char* env = getenv("IQ_DECODE_WGS_PER_CU")) {
+  const long long cus = max(1, num_cus);
+  DecodePlan p;
+  p.waves = (units * max_pages <= cus * 4 * 2) ? 4 : 8;
+  long long rounds = 1;
+  if (const char* env = getenv("IQ_DECODE_ROUNDS")) {
     const long long v = atoll(env);
-    if (v > 0) per_cu = v;
+    if (v > 0) rounds = v;
   }
-  const long long slots = per_cu * max(1, num_cus);
-  long long pps;
-  if (units * max_pages <= slots * 4 * 2) {
-    // latency regime: at most two pages per wave
-    long long splits = (slots + units - 1) / units;
-    if (splits > max_pages) splits = max_pages;
-    pps = (max_pages + splits - 1) / splits;
-  } else {
-    pps = kDefaultPagesPerSplit;
-  }
+  long long splits = (rounds * cus + units - 1) / units;
+  if (splits > max_pages) splits = max_pages;
+  long long pps = (max_pages + splits - 1) / splits;
   if (const char* env = getenv("IQ_DECODE_PAGES_PER_SPLIT")) {
     const long long v = atoll(env);
     if (v > 0) pps = v;
   }
-  if (pps > kMaxPagesPerSplit) pps = kMaxPagesPerSplit;
+  const long long cap = 64LL * p.waves;  // page ids staged per split
+  if (pps > cap) pps = cap;
   if (pps < 1) pps = 1;
-  DecodePlan p;
   p.pages_per_split = (int)pps;
   p.splits = (int)((max_pages + pps - 1) / pps);
   return p;
@@ -813,14 +847,18 @@ hipError_t launch_decode(const CacheView& c, const float* rot, const void* q, in
   a.out = out;
   const uint8_t* qb = static_cast<const uint8_t*>(q);
   const dim3 grid(plan.splits, c.hkv, batch);
-  if (a.group <= 8)
-    hipLaunchKernelGGL(decode_split_kernel<true>, grid, dim3(256), 0, stream, block_table, seq_lens,
-                       qb, rot, a.max_pages, a.pages_per_split, a.hq, a.group, a.q_dtype,
-                       a.splits, a);
-  else
-    hipLaunchKernelGGL(decode_split_kernel<false>, grid, dim3(256), 0, stream, block_table, seq_lens,
-                       qb, rot, a.max_pages, a.pages_per_split, a.hq, a.group, a.q_dtype,
-                       a.splits, a);
+#define IQ_SPLIT(P8, W)                                                                           \
+  hipLaunchKernelGGL((decode_split_kernel<P8, W>), grid, dim3(64 * W), 0, stream, block_table,     \
+                     seq_lens, qb, rot, a.max_pages, a.pages_per_split, a.hq, a.group, a.q_dtype, \
+                     a.splits, a)
+  if (a.group <= 8) {
+    if (plan.waves == 4) IQ_SPLIT(true, 4);
+    else IQ_SPLIT(true, 8);
+  } else {
+    if (plan.waves == 4) IQ_SPLIT(false, 4);
+    else IQ_SPLIT(false, 8);
+  }
+#undef IQ_SPLIT
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_merge_kernel, dim3(hq, batch), dim3(256), 0, stream, rot, a.ws_acc,

@@ -34,6 +34,7 @@ hipError_t launch_quantize_append(const CacheView& c, const float* rot, const vo
 struct DecodePlan {
   int splits;           // workgroups per (sequence, kv head)
   int pages_per_split;
+  int waves;            // waves per workgroup: 4 (one short pass) or 8 (long streams)
 };
 DecodePlan plan_decode(int batch, int hkv, int max_seq_len, int num_cus);
 size_t decode_workspace_bytes(int batch, int hq, const DecodePlan& plan);

@@ -139,29 +139,32 @@ def test_decode_edge_lengths_and_empty_sequence():
     assert np.max(np.abs(out[1, :8] - v0)) <= 1e-3 * np.max(np.abs(v0))
 
 
-def test_decode_split_plans_agree_and_are_deterministic():
+def test_decode_split_plans_agree():
+    """Pages per split from 1 (one page per workgroup) to 512 (one split per
+    sequence, most pages claimed by the waves as they go): every plan is within
+    the oracle tolerance and the plans agree with each other.  Plans (and, with
+    in-split page claiming, repeated runs of one plan) differ only in where P~
+    is rounded to f16 relative to a running maximum, about 2^-11 per weight."""
     lens = [3000, 1500]
     s = Scenario(400, lens, hkv=2, dtype="bf16", outliers=True)
     q = s.queries(401, 2, 16).cuda()
     outs = []
-    old = os.environ.get("IQ_DECODE_TARGET_WGS")
+    old = os.environ.get("IQ_DECODE_PAGES_PER_SPLIT")
     try:
-        for target in ("1", "7", "64", "100000"):
-            os.environ["IQ_DECODE_TARGET_WGS"] = target
+        for pps in ("1", "3", "16", "512"):
+            os.environ["IQ_DECODE_PAGES_PER_SPLIT"] = pps
             outs.append(s.iq.decode_attention(s.cache, s.rot, q, s.bt_dev, s.lens_dev, 3000).cpu().numpy())
         again = s.iq.decode_attention(s.cache, s.rot, q, s.bt_dev, s.lens_dev, 3000).cpu().numpy()
     finally:
         if old is None:
-            os.environ.pop("IQ_DECODE_TARGET_WGS", None)
+            os.environ.pop("IQ_DECODE_PAGES_PER_SPLIT", None)
         else:
-            os.environ["IQ_DECODE_TARGET_WGS"] = old
-    assert np.array_equal(again, outs[-1])           # fixed plan: bit-identical
-    # Each plan is within the oracle tolerance; plans differ only by where P~ is
-    # rounded to f16 (relative to each split's running max), about 2^-11 per weight.
+            os.environ["IQ_DECODE_PAGES_PER_SPLIT"] = old
     ref = O.decode_attention(s.host_cache(), s.blocks, q.double().cpu().numpy(), s.block_table, lens)
-    for o in outs:
+    for o in outs + [again]:
         assert max_row_error(o, ref) <= tol()
         assert max_row_error(o, outs[0]) <= 0.5 * tol()
+    assert max_row_error(again, outs[-1]) <= 0.5 * tol()
 
 
 def test_decode_shuffled_equals_contiguous_block_table():
