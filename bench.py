@@ -98,6 +98,27 @@ class DecodeLayer:
         self.out = torch.empty((b, w.n_q_heads, 128), dtype=torch.float32, device=device)
 
 
+def measured_traffic(workload: str):
+    """HBM bytes per decode call from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE record (scaled by the copy-kernel calibration), or None when no
+    record exists for this workload or the kernel sources changed since."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "decode_gqa_decode_32k_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("workload") != workload:
+        return None
+    h = hashlib.sha256()
+    for src in rec["sources"]:
+        with open(os.path.join(ROOT, src), "rb") as f:
+            h.update(f.read())
+    if h.hexdigest() != rec["sources_sha256"]:
+        return None
+    return int(rec["traffic_bytes_per_call"])
+
+
 def run_decode(args):
     import torch
 
@@ -215,7 +236,8 @@ def run_decode(args):
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(w.name),
+            "algorithmic_bytes": kv_bytes,
         },
         "detail": {
             "pct_hbm_peak_step": round(100 * gbs / HBM_PEAK_GBS, 2),

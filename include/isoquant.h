@@ -77,7 +77,14 @@ enum {
  * g holding coordinates 32g..32g+31.  In a group, the bytes at offsets b, 4+b
  * and 8+b (b = 0..3) form a 24-bit little-endian integer ("byte lane" b); the
  * 3-bit code of coordinate 32g + 4s + b is at bits 3s..3s+2 of byte lane b.
- * The struct is read during the call only.
+ * K pages hold the records slot after slot: record (page, head, slot) starts
+ * at byte ((page * n_kv_heads + head) * 64 + slot) * 48 of k_codes.
+ * V pages hold the same records in the order the decode matrix cores read
+ * them: the 3,072 bytes of (page, head) are 64 regions of 48 bytes, region
+ * n + 16 q (n, q < 16, 4) made of four 12-byte chunks c; byte lane r (bytes r,
+ * 4 + r, 8 + r) of chunk c of region (n, q) is byte lane n % 4 of group n / 4
+ * of the record in slot 16 c + 4 q + r.  Norm arrays are slot-ordered for
+ * both.  The struct is read during the call only.
  */
 typedef struct {
   uint8_t *k_codes_dev;
@@ -124,6 +131,8 @@ iq_status iq_rotation_init(const float *quats_host, int32_t n_kv_heads, void *ro
  * pos_dev          : int32[n_tokens], absolute position of each token.
  * block_table_dev  : int32[*][max_pages_per_seq], row-major.
  * n_tokens == 0 is a no-op.  Inputs with non-finite values give unspecified codes.
+ * A token whose position lies outside the block table, or whose table entry is
+ * not a page of the cache, is skipped: no record is written for it.
  */
 iq_status iq_quantize_append(const iq_cache *cache, const void *rot_dev, const void *k_dev,
                              const void *v_dev, int32_t dtype, int32_t n_tokens,
@@ -145,8 +154,13 @@ iq_status iq_quantize_append(const iq_cache *cache, const void *rot_dev, const v
  * softmax_scale  : <= 0 selects 1/sqrt(128).
  * out_dev        : float[batch][n_q_heads][128], in the original (unrotated) space.
  *                  A sequence of length 0 gives zeros.
- * workspace_dev  : at least iq_decode_workspace_bytes(...) bytes, any contents.
+ * workspace_dev  : at least iq_decode_workspace_bytes(...) bytes, any contents;
+ *                  holds the per-split partials (m, l, accumulator) between the
+ *                  split and merge kernels of this call.
  * Unsupported: n_q_heads / n_kv_heads > IQ_MAX_GROUP.
+ * Determinism: inside a split, pages go to whichever wave asks first, so the
+ * order of the f16 rounding of softmax weights can differ between runs (the
+ * results agree to about 2^-11 of a weight, far inside the 1e-3 tolerance).
  */
 size_t iq_decode_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
                                  int32_t max_seq_len);
@@ -167,7 +181,9 @@ iq_status iq_decode_attention(const iq_cache *cache, const void *rot_dev, const 
  * q_dev          : [n_q][n_q_heads][128] of q_dtype.
  * block_table_dev: int32[max_pages] of this sequence.
  * out_dev        : float[n_q][n_q_heads][128], original space.
- * workspace_dev  : at least iq_prefill_workspace_bytes(...) bytes.
+ * workspace_dev  : at least iq_prefill_workspace_bytes(...) bytes (currently 0).
+ * Unsupported: q_start_pos + n_q > 262,144 (the causal range's page ids are
+ * staged on chip), or n_q_heads / n_kv_heads not a power of two up to 128.
  */
 size_t iq_prefill_workspace_bytes(int32_t n_q, int32_t n_q_heads, int32_t n_kv_heads,
                                   int32_t q_start_pos);
