@@ -146,45 +146,53 @@ def run_decode(args):
     ws = torch.empty(max(16, iq.decode_workspace_bytes(w.batch, w.n_q_heads, w.n_kv_heads, max_len)),
                      dtype=torch.uint8, device=device)
 
-    def step(layer, with_append=True):
-        if with_append:
+    def step(layer, mode="step"):
+        """mode "step": the fused decode step (append + attention, one call);
+        "pair": the same as two calls (quantise-append, then decode attention);
+        "decode": decode attention alone (the cache already holds the token)."""
+        if mode == "step":
+            iq.decode_step(layer.cache, layer.rot, layer.q, layer.k_new, layer.v_new, block_table,
+                           seq_lens, max_len, out=layer.out, workspace=ws)
+            return
+        if mode == "pair":
             iq.quantize_append(layer.cache, layer.rot, layer.k_new, layer.v_new, layer.seq_new,
                                layer.pos_new, block_table)
         iq.decode_attention(layer.cache, layer.rot, layer.q, block_table, seq_lens, max_len,
                             out=layer.out, workspace=ws)
 
-    def run_steps(n, start, with_append=True):
+    def run_steps(n, start, mode="step"):
         for i in range(n):
-            step(layers[(start + i) % ring], with_append)
+            step(layers[(start + i) % ring], mode)
 
     # warmup (eager)
     run_steps(args.warmup, 0)
+    run_steps(2, 0, "pair")
     torch.cuda.synchronize()
 
-    def make_graph(n, with_append):
+    def make_graph(n, mode):
         g = torch.cuda.CUDAGraph()
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s):
             with torch.cuda.graph(g, stream=s):
-                run_steps(n, 0, with_append)
+                run_steps(n, 0, mode)
         torch.cuda.current_stream().wait_stream(s)
         return g
 
-    def timed(n_steps, with_append):
+    def timed(n_steps, mode):
         """Time exactly n_steps steps; returns seconds measured by HIP events."""
         stream = torch.cuda.current_stream()
         if args.no_graph:
             torch.cuda.synchronize()
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
-            run_steps(n_steps, 0, with_append)
+            run_steps(n_steps, 0, mode)
             b.record(stream)
             torch.cuda.synchronize()
             return a.elapsed_time(b) / 1e3
         full, rem = divmod(n_steps, ring)
-        g_full = make_graph(ring, with_append) if full else None
-        g_rem = make_graph(rem, with_append) if rem else None
+        g_full = make_graph(ring, mode) if full else None
+        g_rem = make_graph(rem, mode) if rem else None
         if g_full:
             g_full.replay()      # one untimed replay: the graph's first launch uploads it
         if g_rem:
@@ -200,12 +208,13 @@ def run_decode(args):
         torch.cuda.synchronize()
         return a.elapsed_time(b) / 1e3
 
-    t_step = timed(args.steps, True) / args.steps
-    t_decode = timed(args.steps, False) / args.steps
+    t_step = timed(args.steps, "step") / args.steps
+    t_decode = timed(args.steps, "decode") / args.steps
+    t_pair = timed(args.steps, "pair") / args.steps
     gbs = kv_bytes / t_step / 1e9
     dec_gbs = kv_bytes / t_decode / 1e9
     log(f"[bench] step {t_step * 1e6:.2f} us ({gbs:.0f} GB/s), decode call {t_decode * 1e6:.2f} us "
-        f"({dec_gbs:.0f} GB/s)")
+        f"({dec_gbs:.0f} GB/s), unfused append + decode {t_pair * 1e6:.2f} us")
 
     result = {
         "metric": METRIC,
@@ -227,7 +236,8 @@ def run_decode(args):
             "workload": w.name, "batch": w.batch, "context": max_len, "n_q_heads": w.n_q_heads,
             "n_kv_heads": w.n_kv_heads, "head_dim": 128, "page_tokens": 64,
             "packed_kv_bytes_per_step": kv_bytes, "layer_ring": ring,
-            "step": "quantise-append current token + decode attention, one layer",
+            "step": "one layer's decode step: quantise-append of the current token fused into "
+                    "decode attention (iq_decode_step)",
         },
         "roofline": {
             "bound": "hbm",
@@ -243,12 +253,41 @@ def run_decode(args):
             "pct_hbm_peak_step": round(100 * gbs / HBM_PEAK_GBS, 2),
             "decode_call_us": round(t_decode * 1e6, 3),
             "step_us": round(t_step * 1e6, 3),
+            "unfused_append_then_decode_us": round(t_pair * 1e6, 3),
             "tokens_per_s_per_layer": round(w.batch / t_step, 1),
         },
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline_decode(args, w, layers[0], bt_np, lens)
     return result
+
+
+def probe_bandwidth(mib: int = 1024, iters: int = 20):
+    """Achievable HBM bandwidth on this GPU, from two plain torch kernels on a
+    buffer far above the 256 MB Infinity Cache: a read-only reduction and a
+    device-to-device copy (read + write)."""
+    import torch
+    n = mib * (1 << 20)
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    out = torch.empty((), dtype=torch.float32, device="cuda")
+
+    def timeit(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(iters):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / 1e3 / iters
+
+    t_read = timeit(lambda: torch.sum(src, dim=0, out=out))
+    t_copy = timeit(lambda: dst.copy_(src))
+    del src, dst
+    return {"bytes": n, "read_gbs": round(n / t_read / 1e9, 1), "copy_gbs": round(2 * n / t_copy / 1e9, 1)}
 
 
 def run_prefill_aux(iters=30):
@@ -377,6 +416,10 @@ def main():
     res = run_decode(args)
     if not args.no_aux:
         res["detail"]["prefill"] = run_prefill_aux()
+        probe = probe_bandwidth()
+        res["detail"]["hbm_probe"] = probe
+        res["detail"]["decode_call_frac_of_probe_read"] = round(
+            res["roofline"]["achieved"] / probe["read_gbs"], 4)
     print(json.dumps(res), flush=True)
 
 

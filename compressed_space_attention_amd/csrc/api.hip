@@ -131,7 +131,29 @@ iq_status iq_decode_attention(const iq_cache* cache, const void* rot_dev, const 
   return launch_status(iq::launch_decode(view(cache), reinterpret_cast<const float*>(rot_dev), q_dev,
                                          q_dtype, batch, n_q_heads, block_table_dev, max_pages_per_seq,
                                          seq_lens_dev, plan, resolve_scale(softmax_scale), out_dev,
-                                         workspace_dev, stream));
+                                         workspace_dev, nullptr, nullptr, 0, stream));
+}
+
+iq_status iq_decode_step(const iq_cache* cache, const void* rot_dev, const void* q_dev,
+                         int32_t q_dtype, int32_t batch, int32_t n_q_heads, const void* k_new_dev,
+                         const void* v_new_dev, int32_t kv_dtype, const int32_t* block_table_dev,
+                         int32_t max_pages_per_seq, const int32_t* seq_lens_dev, int32_t max_seq_len,
+                         float softmax_scale, float* out_dev, void* workspace_dev,
+                         size_t workspace_bytes, hipStream_t stream) {
+  if (!cache_ok(cache) || !rot_dev || !q_dev || !dtype_ok(q_dtype) || !k_new_dev || !v_new_dev ||
+      !dtype_ok(kv_dtype) || batch < 1 || batch > 65535 || n_q_heads < 1 || !block_table_dev ||
+      max_pages_per_seq < 1 || !seq_lens_dev || max_seq_len < 0 || !out_dev || !workspace_dev)
+    return IQ_ERR_INVALID_ARG;
+  if (n_q_heads % cache->n_kv_heads != 0) return IQ_ERR_INVALID_ARG;
+  if ((int64_t)max_seq_len > (int64_t)max_pages_per_seq * IQ_PAGE_TOKENS) return IQ_ERR_INVALID_ARG;
+  if (cache->n_kv_heads > 65535) return IQ_ERR_UNSUPPORTED;
+  if (n_q_heads / cache->n_kv_heads > IQ_MAX_GROUP) return IQ_ERR_UNSUPPORTED;
+  const iq::DecodePlan plan = iq::plan_decode(batch, cache->n_kv_heads, max_seq_len, device_cu_count());
+  if (workspace_bytes < iq::decode_workspace_bytes(batch, n_q_heads, plan)) return IQ_ERR_WORKSPACE;
+  return launch_status(iq::launch_decode(view(cache), reinterpret_cast<const float*>(rot_dev), q_dev,
+                                         q_dtype, batch, n_q_heads, block_table_dev, max_pages_per_seq,
+                                         seq_lens_dev, plan, resolve_scale(softmax_scale), out_dev,
+                                         workspace_dev, k_new_dev, v_new_dev, kv_dtype, stream));
 }
 
 size_t iq_prefill_workspace_bytes(int32_t n_q, int32_t n_q_heads, int32_t n_kv_heads,

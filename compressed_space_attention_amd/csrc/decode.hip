@@ -40,10 +40,13 @@
 namespace iq {
 
 struct DecodeArgs {
-  const uint8_t* k_codes;
-  const uint16_t* k_norms;
-  const uint8_t* v_codes;
-  const uint16_t* v_norms;
+  uint8_t* k_codes;  // written only by a decode step (the appended token's record)
+  uint16_t* k_norms;
+  uint8_t* v_codes;
+  uint16_t* v_norms;
+  const uint8_t* k_new;  // decode step: the current token's K and V rows [B][Hkv][128]
+  const uint8_t* v_new;
+  int kv_dtype;
   int num_pages, hkv;
   int q_dtype;
   int hq, group;
@@ -94,12 +97,22 @@ constexpr int kMaxPagesPerSplit = 512;   // the planner keeps splits within this
 #define IQ_MAX_GROUP_BYTES (16 * 128 * 4)  // up to 16 query heads of fp32
 constexpr int kDmaPerPage = 7;
 
+// The direct-to-LDS loads are issued from inline asm, so the compiler does
+// not track them: it cannot tell which ring slot a load writes, and would put
+// a wait for every outstanding load before each LDS read of a page (turning
+// the two-slot ring into a one-slot one).  Every read of loaded LDS data is
+// preceded by an explicit s_waitcnt on the counts of this kernel's issue
+// order instead.  The asm has no register outputs: the address operands are
+// read at issue, and the destination is LDS (m0 = wave-uniform LDS base).
 typedef __attribute__((address_space(3))) void* lds_ptr;
+__device__ __forceinline__ uint32_t lds_base(void* lds) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr)lds);
+}
 __device__ __forceinline__ void lds_dma16(const void* g, void* lds) {
-  __builtin_amdgcn_global_load_lds(g, (lds_ptr)lds, 16, 0, 0);
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds_base(lds)) : "memory");
 }
 __device__ __forceinline__ void lds_dma4(const void* g, void* lds) {
-  __builtin_amdgcn_global_load_lds(g, (lds_ptr)lds, 4, 0, 0);
+  asm volatile("global_load_lds_dword %0, off" ::"v"(g), "{m0}"(lds_base(lds)) : "memory");
 }
 // s_waitcnt immediates (gfx9 encoding: vmcnt [3:0] and [15:14], expcnt [6:4],
 // lgkmcnt [11:8]); issued through the builtin so the compiler's own counter
@@ -384,7 +397,12 @@ __device__ __forceinline__ void rotate_queries(int group, int q_dtype, const uin
   }
 }
 
-template <bool PACK8, int kDecWaves>
+// APPEND (a decode step): the current token of each sequence, at position
+// L - 1, is quantised here instead of by a separate append: the wave that
+// processes the sequence's last page quantises the token's K and V rows,
+// patches the record into its LDS copy of the page before using it, and
+// stores it into the cache.
+template <bool PACK8, int kDecWaves, bool APPEND>
 __global__ __launch_bounds__(64 * kDecWaves, 1) void decode_split_kernel(const int32_t* __restrict__ block_table,
                                                                       const int32_t* __restrict__ seq_lens,
                                                                       const uint8_t* __restrict__ q_bytes,
@@ -410,6 +428,7 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void decode_split_kernel(const i
   __shared__ float s_qinv[16];
   __shared__ float s_m[kDecWaves][16], s_l[kDecWaves][16];
   __shared__ int s_next;  // next unclaimed page of the split (waves claim pages as they go)
+  __shared__ __attribute__((aligned(16))) uint8_t s_xraw[APPEND ? 1024 : 16];  // appended K | V rows
 
   // ---- prologue: every load that needs only the arguments goes out first ----
   // The split's page ids (an eighth per wave), the rotation blocks and the
@@ -425,8 +444,13 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void decode_split_kernel(const i
   // longer proves the table unmodified and would use vector loads + full waits
   const int L = seq_lens[b];
   const int last_entry = max_pages - 1;
-  const uint32_t bt0 = (uint32_t)bt[min(pg_begin + wave, last_entry)];
-  const uint32_t bt1 = (uint32_t)bt[min(pg_begin + wave + kDecWaves, last_entry)];
+  // the wave's first two pool pages, w and w + W; where the split is shorter
+  // a slot repeats a page of the split (the same lines: no extra HBM traffic,
+  // and every wave issues the same loads, so the waits below stay exact)
+  const int first0 = pg_begin + min(wave, pages_per_split - 1);
+  const int first1 = wave + kDecWaves < pages_per_split ? pg_begin + wave + kDecWaves : first0;
+  const uint32_t bt0 = (uint32_t)bt[min(first0, last_entry)];
+  const uint32_t bt1 = (uint32_t)bt[min(first1, last_entry)];
   const uint32_t last_page = (uint32_t)a.num_pages - 1u;
   const int n_alloc = min(pages_per_split, max_pages - pg_begin);  // readable table entries
   if (64 * wave < n_alloc && 64 * wave + lane < n_alloc)
@@ -448,6 +472,16 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void decode_split_kernel(const i
       const int nbytes = max(0, min(2, group - h0)) * (int)row_bytes;
       if (16 * lane < nbytes) lds_dma16(qg + h0 * row_bytes + 16 * lane, s_qraw + h0 * row_bytes);
     }
+    if (APPEND && wave == kLastWave) {
+      // the current token's K and V rows of this kv head (quantised here if
+      // the split holds the sequence's last page)
+      const int vbytes = kD * (a.kv_dtype == 0 ? 4 : 2);
+      const size_t off = ((size_t)b * a.hkv + g) * vbytes;
+      if (16 * lane < vbytes) {
+        lds_dma16(a.k_new + off + 16 * lane, s_xraw);
+        lds_dma16(a.v_new + off + 16 * lane, s_xraw + 512);
+      }
+    }
   }
   issue_page(a, (int)min(bt0, last_page), g, lane, s_ring[wave][0]);
   issue_page(a, (int)min(bt1, last_page), g, lane, s_ring[wave][1]);
@@ -467,12 +501,18 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void decode_split_kernel(const i
   const int pg_end = min(n_pages, pg_begin + pages_per_split);
   // The partial last page of the sequence, if it falls in this split, is kept
   // out of the shared pool and handled (masked) by the last wave.
-  const bool has_tail = (L % kPage) != 0 && n_pages * kPage > L && pg_end == n_pages;
+  // A decode step always treats the last page as the tail: its copy in LDS
+  // gets the appended record before use.
+  const bool append_here = APPEND && pg_end == n_pages && L <= max_pages * kPage;
+  const bool has_tail =
+      append_here || ((L % kPage) != 0 && n_pages * kPage > L && pg_end == n_pages);
   const int n_pool = (pg_end - pg_begin) - (has_tail ? 1 : 0);  // full pages to share
   if (tid == 0) s_next = 2 * kDecWaves;  // pool pages w and w + 8 are each wave's first two
 
   // Everything but the two pages has landed once at most their loads are
-  // outstanding (loads complete in issue order).
+  // outstanding (loads complete in issue order).  (One straight-line wait:
+  // with waits on several paths the compiler would assume the worst and wait
+  // for the pages before the LDS reads of the rotation below.)
   __builtin_amdgcn_s_waitcnt(wait_vm(2 * kDmaPerPage));
 
   // Every wave rotates its query heads (rotate_queries: lane r of a half
@@ -502,6 +542,34 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void decode_split_kernel(const i
   // the last wave brings the partial page now; it is used after its stream
   const bool tail_mine = has_tail && wave == kLastWave;
   if (tail_mine) issue_page(a, (int)min((uint32_t)s_pages[n_pages - 1 - pg_begin], last_page), g, lane, s_tail);
+  // ... and quantises the appended token (lanes 0-31 K, 32-63 V)
+  float x_norm = 0.f;
+  u3 x_rec = {0u, 0u, 0u};
+  if (append_here && wave == kLastWave) {
+    const int r = lane & 31;
+    const uint8_t* src = s_xraw + 512 * (lane >> 5);
+    float x0, x1, x2, x3;
+    if (a.kv_dtype == 0) {
+      const f4 v = *reinterpret_cast<const f4*>(src + 16 * r);
+      x0 = v[0]; x1 = v[1]; x2 = v[2]; x3 = v[3];
+    } else {
+      const u2 v = *reinterpret_cast<const u2*>(src + 8 * r);
+      const uint32_t w0 = v[0], w1 = v[1];
+      if (a.kv_dtype == 1) {
+        x0 = __builtin_bit_cast(float, w0 << 16);
+        x1 = __builtin_bit_cast(float, w0 & 0xFFFF0000u);
+        x2 = __builtin_bit_cast(float, w1 << 16);
+        x3 = __builtin_bit_cast(float, w1 & 0xFFFF0000u);
+      } else {
+        x0 = half_bits_to_float(w0 & 0xFFFFu);
+        x1 = half_bits_to_float(w0 >> 16);
+        x2 = half_bits_to_float(w1 & 0xFFFFu);
+        x3 = half_bits_to_float(w1 >> 16);
+      }
+    }
+    const f4* m = reinterpret_cast<const f4*>(s_rot + 16 * r);
+    quantize_lanes32(x0, x1, x2, x3, m[0], m[1], m[2], m[3], r, x_norm, x_rec);
+  }
 
   PageState st;
   st.m_run = -INFINITY;
@@ -515,7 +583,7 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void decode_split_kernel(const i
   // refilled with the next unclaimed pool page (an LDS counter), so the waves
   // of the workgroup finish within about a page of each other.  seq[] counts
   // page loads in issue order, to know how many may still be outstanding.
-  bool have0 = wave < n_pool, have1 = wave + kDecWaves < n_pool;
+  bool have0 = wave < n_pool, have1 = wave + kDecWaves < n_pool;  // n_pool <= pages_per_split
   int pg0 = pg_begin + wave, pg1 = pg_begin + wave + kDecWaves;
   int seq0 = 0, seq1 = 1, issued = 2;
   int head = 0;
@@ -524,7 +592,7 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void decode_split_kernel(const i
     uint8_t* slot = s_ring[wave][head];
     const int seq_h = head == 0 ? seq0 : seq1;
     // loads issued after this page's: the other slot (and the tail's, which
-    // went out after the first two pages)
+    // went out after the first pages)
     const int after = issued - 1 - seq_h + ((tail_mine && seq_h < 2) ? 1 : 0);
     if (after <= 0) __builtin_amdgcn_s_waitcnt(wait_vm(0));
     else if (after == 1) __builtin_amdgcn_s_waitcnt(wait_vm(kDmaPerPage));
@@ -559,11 +627,25 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void decode_split_kernel(const i
   }
   if (tail_mine) {
     __builtin_amdgcn_s_waitcnt(wait_vm(0));
+    if (append_here) {  // the appended record replaces slot L - 1 of the page copy
+      const bool is_v = lane >= 32;
+      place_record(is_v, lane & 31, x_rec, x_norm, s_tail + (is_v ? 3072 : 0),
+                   reinterpret_cast<uint16_t*>(s_tail + 6144 + (is_v ? 128 : 0)), (L - 1) & 63);
+    }
     PageRegs<PACK8> cur;
     read_page<PACK8>(s_tail, lane, cur);
     process_page<PACK8, true>(cur, st, (n_pages - 1) * kPage, L, lane, fac, qhi, qlo);
   }
   __builtin_amdgcn_s_waitcnt(wait_vm(0));  // a page requested but not used may still be landing
+  if (append_here && wave == kLastWave) {  // the record into the cache (skipped for a bad page id)
+    const uint32_t id = (uint32_t)s_pages[n_pages - 1 - pg_begin];
+    if (id < (uint32_t)a.num_pages) {
+      const size_t blk = (size_t)id * a.hkv + g;
+      const bool is_v = lane >= 32;
+      place_record(is_v, lane & 31, x_rec, x_norm, (is_v ? a.v_codes : a.k_codes) + blk * (kPage * kRec),
+                   (is_v ? a.v_norms : a.k_norms) + blk * kPage, (L - 1) & 63);
+    }
+  }
 
   // ---- merge the eight waves ----
   float l_col = st.l_run;
@@ -789,13 +871,18 @@ __global__ __launch_bounds__(256, 1) void decode_merge_kernel(const float* __res
 // per CU also keeps two workgroups from competing for the same SIMDs (the
 // older would win the issue arbitration and the younger finish late).
 // Ragged batches may ask for more rounds of shorter splits
-// (IQ_DECODE_ROUNDS), which the hardware dispatcher balances.
+// (IQ_DECODE_ROUNDS), which the hardware dispatcher balances; IQ_DECODE_WAVES
+// (4 or 8) overrides the waves per workgroup.
 DecodePlan plan_decode(int batch, int hkv, int max_seq_len, int num_cus) {
   const int max_pages = max(1, (max_seq_len + kPage - 1) / kPage);
   const long long units = (long long)max(1, batch) * max(1, hkv);
   const long long cus = max(1, num_cus);
   DecodePlan p;
   p.waves = (units * max_pages <= cus * 4 * 2) ? 4 : 8;
+  if (const char* env = getenv("IQ_DECODE_WAVES")) {
+    const int v = atoi(env);
+    if (v == 4 || v == 8) p.waves = v;
+  }
   long long rounds = 1;
   if (const char* env = getenv("IQ_DECODE_ROUNDS")) {
     const long long v = atoll(env);
@@ -824,12 +911,15 @@ size_t decode_workspace_bytes(int batch, int hq, const DecodePlan& plan) {
 hipError_t launch_decode(const CacheView& c, const float* rot, const void* q, int q_dtype, int batch,
                          int hq, const int32_t* block_table, int max_pages, const int32_t* seq_lens,
                          const DecodePlan& plan, float softmax_scale, float* out, void* workspace,
-                         hipStream_t stream) {
+                         const void* k_new, const void* v_new, int kv_dtype, hipStream_t stream) {
   DecodeArgs a;
   a.k_codes = c.k_codes;
   a.k_norms = c.k_norms;
   a.v_codes = c.v_codes;
   a.v_norms = c.v_norms;
+  a.k_new = static_cast<const uint8_t*>(k_new);
+  a.v_new = static_cast<const uint8_t*>(v_new);
+  a.kv_dtype = kv_dtype;
   a.num_pages = c.num_pages;
   a.hkv = c.hkv;
   a.q_dtype = q_dtype;
@@ -847,17 +937,22 @@ hipError_t launch_decode(const CacheView& c, const float* rot, const void* q, in
   a.out = out;
   const uint8_t* qb = static_cast<const uint8_t*>(q);
   const dim3 grid(plan.splits, c.hkv, batch);
-#define IQ_SPLIT(P8, W)                                                                           \
-  hipLaunchKernelGGL((decode_split_kernel<P8, W>), grid, dim3(64 * W), 0, stream, block_table,     \
+#define IQ_SPLIT(P8, W, AP)                                                                       \
+  hipLaunchKernelGGL((decode_split_kernel<P8, W, AP>), grid, dim3(64 * W), 0, stream, block_table, \
                      seq_lens, qb, rot, a.max_pages, a.pages_per_split, a.hq, a.group, a.q_dtype, \
                      a.splits, a)
+#define IQ_SPLIT_W(P8, AP)              \
+  if (plan.waves == 4) IQ_SPLIT(P8, 4, AP); \
+  else IQ_SPLIT(P8, 8, AP)
+  const bool append = k_new != nullptr;
   if (a.group <= 8) {
-    if (plan.waves == 4) IQ_SPLIT(true, 4);
-    else IQ_SPLIT(true, 8);
+    if (append) { IQ_SPLIT_W(true, true); }
+    else { IQ_SPLIT_W(true, false); }
   } else {
-    if (plan.waves == 4) IQ_SPLIT(false, 4);
-    else IQ_SPLIT(false, 8);
+    if (append) { IQ_SPLIT_W(false, true); }
+    else { IQ_SPLIT_W(false, false); }
   }
+#undef IQ_SPLIT_W
 #undef IQ_SPLIT
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -261,6 +261,126 @@ __device__ __forceinline__ uint32_t umax_xor32(uint32_t v) {
   return max(p[0], p[1]);
 }
 
+// Exchanges with lane ^ 4 and lane ^ 8 inside rows of 16 (DPP row shifts /
+// rotation), and bitwise-or / sum reductions over them.
+__device__ __forceinline__ float lane_xor4_f(float v) {
+  const int iv = __builtin_bit_cast(int, v);
+  const int t = __builtin_amdgcn_update_dpp(iv, iv, 0x104, 0xF, 0x5, false);  // row_shl:4, banks 0, 2
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(t, iv, 0x114, 0xF, 0xA, false));
+}
+__device__ __forceinline__ float lane_xor8_f(float v) {
+  const int iv = __builtin_bit_cast(int, v);
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(iv, iv, 0x128, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float add_xor4(float v) { return v + lane_xor4_f(v); }
+__device__ __forceinline__ uint32_t or_xor1(uint32_t v) {
+  return v | (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true);
+}
+__device__ __forceinline__ uint32_t or_xor2(uint32_t v) {
+  return v | (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true);
+}
+__device__ __forceinline__ uint32_t or_xor4(uint32_t v) {
+  return v | __builtin_bit_cast(uint32_t, lane_xor4_f(__builtin_bit_cast(float, v)));
+}
+
+// ---------------------------------------------------------------------------
+// Quantise one 128-vector held by the 32 lanes of a half-wave: lane r holds
+// coordinates 4r..4r+3 (x0..x3) and the rows m0..m3 of SO(4) block r.
+// n = ||x|| (every lane); w = the three dwords of group r/8 of the packed
+// record (every lane of the group).  The Walsh-Hadamard butterflies at
+// coordinate distance 1 and 2 are in registers, 4..64 are lane exchanges
+// 1..16; u = (B H x) / n with H unnormalised equals T x sqrt(d) / n.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void quantize_lanes32(float x0, float x1, float x2, float x3,
+                                                 const f4& m0, const f4& m1, const f4& m2,
+                                                 const f4& m3, int r, float& n, u3& w) {
+  float ss = fmaf(x3, x3, fmaf(x2, x2, fmaf(x1, x1, x0 * x0)));
+  ss += quad_xor1(ss);
+  ss += quad_xor2(ss);
+  ss = add_xor4(ss);
+  ss += lane_xor8_f(ss);
+  ss = sum_xor16(ss);
+  n = sqrtf(ss);
+  {
+    const float a0 = x0 + x1, a1 = x0 - x1, a2 = x2 + x3, a3 = x2 - x3;
+    x0 = a0 + a2; x2 = a0 - a2; x1 = a1 + a3; x3 = a1 - a3;
+  }
+  // lower lane keeps y + partner, upper lane partner - y
+  float sg = (r & 1) ? -1.0f : 1.0f;
+  x0 = fmaf(sg, x0, quad_xor1(x0)); x1 = fmaf(sg, x1, quad_xor1(x1));
+  x2 = fmaf(sg, x2, quad_xor1(x2)); x3 = fmaf(sg, x3, quad_xor1(x3));
+  sg = (r & 2) ? -1.0f : 1.0f;
+  x0 = fmaf(sg, x0, quad_xor2(x0)); x1 = fmaf(sg, x1, quad_xor2(x1));
+  x2 = fmaf(sg, x2, quad_xor2(x2)); x3 = fmaf(sg, x3, quad_xor2(x3));
+  sg = (r & 4) ? -1.0f : 1.0f;
+  x0 = fmaf(sg, x0, lane_xor4_f(x0)); x1 = fmaf(sg, x1, lane_xor4_f(x1));
+  x2 = fmaf(sg, x2, lane_xor4_f(x2)); x3 = fmaf(sg, x3, lane_xor4_f(x3));
+  sg = (r & 8) ? -1.0f : 1.0f;
+  x0 = fmaf(sg, x0, lane_xor8_f(x0)); x1 = fmaf(sg, x1, lane_xor8_f(x1));
+  x2 = fmaf(sg, x2, lane_xor8_f(x2)); x3 = fmaf(sg, x3, lane_xor8_f(x3));
+  {
+    // swap pair (A, B) = (own, partner) on the lower row, (partner, own) on
+    // the upper one: the butterfly is A + (+-1) B on both
+    sg = (r & 16) ? -1.0f : 1.0f;
+    u2 q;
+    q = pair_xor16(__builtin_bit_cast(uint32_t, x0));
+    x0 = fmaf(sg, __builtin_bit_cast(float, (uint32_t)q[1]), __builtin_bit_cast(float, (uint32_t)q[0]));
+    q = pair_xor16(__builtin_bit_cast(uint32_t, x1));
+    x1 = fmaf(sg, __builtin_bit_cast(float, (uint32_t)q[1]), __builtin_bit_cast(float, (uint32_t)q[0]));
+    q = pair_xor16(__builtin_bit_cast(uint32_t, x2));
+    x2 = fmaf(sg, __builtin_bit_cast(float, (uint32_t)q[1]), __builtin_bit_cast(float, (uint32_t)q[0]));
+    q = pair_xor16(__builtin_bit_cast(uint32_t, x3));
+    x3 = fmaf(sg, __builtin_bit_cast(float, (uint32_t)q[1]), __builtin_bit_cast(float, (uint32_t)q[0]));
+  }
+  const float z0 = m0[0] * x0 + m0[1] * x1 + m0[2] * x2 + m0[3] * x3;
+  const float z1 = m1[0] * x0 + m1[1] * x1 + m1[2] * x2 + m1[3] * x3;
+  const float z2 = m2[0] * x0 + m2[1] * x1 + m2[2] * x2 + m2[3] * x3;
+  const float z3 = m3[0] * x0 + m3[1] * x1 + m3[2] * x2 + m3[3] * x3;
+  uint32_t sel = 0x04040404u;  // zero vector: every code 4
+  if (n > 0.f) {
+    const float inv_n = 1.0f / n;
+    sel = code_of(z0 * inv_n) | (code_of(z1 * inv_n) << 8) | (code_of(z2 * inv_n) << 16) |
+          (code_of(z3 * inv_n) << 24);
+  }
+  // selector s of group g: its bit fields in the group's three dwords
+  const int s = r & 7;
+  uint32_t w0 = 0, w1 = 0, w2 = 0;
+  switch (s) {
+    case 0: w0 = sel; break;
+    case 1: w0 = sel << 3; break;
+    case 2: w0 = (sel & 0x03030303u) << 6; w1 = (sel >> 2) & 0x01010101u; break;
+    case 3: w1 = sel << 1; break;
+    case 4: w1 = sel << 4; break;
+    case 5: w1 = (sel & 0x01010101u) << 7; w2 = (sel >> 1) & 0x03030303u; break;
+    case 6: w2 = sel << 2; break;
+    default: w2 = sel << 5; break;
+  }
+  w.x = or_xor4(or_xor2(or_xor1(w0)));
+  w.y = or_xor4(or_xor2(or_xor1(w1)));
+  w.z = or_xor4(or_xor2(or_xor1(w2)));
+}
+
+// Store the record of quantize_lanes32 into one (page, kv head) block:
+// `codes` = its 3,072 code bytes, `norms` = its 64 fp16 norms.  K blocks are
+// slot-ordered (lane 8g writes group g); V blocks are in the matrix-core
+// order of the decode kernels: byte lane b of group g goes to region 4g + b
+// of quad (slot / 4) % 4, chunk slot / 16, byte lane slot % 4 (lane 8g + b
+// writes it).  Works for global and LDS destinations alike.
+__device__ __forceinline__ void place_record(bool is_v, int r, const u3& w, float n, uint8_t* codes,
+                                             uint16_t* norms, int slot) {
+  const int s = r & 7, g = r >> 3;
+  if (!is_v) {
+    if (s == 0) *reinterpret_cast<u3*>(codes + slot * kRec + 12 * g) = w;
+  } else if (s < 4) {
+    const int c = slot >> 4, q = (slot >> 2) & 3, rr = slot & 3;
+    uint8_t* dst = codes + (4 * g + s + 16 * q) * kRec + 12 * c + rr;
+    dst[0] = (uint8_t)(w.x >> (8 * s));
+    dst[4] = (uint8_t)(w.y >> (8 * s));
+    dst[8] = (uint8_t)(w.z >> (8 * s));
+  }
+  if (r == 0) norms[slot] = float_to_half_sat(n);
+}
+
 // ---------------------------------------------------------------------------
 // Unnormalised Walsh-Hadamard transform (Sylvester order) of a 128-vector held
 // by the four lanes of a quad, 32 consecutive coordinates each: lane quarter

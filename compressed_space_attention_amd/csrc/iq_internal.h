@@ -39,10 +39,13 @@ struct DecodePlan {
 DecodePlan plan_decode(int batch, int hkv, int max_seq_len, int num_cus);
 size_t decode_workspace_bytes(int batch, int hq, const DecodePlan& plan);
 
+// k_new / v_new non-null: a decode step, which first appends each sequence's
+// token at position seq_lens[b] - 1 (rows [B][Hkv][128] of kv_dtype).
 hipError_t launch_decode(const CacheView& c, const float* rot, const void* q, int q_dtype,
                          int batch, int hq, const int32_t* block_table, int max_pages,
                          const int32_t* seq_lens, const DecodePlan& plan, float softmax_scale,
-                         float* out, void* workspace, hipStream_t stream);
+                         float* out, void* workspace, const void* k_new, const void* v_new,
+                         int kv_dtype, hipStream_t stream);
 
 // Longest causal key range of one prefill call, in pages (the page ids of the
 // range are staged in LDS): 4096 pages = 262,144 tokens.

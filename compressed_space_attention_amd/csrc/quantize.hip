@@ -110,31 +110,6 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(
 // r % 8 of group r / 8, and the eight lanes of a group OR their bit fields
 // into the group's three dwords.  Loads of the position, the rotation block
 // and the vector go out together, the page id as soon as the position lands.
-__device__ __forceinline__ uint32_t or_xor1(uint32_t v) {
-  return v | (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true);
-}
-__device__ __forceinline__ uint32_t or_xor2(uint32_t v) {
-  return v | (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true);
-}
-__device__ __forceinline__ uint32_t or_xor4(uint32_t v) {
-  const uint32_t t = (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x104, 0xF, 0x5, false);
-  return v | (uint32_t)__builtin_amdgcn_update_dpp((int)t, (int)v, 0x114, 0xF, 0xA, false);
-}
-__device__ __forceinline__ float add_xor4(float v) {
-  const int iv = __builtin_bit_cast(int, v);
-  const int t = __builtin_amdgcn_update_dpp(iv, iv, 0x104, 0xF, 0x5, false);
-  return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(t, iv, 0x114, 0xF, 0xA, false));
-}
-__device__ __forceinline__ float lane_xor4_f(float v) {
-  const int iv = __builtin_bit_cast(int, v);
-  const int t = __builtin_amdgcn_update_dpp(iv, iv, 0x104, 0xF, 0x5, false);
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(t, iv, 0x114, 0xF, 0xA, false));
-}
-__device__ __forceinline__ float lane_xor8_f(float v) {
-  const int iv = __builtin_bit_cast(int, v);
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(iv, iv, 0x128, 0xF, 0xF, false));
-}
-
 template <int DT>
 __global__ __launch_bounds__(256) void quantize_small_kernel(
     const void* __restrict__ k, const void* __restrict__ v, const int32_t* __restrict__ seq_idx,
@@ -180,94 +155,13 @@ __global__ __launch_bounds__(256) void quantize_small_kernel(
   const bool in_table = (unsigned)p < (unsigned)max_pages * kPage;
   const int page = in_table ? block_table[(size_t)si * max_pages + (p >> 6)] : -1;
 
-  // norm: sum of squares over the 32 lanes of the vector
-  float ss = fmaf(x3, x3, fmaf(x2, x2, fmaf(x1, x1, x0 * x0)));
-  ss += quad_xor1(ss);
-  ss += quad_xor2(ss);
-  ss = add_xor4(ss);
-  ss += lane_xor8_f(ss);
-  ss = sum_xor16(ss);
-  const float n = sqrtf(ss);
-
-  // Walsh-Hadamard (unnormalised, Sylvester order): distances 1, 2 in
-  // registers, 4..64 across lanes 1..16 (lower lane keeps y + partner)
-  {
-    const float a0 = x0 + x1, a1 = x0 - x1, a2 = x2 + x3, a3 = x2 - x3;
-    x0 = a0 + a2; x2 = a0 - a2; x1 = a1 + a3; x3 = a1 - a3;
-  }
-  float sg = (r & 1) ? -1.0f : 1.0f;
-  x0 = fmaf(sg, x0, quad_xor1(x0)); x1 = fmaf(sg, x1, quad_xor1(x1));
-  x2 = fmaf(sg, x2, quad_xor1(x2)); x3 = fmaf(sg, x3, quad_xor1(x3));
-  sg = (r & 2) ? -1.0f : 1.0f;
-  x0 = fmaf(sg, x0, quad_xor2(x0)); x1 = fmaf(sg, x1, quad_xor2(x1));
-  x2 = fmaf(sg, x2, quad_xor2(x2)); x3 = fmaf(sg, x3, quad_xor2(x3));
-  sg = (r & 4) ? -1.0f : 1.0f;
-  x0 = fmaf(sg, x0, lane_xor4_f(x0)); x1 = fmaf(sg, x1, lane_xor4_f(x1));
-  x2 = fmaf(sg, x2, lane_xor4_f(x2)); x3 = fmaf(sg, x3, lane_xor4_f(x3));
-  sg = (r & 8) ? -1.0f : 1.0f;
-  x0 = fmaf(sg, x0, lane_xor8_f(x0)); x1 = fmaf(sg, x1, lane_xor8_f(x1));
-  x2 = fmaf(sg, x2, lane_xor8_f(x2)); x3 = fmaf(sg, x3, lane_xor8_f(x3));
-  {
-    // swap pair (A, B) = (own, partner) on the lower row, (partner, own) on
-    // the upper one: the butterfly is A + (+-1) B on both
-    sg = (r & 16) ? -1.0f : 1.0f;
-    u2 q;
-    q = pair_xor16(__builtin_bit_cast(uint32_t, x0));
-    x0 = fmaf(sg, __builtin_bit_cast(float, (uint32_t)q[1]), __builtin_bit_cast(float, (uint32_t)q[0]));
-    q = pair_xor16(__builtin_bit_cast(uint32_t, x1));
-    x1 = fmaf(sg, __builtin_bit_cast(float, (uint32_t)q[1]), __builtin_bit_cast(float, (uint32_t)q[0]));
-    q = pair_xor16(__builtin_bit_cast(uint32_t, x2));
-    x2 = fmaf(sg, __builtin_bit_cast(float, (uint32_t)q[1]), __builtin_bit_cast(float, (uint32_t)q[0]));
-    q = pair_xor16(__builtin_bit_cast(uint32_t, x3));
-    x3 = fmaf(sg, __builtin_bit_cast(float, (uint32_t)q[1]), __builtin_bit_cast(float, (uint32_t)q[0]));
-  }
-  // SO(4) block r, then the scalar quantiser on u = z / n
-  const float z0 = m0[0] * x0 + m0[1] * x1 + m0[2] * x2 + m0[3] * x3;
-  const float z1 = m1[0] * x0 + m1[1] * x1 + m1[2] * x2 + m1[3] * x3;
-  const float z2 = m2[0] * x0 + m2[1] * x1 + m2[2] * x2 + m2[3] * x3;
-  const float z3 = m3[0] * x0 + m3[1] * x1 + m3[2] * x2 + m3[3] * x3;
-  uint32_t sel = 0x04040404u;  // zero vector: level +0.2451 * 0
-  if (n > 0.f) {
-    const float inv_n = 1.0f / n;
-    sel = code_of(z0 * inv_n) | (code_of(z1 * inv_n) << 8) | (code_of(z2 * inv_n) << 16) |
-          (code_of(z3 * inv_n) << 24);
-  }
-  // selector s of group g: its bit fields in the group's three dwords
-  const int s = r & 7, g = r >> 3;
-  uint32_t w0 = 0, w1 = 0, w2 = 0;
-  switch (s) {
-    case 0: w0 = sel; break;
-    case 1: w0 = sel << 3; break;
-    case 2: w0 = (sel & 0x03030303u) << 6; w1 = (sel >> 2) & 0x01010101u; break;
-    case 3: w1 = sel << 1; break;
-    case 4: w1 = sel << 4; break;
-    case 5: w1 = (sel & 0x01010101u) << 7; w2 = (sel >> 1) & 0x03030303u; break;
-    case 6: w2 = sel << 2; break;
-    default: w2 = sel << 5; break;
-  }
-  w0 = or_xor4(or_xor2(or_xor1(w0)));
-  w1 = or_xor4(or_xor2(or_xor1(w1)));
-  w2 = or_xor4(or_xor2(or_xor1(w2)));
-
+  float n;
+  u3 w;
+  quantize_lanes32(x0, x1, x2, x3, m0, m1, m2, m3, r, n, w);
   if ((unsigned)page >= (unsigned)num_pages) return;
-  const int slot = p & 63;
-  const size_t rec = ((size_t)page * hkv + head) * kPage + slot;
-  if (!which) {
-    if (s == 0) *reinterpret_cast<u3*>(k_codes + rec * kRec + 12 * g) = u3{w0, w1, w2};
-    if (r == 0) k_norms[rec] = float_to_half_sat(n);
-    return;
-  }
-  // V: byte lane b of group g goes to region 4g + b (quad q of the slot),
-  // chunk c = slot / 16, byte lane slot % 4 -- lane 8g + b stores it
-  if (s < 4) {
-    uint8_t* blk = v_codes + ((size_t)page * hkv + head) * (kPage * kRec);
-    const int c = slot >> 4, q = (slot >> 2) & 3, rr = slot & 3;
-    uint8_t* dst = blk + (4 * g + s + 16 * q) * kRec + 12 * c + rr;
-    dst[0] = (uint8_t)(w0 >> (8 * s));
-    dst[4] = (uint8_t)(w1 >> (8 * s));
-    dst[8] = (uint8_t)(w2 >> (8 * s));
-  }
-  if (r == 0) v_norms[rec] = float_to_half_sat(n);
+  const size_t blk = (size_t)page * hkv + head;  // (page, kv head) block
+  if (!which) place_record(false, r, w, n, k_codes + blk * (kPage * kRec), k_norms + blk * kPage, p & 63);
+  else place_record(true, r, w, n, v_codes + blk * (kPage * kRec), v_norms + blk * kPage, p & 63);
 }
 
 hipError_t launch_quantize_append(const CacheView& c, const float* rot, const void* k, const void* v,

@@ -59,6 +59,8 @@ def _load():
         "iq_quantize_append": (i32, [cp, vp, vp, vp, i32, i32, vp, vp, vp, i32, vp]),
         "iq_decode_workspace_bytes": (sz, [i32, i32, i32, i32]),
         "iq_decode_attention": (i32, [cp, vp, vp, i32, i32, i32, vp, i32, vp, i32, f32, vp, vp, sz, vp]),
+        "iq_decode_step": (i32, [cp, vp, vp, i32, i32, i32, vp, vp, i32, vp, i32, vp, i32, f32, vp, vp,
+                                 sz, vp]),
         "iq_prefill_workspace_bytes": (sz, [i32, i32, i32, i32]),
         "iq_prefill_attention": (i32, [cp, vp, vp, i32, i32, i32, i32, vp, i32, f32, vp, vp, sz, vp]),
     }
@@ -72,7 +74,7 @@ def _load():
 lib = _load()
 EXPORTED = ("iq_status_string", "iq_version", "iq_rotation_bytes", "iq_rotation_init",
             "iq_quantize_append", "iq_decode_workspace_bytes", "iq_decode_attention",
-            "iq_prefill_workspace_bytes", "iq_prefill_attention")
+            "iq_decode_step", "iq_prefill_workspace_bytes", "iq_prefill_attention")
 
 
 def status_string(status: int) -> str:
@@ -188,6 +190,33 @@ def decode_attention(cache: PagedCache, rot: torch.Tensor, q: torch.Tensor, bloc
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
     _check("iq_decode_attention", lib.iq_decode_attention(
         cache.struct, rot.data_ptr(), _contig(q, "q").data_ptr(), _dtype(q), bsz, hq,
+        _contig(block_table, "block_table").data_ptr(), block_table.shape[-1],
+        _contig(seq_lens, "seq_lens").data_ptr(), int(max_seq_len), float(softmax_scale),
+        out.data_ptr(), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
+    return out
+
+
+def decode_step(cache: PagedCache, rot: torch.Tensor, q: torch.Tensor, k_new: torch.Tensor,
+                v_new: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
+                softmax_scale: float = 0.0, out: torch.Tensor | None = None,
+                workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Append each sequence's current token (k_new, v_new: [B][Hkv][128], at position
+    seq_lens[b] - 1) and run decode attention over all seq_lens[b] tokens, in one call."""
+    bsz, hq, d = q.shape
+    if d != HEAD_DIM:
+        raise ValueError("head dim must be 128")
+    if (k_new.shape != v_new.shape or k_new.dtype != v_new.dtype
+            or tuple(k_new.shape) != (bsz, cache.n_kv_heads, HEAD_DIM)):
+        raise ValueError("k_new and v_new must both be [B][Hkv][128] of one dtype")
+    if out is None:
+        out = torch.empty((bsz, hq, HEAD_DIM), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        nbytes = decode_workspace_bytes(bsz, hq, cache.n_kv_heads, max_seq_len)
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    _check("iq_decode_step", lib.iq_decode_step(
+        cache.struct, rot.data_ptr(), _contig(q, "q").data_ptr(), _dtype(q), bsz, hq,
+        _contig(k_new, "k_new").data_ptr(), _contig(v_new, "v_new").data_ptr(), _dtype(k_new),
         _contig(block_table, "block_table").data_ptr(), block_table.shape[-1],
         _contig(seq_lens, "seq_lens").data_ptr(), int(max_seq_len), float(softmax_scale),
         out.data_ptr(), workspace.data_ptr(), workspace.numel() * workspace.element_size(),

@@ -172,6 +172,30 @@ iq_status iq_decode_attention(const iq_cache *cache, const void *rot_dev, const 
                               size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Decode step = quantise-append of each sequence's current token followed by
+ * decode attention, fused ("RotaryQuant ...", abstract: the quantiser and the
+ * packed-tensor attention form one fused GPU pipeline): the append runs inside
+ * the decode kernel, in the workgroup that reads the sequence's last page, so
+ * a step is two launches instead of three.  Equivalent to iq_quantize_append of the
+ * tokens (seq_idx = b, pos = seq_lens[b] - 1) followed by iq_decode_attention
+ * with the same arguments: the same records are written, and the attention
+ * uses the new token.
+ *
+ * k_new_dev, v_new_dev : [batch][n_kv_heads][128] of kv_dtype (IQ_F32/IQ_BF16/IQ_F16),
+ *                        the K and V rows of the token at position seq_lens[b] - 1.
+ * Other arguments and the workspace are those of iq_decode_attention.  A
+ * sequence with seq_lens[b] = 0 appends nothing and gives zeros.  The table
+ * entry of the new token's page must be a page of the cache (otherwise no
+ * record is written and the attention reads an unspecified page).
+ */
+iq_status iq_decode_step(const iq_cache *cache, const void *rot_dev, const void *q_dev,
+                         int32_t q_dtype, int32_t batch, int32_t n_q_heads, const void *k_new_dev,
+                         const void *v_new_dev, int32_t kv_dtype, const int32_t *block_table_dev,
+                         int32_t max_pages_per_seq, const int32_t *seq_lens_dev,
+                         int32_t max_seq_len, float softmax_scale, float *out_dev,
+                         void *workspace_dev, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Chunked causal prefill attention of one sequence on the packed cache
  * ("RotaryQuant ...", abstract; FreeToken issue #141, Proposed Solution:
  * faster prefill with GQA).  Query i sits at position q_start_pos + i and

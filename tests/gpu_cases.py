@@ -18,7 +18,10 @@ class Scenario:
     """Sequences of given lengths, quantised into one paged cache by the GPU."""
 
     def __init__(self, seed, lens, hkv, dtype="bf16", outliers=False, shuffle=True,
-                 identity=False, extra_pages=2, kv_override=None):
+                 identity=False, extra_pages=2, kv_override=None, hold_last=False):
+        """hold_last: append all but the last token of each sequence; that token's
+        rows are kept in k_last / v_last ([B][Hkv][128], zeros for an empty
+        sequence) for a decode step to append."""
         from compressed_space_attention_amd import isoquant as iq
         self.iq = iq
         self.seed, self.lens, self.hkv, self.dtype = seed, [int(n) for n in lens], hkv, dtype
@@ -42,10 +45,23 @@ class Scenario:
         self.cache = iq.PagedCache(self.num_pages, hkv, device=dev, zero=True)
         self.bt_dev = torch.from_numpy(self.block_table).to(dev)
         self.lens_dev = torch.tensor(self.lens, dtype=torch.int32, device=dev)
-        if n_tok:
-            iq.quantize_append(self.cache, self.rot, self.k.to(dev), self.v.to(dev),
-                               torch.from_numpy(self.seq_idx).to(dev),
-                               torch.from_numpy(self.pos).to(dev), self.bt_dev)
+        keep = np.ones(n_tok, bool)
+        if hold_last:
+            ends = np.cumsum(self.lens) - 1
+            self.k_last = torch.zeros((len(self.lens), hkv, 128), dtype=self.k.dtype)
+            self.v_last = torch.zeros_like(self.k_last)
+            for b, n in enumerate(self.lens):
+                if n:
+                    keep[ends[b]] = False
+                    self.k_last[b] = self.k[ends[b]]
+                    self.v_last[b] = self.v[ends[b]]
+            self.k_last, self.v_last = self.k_last.to(dev), self.v_last.to(dev)
+        if keep.any():
+            sel = torch.from_numpy(np.nonzero(keep)[0])
+            iq.quantize_append(self.cache, self.rot, self.k[sel].contiguous().to(dev),
+                               self.v[sel].contiguous().to(dev),
+                               torch.from_numpy(self.seq_idx[keep]).to(dev),
+                               torch.from_numpy(self.pos[keep]).to(dev), self.bt_dev)
         torch.cuda.synchronize()
 
     def host_cache(self) -> O.PagedCache:

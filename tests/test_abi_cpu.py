@@ -89,6 +89,24 @@ def test_decode_validation():
                                  10 ** 9, None) == -1
 
 
+def _step(c, hq=32, ws=10 ** 9, dtype=1, kv_dtype=1, max_len=1024, max_pages=16, batch=1,
+          k_new=FAKE, v_new=FAKE):
+    return L.iq_decode_step(c, FAKE, FAKE, dtype, batch, hq, k_new, v_new, kv_dtype, FAKE, max_pages,
+                            FAKE, max_len, 0.0, FAKE, FAKE, ws, None)
+
+
+def test_decode_step_validation():
+    c = _cache(hkv=4)
+    assert _step(c, hq=30) == -1
+    assert _step(c, kv_dtype=3) == -1               # bad dtype of the appended rows
+    assert _step(c, k_new=None) == -1
+    assert _step(c, v_new=None) == -1
+    assert _step(c, max_len=2000, max_pages=16) == -1
+    assert _step(c, hq=4 * 17) == -2
+    assert _step(c, ws=16) == -3
+    assert _step(None) == -1
+
+
 def test_decode_workspace_is_monotone_in_context():
     a = iq.decode_workspace_bytes(1, 32, 4, 4096)
     b = iq.decode_workspace_bytes(1, 32, 4, 32768)
