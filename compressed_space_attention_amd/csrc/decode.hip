@@ -157,9 +157,14 @@ __device__ __forceinline__ float norm_at(const u2& n, int r) {
   const uint32_t w = (r < 2) ? n[0] : n[1];
   return half_bits_to_float((r & 1) ? (w >> 16) : (w & 0xFFFFu));
 }
+// x * norm r of the pair, as one mixed-precision FMA (the fp16 norm is read
+// from its half of the register, no separate conversion)
+__device__ __forceinline__ float times_norm(float x, const u2& n, int r) {
+  return __builtin_fmaf(x, norm_at(n, r), 0.0f);
+}
 
 struct PageState {
-  float m_run, l_run;  // running max (log2 units) and partial sum
+  float m_run, l_run;  // running max (log2 units) and partial sum (in units of the frame)
   int rho_e;           // value-norm frame 2^rho_e
   f4 acc[8];           // O'^T tiles: coordinates 32*(lane/16) + 4m + r, head lane%16
 };
@@ -202,6 +207,8 @@ __device__ __forceinline__ void process_page(const PageRegs<PACK8>& cur, PageSta
     s[rb] = acc;
   }
 
+  // Scores in column units: raw * key norm; the log2-scaled score is that
+  // times the lane's column factor `fac` (> 0), applied inside the exponent.
   float sc[NT][4];
   float mp = -INFINITY;
 #pragma unroll
@@ -211,7 +218,7 @@ __device__ __forceinline__ void process_page(const PageRegs<PACK8>& cur, PageSta
     for (int r = 0; r < 4; ++r) {
       // with PACK8, columns 8-15 take the scores of the odd token block
       const float raw = PACK8 ? dpp_f<kRowShr8, 0xC>(s[2 * t][r], s[2 * t + 1][r]) : s[t][r];
-      const float v = raw * (norm_at(cur.kn[t], r) * fac);
+      const float v = times_norm(raw, cur.kn[t], r);
       sc[t][r] = (!MASKED || tok + r < L) ? v : -INFINITY;
       mp = fmaxf(mp, sc[t][r]);
     }
@@ -228,21 +235,23 @@ __device__ __forceinline__ void process_page(const PageRegs<PACK8>& cur, PageSta
   }
   uint32_t vbits = PACK8 ? max_half_bits(vn[0], vn[1])
                          : max(max_half_bits(vn[0], vn[1]), max_half_bits(vn[NT - 2], vn[NT - 1]));
-  mp = column_max<PACK8>(mp);
+  mp = column_max<PACK8>(mp) * fac;
   if (PACK8) vbits = max(vbits, dpp_u<kRowRor8, 0xF>(vbits, vbits));
   vbits = umax_xor32(umax_xor16(vbits));
   const float m_new = fmaxf(st.m_run, mp);        // finite: the page has a valid token
   const float corr = fast_exp2(st.m_run - m_new);  // 0 on the first page
   const int rho_new = frame_exp(vbits, st.rho_e);
+  // the accumulator and the sum are both in units of the frame
   const float rescale = __builtin_amdgcn_ldexpf(corr, rho_new - st.rho_e);
-  const float frame = __builtin_amdgcn_ldexpf(1.0f, rho_new);
   if (__any(rescale != 1.0f)) {
 #pragma unroll
     for (int m = 0; m < 8; ++m) st.acc[m] *= rescale;
-    st.l_run *= corr;
+    st.l_run *= rescale;
   }
   st.m_run = m_new;
   st.rho_e = rho_new;
+  // p' = 2^(s - m + rho): the softmax weight times the frame
+  const float m_shift = m_new - (float)rho_new;
 
   uint32_t pw[NT][2];  // P~ as f16 pairs: tokens r = 0,1 and r = 2,3 of each tile
 #pragma unroll
@@ -250,9 +259,9 @@ __device__ __forceinline__ void process_page(const PageRegs<PACK8>& cur, PageSta
     float p[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      p[r] = fast_exp2(sc[t][r] - m_new);  // masked tokens: 2^-inf = 0
+      p[r] = fast_exp2(__builtin_fmaf(sc[t][r], fac, -m_shift));  // masked tokens: 2^-inf = 0
       st.l_run += p[r];
-      p[r] *= norm_at(vn[t], r) * frame;
+      p[r] = times_norm(p[r], vn[t], r);  // p' * vn < 2: inside the f16 range
     }
     // round to nearest even (round-toward-zero would bias every weight down)
     typedef _Float16 hh2 __attribute__((ext_vector_type(2)));
@@ -648,7 +657,7 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void decode_split_kernel(const i
   }
 
   // ---- merge the eight waves ----
-  float l_col = st.l_run;
+  float l_col = __builtin_amdgcn_ldexpf(st.l_run, -st.rho_e);
   if (PACK8) l_col += dpp_f<kRowRor8, 0xF>(l_col, l_col);
   l_col = sum_xor32(sum_xor16(l_col));
   const float fin = __builtin_amdgcn_ldexpf(a.out_factor, -st.rho_e);
