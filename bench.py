@@ -257,20 +257,28 @@ def run_decode(args):
             "tokens_per_s_per_layer": round(w.batch / t_step, 1),
         },
     }
+    layer0 = layers[0]
+    if not args.no_aux:
+        del layers
+        torch.cuda.empty_cache()
+        result["detail"]["dense_bf16_baseline"] = run_dense_aux(w, lens, bt_np, num_pages, t_decode)
+        log(f"[bench] dense bf16 baseline: {result['detail']['dense_bf16_baseline']}")
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline_decode(args, w, layers[0], bt_np, lens)
+        result["cpu_baseline"] = cpu_baseline_decode(args, w, layer0, bt_np, lens)
     return result
 
 
-def probe_bandwidth(mib: int = 1024, iters: int = 20):
-    """Achievable HBM bandwidth on this GPU, from two plain torch kernels on a
-    buffer far above the 256 MB Infinity Cache: a read-only reduction and a
+def probe_bandwidth(mib: int = 2048, iters: int = 20):
+    """Achievable HBM bandwidth on this GPU, on a buffer far above the 256 MB
+    Infinity Cache: the library's streaming read probe (iq_probe_read) and a
     device-to-device copy (read + write)."""
     import torch
+
+    from compressed_space_attention_amd import isoquant as iq
     n = mib * (1 << 20)
     src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
-    out = torch.empty((), dtype=torch.float32, device="cuda")
+    sink = torch.empty(iq.probe_sink_bytes() // 4, dtype=torch.int32, device="cuda")
 
     def timeit(fn):
         for _ in range(3):
@@ -284,10 +292,77 @@ def probe_bandwidth(mib: int = 1024, iters: int = 20):
         torch.cuda.synchronize()
         return a.elapsed_time(b) / 1e3 / iters
 
-    t_read = timeit(lambda: torch.sum(src, dim=0, out=out))
+    t_read = timeit(lambda: iq.probe_read(src, sink))
     t_copy = timeit(lambda: dst.copy_(src))
     del src, dst
-    return {"bytes": n, "read_gbs": round(n / t_read / 1e9, 1), "copy_gbs": round(2 * n / t_copy / 1e9, 1)}
+    return {"bytes": n, "read_gbs": round(n / t_read / 1e9, 1), "copy_gbs": round(2 * n / t_copy / 1e9, 1),
+            "read_kernel": "probe_read_kernel (16-byte loads, 8 in flight per thread)"}
+
+
+def run_dense_aux(w, lens, bt_np, num_pages, t_packed, ring_bytes=1.0e9, steps=400):
+    """The uncompressed bf16 baseline on the same workload: a ring of bf16
+    layer caches (same paging), the decode call timed the same way as the
+    packed one (graph replay, HIP events on the launch stream)."""
+    import torch
+
+    from compressed_space_attention_amd import isoquant as iq
+    from compressed_space_attention_amd import synth
+    dev = "cuda"
+    block_table = torch.from_numpy(bt_np).to(dev)
+    seq_lens = torch.from_numpy(lens).to(dev)
+    max_len = int(lens.max())
+    dense_bytes = 512 * int(lens.sum()) * w.n_kv_heads          # bf16 K + V rows read per call
+    layer_bytes = num_pages * w.n_kv_heads * 64 * 512
+    ring = max(1, math.ceil(ring_bytes / layer_bytes))
+    caches, qs, outs = [], [], []
+    seq_idx = torch.cat([torch.full((int(n),), b, dtype=torch.int32) for b, n in enumerate(lens)]).to(dev)
+    pos = torch.cat([torch.arange(int(n), dtype=torch.int32) for n in lens]).to(dev)
+    total = int(lens.sum())
+    for i in range(ring):
+        c = iq.DenseCache(num_pages, w.n_kv_heads, device=dev)
+        seed = w.seed * 1000 + 500 + i
+        chunk = 1 << 16
+        for s0 in range(0, total, chunk):
+            e = min(total, s0 + chunk)
+            k = synth.draw_normal_device(seed * 7 + s0, (e - s0, w.n_kv_heads, 128), torch.bfloat16, dev)
+            v = synth.draw_normal_device(seed * 11 + s0, (e - s0, w.n_kv_heads, 128), torch.bfloat16, dev)
+            iq.dense_append(c, k, v, seq_idx[s0:e], pos[s0:e], block_table)
+        caches.append(c)
+        qs.append(synth.draw_normal_device(seed * 19, (w.batch, w.n_q_heads, 128), torch.bfloat16, dev))
+        outs.append(torch.empty((w.batch, w.n_q_heads, 128), dtype=torch.float32, device=dev))
+    ws = torch.empty(max(16, iq.dense_decode_workspace_bytes(w.batch, w.n_q_heads, w.n_kv_heads, max_len)),
+                     dtype=torch.uint8, device=dev)
+
+    def run(n):
+        for i in range(n):
+            j = i % ring
+            iq.dense_decode_attention(caches[j], qs[j], block_table, seq_lens, max_len, out=outs[j],
+                                      workspace=ws)
+
+    run(ring)
+    torch.cuda.synchronize()
+    reps = max(1, steps // ring)
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            run(ring)
+    torch.cuda.current_stream().wait_stream(s)
+    g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    t = a.elapsed_time(b) / 1e3 / (reps * ring)
+    del caches
+    return {"kernel": "dense_decode_split_kernel + decode_merge_kernel (bf16 paged cache)",
+            "decode_call_us": round(t * 1e6, 3), "bf16_bytes_per_call": dense_bytes,
+            "gbs": round(dense_bytes / t / 1e9, 1), "frac_of_hbm_peak": round(dense_bytes / t / 1e9 / HBM_PEAK_GBS, 4),
+            "packed_speedup": round(t / t_packed, 3)}
 
 
 def run_prefill_aux(iters=30):

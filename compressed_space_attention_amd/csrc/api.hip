@@ -39,6 +39,14 @@ iq::CacheView view(const iq_cache* c) {
                        c->num_pages, c->n_kv_heads};
 }
 
+bool dense_ok(const iq_dense_cache* c) {
+  return c && c->k_dev && c->v_dev && c->num_pages > 0 && c->n_kv_heads > 0 && c->n_kv_heads <= 65535;
+}
+
+iq::DenseCacheView dense_view(const iq_dense_cache* c) {
+  return iq::DenseCacheView{c->k_dev, c->v_dev, c->num_pages, c->n_kv_heads};
+}
+
 bool dtype_ok(int32_t d) { return d == IQ_F32 || d == IQ_BF16 || d == IQ_F16; }
 
 bool pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
@@ -154,6 +162,57 @@ iq_status iq_decode_step(const iq_cache* cache, const void* rot_dev, const void*
                                          q_dtype, batch, n_q_heads, block_table_dev, max_pages_per_seq,
                                          seq_lens_dev, plan, resolve_scale(softmax_scale), out_dev,
                                          workspace_dev, k_new_dev, v_new_dev, kv_dtype, stream));
+}
+
+iq_status iq_dense_append(const iq_dense_cache* cache, const void* k_dev, const void* v_dev,
+                          int32_t dtype, int32_t n_tokens, const int32_t* seq_idx_dev,
+                          const int32_t* pos_dev, const int32_t* block_table_dev,
+                          int32_t max_pages_per_seq, hipStream_t stream) {
+  if (!dense_ok(cache) || !dtype_ok(dtype) || n_tokens < 0 || max_pages_per_seq < 1)
+    return IQ_ERR_INVALID_ARG;
+  if (n_tokens == 0) return IQ_OK;
+  if (!k_dev || !v_dev || !seq_idx_dev || !pos_dev || !block_table_dev) return IQ_ERR_INVALID_ARG;
+  return launch_status(iq::launch_dense_append(dense_view(cache), k_dev, v_dev, dtype, n_tokens,
+                                               seq_idx_dev, pos_dev, block_table_dev,
+                                               max_pages_per_seq, stream));
+}
+
+size_t iq_dense_decode_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                                       int32_t max_seq_len) {
+  if (batch < 1 || n_q_heads < 1 || n_kv_heads < 1 || max_seq_len < 0) return 0;
+  const iq::DecodePlan plan = iq::plan_dense_decode(batch, n_kv_heads, max_seq_len, device_cu_count());
+  return iq::decode_workspace_bytes(batch, n_q_heads, plan);
+}
+
+iq_status iq_dense_decode_attention(const iq_dense_cache* cache, const void* q_dev, int32_t q_dtype,
+                                    int32_t batch, int32_t n_q_heads, const int32_t* block_table_dev,
+                                    int32_t max_pages_per_seq, const int32_t* seq_lens_dev,
+                                    int32_t max_seq_len, float softmax_scale, float* out_dev,
+                                    void* workspace_dev, size_t workspace_bytes, hipStream_t stream) {
+  if (!dense_ok(cache) || !q_dev || !dtype_ok(q_dtype) || batch < 1 || batch > 65535 ||
+      n_q_heads < 1 || !block_table_dev || max_pages_per_seq < 1 || !seq_lens_dev ||
+      max_seq_len < 0 || !out_dev || !workspace_dev)
+    return IQ_ERR_INVALID_ARG;
+  if (n_q_heads % cache->n_kv_heads != 0) return IQ_ERR_INVALID_ARG;
+  if ((int64_t)max_seq_len > (int64_t)max_pages_per_seq * IQ_PAGE_TOKENS) return IQ_ERR_INVALID_ARG;
+  if (q_dtype != IQ_BF16 || n_q_heads / cache->n_kv_heads > IQ_MAX_GROUP) return IQ_ERR_UNSUPPORTED;
+  const iq::DecodePlan plan = iq::plan_dense_decode(batch, cache->n_kv_heads, max_seq_len, device_cu_count());
+  if (workspace_bytes < iq::decode_workspace_bytes(batch, n_q_heads, plan)) return IQ_ERR_WORKSPACE;
+  return launch_status(iq::launch_dense_decode(dense_view(cache), q_dev, batch, n_q_heads, block_table_dev,
+                                               max_pages_per_seq, seq_lens_dev, plan,
+                                               resolve_scale(softmax_scale), out_dev, workspace_dev,
+                                               stream));
+}
+
+size_t iq_probe_sink_bytes(void) {
+  return (size_t)iq::kProbeBlocks * iq::kProbeThreads * sizeof(uint32_t);
+}
+
+iq_status iq_probe_read(const void* buf_dev, size_t bytes, void* sink_dev, size_t sink_bytes,
+                        hipStream_t stream) {
+  if (!buf_dev || !sink_dev || bytes == 0 || bytes % 16 != 0 || sink_bytes < iq_probe_sink_bytes())
+    return IQ_ERR_INVALID_ARG;
+  return launch_status(iq::launch_probe_read(buf_dev, bytes, static_cast<uint32_t*>(sink_dev), stream));
 }
 
 size_t iq_prefill_workspace_bytes(int32_t n_q, int32_t n_q_heads, int32_t n_kv_heads,

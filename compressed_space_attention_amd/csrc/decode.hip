@@ -723,7 +723,10 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void decode_split_kernel(const i
 // online merge of coordinates 4*(t%32)..+3 over the splits s = t/32 (mod 8),
 // with all of its loads issued before any result is used; the eight groups
 // then combine through LDS.
+// ROTATE = false: the partials are already in the original space (the
+// uncompressed baseline); the merge only normalises.
 constexpr int kMergeChunk = 16;
+template <bool ROTATE>
 __global__ __launch_bounds__(256, 1) void decode_merge_kernel(const float* __restrict__ rot_all,
                                                            const float* __restrict__ ws_acc,
                                                            const float* __restrict__ ws_ml,
@@ -743,7 +746,7 @@ __global__ __launch_bounds__(256, 1) void decode_merge_kernel(const float* __res
   // this lane's rotation block (wave 0 applies B^T); every thread loads one
   // so that no branch separates these loads from the others
   f4 mt[4];
-  {
+  if (ROTATE) {
     const f4* src = reinterpret_cast<const f4*>(rot_all + (size_t)(hq / group) * kRotFloats +
                                                  ((tid & 63) >> 1) * 16);
 #pragma unroll
@@ -815,6 +818,11 @@ __global__ __launch_bounds__(256, 1) void decode_merge_kernel(const float* __res
   const float inv = (Ls > 0.f) ? 1.0f / Ls : 0.f;  // an empty sequence gives zeros
   o0 *= inv;
   o1 *= inv;
+  if (!ROTATE) {
+    float* out = out_all + ((size_t)b * hq_n + hq) * kD;
+    *reinterpret_cast<float2*>(out + 2 * lane) = make_float2(o0, o1);
+    return;
+  }
   // B^T on block lane/2: this lane holds block coordinates c0 = 2*(lane&1), c0+1.
   const float n0 = quad_xor1(o0), n1 = quad_xor1(o1);
   const bool odd = lane & 1;
@@ -965,8 +973,19 @@ hipError_t launch_decode(const CacheView& c, const float* rot, const void* q, in
 #undef IQ_SPLIT
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_merge_kernel, dim3(hq, batch), dim3(256), 0, stream, rot, a.ws_acc,
-                     a.ws_ml, a.splits, a.hq, a.group, a.out);
+  return launch_decode_merge(true, rot, a.ws_acc, a.ws_ml, plan.splits, batch, hq, a.group, out,
+                             stream);
+}
+
+hipError_t launch_decode_merge(bool rotate, const float* rot, const float* ws_acc, const float* ws_ml,
+                               int splits, int batch, int hq, int group, float* out,
+                               hipStream_t stream) {
+  if (rotate)
+    hipLaunchKernelGGL(decode_merge_kernel<true>, dim3(hq, batch), dim3(256), 0, stream, rot, ws_acc,
+                       ws_ml, splits, hq, group, out);
+  else
+    hipLaunchKernelGGL(decode_merge_kernel<false>, dim3(hq, batch), dim3(256), 0, stream, rot,
+                       ws_acc, ws_ml, splits, hq, group, out);
   return hipGetLastError();
 }
 

@@ -47,6 +47,33 @@ hipError_t launch_decode(const CacheView& c, const float* rot, const void* q, in
                          float* out, void* workspace, const void* k_new, const void* v_new,
                          int kv_dtype, hipStream_t stream);
 
+// Merge of the split partials ([B][Hq][splits] rows of m, l and acc[128]):
+// normalise and, with `rotate`, apply T^T (rot = the rotation buffer).
+hipError_t launch_decode_merge(bool rotate, const float* rot, const float* ws_acc, const float* ws_ml,
+                               int splits, int batch, int hq, int group, float* out,
+                               hipStream_t stream);
+
+// Uncompressed bf16 baseline (dense.hip): paged cache of bf16 rows, K
+// token-major [pages][hkv][64][128], V coordinate-major [pages][hkv][128][64].
+struct DenseCacheView {
+  uint16_t* k;
+  uint16_t* v;
+  int32_t num_pages;
+  int32_t hkv;
+};
+hipError_t launch_dense_append(const DenseCacheView& c, const void* k, const void* v, int dtype,
+                               int n_tokens, const int32_t* seq_idx, const int32_t* pos,
+                               const int32_t* block_table, int max_pages, hipStream_t stream);
+DecodePlan plan_dense_decode(int batch, int hkv, int max_seq_len, int num_cus);
+hipError_t launch_dense_decode(const DenseCacheView& c, const void* q, int batch, int hq,
+                               const int32_t* block_table, int max_pages, const int32_t* seq_lens,
+                               const DecodePlan& plan, float softmax_scale, float* out,
+                               void* workspace, hipStream_t stream);
+// Streaming read of `bytes` (a multiple of 16) at `buf`; one word per thread
+// of the fixed grid goes to `sink`.
+constexpr int kProbeBlocks = 2048, kProbeThreads = 256;
+hipError_t launch_probe_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
+
 // Longest causal key range of one prefill call, in pages (the page ids of the
 // range are staged in LDS): 4096 pages = 262,144 tokens.
 constexpr int kPrefillMaxPages = 4096;

@@ -44,6 +44,15 @@ class IqCacheStruct(ctypes.Structure):
     ]
 
 
+class IqDenseCacheStruct(ctypes.Structure):
+    _fields_ = [
+        ("k_dev", ctypes.c_void_p),
+        ("v_dev", ctypes.c_void_p),
+        ("num_pages", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32),
+    ]
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
@@ -51,6 +60,7 @@ def _load():
     lib = ctypes.CDLL(LIB_PATH)
     vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
     cp = ctypes.POINTER(IqCacheStruct)
+    dp = ctypes.POINTER(IqDenseCacheStruct)
     sigs = {
         "iq_status_string": (ctypes.c_char_p, [i32]),
         "iq_version": (i32, []),
@@ -61,6 +71,11 @@ def _load():
         "iq_decode_attention": (i32, [cp, vp, vp, i32, i32, i32, vp, i32, vp, i32, f32, vp, vp, sz, vp]),
         "iq_decode_step": (i32, [cp, vp, vp, i32, i32, i32, vp, vp, i32, vp, i32, vp, i32, f32, vp, vp,
                                  sz, vp]),
+        "iq_dense_append": (i32, [dp, vp, vp, i32, i32, vp, vp, vp, i32, vp]),
+        "iq_dense_decode_workspace_bytes": (sz, [i32, i32, i32, i32]),
+        "iq_dense_decode_attention": (i32, [dp, vp, i32, i32, i32, vp, i32, vp, i32, f32, vp, vp, sz, vp]),
+        "iq_probe_sink_bytes": (sz, []),
+        "iq_probe_read": (i32, [vp, sz, vp, sz, vp]),
         "iq_prefill_workspace_bytes": (sz, [i32, i32, i32, i32]),
         "iq_prefill_attention": (i32, [cp, vp, vp, i32, i32, i32, i32, vp, i32, f32, vp, vp, sz, vp]),
     }
@@ -74,7 +89,9 @@ def _load():
 lib = _load()
 EXPORTED = ("iq_status_string", "iq_version", "iq_rotation_bytes", "iq_rotation_init",
             "iq_quantize_append", "iq_decode_workspace_bytes", "iq_decode_attention",
-            "iq_decode_step", "iq_prefill_workspace_bytes", "iq_prefill_attention")
+            "iq_decode_step", "iq_prefill_workspace_bytes", "iq_prefill_attention",
+            "iq_dense_append", "iq_dense_decode_workspace_bytes", "iq_dense_decode_attention",
+            "iq_probe_sink_bytes", "iq_probe_read")
 
 
 def status_string(status: int) -> str:
@@ -248,3 +265,77 @@ def prefill_attention(cache: PagedCache, rot: torch.Tensor, q: torch.Tensor, q_s
         _contig(block_table, "block_table").data_ptr(), block_table.shape[-1], float(softmax_scale),
         out.data_ptr(), ws_ptr, ws_bytes, _stream(stream)))
     return out
+
+
+# ---------------------------------------------------------------------------
+# Uncompressed bf16 baseline and the HBM read probe.
+# ---------------------------------------------------------------------------
+class DenseCache:
+    """One layer's bf16 paged cache: k[num_pages][Hkv][64][128] (token-major),
+    v[num_pages][Hkv][128][64] (coordinate-major), bf16 bits as int16."""
+
+    def __init__(self, num_pages: int, n_kv_heads: int, device="cuda", zero: bool = False):
+        alloc = torch.zeros if zero else torch.empty
+        self.num_pages, self.n_kv_heads = int(num_pages), int(n_kv_heads)
+        self.k = alloc((self.num_pages, self.n_kv_heads, PAGE_TOKENS, HEAD_DIM), dtype=torch.int16,
+                       device=device)
+        self.v = alloc((self.num_pages, self.n_kv_heads, HEAD_DIM, PAGE_TOKENS), dtype=torch.int16,
+                       device=device)
+        self._struct = IqDenseCacheStruct(self.k.data_ptr(), self.v.data_ptr(), self.num_pages,
+                                          self.n_kv_heads)
+
+    @property
+    def struct(self):
+        return ctypes.byref(self._struct)
+
+    def nbytes(self) -> int:
+        return 2 * (self.k.numel() + self.v.numel())
+
+
+def dense_append(cache: DenseCache, k: torch.Tensor, v: torch.Tensor, seq_idx: torch.Tensor,
+                 pos: torch.Tensor, block_table: torch.Tensor, stream=None):
+    if k.shape != v.shape or k.dtype != v.dtype or k.dim() != 3 or k.shape[2] != HEAD_DIM:
+        raise ValueError("k and v must both be [n_tokens][Hkv][128] of one dtype")
+    if k.shape[1] != cache.n_kv_heads:
+        raise ValueError("kv head count differs from the cache")
+    _check("iq_dense_append", lib.iq_dense_append(
+        cache.struct, _contig(k, "k").data_ptr(), _contig(v, "v").data_ptr(), _dtype(k), k.shape[0],
+        _ptr(_contig(seq_idx, "seq_idx")), _ptr(_contig(pos, "pos")),
+        _ptr(_contig(block_table, "block_table")), block_table.shape[-1], _stream(stream)))
+
+
+def dense_decode_workspace_bytes(batch: int, n_q_heads: int, n_kv_heads: int, max_seq_len: int) -> int:
+    return int(lib.iq_dense_decode_workspace_bytes(batch, n_q_heads, n_kv_heads, max_seq_len))
+
+
+def dense_decode_attention(cache: DenseCache, q: torch.Tensor, block_table: torch.Tensor,
+                           seq_lens: torch.Tensor, max_seq_len: int, softmax_scale: float = 0.0,
+                           out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                           stream=None) -> torch.Tensor:
+    """q: bf16 [B][Hq][128] -> fp32 [B][Hq][128] over the bf16 cache."""
+    bsz, hq, d = q.shape
+    if d != HEAD_DIM:
+        raise ValueError("head dim must be 128")
+    if out is None:
+        out = torch.empty((bsz, hq, HEAD_DIM), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        nbytes = dense_decode_workspace_bytes(bsz, hq, cache.n_kv_heads, max_seq_len)
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    _check("iq_dense_decode_attention", lib.iq_dense_decode_attention(
+        cache.struct, _contig(q, "q").data_ptr(), _dtype(q), bsz, hq,
+        _contig(block_table, "block_table").data_ptr(), block_table.shape[-1],
+        _contig(seq_lens, "seq_lens").data_ptr(), int(max_seq_len), float(softmax_scale),
+        out.data_ptr(), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
+    return out
+
+
+def probe_sink_bytes() -> int:
+    return int(lib.iq_probe_sink_bytes())
+
+
+def probe_read(buf: torch.Tensor, sink: torch.Tensor, stream=None):
+    """Stream `buf` (contiguous, size a multiple of 16 bytes) once on the GPU."""
+    nbytes = buf.numel() * buf.element_size()
+    _check("iq_probe_read", lib.iq_probe_read(_contig(buf, "buf").data_ptr(), nbytes, sink.data_ptr(),
+                                              sink.numel() * sink.element_size(), _stream(stream)))

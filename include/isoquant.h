@@ -217,6 +217,57 @@ iq_status iq_prefill_attention(const iq_cache *cache, const void *rot_dev, const
                                int32_t max_pages, float softmax_scale, float *out_dev,
                                void *workspace_dev, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Uncompressed baseline ("RotaryQuant ...", abstract: the packed attention
+ * avoids materialising full-precision KV state; this is that state).  A bf16
+ * paged cache and its decode attention on the same paging, split planning
+ * and merge as the packed path, so that the packed cache's byte reduction is
+ * measured as time on the same GPU.  Numerics: bf16 inputs, fp32
+ * accumulation, softmax weights as bf16 high + low parts.
+ *
+ * One layer's bf16 cache, in two caller-owned device arrays (bf16 bits):
+ *   k_dev : uint16 [num_pages][n_kv_heads][64][128]   token-major
+ *   v_dev : uint16 [num_pages][n_kv_heads][128][64]   coordinate-major
+ * Token t of a sequence lives in page block_table[seq][t / 64], slot t % 64.
+ */
+typedef struct {
+  uint16_t *k_dev;
+  uint16_t *v_dev;
+  int32_t num_pages;
+  int32_t n_kv_heads;
+} iq_dense_cache;
+
+/* As iq_quantize_append (same arguments, skip rules and errors): stores the K
+ * and V rows of each token, rounded to bf16 (nearest even), in its slot. */
+iq_status iq_dense_append(const iq_dense_cache *cache, const void *k_dev, const void *v_dev,
+                          int32_t dtype, int32_t n_tokens, const int32_t *seq_idx_dev,
+                          const int32_t *pos_dev, const int32_t *block_table_dev,
+                          int32_t max_pages_per_seq, hipStream_t stream);
+
+/* As iq_decode_attention over the bf16 cache: out = softmax(scale q K^T) V per
+ * query head, fp32 [batch][n_q_heads][128].  q_dtype must be IQ_BF16
+ * (IQ_ERR_UNSUPPORTED otherwise); group limit and workspace rules as there. */
+size_t iq_dense_decode_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                                       int32_t max_seq_len);
+iq_status iq_dense_decode_attention(const iq_dense_cache *cache, const void *q_dev,
+                                    int32_t q_dtype, int32_t batch, int32_t n_q_heads,
+                                    const int32_t *block_table_dev, int32_t max_pages_per_seq,
+                                    const int32_t *seq_lens_dev, int32_t max_seq_len,
+                                    float softmax_scale, float *out_dev, void *workspace_dev,
+                                    size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Measurement aid: the achievable HBM read rate of this GPU, against which the
+ * decode kernels' rates are also reported.  Reads `bytes` (a multiple of 16,
+ * buffer 16-byte aligned) at buf_dev once, with 16-byte loads from a fixed
+ * grid; each thread writes one word (the XOR of what it read) to sink_dev,
+ * which must hold iq_probe_sink_bytes() bytes.  IQ_ERR_INVALID_ARG for null
+ * pointers, a size of 0 or not a multiple of 16, or a short sink.
+ */
+size_t iq_probe_sink_bytes(void);
+iq_status iq_probe_read(const void *buf_dev, size_t bytes, void *sink_dev, size_t sink_bytes,
+                        hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -121,3 +121,23 @@ def test_prefill_validation():
     assert L.iq_prefill_attention(c, FAKE, FAKE, 1, 16, 64, 500, FAKE, 8, 0.0, FAKE, FAKE, 0, None) == -1
     assert L.iq_prefill_attention(c, FAKE, FAKE, 1, 0, 64, 0, FAKE, 8, 0.0, FAKE, FAKE, 0, None) == 0
     assert L.iq_prefill_attention(c, FAKE, FAKE, 9, 16, 64, 0, FAKE, 8, 0.0, FAKE, FAKE, 0, None) == -1
+
+
+def test_dense_and_probe_validation():
+    dc = ctypes.byref(iq.IqDenseCacheStruct(FAKE, FAKE, 8, 4))
+    assert L.iq_dense_append(None, FAKE, FAKE, 1, 4, FAKE, FAKE, FAKE, 8, None) == -1
+    assert L.iq_dense_append(dc, FAKE, FAKE, 7, 4, FAKE, FAKE, FAKE, 8, None) == -1
+    assert L.iq_dense_append(dc, FAKE, FAKE, 1, 0, FAKE, FAKE, FAKE, 8, None) == 0
+
+    def dec(hq=32, dtype=1, ws=10 ** 9, max_len=1024):
+        return L.iq_dense_decode_attention(dc, FAKE, dtype, 1, hq, FAKE, 16, FAKE, max_len, 0.0, FAKE,
+                                           FAKE, ws, None)
+    assert dec(hq=30) == -1
+    assert dec(max_len=2000) == -1
+    assert dec(dtype=0) == -2          # q must be bf16
+    assert dec(hq=4 * 17) == -2
+    assert dec(ws=16) == -3
+    assert iq.probe_sink_bytes() > 0
+    assert L.iq_probe_read(FAKE, 24, FAKE, 10 ** 9, None) == -1        # not a multiple of 16
+    assert L.iq_probe_read(FAKE, 0, FAKE, 10 ** 9, None) == -1
+    assert L.iq_probe_read(FAKE, 64, FAKE, 16, None) == -1             # sink too small

@@ -1,0 +1,129 @@
+"""Uncompressed bf16 baseline (iq_dense_append, iq_dense_decode_attention)
+and the HBM read probe (iq_probe_read), through the C-ABI.
+
+The baseline's decode must match plain fp64 softmax attention on the same
+bf16-rounded q, K and V (the oracle's uncompressed reference) within the
+path's attention tolerance, max_rows max|gpu - ref| / max|ref| <= 1e-3.  Its
+append must place every row exactly (bf16 bits) at the documented offsets.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from compressed_space_attention_amd import synth
+from oracle import isoquant_oracle as O
+from tests.gpu_cases import max_row_error, tol
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+class DenseScenario:
+    def __init__(self, seed, lens, hkv, dtype="bf16", outliers=False, shuffle=True):
+        from compressed_space_attention_amd import isoquant as iq
+        self.iq, self.lens, self.hkv = iq, [int(n) for n in lens], hkv
+        pages = [max(1, -(-n // 64)) for n in self.lens]
+        self.block_table, self.num_pages = synth.block_table(seed + 1, pages, shuffle, 2)
+        n_tok = sum(self.lens)
+        out_ch = synth.outlier_channels(seed + 2, hkv) if outliers else None
+        self.k = synth.kv_vectors(seed + 3, n_tok, hkv, dtype, out_ch)
+        self.v = synth.kv_vectors(seed + 4, n_tok, hkv, dtype, None)
+        self.seq_idx = np.concatenate([np.full(n, b, np.int32) for b, n in enumerate(self.lens)])
+        self.pos = np.concatenate([np.arange(n, dtype=np.int32) for n in self.lens])
+        self.cache = iq.DenseCache(self.num_pages, hkv, zero=True)
+        self.bt_dev = torch.from_numpy(self.block_table).cuda()
+        self.lens_dev = torch.tensor(self.lens, dtype=torch.int32).cuda()
+        if n_tok:
+            iq.dense_append(self.cache, self.k.cuda(), self.v.cuda(), torch.from_numpy(self.seq_idx).cuda(),
+                            torch.from_numpy(self.pos).cuda(), self.bt_dev)
+        torch.cuda.synchronize()
+        self.starts = np.concatenate([[0], np.cumsum(self.lens)])
+
+    def reference(self, q):
+        """fp64 attention over the bf16 rows of each sequence (oracle)."""
+        q = q.to(torch.float64).numpy()
+        bsz, hq, _ = q.shape
+        grp = hq // self.hkv
+        kk = self.k.to(torch.float64).numpy()
+        vv = self.v.to(torch.float64).numpy()
+        out = np.zeros((bsz, hq, 128))
+        for b in range(bsz):
+            s, e = self.starts[b], self.starts[b + 1]
+            for g in range(self.hkv):
+                if e > s:
+                    out[b, g * grp:(g + 1) * grp] = O.reference_attention(
+                        q[b, g * grp:(g + 1) * grp], kk[s:e, g], vv[s:e, g])
+        return out
+
+
+def test_dense_append_layout():
+    s = DenseScenario(900, [1, 70, 128], hkv=3, dtype="f32")
+    k_host = s.cache.k.cpu().numpy().view(np.uint16)
+    v_host = s.cache.v.cpu().numpy().view(np.uint16)
+    kb = s.k.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)  # RNE bf16 of the f32 rows
+    vb = s.v.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    page = s.block_table[s.seq_idx, s.pos // 64]
+    slot = s.pos % 64
+    for h in range(3):
+        assert np.array_equal(k_host[page, h, slot], kb[:, h])
+        assert np.array_equal(v_host[page, h, :, slot], vb[:, h])
+
+
+DENSE_CASES = [
+    # (lens, hkv, hq, outliers)
+    ([2048], 1, 1, False),
+    ([1, 31, 32, 33, 63, 64, 65, 700], 2, 4, True),
+    ([130, 1000, 2100], 4, 32, True),
+    ([640, 0, 33], 2, 32, False),
+]
+
+
+@pytest.mark.parametrize("case", range(len(DENSE_CASES)))
+def test_dense_decode_matches_reference(case):
+    lens, hkv, hq, outl = DENSE_CASES[case]
+    _say(f"dense decode lens={lens} hkv={hkv} hq={hq}")
+    s = DenseScenario(910 + case, lens, hkv=hkv, outliers=outl)
+    q = synth.to_dtype(synth.normal(920 + case, (len(lens), hq, 128)), "bf16")
+    out = s.iq.dense_decode_attention(s.cache, q.cuda(), s.bt_dev, s.lens_dev, max(lens)).cpu().numpy()
+    ref = s.reference(q)
+    err = max_row_error(out, ref)
+    _say(f"  max row error {err:.3e}")
+    assert np.all(np.isfinite(out))
+    assert err <= tol()
+    for b, n in enumerate(lens):
+        if n == 0:
+            assert np.all(out[b] == 0)
+
+
+def test_dense_decode_ignores_unwritten_slots():
+    """Slots past the length hold NaN bit patterns: the result must not see them."""
+    s = DenseScenario(930, [40, 100], hkv=2)
+    s.cache.k.fill_(-1)  # 0xFFFF: bf16 NaN everywhere ...
+    s.cache.v.fill_(-1)
+    s.iq.dense_append(s.cache, s.k.cuda(), s.v.cuda(), torch.from_numpy(s.seq_idx).cuda(),
+                      torch.from_numpy(s.pos).cuda(), s.bt_dev)  # ... except the written slots
+    q = synth.to_dtype(synth.normal(931, (2, 8, 128)), "bf16")
+    out = s.iq.dense_decode_attention(s.cache, q.cuda(), s.bt_dev, s.lens_dev, 100).cpu().numpy()
+    assert np.all(np.isfinite(out))
+    assert max_row_error(out, s.reference(q)) <= tol()
+
+
+def test_probe_reads_every_word_once():
+    from compressed_space_attention_amd import isoquant as iq
+    # above eight grid strides (8 x 2048 x 256 x 16 B) and not a multiple of
+    # one: both the unrolled loop and the tail loop run
+    n = (80 << 20) + 48
+    host = np.random.default_rng(5).integers(0, 2 ** 32, size=n // 4, dtype=np.uint32)
+    buf = torch.from_numpy(host.view(np.int32)).cuda()
+    sink = torch.zeros(iq.probe_sink_bytes() // 4, dtype=torch.int32, device="cuda")
+    iq.probe_read(buf, sink)
+    torch.cuda.synchronize()
+    got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+    assert got == np.bitwise_xor.reduce(host)
