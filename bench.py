@@ -50,6 +50,10 @@ def parse():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (20 times): the known-size "
                          "reference that scales the HBM byte counters")
+    ap.add_argument("--write-traffic-record", metavar="DIR", default=None,
+                    help="no GPU work: read the FETCH_SIZE / WRITE_SIZE counter CSVs of the decode "
+                         "call and of the copy calibration under DIR (pmc_FETCH_SIZE, pmc_WRITE_SIZE, "
+                         "cal_FETCH_SIZE, cal_WRITE_SIZE) and write the traffic record under profiles/")
     ap.add_argument("--no-aux", action="store_true",
                     help="skip the chunked-prefill side measurements (append, prefill)")
     return ap.parse_args()
@@ -464,6 +468,77 @@ def cpu_baseline_decode(args, w, layer, bt_np, lens):
     }
 
 
+TRAFFIC_SOURCES = ["compressed_space_attention_amd/csrc/decode.hip",
+                   "compressed_space_attention_amd/csrc/iq_device.h",
+                   "compressed_space_attention_amd/csrc/iq_internal.h"]
+
+
+def write_traffic_record(root: str, workload: str = "gqa_decode_32k_32q4kv", calib_mib: int = 512):
+    """HBM bytes per decode attention call from rocprofv3 counter CSVs: the
+    median FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the decode-only
+    split kernel and of the merge kernel, each scaled by what the counter
+    reads for a plain copy of known size."""
+    import csv
+    import glob
+    import hashlib
+
+    def medians(sub):
+        vals = {}
+        for f in glob.glob(os.path.join(root, sub, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return {k: sorted(v)[len(v) // 2] for k, v in vals.items()}
+
+    def pick(table, pred):
+        hits = [v for k, v in table.items() if pred(k)]
+        if len(hits) != 1:
+            raise SystemExit(f"expected one kernel, found {len(hits)}")
+        return hits[0]
+
+    split = lambda k: "decode_split_kernel<" in k and k.split("<")[1].split(">")[0].endswith("false") \
+        and "dense" not in k
+    merge = lambda k: "decode_merge_kernel<true>" in k
+    copy = lambda k: "copy" in k.lower()
+    fetch, write = medians("pmc_FETCH_SIZE"), medians("pmc_WRITE_SIZE")
+    cf, cw = medians("cal_FETCH_SIZE"), medians("cal_WRITE_SIZE")
+    moved_kib = calib_mib * 1024
+    f_fac = moved_kib / pick(cf, copy)
+    w_fac = moved_kib / pick(cw, copy)
+    counters = {"decode_split_kernel (decode only)": {"FETCH_SIZE": pick(fetch, split), "WRITE_SIZE": pick(write, split)},
+                "decode_merge_kernel": {"FETCH_SIZE": pick(fetch, merge), "WRITE_SIZE": pick(write, merge)}}
+    total_kib = sum(c["FETCH_SIZE"] * f_fac + c["WRITE_SIZE"] * w_fac for c in counters.values())
+    h = hashlib.sha256()
+    for src in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, src), "rb") as f:
+            h.update(f.read())
+    rec = {
+        "kernel": "decode_split_kernel + decode_merge_kernel (one decode attention call)",
+        "workload": workload,
+        "sources_sha256": h.hexdigest(),
+        "sources": TRAFFIC_SOURCES,
+        "counters_kib_per_dispatch": counters,
+        "copy_calibration": {"bytes_per_launch": calib_mib << 20, "FETCH_SIZE_kib": pick(cf, copy),
+                             "WRITE_SIZE_kib": pick(cw, copy), "fetch_factor": round(f_fac, 4),
+                             "write_factor": round(w_fac, 4)},
+        "traffic_bytes_per_call": int(round(total_kib * 1024)),
+        "commands": [
+            "rocprofv3 --pmc FETCH_SIZE --kernel-include-regex 'decode_split|decode_merge' -d DIR/pmc_FETCH_SIZE "
+            "-o d --output-format csv -- python3 bench.py --steps 40 --warmup 8 --no-cpu-baseline --no-graph --no-aux",
+            "rocprofv3 --pmc WRITE_SIZE --kernel-include-regex 'decode_split|decode_merge' -d DIR/pmc_WRITE_SIZE "
+            "-o d --output-format csv -- python3 bench.py --steps 40 --warmup 8 --no-cpu-baseline --no-graph --no-aux",
+            "rocprofv3 --pmc FETCH_SIZE -d DIR/cal_FETCH_SIZE -o c --output-format csv -- python3 bench.py "
+            "--copy-calibration 512",
+            "rocprofv3 --pmc WRITE_SIZE -d DIR/cal_WRITE_SIZE -o c --output-format csv -- python3 bench.py "
+            "--copy-calibration 512",
+            "python3 bench.py --write-traffic-record DIR",
+        ],
+    }
+    out = os.path.join(ROOT, "profiles", "decode_gqa_decode_32k_traffic.json")
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps({"traffic_bytes_per_call": rec["traffic_bytes_per_call"], "record": out}))
+
+
 def copy_calibration(mib: int, reps: int = 20):
     """A plain device-to-device copy of known size, for scaling FETCH_SIZE and
     WRITE_SIZE: each launch reads and writes exactly mib MiB."""
@@ -479,6 +554,9 @@ def copy_calibration(mib: int, reps: int = 20):
 
 def main():
     args = parse()
+    if args.write_traffic_record:
+        write_traffic_record(args.write_traffic_record)
+        return
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
         return
