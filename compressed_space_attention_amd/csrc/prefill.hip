@@ -11,11 +11,13 @@
 //   S^T[token][row] = K^[token] . Q'[row]     (v_mfma_f32_16x16x32_f16, Q' hi+lo)
 //   O'^T[dim][row] += V^T[dim][token] P~[row][token]   (16x16x32)
 //
-// Work decomposition (gfx950): one workgroup of 4 waves per CU owns 128 rows
-// of one kv head (32 rows = two row blocks per wave, so every K^ and V^
-// fragment read from LDS feeds four matrix-core products; LDS read bandwidth,
-// not the matrix cores, bounds a design with more, narrower waves) and walks
-// the pages up to its causal limit.  Per page:
+// Work decomposition (gfx950): one workgroup per CU owns 128 rows of one kv
+// head and walks the pages up to its causal limit.  Two shapes (RB = row
+// blocks of 16 per wave): RB = 2, four waves of 32 rows (every K^ and V^
+// fragment read from LDS feeds four matrix-core products, one wave per SIMD);
+// RB = 1, eight waves of 16 rows (two waves per SIMD, so one wave's softmax
+// and unpacking run while the other's products occupy the matrix core, at
+// twice the LDS reads per product).  Per page:
 //   * raw pages arrive by direct-to-LDS loads three pages ahead (each wave
 //     loads exactly the 12-byte groups it will unpack, so no wave waits for
 //     another's loads);
@@ -27,20 +29,20 @@
 //     masked.
 // The page ids of the whole causal range are staged in LDS once.
 #include <math.h>
+#include <stdlib.h>
 
 #include "iq_device.h"
 #include "iq_internal.h"
 
 namespace iq {
 
-constexpr int kPfWaves = 4;
-constexpr int kPfThreads = 64 * kPfWaves;
-constexpr int kRowsPerTile = 32 * kPfWaves;  // 128 rows = queries x group heads
+constexpr int kRowsPerTile = 128;  // rows = queries x group heads
 constexpr int kKStride = 136;   // halves per K^ row (128 + 8 pad)
 constexpr int kVStride = 68;    // halves per V^T row (64 + 4 pad: 16 rows hit 16 distinct 8-byte bank slots)
-constexpr int kRawWave = 2048;  // raw bytes per wave and page: K then V, 64 lanes x 16 B each
-constexpr int kRawSlot = kPfWaves * kRawWave + 256;  // + the page's K and V norms
+constexpr int kRawPage = 8192;  // raw code bytes of a page in LDS: 512 groups of 12 B at a 16 B stride
+constexpr int kRawSlot = kRawPage + 256;  // + the page's K and V norms
 constexpr int kRawSlots = 3;
+template <int RB> constexpr int pf_waves() { return 8 / RB; }
 
 struct PrefillArgs {
   const uint8_t* k_codes;
@@ -58,12 +60,19 @@ struct PrefillArgs {
   float* out;
 };
 
+// Direct-to-LDS loads, issued from inline asm so that the compiler does not
+// track them: it cannot tell which raw slot a load writes and would otherwise
+// wait for every outstanding load (the two pages in flight) before each LDS
+// read of a raw page.  Every read of loaded LDS data is preceded by an
+// explicit s_waitcnt on this kernel's issue order instead.  No register
+// outputs: the address is read at issue, the destination is LDS at m0.
 typedef __attribute__((address_space(3))) void* pf_lds_ptr;
 __device__ __forceinline__ void pf_dma(const void* g, void* lds, int size) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(pf_lds_ptr)lds);
   if (size == 12)
-    __builtin_amdgcn_global_load_lds(g, (pf_lds_ptr)lds, 12, 0, 0);
+    asm volatile("global_load_lds_dwordx3 %0, off" ::"v"(g), "{m0}"(m0) : "memory");
   else
-    __builtin_amdgcn_global_load_lds(g, (pf_lds_ptr)lds, 4, 0, 0);
+    asm volatile("global_load_lds_dword %0, off" ::"v"(g), "{m0}"(m0) : "memory");
 }
 // s_waitcnt vmcnt(n) (gfx9 encoding, other counters left alone)
 #define IQ_PF_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
@@ -74,62 +83,103 @@ struct PfMaskTag {
   static constexpr bool value = M;
 };
 
+// x * norm r of the pair as one mixed-precision FMA (fp16 operand in place)
+__device__ __forceinline__ float times_norm2(float x, const u2& n, int r);
 __device__ __forceinline__ float norm_at2(const u2& n, int r) {
   const uint32_t w = (r < 2) ? n[0] : n[1];
   return half_bits_to_float((r & 1) ? (w >> 16) : (w & 0xFFFFu));
 }
+__device__ __forceinline__ float times_norm2(float x, const u2& n, int r) {
+  return __builtin_fmaf(x, norm_at2(n, r), 0.0f);
+}
 
-// Raw loads of one page into a slot: wave w brings the K records of tokens
+// Raw loads of one page into a slot (each wave loads exactly the 12-byte
+// groups it unpacks).  Four waves: wave w brings the K records of tokens
 // 16w..16w+15 (lane l: token 16w + l/4, group l%4 -- 768 contiguous bytes)
-// and chunk w of every V region (lane l: region l); wave 0 also the K norms
-// (lanes 0-31) and V norms (lanes 32-63).
-__device__ __forceinline__ void pf_issue(const PrefillArgs& a, int page_id, int g, int wave, int lane,
-                                         uint8_t* slot) {
+// and chunk w of every V region (lane l: region l).  Eight waves: lanes 0-31
+// the K records of tokens 8w..8w+7, lanes 32-63 chunk w/2 of V regions
+// 32(w%2) .. +31.  Wave 0 also brings the K norms (lanes 0-31) and V norms
+// (lanes 32-63).  Returns the number of loads issued.
+template <int W>
+__device__ __forceinline__ int pf_issue(const PrefillArgs& a, int page_id, int g, int wave, int lane,
+                                        uint8_t* slot) {
   // an id outside the cache (a table that breaks the contract) is clamped into
   // it, so a bad table gives wrong numbers, never an out-of-bounds read
   const uint32_t page = min((uint32_t)page_id, (uint32_t)a.num_pages - 1u);
   const size_t base = ((size_t)page * a.hkv + g) * kPage;
-  uint8_t* dst = slot + wave * kRawWave;
-  pf_dma(a.k_codes + base * kRec + 768 * wave + 12 * lane, dst, 12);
-  pf_dma(a.v_codes + (base + lane) * kRec + 12 * wave, dst + 1024, 12);
+  uint8_t* dst = slot + wave * (kRawPage / W);
+  if (W == 4) {
+    pf_dma(a.k_codes + base * kRec + 768 * wave + 12 * lane, dst, 12);
+    pf_dma(a.v_codes + (base + lane) * kRec + 12 * wave, dst + 1024, 12);
+  } else {
+    const uint8_t* src = lane < 32 ? a.k_codes + base * kRec + 384 * wave + 12 * lane
+                                   : a.v_codes + (base + 32 * (wave & 1) + (lane - 32)) * kRec +
+                                         12 * (wave >> 1);
+    pf_dma(src, dst, 12);
+  }
   if (wave == 0) {
     const uint16_t* nb = (lane < 32 ? a.k_norms : a.v_norms) + base + 2 * (lane & 31);
-    pf_dma(nb, slot + kPfWaves * kRawWave, 4);
+    pf_dma(nb, slot + kRawPage, 4);
   }
+  return (W == 4 ? 2 : 1) + (wave == 0 ? 1 : 0);
 }
 
-// Unpack this thread's two groups of a raw page (a K group and a V chunk)
-// into the f16 buffers.
-__device__ __forceinline__ void pf_unpack(const uint8_t* slot, int wave, int lane, _Float16* sk,
-                                          _Float16* sv, uint16_t* snorm) {
-  const uint8_t* raw = slot + wave * kRawWave + 16 * lane;
-  const u3 ck = *reinterpret_cast<const u3*>(raw);
-  const u3 cv = *reinterpret_cast<const u3*>(raw + 1024);
+// One K group (token tok, coordinates 32j..32j+31) into the f16 K^ buffer.
+__device__ __forceinline__ void pf_unpack_k(const u3& ck, int tok, int j, _Float16* sk) {
   uint32_t z[8];
   group_to_selectors(ck.x, ck.y, ck.z, z);
-  {
-    const int tok = 16 * wave + (lane >> 2), j = lane & 3;
-    u4* dst = reinterpret_cast<u4*>(sk + tok * kKStride + 32 * j);
+  u4* dst = reinterpret_cast<u4*>(sk + tok * kKStride + 32 * j);
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const u2 d0 = selector_to_f16(z[2 * kk]), d1 = selector_to_f16(z[2 * kk + 1]);
-      dst[kk] = u4{d0[0], d0[1], d1[0], d1[1]};
-    }
+  for (int kk = 0; kk < 4; ++kk) {
+    const u2 d0 = selector_to_f16(z[2 * kk]), d1 = selector_to_f16(z[2 * kk + 1]);
+    dst[kk] = u4{d0[0], d0[1], d1[0], d1[1]};
   }
+}
+// Chunk c of V region `region` = (n, q) = (region % 16, region / 16): tokens
+// 16c + 4q + r of coordinate rows 16m + n, into the f16 V^T buffer.
+__device__ __forceinline__ void pf_unpack_v(const u3& cv, int region, int c, _Float16* sv) {
+  uint32_t z[8];
   group_to_selectors(cv.x, cv.y, cv.z, z);
-  {
-    // chunk c = wave of region (n, q): tokens 16c + 4q + r of coordinate row 16m + n
-    const int n = lane & 15, q = lane >> 4;
+  const int n = region & 15, q = region >> 4;
 #pragma unroll
-    for (int m = 0; m < 8; ++m)
-      *reinterpret_cast<u2*>(sv + (16 * m + n) * kVStride + 16 * wave + 4 * q) = selector_to_f16(z[m]);
-  }
-  if (wave == 0)
-    reinterpret_cast<uint32_t*>(snorm)[lane] =
-        reinterpret_cast<const uint32_t*>(slot + kPfWaves * kRawWave)[lane];
+  for (int m = 0; m < 8; ++m)
+    *reinterpret_cast<u2*>(sv + (16 * m + n) * kVStride + 16 * c + 4 * q) = selector_to_f16(z[m]);
 }
 
-__global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(PrefillArgs a) {
+// Unpack this thread's groups of a raw page (four waves: a K group and a V
+// chunk; eight waves: one of the two) into the f16 buffers.
+template <int W>
+__device__ __forceinline__ void pf_unpack(const uint8_t* slot, int wave, int lane, _Float16* sk,
+                                          _Float16* sv, uint16_t* snorm) {
+  const uint8_t* raw = slot + wave * (kRawPage / W) + 16 * lane;
+  if (W == 4) {
+    pf_unpack_k(*reinterpret_cast<const u3*>(raw), 16 * wave + (lane >> 2), lane & 3, sk);
+    pf_unpack_v(*reinterpret_cast<const u3*>(raw + 1024), lane, wave, sv);
+  } else if (lane < 32) {
+    pf_unpack_k(*reinterpret_cast<const u3*>(raw), 8 * wave + (lane >> 2), lane & 3, sk);
+  } else {
+    pf_unpack_v(*reinterpret_cast<const u3*>(raw), 32 * (wave & 1) + (lane - 32), wave >> 1, sv);
+  }
+  if (wave == 0)
+    reinterpret_cast<uint32_t*>(snorm)[lane] = reinterpret_cast<const uint32_t*>(slot + kRawPage)[lane];
+}
+
+// s_waitcnt vmcnt(n) for a count known only at run time (0..7)
+__device__ __forceinline__ void pf_wait_vm(int n) {
+  switch (n) {
+    case 0: IQ_PF_WAIT_VM(0); break;
+    case 1: IQ_PF_WAIT_VM(1); break;
+    case 2: IQ_PF_WAIT_VM(2); break;
+    case 3: IQ_PF_WAIT_VM(3); break;
+    case 4: IQ_PF_WAIT_VM(4); break;
+    case 5: IQ_PF_WAIT_VM(5); break;
+    default: IQ_PF_WAIT_VM(6); break;
+  }
+}
+
+template <int RB>
+__global__ __launch_bounds__(64 * pf_waves<RB>(), 1) void prefill_kernel(PrefillArgs a) {
+  constexpr int W = pf_waves<RB>();
   const int g = blockIdx.x, tile = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -148,19 +198,19 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t s_norm[2][2 * kPage];      // K | V norms
   __shared__ int s_pt[kPrefillMaxPages];                                       // 16,384 B
 
-  // ---- page ids of the causal range (wave w: entries 1024w .. 1024w+1023) ----
-  for (int i = 0; i < 16; ++i) {
-    const int e0 = 1024 * wave + 64 * i;
+  // ---- page ids of the causal range (wave w: a 1/W share of the entries) ----
+  for (int i = 0; i < kPrefillMaxPages / (64 * W); ++i) {
+    const int e0 = (kPrefillMaxPages / W) * wave + 64 * i;
     if (e0 < n_pages && e0 + lane < n_pages) pf_dma(a.block_table + e0 + lane, &s_pt[e0], 4);
   }
 
-  // ---- this wave's 32 rows: Q' = T q (lane: row 16cb + col, quarter jq) ----
-  h8 qhi[2][4], qlo[2][4];
-  float fac[2];
-  int qpos[2], qi_row[2], head_row[2];
+  // ---- this wave's 16 RB rows: Q' = T q (lane: row 16cb + col, quarter jq) ----
+  h8 qhi[RB][4], qlo[RB][4];
+  float fac[RB];
+  int qpos[RB], qi_row[RB], head_row[RB];
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
-    const int row = 32 * wave + 16 * cb + col;
+  for (int cb = 0; cb < RB; ++cb) {
+    const int row = 16 * RB * wave + 16 * cb + col;
     const int qi = q0 + row / a.group;
     const int h = row % a.group;
     qi_row[cb] = qi;
@@ -201,26 +251,25 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(PrefillArgs a) {
   __builtin_amdgcn_s_waitcnt(0);  // page-id loads landed (all counters)
   __syncthreads();
 
-  const int per_page = (wave == 0) ? 3 : 2;  // raw loads this wave issues per page
+  // raw loads this wave issues per page
+  const int per_page = (W == 4 ? 2 : 1) + (wave == 0 ? 1 : 0);
   // first three pages in flight, the first unpacked
-  for (int p = 0; p < 3 && p < n_pages; ++p) pf_issue(a, s_pt[p], g, wave, lane, s_raw[p]);
-  {
-    const int after = per_page * (min(n_pages, 3) - 1);
-    if (after == 0) IQ_PF_WAIT_VM(0);
-    else if (after == 2) IQ_PF_WAIT_VM(2);
-    else if (after == 3) IQ_PF_WAIT_VM(3);
-    else if (after == 4) IQ_PF_WAIT_VM(4);
-    else IQ_PF_WAIT_VM(6);
-    pf_unpack(s_raw[0], wave, lane, s_k[0], s_v[0], s_norm[0]);
-  }
+  for (int p = 0; p < 3 && p < n_pages; ++p) pf_issue<W>(a, s_pt[p], g, wave, lane, s_raw[p]);
+  pf_wait_vm(per_page * (min(n_pages, 3) - 1));
+  pf_unpack<W>(s_raw[0], wave, lane, s_k[0], s_v[0], s_norm[0]);
   __builtin_amdgcn_s_waitcnt(kPfWaitLgkm0);
   __builtin_amdgcn_s_barrier();
 
-  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+  float m_run[RB], l_run[RB];
   int rho_e = 0;
-  f4 acc[2][8];
+  f4 acc[RB][8];
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb)
+  for (int cb = 0; cb < RB; ++cb) {
+    m_run[cb] = -INFINITY;
+    l_run[cb] = 0.f;
+  }
+#pragma unroll
+  for (int cb = 0; cb < RB; ++cb)
 #pragma unroll
     for (int m = 0; m < 8; ++m) acc[cb][m] = f4{0.f, 0.f, 0.f, 0.f};
 
@@ -229,21 +278,21 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(PrefillArgs a) {
   auto page_step = [&](int pg, auto masked_tag) {
     constexpr bool MASKED = decltype(masked_tag)::value;
     const int f = pg & 1;
-    if (pg + 3 < n_pages) pf_issue(a, s_pt[pg + 3], g, wave, lane, s_raw[pg % 3]);
+    if (pg + 3 < n_pages) pf_issue<W>(a, s_pt[pg + 3], g, wave, lane, s_raw[pg % 3]);
 
     // ---- S^T tiles [token block tb][row block cb]: each K^ fragment feeds
-    // both row blocks (hi and lo parts of Q') ----
+    // every row block (hi and lo parts of Q') ----
     const _Float16* sk = s_k[f];
-    f4 s[4][2];
+    f4 s[4][RB];
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
-      s[tb][0] = f4{0.f, 0.f, 0.f, 0.f};
-      s[tb][1] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int cb = 0; cb < RB; ++cb) s[tb][cb] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         const h8 av = *reinterpret_cast<const h8*>(sk + (16 * tb + col) * kKStride + 32 * jq + 8 * kk);
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb) {
+        for (int cb = 0; cb < RB; ++cb) {
           s[tb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, qhi[cb][kk], s[tb][cb], 0, 0, 0);
           s[tb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, qlo[cb][kk], s[tb][cb], 0, 0, 0);
         }
@@ -253,13 +302,8 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(PrefillArgs a) {
     // (independent of them: VALU and LDS work between matrix-core issues) ----
     if (pg + 1 < n_pages) {
       // loads of this wave still allowed in flight: those of pages pg+2, pg+3
-      const int after = per_page * min(2, n_pages - 2 - pg);
-      if (after == 0) IQ_PF_WAIT_VM(0);
-      else if (after == 2) IQ_PF_WAIT_VM(2);
-      else if (after == 3) IQ_PF_WAIT_VM(3);
-      else if (after == 4) IQ_PF_WAIT_VM(4);
-      else IQ_PF_WAIT_VM(6);
-      pf_unpack(s_raw[(pg + 1) % 3], wave, lane, s_k[f ^ 1], s_v[f ^ 1], s_norm[f ^ 1]);
+      pf_wait_vm(per_page * min(2, n_pages - 2 - pg));
+      pf_unpack<W>(s_raw[(pg + 1) % 3], wave, lane, s_k[f ^ 1], s_v[f ^ 1], s_norm[f ^ 1]);
     }
 
     const uint16_t* nrm = s_norm[f];
@@ -282,13 +326,28 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(PrefillArgs a) {
     }
     vbits = umax_xor32(umax_xor16(vbits));
     const int rho_new = (vbits == 0) ? rho_e : 15 - (int)((vbits >> 10) & 0x1Fu);
-    const float frame = __builtin_amdgcn_ldexpf(1.0f, rho_new);
     const int tok_base = pg * kPage + 4 * jq;
 
-    // ---- online softmax per row (column of S^T) ----
-    h8 pb[2][2];  // [token pair tp][row block cb]
+    // value norms of the page; on a masked page, slots at or past the end of
+    // the appended chunk were never written and read as zero
+    u2 vnp[4];
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
+    for (int tb = 0; tb < 4; ++tb) {
+      vnp[tb] = *reinterpret_cast<const u2*>(nrm + kPage + 16 * tb + 4 * jq);
+      if (MASKED) {
+        const int t0 = tok_base + 16 * tb;
+        vnp[tb][0] &= (t0 < kv_end ? 0xFFFFu : 0u) | (t0 + 1 < kv_end ? 0xFFFF0000u : 0u);
+        vnp[tb][1] &= (t0 + 2 < kv_end ? 0xFFFFu : 0u) | (t0 + 3 < kv_end ? 0xFFFF0000u : 0u);
+      }
+    }
+
+    // ---- online softmax per row (column of S^T) ----
+    // Scores in row units (raw x key norm); the log2-scaled score is that
+    // times the row factor fac[cb] > 0, applied inside the exponent.  The
+    // accumulator and the sum are in units of the value-norm frame 2^rho.
+    h8 pb[2][RB];  // [token pair tp][row block cb]
+#pragma unroll
+    for (int cb = 0; cb < RB; ++cb) {
       float sv[4][4];
       float mp = -INFINITY;
 #pragma unroll
@@ -296,7 +355,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(PrefillArgs a) {
         const u2 kn = *reinterpret_cast<const u2*>(nrm + 16 * tb + 4 * jq);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float v = s[tb][cb][r] * (norm_at2(kn, r) * fac[cb]);
+          const float v = times_norm2(s[tb][cb][r], kn, r);
           if (MASKED) {
             const int tok = tok_base + 16 * tb + r;
             sv[tb][r] = (tok <= qpos[cb] && tok < kv_end) ? v : -INFINITY;
@@ -306,7 +365,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(PrefillArgs a) {
           mp = fmaxf(mp, sv[tb][r]);
         }
       }
-      mp = max_xor32(max_xor16(mp));
+      mp = max_xor32(max_xor16(mp)) * fac[cb];
       const float m_new = fmaxf(m_run[cb], mp);
       // a row whose keys on this page are all masked keeps its state
       const bool live = !MASKED || m_new != -INFINITY;
@@ -316,17 +375,17 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int m = 0; m < 8; ++m) acc[cb][m] *= rescale;
       }
-      l_run[cb] *= corr;
+      l_run[cb] *= rescale;
       m_run[cb] = m_new;
+      const float m_shift = m_new - (float)rho_new;  // p' = 2^(s - m + rho)
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) {
-        const u2 vn = *reinterpret_cast<const u2*>(nrm + kPage + 16 * tb + 4 * jq);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           // masked scores: 2^-inf = 0
-          const float p = (!MASKED || live) ? fast_exp2(sv[tb][r] - m_new) : 0.f;
+          const float p = (!MASKED || live) ? fast_exp2(__builtin_fmaf(sv[tb][r], fac[cb], -m_shift)) : 0.f;
           l_run[cb] += p;
-          pb[tb >> 1][cb][4 * (tb & 1) + r] = (_Float16)(p * (norm_at2(vn, r) * frame));
+          pb[tb >> 1][cb][4 * (tb & 1) + r] = (_Float16)times_norm2(p, vnp[tb], r);  // p' vn < 2
         }
       }
     }
@@ -343,7 +402,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(PrefillArgs a) {
         const h4 v1 = *reinterpret_cast<const h4*>(vr + 16);
         const h8 av = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb)
+        for (int cb = 0; cb < RB; ++cb)
           acc[cb][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pb[tp][cb], acc[cb][m], 0, 0, 0);
       }
     }
@@ -358,9 +417,9 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(PrefillArgs a) {
   // ---- epilogue: normalise, rotate back (B^T then H / sqrt(d)), store ----
   const float* rot = a.rot + (size_t)g * kRotFloats;
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
-    const float l = sum_xor32(sum_xor16(l_run[cb]));
-    const float scale = (l > 0.f) ? __builtin_amdgcn_ldexpf(a.out_factor, -rho_e) / l : 0.f;
+  for (int cb = 0; cb < RB; ++cb) {
+    const float l = sum_xor32(sum_xor16(l_run[cb]));  // in units of the frame, as acc
+    const float scale = (l > 0.f) ? a.out_factor / l : 0.f;
     float o[32], y[32];
 #pragma unroll
     for (int k = 0; k < 32; ++k) o[k] = acc[cb][k >> 2][k & 3] * scale;
@@ -429,7 +488,14 @@ hipError_t launch_prefill(const CacheView& c, const float* rot, const void* q, i
   a.score_factor = (float)((double)softmax_scale * log2e / (128.0 * (double)kLevelScale));
   a.out_factor = (float)(1.0 / (sqrt(128.0) * (double)kLevelScale));
   a.out = out;
-  hipLaunchKernelGGL(prefill_kernel, dim3(c.hkv, plan.row_tiles), dim3(kPfThreads), 0, stream, a);
+  int rb = 1;
+  if (const char* env = getenv("IQ_PREFILL_WAVES")) rb = atoi(env) == 4 ? 2 : 1;
+  if (rb == 2)
+    hipLaunchKernelGGL(prefill_kernel<2>, dim3(c.hkv, plan.row_tiles), dim3(64 * pf_waves<2>()), 0,
+                       stream, a);
+  else
+    hipLaunchKernelGGL(prefill_kernel<1>, dim3(c.hkv, plan.row_tiles), dim3(64 * pf_waves<1>()), 0,
+                       stream, a);
   return hipGetLastError();
 }
 

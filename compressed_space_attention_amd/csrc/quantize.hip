@@ -21,32 +21,43 @@ namespace iq {
 // latency-oriented kernel.
 constexpr long long kSmallAppendVectors = 16384;
 
+// Grid (token blocks of 64, kv heads, K|V): a workgroup quantises 64
+// consecutive input tokens of one kv head and one tensor, a quad of lanes per
+// vector.  When the 64 tokens are one whole page of one sequence (positions
+// p0 .. p0 + 63, p0 a multiple of 64: a prefill chunk), their K records and
+// norms land contiguously, and the V block -- whose matrix-core order
+// interleaves the page's tokens -- is assembled in LDS and written as 3,072
+// contiguous bytes; otherwise each quad stores its own record.
 // The first 14 argument dwords (everything the first loads need) are
 // preloaded into SGPRs; the cache pointers follow from the argument segment.
 template <int DT>
 __global__ __launch_bounds__(256) void quantize_append_kernel(
     const void* __restrict__ k, const void* __restrict__ v, const int32_t* __restrict__ seq_idx,
-    const int32_t* __restrict__ pos, const int32_t* __restrict__ block_table, long long n_vec,
+    const int32_t* __restrict__ pos, const int32_t* __restrict__ block_table, int n_tok,
     int hkv, int max_pages, const float* __restrict__ rot, int num_pages,
     uint8_t* __restrict__ k_codes, uint16_t* __restrict__ k_norms, uint8_t* __restrict__ v_codes,
     uint16_t* __restrict__ v_norms) {
-  const long long gv = (long long)blockIdx.x * 64 + (threadIdx.x >> 2);
-  const int j = threadIdx.x & 3;
-  if (gv >= 2 * n_vec) return;  // whole quads leave together
-  const int which = gv >= n_vec;
-  const long long vi = gv - (which ? n_vec : 0);  // token * hkv + head
-  const int tok = (int)(vi / hkv);
-  const int head = (int)(vi - (long long)tok * hkv);
+  const int tl = threadIdx.x >> 2, j = threadIdx.x & 3;
+  const int head = blockIdx.y, which = blockIdx.z;
+  const int t0 = blockIdx.x * 64;
+  const int tok = t0 + tl;
+  const bool valid = tok < n_tok;
+  __shared__ __attribute__((aligned(16))) uint8_t s_v[kPage * kRec];  // the page's V block
 
   // The destination is looked up while the vector is transformed: position
   // and sequence first, then the page id, all before the arithmetic.
-  const int p = pos[tok];
-  const int si = seq_idx[tok];
+  const int p = valid ? pos[tok] : -1;
+  const int si = valid ? seq_idx[tok] : -1;
+  const int p0 = pos[t0], s0 = seq_idx[t0];
   float x[32];
-  load32(which ? v : k, (size_t)vi * kD + 32 * j, DT, x);
+  const size_t vi = (size_t)(valid ? tok : t0) * hkv + head;
+  load32(which ? v : k, vi * kD + 32 * j, DT, x);
   // a position outside the table or a page id outside the cache is skipped
   const bool in_table = (unsigned)p < (unsigned)max_pages * kPage;
   const int page = in_table ? block_table[(size_t)si * max_pages + (p >> 6)] : -1;
+  const bool stored = (unsigned)page < (unsigned)num_pages;
+  // one whole page: every token in order, all stored (uniform for the workgroup)
+  const bool whole = __syncthreads_and(valid && si == s0 && p == p0 + tl && (p0 & 63) == 0 && stored);
 
   float ss0 = 0.f, ss1 = 0.f, ss2 = 0.f, ss3 = 0.f;
 #pragma unroll
@@ -80,27 +91,37 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(
   u3 w;
   selectors_to_group(sel, w.x, w.y, w.z);
 
-  if ((unsigned)page >= (unsigned)num_pages) return;
   const int slot = p & 63;
   const size_t rec = ((size_t)page * hkv + head) * kPage + slot;
   if (!which) {
-    *reinterpret_cast<u3*>(k_codes + rec * kRec + 12 * j) = w;
-    if (j == 0) k_norms[rec] = float_to_half_sat(n);
+    if (stored) {
+      *reinterpret_cast<u3*>(k_codes + rec * kRec + 12 * j) = w;
+      if (j == 0) k_norms[rec] = float_to_half_sat(n);
+    }
     return;
   }
   // V: byte lane b of this group goes to region n = 4j + b (quad q of the
   // slot), chunk c = slot / 16, byte lane r = slot % 4 -- the order in which
   // the decode matrix cores consume V (see the cache layout in isoquant.h).
-  uint8_t* blk = v_codes + ((size_t)page * hkv + head) * (kPage * kRec);
   const int c = slot >> 4, q = (slot >> 2) & 3, r = slot & 3;
+  uint8_t* blk = whole ? s_v : v_codes + ((size_t)page * hkv + head) * (kPage * kRec);
+  if (stored) {
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    uint8_t* dst = blk + (4 * j + b + 16 * q) * kRec + 12 * c + r;
-    dst[0] = (uint8_t)(w.x >> (8 * b));
-    dst[4] = (uint8_t)(w.y >> (8 * b));
-    dst[8] = (uint8_t)(w.z >> (8 * b));
+    for (int b = 0; b < 4; ++b) {
+      uint8_t* dst = blk + (4 * j + b + 16 * q) * kRec + 12 * c + r;
+      dst[0] = (uint8_t)(w.x >> (8 * b));
+      dst[4] = (uint8_t)(w.y >> (8 * b));
+      dst[8] = (uint8_t)(w.z >> (8 * b));
+    }
+    if (j == 0) v_norms[rec] = float_to_half_sat(n);
   }
-  if (j == 0) v_norms[rec] = float_to_half_sat(n);
+  if (whole) {
+    __syncthreads();
+    if (threadIdx.x < kPage * kRec / 16) {
+      uint8_t* gblk = v_codes + ((size_t)page * hkv + head) * (kPage * kRec);
+      reinterpret_cast<u4*>(gblk)[threadIdx.x] = reinterpret_cast<const u4*>(s_v)[threadIdx.x];
+    }
+  }
 }
 
 // Few vectors (a decode step appends one token per sequence): the latency
@@ -182,11 +203,10 @@ hipError_t launch_quantize_append(const CacheView& c, const float* rot, const vo
 #undef IQ_SMALL
     return hipGetLastError();
   }
-  const long long blocks = (2 * n_vec + 63) / 64;
-#define IQ_QUADS(DT)                                                                             \
-  hipLaunchKernelGGL(quantize_append_kernel<DT>, dim3((unsigned)blocks), dim3(256), 0, stream, k, \
-                     v, seq_idx, pos, block_table, n_vec, c.hkv, max_pages, rot, c.num_pages,     \
-                     c.k_codes,                                                                   \
+  const dim3 grid((unsigned)((n_tokens + 63) / 64), (unsigned)c.hkv, 2);
+#define IQ_QUADS(DT)                                                                              \
+  hipLaunchKernelGGL(quantize_append_kernel<DT>, grid, dim3(256), 0, stream, k, v, seq_idx, pos,   \
+                     block_table, n_tokens, c.hkv, max_pages, rot, c.num_pages, c.k_codes,          \
                      c.k_norms, c.v_codes, c.v_norms)
   if (dtype == 0) IQ_QUADS(0);
   else if (dtype == 1) IQ_QUADS(1);

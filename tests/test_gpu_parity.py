@@ -205,3 +205,20 @@ def test_prefill_matches_oracle(case):
     err = max_row_error(out[rows], ref)
     _say(f"  max row error {err:.3e}")
     assert err <= tol()
+
+
+def test_prefill_ignores_unwritten_slots():
+    """Slots past the appended chunk hold NaN norm patterns (an uninitialised
+    cache): the masked tail of the last page must not reach the output."""
+    total, n_q = 700, 60
+    s = Scenario(650, [total], hkv=2, dtype="bf16")
+    bt = s.block_table[0]
+    last_page, first_unwritten = bt[(total - 1) // 64], total % 64
+    for norms in (s.cache.k_norms, s.cache.v_norms):
+        norms[last_page, :, first_unwritten:] = -1  # 0xFFFF: fp16 NaN
+    q = synth.to_dtype(synth.normal(651, (n_q, 16, 128)), "bf16")
+    out = s.iq.prefill_attention(s.cache, s.rot, q.cuda(), total - n_q, s.bt_dev[0]).cpu().numpy()
+    assert np.all(np.isfinite(out))
+    rows = np.array([0, 17, n_q - 1])
+    ref = O.prefill_attention(s.host_cache(), s.blocks, q.double().numpy(), total - n_q, bt, rows=rows)
+    assert max_row_error(out[rows], ref) <= tol()
