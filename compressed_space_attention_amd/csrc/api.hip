@@ -247,4 +247,35 @@ iq_status iq_prefill_attention(const iq_cache* cache, const void* rot_dev, const
                                           stream));
 }
 
+iq_status iq_prefill_attention_varlen(const iq_cache* cache, const void* rot_dev, const void* q_dev,
+                                      int32_t q_dtype, int32_t batch, int32_t n_q_heads, int32_t total_q,
+                                      const int32_t* cu_q_dev, const int32_t* q_start_dev,
+                                      int32_t max_q_per_seq, int32_t max_kv_len,
+                                      const int32_t* block_table_dev, int32_t max_pages_per_seq,
+                                      float softmax_scale, float* out_dev, void* workspace_dev,
+                                      size_t workspace_bytes, hipStream_t stream) {
+  if (!cache_ok(cache) || !rot_dev || !dtype_ok(q_dtype) || batch < 1 || batch > 65535 ||
+      n_q_heads < 1 || total_q < 0 || max_q_per_seq < 0 || max_kv_len < 0 ||
+      max_pages_per_seq < 1 || !block_table_dev || !cu_q_dev || !q_start_dev)
+    return IQ_ERR_INVALID_ARG;
+  if (n_q_heads % cache->n_kv_heads != 0) return IQ_ERR_INVALID_ARG;
+  if ((int64_t)max_q_per_seq > (int64_t)max_kv_len || max_q_per_seq > total_q) return IQ_ERR_INVALID_ARG;
+  if ((int64_t)max_kv_len > (int64_t)max_pages_per_seq * IQ_PAGE_TOKENS) return IQ_ERR_INVALID_ARG;
+  if (total_q == 0 || max_q_per_seq == 0) return IQ_OK;
+  if (!q_dev || !out_dev) return IQ_ERR_INVALID_ARG;
+  const int group = n_q_heads / cache->n_kv_heads;
+  if (!pow2(group) || group > 128 || cache->n_kv_heads > 65535) return IQ_ERR_UNSUPPORTED;
+  if ((int64_t)max_kv_len > (int64_t)iq::kPrefillMaxPages * IQ_PAGE_TOKENS) return IQ_ERR_UNSUPPORTED;
+  const iq::PrefillPlan plan =
+      iq::plan_prefill(max_q_per_seq, n_q_heads, cache->n_kv_heads, 0, device_cu_count());
+  if (plan.row_tiles > 65535) return IQ_ERR_UNSUPPORTED;
+  const size_t need = iq::prefill_workspace_bytes(total_q, n_q_heads, plan);
+  if (need > 0 && (!workspace_dev || workspace_bytes < need)) return IQ_ERR_WORKSPACE;
+  return launch_status(iq::launch_prefill_varlen(view(cache), reinterpret_cast<const float*>(rot_dev),
+                                                 q_dev, q_dtype, batch, total_q, n_q_heads, cu_q_dev, 0,
+                                                 q_start_dev, block_table_dev, max_pages_per_seq, plan,
+                                                 resolve_scale(softmax_scale), out_dev, workspace_dev,
+                                                 stream));
+}
+
 }  // extern "C"

@@ -88,5 +88,14 @@ hipError_t launch_prefill(const CacheView& c, const float* rot, const void* q, i
                           int n_q, int hq, int q_start, const int32_t* block_table,
                           int max_pages, const PrefillPlan& plan, float softmax_scale,
                           float* out, void* workspace, hipStream_t stream);
+// Several sequences in one launch: sequence b's queries are rows cu_q[b] ..
+// cu_q[b+1]-1 (device), its first at position q_starts[b] (device), its
+// block-table row block_table + b * max_pages; plan.row_tiles covers the
+// longest query count.
+hipError_t launch_prefill_varlen(const CacheView& c, const float* rot, const void* q, int q_dtype,
+                                 int batch, int n_q, int hq, const int32_t* cu_q, int q_start,
+                                 const int32_t* q_starts, const int32_t* block_table, int max_pages,
+                                 const PrefillPlan& plan, float softmax_scale, float* out,
+                                 void* workspace, hipStream_t stream);
 
 }  // namespace iq

@@ -55,6 +55,12 @@ struct PrefillArgs {
   int q_dtype;
   int n_q, hq, group, q_start;
   const int32_t* block_table;
+  // Batched variable-length form (null for one sequence): sequence b = blockIdx.z
+  // owns query rows cu_q[b] .. cu_q[b+1]-1 of q and out, its first query sits at
+  // q_starts[b], and its block-table row is block_table + b * max_pages.
+  const int32_t* cu_q;
+  const int32_t* q_starts;
+  int max_pages;
   float score_factor;  // softmax_scale * log2(e) / (128 * alpha)
   float out_factor;    // 1 / (sqrt(128) * alpha)
   float* out;
@@ -180,17 +186,29 @@ __device__ __forceinline__ void pf_wait_vm(int n) {
 template <int RB>
 __global__ __launch_bounds__(64 * pf_waves<RB>(), 1) void prefill_kernel(PrefillArgs a) {
   constexpr int W = pf_waves<RB>();
-  const int g = blockIdx.x, tile = blockIdx.y;
+  const int g = blockIdx.x, tile = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, jq = lane >> 4;
+  // this sequence's queries: rows row0 .. row0 + n_q - 1 of q and out
+  int n_q = a.n_q, q_start = a.q_start, row0 = 0;
+  const int32_t* btab = a.block_table;
+  if (a.cu_q) {
+    row0 = a.cu_q[b];
+    n_q = a.cu_q[b + 1] - row0;
+    q_start = a.q_starts[b];
+    btab += (size_t)b * a.max_pages;
+  }
   const int qpt = kRowsPerTile / a.group;  // queries per tile
   const int q0 = tile * qpt;
-  const int q_last = min(a.n_q, q0 + qpt) - 1;
-  const int kv_end = a.q_start + q_last + 1;
-  const int n_pages = (kv_end + kPage - 1) / kPage;
+  if (q0 >= n_q) return;  // a tile past this sequence's queries (uniform)
+  const int q_last = min(n_q, q0 + qpt) - 1;
+  const int kv_end = q_start + q_last + 1;
+  // (a range beyond the table or the staging limit breaks the contract: never
+  // read past either)
+  const int n_pages = min((kv_end + kPage - 1) / kPage, min(a.max_pages, kPrefillMaxPages));
   // pages entirely at or before the smallest query position need no mask
-  const int n_full = min(n_pages, (a.q_start + q0 + 1) / kPage);
+  const int n_full = min(n_pages, (q_start + q0 + 1) / kPage);
 
   __shared__ __attribute__((aligned(16))) _Float16 s_k[2][kPage * kKStride];  // 34,816 B
   __shared__ __attribute__((aligned(16))) _Float16 s_v[2][kD * kVStride];     // 36,864 B
@@ -201,7 +219,7 @@ __global__ __launch_bounds__(64 * pf_waves<RB>(), 1) void prefill_kernel(Prefill
   // ---- page ids of the causal range (wave w: a 1/W share of the entries) ----
   for (int i = 0; i < kPrefillMaxPages / (64 * W); ++i) {
     const int e0 = (kPrefillMaxPages / W) * wave + 64 * i;
-    if (e0 < n_pages && e0 + lane < n_pages) pf_dma(a.block_table + e0 + lane, &s_pt[e0], 4);
+    if (e0 < n_pages && e0 + lane < n_pages) pf_dma(btab + e0 + lane, &s_pt[e0], 4);
   }
 
   // ---- this wave's 16 RB rows: Q' = T q (lane: row 16cb + col, quarter jq) ----
@@ -215,10 +233,10 @@ __global__ __launch_bounds__(64 * pf_waves<RB>(), 1) void prefill_kernel(Prefill
     const int h = row % a.group;
     qi_row[cb] = qi;
     head_row[cb] = h;
-    qpos[cb] = (qi < a.n_q) ? a.q_start + qi : 0x7FFFFFFF;
+    qpos[cb] = (qi < n_q) ? q_start + qi : 0x7FFFFFFF;
     float x[32];
-    if (qi < a.n_q) {
-      load32(a.q, ((size_t)qi * a.hq + (size_t)g * a.group + h) * kD + 32 * jq, a.q_dtype, x);
+    if (qi < n_q) {
+      load32(a.q, ((size_t)(row0 + qi) * a.hq + (size_t)g * a.group + h) * kD + 32 * jq, a.q_dtype, x);
     } else {
 #pragma unroll
       for (int i = 0; i < 32; ++i) x[i] = 0.f;
@@ -433,9 +451,9 @@ __global__ __launch_bounds__(64 * pf_waves<RB>(), 1) void prefill_kernel(Prefill
                         r3[c] * o[4 * bb + 3];
     }
     wht128_spread<16, 32>(y, jq);
-    if (qi_row[cb] < a.n_q) {
+    if (qi_row[cb] < n_q) {
       f4* dst = reinterpret_cast<f4*>(a.out +
-                                      ((size_t)qi_row[cb] * a.hq + (size_t)g * a.group + head_row[cb]) * kD +
+                                      ((size_t)(row0 + qi_row[cb]) * a.hq + (size_t)g * a.group + head_row[cb]) * kD +
                                       32 * jq);
       const float nrm = 0.08838834764831845f;  // 1/sqrt(128)
 #pragma unroll
@@ -467,7 +485,15 @@ hipError_t launch_prefill(const CacheView& c, const float* rot, const void* q, i
                           int hq, int q_start, const int32_t* block_table, int max_pages,
                           const PrefillPlan& plan, float softmax_scale, float* out, void* workspace,
                           hipStream_t stream) {
-  (void)max_pages;
+  return launch_prefill_varlen(c, rot, q, q_dtype, 1, n_q, hq, nullptr, q_start, nullptr, block_table,
+                               max_pages, plan, softmax_scale, out, workspace, stream);
+}
+
+hipError_t launch_prefill_varlen(const CacheView& c, const float* rot, const void* q, int q_dtype,
+                                 int batch, int n_q, int hq, const int32_t* cu_q, int q_start,
+                                 const int32_t* q_starts, const int32_t* block_table, int max_pages,
+                                 const PrefillPlan& plan, float softmax_scale, float* out,
+                                 void* workspace, hipStream_t stream) {
   (void)workspace;
   PrefillArgs a;
   a.k_codes = c.k_codes;
@@ -484,18 +510,20 @@ hipError_t launch_prefill(const CacheView& c, const float* rot, const void* q, i
   a.group = hq / c.hkv;
   a.q_start = q_start;
   a.block_table = block_table;
+  a.cu_q = cu_q;
+  a.q_starts = q_starts;
+  a.max_pages = max_pages;
   const double log2e = 1.4426950408889634;
   a.score_factor = (float)((double)softmax_scale * log2e / (128.0 * (double)kLevelScale));
   a.out_factor = (float)(1.0 / (sqrt(128.0) * (double)kLevelScale));
   a.out = out;
   int rb = 1;
   if (const char* env = getenv("IQ_PREFILL_WAVES")) rb = atoi(env) == 4 ? 2 : 1;
+  const dim3 grid(c.hkv, plan.row_tiles, batch);
   if (rb == 2)
-    hipLaunchKernelGGL(prefill_kernel<2>, dim3(c.hkv, plan.row_tiles), dim3(64 * pf_waves<2>()), 0,
-                       stream, a);
+    hipLaunchKernelGGL(prefill_kernel<2>, grid, dim3(64 * pf_waves<2>()), 0, stream, a);
   else
-    hipLaunchKernelGGL(prefill_kernel<1>, dim3(c.hkv, plan.row_tiles), dim3(64 * pf_waves<1>()), 0,
-                       stream, a);
+    hipLaunchKernelGGL(prefill_kernel<1>, grid, dim3(64 * pf_waves<1>()), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -77,6 +77,8 @@ def _load():
         "iq_probe_sink_bytes": (sz, []),
         "iq_probe_read": (i32, [vp, sz, vp, sz, vp]),
         "iq_prefill_workspace_bytes": (sz, [i32, i32, i32, i32]),
+        "iq_prefill_attention_varlen": (i32, [cp, vp, vp, i32, i32, i32, i32, vp, vp, i32, i32, vp, i32, f32,
+                                              vp, vp, sz, vp]),
         "iq_prefill_attention": (i32, [cp, vp, vp, i32, i32, i32, i32, vp, i32, f32, vp, vp, sz, vp]),
     }
     for name, (res, args) in sigs.items():
@@ -90,6 +92,7 @@ lib = _load()
 EXPORTED = ("iq_status_string", "iq_version", "iq_rotation_bytes", "iq_rotation_init",
             "iq_quantize_append", "iq_decode_workspace_bytes", "iq_decode_attention",
             "iq_decode_step", "iq_prefill_workspace_bytes", "iq_prefill_attention",
+            "iq_prefill_attention_varlen",
             "iq_dense_append", "iq_dense_decode_workspace_bytes", "iq_dense_decode_attention",
             "iq_probe_sink_bytes", "iq_probe_read")
 
@@ -264,6 +267,26 @@ def prefill_attention(cache: PagedCache, rot: torch.Tensor, q: torch.Tensor, q_s
         cache.struct, rot.data_ptr(), _contig(q, "q").data_ptr(), _dtype(q), n_q, hq, int(q_start),
         _contig(block_table, "block_table").data_ptr(), block_table.shape[-1], float(softmax_scale),
         out.data_ptr(), ws_ptr, ws_bytes, _stream(stream)))
+    return out
+
+
+def prefill_attention_varlen(cache: PagedCache, rot: torch.Tensor, q: torch.Tensor, cu_q: torch.Tensor,
+                             q_start: torch.Tensor, block_table: torch.Tensor, max_q_per_seq: int,
+                             max_kv_len: int, softmax_scale: float = 0.0,
+                             out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """q: [total_q][Hq][128]; cu_q int32[B+1], q_start int32[B] (device);
+    block_table int32[B][max_pages] -> fp32 [total_q][Hq][128]."""
+    total_q, hq, d = q.shape
+    if d != HEAD_DIM:
+        raise ValueError("head dim must be 128")
+    bsz = cu_q.numel() - 1
+    if out is None:
+        out = torch.zeros((total_q, hq, HEAD_DIM), dtype=torch.float32, device=q.device)
+    _check("iq_prefill_attention_varlen", lib.iq_prefill_attention_varlen(
+        cache.struct, rot.data_ptr(), _contig(q, "q").data_ptr(), _dtype(q), bsz, hq, total_q,
+        _contig(cu_q, "cu_q").data_ptr(), _contig(q_start, "q_start").data_ptr(), int(max_q_per_seq),
+        int(max_kv_len), _contig(block_table, "block_table").data_ptr(), block_table.shape[-1],
+        float(softmax_scale), out.data_ptr(), None, 0, _stream(stream)))
     return out
 
 

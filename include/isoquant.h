@@ -218,6 +218,33 @@ iq_status iq_prefill_attention(const iq_cache *cache, const void *rot_dev, const
                                void *workspace_dev, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Batched variable-length chunked prefill: several sequences' query chunks in
+ * one launch (the same attention as iq_prefill_attention for each sequence;
+ * "RotaryQuant ...", abstract, and FreeToken issue #141, Proposed Solution).
+ *
+ * q_dev          : [total_q][n_q_heads][128] of q_dtype; sequence b's queries are
+ *                  rows cu_q[b] .. cu_q[b+1]-1, query i of it at position
+ *                  q_start[b] + i, attending that sequence's keys 0 .. q_start[b] + i.
+ * cu_q_dev       : int32[batch + 1], nondecreasing, cu_q[0] = 0, cu_q[batch] <= total_q.
+ * q_start_dev    : int32[batch].
+ * max_q_per_seq  : host bound of cu_q[b+1] - cu_q[b] (sizes the grid).
+ * max_kv_len     : host bound of q_start[b] + cu_q[b+1] - cu_q[b].
+ * block_table_dev: int32[batch][max_pages_per_seq].
+ * out_dev        : float[total_q][n_q_heads][128], original space; rows of no
+ *                  sequence are not written.
+ * Unsupported: max_kv_len > 262,144, or n_q_heads / n_kv_heads not a power of two
+ * up to 128.  Device data beyond the bounds breaks the contract (wrong results,
+ * never reads outside the table or the cache).  total_q = 0 is a no-op.
+ */
+iq_status iq_prefill_attention_varlen(const iq_cache *cache, const void *rot_dev, const void *q_dev,
+                                      int32_t q_dtype, int32_t batch, int32_t n_q_heads,
+                                      int32_t total_q, const int32_t *cu_q_dev,
+                                      const int32_t *q_start_dev, int32_t max_q_per_seq,
+                                      int32_t max_kv_len, const int32_t *block_table_dev,
+                                      int32_t max_pages_per_seq, float softmax_scale, float *out_dev,
+                                      void *workspace_dev, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Uncompressed baseline ("RotaryQuant ...", abstract: the packed attention
  * avoids materialising full-precision KV state; this is that state).  A bf16
  * paged cache and its decode attention on the same paging, split planning

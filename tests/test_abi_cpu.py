@@ -141,3 +141,20 @@ def test_dense_and_probe_validation():
     assert L.iq_probe_read(FAKE, 24, FAKE, 10 ** 9, None) == -1        # not a multiple of 16
     assert L.iq_probe_read(FAKE, 0, FAKE, 10 ** 9, None) == -1
     assert L.iq_probe_read(FAKE, 64, FAKE, 16, None) == -1             # sink too small
+
+
+def test_prefill_varlen_validation():
+    c = _cache(hkv=8)
+
+    def call(batch=2, hq=64, total_q=100, max_q=60, max_kv=500, max_pages=8, dtype=1, cu=FAKE):
+        return L.iq_prefill_attention_varlen(c, FAKE, FAKE, dtype, batch, hq, total_q, cu, FAKE, max_q,
+                                             max_kv, FAKE, max_pages, 0.0, FAKE, None, 0, None)
+    assert call(hq=60) == -1                 # Hq not a multiple of Hkv
+    assert call(hq=24) == -2                 # group 3 not a power of two
+    assert call(max_kv=600) == -1            # beyond the block table
+    assert call(max_q=120) == -1             # more queries per sequence than in total
+    assert call(max_q=600, max_kv=500) == -1  # more queries than keys
+    assert call(cu=None) == -1
+    assert call(batch=0) == -1
+    assert call(total_q=0, max_q=0) == 0     # no-op
+    assert call(max_kv=300000, max_pages=5000) == -2   # beyond the staging limit

@@ -222,3 +222,39 @@ def test_prefill_ignores_unwritten_slots():
     rows = np.array([0, 17, n_q - 1])
     ref = O.prefill_attention(s.host_cache(), s.blocks, q.double().numpy(), total - n_q, bt, rows=rows)
     assert max_row_error(out[rows], ref) <= tol()
+
+
+VARLEN_CASES = [
+    # (cache lengths, queries per sequence (the last ones), hkv, hq)
+    ([700, 130, 2048, 64], [77, 0, 128, 64], 2, 16),
+    ([300, 1000, 65], [300, 1, 65], 1, 1),
+    ([900, 640], [200, 640], 2, 64),
+]
+
+
+@pytest.mark.parametrize("case", range(len(VARLEN_CASES)))
+def test_prefill_varlen_matches_oracle_and_single_calls(case):
+    lens, nq, hkv, hq = VARLEN_CASES[case]
+    _say(f"prefill varlen lens={lens} n_q={nq} hkv={hkv} hq={hq}")
+    s = Scenario(680 + case, lens, hkv=hkv, dtype="bf16")
+    total_q = sum(nq)
+    q = synth.to_dtype(synth.normal(690 + case, (total_q, hq, 128)), "bf16")
+    cu = np.concatenate([[0], np.cumsum(nq)]).astype(np.int32)
+    starts = np.array([n - k for n, k in zip(lens, nq)], dtype=np.int32)
+    out = s.iq.prefill_attention_varlen(
+        s.cache, s.rot, q.cuda(), torch.from_numpy(cu).cuda(), torch.from_numpy(starts).cuda(), s.bt_dev,
+        max(nq), max(lens)).cpu().numpy()
+    host = s.host_cache()
+    worst = 0.0
+    for b in range(len(lens)):
+        if nq[b] == 0:
+            continue
+        rows = np.unique(np.linspace(0, nq[b] - 1, min(nq[b], 12)).astype(int))
+        ref = O.prefill_attention(host, s.blocks, q[cu[b]:cu[b + 1]].double().numpy(), int(starts[b]),
+                                  s.block_table[b], rows=rows)
+        worst = max(worst, max_row_error(out[cu[b] + rows], ref))
+        one = s.iq.prefill_attention(s.cache, s.rot, q[cu[b]:cu[b + 1]].cuda(), int(starts[b]),
+                                     s.bt_dev[b]).cpu().numpy()
+        assert np.array_equal(one, out[cu[b]:cu[b + 1]])   # the same tiles, the same arithmetic
+    _say(f"  max row error {worst:.3e}")
+    assert worst <= tol()
