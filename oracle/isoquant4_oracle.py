@@ -24,10 +24,9 @@ Readings (the pages fix the pipeline, not the 4-bit codebook or packing):
 * R4-3 Stored nibble: sign-magnitude, nib = c - 8 for c >= 8 (levels >= 0)
   and nib = 8 + (7 - c) for c < 8: bit 3 marks the negative side, bits 0-2
   the magnitude index (0 = smallest).  A bijection of the 16 codes.
-* R4-4 Record: 64 bytes of nibbles + fp16 norm (66 B per vector).  16-byte
-  chunk j (0..3), dword kk (0..3) of the chunk holds coordinates
-  32 kk + 8 j + e (e = 0..7): byte b of the dword carries coordinate
-  32 kk + 8 j + b in its low nibble and 32 kk + 8 j + 4 + b in its high one.
+* R4-4 Record: 64 bytes of nibbles + fp16 norm (66 B per vector).  Dword d
+  (d = 0..15) holds coordinates 8 d .. 8 d + 7: byte b of it carries
+  coordinate 8 d + b in its low nibble and 8 d + 4 + b in its high one.
 * R4-5 V blocks: the 4,096 bytes of (page, kv head) are 64 regions of 64 B;
   region n + 16 jq (n < 16, jq < 4) is 16 dwords, dword 4 p + 2 th + q
   (p < 4, th < 2, q < 2); byte r of it belongs to the token in slot
@@ -156,9 +155,8 @@ def quantize4(x, blocks):
 # ----------------------------------------------------------------------------
 def record_position(coord: int):
     """(byte offset in the 64-byte record, nibble shift 0 or 4)."""
-    kk, r = divmod(coord, 32)
-    j, e = divmod(r, 8)
-    return 16 * j + 4 * kk + (e % 4), 4 * (e // 4)
+    d, e = divmod(coord, 8)
+    return 4 * d + (e % 4), 4 * (e // 4)
 
 
 def pack4(codes) -> np.ndarray:
