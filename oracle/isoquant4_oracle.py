@@ -30,9 +30,9 @@ Readings (the pages fix the pipeline, not the 4-bit codebook or packing):
 * R4-5 V blocks: the 4,096 bytes of (page, kv head) are 64 regions of 64 B;
   region n + 16 jq (n < 16, jq < 4) is 16 dwords, dword 4 p + 2 th + q
   (p < 4, th < 2, q < 2); byte r of it belongs to the token in slot
-  32 th + 16 q + 4 jq + r and carries coordinate 16 p + n in its low nibble
-  and coordinate 64 + 16 p + n in its high one.  Every byte holds two codes
-  of one token.
+  32 th + 16 q + 4 jq + r and carries coordinate c = 32 (n // 4) + 4 p +
+  n % 4 in its low nibble and c + 16 in its high one.  Every byte holds two
+  codes of one token.
 """
 
 from __future__ import annotations
@@ -188,9 +188,10 @@ def v4_position(slot: int, coord: int):
     th, rest = divmod(slot, 32)
     q, rest = divmod(rest, 16)
     jq, r = divmod(rest, 4)
-    high, cc = divmod(coord, 64)
-    p, n = divmod(cc, 16)
-    region = n + 16 * jq
+    a, rest = divmod(coord, 32)
+    m, b = divmod(rest, 4)            # coordinate 32 a + 4 m + b, m = 0..7
+    high, p = divmod(m, 4)
+    region = (4 * a + b) + 16 * jq
     return region * 64 + 4 * (4 * p + 2 * th + q) + r, 4 * high
 
 
