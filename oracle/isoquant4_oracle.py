@@ -242,12 +242,15 @@ class PagedCache4:
             self.k_codes[page, head, slot] = pack4(codes)
             return
         off, sh = v4_offsets()
-        nib = nibble_of_code(codes)
+        nib = nibble_of_code(codes).astype(np.uint8)
         flat = self.v_codes.reshape(self.num_pages, self.n_kv_heads, PAGE_TOKENS * CODE_BYTES4)
         for i in range(len(page)):
-            o, s = off[slot[i]], sh[slot[i]]
-            keep = ~(np.uint8(15) << s.astype(np.uint8)).astype(np.uint8)
-            flat[page[i], head, o] = (flat[page[i], head, o] & keep) | (nib[i] << s).astype(np.uint8)
+            # two coordinates share each byte: clear and set nibble by nibble
+            # (ufunc.at applies repeated byte indices one after another)
+            o, s = off[slot[i]], sh[slot[i]].astype(np.uint8)
+            row = flat[int(page[i]), head]
+            np.bitwise_and.at(row, o, ~(np.uint8(15) << s))
+            np.bitwise_or.at(row, o, nib[i] << s)
 
     def gather(self, block_table, seq: int, length: int, head: int, which: str):
         pos = np.arange(length)

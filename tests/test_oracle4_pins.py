@@ -118,6 +118,46 @@ def test_v4_positions_are_a_bijection_with_one_token_per_byte():
             owner[b] = t
 
 
+def _v_block_from_layout(slot_codes):
+    """The 4,096-byte V block of a page from the layout statement, walked byte
+    by byte (region n + 16 jq, dword 4p + 2 th + q, byte r: token slot 32 th +
+    16 q + 4 jq + r; low nibble coordinate 32 (n // 4) + 4p + n % 4, high
+    nibble that + 16).  slot_codes: [64][128] codes."""
+    nib = O4.nibble_of_code(slot_codes)
+    blk = np.zeros(4096, dtype=np.uint8)
+    for jq in range(4):
+        for n in range(16):
+            for p in range(4):
+                for th in range(2):
+                    for q in range(2):
+                        for r in range(4):
+                            t = 32 * th + 16 * q + 4 * jq + r
+                            c = 32 * (n // 4) + 4 * p + n % 4
+                            blk[(n + 16 * jq) * 64 + 4 * (4 * p + 2 * th + q) + r] = \
+                                nib[t, c] | (nib[t, c + 16] << 4)
+    return blk
+
+
+def test_v4_store_matches_layout_and_round_trips():
+    """Every byte carries two codes of one token: storing tokens one at a
+    time, in any order, must leave both nibbles (the block equals the
+    byte-by-byte construction) and read back the codes."""
+    rng = np.random.default_rng(5)
+    codes = rng.integers(0, 16, size=(64, 128)).astype(np.uint8)
+    cache = O4.PagedCache4(2, 1)
+    order = rng.permutation(64)
+    for t in order:                                  # one token per call
+        cache.store("v", np.array([1]), 0, np.array([t]), codes[t:t + 1])
+    assert np.array_equal(cache.v_codes[1, 0].reshape(-1), _v_block_from_layout(codes))
+    assert np.array_equal(cache.codes("v", np.full(64, 1), 0, np.arange(64)), codes)
+    assert not cache.v_codes[0].any()
+    # overwriting a slot changes only that token's nibbles
+    new = rng.integers(0, 16, size=(1, 128)).astype(np.uint8)
+    cache.store("v", np.array([1]), 0, np.array([37]), new)
+    codes[37] = new[0]
+    assert np.array_equal(cache.v_codes[1, 0].reshape(-1), _v_block_from_layout(codes))
+
+
 def test_decode4_equals_plain_attention_on_materialised_kv():
     rng = np.random.default_rng(7)
     hkv, hq, lens = 2, 4, [1, 70, 130]
@@ -151,3 +191,5 @@ def test_decode4_equals_plain_attention_on_materialised_kv():
     # the stored records hold the quantiser's codes
     kc, _ = cache.gather(bt, 2, 130, 1, "k")
     assert np.array_equal(kc, O4.quantize4(k[sum(lens[:2]):, 1], blocks[1])["codes"])
+    vc, _ = cache.gather(bt, 2, 130, 1, "v")
+    assert np.array_equal(vc, O4.quantize4(v[sum(lens[:2]):, 1], blocks[1])["codes"])
