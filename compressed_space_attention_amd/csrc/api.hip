@@ -31,12 +31,12 @@ int device_cu_count() {
 
 bool cache_ok(const iq_cache* c) {
   return c && c->k_codes_dev && c->k_norms_dev && c->v_codes_dev && c->v_norms_dev &&
-         c->num_pages > 0 && c->n_kv_heads > 0;
+         c->num_pages > 0 && c->n_kv_heads > 0 && (c->bits == 0 || c->bits == 3 || c->bits == 4);
 }
 
 iq::CacheView view(const iq_cache* c) {
   return iq::CacheView{c->k_codes_dev, c->k_norms_dev, c->v_codes_dev, c->v_norms_dev,
-                       c->num_pages, c->n_kv_heads};
+                       c->num_pages, c->n_kv_heads, c->bits == 4 ? 4 : 3};
 }
 
 bool dense_ok(const iq_dense_cache* c) {
@@ -72,6 +72,28 @@ const char* iq_status_string(int32_t status) {
 }
 
 int32_t iq_version(void) { return 10000; }
+
+iq_status iq_codebook(int32_t bits, double* levels_host, float* thresholds_host, float* level_scale) {
+  if ((bits != 3 && bits != 4) || !levels_host || !thresholds_host) return IQ_ERR_INVALID_ARG;
+  if (bits == 3) {
+    for (int k = 0; k < 4; ++k) {
+      levels_host[4 + k] = iq::kLevel3[k];
+      levels_host[3 - k] = -iq::kLevel3[k];
+    }
+    for (int k = 0; k < 3; ++k) {
+      thresholds_host[4 + k] = iq::kThr3[k];
+      thresholds_host[2 - k] = -iq::kThr3[k];
+    }
+    thresholds_host[3] = 0.0f;
+    if (level_scale) *level_scale = iq::kLevelScale;
+    return IQ_OK;
+  }
+  const iq::Codebook4& cb = iq::codebook4();
+  for (int k = 0; k < 16; ++k) levels_host[k] = cb.level[k];
+  for (int k = 0; k < 15; ++k) thresholds_host[k] = cb.thr[k];
+  if (level_scale) *level_scale = cb.alpha;
+  return IQ_OK;
+}
 
 size_t iq_rotation_bytes(int32_t n_kv_heads) {
   return n_kv_heads > 0 ? iq::rotation_total_bytes(n_kv_heads) : 0;
@@ -234,7 +256,8 @@ iq_status iq_prefill_attention(const iq_cache* cache, const void* rot_dev, const
   if ((int64_t)q_start_pos + n_q > (int64_t)max_pages * IQ_PAGE_TOKENS) return IQ_ERR_INVALID_ARG;
   if (n_q == 0) return IQ_OK;
   const int group = n_q_heads / cache->n_kv_heads;
-  if (!pow2(group) || group > 128 || cache->n_kv_heads > 65535) return IQ_ERR_UNSUPPORTED;
+  if (!pow2(group) || group > 128 || cache->n_kv_heads > 65535 || cache->bits == 4)
+    return IQ_ERR_UNSUPPORTED;
   if ((int64_t)q_start_pos + n_q > (int64_t)iq::kPrefillMaxPages * IQ_PAGE_TOKENS)
     return IQ_ERR_UNSUPPORTED;
   const iq::PrefillPlan plan = iq::plan_prefill(n_q, n_q_heads, cache->n_kv_heads, q_start_pos, device_cu_count());
@@ -264,7 +287,8 @@ iq_status iq_prefill_attention_varlen(const iq_cache* cache, const void* rot_dev
   if (total_q == 0 || max_q_per_seq == 0) return IQ_OK;
   if (!q_dev || !out_dev) return IQ_ERR_INVALID_ARG;
   const int group = n_q_heads / cache->n_kv_heads;
-  if (!pow2(group) || group > 128 || cache->n_kv_heads > 65535) return IQ_ERR_UNSUPPORTED;
+  if (!pow2(group) || group > 128 || cache->n_kv_heads > 65535 || cache->bits == 4)
+    return IQ_ERR_UNSUPPORTED;
   if ((int64_t)max_kv_len > (int64_t)iq::kPrefillMaxPages * IQ_PAGE_TOKENS) return IQ_ERR_UNSUPPORTED;
   const iq::PrefillPlan plan =
       iq::plan_prefill(max_q_per_seq, n_q_heads, cache->n_kv_heads, 0, device_cu_count());

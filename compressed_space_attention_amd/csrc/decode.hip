@@ -28,11 +28,16 @@
 // With G <= 8 two 16-token score tiles share one set of registers (columns
 // 0-7 and 8-15), which halves the softmax work; the shared layout is also the
 // B operand of the PV product after one row shift.
+// 4-bit records (BITS = 4) use the same tiles: a record dword is eight
+// coordinates of the score operand, and a V region dword eight tokens' nibbles
+// of one coordinate pair (c, c + 16), i.e. accumulator tiles m and m + 4.
 // Levels enter as alpha-scaled f16 (see iq_device.h); the key norm, 1/alpha,
 // the softmax scale and log2(e) are one fp32 factor per score.  The value
 // norm is folded into P~ relative to a per-page power-of-two frame so that P~
 // stays inside the f16 range for any norm.
 #include <math.h>
+
+#include <type_traits>
 
 #include "iq_device.h"
 #include "iq_internal.h"
@@ -54,6 +59,7 @@ struct DecodeArgs {
   int pages_per_split, splits;
   float score_factor;  // softmax_scale * log2(e) / (128 * alpha)
   float out_factor;    // 1 / (sqrt(128) * alpha)
+  Levels4 lv4;         // 4-bit records: thresholds and f16 level tables
   float* ws_acc;       // [B][Hq][splits][128]
   float* ws_ml;        // [B][Hq][splits][2]
   float* out;          // [B][Hq][128]
@@ -74,11 +80,14 @@ __device__ __forceinline__ float dpp_f(float old, float src) {
 
 // Score tiles held by one lane: with PACK8 (G <= 8) tile t covers token block
 // 2t + (lane%16 >= 8); otherwise tile t is token block t.
-template <bool PACK8>
+template <bool PACK8, int BITS>
 struct PageRegs {
   static constexpr int NT = PACK8 ? 2 : 4;
-  u3 kc[4];       // K: 12 code bytes of token 16*rb + lane%16, group lane/16
-  u4 vr[3];       // V: the lane's 48-byte region (chunks c = 0..3, dwords 3c..3c+2)
+  // K: the code bytes of coordinates 32*(lane/16) .. +31 of token 16*rb + lane%16
+  // (12 of a 3-bit record, 16 of a 4-bit one)
+  using KRec = typename std::conditional<BITS == 3, u3, u4>::type;
+  KRec kc[4];
+  u4 vr[BITS];    // V: the lane's 48- or 64-byte region
   u2 kn[NT], vn[NT];  // fp16 norms of the lane's four score tokens per tile
 };
 
@@ -88,14 +97,20 @@ __device__ __forceinline__ int tile_block(int t, int col) {
 }
 
 // ---- LDS page ring -------------------------------------------------------
-// Each wave streams its pages through two LDS slots of 6,400 bytes (the
-// packed page of one kv head: K codes 3,072 | V codes 3,072 | K norms 128 |
-// V norms 128), filled by direct global->LDS loads (7 per page).  Two pages are
-// in flight while the wave computes a third from registers.
-constexpr int kSlotBytes = 6400;
+// Each wave streams its pages through two LDS slots, each the packed page of
+// one kv head: K codes | V codes | K norms 128 | V norms 128 (3-bit: 6,400
+// bytes, 4-bit: 8,448), filled by direct global->LDS loads of 1 KiB (K and V)
+// and one of the norms.  Two pages are in flight while the wave computes a
+// third from registers.
+template <int BITS>
+struct PageFmt {
+  static constexpr int kRecBytes = BITS == 4 ? kRec4 : kRec;  // code bytes per vector
+  static constexpr int kBlockBytes = kPage * kRecBytes;          // codes of one (page, kv head)
+  static constexpr int kSlotBytes = 2 * kBlockBytes + 256;
+  static constexpr int kDmaPerPage = 2 * kBlockBytes / 1024 + 1;
+};
 constexpr int kMaxPagesPerSplit = 512;   // the planner keeps splits within this (64 per wave)
 #define IQ_MAX_GROUP_BYTES (16 * 128 * 4)  // up to 16 query heads of fp32
-constexpr int kDmaPerPage = 7;
 
 // The direct-to-LDS loads are issued from inline asm, so the compiler does
 // not track them: it cannot tell which ring slot a load writes, and would put
@@ -120,33 +135,38 @@ __device__ __forceinline__ void lds_dma4(const void* g, void* lds) {
 constexpr int wait_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 constexpr int kWaitLgkm0 = 0xF | (0x3 << 14) | (0x7 << 4);
 
-// Issue the 7 loads of one page into `slot` (wave-uniform pointer).
+// Issue the loads of one page into `slot` (wave-uniform pointer).
+template <int BITS>
 __device__ __forceinline__ void issue_page(const DecodeArgs& a, int page, int g, int lane,
                                            uint8_t* slot) {
+  using F = PageFmt<BITS>;
   const size_t base = ((size_t)page * a.hkv + g) * kPage;  // record index of slot 0
-  const uint8_t* kb = a.k_codes + base * kRec + 16 * lane;
-  const uint8_t* vb = a.v_codes + base * kRec + 16 * lane;
+  const uint8_t* kb = a.k_codes + base * F::kRecBytes + 16 * lane;
+  const uint8_t* vb = a.v_codes + base * F::kRecBytes + 16 * lane;
 #pragma unroll
-  for (int i = 0; i < 3; ++i) lds_dma16(kb + 1024 * i, slot + 1024 * i);
+  for (int i = 0; i < F::kBlockBytes / 1024; ++i) lds_dma16(kb + 1024 * i, slot + 1024 * i);
 #pragma unroll
-  for (int i = 0; i < 3; ++i) lds_dma16(vb + 1024 * i, slot + 3072 + 1024 * i);
+  for (int i = 0; i < F::kBlockBytes / 1024; ++i)
+    lds_dma16(vb + 1024 * i, slot + F::kBlockBytes + 1024 * i);
   // lanes 0-31 bring the K norms (two per lane), lanes 32-63 the V norms
   const uint16_t* nb = (lane < 32 ? a.k_norms : a.v_norms) + base + 2 * (lane & 31);
-  lds_dma4(nb, slot + 6144);
+  lds_dma4(nb, slot + 2 * F::kBlockBytes);
 }
 
-template <bool PACK8>
-__device__ __forceinline__ void read_page(const uint8_t* slot, int lane, PageRegs<PACK8>& r) {
+template <bool PACK8, int BITS>
+__device__ __forceinline__ void read_page(const uint8_t* slot, int lane, PageRegs<PACK8, BITS>& r) {
+  using F = PageFmt<BITS>;
   const int col = lane & 15, jq = lane >> 4;
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb)
-    r.kc[rb] = *reinterpret_cast<const u3*>(slot + (16 * rb + col) * kRec + 12 * jq);
-  const u4* vreg = reinterpret_cast<const u4*>(slot + 3072 + lane * kRec);
+    r.kc[rb] = *reinterpret_cast<const typename PageRegs<PACK8, BITS>::KRec*>(
+        slot + (16 * rb + col) * F::kRecBytes + (F::kRecBytes / 4) * jq);
+  const u4* vreg = reinterpret_cast<const u4*>(slot + F::kBlockBytes + lane * F::kRecBytes);
 #pragma unroll
-  for (int i = 0; i < 3; ++i) r.vr[i] = vreg[i];
-  const uint16_t* kn = reinterpret_cast<const uint16_t*>(slot + 6144);
+  for (int i = 0; i < BITS; ++i) r.vr[i] = vreg[i];
+  const uint16_t* kn = reinterpret_cast<const uint16_t*>(slot + 2 * F::kBlockBytes);
 #pragma unroll
-  for (int t = 0; t < PageRegs<PACK8>::NT; ++t) {
+  for (int t = 0; t < PageRegs<PACK8, BITS>::NT; ++t) {
     const int tok = 16 * tile_block<PACK8>(t, col) + 4 * jq;
     r.kn[t] = *reinterpret_cast<const u2*>(kn + tok);
     r.vn[t] = *reinterpret_cast<const u2*>(kn + 64 + tok);
@@ -185,24 +205,34 @@ __device__ __forceinline__ float column_max(float v) {
 
 // One page for one wave: scores on the matrix cores, online-softmax update,
 // P~ V^ accumulation.  MASKED pages hold tokens at or beyond the length L.
-template <bool PACK8, bool MASKED>
-__device__ __forceinline__ void process_page(const PageRegs<PACK8>& cur, PageState& st, int tok0,
+template <bool PACK8, bool MASKED, int BITS>
+__device__ __forceinline__ void process_page(const PageRegs<PACK8, BITS>& cur, PageState& st, int tok0,
                                              int L, int lane, float fac, const h8 qhi[4],
-                                             const h8 qlo[4]) {
-  constexpr int NT = PageRegs<PACK8>::NT;
+                                             const h8 qlo[4], const Levels4& lv) {
+  constexpr int NT = PageRegs<PACK8, BITS>::NT;
   const int col = lane & 15, jq = lane >> 4;
   f4 s[4];
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb) {
-    uint32_t z[8];
-    group_to_selectors(cur.kc[rb].x, cur.kc[rb].y, cur.kc[rb].z, z);
+    // k-step kk takes coordinates 32 jq + 8 kk .. + 7 of the lane's token
+    h8 av[4];
+    if constexpr (BITS == 3) {
+      uint32_t z[8];
+      group_to_selectors(cur.kc[rb].x, cur.kc[rb].y, cur.kc[rb].z, z);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const u2 d0 = selector_to_f16(z[2 * kk]), d1 = selector_to_f16(z[2 * kk + 1]);
+        av[kk] = __builtin_bit_cast(h8, u4{d0[0], d0[1], d1[0], d1[1]});
+      }
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) av[kk] = dword4_to_h8(cur.kc[rb][kk], lv);
+    }
     f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      const u2 d0 = selector_to_f16(z[2 * kk]), d1 = selector_to_f16(z[2 * kk + 1]);
-      const h8 av = __builtin_bit_cast(h8, u4{d0[0], d0[1], d1[0], d1[1]});
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, qhi[kk], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, qlo[kk], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[kk], qhi[kk], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[kk], qlo[kk], acc, 0, 0, 0);
     }
     s[rb] = acc;
   }
@@ -286,20 +316,38 @@ __device__ __forceinline__ void process_page(const PageRegs<PACK8>& cur, PageSta
     pb[th] = __builtin_bit_cast(h8, w);
   }
 
-  uint32_t zv[4][8];
+  if constexpr (BITS == 3) {
+    uint32_t zv[4][8];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const int d = 3 * c;
-    group_to_selectors(cur.vr[d / 4][d % 4], cur.vr[(d + 1) / 4][(d + 1) % 4],
-                       cur.vr[(d + 2) / 4][(d + 2) % 4], zv[c]);
-  }
+    for (int c = 0; c < 4; ++c) {
+      const int d = 3 * c;
+      group_to_selectors(cur.vr[d / 4][d % 4], cur.vr[(d + 1) / 4][(d + 1) % 4],
+                         cur.vr[(d + 2) / 4][(d + 2) % 4], zv[c]);
+    }
 #pragma unroll
-  for (int m = 0; m < 8; ++m) {
+    for (int m = 0; m < 8; ++m) {
 #pragma unroll
-    for (int th = 0; th < 2; ++th) {
-      const u2 d0 = selector_to_f16(zv[2 * th][m]), d1 = selector_to_f16(zv[2 * th + 1][m]);
-      const h8 av = __builtin_bit_cast(h8, u4{d0[0], d0[1], d1[0], d1[1]});
-      st.acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pb[th], st.acc[m], 0, 0, 0);
+      for (int th = 0; th < 2; ++th) {
+        const u2 d0 = selector_to_f16(zv[2 * th][m]), d1 = selector_to_f16(zv[2 * th + 1][m]);
+        const h8 av = __builtin_bit_cast(h8, u4{d0[0], d0[1], d1[0], d1[1]});
+        st.acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pb[th], st.acc[m], 0, 0, 0);
+      }
+    }
+  } else {
+    // dword 4p + 2 th + q of the region: tokens 32 th + 16 q + 4 jq + r of
+    // coordinates 32 (col / 4) + 4p + col % 4 (low nibbles, tile p) and
+    // + 16 (high nibbles, tile p + 4)
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+#pragma unroll
+      for (int th = 0; th < 2; ++th) {
+        const uint32_t w0 = cur.vr[m & 3][2 * th], w1 = cur.vr[m & 3][2 * th + 1];
+        const int sh = m < 4 ? 0 : 4;
+        const u2 d0 = nibbles_to_f16((w0 >> sh) & 0x0F0F0F0Fu, lv);
+        const u2 d1 = nibbles_to_f16((w1 >> sh) & 0x0F0F0F0Fu, lv);
+        const h8 av = __builtin_bit_cast(h8, u4{d0[0], d0[1], d1[0], d1[1]});
+        st.acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pb[th], st.acc[m], 0, 0, 0);
+      }
     }
   }
 }
@@ -411,7 +459,7 @@ __device__ __forceinline__ void rotate_queries(int group, int q_dtype, const uin
 // processes the sequence's last page quantises the token's K and V rows,
 // patches the record into its LDS copy of the page before using it, and
 // stores it into the cache.
-template <bool PACK8, int kDecWaves, bool APPEND>
+template <bool PACK8, int kDecWaves, bool APPEND, int BITS>
 __global__ __launch_bounds__(64 * kDecWaves, 1) void decode_split_kernel(const int32_t* __restrict__ block_table,
                                                                       const int32_t* __restrict__ seq_lens,
                                                                       const uint8_t* __restrict__ q_bytes,
@@ -427,13 +475,20 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void decode_split_kernel(const i
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, jq = lane >> 4;
   constexpr int kLastWave = kDecWaves - 1;
+  using F = PageFmt<BITS>;
+  constexpr int kSlotBytes = F::kSlotBytes, kDmaPerPage = F::kDmaPerPage;
 
-  __shared__ __attribute__((aligned(16))) uint8_t s_ring[kDecWaves][2][kSlotBytes];  // 102,400 B
-  __shared__ __attribute__((aligned(16))) uint8_t s_tail[kSlotBytes];  // the sequence's partial last page
+  // (eight waves: 102,400 B for 3-bit pages, 135,168 B for 4-bit ones)
+  __shared__ __attribute__((aligned(16))) uint8_t s_ring[kDecWaves][2][kSlotBytes];
+  // The sequence's partial last page, and before it the group's raw queries:
+  // the queries are read only before the workgroup barrier that precedes the
+  // first load into the tail slot.
+  constexpr int kTailBytes = kSlotBytes > IQ_MAX_GROUP_BYTES ? kSlotBytes : IQ_MAX_GROUP_BYTES;
+  __shared__ __attribute__((aligned(16))) uint8_t s_tail[kTailBytes];
+  uint8_t* const s_qraw = s_tail;
   __shared__ __attribute__((aligned(16))) float s_rot[kRotFloats];     // 2,048 B
   __shared__ uint32_t s_q[32 * 64];  // Q' operands: [kstep*8 + dword][lane]
   __shared__ int s_pages[64 * kDecWaves];  // the split's page ids
-  __shared__ __attribute__((aligned(16))) uint8_t s_qraw[IQ_MAX_GROUP_BYTES];  // the group's queries
   __shared__ float s_qinv[16];
   __shared__ float s_m[kDecWaves][16], s_l[kDecWaves][16];
   __shared__ int s_next;  // next unclaimed page of the split (waves claim pages as they go)
@@ -492,8 +547,8 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void decode_split_kernel(const i
       }
     }
   }
-  issue_page(a, (int)min(bt0, last_page), g, lane, s_ring[wave][0]);
-  issue_page(a, (int)min(bt1, last_page), g, lane, s_ring[wave][1]);
+  issue_page<BITS>(a, (int)min(bt0, last_page), g, lane, s_ring[wave][0]);
+  issue_page<BITS>(a, (int)min(bt1, last_page), g, lane, s_ring[wave][1]);
 
   // (a length beyond the block table breaks the contract; never read past it)
   const int n_pages = min((L + kPage - 1) / kPage, max_pages);
@@ -550,10 +605,11 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void decode_split_kernel(const i
 
   // the last wave brings the partial page now; it is used after its stream
   const bool tail_mine = has_tail && wave == kLastWave;
-  if (tail_mine) issue_page(a, (int)min((uint32_t)s_pages[n_pages - 1 - pg_begin], last_page), g, lane, s_tail);
+  if (tail_mine)
+    issue_page<BITS>(a, (int)min((uint32_t)s_pages[n_pages - 1 - pg_begin], last_page), g, lane, s_tail);
   // ... and quantises the appended token (lanes 0-31 K, 32-63 V)
   float x_norm = 0.f;
-  u3 x_rec = {0u, 0u, 0u};
+  u3 x_rec = {0u, 0u, 0u};  // 3-bit: the group's three dwords; 4-bit: x_rec.x, this lane's dword
   if (append_here && wave == kLastWave) {
     const int r = lane & 31;
     const uint8_t* src = s_xraw + 512 * (lane >> 5);
@@ -577,7 +633,10 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void decode_split_kernel(const i
       }
     }
     const f4* m = reinterpret_cast<const f4*>(s_rot + 16 * r);
-    quantize_lanes32(x0, x1, x2, x3, m[0], m[1], m[2], m[3], r, x_norm, x_rec);
+    if constexpr (BITS == 3)
+      quantize_lanes32(x0, x1, x2, x3, m[0], m[1], m[2], m[3], r, x_norm, x_rec);
+    else
+      x_rec.x = quantize_lanes32_4(x0, x1, x2, x3, m[0], m[1], m[2], m[3], r, lane >= 32, a.lv4, x_norm);
   }
 
   PageState st;
@@ -606,8 +665,8 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void decode_split_kernel(const i
     if (after <= 0) __builtin_amdgcn_s_waitcnt(wait_vm(0));
     else if (after == 1) __builtin_amdgcn_s_waitcnt(wait_vm(kDmaPerPage));
     else __builtin_amdgcn_s_waitcnt(wait_vm(2 * kDmaPerPage));
-    PageRegs<PACK8> cur;
-    read_page<PACK8>(slot, lane, cur);
+    PageRegs<PACK8, BITS> cur;
+    read_page<PACK8, BITS>(slot, lane, cur);
     const int pg = head == 0 ? pg0 : pg1;
     // claim the next page and reuse this slot for it (claims only grow: a
     // failed claim ends the stream)
@@ -622,7 +681,7 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void decode_split_kernel(const i
     if (got) {
       const uint32_t id = min((uint32_t)s_pages[claim], last_page);
       __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // slot read before it is refilled
-      issue_page(a, (int)__builtin_amdgcn_readfirstlane(id), g, lane, slot);
+      issue_page<BITS>(a, (int)__builtin_amdgcn_readfirstlane(id), g, lane, slot);
     }
     if (head == 0) {
       have0 = got; pg0 = pg_begin + claim; seq0 = issued;
@@ -630,7 +689,7 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void decode_split_kernel(const i
       have1 = got; pg1 = pg_begin + claim; seq1 = issued;
     }
     issued += got ? 1 : 0;
-    process_page<PACK8, false>(cur, st, pg * kPage, L, lane, fac, qhi, qlo);
+    process_page<PACK8, false, BITS>(cur, st, pg * kPage, L, lane, fac, qhi, qlo, a.lv4);
     // the other slot's page is older than the refill, if it holds one
     if (head == 0 ? have1 : have0) head ^= 1;
   }
@@ -638,12 +697,14 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void decode_split_kernel(const i
     __builtin_amdgcn_s_waitcnt(wait_vm(0));
     if (append_here) {  // the appended record replaces slot L - 1 of the page copy
       const bool is_v = lane >= 32;
-      place_record(is_v, lane & 31, x_rec, x_norm, s_tail + (is_v ? 3072 : 0),
-                   reinterpret_cast<uint16_t*>(s_tail + 6144 + (is_v ? 128 : 0)), (L - 1) & 63);
+      uint8_t* codes = s_tail + (is_v ? F::kBlockBytes : 0);
+      uint16_t* norms = reinterpret_cast<uint16_t*>(s_tail + 2 * F::kBlockBytes + (is_v ? 128 : 0));
+      if constexpr (BITS == 3) place_record(is_v, lane & 31, x_rec, x_norm, codes, norms, (L - 1) & 63);
+      else place_record4(is_v, lane & 31, x_rec.x, x_norm, codes, norms, (L - 1) & 63);
     }
-    PageRegs<PACK8> cur;
-    read_page<PACK8>(s_tail, lane, cur);
-    process_page<PACK8, true>(cur, st, (n_pages - 1) * kPage, L, lane, fac, qhi, qlo);
+    PageRegs<PACK8, BITS> cur;
+    read_page<PACK8, BITS>(s_tail, lane, cur);
+    process_page<PACK8, true, BITS>(cur, st, (n_pages - 1) * kPage, L, lane, fac, qhi, qlo, a.lv4);
   }
   __builtin_amdgcn_s_waitcnt(wait_vm(0));  // a page requested but not used may still be landing
   if (append_here && wave == kLastWave) {  // the record into the cache (skipped for a bad page id)
@@ -651,8 +712,10 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void decode_split_kernel(const i
     if (id < (uint32_t)a.num_pages) {
       const size_t blk = (size_t)id * a.hkv + g;
       const bool is_v = lane >= 32;
-      place_record(is_v, lane & 31, x_rec, x_norm, (is_v ? a.v_codes : a.k_codes) + blk * (kPage * kRec),
-                   (is_v ? a.v_norms : a.k_norms) + blk * kPage, (L - 1) & 63);
+      uint8_t* codes = (is_v ? a.v_codes : a.k_codes) + blk * F::kBlockBytes;
+      uint16_t* norms = (is_v ? a.v_norms : a.k_norms) + blk * kPage;
+      if constexpr (BITS == 3) place_record(is_v, lane & 31, x_rec, x_norm, codes, norms, (L - 1) & 63);
+      else place_record4(is_v, lane & 31, x_rec.x, x_norm, codes, norms, (L - 1) & 63);
     }
   }
 
@@ -930,6 +993,9 @@ hipError_t launch_decode(const CacheView& c, const float* rot, const void* q, in
                          const DecodePlan& plan, float softmax_scale, float* out, void* workspace,
                          const void* k_new, const void* v_new, int kv_dtype, hipStream_t stream) {
   DecodeArgs a;
+  const bool four = c.bits == 4;
+  const double alpha = four ? (double)codebook4().alpha : (double)kLevelScale;
+  a.lv4 = four ? codebook4().lv : Levels4{};
   a.k_codes = c.k_codes;
   a.k_norms = c.k_norms;
   a.v_codes = c.v_codes;
@@ -946,21 +1012,24 @@ hipError_t launch_decode(const CacheView& c, const float* rot, const void* q, in
   a.pages_per_split = plan.pages_per_split;
   a.splits = plan.splits;
   const double log2e = 1.4426950408889634;
-  a.score_factor = (float)((double)softmax_scale * log2e / (128.0 * (double)kLevelScale));
-  a.out_factor = (float)(1.0 / (sqrt(128.0) * (double)kLevelScale));
+  a.score_factor = (float)((double)softmax_scale * log2e / (128.0 * alpha));
+  a.out_factor = (float)(1.0 / (sqrt(128.0) * alpha));
   const size_t rows = (size_t)batch * hq * plan.splits;
   a.ws_acc = reinterpret_cast<float*>(workspace);
   a.ws_ml = a.ws_acc + rows * kD;
   a.out = out;
   const uint8_t* qb = static_cast<const uint8_t*>(q);
   const dim3 grid(plan.splits, c.hkv, batch);
-#define IQ_SPLIT(P8, W, AP)                                                                       \
-  hipLaunchKernelGGL((decode_split_kernel<P8, W, AP>), grid, dim3(64 * W), 0, stream, block_table, \
-                     seq_lens, qb, rot, a.max_pages, a.pages_per_split, a.hq, a.group, a.q_dtype, \
-                     a.splits, a)
+#define IQ_SPLIT(P8, W, AP, B)                                                                    \
+  hipLaunchKernelGGL((decode_split_kernel<P8, W, AP, B>), grid, dim3(64 * W), 0, stream,           \
+                     block_table, seq_lens, qb, rot, a.max_pages, a.pages_per_split, a.hq, a.group, \
+                     a.q_dtype, a.splits, a)
+#define IQ_SPLIT_B(P8, W, AP)             \
+  if (four) IQ_SPLIT(P8, W, AP, 4);       \
+  else IQ_SPLIT(P8, W, AP, 3)
 #define IQ_SPLIT_W(P8, AP)              \
-  if (plan.waves == 4) IQ_SPLIT(P8, 4, AP); \
-  else IQ_SPLIT(P8, 8, AP)
+  if (plan.waves == 4) { IQ_SPLIT_B(P8, 4, AP); } \
+  else { IQ_SPLIT_B(P8, 8, AP); }
   const bool append = k_new != nullptr;
   if (a.group <= 8) {
     if (append) { IQ_SPLIT_W(true, true); }
@@ -970,6 +1039,7 @@ hipError_t launch_decode(const CacheView& c, const float* rot, const void* q, in
     else { IQ_SPLIT_W(false, false); }
   }
 #undef IQ_SPLIT_W
+#undef IQ_SPLIT_B
 #undef IQ_SPLIT
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

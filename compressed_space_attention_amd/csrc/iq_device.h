@@ -13,7 +13,8 @@ namespace iq {
 
 constexpr int kD = 128;        // head dimension
 constexpr int kPage = 64;      // tokens per page
-constexpr int kRec = 48;       // code bytes per vector
+constexpr int kRec = 48;       // code bytes per vector (3-bit records)
+constexpr int kRec4 = 64;      // code bytes per vector (4-bit records)
 constexpr int kBlocks = 32;    // SO(4) blocks per head
 constexpr int kRotFloats = kBlocks * 16;  // fp32 4x4 matrices per kv head
 
@@ -28,17 +29,20 @@ struct __attribute__((aligned(4))) u3 {
 };
 
 // ---------------------------------------------------------------------------
-// Quantiser constants.  Decision thresholds = midpoints between adjacent
-// Gaussian Lloyd-Max levels (+-0.2451, +-0.7560, +-1.3440, +-2.1520), as fp32.
+// 3-bit quantiser constants: the Gaussian Lloyd-Max levels the pages print
+// (positive half), and the decision thresholds = midpoints between adjacent
+// levels, as fp32 (the middle threshold is 0).
 // ---------------------------------------------------------------------------
+constexpr double kLevel3[4] = {0.2451, 0.7560, 1.3440, 2.1520};
+constexpr float kThr3[3] = {0.50055f, 1.05f, 1.748f};
 __device__ __forceinline__ uint32_t code_of(float u) {
-  uint32_t c = (u >= -1.748f);
-  c += (u >= -1.05f);
-  c += (u >= -0.50055f);
+  uint32_t c = (u >= -kThr3[2]);
+  c += (u >= -kThr3[1]);
+  c += (u >= -kThr3[0]);
   c += (u >= 0.0f);
-  c += (u >= 0.50055f);
-  c += (u >= 1.05f);
-  c += (u >= 1.748f);
+  c += (u >= kThr3[0]);
+  c += (u >= kThr3[1]);
+  c += (u >= kThr3[2]);
   return c;
 }
 
@@ -96,6 +100,54 @@ __device__ __forceinline__ u2 selector_to_f16(uint32_t z) {
   const uint32_t l = __builtin_amdgcn_perm(kLo4567, kLo0123, z);  // low bytes of 4 levels
   const uint32_t h = __builtin_amdgcn_perm(kHi4567, kHi0123, z);  // high bytes
   return u2{__builtin_amdgcn_perm(h, l, 0x05010400u), __builtin_amdgcn_perm(h, l, 0x07030602u)};
+}
+
+// ---------------------------------------------------------------------------
+// 4-bit records (the 4-bit member of the same family: 16 Gaussian Lloyd-Max
+// levels, symmetric about 0).  A stored nibble is sign-magnitude: bit 3 marks
+// the negative side, bits 0-2 index the magnitude (0 = smallest); code c of
+// the 15-threshold quantiser (c = number of thresholds u reaches, 0..15) is
+// stored as c - 8 for c >= 8 and 15 - c below.  A 64-byte record: dword d holds
+// coordinates 8d..8d+7, byte b of it coordinate 8d+b in its low nibble and
+// 8d+4+b in its high one.
+//
+// The host computes the codebook (Lloyd's iteration) and passes it to the
+// kernels as this struct: the seven positive thresholds (the negative ones
+// mirror them exactly) and v_perm_b32 tables of the f16 bytes of alpha times
+// the eight magnitudes.
+// ---------------------------------------------------------------------------
+struct Levels4 {
+  float t[7];                                // positive decision thresholds, ascending
+  uint32_t lo0123, lo4567, hi0123, hi4567;   // f16 low / high bytes of alpha * magnitude k
+};
+
+// Nibble of u.  Nonnegative u (including -0): the magnitudes whose lower
+// threshold it reaches; negative u: 8 + the thresholds |u| exceeds (a tie
+// belongs to the upper code on either side).
+__device__ __forceinline__ uint32_t nibble_of(float u, const Levels4& lv) {
+  const float a = fabsf(u);
+  uint32_t ge = 0, gt = 0;
+#pragma unroll
+  for (int k = 0; k < 7; ++k) {
+    ge += (a >= lv.t[k]);
+    gt += (a > lv.t[k]);
+  }
+  return u >= 0.0f ? ge : 8u + gt;
+}
+
+// Four nibbles (one per byte, bits 0-3) -> four f16 levels (alpha-scaled) in
+// two dwords, ordered like the bytes.
+__device__ __forceinline__ u2 nibbles_to_f16(uint32_t z, const Levels4& lv) {
+  const uint32_t k = z & 0x07070707u;
+  const uint32_t l = __builtin_amdgcn_perm(lv.lo4567, lv.lo0123, k);
+  const uint32_t h = __builtin_amdgcn_perm(lv.hi4567, lv.hi0123, k) | ((z << 4) & 0x80808080u);
+  return u2{__builtin_amdgcn_perm(h, l, 0x05010400u), __builtin_amdgcn_perm(h, l, 0x07030602u)};
+}
+
+// The eight f16 levels of one record dword (coordinates 8d..8d+7 in order).
+__device__ __forceinline__ h8 dword4_to_h8(uint32_t w, const Levels4& lv) {
+  const u2 a = nibbles_to_f16(w & 0x0F0F0F0Fu, lv), b = nibbles_to_f16((w >> 4) & 0x0F0F0F0Fu, lv);
+  return __builtin_bit_cast(h8, u4{a[0], a[1], b[0], b[1]});
 }
 
 // ---------------------------------------------------------------------------
@@ -284,16 +336,17 @@ __device__ __forceinline__ uint32_t or_xor4(uint32_t v) {
 }
 
 // ---------------------------------------------------------------------------
-// Quantise one 128-vector held by the 32 lanes of a half-wave: lane r holds
+// Rotate one 128-vector held by the 32 lanes of a half-wave: lane r holds
 // coordinates 4r..4r+3 (x0..x3) and the rows m0..m3 of SO(4) block r.
-// n = ||x|| (every lane); w = the three dwords of group r/8 of the packed
-// record (every lane of the group).  The Walsh-Hadamard butterflies at
-// coordinate distance 1 and 2 are in registers, 4..64 are lane exchanges
-// 1..16; u = (B H x) / n with H unnormalised equals T x sqrt(d) / n.
+// n = ||x|| (every lane); z0..z3 = coordinates 4r..4r+3 of B H x.  The
+// Walsh-Hadamard butterflies at coordinate distance 1 and 2 are in registers,
+// 4..64 are lane exchanges 1..16; u = (B H x) / n with H unnormalised equals
+// T x sqrt(d) / n.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void quantize_lanes32(float x0, float x1, float x2, float x3,
-                                                 const f4& m0, const f4& m1, const f4& m2,
-                                                 const f4& m3, int r, float& n, u3& w) {
+__device__ __forceinline__ void rotate_lanes32(float x0, float x1, float x2, float x3,
+                                               const f4& m0, const f4& m1, const f4& m2,
+                                               const f4& m3, int r, float& n, float& z0, float& z1,
+                                               float& z2, float& z3) {
   float ss = fmaf(x3, x3, fmaf(x2, x2, fmaf(x1, x1, x0 * x0)));
   ss += quad_xor1(ss);
   ss += quad_xor2(ss);
@@ -332,10 +385,19 @@ __device__ __forceinline__ void quantize_lanes32(float x0, float x1, float x2, f
     q = pair_xor16(__builtin_bit_cast(uint32_t, x3));
     x3 = fmaf(sg, __builtin_bit_cast(float, (uint32_t)q[1]), __builtin_bit_cast(float, (uint32_t)q[0]));
   }
-  const float z0 = m0[0] * x0 + m0[1] * x1 + m0[2] * x2 + m0[3] * x3;
-  const float z1 = m1[0] * x0 + m1[1] * x1 + m1[2] * x2 + m1[3] * x3;
-  const float z2 = m2[0] * x0 + m2[1] * x1 + m2[2] * x2 + m2[3] * x3;
-  const float z3 = m3[0] * x0 + m3[1] * x1 + m3[2] * x2 + m3[3] * x3;
+  z0 = m0[0] * x0 + m0[1] * x1 + m0[2] * x2 + m0[3] * x3;
+  z1 = m1[0] * x0 + m1[1] * x1 + m1[2] * x2 + m1[3] * x3;
+  z2 = m2[0] * x0 + m2[1] * x1 + m2[2] * x2 + m2[3] * x3;
+  z3 = m3[0] * x0 + m3[1] * x1 + m3[2] * x2 + m3[3] * x3;
+}
+
+// 3-bit record of rotate_lanes32's vector: w = the three dwords of group r/8
+// of the packed record (every lane of the group).
+__device__ __forceinline__ void quantize_lanes32(float x0, float x1, float x2, float x3,
+                                                 const f4& m0, const f4& m1, const f4& m2,
+                                                 const f4& m3, int r, float& n, u3& w) {
+  float z0, z1, z2, z3;
+  rotate_lanes32(x0, x1, x2, x3, m0, m1, m2, m3, r, n, z0, z1, z2, z3);
   uint32_t sel = 0x04040404u;  // zero vector: every code 4
   if (n > 0.f) {
     const float inv_n = 1.0f / n;
@@ -377,6 +439,48 @@ __device__ __forceinline__ void place_record(bool is_v, int r, const u3& w, floa
     dst[0] = (uint8_t)(w.x >> (8 * s));
     dst[4] = (uint8_t)(w.y >> (8 * s));
     dst[8] = (uint8_t)(w.z >> (8 * s));
+  }
+  if (r == 0) norms[slot] = float_to_half_sat(n);
+}
+
+// 4-bit record of rotate_lanes32's vector.  Returns the dword this lane
+// stores: for K (is_v false) lane r = 2d holds record dword d (its own four
+// nibbles low, lane 2d+1's high); for V lane r = 8a + p (p < 4) holds the
+// four V-block bytes of coordinates c = 32a + 4p + b (low nibble) and c + 16
+// (high nibble, from lane r + 4).  Every lane of the half-wave must call it.
+__device__ __forceinline__ uint32_t quantize_lanes32_4(float x0, float x1, float x2, float x3,
+                                                       const f4& m0, const f4& m1, const f4& m2,
+                                                       const f4& m3, int r, bool is_v,
+                                                       const Levels4& lv, float& n) {
+  float z0, z1, z2, z3;
+  rotate_lanes32(x0, x1, x2, x3, m0, m1, m2, m3, r, n, z0, z1, z2, z3);
+  uint32_t sel = 0;  // zero vector: every nibble 0 (code 8, level +0.128 * 0)
+  if (n > 0.f) {
+    const float inv_n = 1.0f / n;
+    sel = nibble_of(z0 * inv_n, lv) | (nibble_of(z1 * inv_n, lv) << 8) |
+          (nibble_of(z2 * inv_n, lv) << 16) | (nibble_of(z3 * inv_n, lv) << 24);
+  }
+  const uint32_t p1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)sel, 0xB1, 0xF, 0xF, true);
+  const uint32_t p4 = __builtin_bit_cast(uint32_t, lane_xor4_f(__builtin_bit_cast(float, sel)));
+  return sel | ((is_v ? p4 : p1) << 4);
+}
+
+// Store the 4-bit record of quantize_lanes32_4 (w = its return value) into one
+// (page, kv head) block: `codes` = its 4,096 code bytes, `norms` = its 64 fp16
+// norms.  K blocks are slot-ordered; V blocks are in the matrix-core order of
+// the decode kernels: the byte of (slot, coordinates c, c + 16), c = 32a + 4p
+// + b, is byte slot % 4 of dword 4p + 2 th + q of region (4a + b) + 16 jq, for
+// slot = 32 th + 16 q + 4 jq + slot % 4.  Global and LDS destinations alike.
+__device__ __forceinline__ void place_record4(bool is_v, int r, uint32_t w, float n, uint8_t* codes,
+                                              uint16_t* norms, int slot) {
+  if (!is_v) {
+    if ((r & 1) == 0) *reinterpret_cast<uint32_t*>(codes + slot * kRec4 + 2 * r) = w;
+  } else if ((r & 4) == 0) {
+    const int a = r >> 3, p = r & 3;
+    const int th = slot >> 5, q = (slot >> 4) & 1, jq = (slot >> 2) & 3, rr = slot & 3;
+    uint8_t* dst = codes + (4 * a + 16 * jq) * 64 + 4 * (4 * p + 2 * th + q) + rr;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) dst[64 * b] = (uint8_t)(w >> (8 * b));
   }
   if (r == 0) norms[slot] = float_to_half_sat(n);
 }

@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "iq_device.h"
+
 namespace iq {
 
 struct CacheView {
@@ -14,7 +16,19 @@ struct CacheView {
   uint16_t* v_norms;
   int32_t num_pages;
   int32_t hkv;
+  int32_t bits;  // 3 or 4: record width
 };
+
+// The 4-bit quantiser (codebook.hip), computed once per process.
+struct Codebook4 {
+  double level[16];       // ascending Lloyd-Max levels of N(0, 1)
+  float thr[15];          // fp32 decision thresholds (midpoints; thr[7] = 0)
+  float alpha;            // scale of the f16 level operands
+  double alpha_rel_err;   // worst relative error of the eight f16 magnitudes
+  uint16_t level_f16[8];  // f16 bits of alpha * level[8 + k]
+  Levels4 lv;             // the kernels' form
+};
+const Codebook4& codebook4();
 
 // Rotation buffer: fp32 matrices [hkv][32][4][4], then fp32 quaternion staging
 // [hkv][32][2][4].

@@ -1,9 +1,9 @@
-// Quantise-append: K/V head vectors -> 48-byte 3-bit records + fp16 norms in
-// a 64-token paged cache.
+// Quantise-append: K/V head vectors -> packed 3-bit (48-byte) or 4-bit
+// (64-byte) records + fp16 norms in a 64-token paged cache.
 //
 // "RotaryQuant: Fitting 120B MoE Models on Consumer Hardware via Fused
 // Compressed-Space Attention", abstract: Walsh-Hadamard transform, then
-// block-diagonal SO(4) rotations, then 3-bit scalar quantisation.  Per vector
+// block-diagonal SO(4) rotations, then low-bit scalar quantisation.  Per vector
 // x: n = ||x||, u = (B H x) / n (H unnormalised, so u = T x sqrt(d) / n),
 // code = number of thresholds u reaches, record = packed codes, norm = fp16(n).
 //
@@ -30,19 +30,23 @@ constexpr long long kSmallAppendVectors = 16384;
 // contiguous bytes; otherwise each quad stores its own record.
 // The first 14 argument dwords (everything the first loads need) are
 // preloaded into SGPRs; the cache pointers follow from the argument segment.
-template <int DT>
+// BITS = 4: the 4-bit records (nibbles, see iq_device.h); a quad lane's
+// quarter is then record dwords 4j..4j+3, and its V bytes pair coordinates
+// 32j + 4p + b and 32j + 16 + 4p + b of the token.
+template <int DT, int BITS>
 __global__ __launch_bounds__(256) void quantize_append_kernel(
     const void* __restrict__ k, const void* __restrict__ v, const int32_t* __restrict__ seq_idx,
     const int32_t* __restrict__ pos, const int32_t* __restrict__ block_table, int n_tok,
     int hkv, int max_pages, const float* __restrict__ rot, int num_pages,
     uint8_t* __restrict__ k_codes, uint16_t* __restrict__ k_norms, uint8_t* __restrict__ v_codes,
-    uint16_t* __restrict__ v_norms) {
+    uint16_t* __restrict__ v_norms, Levels4 lv) {
+  constexpr int kRecB = BITS == 4 ? kRec4 : kRec;
   const int tl = threadIdx.x >> 2, j = threadIdx.x & 3;
   const int head = blockIdx.y, which = blockIdx.z;
   const int t0 = blockIdx.x * 64;
   const int tok = t0 + tl;
   const bool valid = tok < n_tok;
-  __shared__ __attribute__((aligned(16))) uint8_t s_v[kPage * kRec];  // the page's V block
+  __shared__ __attribute__((aligned(16))) uint8_t s_v[kPage * kRecB];  // the page's V block
 
   // The destination is looked up while the vector is transformed: position
   // and sequence first, then the page id, all before the arithmetic.
@@ -76,49 +80,79 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(
   float z[32];
   so4_forward_quarter(rot + (size_t)head * kRotFloats, j, x, z);
 
-  uint32_t sel[8];
-  if (n > 0.f) {
-    const float inv_n = 1.0f / n;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      sel[s] = code_of(z[4 * s] * inv_n) | (code_of(z[4 * s + 1] * inv_n) << 8) |
-               (code_of(z[4 * s + 2] * inv_n) << 16) | (code_of(z[4 * s + 3] * inv_n) << 24);
-    }
-  } else {
-#pragma unroll
-    for (int s = 0; s < 8; ++s) sel[s] = 0x04040404u;  // zero vector: level +0.2451 * 0
-  }
-  u3 w;
-  selectors_to_group(sel, w.x, w.y, w.z);
-
   const int slot = p & 63;
   const size_t rec = ((size_t)page * hkv + head) * kPage + slot;
-  if (!which) {
-    if (stored) {
-      *reinterpret_cast<u3*>(k_codes + rec * kRec + 12 * j) = w;
-      if (j == 0) k_norms[rec] = float_to_half_sat(n);
-    }
-    return;
-  }
-  // V: byte lane b of this group goes to region n = 4j + b (quad q of the
-  // slot), chunk c = slot / 16, byte lane r = slot % 4 -- the order in which
-  // the decode matrix cores consume V (see the cache layout in isoquant.h).
-  const int c = slot >> 4, q = (slot >> 2) & 3, r = slot & 3;
-  uint8_t* blk = whole ? s_v : v_codes + ((size_t)page * hkv + head) * (kPage * kRec);
-  if (stored) {
+  uint8_t* blk = whole ? s_v : v_codes + ((size_t)page * hkv + head) * (kPage * kRecB);
+  if constexpr (BITS == 3) {
+    uint32_t sel[8];
+    if (n > 0.f) {
+      const float inv_n = 1.0f / n;
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      uint8_t* dst = blk + (4 * j + b + 16 * q) * kRec + 12 * c + r;
-      dst[0] = (uint8_t)(w.x >> (8 * b));
-      dst[4] = (uint8_t)(w.y >> (8 * b));
-      dst[8] = (uint8_t)(w.z >> (8 * b));
+      for (int s = 0; s < 8; ++s) {
+        sel[s] = code_of(z[4 * s] * inv_n) | (code_of(z[4 * s + 1] * inv_n) << 8) |
+                 (code_of(z[4 * s + 2] * inv_n) << 16) | (code_of(z[4 * s + 3] * inv_n) << 24);
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < 8; ++s) sel[s] = 0x04040404u;  // zero vector: level +0.2451 * 0
     }
-    if (j == 0) v_norms[rec] = float_to_half_sat(n);
+    u3 w;
+    selectors_to_group(sel, w.x, w.y, w.z);
+    if (!which) {
+      if (stored) *reinterpret_cast<u3*>(k_codes + rec * kRec + 12 * j) = w;
+    } else if (stored) {
+      // V: byte lane b of this group goes to region n = 4j + b (quad q of the
+      // slot), chunk c = slot / 16, byte lane r = slot % 4 -- the order in
+      // which the decode matrix cores consume V (see the cache layout in
+      // isoquant.h).
+      const int c = slot >> 4, q = (slot >> 2) & 3, r = slot & 3;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        uint8_t* dst = blk + (4 * j + b + 16 * q) * kRec + 12 * c + r;
+        dst[0] = (uint8_t)(w.x >> (8 * b));
+        dst[4] = (uint8_t)(w.y >> (8 * b));
+        dst[8] = (uint8_t)(w.z >> (8 * b));
+      }
+    }
+  } else {
+    uint32_t nib[32];
+    if (n > 0.f) {
+      const float inv_n = 1.0f / n;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) nib[i] = nibble_of(z[i] * inv_n, lv);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) nib[i] = 0;  // zero vector: code 8 (level +0.128 * 0)
+    }
+    if (!which) {
+      // record dword 4j + kk: byte b = coordinate 32j + 8kk + b (low), + 4 (high)
+      u4 w;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        uint32_t d = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) d |= (nib[8 * kk + b] | (nib[8 * kk + 4 + b] << 4)) << (8 * b);
+        w[kk] = d;
+      }
+      if (stored) *reinterpret_cast<u4*>(k_codes + rec * kRec4 + 16 * j) = w;
+    } else if (stored) {
+      // V: coordinates 32j + 4p + b and + 16 share byte slot % 4 of dword
+      // 4p + 2 th + q of region (4j + b) + 16 jq (slot = 32 th + 16 q + 4 jq + r)
+      const int th = slot >> 5, q = (slot >> 4) & 1, jq = (slot >> 2) & 3, r = slot & 3;
+      uint8_t* dst = blk + (4 * j + 16 * jq) * 64 + 4 * (2 * th + q) + r;
+#pragma unroll
+      for (int pp = 0; pp < 4; ++pp)
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+          dst[64 * b + 16 * pp] = (uint8_t)(nib[4 * pp + b] | (nib[16 + 4 * pp + b] << 4));
+    }
   }
-  if (whole) {
+  if (stored && j == 0) (which ? v_norms : k_norms)[rec] = float_to_half_sat(n);
+  if (which && whole) {
     __syncthreads();
-    if (threadIdx.x < kPage * kRec / 16) {
-      uint8_t* gblk = v_codes + ((size_t)page * hkv + head) * (kPage * kRec);
+    constexpr int kChunks = kPage * kRecB / 16;
+    if (threadIdx.x < kChunks) {
+      uint8_t* gblk = v_codes + ((size_t)page * hkv + head) * (kPage * kRecB);
       reinterpret_cast<u4*>(gblk)[threadIdx.x] = reinterpret_cast<const u4*>(s_v)[threadIdx.x];
     }
   }
@@ -131,13 +165,13 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(
 // r % 8 of group r / 8, and the eight lanes of a group OR their bit fields
 // into the group's three dwords.  Loads of the position, the rotation block
 // and the vector go out together, the page id as soon as the position lands.
-template <int DT>
+template <int DT, int BITS>
 __global__ __launch_bounds__(256) void quantize_small_kernel(
     const void* __restrict__ k, const void* __restrict__ v, const int32_t* __restrict__ seq_idx,
     const int32_t* __restrict__ pos, const int32_t* __restrict__ block_table,
     const float* __restrict__ rot, int n_vec, int hkv, int max_pages, int num_pages,
     uint8_t* __restrict__ k_codes, uint16_t* __restrict__ k_norms, uint8_t* __restrict__ v_codes,
-    uint16_t* __restrict__ v_norms) {
+    uint16_t* __restrict__ v_norms, Levels4 lv) {
   const int gv = blockIdx.x * 8 + (threadIdx.x >> 5);  // K vectors first, then V
   const int r = threadIdx.x & 31;
   if (gv >= 2 * n_vec) return;  // whole half-waves leave together
@@ -177,40 +211,56 @@ __global__ __launch_bounds__(256) void quantize_small_kernel(
   const int page = in_table ? block_table[(size_t)si * max_pages + (p >> 6)] : -1;
 
   float n;
-  u3 w;
-  quantize_lanes32(x0, x1, x2, x3, m0, m1, m2, m3, r, n, w);
-  if ((unsigned)page >= (unsigned)num_pages) return;
-  const size_t blk = (size_t)page * hkv + head;  // (page, kv head) block
-  if (!which) place_record(false, r, w, n, k_codes + blk * (kPage * kRec), k_norms + blk * kPage, p & 63);
-  else place_record(true, r, w, n, v_codes + blk * (kPage * kRec), v_norms + blk * kPage, p & 63);
+  if constexpr (BITS == 3) {
+    u3 w;
+    quantize_lanes32(x0, x1, x2, x3, m0, m1, m2, m3, r, n, w);
+    if ((unsigned)page >= (unsigned)num_pages) return;
+    const size_t blk = (size_t)page * hkv + head;  // (page, kv head) block
+    place_record(which, r, w, n, (which ? v_codes : k_codes) + blk * (kPage * kRec),
+                 (which ? v_norms : k_norms) + blk * kPage, p & 63);
+  } else {
+    const uint32_t w = quantize_lanes32_4(x0, x1, x2, x3, m0, m1, m2, m3, r, which, lv, n);
+    if ((unsigned)page >= (unsigned)num_pages) return;
+    const size_t blk = (size_t)page * hkv + head;
+    place_record4(which, r, w, n, (which ? v_codes : k_codes) + blk * (kPage * kRec4),
+                  (which ? v_norms : k_norms) + blk * kPage, p & 63);
+  }
 }
 
 hipError_t launch_quantize_append(const CacheView& c, const float* rot, const void* k, const void* v,
                                   int dtype, int n_tokens, const int32_t* seq_idx,
                                   const int32_t* pos, const int32_t* block_table, int max_pages,
                                   hipStream_t stream) {
+  const Levels4 lv = c.bits == 4 ? codebook4().lv : Levels4{};
   const long long n_vec = (long long)n_tokens * c.hkv;
   if (2 * n_vec <= kSmallAppendVectors) {
     const unsigned blocks = (unsigned)((2 * n_vec + 7) / 8);
-#define IQ_SMALL(DT)                                                                          \
-  hipLaunchKernelGGL(quantize_small_kernel<DT>, dim3(blocks), dim3(256), 0, stream, k, v,     \
-                     seq_idx, pos, block_table, rot, (int)n_vec, c.hkv, max_pages,            \
-                     c.num_pages, c.k_codes,                                                  \
-                     c.k_norms, c.v_codes, c.v_norms)
-    if (dtype == 0) IQ_SMALL(0);
-    else if (dtype == 1) IQ_SMALL(1);
-    else IQ_SMALL(2);
+#define IQ_SMALL(DT, B)                                                                          \
+  hipLaunchKernelGGL((quantize_small_kernel<DT, B>), dim3(blocks), dim3(256), 0, stream, k, v,   \
+                     seq_idx, pos, block_table, rot, (int)n_vec, c.hkv, max_pages,               \
+                     c.num_pages, c.k_codes, c.k_norms, c.v_codes, c.v_norms, lv)
+#define IQ_SMALL_B(B)            \
+  if (dtype == 0) IQ_SMALL(0, B); \
+  else if (dtype == 1) IQ_SMALL(1, B); \
+  else IQ_SMALL(2, B)
+    if (c.bits == 4) { IQ_SMALL_B(4); }
+    else { IQ_SMALL_B(3); }
+#undef IQ_SMALL_B
 #undef IQ_SMALL
     return hipGetLastError();
   }
   const dim3 grid((unsigned)((n_tokens + 63) / 64), (unsigned)c.hkv, 2);
-#define IQ_QUADS(DT)                                                                              \
-  hipLaunchKernelGGL(quantize_append_kernel<DT>, grid, dim3(256), 0, stream, k, v, seq_idx, pos,   \
-                     block_table, n_tokens, c.hkv, max_pages, rot, c.num_pages, c.k_codes,          \
-                     c.k_norms, c.v_codes, c.v_norms)
-  if (dtype == 0) IQ_QUADS(0);
-  else if (dtype == 1) IQ_QUADS(1);
-  else IQ_QUADS(2);
+#define IQ_QUADS(DT, B)                                                                           \
+  hipLaunchKernelGGL((quantize_append_kernel<DT, B>), grid, dim3(256), 0, stream, k, v, seq_idx,   \
+                     pos, block_table, n_tokens, c.hkv, max_pages, rot, c.num_pages, c.k_codes,     \
+                     c.k_norms, c.v_codes, c.v_norms, lv)
+#define IQ_QUADS_B(B)            \
+  if (dtype == 0) IQ_QUADS(0, B); \
+  else if (dtype == 1) IQ_QUADS(1, B); \
+  else IQ_QUADS(2, B)
+  if (c.bits == 4) { IQ_QUADS_B(4); }
+  else { IQ_QUADS_B(3); }
+#undef IQ_QUADS_B
 #undef IQ_QUADS
   return hipGetLastError();
 }

@@ -21,6 +21,7 @@ LIB_PATH = os.environ.get("ISOQUANT_LIB") or os.path.join(_HERE, "libisoquant.so
 HEAD_DIM = 128
 PAGE_TOKENS = 64
 CODE_BYTES = 48
+CODE_BYTES4 = 64
 MAX_GROUP = 16
 
 IQ_F32, IQ_BF16, IQ_F16 = 0, 1, 2
@@ -41,6 +42,7 @@ class IqCacheStruct(ctypes.Structure):
         ("v_norms_dev", ctypes.c_void_p),
         ("num_pages", ctypes.c_int32),
         ("n_kv_heads", ctypes.c_int32),
+        ("bits", ctypes.c_int32),
     ]
 
 
@@ -64,6 +66,7 @@ def _load():
     sigs = {
         "iq_status_string": (ctypes.c_char_p, [i32]),
         "iq_version": (i32, []),
+        "iq_codebook": (i32, [i32, vp, vp, vp]),
         "iq_rotation_bytes": (sz, [i32]),
         "iq_rotation_init": (i32, [vp, i32, vp, sz, vp]),
         "iq_quantize_append": (i32, [cp, vp, vp, vp, i32, i32, vp, vp, vp, i32, vp]),
@@ -89,7 +92,7 @@ def _load():
 
 
 lib = _load()
-EXPORTED = ("iq_status_string", "iq_version", "iq_rotation_bytes", "iq_rotation_init",
+EXPORTED = ("iq_status_string", "iq_version", "iq_codebook", "iq_rotation_bytes", "iq_rotation_init",
             "iq_quantize_append", "iq_decode_workspace_bytes", "iq_decode_attention",
             "iq_decode_step", "iq_prefill_workspace_bytes", "iq_prefill_attention",
             "iq_prefill_attention_varlen",
@@ -128,23 +131,38 @@ def _contig(t: torch.Tensor, name: str) -> torch.Tensor:
     return t
 
 
+def codebook(bits: int):
+    """(levels float64[2^bits], thresholds float32[2^bits - 1], alpha) of the
+    library's quantiser for 3- or 4-bit records (host only)."""
+    levels = np.zeros(1 << bits, dtype=np.float64)
+    thr = np.zeros((1 << bits) - 1, dtype=np.float32)
+    alpha = ctypes.c_float(0.0)
+    _check("iq_codebook", lib.iq_codebook(bits, levels.ctypes.data, thr.ctypes.data,
+                                          ctypes.addressof(alpha)))
+    return levels, thr, float(alpha.value)
+
+
 class PagedCache:
     """One layer's packed cache in caller-owned torch device memory.
 
-    k_codes/v_codes: uint8[num_pages][Hkv][64][48]; k_norms/v_norms: int16 holding
-    fp16 bit patterns [num_pages][Hkv][64]."""
+    k_codes/v_codes: uint8[num_pages][Hkv][64][48] (bits=3) or [..][64] (bits=4);
+    k_norms/v_norms: int16 holding fp16 bit patterns [num_pages][Hkv][64]."""
 
-    def __init__(self, num_pages: int, n_kv_heads: int, device="cuda", zero: bool = False):
+    def __init__(self, num_pages: int, n_kv_heads: int, device="cuda", zero: bool = False,
+                 bits: int = 3):
+        if bits not in (3, 4):
+            raise ValueError("bits must be 3 or 4")
         alloc = torch.zeros if zero else torch.empty
-        self.num_pages, self.n_kv_heads = int(num_pages), int(n_kv_heads)
+        self.num_pages, self.n_kv_heads, self.bits = int(num_pages), int(n_kv_heads), int(bits)
+        rec = CODE_BYTES if bits == 3 else CODE_BYTES4
         shp = (self.num_pages, self.n_kv_heads, PAGE_TOKENS)
-        self.k_codes = alloc(shp + (CODE_BYTES,), dtype=torch.uint8, device=device)
-        self.v_codes = alloc(shp + (CODE_BYTES,), dtype=torch.uint8, device=device)
+        self.k_codes = alloc(shp + (rec,), dtype=torch.uint8, device=device)
+        self.v_codes = alloc(shp + (rec,), dtype=torch.uint8, device=device)
         self.k_norms = alloc(shp, dtype=torch.int16, device=device)
         self.v_norms = alloc(shp, dtype=torch.int16, device=device)
         self._struct = IqCacheStruct(self.k_codes.data_ptr(), self.k_norms.data_ptr(),
                                      self.v_codes.data_ptr(), self.v_norms.data_ptr(),
-                                     self.num_pages, self.n_kv_heads)
+                                     self.num_pages, self.n_kv_heads, self.bits)
 
     @property
     def struct(self):

@@ -62,6 +62,7 @@ enum {
   IQ_HEAD_DIM = 128,         /* d                                               */
   IQ_PAGE_TOKENS = 64,       /* tokens per cache page                           */
   IQ_CODE_BYTES = 48,        /* 128 codes x 3 bits                              */
+  IQ_CODE_BYTES4 = 64,       /* 128 codes x 4 bits (4-bit caches)               */
   IQ_ROT_PARAMS = 256,       /* stored rotation parameters per kv head          */
   IQ_MAX_GROUP = 16          /* query heads per kv head handled by decode       */
 };
@@ -85,6 +86,20 @@ enum {
  * 4 + r, 8 + r) of chunk c of region (n, q) is byte lane n % 4 of group n / 4
  * of the record in slot 16 c + 4 q + r.  Norm arrays are slot-ordered for
  * both.  The struct is read during the call only.
+ *
+ * bits = 4 selects the 4-bit variant of the same pipeline (the pages' family
+ * spans 3 and 4 bits; "TurboQuant and RotorQuant ...": 3-4 bit KV cache
+ * compression): codes are the 16-level Gaussian Lloyd-Max quantiser's (see
+ * iq_codebook), 64 bytes per record, k_codes/v_codes [num_pages][n_kv_heads][64][64].
+ * A stored nibble is sign-magnitude: code c (0..15, ascending levels) is stored
+ * as c - 8 for c >= 8 and 15 - c below.  Record: dword d (bytes 4d..4d+3)
+ * holds coordinates 8d..8d+7, byte b of it coordinate 8d + b in its low nibble
+ * and 8d + 4 + b in its high one.  V blocks (4,096 bytes per (page, head)):
+ * 64 regions of 64 bytes; region n + 16 jq (n < 16, jq < 4) is 16 dwords, dword
+ * 4p + 2 th + q (p < 4, th < 2, q < 2) holds in byte r the token of slot
+ * 32 th + 16 q + 4 jq + r, its coordinate c = 32 (n / 4) + 4p + n % 4 in the low
+ * nibble and c + 16 in the high one.  bits = 0 or 3: the 3-bit records above.
+ * Prefill supports 3-bit caches only (IQ_ERR_UNSUPPORTED for bits = 4).
  */
 typedef struct {
   uint8_t *k_codes_dev;
@@ -93,6 +108,7 @@ typedef struct {
   uint16_t *v_norms_dev;
   int32_t num_pages;
   int32_t n_kv_heads;
+  int32_t bits;              /* 0 or 3: 3-bit records; 4: 4-bit records; else invalid */
 } iq_cache;
 
 /* Human-readable text for a status code (static storage). */
@@ -100,6 +116,25 @@ const char *iq_status_string(int32_t status);
 
 /* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
 int32_t iq_version(void);
+
+/*
+ * The scalar quantiser of a record width, as the kernels apply it (host
+ * only; no device is needed).  bits = 3: the Gaussian Lloyd-Max levels the
+ * pages print ("TurboQuant and RotorQuant ...", the 3-bit codebook); bits = 4:
+ * the 16-level Gaussian Lloyd-Max quantiser, computed by Lloyd's iteration
+ * (thresholds at the midpoints of adjacent levels, each level the mean of
+ * N(0, 1) over its cell) once per process.
+ *
+ * levels_host     : 2^bits doubles, written: the ascending levels.
+ * thresholds_host : 2^bits - 1 floats, written: the fp32 decision thresholds;
+ *                   code = number of thresholds u reaches (u >= t).
+ * level_scale     : may be null; written: alpha, the factor applied to the
+ *                   levels before they are rounded to the f16 operands of the
+ *                   matrix cores (1/alpha is folded into the norm factors).
+ * Errors          : IQ_ERR_INVALID_ARG for bits not 3 or 4 or a null array.
+ */
+iq_status iq_codebook(int32_t bits, double *levels_host, float *thresholds_host,
+                      float *level_scale);
 
 /*
  * Rotation setup ("RotaryQuant ...", abstract: WHT followed by block-diagonal
@@ -207,7 +242,8 @@ iq_status iq_decode_step(const iq_cache *cache, const void *rot_dev, const void 
  * out_dev        : float[n_q][n_q_heads][128], original space.
  * workspace_dev  : at least iq_prefill_workspace_bytes(...) bytes (currently 0).
  * Unsupported: q_start_pos + n_q > 262,144 (the causal range's page ids are
- * staged on chip), or n_q_heads / n_kv_heads not a power of two up to 128.
+ * staged on chip), n_q_heads / n_kv_heads not a power of two up to 128, or a
+ * 4-bit cache.
  */
 size_t iq_prefill_workspace_bytes(int32_t n_q, int32_t n_q_heads, int32_t n_kv_heads,
                                   int32_t q_start_pos);
@@ -232,8 +268,8 @@ iq_status iq_prefill_attention(const iq_cache *cache, const void *rot_dev, const
  * block_table_dev: int32[batch][max_pages_per_seq].
  * out_dev        : float[total_q][n_q_heads][128], original space; rows of no
  *                  sequence are not written.
- * Unsupported: max_kv_len > 262,144, or n_q_heads / n_kv_heads not a power of two
- * up to 128.  Device data beyond the bounds breaks the contract (wrong results,
+ * Unsupported: max_kv_len > 262,144, n_q_heads / n_kv_heads not a power of two
+ * up to 128, or a 4-bit cache.  Device data beyond the bounds breaks the contract (wrong results,
  * never reads outside the table or the cache).  total_q = 0 is a no-op.
  */
 iq_status iq_prefill_attention_varlen(const iq_cache *cache, const void *rot_dev, const void *q_dev,

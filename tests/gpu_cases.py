@@ -9,6 +9,7 @@ import numpy as np
 import torch
 
 from compressed_space_attention_amd import synth
+from oracle import isoquant4_oracle as O4
 from oracle import isoquant_oracle as O
 
 TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
@@ -18,12 +19,13 @@ class Scenario:
     """Sequences of given lengths, quantised into one paged cache by the GPU."""
 
     def __init__(self, seed, lens, hkv, dtype="bf16", outliers=False, shuffle=True,
-                 identity=False, extra_pages=2, kv_override=None, hold_last=False):
+                 identity=False, extra_pages=2, kv_override=None, hold_last=False, bits=3):
         """hold_last: append all but the last token of each sequence; that token's
         rows are kept in k_last / v_last ([B][Hkv][128], zeros for an empty
-        sequence) for a decode step to append."""
+        sequence) for a decode step to append.  bits: record width (3 or 4)."""
         from compressed_space_attention_amd import isoquant as iq
         self.iq = iq
+        self.bits = bits
         self.seed, self.lens, self.hkv, self.dtype = seed, [int(n) for n in lens], hkv, dtype
         self.quats = synth.identity_quaternions(hkv) if identity else synth.quaternions(seed, hkv)
         self.blocks = O.rotation_matrices(self.quats)
@@ -42,7 +44,7 @@ class Scenario:
             if n_tok else np.zeros(0, np.int32)
         dev = "cuda"
         self.rot = iq.rotation_init(self.quats, device=dev)
-        self.cache = iq.PagedCache(self.num_pages, hkv, device=dev, zero=True)
+        self.cache = iq.PagedCache(self.num_pages, hkv, device=dev, zero=True, bits=bits)
         self.bt_dev = torch.from_numpy(self.block_table).to(dev)
         self.lens_dev = torch.tensor(self.lens, dtype=torch.int32, device=dev)
         keep = np.ones(n_tok, bool)
@@ -64,14 +66,25 @@ class Scenario:
                                torch.from_numpy(self.pos[keep]).to(dev), self.bt_dev)
         torch.cuda.synchronize()
 
-    def host_cache(self) -> O.PagedCache:
+    def host_cache(self):
+        if self.bits == 4:
+            return O4.PagedCache4.from_arrays(*self.cache.to_host())
         return O.PagedCache.from_arrays(*self.cache.to_host())
 
     def oracle_cache(self):
-        c = O.PagedCache(self.num_pages, self.hkv)
-        info = O.quantize_append(c, self.blocks, self.k.double().numpy(), self.v.double().numpy(),
-                                 self.seq_idx, self.pos, self.block_table)
+        k, v = self.k.double().numpy(), self.v.double().numpy()
+        if self.bits == 4:
+            c = O4.PagedCache4(self.num_pages, self.hkv)
+            info = O4.quantize_append4(c, self.blocks, k, v, self.seq_idx, self.pos, self.block_table)
+        else:
+            c = O.PagedCache(self.num_pages, self.hkv)
+            info = O.quantize_append(c, self.blocks, k, v, self.seq_idx, self.pos, self.block_table)
         return c, info
+
+    def oracle_decode(self, cache, q, lens=None):
+        """The oracle's decode attention over `cache` (a host copy)."""
+        fn = O4.decode_attention4 if self.bits == 4 else O.decode_attention
+        return fn(cache, self.blocks, q, self.block_table, self.lens if lens is None else lens)
 
     def queries(self, seed, batch, hq, dtype=None):
         x = synth.normal(seed, (batch, hq, 128))
@@ -110,6 +123,42 @@ def code_parity(gpu: O.PagedCache, ref: O.PagedCache, info, scen: Scenario):
             if np.any(nb & ~info[name][h]["norm_near"]):
                 i = int(np.argwhere(nb & ~info[name][h]["norm_near"])[0][0])
                 raise AssertionError(f"{name} head {h} vector {i}: norm bits {gn[i]:#x} vs {rn[i]:#x}")
+    return stats
+
+
+def code_parity4(gpu: O4.PagedCache4, ref: O4.PagedCache4, info, scen: Scenario):
+    """code_parity for 4-bit caches: codes bit for bit outside the boundary
+    exemption; K records of agreeing vectors byte for byte; the V blocks of
+    the touched pages byte for byte where every code agrees; norms as there."""
+    page, slot = scen.block_table[scen.seq_idx, scen.pos // 64], scen.pos % 64
+    stats = {"codes": 0, "mismatch": 0, "near": 0, "norm_mismatch": 0}
+    for name in ("k", "v"):
+        all_same = True
+        for h in range(scen.hkv):
+            g_codes, r_codes = gpu.codes(name, page, h, slot), ref.codes(name, page, h, slot)
+            near = info[name][h]["near"]
+            bad = g_codes != r_codes
+            stats["codes"] += g_codes.size
+            stats["mismatch"] += int(bad.sum())
+            stats["near"] += int(near.sum())
+            if np.any(bad & ~near):
+                i, j = np.argwhere(bad & ~near)[0]
+                raise AssertionError(f"{name} head {h} vector {i} coord {j}: gpu {g_codes[i, j]} "
+                                     f"oracle {r_codes[i, j]} u={info[name][h]['u'][i, j]!r}")
+            same = ~bad.any(axis=1)
+            all_same &= bool(np.all(same))
+            if name == "k":
+                assert np.array_equal(gpu.k_codes[page, h, slot][same], ref.k_codes[page, h, slot][same])
+            gn = getattr(gpu, name + "_norms")[page, h, slot]
+            rn = getattr(ref, name + "_norms")[page, h, slot]
+            nb = gn != rn
+            stats["norm_mismatch"] += int(nb.sum())
+            if np.any(nb & ~info[name][h]["norm_near"]):
+                i = int(np.argwhere(nb & ~info[name][h]["norm_near"])[0][0])
+                raise AssertionError(f"{name} head {h} vector {i}: norm bits {gn[i]:#x} vs {rn[i]:#x}")
+        if name == "v" and all_same and len(page):
+            pg = np.unique(page)
+            assert np.array_equal(gpu.v_codes[pg], ref.v_codes[pg]), "V block bytes differ"
     return stats
 
 

@@ -44,8 +44,8 @@ def test_status_strings_and_sizes():
     assert iq.decode_workspace_bytes(0, 32, 4, 1024) == 0
 
 
-def _cache(hkv=4, pages=8):
-    return ctypes.byref(iq.IqCacheStruct(FAKE, FAKE, FAKE, FAKE, pages, hkv))
+def _cache(hkv=4, pages=8, bits=0):
+    return ctypes.byref(iq.IqCacheStruct(FAKE, FAKE, FAKE, FAKE, pages, hkv, bits))
 
 
 def test_rotation_init_validation():
@@ -70,6 +70,10 @@ def test_quantize_append_validation():
     assert L.iq_quantize_append(c, FAKE, FAKE, FAKE, 1, 0, FAKE, FAKE, FAKE, 8, None) == 0   # no-op
     empty = ctypes.byref(iq.IqCacheStruct(FAKE, FAKE, FAKE, FAKE, 0, 4))
     assert L.iq_quantize_append(empty, FAKE, FAKE, FAKE, 1, 4, FAKE, FAKE, FAKE, 8, None) == -1
+    for bad_bits in (1, 2, 5, 8, -3):                      # record width neither 3 nor 4
+        bad = _cache(bits=bad_bits)
+        assert L.iq_quantize_append(bad, FAKE, FAKE, FAKE, 1, 0, FAKE, FAKE, FAKE, 8, None) == -1
+        assert _decode(bad) == -1
 
 
 def _decode(c, hq=32, ws=10 ** 9, dtype=1, max_len=1024, max_pages=16, batch=1):
@@ -107,6 +111,16 @@ def test_decode_step_validation():
     assert _step(None) == -1
 
 
+def test_codebook_validation():
+    lv = np.zeros(16)
+    th = np.zeros(15, np.float32)
+    for bits in (0, 2, 5):
+        assert L.iq_codebook(bits, lv.ctypes.data, th.ctypes.data, None) == -1
+    assert L.iq_codebook(4, None, th.ctypes.data, None) == -1
+    assert L.iq_codebook(4, lv.ctypes.data, None, None) == -1
+    assert L.iq_codebook(4, lv.ctypes.data, th.ctypes.data, None) == 0
+
+
 def test_decode_workspace_is_monotone_in_context():
     a = iq.decode_workspace_bytes(1, 32, 4, 4096)
     b = iq.decode_workspace_bytes(1, 32, 4, 32768)
@@ -121,6 +135,10 @@ def test_prefill_validation():
     assert L.iq_prefill_attention(c, FAKE, FAKE, 1, 16, 64, 500, FAKE, 8, 0.0, FAKE, FAKE, 0, None) == -1
     assert L.iq_prefill_attention(c, FAKE, FAKE, 1, 0, 64, 0, FAKE, 8, 0.0, FAKE, FAKE, 0, None) == 0
     assert L.iq_prefill_attention(c, FAKE, FAKE, 9, 16, 64, 0, FAKE, 8, 0.0, FAKE, FAKE, 0, None) == -1
+    c4 = _cache(hkv=8, bits=4)                  # prefill reads 3-bit caches only
+    assert L.iq_prefill_attention(c4, FAKE, FAKE, 1, 16, 64, 0, FAKE, 8, 0.0, FAKE, FAKE, 0, None) == -2
+    assert L.iq_prefill_attention_varlen(c4, FAKE, FAKE, 1, 2, 64, 100, FAKE, FAKE, 60, 500, FAKE, 8,
+                                         0.0, FAKE, None, 0, None) == -2
 
 
 def test_dense_and_probe_validation():
