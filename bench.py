@@ -33,6 +33,7 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
 MFMA_F16_PEAK_TFLOPS = 2500.0    # MI355X dense f16 matrix peak, published
 METRIC = "packed-KV decode attention GB/s (% of HBM peak) + tokens/s at 32K ctx"
 REC_BYTES = 100                  # K + V records per (token, kv head): 2 x (48 + 2)
+REC_BYTES4 = 132                 # the same with 4-bit records: 2 x (64 + 2)
 
 
 def parse():
@@ -41,6 +42,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=160)
     ap.add_argument("--workload", default="gqa_decode_32k_32q4kv")
+    ap.add_argument("--bits", type=int, default=3, choices=(3, 4),
+                    help="record width of the measured packed cache (3: the method's; 4: the 4-bit variant)")
     ap.add_argument("--ring-bytes", type=float, default=1.0e9,
                     help="minimum bytes of distinct layer caches cycled by the steps")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -67,12 +70,12 @@ class DecodeLayer:
     """One layer: rotation, packed cache holding context-1 tokens, and the
     current token's q/k/v."""
 
-    def __init__(self, iq, synth, w, idx, block_table, num_pages, device):
+    def __init__(self, iq, synth, w, idx, block_table, num_pages, device, bits=3):
         import torch
         self.idx = idx
         seed = w.seed * 1000 + idx
         self.rot = iq.rotation_init(synth.quaternions(seed, w.n_kv_heads), device=device)
-        self.cache = iq.PagedCache(num_pages, w.n_kv_heads, device=device)
+        self.cache = iq.PagedCache(num_pages, w.n_kv_heads, device=device, bits=bits)
         lens = w.seq_lens()
         n_prev = [int(n) - 1 for n in lens]
         total = sum(n_prev)
@@ -138,13 +141,14 @@ def run_decode(args):
     block_table = torch.from_numpy(bt_np).to(device)
     seq_lens = torch.from_numpy(lens).to(device)
     max_len = int(lens.max())
-    kv_bytes = REC_BYTES * int(lens.sum()) * w.n_kv_heads            # read by one decode call
-    layer_bytes = num_pages * w.n_kv_heads * 64 * REC_BYTES
+    rec_bytes = REC_BYTES if args.bits == 3 else REC_BYTES4
+    kv_bytes = rec_bytes * int(lens.sum()) * w.n_kv_heads            # read by one decode call
+    layer_bytes = num_pages * w.n_kv_heads * 64 * rec_bytes
     ring = max(1, math.ceil(args.ring_bytes / layer_bytes))
     log(f"[bench] workload {w.name}: {kv_bytes / 1e6:.1f} MB packed KV per call, ring of {ring} layers "
         f"({ring * layer_bytes / 1e9:.2f} GB)")
     t0 = time.time()
-    layers = [DecodeLayer(iq, synth, w, i, block_table, num_pages, device) for i in range(ring)]
+    layers = [DecodeLayer(iq, synth, w, i, block_table, num_pages, device, args.bits) for i in range(ring)]
     torch.cuda.synchronize()
     log(f"[bench] caches built in {time.time() - t0:.1f} s")
     ws = torch.empty(max(16, iq.decode_workspace_bytes(w.batch, w.n_q_heads, w.n_kv_heads, max_len)),
@@ -238,7 +242,7 @@ def run_decode(args):
                  + ("shuffled" if w.shuffle_pages else "contiguous") + " 64-token page table"),
         "config": {
             "workload": w.name, "batch": w.batch, "context": max_len, "n_q_heads": w.n_q_heads,
-            "n_kv_heads": w.n_kv_heads, "head_dim": 128, "page_tokens": 64,
+            "n_kv_heads": w.n_kv_heads, "head_dim": 128, "page_tokens": 64, "record_bits": args.bits,
             "packed_kv_bytes_per_step": kv_bytes, "layer_ring": ring,
             "step": "one layer's decode step: quantise-append of the current token fused into "
                     "decode attention (iq_decode_step)",
@@ -250,7 +254,7 @@ def run_decode(args):
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(w.name),
+            "traffic": measured_traffic(w.name) if args.bits == 3 else None,
             "algorithmic_bytes": kv_bytes,
         },
         "detail": {
@@ -267,6 +271,9 @@ def run_decode(args):
         torch.cuda.empty_cache()
         result["detail"]["dense_bf16_baseline"] = run_dense_aux(w, lens, bt_np, num_pages, t_decode)
         log(f"[bench] dense bf16 baseline: {result['detail']['dense_bf16_baseline']}")
+        if args.bits == 3:
+            result["detail"]["four_bit"] = run_four_bit_aux(w, lens, bt_np, num_pages, t_decode, t_step)
+            log(f"[bench] 4-bit records: {result['detail']['four_bit']}")
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline_decode(args, w, layer0, bt_np, lens)
     return result
@@ -369,6 +376,86 @@ def run_dense_aux(w, lens, bt_np, num_pages, t_packed, ring_bytes=1.0e9, steps=4
             "packed_speedup": round(t / t_packed, 3)}
 
 
+def run_four_bit_aux(w, lens, bt_np, num_pages, t_decode3, t_step3, ring_bytes=1.0e9, steps=400):
+    """The 4-bit variant on the same workload: a ring of 4-bit layer caches
+    (same paging, same synthetic recipe), its decode step and decode call
+    timed like the 3-bit ones (graph replay, HIP events on the launch stream)."""
+    import torch
+
+    from compressed_space_attention_amd import isoquant as iq
+    from compressed_space_attention_amd import synth
+    dev = "cuda"
+    block_table = torch.from_numpy(bt_np).to(dev)
+    seq_lens = torch.from_numpy(lens).to(dev)
+    max_len = int(lens.max())
+    kv_bytes = REC_BYTES4 * int(lens.sum()) * w.n_kv_heads
+    layer_bytes = num_pages * w.n_kv_heads * 64 * REC_BYTES4
+    ring = max(1, math.ceil(ring_bytes / layer_bytes))
+    n_prev = [int(n) - 1 for n in lens]
+    seq_idx = torch.cat([torch.full((n,), b, dtype=torch.int32) for b, n in enumerate(n_prev)]).to(dev)
+    pos = torch.cat([torch.arange(n, dtype=torch.int32) for n in n_prev]).to(dev)
+    total = sum(n_prev)
+    layers = []
+    for i in range(ring):
+        seed = w.seed * 1000 + 700 + i
+        rot = iq.rotation_init(synth.quaternions(seed, w.n_kv_heads), device=dev)
+        c = iq.PagedCache(num_pages, w.n_kv_heads, device=dev, bits=4)
+        chunk = 1 << 16
+        for s0 in range(0, total, chunk):
+            e = min(total, s0 + chunk)
+            k = synth.draw_normal_device(seed * 7 + s0, (e - s0, w.n_kv_heads, 128), torch.bfloat16, dev)
+            v = synth.draw_normal_device(seed * 11 + s0, (e - s0, w.n_kv_heads, 128), torch.bfloat16, dev)
+            iq.quantize_append(c, rot, k, v, seq_idx[s0:e], pos[s0:e], block_table)
+        kn = synth.draw_normal_device(seed * 13, (w.batch, w.n_kv_heads, 128), torch.bfloat16, dev)
+        vn = synth.draw_normal_device(seed * 17, (w.batch, w.n_kv_heads, 128), torch.bfloat16, dev)
+        q = synth.draw_normal_device(seed * 19, (w.batch, w.n_q_heads, 128), torch.bfloat16, dev)
+        out = torch.empty((w.batch, w.n_q_heads, 128), dtype=torch.float32, device=dev)
+        layers.append((c, rot, kn, vn, q, out))
+    ws = torch.empty(max(16, iq.decode_workspace_bytes(w.batch, w.n_q_heads, w.n_kv_heads, max_len)),
+                     dtype=torch.uint8, device=dev)
+
+    def run(n, mode):
+        for i in range(n):
+            c, rot, kn, vn, q, out = layers[i % ring]
+            if mode == "step":
+                iq.decode_step(c, rot, q, kn, vn, block_table, seq_lens, max_len, out=out, workspace=ws)
+            else:
+                iq.decode_attention(c, rot, q, block_table, seq_lens, max_len, out=out, workspace=ws)
+
+    def timed(mode):
+        run(ring, mode)
+        torch.cuda.synchronize()
+        reps = max(1, steps // ring)
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                run(ring, mode)
+        torch.cuda.current_stream().wait_stream(s)
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / 1e3 / (reps * ring)
+
+    t_step = timed("step")
+    t_dec = timed("decode")
+    del layers
+    torch.cuda.empty_cache()
+    return {"kernel": "decode_split_kernel<..., 4-bit> + decode_merge_kernel",
+            "packed_kv_bytes_per_call": kv_bytes,
+            "step_us": round(t_step * 1e6, 3), "decode_call_us": round(t_dec * 1e6, 3),
+            "decode_call_gbs": round(kv_bytes / t_dec / 1e9, 1),
+            "decode_call_frac_of_hbm_peak": round(kv_bytes / t_dec / 1e9 / HBM_PEAK_GBS, 4),
+            "time_vs_3bit_decode_call": round(t_dec / t_decode3, 3),
+            "time_vs_3bit_step": round(t_step / t_step3, 3)}
+
+
 def run_prefill_aux(iters=30):
     """The chunked-prefill workload (8192-token quantise-append into a 32,768-token
     cache, then causal attention of the last 512 positions x 64 query heads):
@@ -434,10 +521,13 @@ def cpu_baseline_decode(args, w, layer, bt_np, lens):
     quantise-append the current token, then decode over the layer's cache."""
     import threadpoolctl
 
+    from oracle import isoquant4_oracle as O4
     from oracle import isoquant_oracle as O
 
-    host = O.PagedCache.from_arrays(*layer.cache.to_host())
-    quats = None
+    four = layer.cache.bits == 4
+    host = (O4.PagedCache4 if four else O.PagedCache).from_arrays(*layer.cache.to_host())
+    append = O4.quantize_append4 if four else O.quantize_append
+    decode = O4.decode_attention4 if four else O.decode_attention
     from compressed_space_attention_amd import synth
     quats = synth.quaternions(w.seed * 1000 + layer.idx, w.n_kv_heads)
     blocks = O.rotation_matrices(quats)
@@ -446,13 +536,13 @@ def cpu_baseline_decode(args, w, layer, bt_np, lens):
     v_new = layer.v_new.float().cpu().numpy().astype(np.float64)
     pos_new = layer.pos_new.cpu().numpy()
     seq_new = layer.seq_new.cpu().numpy()
-    kv_bytes = REC_BYTES * int(lens.sum()) * w.n_kv_heads
+    kv_bytes = (REC_BYTES4 if four else REC_BYTES) * int(lens.sum()) * w.n_kv_heads
     info = threadpoolctl.threadpool_info()
     threads = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
     steps, t0 = 0, time.perf_counter()
     while True:
-        O.quantize_append(host, blocks, k_new, v_new, seq_new, pos_new, bt_np)
-        O.decode_attention(host, blocks, q, bt_np, lens)
+        append(host, blocks, k_new, v_new, seq_new, pos_new, bt_np)
+        decode(host, blocks, q, bt_np, lens)
         steps += 1
         el = time.perf_counter() - t0
         if el >= args.cpu_seconds or el * (steps + 1) / steps > 30.0:
@@ -462,7 +552,7 @@ def cpu_baseline_decode(args, w, layer, bt_np, lens):
         "unit": "GB/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": f"{steps} oracle steps of one layer (append 1 token + decode over "
+        "sample": f"{steps} {'4-bit ' if four else ''}oracle steps of one layer (append 1 token + decode over "
                   f"{int(lens.max())} tokens, {w.n_q_heads}q/{w.n_kv_heads}kv) in {el:.1f} s; "
                   f"host has {os.cpu_count()} logical CPUs",
     }
@@ -495,8 +585,12 @@ def write_traffic_record(root: str, workload: str = "gqa_decode_32k_32q4kv", cal
             raise SystemExit(f"expected one kernel, found {len(hits)}")
         return hits[0]
 
-    split = lambda k: "decode_split_kernel<" in k and k.split("<")[1].split(">")[0].endswith("false") \
-        and "dense" not in k
+    def split(k):  # decode_split_kernel<PACK8, waves, APPEND = false, record bits = 3>
+        if "decode_split_kernel<" not in k or "dense" in k:
+            return False
+        targs = [a.strip() for a in k.split("<")[1].split(">")[0].split(",")]
+        return len(targs) == 4 and targs[2] == "false" and targs[3] == "3"
+
     merge = lambda k: "decode_merge_kernel<true>" in k
     copy = lambda k: "copy" in k.lower()
     fetch, write = medians("pmc_FETCH_SIZE"), medians("pmc_WRITE_SIZE")
