@@ -256,8 +256,7 @@ iq_status iq_prefill_attention(const iq_cache* cache, const void* rot_dev, const
   if ((int64_t)q_start_pos + n_q > (int64_t)max_pages * IQ_PAGE_TOKENS) return IQ_ERR_INVALID_ARG;
   if (n_q == 0) return IQ_OK;
   const int group = n_q_heads / cache->n_kv_heads;
-  if (!pow2(group) || group > 128 || cache->n_kv_heads > 65535 || cache->bits == 4)
-    return IQ_ERR_UNSUPPORTED;
+  if (!pow2(group) || group > 128 || cache->n_kv_heads > 65535) return IQ_ERR_UNSUPPORTED;
   if ((int64_t)q_start_pos + n_q > (int64_t)iq::kPrefillMaxPages * IQ_PAGE_TOKENS)
     return IQ_ERR_UNSUPPORTED;
   const iq::PrefillPlan plan = iq::plan_prefill(n_q, n_q_heads, cache->n_kv_heads, q_start_pos, device_cu_count());
@@ -287,8 +286,7 @@ iq_status iq_prefill_attention_varlen(const iq_cache* cache, const void* rot_dev
   if (total_q == 0 || max_q_per_seq == 0) return IQ_OK;
   if (!q_dev || !out_dev) return IQ_ERR_INVALID_ARG;
   const int group = n_q_heads / cache->n_kv_heads;
-  if (!pow2(group) || group > 128 || cache->n_kv_heads > 65535 || cache->bits == 4)
-    return IQ_ERR_UNSUPPORTED;
+  if (!pow2(group) || group > 128 || cache->n_kv_heads > 65535) return IQ_ERR_UNSUPPORTED;
   if ((int64_t)max_kv_len > (int64_t)iq::kPrefillMaxPages * IQ_PAGE_TOKENS) return IQ_ERR_UNSUPPORTED;
   const iq::PrefillPlan plan =
       iq::plan_prefill(max_q_per_seq, n_q_heads, cache->n_kv_heads, 0, device_cu_count());

@@ -1,4 +1,4 @@
-// Chunked causal prefill attention on the packed 3-bit cache.
+// Chunked causal prefill attention on the packed 3-bit (or 4-bit) cache.
 //
 // "RotaryQuant: Fitting 120B MoE Models on Consumer Hardware via Fused
 // Compressed-Space Attention", abstract: attention directly on packed 3-bit
@@ -28,6 +28,9 @@
 //   * only pages that reach past the smallest query position of the tile are
 //     masked.
 // The page ids of the whole causal range are staged in LDS once.
+// 4-bit records (BITS = 4): a page's 8,192 code bytes fill the same raw slot
+// (16-byte units: a quarter of a K record, or a quarter of a V region, per
+// lane), and unpack into the same f16 buffers.
 #include <math.h>
 #include <stdlib.h>
 
@@ -64,6 +67,7 @@ struct PrefillArgs {
   float score_factor;  // softmax_scale * log2(e) / (128 * alpha)
   float out_factor;    // 1 / (sqrt(128) * alpha)
   float* out;
+  Levels4 lv4;         // 4-bit records: thresholds and f16 level tables
 };
 
 // Direct-to-LDS loads, issued from inline asm so that the compiler does not
@@ -75,7 +79,9 @@ struct PrefillArgs {
 typedef __attribute__((address_space(3))) void* pf_lds_ptr;
 __device__ __forceinline__ void pf_dma(const void* g, void* lds, int size) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(pf_lds_ptr)lds);
-  if (size == 12)
+  if (size == 16)
+    asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(m0) : "memory");
+  else if (size == 12)
     asm volatile("global_load_lds_dwordx3 %0, off" ::"v"(g), "{m0}"(m0) : "memory");
   else
     asm volatile("global_load_lds_dword %0, off" ::"v"(g), "{m0}"(m0) : "memory");
@@ -106,7 +112,10 @@ __device__ __forceinline__ float times_norm2(float x, const u2& n, int r) {
 // the K records of tokens 8w..8w+7, lanes 32-63 chunk w/2 of V regions
 // 32(w%2) .. +31.  Wave 0 also brings the K norms (lanes 0-31) and V norms
 // (lanes 32-63).  Returns the number of loads issued.
-template <int W>
+// BITS = 4: the same split in 16-byte units of the 4,096-byte K and V blocks,
+// contiguous per wave: four waves, bytes 1024w.. of each block; eight waves,
+// lanes 0-31 bytes 512w.. of the K block and lanes 32-63 of the V block.
+template <int W, int BITS>
 __device__ __forceinline__ int pf_issue(const PrefillArgs& a, int page_id, int g, int wave, int lane,
                                         uint8_t* slot) {
   // an id outside the cache (a table that breaks the contract) is clamped into
@@ -114,7 +123,15 @@ __device__ __forceinline__ int pf_issue(const PrefillArgs& a, int page_id, int g
   const uint32_t page = min((uint32_t)page_id, (uint32_t)a.num_pages - 1u);
   const size_t base = ((size_t)page * a.hkv + g) * kPage;
   uint8_t* dst = slot + wave * (kRawPage / W);
-  if (W == 4) {
+  if (BITS == 4) {
+    const size_t blk = base * kRec4;
+    if (W == 4) {
+      pf_dma(a.k_codes + blk + 1024 * wave + 16 * lane, dst, 16);
+      pf_dma(a.v_codes + blk + 1024 * wave + 16 * lane, dst + 1024, 16);
+    } else {
+      pf_dma((lane < 32 ? a.k_codes : a.v_codes) + blk + 512 * wave + 16 * (lane & 31), dst, 16);
+    }
+  } else if (W == 4) {
     pf_dma(a.k_codes + base * kRec + 768 * wave + 12 * lane, dst, 12);
     pf_dma(a.v_codes + (base + lane) * kRec + 12 * wave, dst + 1024, 12);
   } else {
@@ -142,7 +159,8 @@ __device__ __forceinline__ void pf_unpack_k(const u3& ck, int tok, int j, _Float
   }
 }
 // Chunk c of V region `region` = (n, q) = (region % 16, region / 16): tokens
-// 16c + 4q + r of coordinate rows 16m + n, into the f16 V^T buffer.
+// 16c + 4q + r, selector m, into row 16m + n of the f16 V^T buffer (row 16m + n
+// holds coordinate 32 (n / 4) + 4m + n % 4: accumulator order).
 __device__ __forceinline__ void pf_unpack_v(const u3& cv, int region, int c, _Float16* sv) {
   uint32_t z[8];
   group_to_selectors(cv.x, cv.y, cv.z, z);
@@ -152,13 +170,51 @@ __device__ __forceinline__ void pf_unpack_v(const u3& cv, int region, int c, _Fl
     *reinterpret_cast<u2*>(sv + (16 * m + n) * kVStride + 16 * c + 4 * q) = selector_to_f16(z[m]);
 }
 
+// 4-bit: quarter j of token tok's record (dword kk = coordinates 32j + 8kk
+// .. + 7) into the f16 K^ buffer.
+__device__ __forceinline__ void pf_unpack_k4(const u4& ck, int tok, int j, _Float16* sk,
+                                             const Levels4& lv) {
+  u4* dst = reinterpret_cast<u4*>(sk + tok * kKStride + 32 * j);
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) dst[kk] = __builtin_bit_cast(u4, dword4_to_h8(ck[kk], lv));
+}
+// 4-bit: dwords 4p .. 4p+3 of V region `region` = n + 16 jq: dword (th, q)
+// holds tokens 32 th + 16 q + 4 jq + r of coordinate 32 (n / 4) + 4p + n % 4
+// (low nibbles) and that + 16 (high nibbles).  The V^T buffer is in
+// accumulator order, as for 3-bit pages: row 16m + n holds coordinate
+// 32 (n / 4) + 4m + n % 4, so the low nibbles go to row 16p + n and the high
+// ones to row 16 (p + 4) + n.
+__device__ __forceinline__ void pf_unpack_v4(const u4& cv, int region, int p, _Float16* sv,
+                                             const Levels4& lv) {
+  const int n = region & 15, jq = region >> 4;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const int tok = 32 * (d >> 1) + 16 * (d & 1) + 4 * jq;
+    const uint32_t w = cv[d];
+    *reinterpret_cast<u2*>(sv + (16 * p + n) * kVStride + tok) = nibbles_to_f16(w & 0x0F0F0F0Fu, lv);
+    *reinterpret_cast<u2*>(sv + (16 * (p + 4) + n) * kVStride + tok) =
+        nibbles_to_f16((w >> 4) & 0x0F0F0F0Fu, lv);
+  }
+}
+
 // Unpack this thread's groups of a raw page (four waves: a K group and a V
 // chunk; eight waves: one of the two) into the f16 buffers.
-template <int W>
+template <int W, int BITS>
 __device__ __forceinline__ void pf_unpack(const uint8_t* slot, int wave, int lane, _Float16* sk,
-                                          _Float16* sv, uint16_t* snorm) {
+                                          _Float16* sv, uint16_t* snorm, const Levels4& lv) {
   const uint8_t* raw = slot + wave * (kRawPage / W) + 16 * lane;
-  if (W == 4) {
+  if (BITS == 4) {
+    // 16-byte unit u of a block: K token u / 4, quarter u % 4; V region u / 4, dwords 4(u % 4)..
+    if (W == 4) {
+      const int u = 64 * wave + lane;
+      pf_unpack_k4(*reinterpret_cast<const u4*>(raw), u >> 2, u & 3, sk, lv);
+      pf_unpack_v4(*reinterpret_cast<const u4*>(raw + 1024), u >> 2, u & 3, sv, lv);
+    } else {
+      const int u = 32 * wave + (lane & 31);
+      if (lane < 32) pf_unpack_k4(*reinterpret_cast<const u4*>(raw), u >> 2, u & 3, sk, lv);
+      else pf_unpack_v4(*reinterpret_cast<const u4*>(raw), u >> 2, u & 3, sv, lv);
+    }
+  } else if (W == 4) {
     pf_unpack_k(*reinterpret_cast<const u3*>(raw), 16 * wave + (lane >> 2), lane & 3, sk);
     pf_unpack_v(*reinterpret_cast<const u3*>(raw + 1024), lane, wave, sv);
   } else if (lane < 32) {
@@ -183,7 +239,7 @@ __device__ __forceinline__ void pf_wait_vm(int n) {
   }
 }
 
-template <int RB>
+template <int RB, int BITS>
 __global__ __launch_bounds__(64 * pf_waves<RB>(), 1) void prefill_kernel(PrefillArgs a) {
   constexpr int W = pf_waves<RB>();
   const int g = blockIdx.x, tile = blockIdx.y, b = blockIdx.z;
@@ -272,9 +328,9 @@ __global__ __launch_bounds__(64 * pf_waves<RB>(), 1) void prefill_kernel(Prefill
   // raw loads this wave issues per page
   const int per_page = (W == 4 ? 2 : 1) + (wave == 0 ? 1 : 0);
   // first three pages in flight, the first unpacked
-  for (int p = 0; p < 3 && p < n_pages; ++p) pf_issue<W>(a, s_pt[p], g, wave, lane, s_raw[p]);
+  for (int p = 0; p < 3 && p < n_pages; ++p) pf_issue<W, BITS>(a, s_pt[p], g, wave, lane, s_raw[p]);
   pf_wait_vm(per_page * (min(n_pages, 3) - 1));
-  pf_unpack<W>(s_raw[0], wave, lane, s_k[0], s_v[0], s_norm[0]);
+  pf_unpack<W, BITS>(s_raw[0], wave, lane, s_k[0], s_v[0], s_norm[0], a.lv4);
   __builtin_amdgcn_s_waitcnt(kPfWaitLgkm0);
   __builtin_amdgcn_s_barrier();
 
@@ -296,7 +352,7 @@ __global__ __launch_bounds__(64 * pf_waves<RB>(), 1) void prefill_kernel(Prefill
   auto page_step = [&](int pg, auto masked_tag) {
     constexpr bool MASKED = decltype(masked_tag)::value;
     const int f = pg & 1;
-    if (pg + 3 < n_pages) pf_issue<W>(a, s_pt[pg + 3], g, wave, lane, s_raw[pg % 3]);
+    if (pg + 3 < n_pages) pf_issue<W, BITS>(a, s_pt[pg + 3], g, wave, lane, s_raw[pg % 3]);
 
     // ---- S^T tiles [token block tb][row block cb]: each K^ fragment feeds
     // every row block (hi and lo parts of Q') ----
@@ -321,7 +377,7 @@ __global__ __launch_bounds__(64 * pf_waves<RB>(), 1) void prefill_kernel(Prefill
     if (pg + 1 < n_pages) {
       // loads of this wave still allowed in flight: those of pages pg+2, pg+3
       pf_wait_vm(per_page * min(2, n_pages - 2 - pg));
-      pf_unpack<W>(s_raw[(pg + 1) % 3], wave, lane, s_k[f ^ 1], s_v[f ^ 1], s_norm[f ^ 1]);
+      pf_unpack<W, BITS>(s_raw[(pg + 1) % 3], wave, lane, s_k[f ^ 1], s_v[f ^ 1], s_norm[f ^ 1], a.lv4);
     }
 
     const uint16_t* nrm = s_norm[f];
@@ -513,17 +569,26 @@ hipError_t launch_prefill_varlen(const CacheView& c, const float* rot, const voi
   a.cu_q = cu_q;
   a.q_starts = q_starts;
   a.max_pages = max_pages;
+  const bool four = c.bits == 4;
+  const double alpha = four ? (double)codebook4().alpha : (double)kLevelScale;
+  a.lv4 = four ? codebook4().lv : Levels4{};
   const double log2e = 1.4426950408889634;
-  a.score_factor = (float)((double)softmax_scale * log2e / (128.0 * (double)kLevelScale));
-  a.out_factor = (float)(1.0 / (sqrt(128.0) * (double)kLevelScale));
+  a.score_factor = (float)((double)softmax_scale * log2e / (128.0 * alpha));
+  a.out_factor = (float)(1.0 / (sqrt(128.0) * alpha));
   a.out = out;
   int rb = 1;
   if (const char* env = getenv("IQ_PREFILL_WAVES")) rb = atoi(env) == 4 ? 2 : 1;
   const dim3 grid(c.hkv, plan.row_tiles, batch);
-  if (rb == 2)
-    hipLaunchKernelGGL(prefill_kernel<2>, grid, dim3(64 * pf_waves<2>()), 0, stream, a);
-  else
-    hipLaunchKernelGGL(prefill_kernel<1>, grid, dim3(64 * pf_waves<1>()), 0, stream, a);
+#define IQ_PREFILL(RB, B) \
+  hipLaunchKernelGGL((prefill_kernel<RB, B>), grid, dim3(64 * pf_waves<RB>()), 0, stream, a)
+  if (rb == 2) {
+    if (four) IQ_PREFILL(2, 4);
+    else IQ_PREFILL(2, 3);
+  } else {
+    if (four) IQ_PREFILL(1, 4);
+    else IQ_PREFILL(1, 3);
+  }
+#undef IQ_PREFILL
   return hipGetLastError();
 }
 

@@ -99,7 +99,7 @@ enum {
  * 4p + 2 th + q (p < 4, th < 2, q < 2) holds in byte r the token of slot
  * 32 th + 16 q + 4 jq + r, its coordinate c = 32 (n / 4) + 4p + n % 4 in the low
  * nibble and c + 16 in the high one.  bits = 0 or 3: the 3-bit records above.
- * Prefill supports 3-bit caches only (IQ_ERR_UNSUPPORTED for bits = 4).
+ * Every entry point taking an iq_cache handles both widths.
  */
 typedef struct {
   uint8_t *k_codes_dev;
@@ -242,8 +242,7 @@ iq_status iq_decode_step(const iq_cache *cache, const void *rot_dev, const void 
  * out_dev        : float[n_q][n_q_heads][128], original space.
  * workspace_dev  : at least iq_prefill_workspace_bytes(...) bytes (currently 0).
  * Unsupported: q_start_pos + n_q > 262,144 (the causal range's page ids are
- * staged on chip), n_q_heads / n_kv_heads not a power of two up to 128, or a
- * 4-bit cache.
+ * staged on chip), or n_q_heads / n_kv_heads not a power of two up to 128.
  */
 size_t iq_prefill_workspace_bytes(int32_t n_q, int32_t n_q_heads, int32_t n_kv_heads,
                                   int32_t q_start_pos);
@@ -268,8 +267,8 @@ iq_status iq_prefill_attention(const iq_cache *cache, const void *rot_dev, const
  * block_table_dev: int32[batch][max_pages_per_seq].
  * out_dev        : float[total_q][n_q_heads][128], original space; rows of no
  *                  sequence are not written.
- * Unsupported: max_kv_len > 262,144, n_q_heads / n_kv_heads not a power of two
- * up to 128, or a 4-bit cache.  Device data beyond the bounds breaks the contract (wrong results,
+ * Unsupported: max_kv_len > 262,144, or n_q_heads / n_kv_heads not a power of two
+ * up to 128.  Device data beyond the bounds breaks the contract (wrong results,
  * never reads outside the table or the cache).  total_q = 0 is a no-op.
  */
 iq_status iq_prefill_attention_varlen(const iq_cache *cache, const void *rot_dev, const void *q_dev,

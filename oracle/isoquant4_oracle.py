@@ -298,3 +298,29 @@ def decode_attention4(cache: PagedCache4, blocks_all, q, block_table, seq_lens, 
             o_rot = O._softmax_weighted(sc * qr @ dequantize_rotated4(kc, kn).T, dequantize_rotated4(vc, vn))
             out[b, g * grp:(g + 1) * grp] = O.inverse_rotate(o_rot, blocks_all[g])
     return out
+
+
+def prefill_attention4(cache: PagedCache4, blocks_all, q, q_start, block_table_row, scale=None,
+                       rows=None):
+    """As isoquant_oracle.prefill_attention over 4-bit records: query i sits at
+    position q_start + i and attends keys 0 .. q_start + i."""
+    q = np.asarray(q, dtype=np.float64)
+    n_q, hq, _ = q.shape
+    hkv = cache.n_kv_heads
+    grp = hq // hkv
+    sc = O.default_scale(scale)
+    rows = np.arange(n_q) if rows is None else np.asarray(rows)
+    kv_len = int(q_start + rows.max() + 1)
+    bt = np.asarray(block_table_row).reshape(1, -1)
+    out = np.zeros((len(rows), hq, HEAD_DIM))
+    for g in range(hkv):
+        kc, kn = cache.gather(bt, 0, kv_len, g, "k")
+        vc, vn = cache.gather(bt, 0, kv_len, g, "v")
+        k_rot = dequantize_rotated4(kc, kn)
+        v_rot = dequantize_rotated4(vc, vn)
+        for ri, i in enumerate(rows):
+            visible = int(q_start + i + 1)
+            qr = O.forward_rotate(q[i, g * grp:(g + 1) * grp], blocks_all[g])
+            o_rot = O._softmax_weighted(sc * qr @ k_rot[:visible].T, v_rot[:visible])
+            out[ri, g * grp:(g + 1) * grp] = O.inverse_rotate(o_rot, blocks_all[g])
+    return out

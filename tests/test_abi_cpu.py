@@ -135,10 +135,11 @@ def test_prefill_validation():
     assert L.iq_prefill_attention(c, FAKE, FAKE, 1, 16, 64, 500, FAKE, 8, 0.0, FAKE, FAKE, 0, None) == -1
     assert L.iq_prefill_attention(c, FAKE, FAKE, 1, 0, 64, 0, FAKE, 8, 0.0, FAKE, FAKE, 0, None) == 0
     assert L.iq_prefill_attention(c, FAKE, FAKE, 9, 16, 64, 0, FAKE, 8, 0.0, FAKE, FAKE, 0, None) == -1
-    c4 = _cache(hkv=8, bits=4)                  # prefill reads 3-bit caches only
-    assert L.iq_prefill_attention(c4, FAKE, FAKE, 1, 16, 64, 0, FAKE, 8, 0.0, FAKE, FAKE, 0, None) == -2
-    assert L.iq_prefill_attention_varlen(c4, FAKE, FAKE, 1, 2, 64, 100, FAKE, FAKE, 60, 500, FAKE, 8,
-                                         0.0, FAKE, None, 0, None) == -2
+    c4 = _cache(hkv=8, bits=4)                  # the same checks on a 4-bit cache
+    assert L.iq_prefill_attention(c4, FAKE, FAKE, 1, 16, 24, 0, FAKE, 8, 0.0, FAKE, FAKE, 0, None) == -2
+    assert L.iq_prefill_attention(c4, FAKE, FAKE, 1, 0, 64, 0, FAKE, 8, 0.0, FAKE, FAKE, 0, None) == 0
+    c5 = _cache(hkv=8, bits=5)
+    assert L.iq_prefill_attention(c5, FAKE, FAKE, 1, 16, 64, 0, FAKE, 8, 0.0, FAKE, FAKE, 0, None) == -1
 
 
 def test_dense_and_probe_validation():

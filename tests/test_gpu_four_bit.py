@@ -170,9 +170,83 @@ def test_decode4_single_token_is_its_value():
             assert np.max(np.abs(rows - v0)) <= 1e-3 * np.max(np.abs(v0))
 
 
-def test_prefill_rejects_four_bit_cache():
-    s = Scenario(1470, [64], hkv=2, dtype="bf16", bits=4)
-    q = s.queries(1471, 64, 8).cuda()
-    with pytest.raises(s.iq.IsoQuantError) as e:
-        s.iq.prefill_attention(s.cache, s.rot, q, 0, s.bt_dev[0])
-    assert e.value.status == -2
+PREFILL4_CASES = [
+    # (cache length, n_q, hkv, hq, waves per workgroup or None): groups 1..128,
+    # ragged last tiles, a single query, both workgroup shapes
+    (1000, 200, 2, 16, None),
+    (300, 300, 1, 1, None),
+    (700, 77, 2, 8, 4),
+    (640, 1, 2, 4, None),
+    (200, 70, 1, 128, 4),
+]
+
+
+def _with_prefill_waves(waves, fn):
+    old = os.environ.get("IQ_PREFILL_WAVES")
+    try:
+        if waves is None:
+            os.environ.pop("IQ_PREFILL_WAVES", None)
+        else:
+            os.environ["IQ_PREFILL_WAVES"] = str(waves)
+        return fn()
+    finally:
+        if old is None:
+            os.environ.pop("IQ_PREFILL_WAVES", None)
+        else:
+            os.environ["IQ_PREFILL_WAVES"] = old
+
+
+@pytest.mark.parametrize("case", range(len(PREFILL4_CASES)))
+def test_prefill4_matches_oracle(case):
+    total, n_q, hkv, hq, waves = PREFILL4_CASES[case]
+    _say(f"4-bit prefill parity total={total} n_q={n_q} hkv={hkv} hq={hq} waves={waves}")
+    s = Scenario(1500 + case, [total], hkv=hkv, dtype="bf16", bits=4)
+    q = synth.to_dtype(synth.normal(1501 + case, (n_q, hq, 128)), "bf16")
+    q_start = total - n_q
+    out = _with_prefill_waves(waves, lambda: s.iq.prefill_attention(
+        s.cache, s.rot, q.cuda(), q_start, s.bt_dev[0]).cpu().numpy())
+    rows = np.unique(np.linspace(0, n_q - 1, min(n_q, 24)).astype(int))
+    ref = O4.prefill_attention4(s.host_cache(), s.blocks, q.double().numpy(), q_start, s.block_table[0],
+                                rows=rows)
+    err = max_row_error(out[rows], ref)
+    _say(f"  max row error {err:.3e}")
+    assert np.all(np.isfinite(out))
+    assert err <= tol()
+
+
+def test_prefill4_varlen_matches_oracle_and_single_calls():
+    lens, nq, hkv, hq = [700, 130, 2048, 64], [77, 0, 128, 64], 2, 16
+    s = Scenario(1560, lens, hkv=hkv, dtype="bf16", bits=4)
+    total_q = sum(nq)
+    q = synth.to_dtype(synth.normal(1561, (total_q, hq, 128)), "bf16")
+    cu = np.concatenate([[0], np.cumsum(nq)]).astype(np.int32)
+    starts = np.array([n - k for n, k in zip(lens, nq)], dtype=np.int32)
+    out = s.iq.prefill_attention_varlen(
+        s.cache, s.rot, q.cuda(), torch.from_numpy(cu).cuda(), torch.from_numpy(starts).cuda(), s.bt_dev,
+        max(nq), max(lens)).cpu().numpy()
+    host = s.host_cache()
+    worst = 0.0
+    for b in range(len(lens)):
+        if nq[b] == 0:
+            continue
+        rows = np.unique(np.linspace(0, nq[b] - 1, min(nq[b], 12)).astype(int))
+        ref = O4.prefill_attention4(host, s.blocks, q[cu[b]:cu[b + 1]].double().numpy(), int(starts[b]),
+                                    s.block_table[b], rows=rows)
+        worst = max(worst, max_row_error(out[cu[b] + rows], ref))
+        one = s.iq.prefill_attention(s.cache, s.rot, q[cu[b]:cu[b + 1]].cuda(), int(starts[b]),
+                                     s.bt_dev[b]).cpu().numpy()
+        assert np.array_equal(one, out[cu[b]:cu[b + 1]])
+    _say(f"  max row error {worst:.3e}")
+    assert worst <= tol()
+
+
+def test_prefill4_agrees_with_decode4_on_the_last_query():
+    """The last query of a chunk attends the whole cache: prefill's row and the
+    decode call on the same 4-bit cache agree (two different kernels)."""
+    total, n_q, hkv, hq = 900, 33, 2, 16
+    s = Scenario(1570, [total], hkv=hkv, dtype="bf16", bits=4)
+    q = synth.to_dtype(synth.normal(1571, (n_q, hq, 128)), "bf16")
+    pre = s.iq.prefill_attention(s.cache, s.rot, q.cuda(), total - n_q, s.bt_dev[0]).cpu().numpy()
+    dec = s.iq.decode_attention(s.cache, s.rot, q[-1:].contiguous().cuda(), s.bt_dev, s.lens_dev,
+                                total).cpu().numpy()
+    assert max_row_error(pre[-1:], dec) <= tol()

@@ -193,3 +193,35 @@ def test_decode4_equals_plain_attention_on_materialised_kv():
     assert np.array_equal(kc, O4.quantize4(k[sum(lens[:2]):, 1], blocks[1])["codes"])
     vc, _ = cache.gather(bt, 2, 130, 1, "v")
     assert np.array_equal(vc, O4.quantize4(v[sum(lens[:2]):, 1], blocks[1])["codes"])
+
+
+def test_prefill4_rows_equal_causal_plain_attention():
+    """Each query row equals plain softmax attention of the unrotated query
+    over the dequantised keys and values up to its own position."""
+    rng = np.random.default_rng(9)
+    hkv, hq, n_ctx, q_start = 2, 8, 150, 100
+    quats = rng.standard_normal((hkv, 32, 2, 4))
+    blocks = O.rotation_matrices(quats)
+    bt = rng.permutation(4).reshape(1, 4)
+    cache = O4.PagedCache4(4, hkv)
+    k = rng.standard_normal((n_ctx, hkv, 128))
+    v = rng.standard_normal((n_ctx, hkv, 128))
+    O4.quantize_append4(cache, blocks, k, v, np.zeros(n_ctx, int), np.arange(n_ctx), bt)
+    q = rng.standard_normal((n_ctx - q_start, hq, 128))
+    out = O4.prefill_attention4(cache, blocks, q, q_start, bt[0])
+    for g in range(hkv):
+        kc, kn = cache.gather(bt, 0, n_ctx, g, "k")
+        vc, vn = cache.gather(bt, 0, n_ctx, g, "v")
+        kk = O.inverse_rotate(O4.dequantize_rotated4(kc, kn), blocks[g])
+        vv = O.inverse_rotate(O4.dequantize_rotated4(vc, vn), blocks[g])
+        for i in (0, 7, 49):
+            for h in range(g * 4, g * 4 + 4):
+                ref = O.reference_attention(q[i, h:h + 1], kk[:q_start + i + 1], vv[:q_start + i + 1])
+                assert np.max(np.abs(out[i, h] - ref[0])) < 1e-12
+    # the first query sees exactly q_start + 1 keys: a later key does not move it
+    k2 = k.copy()
+    k2[q_start + 1:] *= -3.0
+    cache2 = O4.PagedCache4(4, hkv)
+    O4.quantize_append4(cache2, blocks, k2, v, np.zeros(n_ctx, int), np.arange(n_ctx), bt)
+    out2 = O4.prefill_attention4(cache2, blocks, q[:1], q_start, bt[0])
+    assert np.array_equal(out2[0], out[0])
