@@ -456,10 +456,11 @@ def run_four_bit_aux(w, lens, bt_np, num_pages, t_decode3, t_step3, ring_bytes=1
             "time_vs_3bit_step": round(t_step / t_step3, 3)}
 
 
-def run_prefill_aux(iters=30):
+def run_prefill_aux(iters=30, bits=3):
     """The chunked-prefill workload (8192-token quantise-append into a 32,768-token
     cache, then causal attention of the last 512 positions x 64 query heads):
-    append tokens/s and prefill TFLOP/s against the f16 matrix-core peak."""
+    append tokens/s and prefill TFLOP/s against the f16 matrix-core peak, on a
+    cache of 3- or 4-bit records."""
     import torch
 
     from compressed_space_attention_amd import isoquant as iq
@@ -471,7 +472,7 @@ def run_prefill_aux(iters=30):
     bt_np, num_pages = synth.block_table(p.seed + 9, [pages], shuffle=True)
     bt = torch.from_numpy(bt_np).to(dev)
     rot = iq.rotation_init(synth.quaternions(p.seed, p.n_kv_heads), device=dev)
-    cache = iq.PagedCache(num_pages, p.n_kv_heads, device=dev, zero=True)
+    cache = iq.PagedCache(num_pages, p.n_kv_heads, device=dev, zero=True, bits=bits)
     k = synth.draw_normal_device(p.seed + 2, (p.total, p.n_kv_heads, 128), torch.bfloat16, dev)
     v = synth.draw_normal_device(p.seed + 3, (p.total, p.n_kv_heads, 128), torch.bfloat16, dev)
     pos = torch.arange(p.total, dtype=torch.int32, device=dev)
@@ -502,10 +503,12 @@ def run_prefill_aux(iters=30):
     # algorithmic flops: 2 d for q.k and 2 d for p.v per (query head, key) pair
     keys = sum(p.q_start + i + 1 for i in range(p.n_queries))
     flops = 4.0 * 128 * p.n_q_heads * keys
-    moved = p.appended * p.n_kv_heads * 2 * (128 * 2 + 50)  # bf16 in, packed record out
+    rec = 50 if bits == 3 else 66
+    moved = p.appended * p.n_kv_heads * 2 * (128 * 2 + rec)  # bf16 in, packed record out
     tf = flops / t_pre / 1e12
     return {
         "workload": p.name,
+        "record_bits": bits,
         "append_us": round(t_app * 1e6, 2),
         "append_tokens_per_s": round(p.appended / t_app, 1),
         "append_gbs": round(moved / t_app / 1e9, 1),
@@ -663,6 +666,7 @@ def main():
     res = run_decode(args)
     if not args.no_aux:
         res["detail"]["prefill"] = run_prefill_aux()
+        res["detail"]["prefill_4bit"] = run_prefill_aux(bits=4)
         probe = probe_bandwidth()
         res["detail"]["hbm_probe"] = probe
         res["detail"]["decode_call_frac_of_probe_read"] = round(
