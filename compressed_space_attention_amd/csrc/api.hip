@@ -39,12 +39,20 @@ iq::CacheView view(const iq_cache* c) {
                        c->num_pages, c->n_kv_heads, c->bits == 4 ? 4 : 3};
 }
 
+bool scale_ok(float s) { return isfinite(s) && s >= 0.f; }
+
 bool dense_ok(const iq_dense_cache* c) {
-  return c && c->k_dev && c->v_dev && c->num_pages > 0 && c->n_kv_heads > 0 && c->n_kv_heads <= 65535;
+  return c && c->k_dev && c->v_dev && c->num_pages > 0 && c->n_kv_heads > 0 && c->n_kv_heads <= 65535 &&
+         (c->format == IQ_KV_BF16 ||
+          (c->format == IQ_KV_FP8_E4M3 && scale_ok(c->k_scale) && scale_ok(c->v_scale)));
 }
 
 iq::DenseCacheView dense_view(const iq_dense_cache* c) {
-  return iq::DenseCacheView{c->k_dev, c->v_dev, c->num_pages, c->n_kv_heads};
+  const bool fp8 = c->format == IQ_KV_FP8_E4M3;
+  return iq::DenseCacheView{static_cast<uint8_t*>(c->k_dev), static_cast<uint8_t*>(c->v_dev), c->num_pages,
+                            c->n_kv_heads, c->format,
+                            fp8 && c->k_scale > 0.f ? c->k_scale : 1.0f,
+                            fp8 && c->v_scale > 0.f ? c->v_scale : 1.0f};
 }
 
 bool dtype_ok(int32_t d) { return d == IQ_F32 || d == IQ_BF16 || d == IQ_F16; }

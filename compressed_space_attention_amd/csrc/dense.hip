@@ -20,7 +20,18 @@
 //   O^T[coord][head] += V^T[coord][token] . P^T[token][head], with P in bf16
 //   high + low parts (two products, ~2^-16 relative)
 // and the same partial rows (m, l, acc[128]) and merge as the packed path.
+//
+// FP8 fallback (FreeToken issue #141, Proposed Solution: standard FP8 KV as
+// the fallback format): the same layouts with one byte per value, OCP E4M3
+// (bias 7, 3 mantissa bits, largest finite 448, no infinities) of x / scale
+// with one scale per tensor and cache.  Every E4M3 value is exact in f16, so
+// the kernel converts bytes to f16 with the gfx950 conversion instruction and
+// runs the same products on v_mfma_f32_16x16x32_f16 (q converted from bf16 to
+// f16, P as f16 high + low parts); K's scale joins the score factor, V's the
+// partial accumulator.
 #include <math.h>
+
+#include <type_traits>
 
 #include "iq_device.h"
 #include "iq_internal.h"
@@ -29,6 +40,26 @@ namespace iq {
 
 typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+typedef _Float16 hh2 __attribute__((ext_vector_type(2)));
+typedef short ss2 __attribute__((ext_vector_type(2)));
+
+// Cache formats (template parameter FMT).
+constexpr int kFmtBf16 = 0, kFmtFp8 = 1;
+
+// Four E4M3 bytes -> four f16 values (exact).
+__device__ __forceinline__ u2 fp8x4_to_f16(uint32_t w) {
+  const hh2 lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
+  const hh2 hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true);
+  return u2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+}
+// Two floats -> two E4M3 bytes (round to nearest even), saturated at +-448,
+// in the low 16 bits.
+__device__ __forceinline__ uint32_t f32x2_to_fp8(float a, float b) {
+  a = fminf(fmaxf(a, -448.0f), 448.0f);
+  b = fminf(fmaxf(b, -448.0f), 448.0f);
+  const ss2 r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(ss2{0, 0}, a, b, 1.0f, false);
+  return __builtin_bit_cast(uint32_t, r) & 0xFFFFu;
+}
 
 constexpr int kDenseChunk = 32;       // tokens per wave step (half a page)
 constexpr int kDenseWaves = 8;
@@ -42,11 +73,12 @@ __device__ __forceinline__ uint16_t to_bf16_bits(float x) {
 // Append: one thread per (token, kv head, 8 coordinates) and tensor; K rows go
 // to their slot as one 16-byte store, V values to eight coordinate rows.
 // ---------------------------------------------------------------------------
-template <int DT>
+template <int DT, int FMT>
 __global__ __launch_bounds__(256) void dense_append_kernel(
     const void* __restrict__ k, const void* __restrict__ v, const int32_t* __restrict__ seq_idx,
     const int32_t* __restrict__ pos, const int32_t* __restrict__ block_table, long long n_vec,
-    int hkv, int max_pages, int num_pages, uint16_t* __restrict__ kc, uint16_t* __restrict__ vc) {
+    int hkv, int max_pages, int num_pages, uint8_t* __restrict__ kc, uint8_t* __restrict__ vc,
+    float inv_k_scale, float inv_v_scale) {
   const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
   if (gid >= 2 * n_vec * 16) return;
   const int part = (int)(gid & 15);  // coordinates 8 part .. 8 part + 7
@@ -86,15 +118,32 @@ __global__ __launch_bounds__(256) void dense_append_kernel(
   if ((unsigned)page >= (unsigned)num_pages) return;  // skipped, as the packed append
   const int slot = p & 63;
   const size_t blk = (size_t)page * hkv + head;
-  if (!which) {
-    u4 w;
+  if (FMT == kFmtBf16) {
+    uint16_t* kh = reinterpret_cast<uint16_t*>(kc);
+    uint16_t* vh = reinterpret_cast<uint16_t*>(vc);
+    if (!which) {
+      u4 w;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      w[i] = (uint32_t)to_bf16_bits(x[2 * i]) | ((uint32_t)to_bf16_bits(x[2 * i + 1]) << 16);
-    *reinterpret_cast<u4*>(kc + (blk * kPage + slot) * kD + 8 * part) = w;
+      for (int i = 0; i < 4; ++i)
+        w[i] = (uint32_t)to_bf16_bits(x[2 * i]) | ((uint32_t)to_bf16_bits(x[2 * i + 1]) << 16);
+      *reinterpret_cast<u4*>(kh + (blk * kPage + slot) * kD + 8 * part) = w;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) vh[(blk * kD + 8 * part + i) * kPage + slot] = to_bf16_bits(x[i]);
+    }
   } else {
+    const float inv = which ? inv_v_scale : inv_k_scale;
+    uint32_t b[4];  // bytes of coordinates 2i, 2i + 1
 #pragma unroll
-    for (int i = 0; i < 8; ++i) vc[(blk * kD + 8 * part + i) * kPage + slot] = to_bf16_bits(x[i]);
+    for (int i = 0; i < 4; ++i) b[i] = f32x2_to_fp8(x[2 * i] * inv, x[2 * i + 1] * inv);
+    if (!which) {
+      *reinterpret_cast<u2*>(kc + (blk * kPage + slot) * kD + 8 * part) =
+          u2{b[0] | (b[1] << 16), b[2] | (b[3] << 16)};
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        vc[(blk * kD + 8 * part + i) * kPage + slot] = (uint8_t)(b[i >> 1] >> (8 * (i & 1)));
+    }
   }
 }
 
@@ -104,12 +153,17 @@ hipError_t launch_dense_append(const DenseCacheView& c, const void* k, const voi
   const long long n_vec = (long long)n_tokens * c.hkv;
   const long long threads = 2 * n_vec * 16;
   const unsigned blocks = (unsigned)((threads + 255) / 256);
-#define IQ_DAPP(DT)                                                                               \
-  hipLaunchKernelGGL(dense_append_kernel<DT>, dim3(blocks), dim3(256), 0, stream, k, v, seq_idx, \
-                     pos, block_table, n_vec, c.hkv, max_pages, c.num_pages, c.k, c.v)
-  if (dtype == 0) IQ_DAPP(0);
-  else if (dtype == 1) IQ_DAPP(1);
-  else IQ_DAPP(2);
+  const float ik = 1.0f / c.k_scale, iv = 1.0f / c.v_scale;
+#define IQ_DAPP(DT, F)                                                                               \
+  hipLaunchKernelGGL((dense_append_kernel<DT, F>), dim3(blocks), dim3(256), 0, stream, k, v, seq_idx, \
+                     pos, block_table, n_vec, c.hkv, max_pages, c.num_pages, c.k, c.v, ik, iv)
+#define IQ_DAPP_F(F)               \
+  if (dtype == 0) IQ_DAPP(0, F);     \
+  else if (dtype == 1) IQ_DAPP(1, F); \
+  else IQ_DAPP(2, F)
+  if (c.format == kFmtFp8) { IQ_DAPP_F(kFmtFp8); }
+  else { IQ_DAPP_F(kFmtBf16); }
+#undef IQ_DAPP_F
 #undef IQ_DAPP
   return hipGetLastError();
 }
@@ -118,34 +172,50 @@ hipError_t launch_dense_append(const DenseCacheView& c, const void* k, const voi
 // Decode split kernel.
 // ---------------------------------------------------------------------------
 struct DenseArgs {
-  const uint16_t* k;
-  const uint16_t* v;
+  const uint8_t* k;
+  const uint8_t* v;
   int num_pages, hkv;
-  float score_factor;  // softmax_scale * log2(e)
+  float score_factor;  // softmax_scale * log2(e) (* K's scale for FP8)
+  float v_scale;       // FP8: V's scale, applied to the partial accumulator
   float* ws_acc;       // [B][Hq][splits][128]
   float* ws_ml;        // [B][Hq][splits][2]
 };
 
 // One 32-token chunk of one kv head, in this lane's operand layout.
-struct DenseChunk {
-  u4 k[2][4];  // K: token 16t + lane%16, coordinates 32kk + 8(lane/16) .. +7
-  u2 v[8][2];  // V: coordinate 16m + lane%16, tokens 4(lane/16) + 16h .. +3
+//   K: token 16t + lane%16, coordinates 32kk + 8(lane/16) .. +7
+//   V: coordinate 16m + lane%16, tokens 4(lane/16) + 16h .. +3
+template <int FMT> struct DenseChunk;
+template <> struct DenseChunk<kFmtBf16> {
+  u4 k[2][4];
+  u2 v[8][2];
+};
+template <> struct DenseChunk<kFmtFp8> {
+  u2 k[2][4];
+  uint32_t v[8][2];
 };
 
+template <int FMT>
 __device__ __forceinline__ void load_chunk(const DenseArgs& a, int page, int g, int half, int lane,
-                                           DenseChunk& c) {
+                                           DenseChunk<FMT>& c) {
+  constexpr int E = FMT == kFmtFp8 ? 1 : 2;  // bytes per value
+  using KT = decltype(c.k[0][0]);
+  using VT = decltype(c.v[0][0]);
   const int col = lane & 15, jq = lane >> 4;
   const size_t blk = (size_t)page * a.hkv + g;
-  const uint16_t* kb = a.k + (blk * kPage + kDenseChunk * half + col) * kD + 8 * jq;
+  const uint8_t* kb = a.k + ((blk * kPage + kDenseChunk * half + col) * kD + 8 * jq) * E;
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) c.k[t][kk] = *reinterpret_cast<const u4*>(kb + 16 * t * kD + 32 * kk);
-  const uint16_t* vb = a.v + (blk * kD + col) * kPage + kDenseChunk * half + 4 * jq;
+    for (int kk = 0; kk < 4; ++kk)
+      c.k[t][kk] = *reinterpret_cast<const typename std::remove_reference<KT>::type*>(
+          kb + (16 * t * kD + 32 * kk) * E);
+  const uint8_t* vb = a.v + ((blk * kD + col) * kPage + kDenseChunk * half + 4 * jq) * E;
 #pragma unroll
   for (int m = 0; m < 8; ++m)
 #pragma unroll
-    for (int h = 0; h < 2; ++h) c.v[m][h] = *reinterpret_cast<const u2*>(vb + 16 * m * kPage + 16 * h);
+    for (int h = 0; h < 2; ++h)
+      c.v[m][h] = *reinterpret_cast<const typename std::remove_reference<VT>::type*>(
+          vb + (16 * m * kPage + 16 * h) * E);
 }
 
 struct DenseState {
@@ -153,20 +223,39 @@ struct DenseState {
   f4 acc[8];  // O^T: coordinates 16m + 4(lane/16) + r, head lane%16
 };
 
+// One matrix-core product in the format's operand type.
+template <int FMT>
+__device__ __forceinline__ f4 dense_mfma(const u4& a, const u4& b, const f4& c) {
+  if constexpr (FMT == kFmtFp8)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, a), __builtin_bit_cast(h8, b), c,
+                                                  0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8, a), __builtin_bit_cast(bf8, b),
+                                                   c, 0, 0, 0);
+}
+
 // MASKED: the chunk holds tokens at or beyond L (their scores are -inf and
 // their values are zeroed, so never-written slots cannot inject NaN).
-template <bool MASKED>
-__device__ __forceinline__ void dense_chunk_step(DenseChunk c, DenseState& st, int tok0, int L,
-                                                 int lane, float fac, const bf8 qb[4]) {
+// qb: the queries as the B operand (bf16, or f16 for the FP8 format).
+template <bool MASKED, int FMT>
+__device__ __forceinline__ void dense_chunk_step(DenseChunk<FMT> c, DenseState& st, int tok0, int L,
+                                                 int lane, float fac, const u4 qb[4]) {
   const int jq = lane >> 4;
   f4 s[2];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8, c.k[t][kk]), qb[kk], acc,
-                                                    0, 0, 0);
+    for (int kk = 0; kk < 4; ++kk) {
+      u4 ka;
+      if constexpr (FMT == kFmtFp8) {
+        const u2 lo = fp8x4_to_f16(c.k[t][kk][0]), hi = fp8x4_to_f16(c.k[t][kk][1]);
+        ka = u4{lo[0], lo[1], hi[0], hi[1]};
+      } else {
+        ka = c.k[t][kk];
+      }
+      acc = dense_mfma<FMT>(ka, qb[kk], acc);
+    }
     s[t] = acc;
   }
   float sc[2][4];
@@ -183,12 +272,19 @@ __device__ __forceinline__ void dense_chunk_step(DenseChunk c, DenseState& st, i
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int t0 = tok0 + 16 * h + 4 * jq;
-      const uint32_t m0 = (t0 < L ? 0xFFFFu : 0u) | (t0 + 1 < L ? 0xFFFF0000u : 0u);
-      const uint32_t m1 = (t0 + 2 < L ? 0xFFFFu : 0u) | (t0 + 3 < L ? 0xFFFF0000u : 0u);
+      if constexpr (FMT == kFmtFp8) {
+        const uint32_t mk = (t0 < L ? 0xFFu : 0u) | (t0 + 1 < L ? 0xFF00u : 0u) |
+                            (t0 + 2 < L ? 0xFF0000u : 0u) | (t0 + 3 < L ? 0xFF000000u : 0u);
 #pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        c.v[m][h][0] &= m0;
-        c.v[m][h][1] &= m1;
+        for (int m = 0; m < 8; ++m) c.v[m][h] &= mk;
+      } else {
+        const uint32_t m0 = (t0 < L ? 0xFFFFu : 0u) | (t0 + 1 < L ? 0xFFFF0000u : 0u);
+        const uint32_t m1 = (t0 + 2 < L ? 0xFFFFu : 0u) | (t0 + 3 < L ? 0xFFFF0000u : 0u);
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          c.v[m][h][0] &= m0;
+          c.v[m][h][1] &= m1;
+        }
       }
     }
   }
@@ -211,21 +307,41 @@ __device__ __forceinline__ void dense_chunk_step(DenseChunk c, DenseState& st, i
       p[4 * t + r] = fast_exp2(sc[t][r] - m_new);
       st.l_run += p[4 * t + r];
     }
-  bf8 ph, pl;
+  u4 ph, pl;  // P as high + low parts in the operand type
+  if constexpr (FMT == kFmtFp8) {
+    h8 h, l;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    ph[i] = (__bf16)p[i];
-    pl[i] = (__bf16)(p[i] - (float)ph[i]);
+    for (int i = 0; i < 8; ++i) {
+      h[i] = (_Float16)p[i];
+      l[i] = (_Float16)(p[i] - (float)h[i]);
+    }
+    ph = __builtin_bit_cast(u4, h);
+    pl = __builtin_bit_cast(u4, l);
+  } else {
+    bf8 h, l;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      h[i] = (__bf16)p[i];
+      l[i] = (__bf16)(p[i] - (float)h[i]);
+    }
+    ph = __builtin_bit_cast(u4, h);
+    pl = __builtin_bit_cast(u4, l);
   }
 #pragma unroll
   for (int m = 0; m < 8; ++m) {
-    const u4 vw = u4{c.v[m][0][0], c.v[m][0][1], c.v[m][1][0], c.v[m][1][1]};
-    const bf8 va = __builtin_bit_cast(bf8, vw);
-    st.acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, ph, st.acc[m], 0, 0, 0);
-    st.acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pl, st.acc[m], 0, 0, 0);
+    u4 va;
+    if constexpr (FMT == kFmtFp8) {
+      const u2 t0 = fp8x4_to_f16(c.v[m][0]), t1 = fp8x4_to_f16(c.v[m][1]);
+      va = u4{t0[0], t0[1], t1[0], t1[1]};
+    } else {
+      va = u4{c.v[m][0][0], c.v[m][0][1], c.v[m][1][0], c.v[m][1][1]};
+    }
+    st.acc[m] = dense_mfma<FMT>(va, ph, st.acc[m]);
+    st.acc[m] = dense_mfma<FMT>(va, pl, st.acc[m]);
   }
 }
 
+template <int FMT>
 __global__ __launch_bounds__(64 * kDenseWaves, 1) void dense_decode_split_kernel(
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
     const uint16_t* __restrict__ q, int max_pages, int pages_per_split, int hq, int group, int splits,
@@ -254,13 +370,21 @@ __global__ __launch_bounds__(64 * kDenseWaves, 1) void dense_decode_split_kernel
   for (int i = tid; i < pg_end - pg_begin; i += 64 * kDenseWaves)
     s_pages[i] = min(max(bt[pg_begin + i], 0), a.num_pages - 1);
   // queries of the group as the B operand: head lane%16, coordinates 32kk + 8jq ..
-  bf8 qb[4];
+  u4 qb[4];
   {
     const uint16_t* qh = q + ((size_t)b * hq + (size_t)g * group + col) * kD + 8 * jq;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      const u4 w = col < group ? *reinterpret_cast<const u4*>(qh + 32 * kk) : u4{0u, 0u, 0u, 0u};
-      qb[kk] = __builtin_bit_cast(bf8, w);
+      u4 w = col < group ? *reinterpret_cast<const u4*>(qh + 32 * kk) : u4{0u, 0u, 0u, 0u};
+      if constexpr (FMT == kFmtFp8) {  // bf16 -> f16
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const hh2 hv = {(_Float16)__builtin_bit_cast(float, w[i] << 16),
+                          (_Float16)__builtin_bit_cast(float, w[i] & 0xFFFF0000u)};
+          w[i] = __builtin_bit_cast(uint32_t, hv);
+        }
+      }
+      qb[kk] = w;
     }
   }
   __syncthreads();
@@ -280,16 +404,16 @@ __global__ __launch_bounds__(64 * kDenseWaves, 1) void dense_decode_split_kernel
   // split's end repeats its last chunk: lines already in cache), so every
   // wait is a plain count of the loads issued since.
   const int last = n_chunks - 1;
-  auto fetch = [&](int chunk, DenseChunk& dst) {
+  auto fetch = [&](int chunk, DenseChunk<FMT>& dst) {
     const int cc = min(chunk, last);
-    load_chunk(a, s_pages[cc >> 1], g, cc & 1, lane, dst);
+    load_chunk<FMT>(a, s_pages[cc >> 1], g, cc & 1, lane, dst);
   };
-  auto step = [&](const DenseChunk& src, int chunk) {
+  auto step = [&](const DenseChunk<FMT>& src, int chunk) {
     const int tok0 = tok_begin + kDenseChunk * chunk;
-    if (tok0 + kDenseChunk <= L) dense_chunk_step<false>(src, st, tok0, L, lane, fac, qb);
-    else dense_chunk_step<true>(src, st, tok0, L, lane, fac, qb);
+    if (tok0 + kDenseChunk <= L) dense_chunk_step<false, FMT>(src, st, tok0, L, lane, fac, qb);
+    else dense_chunk_step<true, FMT>(src, st, tok0, L, lane, fac, qb);
   };
-  DenseChunk b0, b1;
+  DenseChunk<FMT> b0, b1;
   fetch(wave, b0);
   fetch(wave + kDenseWaves, b1);
   for (int c = wave; c < n_chunks; c += 2 * kDenseWaves) {
@@ -328,13 +452,14 @@ __global__ __launch_bounds__(64 * kDenseWaves, 1) void dense_decode_split_kernel
     }
     if (col < group) {
       const size_t row = ((size_t)b * hq + (size_t)g * group + col) * splits + split;
+      const float vs = FMT == kFmtFp8 ? a.v_scale : 1.0f;
       f4 o;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         float sum = 0.f;
 #pragma unroll
         for (int w = 0; w < kDenseWaves; ++w) sum += wt[w] * s_acc[w][4 * wave + r][lane];
-        o[r] = sum;
+        o[r] = sum * vs;
       }
       // value index 4 wave + r = 4 m + r: coordinate 16 wave + 4 jq + r
       *reinterpret_cast<f4*>(a.ws_acc + row * kD + 16 * wave + 4 * jq) = o;
@@ -365,19 +490,26 @@ hipError_t launch_dense_decode(const DenseCacheView& c, const void* q, int batch
                                const int32_t* block_table, int max_pages, const int32_t* seq_lens,
                                const DecodePlan& plan, float softmax_scale, float* out,
                                void* workspace, hipStream_t stream) {
+  const bool fp8 = c.format == kFmtFp8;
   DenseArgs a;
   a.k = c.k;
   a.v = c.v;
   a.num_pages = c.num_pages;
   a.hkv = c.hkv;
-  a.score_factor = (float)((double)softmax_scale * 1.4426950408889634);
+  a.score_factor = (float)((double)softmax_scale * 1.4426950408889634 * (fp8 ? (double)c.k_scale : 1.0));
+  a.v_scale = fp8 ? c.v_scale : 1.0f;
   const size_t rows = (size_t)batch * hq * plan.splits;
   a.ws_acc = reinterpret_cast<float*>(workspace);
   a.ws_ml = a.ws_acc + rows * kD;
   const int group = hq / c.hkv;
-  hipLaunchKernelGGL(dense_decode_split_kernel, dim3(plan.splits, c.hkv, batch), dim3(64 * kDenseWaves),
-                     0, stream, block_table, seq_lens, static_cast<const uint16_t*>(q), max_pages,
-                     plan.pages_per_split, hq, group, plan.splits, a);
+  const dim3 grid(plan.splits, c.hkv, batch);
+  const uint16_t* qh = static_cast<const uint16_t*>(q);
+  if (fp8)
+    hipLaunchKernelGGL(dense_decode_split_kernel<kFmtFp8>, grid, dim3(64 * kDenseWaves), 0, stream,
+                       block_table, seq_lens, qh, max_pages, plan.pages_per_split, hq, group, plan.splits, a);
+  else
+    hipLaunchKernelGGL(dense_decode_split_kernel<kFmtBf16>, grid, dim3(64 * kDenseWaves), 0, stream,
+                       block_table, seq_lens, qh, max_pages, plan.pages_per_split, hq, group, plan.splits, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_decode_merge(false, nullptr, a.ws_acc, a.ws_ml, plan.splits, batch, hq, group, out,

@@ -67,13 +67,16 @@ hipError_t launch_decode_merge(bool rotate, const float* rot, const float* ws_ac
                                int splits, int batch, int hq, int group, float* out,
                                hipStream_t stream);
 
-// Uncompressed bf16 baseline (dense.hip): paged cache of bf16 rows, K
-// token-major [pages][hkv][64][128], V coordinate-major [pages][hkv][128][64].
+// Uncompressed baseline (dense.hip): paged cache of bf16 (format 0) or FP8
+// E4M3 (format 1) values, K token-major [pages][hkv][64][128], V
+// coordinate-major [pages][hkv][128][64]; FP8 values are x / scale.
 struct DenseCacheView {
-  uint16_t* k;
-  uint16_t* v;
+  uint8_t* k;
+  uint8_t* v;
   int32_t num_pages;
   int32_t hkv;
+  int32_t format;
+  float k_scale, v_scale;  // FP8 only; positive
 };
 hipError_t launch_dense_append(const DenseCacheView& c, const void* k, const void* v, int dtype,
                                int n_tokens, const int32_t* seq_idx, const int32_t* pos,

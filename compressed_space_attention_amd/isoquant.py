@@ -46,12 +46,18 @@ class IqCacheStruct(ctypes.Structure):
     ]
 
 
+IQ_KV_BF16, IQ_KV_FP8_E4M3 = 0, 1
+
+
 class IqDenseCacheStruct(ctypes.Structure):
     _fields_ = [
         ("k_dev", ctypes.c_void_p),
         ("v_dev", ctypes.c_void_p),
         ("num_pages", ctypes.c_int32),
         ("n_kv_heads", ctypes.c_int32),
+        ("format", ctypes.c_int32),
+        ("k_scale", ctypes.c_float),
+        ("v_scale", ctypes.c_float),
     ]
 
 
@@ -312,25 +318,30 @@ def prefill_attention_varlen(cache: PagedCache, rot: torch.Tensor, q: torch.Tens
 # Uncompressed bf16 baseline and the HBM read probe.
 # ---------------------------------------------------------------------------
 class DenseCache:
-    """One layer's bf16 paged cache: k[num_pages][Hkv][64][128] (token-major),
-    v[num_pages][Hkv][128][64] (coordinate-major), bf16 bits as int16."""
+    """One layer's uncompressed paged cache: k[num_pages][Hkv][64][128]
+    (token-major), v[num_pages][Hkv][128][64] (coordinate-major); format "bf16"
+    (bf16 bits as int16) or "fp8" (OCP E4M3 bytes as uint8, holding x / scale)."""
 
-    def __init__(self, num_pages: int, n_kv_heads: int, device="cuda", zero: bool = False):
+    def __init__(self, num_pages: int, n_kv_heads: int, device="cuda", zero: bool = False,
+                 format: str = "bf16", k_scale: float = 1.0, v_scale: float = 1.0):
+        if format not in ("bf16", "fp8"):
+            raise ValueError("format must be 'bf16' or 'fp8'")
         alloc = torch.zeros if zero else torch.empty
-        self.num_pages, self.n_kv_heads = int(num_pages), int(n_kv_heads)
-        self.k = alloc((self.num_pages, self.n_kv_heads, PAGE_TOKENS, HEAD_DIM), dtype=torch.int16,
-                       device=device)
-        self.v = alloc((self.num_pages, self.n_kv_heads, HEAD_DIM, PAGE_TOKENS), dtype=torch.int16,
-                       device=device)
+        self.num_pages, self.n_kv_heads, self.format = int(num_pages), int(n_kv_heads), format
+        dt = torch.int16 if format == "bf16" else torch.uint8
+        self.k = alloc((self.num_pages, self.n_kv_heads, PAGE_TOKENS, HEAD_DIM), dtype=dt, device=device)
+        self.v = alloc((self.num_pages, self.n_kv_heads, HEAD_DIM, PAGE_TOKENS), dtype=dt, device=device)
         self._struct = IqDenseCacheStruct(self.k.data_ptr(), self.v.data_ptr(), self.num_pages,
-                                          self.n_kv_heads)
+                                          self.n_kv_heads,
+                                          IQ_KV_BF16 if format == "bf16" else IQ_KV_FP8_E4M3,
+                                          float(k_scale), float(v_scale))
 
     @property
     def struct(self):
         return ctypes.byref(self._struct)
 
     def nbytes(self) -> int:
-        return 2 * (self.k.numel() + self.v.numel())
+        return self.k.element_size() * (self.k.numel() + self.v.numel())
 
 
 def dense_append(cache: DenseCache, k: torch.Tensor, v: torch.Tensor, seq_idx: torch.Tensor,

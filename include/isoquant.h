@@ -281,33 +281,46 @@ iq_status iq_prefill_attention_varlen(const iq_cache *cache, const void *rot_dev
 
 /*
  * Uncompressed baseline ("RotaryQuant ...", abstract: the packed attention
- * avoids materialising full-precision KV state; this is that state).  A bf16
- * paged cache and its decode attention on the same paging, split planning
- * and merge as the packed path, so that the packed cache's byte reduction is
- * measured as time on the same GPU.  Numerics: bf16 inputs, fp32
- * accumulation, softmax weights as bf16 high + low parts.
+ * avoids materialising full-precision KV state; this is that state) and the
+ * FP8 fallback (FreeToken issue #141, Proposed Solution: standard FP8 KV as
+ * the fallback format).  A paged cache of bf16 or FP8 values and its decode
+ * attention on the same paging, split planning and merge as the packed path,
+ * so that the packed cache's byte reduction is measured as time on the same
+ * GPU.  Numerics: exact products of the stored values and the query (bf16,
+ * or f16 for FP8), fp32 accumulation, softmax weights as high + low parts.
  *
- * One layer's bf16 cache, in two caller-owned device arrays (bf16 bits):
- *   k_dev : uint16 [num_pages][n_kv_heads][64][128]   token-major
- *   v_dev : uint16 [num_pages][n_kv_heads][128][64]   coordinate-major
+ * One layer's cache, in two caller-owned device arrays:
+ *   k_dev : [num_pages][n_kv_heads][64][128]   token-major
+ *   v_dev : [num_pages][n_kv_heads][128][64]   coordinate-major
+ * of uint16 bf16 bits (format IQ_KV_BF16) or uint8 FP8 bytes (IQ_KV_FP8_E4M3:
+ * OCP E4M3, 1 sign, 4 exponent bits with bias 7, 3 mantissa bits, largest
+ * finite value 448, no infinities).  FP8 holds x / scale, rounded to nearest
+ * even and saturated at +-448: byte = e4m3(float(x) * float(1 / k_scale)) for
+ * K and likewise for V; the attention reads e4m3 * scale.  Scales must be
+ * positive and finite (0 selects 1); bf16 ignores them.
  * Token t of a sequence lives in page block_table[seq][t / 64], slot t % 64.
  */
+typedef enum { IQ_KV_BF16 = 0, IQ_KV_FP8_E4M3 = 1 } iq_kv_format;
 typedef struct {
-  uint16_t *k_dev;
-  uint16_t *v_dev;
+  void *k_dev;
+  void *v_dev;
   int32_t num_pages;
   int32_t n_kv_heads;
+  int32_t format;            /* iq_kv_format */
+  float k_scale, v_scale;    /* FP8 only */
 } iq_dense_cache;
 
 /* As iq_quantize_append (same arguments, skip rules and errors): stores the K
- * and V rows of each token, rounded to bf16 (nearest even), in its slot. */
+ * and V rows of each token, rounded to bf16 (nearest even) or encoded as FP8,
+ * in its slot.  IQ_ERR_INVALID_ARG also for an unknown format or a negative or
+ * non-finite scale. */
 iq_status iq_dense_append(const iq_dense_cache *cache, const void *k_dev, const void *v_dev,
                           int32_t dtype, int32_t n_tokens, const int32_t *seq_idx_dev,
                           const int32_t *pos_dev, const int32_t *block_table_dev,
                           int32_t max_pages_per_seq, hipStream_t stream);
 
-/* As iq_decode_attention over the bf16 cache: out = softmax(scale q K^T) V per
- * query head, fp32 [batch][n_q_heads][128].  q_dtype must be IQ_BF16
+/* As iq_decode_attention over the bf16 or FP8 cache: out = softmax(scale q K^T) V
+ * per query head over the stored values, fp32 [batch][n_q_heads][128].  q_dtype must be IQ_BF16
  * (IQ_ERR_UNSUPPORTED otherwise); group limit and workspace rules as there. */
 size_t iq_dense_decode_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
                                        int32_t max_seq_len);

@@ -143,7 +143,13 @@ def test_prefill_validation():
 
 
 def test_dense_and_probe_validation():
-    dc = ctypes.byref(iq.IqDenseCacheStruct(FAKE, FAKE, 8, 4))
+    dc = ctypes.byref(iq.IqDenseCacheStruct(FAKE, FAKE, 8, 4, 0, 0.0, 0.0))
+    for fmt, ks, vs in [(2, 1.0, 1.0), (-1, 1.0, 1.0), (1, -1.0, 1.0), (1, 1.0, float("nan")),
+                        (1, float("inf"), 1.0)]:            # unknown format, bad FP8 scales
+        bad = ctypes.byref(iq.IqDenseCacheStruct(FAKE, FAKE, 8, 4, fmt, ks, vs))
+        assert L.iq_dense_append(bad, FAKE, FAKE, 1, 0, FAKE, FAKE, FAKE, 8, None) == -1
+    f8 = ctypes.byref(iq.IqDenseCacheStruct(FAKE, FAKE, 8, 4, 1, 0.0, 2.5))   # 0 selects 1
+    assert L.iq_dense_append(f8, FAKE, FAKE, 1, 0, FAKE, FAKE, FAKE, 8, None) == 0
     assert L.iq_dense_append(None, FAKE, FAKE, 1, 4, FAKE, FAKE, FAKE, 8, None) == -1
     assert L.iq_dense_append(dc, FAKE, FAKE, 7, 4, FAKE, FAKE, FAKE, 8, None) == -1
     assert L.iq_dense_append(dc, FAKE, FAKE, 1, 0, FAKE, FAKE, FAKE, 8, None) == 0
