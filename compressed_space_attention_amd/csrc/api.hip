@@ -234,6 +234,25 @@ iq_status iq_dense_decode_attention(const iq_dense_cache* cache, const void* q_d
                                                stream));
 }
 
+iq_status iq_dense_prefill_attention(const iq_dense_cache* cache, const void* q_dev, int32_t q_dtype,
+                                     int32_t n_q, int32_t n_q_heads, int32_t q_start_pos,
+                                     const int32_t* block_table_dev, int32_t max_pages, float softmax_scale,
+                                     float* out_dev, hipStream_t stream) {
+  if (!dense_ok(cache) || !q_dev || !dtype_ok(q_dtype) || n_q < 0 || n_q_heads < 1 || q_start_pos < 0 ||
+      !block_table_dev || max_pages < 1 || !out_dev)
+    return IQ_ERR_INVALID_ARG;
+  if (n_q_heads % cache->n_kv_heads != 0) return IQ_ERR_INVALID_ARG;
+  if ((int64_t)q_start_pos + n_q > (int64_t)max_pages * IQ_PAGE_TOKENS) return IQ_ERR_INVALID_ARG;
+  if (n_q == 0) return IQ_OK;
+  const int group = n_q_heads / cache->n_kv_heads;
+  if (q_dtype != IQ_BF16 || !pow2(group) || group > 128) return IQ_ERR_UNSUPPORTED;
+  if ((int64_t)q_start_pos + n_q > (int64_t)iq::kPrefillMaxPages * IQ_PAGE_TOKENS) return IQ_ERR_UNSUPPORTED;
+  if ((n_q + 128 / group - 1) / (128 / group) > 65535) return IQ_ERR_UNSUPPORTED;
+  return launch_status(iq::launch_dense_prefill(dense_view(cache), q_dev, n_q, n_q_heads, q_start_pos,
+                                                block_table_dev, max_pages, resolve_scale(softmax_scale),
+                                                out_dev, stream));
+}
+
 size_t iq_probe_sink_bytes(void) {
   return (size_t)iq::kProbeBlocks * iq::kProbeThreads * sizeof(uint32_t);
 }

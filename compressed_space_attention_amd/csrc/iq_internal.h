@@ -86,6 +86,11 @@ hipError_t launch_dense_decode(const DenseCacheView& c, const void* q, int batch
                                const int32_t* block_table, int max_pages, const int32_t* seq_lens,
                                const DecodePlan& plan, float softmax_scale, float* out,
                                void* workspace, hipStream_t stream);
+// Chunked causal prefill of one sequence over the uncompressed cache (q bf16
+// [n_q][hq][128], query i at position q_start + i); no workspace.
+hipError_t launch_dense_prefill(const DenseCacheView& c, const void* q, int n_q, int hq, int q_start,
+                                const int32_t* block_table, int max_pages, float softmax_scale, float* out,
+                                hipStream_t stream);
 // Streaming read of `bytes` (a multiple of 16) at `buf`; one word per thread
 // of the fixed grid goes to `sink`.
 constexpr int kProbeBlocks = 2048, kProbeThreads = 256;

@@ -83,6 +83,7 @@ def _load():
         "iq_dense_append": (i32, [dp, vp, vp, i32, i32, vp, vp, vp, i32, vp]),
         "iq_dense_decode_workspace_bytes": (sz, [i32, i32, i32, i32]),
         "iq_dense_decode_attention": (i32, [dp, vp, i32, i32, i32, vp, i32, vp, i32, f32, vp, vp, sz, vp]),
+        "iq_dense_prefill_attention": (i32, [dp, vp, i32, i32, i32, i32, vp, i32, f32, vp, vp]),
         "iq_probe_sink_bytes": (sz, []),
         "iq_probe_read": (i32, [vp, sz, vp, sz, vp]),
         "iq_prefill_workspace_bytes": (sz, [i32, i32, i32, i32]),
@@ -103,6 +104,7 @@ EXPORTED = ("iq_status_string", "iq_version", "iq_codebook", "iq_rotation_bytes"
             "iq_decode_step", "iq_prefill_workspace_bytes", "iq_prefill_attention",
             "iq_prefill_attention_varlen",
             "iq_dense_append", "iq_dense_decode_workspace_bytes", "iq_dense_decode_attention",
+            "iq_dense_prefill_attention",
             "iq_probe_sink_bytes", "iq_probe_read")
 
 
@@ -379,6 +381,23 @@ def dense_decode_attention(cache: DenseCache, q: torch.Tensor, block_table: torc
         _contig(seq_lens, "seq_lens").data_ptr(), int(max_seq_len), float(softmax_scale),
         out.data_ptr(), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
         _stream(stream)))
+    return out
+
+
+def dense_prefill_attention(cache: DenseCache, q: torch.Tensor, q_start: int, block_table: torch.Tensor,
+                            softmax_scale: float = 0.0, out: torch.Tensor | None = None,
+                            stream=None) -> torch.Tensor:
+    """q: bf16 [n_q][Hq][128] at positions q_start..; block_table int32[max_pages]
+    -> fp32 [n_q][Hq][128] over the bf16 / FP8 cache."""
+    n_q, hq, d = q.shape
+    if d != HEAD_DIM:
+        raise ValueError("head dim must be 128")
+    if out is None:
+        out = torch.empty((n_q, hq, HEAD_DIM), dtype=torch.float32, device=q.device)
+    _check("iq_dense_prefill_attention", lib.iq_dense_prefill_attention(
+        cache.struct, _contig(q, "q").data_ptr(), _dtype(q), n_q, hq, int(q_start),
+        _contig(block_table, "block_table").data_ptr(), block_table.shape[-1], float(softmax_scale),
+        out.data_ptr(), _stream(stream)))
     return out
 
 

@@ -331,6 +331,17 @@ iq_status iq_dense_decode_attention(const iq_dense_cache *cache, const void *q_d
                                     float softmax_scale, float *out_dev, void *workspace_dev,
                                     size_t workspace_bytes, hipStream_t stream);
 
+/* Chunked causal prefill of one sequence over the bf16 or FP8 cache: the
+ * attention of iq_prefill_attention (query i at position q_start_pos + i
+ * attends keys 0 .. q_start_pos + i) over the stored values, fp32
+ * [n_q][n_q_heads][128].  q_dtype must be IQ_BF16 (IQ_ERR_UNSUPPORTED
+ * otherwise); other limits, the block table and errors as iq_prefill_attention;
+ * no workspace. */
+iq_status iq_dense_prefill_attention(const iq_dense_cache *cache, const void *q_dev, int32_t q_dtype,
+                                     int32_t n_q, int32_t n_q_heads, int32_t q_start_pos,
+                                     const int32_t *block_table_dev, int32_t max_pages,
+                                     float softmax_scale, float *out_dev, hipStream_t stream);
+
 /*
  * Measurement aid: the achievable HBM read rate of this GPU, against which the
  * decode kernels' rates are also reported.  Reads `bytes` (a multiple of 16,

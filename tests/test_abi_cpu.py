@@ -150,6 +150,16 @@ def test_dense_and_probe_validation():
         assert L.iq_dense_append(bad, FAKE, FAKE, 1, 0, FAKE, FAKE, FAKE, 8, None) == -1
     f8 = ctypes.byref(iq.IqDenseCacheStruct(FAKE, FAKE, 8, 4, 1, 0.0, 2.5))   # 0 selects 1
     assert L.iq_dense_append(f8, FAKE, FAKE, 1, 0, FAKE, FAKE, FAKE, 8, None) == 0
+
+    def pre(c=dc, dtype=1, n_q=16, hq=32, q_start=0, max_pages=8):
+        return L.iq_dense_prefill_attention(c, FAKE, dtype, n_q, hq, q_start, FAKE, max_pages, 0.0, FAKE, None)
+    assert pre(hq=30) == -1                   # Hq not a multiple of Hkv
+    assert pre(q_start=500) == -1             # beyond the block table
+    assert pre(dtype=0) == -2                 # q must be bf16
+    assert pre(hq=4 * 3) == -2                # group 3 not a power of two
+    assert pre(n_q=0) == 0                    # no-op
+    assert pre(c=f8, n_q=0) == 0
+    assert pre(n_q=64, q_start=300000, max_pages=5000) == -2   # beyond the staging limit
     assert L.iq_dense_append(None, FAKE, FAKE, 1, 4, FAKE, FAKE, FAKE, 8, None) == -1
     assert L.iq_dense_append(dc, FAKE, FAKE, 7, 4, FAKE, FAKE, FAKE, 8, None) == -1
     assert L.iq_dense_append(dc, FAKE, FAKE, 1, 0, FAKE, FAKE, FAKE, 8, None) == 0

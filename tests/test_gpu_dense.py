@@ -194,3 +194,43 @@ def test_fp8_decode_ignores_unwritten_slots():
     out = s.iq.dense_decode_attention(s.cache, q.cuda(), s.bt_dev, s.lens_dev, 100).cpu().numpy()
     assert np.all(np.isfinite(out))
     assert max_row_error(out, s.reference(q)) <= tol()
+
+
+DENSE_PREFILL_CASES = [
+    # (cache length, n_q, hkv, hq, format): groups 1..128, ragged tiles, one query
+    (1000, 200, 2, 16, "bf16"),
+    (300, 300, 1, 1, "bf16"),
+    (700, 77, 2, 8, "fp8"),
+    (640, 1, 2, 4, "fp8"),
+    (200, 70, 1, 128, "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", range(len(DENSE_PREFILL_CASES)))
+def test_dense_prefill_matches_reference(case):
+    total, n_q, hkv, hq, fmt = DENSE_PREFILL_CASES[case]
+    _say(f"dense prefill total={total} n_q={n_q} hkv={hkv} hq={hq} format={fmt}")
+    ks, vs = (1.0, 1.0) if fmt == "bf16" else (0.5, 2.0)
+    s = DenseScenario(980 + case, [total], hkv=hkv, outliers=True, fmt=fmt, k_scale=ks, v_scale=vs,
+                      fill=-1 if fmt == "bf16" else 255)       # unwritten slots: NaN patterns
+    q = synth.to_dtype(synth.normal(990 + case, (n_q, hq, 128)), "bf16")
+    q_start = total - n_q
+    out = s.iq.dense_prefill_attention(s.cache, q.cuda(), q_start, s.bt_dev[0]).cpu().numpy()
+    assert np.all(np.isfinite(out))
+    if fmt == "fp8":
+        kq = F.dequantize_rows(F.quantize_rows(s.k.float().numpy(), ks), ks)
+        vq = F.dequantize_rows(F.quantize_rows(s.v.float().numpy(), vs), vs)
+    else:
+        kq, vq = s.k.double().numpy(), s.v.double().numpy()
+    qd = q.double().numpy()
+    grp = hq // hkv
+    rows = np.unique(np.linspace(0, n_q - 1, min(n_q, 24)).astype(int))
+    ref = np.zeros((len(rows), hq, 128))
+    for ri, i in enumerate(rows):
+        vis = q_start + i + 1
+        for g in range(hkv):
+            ref[ri, g * grp:(g + 1) * grp] = O.reference_attention(qd[i, g * grp:(g + 1) * grp],
+                                                                   kq[:vis, g], vq[:vis, g])
+    err = max_row_error(out[rows], ref)
+    _say(f"  max row error {err:.3e}")
+    assert err <= tol()
