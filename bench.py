@@ -271,6 +271,8 @@ def run_decode(args):
         torch.cuda.empty_cache()
         result["detail"]["dense_bf16_baseline"] = run_dense_aux(w, lens, bt_np, num_pages, t_decode)
         log(f"[bench] dense bf16 baseline: {result['detail']['dense_bf16_baseline']}")
+        result["detail"]["fp8_baseline"] = run_dense_aux(w, lens, bt_np, num_pages, t_decode, fmt="fp8")
+        log(f"[bench] fp8 baseline: {result['detail']['fp8_baseline']}")
         if args.bits == 3:
             result["detail"]["four_bit"] = run_four_bit_aux(w, lens, bt_np, num_pages, t_decode, t_step)
             log(f"[bench] 4-bit records: {result['detail']['four_bit']}")
@@ -310,10 +312,11 @@ def probe_bandwidth(mib: int = 2048, iters: int = 20):
             "read_kernel": "probe_read_kernel (16-byte loads, 8 in flight per thread)"}
 
 
-def run_dense_aux(w, lens, bt_np, num_pages, t_packed, ring_bytes=1.0e9, steps=400):
-    """The uncompressed bf16 baseline on the same workload: a ring of bf16
-    layer caches (same paging), the decode call timed the same way as the
-    packed one (graph replay, HIP events on the launch stream)."""
+def run_dense_aux(w, lens, bt_np, num_pages, t_packed, ring_bytes=1.0e9, steps=400, fmt="bf16"):
+    """The uncompressed baseline on the same workload: a ring of bf16 (or FP8
+    E4M3, unit scales) layer caches (same paging), the decode call timed the
+    same way as the packed one (graph replay, HIP events on the launch
+    stream)."""
     import torch
 
     from compressed_space_attention_amd import isoquant as iq
@@ -322,15 +325,16 @@ def run_dense_aux(w, lens, bt_np, num_pages, t_packed, ring_bytes=1.0e9, steps=4
     block_table = torch.from_numpy(bt_np).to(dev)
     seq_lens = torch.from_numpy(lens).to(dev)
     max_len = int(lens.max())
-    dense_bytes = 512 * int(lens.sum()) * w.n_kv_heads          # bf16 K + V rows read per call
-    layer_bytes = num_pages * w.n_kv_heads * 64 * 512
+    per_tok = 512 if fmt == "bf16" else 256                      # K + V rows per (token, kv head)
+    dense_bytes = per_tok * int(lens.sum()) * w.n_kv_heads
+    layer_bytes = num_pages * w.n_kv_heads * 64 * per_tok
     ring = max(1, math.ceil(ring_bytes / layer_bytes))
     caches, qs, outs = [], [], []
     seq_idx = torch.cat([torch.full((int(n),), b, dtype=torch.int32) for b, n in enumerate(lens)]).to(dev)
     pos = torch.cat([torch.arange(int(n), dtype=torch.int32) for n in lens]).to(dev)
     total = int(lens.sum())
     for i in range(ring):
-        c = iq.DenseCache(num_pages, w.n_kv_heads, device=dev)
+        c = iq.DenseCache(num_pages, w.n_kv_heads, device=dev, format=fmt)
         seed = w.seed * 1000 + 500 + i
         chunk = 1 << 16
         for s0 in range(0, total, chunk):
@@ -370,8 +374,8 @@ def run_dense_aux(w, lens, bt_np, num_pages, t_packed, ring_bytes=1.0e9, steps=4
     torch.cuda.synchronize()
     t = a.elapsed_time(b) / 1e3 / (reps * ring)
     del caches
-    return {"kernel": "dense_decode_split_kernel + decode_merge_kernel (bf16 paged cache)",
-            "decode_call_us": round(t * 1e6, 3), "bf16_bytes_per_call": dense_bytes,
+    return {"kernel": f"dense_decode_split_kernel + decode_merge_kernel ({fmt} paged cache)",
+            "decode_call_us": round(t * 1e6, 3), f"{fmt}_bytes_per_call": dense_bytes,
             "gbs": round(dense_bytes / t / 1e9, 1), "frac_of_hbm_peak": round(dense_bytes / t / 1e9 / HBM_PEAK_GBS, 4),
             "packed_speedup": round(t / t_packed, 3)}
 
@@ -519,6 +523,44 @@ def run_prefill_aux(iters=30, bits=3):
     }
 
 
+def run_dense_prefill_aux(fmt="bf16", iters=30):
+    """The chunked-prefill workload's attention over an uncompressed (bf16 or
+    FP8, unit scales) cache of the same 32,768 tokens: the baseline of the
+    packed prefill call."""
+    import torch
+
+    from compressed_space_attention_amd import isoquant as iq
+    from compressed_space_attention_amd import synth, workloads
+
+    p = workloads.CHUNKED_PREFILL
+    dev = "cuda"
+    pages = -(-p.total // 64)
+    bt_np, num_pages = synth.block_table(p.seed + 9, [pages], shuffle=True)
+    bt = torch.from_numpy(bt_np).to(dev)
+    cache = iq.DenseCache(num_pages, p.n_kv_heads, device=dev, zero=True, format=fmt)
+    k = synth.draw_normal_device(p.seed + 2, (p.total, p.n_kv_heads, 128), torch.bfloat16, dev)
+    v = synth.draw_normal_device(p.seed + 3, (p.total, p.n_kv_heads, 128), torch.bfloat16, dev)
+    pos = torch.arange(p.total, dtype=torch.int32, device=dev)
+    iq.dense_append(cache, k, v, torch.zeros_like(pos), pos, bt)
+    q = synth.draw_normal_device(p.seed + 10, (p.n_queries, p.n_q_heads, 128), torch.bfloat16, dev)
+    out = torch.empty((p.n_queries, p.n_q_heads, 128), dtype=torch.float32, device=dev)
+    for _ in range(3):
+        iq.dense_prefill_attention(cache, q, p.q_start, bt[0], out=out)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(iters):
+        iq.dense_prefill_attention(cache, q, p.q_start, bt[0], out=out)
+    b.record()
+    torch.cuda.synchronize()
+    t = a.elapsed_time(b) / 1e3 / iters
+    keys = sum(p.q_start + i + 1 for i in range(p.n_queries))
+    tf = 4.0 * 128 * p.n_q_heads * keys / t / 1e12
+    del cache
+    return {"kernel": f"dense_prefill_kernel ({fmt} paged cache)", "prefill_us": round(t * 1e6, 2),
+            "prefill_tflops": round(tf, 2), "prefill_frac_of_f16_peak": round(tf / MFMA_F16_PEAK_TFLOPS, 4)}
+
+
 def cpu_baseline_decode(args, w, layer, bt_np, lens):
     """The CPU oracle, as it stands, on a bounded sample of the same step:
     quantise-append the current token, then decode over the layer's cache."""
@@ -542,14 +584,19 @@ def cpu_baseline_decode(args, w, layer, bt_np, lens):
     kv_bytes = (REC_BYTES4 if four else REC_BYTES) * int(lens.sum()) * w.n_kv_heads
     info = threadpoolctl.threadpool_info()
     threads = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
-    steps, t0 = 0, time.perf_counter()
-    while True:
-        append(host, blocks, k_new, v_new, seq_new, pos_new, bt_np)
-        decode(host, blocks, q, bt_np, lens)
-        steps += 1
-        el = time.perf_counter() - t0
-        if el >= args.cpu_seconds or el * (steps + 1) / steps > 30.0:
-            break
+    def run(seconds):
+        steps, t0 = 0, time.perf_counter()
+        while True:
+            append(host, blocks, k_new, v_new, seq_new, pos_new, bt_np)
+            decode(host, blocks, q, bt_np, lens)
+            steps += 1
+            el = time.perf_counter() - t0
+            if el >= seconds or el * (steps + 1) / steps > 3 * seconds:
+                return steps, el
+
+    steps, el = run(args.cpu_seconds)
+    with threadpoolctl.threadpool_limits(1):       # the same oracle on one core
+        steps1, el1 = run(args.cpu_seconds / 2)
     return {
         "value": round(kv_bytes * steps / el / 1e9, 5),
         "unit": "GB/s",
@@ -558,6 +605,8 @@ def cpu_baseline_decode(args, w, layer, bt_np, lens):
         "sample": f"{steps} {'4-bit ' if four else ''}oracle steps of one layer (append 1 token + decode over "
                   f"{int(lens.max())} tokens, {w.n_q_heads}q/{w.n_kv_heads}kv) in {el:.1f} s; "
                   f"host has {os.cpu_count()} logical CPUs",
+        "single_thread": {"value": round(kv_bytes * steps1 / el1 / 1e9, 5), "unit": "GB/s", "cores": 1,
+                          "sample": f"{steps1} steps in {el1:.1f} s"},
     }
 
 
@@ -667,6 +716,8 @@ def main():
     if not args.no_aux:
         res["detail"]["prefill"] = run_prefill_aux()
         res["detail"]["prefill_4bit"] = run_prefill_aux(bits=4)
+        res["detail"]["prefill_bf16_baseline"] = run_dense_prefill_aux("bf16")
+        res["detail"]["prefill_fp8_baseline"] = run_dense_prefill_aux("fp8")
         probe = probe_bandwidth()
         res["detail"]["hbm_probe"] = probe
         res["detail"]["decode_call_frac_of_probe_read"] = round(
