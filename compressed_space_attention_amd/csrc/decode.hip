@@ -63,6 +63,10 @@ struct DecodeArgs {
   float* ws_acc;       // [B][Hq][splits][128]
   float* ws_ml;        // [B][Hq][splits][2]
   float* out;          // [B][Hq][128]
+  // Balanced plan (several sequences): the plan's workgroup count, the batch,
+  // and each sequence's split count, written for the merge.
+  int plan_wgs, batch;
+  int32_t* n_splits;
 };
 
 // DPP controls (gfx9): shifts and rotation inside rows of 16 lanes.
@@ -459,18 +463,85 @@ __device__ __forceinline__ void rotate_queries(int group, int q_dtype, const uin
 // processes the sequence's last page quantises the token's K and V rows,
 // patches the record into its LDS copy of the page before using it, and
 // stores it into the cache.
-template <bool PACK8, int kDecWaves, bool APPEND, int BITS>
+// BALANCED (several sequences of unequal length): the split plan is made on
+// the device from the lengths, so that every workgroup gets about the same
+// number of pages: sequence b receives n_b = ceil(pages_b / P) splits per kv
+// head, P the smallest budget for which these fit the plan's workgroups (a
+// binary search from total pages / workgroups), and workgroup i (a flat grid)
+// finds its (sequence, kv head, split) by a prefix sum over the sequences.
+// Without it the host plans from the longest length alone, and the splits of
+// short sequences idle while those of the longest run.
+template <bool PACK8, int kDecWaves, bool APPEND, int BITS, bool BALANCED>
 __global__ __launch_bounds__(64 * kDecWaves, 1) void decode_split_kernel(const int32_t* __restrict__ block_table,
                                                                       const int32_t* __restrict__ seq_lens,
                                                                       const uint8_t* __restrict__ q_bytes,
                                                                       const float* __restrict__ rot_all,
-                                                                      int max_pages, int pages_per_split,
+                                                                      int max_pages, int pps_arg,
                                                                       int hq, int group, int q_dtype,
                                                                       int splits, DecodeArgs a) {
   // The leading arguments are preloaded into SGPRs (14 dwords): everything
   // the first loads need.  The rest come from the argument struct.
-  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
+  int split, g, b, pages_per_split;
+  if constexpr (BALANCED) {
+    // every wave computes the same plan; lane s holds sequence s (batch <= 64)
+    int pages = 0;
+    if (lane < a.batch) pages = min((seq_lens[lane] + kPage - 1) / kPage, max_pages);
+    // sums over the lanes on the DPP / permlane path, in fp32 (exact: counts
+    // stay far below 2^24)
+    auto wave_sum = [](float v) {
+      v += quad_xor1(v);
+      v += quad_xor2(v);
+      v = add_xor4(v);
+      v += lane_xor8_f(v);
+      return sum_xor32(sum_xor16(v));
+    };
+    const long long total = (long long)wave_sum((float)pages) * a.hkv;
+    // the smallest per-workgroup budget P whose splits, rounded up per
+    // sequence, fit the plan's workgroups (at most the staging cap)
+    constexpr int kCap = 64 * kDecWaves;
+    const int G = a.plan_wgs;
+    const long long units = (long long)a.batch * a.hkv;
+    auto fits = [&](int p) {  // the rounded-up split count fits the plan's workgroups
+      const float n = wave_sum(lane < a.batch ? (float)max(1, (pages + p - 1) / p) : 0.f);
+      return (long long)n * a.hkv <= G;
+    };
+    // bounds: total / G pages each is the least possible; total / (G - units)
+    // always fits (rounding adds at most one split per kv head and sequence)
+    int lo = (int)max(1LL, (total + G - 1) / G);
+    int hi = G > units ? (int)max((long long)lo, (total + (G - units) - 1) / (G - units)) : max(lo, max_pages);
+    hi = min(hi, max(lo, max_pages));
+    if (fits(lo)) hi = lo;  // equal lengths: the even split
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (fits(mid)) hi = mid;
+      else lo = mid + 1;
+    }
+    const int pbar = min(lo, kCap);
+    const int nb = lane < a.batch ? max(1, (pages + pbar - 1) / pbar) : 0;  // an empty one gets 1
+    int cum = nb * a.hkv;  // inclusive prefix sum over the sequences
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int t = __shfl_up(cum, o);
+      if (lane >= o) cum += t;
+    }
+    const int i = blockIdx.x;
+    const int bb = __popcll(__ballot(lane < a.batch && cum <= i));
+    if (bb >= a.batch) return;  // a workgroup beyond the plan (uniform)
+    const int base = bb == 0 ? 0 : __shfl(cum, bb - 1);
+    const int nbb = __shfl(nb, bb), pb = __shfl(pages, bb);
+    const int off = i - base;
+    b = __builtin_amdgcn_readfirstlane(bb);
+    g = __builtin_amdgcn_readfirstlane(off / nbb);
+    split = __builtin_amdgcn_readfirstlane(off - (off / nbb) * nbb);
+    pages_per_split = __builtin_amdgcn_readfirstlane(max(1, (pb + nbb - 1) / nbb));
+    if (tid == 0 && g == 0 && split == 0) a.n_splits[b] = nbb;
+  } else {
+    split = blockIdx.x;
+    g = blockIdx.y;
+    b = blockIdx.z;
+    pages_per_split = pps_arg;
+  }
   // wave-uniform: keeps the wave's page bookkeeping in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, jq = lane >> 4;
@@ -794,15 +865,19 @@ __global__ __launch_bounds__(256, 1) void decode_merge_kernel(const float* __res
                                                            const float* __restrict__ ws_acc,
                                                            const float* __restrict__ ws_ml,
                                                            int splits, int hq_n, int group,
+                                                           const int32_t* __restrict__ n_splits,
                                                            float* __restrict__ out_all) {
   // All arguments arrive preloaded in SGPRs and every load is issued at once.
   // Each planned split has written its row (an empty one only m = -inf,
   // l = 0), so no length is needed here; zero-weight rows never touch the sums.
+  // (A sequence's first merge chunk always exists: count >= 1.)
   const int hq = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int quad = tid & 31, grp = tid >> 5;
   __shared__ float s_m[8], s_l[8];
   __shared__ f4 s_part[8][32];
   const size_t row0 = ((size_t)b * hq_n + hq) * splits;
+  // rows hold `splits` slots; a balanced plan used the first n_splits[b]
+  const int count = n_splits ? n_splits[b] : splits;
   const float2* ml = reinterpret_cast<const float2*>(ws_ml) + row0;
   const f4* accp = reinterpret_cast<const f4*>(ws_acc + row0 * kD) + quad;
 
@@ -824,14 +899,14 @@ __global__ __launch_bounds__(256, 1) void decode_merge_kernel(const float* __res
     f4 av[kMergeChunk];
 #pragma unroll
     for (int k = 0; k < kMergeChunk; ++k) {  // rows past the end repeat the last one
-      const int s = min(s0 + 8 * k, splits - 1);
+      const int s = min(s0 + 8 * k, count - 1);
       mv[k] = ml[s];
       av[k] = accp[(size_t)s * (kD / 4)];
     }
     __builtin_amdgcn_sched_barrier(0);  // every load above issues before any use
 #pragma unroll
     for (int k = 0; k < kMergeChunk; ++k)
-      if (s0 + 8 * k >= splits) mv[k].x = -INFINITY;  // ... with zero weight
+      if (s0 + 8 * k >= count) mv[k].x = -INFINITY;  // ... with zero weight
     float cm = m_t;
 #pragma unroll
     for (int k = 0; k < kMergeChunk; ++k) cm = fmaxf(cm, mv[k].x);
@@ -854,7 +929,7 @@ __global__ __launch_bounds__(256, 1) void decode_merge_kernel(const float* __res
     m_t = cm;
   };
   merge_chunk(grp);  // no loop before the first chunk: its loads follow the ones above
-  for (int s0 = grp + 8 * kMergeChunk; s0 < splits; s0 += 8 * kMergeChunk) merge_chunk(s0);
+  for (int s0 = grp + 8 * kMergeChunk; s0 < count; s0 += 8 * kMergeChunk) merge_chunk(s0);
   s_part[grp][quad] = acc_t;
   if (quad == 0) {
     s_m[grp] = m_t;
@@ -957,7 +1032,7 @@ DecodePlan plan_decode(int batch, int hkv, int max_seq_len, int num_cus) {
   const int max_pages = max(1, (max_seq_len + kPage - 1) / kPage);
   const long long units = (long long)max(1, batch) * max(1, hkv);
   const long long cus = max(1, num_cus);
-  DecodePlan p;
+  DecodePlan p{};
   p.waves = (units * max_pages <= cus * 4 * 2) ? 4 : 8;
   if (const char* env = getenv("IQ_DECODE_WAVES")) {
     const int v = atoi(env);
@@ -980,12 +1055,37 @@ DecodePlan plan_decode(int batch, int hkv, int max_seq_len, int num_cus) {
   if (pps < 1) pps = 1;
   p.pages_per_split = (int)pps;
   p.splits = (int)((max_pages + pps - 1) / pps);
+  p.balanced = 0;
+  p.grid_x = p.splits;
+  p.plan_wgs = 0;
+  // Several sequences: the device balances the pages (their lengths are known
+  // only there).  The plan's G workgroups hold at most `cap` pages each; rows
+  // of the workspace get ceil(G / Hkv) slots, the most one sequence can take
+  // (its pages are at most total / Hkv), and the grid G + B Hkv workgroups
+  // (rounding up every sequence's count adds at most one per kv head).
+  bool balanced = batch > 1 && batch <= 64;
+  if (const char* env = getenv("IQ_DECODE_BALANCED")) balanced = balanced && atoi(env) != 0;
+  if (balanced) {
+    long long G = rounds * cus;
+    const long long need = (units * max_pages + cap - 1) / cap;
+    if (G < need) G = need;
+    long long slots = (G + hkv - 1) / hkv;
+    if (slots > max_pages) slots = max_pages;
+    if (slots < 1) slots = 1;
+    p.balanced = 1;
+    p.plan_wgs = (int)G;
+    p.grid_x = (int)(G + units);
+    p.splits = (int)slots;
+    p.pages_per_split = (int)cap;
+  }
   return p;
 }
 
 size_t decode_workspace_bytes(int batch, int hq, const DecodePlan& plan) {
   const size_t rows = (size_t)batch * hq * plan.splits;
-  return rows * kD * sizeof(float) + rows * 2 * sizeof(float);
+  // + one split count per sequence for a balanced plan
+  return rows * kD * sizeof(float) + rows * 2 * sizeof(float) +
+         (plan.balanced ? (size_t)batch * sizeof(int32_t) : 0);
 }
 
 hipError_t launch_decode(const CacheView& c, const float* rot, const void* q, int q_dtype, int batch,
@@ -1018,15 +1118,21 @@ hipError_t launch_decode(const CacheView& c, const float* rot, const void* q, in
   a.ws_acc = reinterpret_cast<float*>(workspace);
   a.ws_ml = a.ws_acc + rows * kD;
   a.out = out;
+  a.plan_wgs = plan.plan_wgs;
+  a.batch = batch;
+  a.n_splits = plan.balanced ? reinterpret_cast<int32_t*>(a.ws_ml + rows * 2) : nullptr;
   const uint8_t* qb = static_cast<const uint8_t*>(q);
-  const dim3 grid(plan.splits, c.hkv, batch);
-#define IQ_SPLIT(P8, W, AP, B)                                                                    \
-  hipLaunchKernelGGL((decode_split_kernel<P8, W, AP, B>), grid, dim3(64 * W), 0, stream,           \
+  const dim3 grid = plan.balanced ? dim3(plan.grid_x, 1, 1) : dim3(plan.splits, c.hkv, batch);
+#define IQ_SPLIT_K(P8, W, AP, B, BAL)                                                             \
+  hipLaunchKernelGGL((decode_split_kernel<P8, W, AP, B, BAL>), grid, dim3(64 * W), 0, stream,      \
                      block_table, seq_lens, qb, rot, a.max_pages, a.pages_per_split, a.hq, a.group, \
                      a.q_dtype, a.splits, a)
-#define IQ_SPLIT_B(P8, W, AP)             \
-  if (four) IQ_SPLIT(P8, W, AP, 4);       \
-  else IQ_SPLIT(P8, W, AP, 3)
+#define IQ_SPLIT(P8, W, AP, B)                    \
+  if (plan.balanced) IQ_SPLIT_K(P8, W, AP, B, true); \
+  else IQ_SPLIT_K(P8, W, AP, B, false)
+#define IQ_SPLIT_B(P8, W, AP)               \
+  if (four) { IQ_SPLIT(P8, W, AP, 4); }     \
+  else { IQ_SPLIT(P8, W, AP, 3); }
 #define IQ_SPLIT_W(P8, AP)              \
   if (plan.waves == 4) { IQ_SPLIT_B(P8, 4, AP); } \
   else { IQ_SPLIT_B(P8, 8, AP); }
@@ -1041,21 +1147,22 @@ hipError_t launch_decode(const CacheView& c, const float* rot, const void* q, in
 #undef IQ_SPLIT_W
 #undef IQ_SPLIT_B
 #undef IQ_SPLIT
+#undef IQ_SPLIT_K
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_decode_merge(true, rot, a.ws_acc, a.ws_ml, plan.splits, batch, hq, a.group, out,
-                             stream);
+  return launch_decode_merge(true, rot, a.ws_acc, a.ws_ml, plan.splits, batch, hq, a.group, a.n_splits,
+                             out, stream);
 }
 
 hipError_t launch_decode_merge(bool rotate, const float* rot, const float* ws_acc, const float* ws_ml,
-                               int splits, int batch, int hq, int group, float* out,
-                               hipStream_t stream) {
+                               int splits, int batch, int hq, int group, const int32_t* n_splits,
+                               float* out, hipStream_t stream) {
   if (rotate)
     hipLaunchKernelGGL(decode_merge_kernel<true>, dim3(hq, batch), dim3(256), 0, stream, rot, ws_acc,
-                       ws_ml, splits, hq, group, out);
+                       ws_ml, splits, hq, group, n_splits, out);
   else
     hipLaunchKernelGGL(decode_merge_kernel<false>, dim3(hq, batch), dim3(256), 0, stream, rot,
-                       ws_acc, ws_ml, splits, hq, group, out);
+                       ws_acc, ws_ml, splits, hq, group, n_splits, out);
   return hipGetLastError();
 }
 

@@ -479,7 +479,7 @@ DecodePlan plan_dense_decode(int batch, int hkv, int max_seq_len, int num_cus) {
   if (splits > max_pages) splits = max_pages;
   long long pps = (max_pages + splits - 1) / splits;
   if (pps > kDenseMaxPagesPerSplit) pps = kDenseMaxPagesPerSplit;
-  DecodePlan p;
+  DecodePlan p{};
   p.waves = kDenseWaves;
   p.pages_per_split = (int)pps;
   p.splits = (int)((max_pages + pps - 1) / pps);
@@ -512,8 +512,8 @@ hipError_t launch_dense_decode(const DenseCacheView& c, const void* q, int batch
                        block_table, seq_lens, qh, max_pages, plan.pages_per_split, hq, group, plan.splits, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_decode_merge(false, nullptr, a.ws_acc, a.ws_ml, plan.splits, batch, hq, group, out,
-                             stream);
+  return launch_decode_merge(false, nullptr, a.ws_acc, a.ws_ml, plan.splits, batch, hq, group, nullptr,
+                             out, stream);
 }
 
 // ---------------------------------------------------------------------------

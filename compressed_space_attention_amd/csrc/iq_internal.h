@@ -46,9 +46,12 @@ hipError_t launch_quantize_append(const CacheView& c, const float* rot, const vo
                                   hipStream_t stream);
 
 struct DecodePlan {
-  int splits;           // workgroups per (sequence, kv head)
+  int splits;           // workgroups per (sequence, kv head); balanced: slots per workspace row
   int pages_per_split;
   int waves;            // waves per workgroup: 4 (one short pass) or 8 (long streams)
+  int balanced;         // several sequences: the split plan is made on the device
+  int grid_x;           // balanced: workgroups launched (the plan's plus spare ones)
+  int plan_wgs;         // balanced: workgroups the pages are spread over
 };
 DecodePlan plan_decode(int batch, int hkv, int max_seq_len, int num_cus);
 size_t decode_workspace_bytes(int batch, int hq, const DecodePlan& plan);
@@ -63,9 +66,10 @@ hipError_t launch_decode(const CacheView& c, const float* rot, const void* q, in
 
 // Merge of the split partials ([B][Hq][splits] rows of m, l and acc[128]):
 // normalise and, with `rotate`, apply T^T (rot = the rotation buffer).
+// n_splits (nullable, device int[B]): the slots sequence b used.
 hipError_t launch_decode_merge(bool rotate, const float* rot, const float* ws_acc, const float* ws_ml,
-                               int splits, int batch, int hq, int group, float* out,
-                               hipStream_t stream);
+                               int splits, int batch, int hq, int group, const int32_t* n_splits,
+                               float* out, hipStream_t stream);
 
 // Uncompressed baseline (dense.hip): paged cache of bf16 (format 0) or FP8
 // E4M3 (format 1) values, K token-major [pages][hkv][64][128], V

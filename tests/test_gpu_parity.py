@@ -149,22 +149,70 @@ def test_decode_split_plans_agree():
     s = Scenario(400, lens, hkv=2, dtype="bf16", outliers=True)
     q = s.queries(401, 2, 16).cuda()
     outs = []
-    old = os.environ.get("IQ_DECODE_PAGES_PER_SPLIT")
+    saved = {k: os.environ.get(k) for k in ("IQ_DECODE_PAGES_PER_SPLIT", "IQ_DECODE_BALANCED")}
     try:
+        os.environ["IQ_DECODE_BALANCED"] = "0"        # host plans from the longest length
         for pps in ("1", "3", "16", "512"):
             os.environ["IQ_DECODE_PAGES_PER_SPLIT"] = pps
             outs.append(s.iq.decode_attention(s.cache, s.rot, q, s.bt_dev, s.lens_dev, 3000).cpu().numpy())
         again = s.iq.decode_attention(s.cache, s.rot, q, s.bt_dev, s.lens_dev, 3000).cpu().numpy()
+        os.environ.pop("IQ_DECODE_PAGES_PER_SPLIT")
+        os.environ["IQ_DECODE_BALANCED"] = "1"        # the device-balanced plan
+        outs.append(s.iq.decode_attention(s.cache, s.rot, q, s.bt_dev, s.lens_dev, 3000).cpu().numpy())
     finally:
-        if old is None:
-            os.environ.pop("IQ_DECODE_PAGES_PER_SPLIT", None)
-        else:
-            os.environ["IQ_DECODE_PAGES_PER_SPLIT"] = old
+        for k, v in saved.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
     ref = O.decode_attention(s.host_cache(), s.blocks, q.double().cpu().numpy(), s.block_table, lens)
     for o in outs + [again]:
         assert max_row_error(o, ref) <= tol()
         assert max_row_error(o, outs[0]) <= 0.5 * tol()
-    assert max_row_error(again, outs[-1]) <= 0.5 * tol()
+    assert max_row_error(again, outs[3]) <= 0.5 * tol()
+
+
+BALANCED_CASES = [
+    # (lens, hkv, hq, waves): very unequal lengths, empty and one-token
+    # sequences, more sequences than one wave of lanes would hold per kv head
+    ([0, 5, 64, 20000, 3000, 1], 2, 16, None),
+    ([40000, 64, 65, 128, 100, 7000, 3, 900], 4, 32, 8),
+    ([9000] * 3 + [0], 1, 4, 4),
+    (list(range(1, 2000, 45)), 2, 4, None),          # 45 sequences
+]
+
+
+@pytest.mark.parametrize("case", range(len(BALANCED_CASES)))
+def test_decode_balanced_plan(case):
+    """The device-balanced split plan (several sequences) against the oracle
+    and against the host plan from the longest length."""
+    lens, hkv, hq, waves = BALANCED_CASES[case]
+    _say(f"balanced decode lens={lens[:8]}... B={len(lens)} hkv={hkv} hq={hq} waves={waves}")
+    s = Scenario(450 + case, lens, hkv=hkv, dtype="bf16", outliers=True)
+    q = s.queries(460 + case, len(lens), hq).cuda()
+    saved = {k: os.environ.get(k) for k in ("IQ_DECODE_BALANCED", "IQ_DECODE_WAVES")}
+    try:
+        if waves:
+            os.environ["IQ_DECODE_WAVES"] = str(waves)
+        os.environ["IQ_DECODE_BALANCED"] = "1"
+        bal = s.iq.decode_attention(s.cache, s.rot, q, s.bt_dev, s.lens_dev, max(lens)).cpu().numpy()
+        os.environ["IQ_DECODE_BALANCED"] = "0"
+        uni = s.iq.decode_attention(s.cache, s.rot, q, s.bt_dev, s.lens_dev, max(lens)).cpu().numpy()
+    finally:
+        for k, v in saved.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+    ref = O.decode_attention(s.host_cache(), s.blocks, q.double().cpu().numpy(), s.block_table, lens)
+    err = max_row_error(bal, ref)
+    _say(f"  max row error {err:.3e}")
+    assert np.all(np.isfinite(bal))
+    assert err <= tol()
+    assert max_row_error(bal, uni) <= 0.5 * tol()
+    for b, n in enumerate(lens):
+        if n == 0:
+            assert np.all(bal[b] == 0)
 
 
 def test_decode_shuffled_equals_contiguous_block_table():
