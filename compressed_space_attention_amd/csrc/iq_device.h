@@ -35,15 +35,16 @@ struct __attribute__((aligned(4))) u3 {
 // ---------------------------------------------------------------------------
 constexpr double kLevel3[4] = {0.2451, 0.7560, 1.3440, 2.1520};
 constexpr float kThr3[3] = {0.50055f, 1.05f, 1.748f};
-__device__ __forceinline__ uint32_t code_of(float u) {
-  uint32_t c = (u >= -kThr3[2]);
-  c += (u >= -kThr3[1]);
-  c += (u >= -kThr3[0]);
-  c += (u >= 0.0f);
-  c += (u >= kThr3[0]);
-  c += (u >= kThr3[1]);
-  c += (u >= kThr3[2]);
-  return c;
+// code = number of the seven thresholds (-t3, -t2, -t1, 0, t1, t2, t3) that u
+// reaches, found by a binary search over them (three comparisons): code >= 4
+// iff u >= 0, then >= base + 2 iff u >= the threshold above base + 1, then
+// >= base + 1 likewise.
+__host__ __device__ __forceinline__ uint32_t code_of(float u) {
+  const bool b2 = u >= 0.0f;
+  const bool b1 = u >= (b2 ? kThr3[1] : -kThr3[1]);
+  const float t0 = b2 ? (b1 ? kThr3[2] : kThr3[0]) : (b1 ? -kThr3[0] : -kThr3[2]);
+  const bool b0 = u >= t0;
+  return (b2 ? 4u : 0u) | (b1 ? 2u : 0u) | (b0 ? 1u : 0u);
 }
 
 // The matrix-core kernels consume the levels as f16 operands.  They carry
@@ -123,16 +124,18 @@ struct Levels4 {
 
 // Nibble of u.  Nonnegative u (including -0): the magnitudes whose lower
 // threshold it reaches; negative u: 8 + the thresholds |u| exceeds (a tie
-// belongs to the upper code on either side).
-__device__ __forceinline__ uint32_t nibble_of(float u, const Levels4& lv) {
+// belongs to the upper code on either side).  "|u| > t" is "x >= t" for x the
+// float just below |u| (|u| > 0 there), so one binary search over the seven
+// ascending thresholds (three comparisons) serves both sides.
+__host__ __device__ __forceinline__ uint32_t nibble_of(float u, const Levels4& lv) {
+  const bool neg = !(u >= 0.0f);
   const float a = fabsf(u);
-  uint32_t ge = 0, gt = 0;
-#pragma unroll
-  for (int k = 0; k < 7; ++k) {
-    ge += (a >= lv.t[k]);
-    gt += (a > lv.t[k]);
-  }
-  return u >= 0.0f ? ge : 8u + gt;
+  const float x = neg ? __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, a) - 1u) : a;
+  const bool b2 = x >= lv.t[3];
+  const bool b1 = x >= (b2 ? lv.t[5] : lv.t[1]);
+  const float t0 = b2 ? (b1 ? lv.t[6] : lv.t[4]) : (b1 ? lv.t[2] : lv.t[0]);
+  const bool b0 = x >= t0;
+  return (neg ? 8u : 0u) | (b2 ? 4u : 0u) | (b1 ? 2u : 0u) | (b0 ? 1u : 0u);
 }
 
 // Four nibbles (one per byte, bits 0-3) -> four f16 levels (alpha-scaled) in

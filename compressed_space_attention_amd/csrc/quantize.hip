@@ -47,6 +47,9 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(
   const int tok = t0 + tl;
   const bool valid = tok < n_tok;
   __shared__ __attribute__((aligned(16))) uint8_t s_v[kPage * kRecB];  // the page's V block
+  // the head's rotation blocks, read from LDS by the transform (loaded once
+  // per workgroup instead of 32 16-byte loads per lane)
+  __shared__ __attribute__((aligned(16))) float s_rot[kRotFloats];
 
   // The destination is looked up while the vector is transformed: position
   // and sequence first, then the page id, all before the arithmetic.
@@ -60,7 +63,11 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(
   const bool in_table = (unsigned)p < (unsigned)max_pages * kPage;
   const int page = in_table ? block_table[(size_t)si * max_pages + (p >> 6)] : -1;
   const bool stored = (unsigned)page < (unsigned)num_pages;
-  // one whole page: every token in order, all stored (uniform for the workgroup)
+  if (threadIdx.x < kRotFloats / 4)
+    reinterpret_cast<f4*>(s_rot)[threadIdx.x] =
+        reinterpret_cast<const f4*>(rot + (size_t)head * kRotFloats)[threadIdx.x];
+  // one whole page: every token in order, all stored (uniform for the
+  // workgroup); the barrier also publishes the rotation blocks
   const bool whole = __syncthreads_and(valid && si == s0 && p == p0 + tl && (p0 & 63) == 0 && stored);
 
   float ss0 = 0.f, ss1 = 0.f, ss2 = 0.f, ss3 = 0.f;
@@ -77,25 +84,35 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(
   const float n = sqrtf(ss);
 
   wht128_quad(x, j);
-  float z[32];
-  so4_forward_quarter(rot + (size_t)head * kRotFloats, j, x, z);
+  // SO(4) block by block (blocks 8j .. 8j + 7 of the quarter), each block's
+  // four outputs turned into codes at once: sel[bb] holds the codes (3-bit)
+  // or nibbles (4-bit) of coordinates 32j + 4bb .. + 3, one per byte.  (The
+  // zero vector: every code 4, resp. nibble 0 = code 8.)
+  uint32_t sel[8];
+  {
+    const float inv_n = n > 0.f ? 1.0f / n : 0.f;
+#pragma unroll
+    for (int bb = 0; bb < 8; ++bb) {
+      const f4* m = reinterpret_cast<const f4*>(s_rot + (8 * j + bb) * 16);
+      uint32_t w = 0;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const f4 row = m[r];
+        const float zr = row[0] * x[4 * bb] + row[1] * x[4 * bb + 1] + row[2] * x[4 * bb + 2] +
+                         row[3] * x[4 * bb + 3];
+        uint32_t c;
+        if constexpr (BITS == 3) c = n > 0.f ? code_of(zr * inv_n) : 4u;
+        else c = n > 0.f ? nibble_of(zr * inv_n, lv) : 0u;
+        w |= c << (8 * r);
+      }
+      sel[bb] = w;
+    }
+  }
 
   const int slot = p & 63;
   const size_t rec = ((size_t)page * hkv + head) * kPage + slot;
   uint8_t* blk = whole ? s_v : v_codes + ((size_t)page * hkv + head) * (kPage * kRecB);
   if constexpr (BITS == 3) {
-    uint32_t sel[8];
-    if (n > 0.f) {
-      const float inv_n = 1.0f / n;
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        sel[s] = code_of(z[4 * s] * inv_n) | (code_of(z[4 * s + 1] * inv_n) << 8) |
-                 (code_of(z[4 * s + 2] * inv_n) << 16) | (code_of(z[4 * s + 3] * inv_n) << 24);
-      }
-    } else {
-#pragma unroll
-      for (int s = 0; s < 8; ++s) sel[s] = 0x04040404u;  // zero vector: level +0.2451 * 0
-    }
     u3 w;
     selectors_to_group(sel, w.x, w.y, w.z);
     if (!which) {
@@ -115,36 +132,25 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(
       }
     }
   } else {
-    uint32_t nib[32];
-    if (n > 0.f) {
-      const float inv_n = 1.0f / n;
-#pragma unroll
-      for (int i = 0; i < 32; ++i) nib[i] = nibble_of(z[i] * inv_n, lv);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 32; ++i) nib[i] = 0;  // zero vector: code 8 (level +0.128 * 0)
-    }
     if (!which) {
-      // record dword 4j + kk: byte b = coordinate 32j + 8kk + b (low), + 4 (high)
+      // record dword 4j + kk: byte b = coordinate 32j + 8kk + b (low nibble,
+      // selector 2kk) and 32j + 8kk + 4 + b (high nibble, selector 2kk + 1)
       u4 w;
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        uint32_t d = 0;
-#pragma unroll
-        for (int b = 0; b < 4; ++b) d |= (nib[8 * kk + b] | (nib[8 * kk + 4 + b] << 4)) << (8 * b);
-        w[kk] = d;
-      }
+      for (int kk = 0; kk < 4; ++kk) w[kk] = sel[2 * kk] | (sel[2 * kk + 1] << 4);
       if (stored) *reinterpret_cast<u4*>(k_codes + rec * kRec4 + 16 * j) = w;
     } else if (stored) {
-      // V: coordinates 32j + 4p + b and + 16 share byte slot % 4 of dword
-      // 4p + 2 th + q of region (4j + b) + 16 jq (slot = 32 th + 16 q + 4 jq + r)
+      // V: coordinates 32j + 4p + b (selector p) and + 16 (selector p + 4)
+      // share byte slot % 4 of dword 4p + 2 th + q of region (4j + b) + 16 jq
+      // (slot = 32 th + 16 q + 4 jq + r)
       const int th = slot >> 5, q = (slot >> 4) & 1, jq = (slot >> 2) & 3, r = slot & 3;
       uint8_t* dst = blk + (4 * j + 16 * jq) * 64 + 4 * (2 * th + q) + r;
 #pragma unroll
-      for (int pp = 0; pp < 4; ++pp)
+      for (int pp = 0; pp < 4; ++pp) {
+        const uint32_t v = sel[pp] | (sel[pp + 4] << 4);
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
-          dst[64 * b + 16 * pp] = (uint8_t)(nib[4 * pp + b] | (nib[16 + 4 * pp + b] << 4));
+        for (int b = 0; b < 4; ++b) dst[64 * b + 16 * pp] = (uint8_t)(v >> (8 * b));
+      }
     }
   }
   if (stored && j == 0) (which ? v_norms : k_norms)[rec] = float_to_half_sat(n);
