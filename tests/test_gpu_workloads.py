@@ -13,6 +13,7 @@ import pytest
 import torch
 
 from compressed_space_attention_amd import synth, workloads
+from oracle import isoquant4_oracle as O4
 from oracle import isoquant_oracle as O
 from tests.gpu_cases import max_row_error, tol
 
@@ -31,8 +32,8 @@ def _say(*a):
 class Built:
     """A workload's cache quantised by the GPU, inputs kept on the device."""
 
-    def __init__(self, w, lens, device="cuda"):
-        self.w = w
+    def __init__(self, w, lens, device="cuda", bits=3):
+        self.w, self.bits = w, bits
         self.lens = np.asarray(lens, dtype=np.int64)
         self.quats = synth.quaternions(w.seed, w.n_kv_heads)
         self.blocks = O.rotation_matrices(self.quats)
@@ -41,7 +42,7 @@ class Built:
         self.bt_dev = torch.from_numpy(self.bt).to(device)
         self.lens_dev = torch.from_numpy(self.lens.astype(np.int32)).to(device)
         self.rot = iq.rotation_init(self.quats, device=device)
-        self.cache = iq.PagedCache(self.num_pages, w.n_kv_heads, device=device, zero=True)
+        self.cache = iq.PagedCache(self.num_pages, w.n_kv_heads, device=device, zero=True, bits=bits)
         dt = {"bf16": torch.bfloat16, "f32": torch.float32}[w.dtype]
         total = int(self.lens.sum())
         scale = torch.ones(w.n_kv_heads, 128, device=device)
@@ -59,6 +60,10 @@ class Built:
         self.q = synth.draw_normal_device(w.seed + 4, (len(self.lens), w.n_q_heads, 128), dt, device)
         torch.cuda.synchronize()
 
+    def host(self):
+        arrays = self.cache.to_host()
+        return O4.PagedCache4.from_arrays(*arrays) if self.bits == 4 else O.PagedCache.from_arrays(*arrays)
+
     def sampled_code_parity(self, n_sample, seed):
         rng = np.random.default_rng(seed)
         idx = np.unique(rng.integers(0, len(self.pos), size=n_sample))
@@ -66,12 +71,16 @@ class Built:
         page = self.bt[self.seq_idx[idx], self.pos[idx] // 64]
         slot = self.pos[idx] % 64
         codes = mism = near = 0
-        host = O.PagedCache.from_arrays(*self.cache.to_host())
+        host = self.host()
         for name, x in (("k", self.k), ("v", self.v)):
             xs = x[torch.from_numpy(idx).cuda()].double().cpu().numpy()
             for h in range(self.w.n_kv_heads):
-                q = O.quantize(xs[:, h], self.blocks[h])
-                gc = O.unpack_codes(host.records(name, page, h, slot))
+                if self.bits == 4:
+                    q = O4.quantize4(xs[:, h], self.blocks[h])
+                    gc = host.codes(name, page, h, slot)
+                else:
+                    q = O.quantize(xs[:, h], self.blocks[h])
+                    gc = O.unpack_codes(host.records(name, page, h, slot))
                 gn = getattr(host, name + "_norms")[page, h, slot]
                 bad = gc != q["codes"]
                 assert not np.any(bad & ~q["near"]), f"{name} head {h}: code mismatch off-boundary"
@@ -89,10 +98,10 @@ class Built:
                                    int(self.lens.max()))
 
     def oracle_decode(self, seqs):
-        host = O.PagedCache.from_arrays(*self.cache.to_host())
         q = self.q.double().cpu().numpy()
         bt = self.bt[seqs]
-        return O.decode_attention(host, self.blocks, q[seqs], bt, self.lens[seqs])
+        fn = O4.decode_attention4 if self.bits == 4 else O.decode_attention
+        return fn(self.host(), self.blocks, q[seqs], bt, self.lens[seqs])
 
     def cosine_vs_uncompressed(self, seq, heads, out):
         grp = self.w.group
@@ -121,9 +130,10 @@ def test_tiny_decode_full():
     assert err <= tol()
 
 
-def test_gqa_decode_32k_full():
+@pytest.mark.parametrize("bits", [3, 4])
+def test_gqa_decode_32k_full(bits):
     w = workloads.GQA_DECODE_32K
-    b = Built(w, w.seq_lens())
+    b = Built(w, w.seq_lens(), bits=bits)
     b.sampled_code_parity(8192, 2)
     out = b.decode().cpu().numpy()
     ref = b.oracle_decode(np.arange(w.batch))
@@ -133,10 +143,11 @@ def test_gqa_decode_32k_full():
     assert err <= tol()
 
 
-def test_ragged_decode_sampled_sequences():
+@pytest.mark.parametrize("bits", [3, 4])
+def test_ragged_decode_sampled_sequences(bits):
     w = workloads.RAGGED_DECODE
     lens = w.seq_lens()
-    b = Built(w, lens)
+    b = Built(w, lens, bits=bits)
     b.sampled_code_parity(8192, 3)
     out = b.decode().cpu().numpy()
     pick = np.unique([int(np.argmin(lens)), int(np.argmax(lens)), 5])
@@ -158,18 +169,19 @@ def test_long_decode_128k_sampled_sequence():
     assert np.all(np.isfinite(out))
 
 
-def test_chunked_prefill_full_shape_sampled_rows():
+@pytest.mark.parametrize("bits", [3, 4])
+def test_chunked_prefill_full_shape_sampled_rows(bits):
     p = workloads.CHUNKED_PREFILL
     w = workloads.DecodeWorkload(p.name, 1, p.n_q_heads, p.n_kv_heads, p.dtype, False, True,
                                  p.seed, context=p.total)
     # cache: the first `cached` tokens, then the appended chunk in a second call
-    b = Built(w, [p.cached])
+    b = Built(w, [p.cached], bits=bits)
     k2 = synth.draw_normal_device(p.seed + 7, (p.appended, p.n_kv_heads, 128), torch.bfloat16)
     v2 = synth.draw_normal_device(p.seed + 8, (p.appended, p.n_kv_heads, 128), torch.bfloat16)
     pages = -(-p.total // 64)
     bt, num_pages = synth.block_table(p.seed + 9, [pages], shuffle=True)
     b.bt, b.bt_dev = bt, torch.from_numpy(bt).cuda()
-    b.cache = iq.PagedCache(num_pages, p.n_kv_heads, zero=True)
+    b.cache = iq.PagedCache(num_pages, p.n_kv_heads, zero=True, bits=bits)
     pos1 = torch.arange(p.cached, dtype=torch.int32, device="cuda")
     pos2 = torch.arange(p.cached, p.total, dtype=torch.int32, device="cuda")
     iq.quantize_append(b.cache, b.rot, b.k, b.v, torch.zeros_like(pos1), pos1, b.bt_dev)
@@ -183,8 +195,8 @@ def test_chunked_prefill_full_shape_sampled_rows():
     q = synth.draw_normal_device(p.seed + 10, (p.n_queries, p.n_q_heads, 128), torch.bfloat16)
     out = iq.prefill_attention(b.cache, b.rot, q, p.q_start, b.bt_dev[0]).cpu().numpy()
     rows = np.array([0, 1, 100, 255, 256, 400, p.n_queries - 2, p.n_queries - 1])
-    host = O.PagedCache.from_arrays(*b.cache.to_host())
-    ref = O.prefill_attention(host, b.blocks, q.double().cpu().numpy(), p.q_start, bt[0], rows=rows)
+    fn = O4.prefill_attention4 if bits == 4 else O.prefill_attention
+    ref = fn(b.host(), b.blocks, q.double().cpu().numpy(), p.q_start, bt[0], rows=rows)
     err = max_row_error(out[rows], ref)
     _say(f"  {p.name}: max row error {err:.3e} over rows {rows.tolist()}")
     assert err <= tol()
