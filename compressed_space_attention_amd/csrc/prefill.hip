@@ -41,7 +41,16 @@ namespace iq {
 
 constexpr int kRowsPerTile = 128;  // rows = queries x group heads
 constexpr int kKStride = 136;   // halves per K^ row (128 + 8 pad)
-constexpr int kVStride = 68;    // halves per V^T row (64 + 4 pad: 16 rows hit 16 distinct 8-byte bank slots)
+// halves per V^T row (64 + 8 pad: rows start 16-byte aligned and the 16 rows of
+// one fragment read cover the 64 banks once).  Within a row the tokens of each
+// 32-token half are in the matrix-core k order (see vt_col), so a lane's eight
+// P.V operands are one 16-byte read.
+constexpr int kVStride = 72;
+// column of token t (0..63) in a V^T row: half tp = t / 32 holds, for lane
+// group jq, tokens 4 jq .. +3 then 16 + 4 jq .. +3 at columns 32 tp + 8 jq ..
+__host__ __device__ constexpr int vt_col(int t) {
+  return 32 * (t >> 5) + 8 * ((t & 15) >> 2) + 4 * ((t & 31) >> 4) + (t & 3);
+}
 constexpr int kRawPage = 8192;  // raw code bytes of a page in LDS: 512 groups of 12 B at a 16 B stride
 constexpr int kRawSlot = kRawPage + 256;  // + the page's K and V norms
 constexpr int kRawSlots = 3;
@@ -165,9 +174,10 @@ __device__ __forceinline__ void pf_unpack_v(const u3& cv, int region, int c, _Fl
   uint32_t z[8];
   group_to_selectors(cv.x, cv.y, cv.z, z);
   const int n = region & 15, q = region >> 4;
+  const int col = vt_col(16 * c + 4 * q);  // the four tokens stay adjacent
 #pragma unroll
   for (int m = 0; m < 8; ++m)
-    *reinterpret_cast<u2*>(sv + (16 * m + n) * kVStride + 16 * c + 4 * q) = selector_to_f16(z[m]);
+    *reinterpret_cast<u2*>(sv + (16 * m + n) * kVStride + col) = selector_to_f16(z[m]);
 }
 
 // 4-bit: quarter j of token tok's record (dword kk = coordinates 32j + 8kk
@@ -189,10 +199,10 @@ __device__ __forceinline__ void pf_unpack_v4(const u4& cv, int region, int p, _F
   const int n = region & 15, jq = region >> 4;
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
-    const int tok = 32 * (d >> 1) + 16 * (d & 1) + 4 * jq;
+    const int col = vt_col(32 * (d >> 1) + 16 * (d & 1) + 4 * jq);
     const uint32_t w = cv[d];
-    *reinterpret_cast<u2*>(sv + (16 * p + n) * kVStride + tok) = nibbles_to_f16(w & 0x0F0F0F0Fu, lv);
-    *reinterpret_cast<u2*>(sv + (16 * (p + 4) + n) * kVStride + tok) =
+    *reinterpret_cast<u2*>(sv + (16 * p + n) * kVStride + col) = nibbles_to_f16(w & 0x0F0F0F0Fu, lv);
+    *reinterpret_cast<u2*>(sv + (16 * (p + 4) + n) * kVStride + col) =
         nibbles_to_f16((w >> 4) & 0x0F0F0F0Fu, lv);
   }
 }
@@ -471,10 +481,8 @@ __global__ __launch_bounds__(64 * pf_waves<RB>(), 1) void prefill_kernel(Prefill
     for (int m = 0; m < 8; ++m) {
 #pragma unroll
       for (int tp = 0; tp < 2; ++tp) {
-        const _Float16* vr = svp + (16 * m + col) * kVStride + 32 * tp + 4 * jq;
-        const h4 v0 = *reinterpret_cast<const h4*>(vr);
-        const h4 v1 = *reinterpret_cast<const h4*>(vr + 16);
-        const h8 av = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        // k index 8 jq + i: token 32 tp + 4 jq + i (i < 4) or 32 tp + 16 + 4 jq + i - 4
+        const h8 av = *reinterpret_cast<const h8*>(svp + (16 * m + col) * kVStride + 32 * tp + 8 * jq);
 #pragma unroll
         for (int cb = 0; cb < RB; ++cb)
           acc[cb][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pb[tp][cb], acc[cb][m], 0, 0, 0);
