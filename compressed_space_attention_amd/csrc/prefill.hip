@@ -15,16 +15,16 @@
 // head and walks the pages up to its causal limit.  Two shapes (RB = row
 // blocks of 16 per wave): RB = 2, four waves of 32 rows (every K^ and V^
 // fragment read from LDS feeds four matrix-core products, one wave per SIMD);
-// RB = 1, eight waves of 16 rows (two waves per SIMD, so one wave's softmax
-// and unpacking run while the other's products occupy the matrix core, at
-// twice the LDS reads per product).  Per page:
-//   * raw pages arrive by direct-to-LDS loads three pages ahead (each wave
-//     loads exactly the 12-byte groups it will unpack, so no wave waits for
-//     another's loads);
-//   * the unpacked page -- K^ token-major, V^ as [coordinate][token], both
-//     alpha-scaled f16, and the fp16 norms -- is double-buffered in LDS, so a
-//     page is unpacked while the previous one is multiplied and one barrier
-//     per page suffices;
+// RB = 1, eight waves of 16 rows (two waves per SIMD).  The pages run as a
+// software pipeline, one barrier per page:
+//   * raw pages arrive by direct-to-LDS loads issued two steps before they
+//     are unpacked (each wave loads exactly the code bytes it will unpack,
+//     so no wave waits for another's loads);
+//   * unpacked pages -- K^ token-major, V^ as [coordinate][token], both
+//     alpha-scaled f16, and the fp16 norms -- sit in a ring of three LDS
+//     buffers: while page p's softmax and P.V products run, page p + 1's
+//     scores are already on the matrix cores (in a second register set) and
+//     page p + 2 is being unpacked;
 //   * only pages that reach past the smallest query position of the tile are
 //     masked.
 // The page ids of the whole causal range are staged in LDS once.
@@ -86,8 +86,13 @@ struct PrefillArgs {
 // explicit s_waitcnt on this kernel's issue order instead.  No register
 // outputs: the address is read at issue, the destination is LDS at m0.
 typedef __attribute__((address_space(3))) void* pf_lds_ptr;
-__device__ __forceinline__ void pf_dma(const void* g, void* lds, int size) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(pf_lds_ptr)lds);
+// LDS byte address of a shared-memory pointer (pointers into a kernel's
+// __shared__ arrays only)
+__device__ __forceinline__ uint32_t pf_lds_addr(const void* lds) {
+  return (uint32_t)(uintptr_t)(pf_lds_ptr)lds;
+}
+__device__ __forceinline__ void pf_dma(const void* g, uint32_t lds, int size) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds);
   if (size == 16)
     asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(m0) : "memory");
   else if (size == 12)
@@ -100,7 +105,7 @@ __device__ __forceinline__ void pf_dma(const void* g, void* lds, int size) {
 constexpr int kPfWaitLgkm0 = 0xF | (0x3 << 14) | (0x7 << 4);
 
 template <bool M>
-struct PfMaskTag {
+struct PfTag {
   static constexpr bool value = M;
 };
 
@@ -114,46 +119,44 @@ __device__ __forceinline__ float times_norm2(float x, const u2& n, int r) {
   return __builtin_fmaf(x, norm_at2(n, r), 0.0f);
 }
 
-// Raw loads of one page into a slot (each wave loads exactly the 12-byte
-// groups it unpacks).  Four waves: wave w brings the K records of tokens
-// 16w..16w+15 (lane l: token 16w + l/4, group l%4 -- 768 contiguous bytes)
-// and chunk w of every V region (lane l: region l).  Eight waves: lanes 0-31
-// the K records of tokens 8w..8w+7, lanes 32-63 chunk w/2 of V regions
-// 32(w%2) .. +31.  Wave 0 also brings the K norms (lanes 0-31) and V norms
-// (lanes 32-63).  Returns the number of loads issued.
-// BITS = 4: the same split in 16-byte units of the 4,096-byte K and V blocks,
-// contiguous per wave: four waves, bytes 1024w.. of each block; eight waves,
-// lanes 0-31 bytes 512w.. of the K block and lanes 32-63 of the V block.
-template <int W, int BITS>
-__device__ __forceinline__ int pf_issue(const PrefillArgs& a, int page_id, int g, int wave, int lane,
-                                        uint8_t* slot) {
+// What one wave loads and unpacks of every page: a quarter `part` of the K
+// codes (DO_K) and/or of the V codes (DO_V), and with NORMS (wave 0) also the
+// page's norms.  Four waves carry both quarters of their part; eight waves
+// split them, waves 0-3 the K quarters and waves 4-7 the V quarters, so that
+// every unpack runs on all 64 lanes.
+template <bool DO_K, bool DO_V, bool NORMS>
+struct PfRole {
+  static constexpr bool k = DO_K, v = DO_V, norms = NORMS;
+  static constexpr int loads = (DO_K ? 1 : 0) + (DO_V ? 1 : 0) + (NORMS ? 1 : 0);  // per page
+};
+
+// Raw loads of one page into a slot (each wave loads exactly the groups it
+// unpacks).  Part p of a raw slot: K bytes at 2048 p, V bytes at 2048 p + 1024
+// (64 lanes x 16 bytes each).  3-bit: the K quarter is the records of tokens
+// 16p..16p+15 (lane l: token 16p + l/4, group l%4 -- 768 contiguous bytes),
+// the V quarter chunk p of every V region (lane l: region l).  4-bit: bytes
+// 1024p.. of the 4,096-byte K and V blocks.  NORMS: the K norms (lanes 0-31)
+// and V norms (lanes 32-63).
+template <int BITS, class R>
+__device__ __forceinline__ void pf_issue(const PrefillArgs& a, int page_id, int g, int part, int lane,
+                                         uint32_t slot) {
   // an id outside the cache (a table that breaks the contract) is clamped into
   // it, so a bad table gives wrong numbers, never an out-of-bounds read
   const uint32_t page = min((uint32_t)page_id, (uint32_t)a.num_pages - 1u);
   const size_t base = ((size_t)page * a.hkv + g) * kPage;
-  uint8_t* dst = slot + wave * (kRawPage / W);
+  const uint32_t dst = slot + 2048 * part;
   if (BITS == 4) {
     const size_t blk = base * kRec4;
-    if (W == 4) {
-      pf_dma(a.k_codes + blk + 1024 * wave + 16 * lane, dst, 16);
-      pf_dma(a.v_codes + blk + 1024 * wave + 16 * lane, dst + 1024, 16);
-    } else {
-      pf_dma((lane < 32 ? a.k_codes : a.v_codes) + blk + 512 * wave + 16 * (lane & 31), dst, 16);
-    }
-  } else if (W == 4) {
-    pf_dma(a.k_codes + base * kRec + 768 * wave + 12 * lane, dst, 12);
-    pf_dma(a.v_codes + (base + lane) * kRec + 12 * wave, dst + 1024, 12);
+    if (R::k) pf_dma(a.k_codes + blk + 1024 * part + 16 * lane, dst, 16);
+    if (R::v) pf_dma(a.v_codes + blk + 1024 * part + 16 * lane, dst + 1024, 16);
   } else {
-    const uint8_t* src = lane < 32 ? a.k_codes + base * kRec + 384 * wave + 12 * lane
-                                   : a.v_codes + (base + 32 * (wave & 1) + (lane - 32)) * kRec +
-                                         12 * (wave >> 1);
-    pf_dma(src, dst, 12);
+    if (R::k) pf_dma(a.k_codes + base * kRec + 768 * part + 12 * lane, dst, 12);
+    if (R::v) pf_dma(a.v_codes + (base + lane) * kRec + 12 * part, dst + 1024, 12);
   }
-  if (wave == 0) {
+  if (R::norms) {
     const uint16_t* nb = (lane < 32 ? a.k_norms : a.v_norms) + base + 2 * (lane & 31);
     pf_dma(nb, slot + kRawPage, 4);
   }
-  return (W == 4 ? 2 : 1) + (wave == 0 ? 1 : 0);
 }
 
 // One K group (token tok, coordinates 32j..32j+31) into the f16 K^ buffer.
@@ -207,46 +210,22 @@ __device__ __forceinline__ void pf_unpack_v4(const u4& cv, int region, int p, _F
   }
 }
 
-// Unpack this thread's groups of a raw page (four waves: a K group and a V
-// chunk; eight waves: one of the two) into the f16 buffers.
-template <int W, int BITS>
-__device__ __forceinline__ void pf_unpack(const uint8_t* slot, int wave, int lane, _Float16* sk,
+// Unpack this wave's part of a raw page into the f16 buffers.
+template <int BITS, class R>
+__device__ __forceinline__ void pf_unpack(const uint8_t* slot, int part, int lane, _Float16* sk,
                                           _Float16* sv, uint16_t* snorm, const Levels4& lv) {
-  const uint8_t* raw = slot + wave * (kRawPage / W) + 16 * lane;
+  const uint8_t* raw = slot + 2048 * part + 16 * lane;
   if (BITS == 4) {
     // 16-byte unit u of a block: K token u / 4, quarter u % 4; V region u / 4, dwords 4(u % 4)..
-    if (W == 4) {
-      const int u = 64 * wave + lane;
-      pf_unpack_k4(*reinterpret_cast<const u4*>(raw), u >> 2, u & 3, sk, lv);
-      pf_unpack_v4(*reinterpret_cast<const u4*>(raw + 1024), u >> 2, u & 3, sv, lv);
-    } else {
-      const int u = 32 * wave + (lane & 31);
-      if (lane < 32) pf_unpack_k4(*reinterpret_cast<const u4*>(raw), u >> 2, u & 3, sk, lv);
-      else pf_unpack_v4(*reinterpret_cast<const u4*>(raw), u >> 2, u & 3, sv, lv);
-    }
-  } else if (W == 4) {
-    pf_unpack_k(*reinterpret_cast<const u3*>(raw), 16 * wave + (lane >> 2), lane & 3, sk);
-    pf_unpack_v(*reinterpret_cast<const u3*>(raw + 1024), lane, wave, sv);
-  } else if (lane < 32) {
-    pf_unpack_k(*reinterpret_cast<const u3*>(raw), 8 * wave + (lane >> 2), lane & 3, sk);
+    const int u = 64 * part + lane;
+    if (R::k) pf_unpack_k4(*reinterpret_cast<const u4*>(raw), u >> 2, u & 3, sk, lv);
+    if (R::v) pf_unpack_v4(*reinterpret_cast<const u4*>(raw + 1024), u >> 2, u & 3, sv, lv);
   } else {
-    pf_unpack_v(*reinterpret_cast<const u3*>(raw), 32 * (wave & 1) + (lane - 32), wave >> 1, sv);
+    if (R::k) pf_unpack_k(*reinterpret_cast<const u3*>(raw), 16 * part + (lane >> 2), lane & 3, sk);
+    if (R::v) pf_unpack_v(*reinterpret_cast<const u3*>(raw + 1024), lane, part, sv);
   }
-  if (wave == 0)
+  if (R::norms)
     reinterpret_cast<uint32_t*>(snorm)[lane] = reinterpret_cast<const uint32_t*>(slot + kRawPage)[lane];
-}
-
-// s_waitcnt vmcnt(n) for a count known only at run time (0..7)
-__device__ __forceinline__ void pf_wait_vm(int n) {
-  switch (n) {
-    case 0: IQ_PF_WAIT_VM(0); break;
-    case 1: IQ_PF_WAIT_VM(1); break;
-    case 2: IQ_PF_WAIT_VM(2); break;
-    case 3: IQ_PF_WAIT_VM(3); break;
-    case 4: IQ_PF_WAIT_VM(4); break;
-    case 5: IQ_PF_WAIT_VM(5); break;
-    default: IQ_PF_WAIT_VM(6); break;
-  }
 }
 
 template <int RB, int BITS>
@@ -276,16 +255,16 @@ __global__ __launch_bounds__(64 * pf_waves<RB>(), 1) void prefill_kernel(Prefill
   // pages entirely at or before the smallest query position need no mask
   const int n_full = min(n_pages, (q_start + q0 + 1) / kPage);
 
-  __shared__ __attribute__((aligned(16))) _Float16 s_k[2][kPage * kKStride];  // 34,816 B
-  __shared__ __attribute__((aligned(16))) _Float16 s_v[2][kD * kVStride];     // 36,864 B
+  __shared__ __attribute__((aligned(16))) _Float16 s_k[3][kPage * kKStride];  // 52,224 B
+  __shared__ __attribute__((aligned(16))) _Float16 s_v[3][kD * kVStride];     // 55,296 B
   __shared__ __attribute__((aligned(16))) uint8_t s_raw[kRawSlots][kRawSlot];  // 25,344 B
-  __shared__ __attribute__((aligned(16))) uint16_t s_norm[2][2 * kPage];      // K | V norms
+  __shared__ __attribute__((aligned(16))) uint16_t s_norm[3][2 * kPage];      // K | V norms
   __shared__ int s_pt[kPrefillMaxPages];                                       // 16,384 B
 
   // ---- page ids of the causal range (wave w: a 1/W share of the entries) ----
   for (int i = 0; i < kPrefillMaxPages / (64 * W); ++i) {
     const int e0 = (kPrefillMaxPages / W) * wave + 64 * i;
-    if (e0 < n_pages && e0 + lane < n_pages) pf_dma(btab + e0 + lane, &s_pt[e0], 4);
+    if (e0 < n_pages && e0 + lane < n_pages) pf_dma(btab + e0 + lane, pf_lds_addr(&s_pt[e0]), 4);
   }
 
   // ---- this wave's 16 RB rows: Q' = T q (lane: row 16cb + col, quarter jq) ----
@@ -335,15 +314,7 @@ __global__ __launch_bounds__(64 * pf_waves<RB>(), 1) void prefill_kernel(Prefill
   __builtin_amdgcn_s_waitcnt(0);  // page-id loads landed (all counters)
   __syncthreads();
 
-  // raw loads this wave issues per page
-  const int per_page = (W == 4 ? 2 : 1) + (wave == 0 ? 1 : 0);
-  // first three pages in flight, the first unpacked
-  for (int p = 0; p < 3 && p < n_pages; ++p) pf_issue<W, BITS>(a, s_pt[p], g, wave, lane, s_raw[p]);
-  pf_wait_vm(per_page * (min(n_pages, 3) - 1));
-  pf_unpack<W, BITS>(s_raw[0], wave, lane, s_k[0], s_v[0], s_norm[0], a.lv4);
-  __builtin_amdgcn_s_waitcnt(kPfWaitLgkm0);
-  __builtin_amdgcn_s_barrier();
-
+  const uint32_t raw_base = pf_lds_addr(&s_raw[0][0]);
   float m_run[RB], l_run[RB];
   int rho_e = 0;
   f4 acc[RB][8];
@@ -357,17 +328,10 @@ __global__ __launch_bounds__(64 * pf_waves<RB>(), 1) void prefill_kernel(Prefill
 #pragma unroll
     for (int m = 0; m < 8; ++m) acc[cb][m] = f4{0.f, 0.f, 0.f, 0.f};
 
-  // One page: products from the f16 buffers, online softmax, and the next
-  // page's unpacking.  MASKED pages apply the causal and length masks.
-  auto page_step = [&](int pg, auto masked_tag) {
-    constexpr bool MASKED = decltype(masked_tag)::value;
-    const int f = pg & 1;
-    if (pg + 3 < n_pages) pf_issue<W, BITS>(a, s_pt[pg + 3], g, wave, lane, s_raw[pg % 3]);
-
-    // ---- S^T tiles [token block tb][row block cb]: each K^ fragment feeds
-    // every row block (hi and lo parts of Q') ----
-    const _Float16* sk = s_k[f];
-    f4 s[4][RB];
+  // ---- S^T tiles [token block tb][row block cb] of the page in f16 buffer
+  // `buf`: each K^ fragment feeds every row block (hi and lo parts of Q') ----
+  auto scores = [&](int buf, f4 (&s)[4][RB]) {
+    const _Float16* sk = s_k[buf];
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
 #pragma unroll
@@ -382,119 +346,182 @@ __global__ __launch_bounds__(64 * pf_waves<RB>(), 1) void prefill_kernel(Prefill
         }
       }
     }
-    // ---- unpack the next page into the other buffer while the products run
-    // (independent of them: VALU and LDS work between matrix-core issues) ----
-    if (pg + 1 < n_pages) {
-      // loads of this wave still allowed in flight: those of pages pg+2, pg+3
-      pf_wait_vm(per_page * min(2, n_pages - 2 - pg));
-      pf_unpack<W, BITS>(s_raw[(pg + 1) % 3], wave, lane, s_k[f ^ 1], s_v[f ^ 1], s_norm[f ^ 1], a.lv4);
-    }
-
-    const uint16_t* nrm = s_norm[f];
-    uint32_t vbits = 0;
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-      const u2 vn = *reinterpret_cast<const u2*>(nrm + kPage + 16 * tb + 4 * jq);
-      const us2 h0 = __builtin_bit_cast(us2, (uint32_t)vn[0]), h1 = __builtin_bit_cast(us2, (uint32_t)vn[1]);
-      if (!MASKED) {
-        const us2 m = __builtin_elementwise_max(h0, h1);
-        vbits = max(vbits, (uint32_t)max(m[0], m[1]));
-      } else {
-        // tokens past the end of the chunk carry no norm
-        const int t0 = pg * kPage + 16 * tb + 4 * jq;
-        if (t0 < kv_end) vbits = max(vbits, (uint32_t)h0[0]);
-        if (t0 + 1 < kv_end) vbits = max(vbits, (uint32_t)h0[1]);
-        if (t0 + 2 < kv_end) vbits = max(vbits, (uint32_t)h1[0]);
-        if (t0 + 3 < kv_end) vbits = max(vbits, (uint32_t)h1[1]);
-      }
-    }
-    vbits = umax_xor32(umax_xor16(vbits));
-    const int rho_new = (vbits == 0) ? rho_e : 15 - (int)((vbits >> 10) & 0x1Fu);
-    const int tok_base = pg * kPage + 4 * jq;
-
-    // value norms of the page; on a masked page, slots at or past the end of
-    // the appended chunk were never written and read as zero
-    u2 vnp[4];
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-      vnp[tb] = *reinterpret_cast<const u2*>(nrm + kPage + 16 * tb + 4 * jq);
-      if (MASKED) {
-        const int t0 = tok_base + 16 * tb;
-        vnp[tb][0] &= (t0 < kv_end ? 0xFFFFu : 0u) | (t0 + 1 < kv_end ? 0xFFFF0000u : 0u);
-        vnp[tb][1] &= (t0 + 2 < kv_end ? 0xFFFFu : 0u) | (t0 + 3 < kv_end ? 0xFFFF0000u : 0u);
-      }
-    }
-
-    // ---- online softmax per row (column of S^T) ----
-    // Scores in row units (raw x key norm); the log2-scaled score is that
-    // times the row factor fac[cb] > 0, applied inside the exponent.  The
-    // accumulator and the sum are in units of the value-norm frame 2^rho.
-    h8 pb[2][RB];  // [token pair tp][row block cb]
-#pragma unroll
-    for (int cb = 0; cb < RB; ++cb) {
-      float sv[4][4];
-      float mp = -INFINITY;
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
-        const u2 kn = *reinterpret_cast<const u2*>(nrm + 16 * tb + 4 * jq);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float v = times_norm2(s[tb][cb][r], kn, r);
-          if (MASKED) {
-            const int tok = tok_base + 16 * tb + r;
-            sv[tb][r] = (tok <= qpos[cb] && tok < kv_end) ? v : -INFINITY;
-          } else {
-            sv[tb][r] = v;
-          }
-          mp = fmaxf(mp, sv[tb][r]);
-        }
-      }
-      mp = max_xor32(max_xor16(mp)) * fac[cb];
-      const float m_new = fmaxf(m_run[cb], mp);
-      // a row whose keys on this page are all masked keeps its state
-      const bool live = !MASKED || m_new != -INFINITY;
-      const float corr = live ? fast_exp2(m_run[cb] - m_new) : 1.0f;
-      const float rescale = __builtin_amdgcn_ldexpf(corr, rho_new - rho_e);
-      if (__any(rescale != 1.0f)) {
-#pragma unroll
-        for (int m = 0; m < 8; ++m) acc[cb][m] *= rescale;
-      }
-      l_run[cb] *= rescale;
-      m_run[cb] = m_new;
-      const float m_shift = m_new - (float)rho_new;  // p' = 2^(s - m + rho)
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          // masked scores: 2^-inf = 0
-          const float p = (!MASKED || live) ? fast_exp2(__builtin_fmaf(sv[tb][r], fac[cb], -m_shift)) : 0.f;
-          l_run[cb] += p;
-          pb[tb >> 1][cb][4 * (tb & 1) + r] = (_Float16)times_norm2(p, vnp[tb], r);  // p' vn < 2
-        }
-      }
-    }
-    rho_e = rho_new;
-
-    // ---- O'^T += V^T P~: each V^ fragment feeds both row blocks ----
-    const _Float16* svp = s_v[f];
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-#pragma unroll
-      for (int tp = 0; tp < 2; ++tp) {
-        // k index 8 jq + i: token 32 tp + 4 jq + i (i < 4) or 32 tp + 16 + 4 jq + i - 4
-        const h8 av = *reinterpret_cast<const h8*>(svp + (16 * m + col) * kVStride + 32 * tp + 8 * jq);
-#pragma unroll
-        for (int cb = 0; cb < RB; ++cb)
-          acc[cb][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pb[tp][cb], acc[cb][m], 0, 0, 0);
-      }
-    }
-
-    __builtin_amdgcn_s_waitcnt(kPfWaitLgkm0);
-    __builtin_amdgcn_s_barrier();
   };
-  int pg = 0;
-  for (; pg < n_full; ++pg) page_step(pg, PfMaskTag<false>{});
-  for (; pg < n_pages; ++pg) page_step(pg, PfMaskTag<true>{});
+
+  // Software pipeline over the pages.  Raw page p sits in raw slot p % 3 and
+  // is unpacked into f16 buffer p % 3.  Step pg: request raw page pg + 4,
+  // issue the scores of page pg + 1 (the matrix cores work on them while the
+  // vector ALU runs page pg's softmax), unpack page pg + 2 (while page pg's
+  // P.V products run), one barrier.  Every step issues the same loads -- past
+  // the last page it requests the last page again, and the steps past the
+  // end compute and unpack pages whose results are never used -- so the
+  // steady state holds no branch and every wait is a constant count.
+  const int part = wave & 3;
+  auto run = [&](auto role) {
+    using R = decltype(role);
+    constexpr int per_page = R::loads;
+    const int last = n_pages - 1;
+    auto issue = [&](int p) {
+      pf_issue<BITS, R>(a, s_pt[min(p, last)], g, part, lane, raw_base + (p % 3) * kRawSlot);
+    };
+    auto unpack = [&](int p) {
+      const int u = p % 3;
+      pf_unpack<BITS, R>(s_raw[u], part, lane, s_k[u], s_v[u], s_norm[u], a.lv4);
+    };
+    issue(0);
+    issue(1);
+    issue(2);
+    IQ_PF_WAIT_VM(2 * per_page);
+    unpack(0);
+    IQ_PF_WAIT_VM(per_page);
+    unpack(1);
+    __builtin_amdgcn_s_waitcnt(kPfWaitLgkm0);  // slot 0 read out before it is refilled
+    issue(3);
+    __builtin_amdgcn_s_barrier();
+
+    auto page_step = [&](int pg, f4 (&s)[4][RB], f4 (&s_next)[4][RB], auto masked_tag) {
+      constexpr bool MASKED = decltype(masked_tag)::value;
+      const int f = pg % 3;
+      issue(pg + 4);  // into the slot page pg + 1 left (read out before the last barrier)
+      scores((pg + 1) % 3, s_next);
+
+      const uint16_t* nrm = s_norm[f];
+      uint32_t vbits = 0;
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        const u2 vn = *reinterpret_cast<const u2*>(nrm + kPage + 16 * tb + 4 * jq);
+        const us2 h0 = __builtin_bit_cast(us2, (uint32_t)vn[0]), h1 = __builtin_bit_cast(us2, (uint32_t)vn[1]);
+        if (!MASKED) {
+          const us2 m = __builtin_elementwise_max(h0, h1);
+          vbits = max(vbits, (uint32_t)max(m[0], m[1]));
+        } else {
+          // tokens past the end of the chunk carry no norm
+          const int t0 = pg * kPage + 16 * tb + 4 * jq;
+          if (t0 < kv_end) vbits = max(vbits, (uint32_t)h0[0]);
+          if (t0 + 1 < kv_end) vbits = max(vbits, (uint32_t)h0[1]);
+          if (t0 + 2 < kv_end) vbits = max(vbits, (uint32_t)h1[0]);
+          if (t0 + 3 < kv_end) vbits = max(vbits, (uint32_t)h1[1]);
+        }
+      }
+      vbits = umax_xor32(umax_xor16(vbits));
+      const int rho_new = (vbits == 0) ? rho_e : 15 - (int)((vbits >> 10) & 0x1Fu);
+      const int tok_base = pg * kPage + 4 * jq;
+
+      // value norms of the page; on a masked page, slots at or past the end of
+      // the appended chunk were never written and read as zero
+      u2 vnp[4];
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        vnp[tb] = *reinterpret_cast<const u2*>(nrm + kPage + 16 * tb + 4 * jq);
+        if (MASKED) {
+          const int t0 = tok_base + 16 * tb;
+          vnp[tb][0] &= (t0 < kv_end ? 0xFFFFu : 0u) | (t0 + 1 < kv_end ? 0xFFFF0000u : 0u);
+          vnp[tb][1] &= (t0 + 2 < kv_end ? 0xFFFFu : 0u) | (t0 + 3 < kv_end ? 0xFFFF0000u : 0u);
+        }
+      }
+
+      // ---- online softmax per row (column of S^T) ----
+      // Scores in row units (raw x key norm); the log2-scaled score is that
+      // times the row factor fac[cb] > 0, applied inside the exponent.  The
+      // accumulator and the sum are in units of the value-norm frame 2^rho.
+      h8 pb[2][RB];  // [token pair tp][row block cb]
+#pragma unroll
+      for (int cb = 0; cb < RB; ++cb) {
+        float sv[4][4];
+        float mp = -INFINITY;
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+          const u2 kn = *reinterpret_cast<const u2*>(nrm + 16 * tb + 4 * jq);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float v = times_norm2(s[tb][cb][r], kn, r);
+            if (MASKED) {
+              const int tok = tok_base + 16 * tb + r;
+              sv[tb][r] = (tok <= qpos[cb] && tok < kv_end) ? v : -INFINITY;
+            } else {
+              sv[tb][r] = v;
+            }
+            mp = fmaxf(mp, sv[tb][r]);
+          }
+        }
+        mp = max_xor32(max_xor16(mp)) * fac[cb];
+        const float m_new = fmaxf(m_run[cb], mp);
+        // a row whose keys on this page are all masked keeps its state
+        const bool live = !MASKED || m_new != -INFINITY;
+        const float corr = live ? fast_exp2(m_run[cb] - m_new) : 1.0f;
+        const float rescale = __builtin_amdgcn_ldexpf(corr, rho_new - rho_e);
+        if (__any(rescale != 1.0f)) {
+#pragma unroll
+          for (int m = 0; m < 8; ++m) acc[cb][m] *= rescale;
+        }
+        l_run[cb] *= rescale;
+        m_run[cb] = m_new;
+        const float m_shift = m_new - (float)rho_new;  // p' = 2^(s - m + rho)
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            // masked scores: 2^-inf = 0
+            const float p = (!MASKED || live) ? fast_exp2(__builtin_fmaf(sv[tb][r], fac[cb], -m_shift)) : 0.f;
+            l_run[cb] += p;
+            pb[tb >> 1][cb][4 * (tb & 1) + r] = (_Float16)times_norm2(p, vnp[tb], r);  // p' vn < 2
+          }
+        }
+      }
+      rho_e = rho_new;
+
+      // ---- unpack page pg + 2 into the buffer page pg - 1 used (every wave
+      // has passed the barrier after its last read); loads still allowed in
+      // flight: pages pg + 3 and pg + 4 ----
+      IQ_PF_WAIT_VM(2 * per_page);
+      unpack(pg + 2);
+
+      // ---- O'^T += V^T P~: each V^ fragment feeds both row blocks ----
+      const _Float16* svp = s_v[f];
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+#pragma unroll
+        for (int tp = 0; tp < 2; ++tp) {
+          // k index 8 jq + i: token 32 tp + 4 jq + i (i < 4) or 32 tp + 16 + 4 jq + i - 4
+          const h8 av = *reinterpret_cast<const h8*>(svp + (16 * m + col) * kVStride + 32 * tp + 8 * jq);
+#pragma unroll
+          for (int cb = 0; cb < RB; ++cb)
+            acc[cb][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pb[tp][cb], acc[cb][m], 0, 0, 0);
+        }
+      }
+
+      __builtin_amdgcn_s_waitcnt(kPfWaitLgkm0);
+      __builtin_amdgcn_s_barrier();
+    };
+
+    f4 s_cur[4][RB], s_nxt[4][RB];
+    scores(0, s_cur);
+    int pg = 0;
+    for (; pg < n_full; ++pg) {
+      page_step(pg, s_cur, s_nxt, PfTag<false>{});
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+        for (int cb = 0; cb < RB; ++cb) s_cur[tb][cb] = s_nxt[tb][cb];
+    }
+    for (; pg < n_pages; ++pg) {
+      page_step(pg, s_cur, s_nxt, PfTag<true>{});
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+        for (int cb = 0; cb < RB; ++cb) s_cur[tb][cb] = s_nxt[tb][cb];
+    }
+    // the last requests (repeats of the last page) land before the kernel ends
+    IQ_PF_WAIT_VM(0);
+  };
+  if (W == 4) {
+    if (wave == 0) run(PfRole<true, true, true>{});
+    else run(PfRole<true, true, false>{});
+  } else {
+    if (wave == 0) run(PfRole<true, false, true>{});
+    else if (wave < 4) run(PfRole<true, false, false>{});
+    else run(PfRole<false, true, false>{});
+  }
 
   // ---- epilogue: normalise, rotate back (B^T then H / sqrt(d)), store ----
   const float* rot = a.rot + (size_t)g * kRotFloats;
