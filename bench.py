@@ -460,7 +460,27 @@ def run_four_bit_aux(w, lens, bt_np, num_pages, t_decode3, t_step3, ring_bytes=1
             "time_vs_3bit_step": round(t_step / t_step3, 3)}
 
 
-def run_prefill_aux(iters=30, bits=3):
+def median_call_seconds(fn, calls=10, reps=5, warm=20):
+    """Seconds per call of fn: `warm` untimed calls (until the GPU's clocks
+    have settled under this load), then `reps` event-timed runs of `calls`
+    calls each on the current stream; the median run."""
+    import torch
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    runs = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(calls):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        runs.append(a.elapsed_time(b) / 1e3 / calls)
+    return sorted(runs)[len(runs) // 2]
+
+
+def run_prefill_aux(bits=3):
     """The chunked-prefill workload (8192-token quantise-append into a 32,768-token
     cache, then causal attention of the last 512 positions x 64 query heads):
     append tokens/s and prefill TFLOP/s against the f16 matrix-core peak, on a
@@ -489,21 +509,9 @@ def run_prefill_aux(iters=30, bits=3):
     ws_n = iq.prefill_workspace_bytes(p.n_queries, p.n_q_heads, p.n_kv_heads, p.q_start)
     ws = torch.empty(max(16, ws_n), dtype=torch.uint8, device=dev)
 
-    def timeit(fn):
-        for _ in range(3):
-            fn()
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        for _ in range(iters):
-            fn()
-        b.record()
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / 1e3 / iters
-
-    t_app = timeit(lambda: iq.quantize_append(cache, rot, k2, v2, s2, p2, bt))
-    t_pre = timeit(lambda: iq.prefill_attention(cache, rot, q, p.q_start, bt[0], out=out,
-                                                 workspace=ws))
+    t_app = median_call_seconds(lambda: iq.quantize_append(cache, rot, k2, v2, s2, p2, bt), calls=30)
+    t_pre = median_call_seconds(lambda: iq.prefill_attention(cache, rot, q, p.q_start, bt[0], out=out,
+                                                             workspace=ws))
     # algorithmic flops: 2 d for q.k and 2 d for p.v per (query head, key) pair
     keys = sum(p.q_start + i + 1 for i in range(p.n_queries))
     flops = 4.0 * 128 * p.n_q_heads * keys
@@ -523,7 +531,7 @@ def run_prefill_aux(iters=30, bits=3):
     }
 
 
-def run_dense_prefill_aux(fmt="bf16", iters=30):
+def run_dense_prefill_aux(fmt="bf16"):
     """The chunked-prefill workload's attention over an uncompressed (bf16 or
     FP8, unit scales) cache of the same 32,768 tokens: the baseline of the
     packed prefill call."""
@@ -544,16 +552,7 @@ def run_dense_prefill_aux(fmt="bf16", iters=30):
     iq.dense_append(cache, k, v, torch.zeros_like(pos), pos, bt)
     q = synth.draw_normal_device(p.seed + 10, (p.n_queries, p.n_q_heads, 128), torch.bfloat16, dev)
     out = torch.empty((p.n_queries, p.n_q_heads, 128), dtype=torch.float32, device=dev)
-    for _ in range(3):
-        iq.dense_prefill_attention(cache, q, p.q_start, bt[0], out=out)
-    torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    for _ in range(iters):
-        iq.dense_prefill_attention(cache, q, p.q_start, bt[0], out=out)
-    b.record()
-    torch.cuda.synchronize()
-    t = a.elapsed_time(b) / 1e3 / iters
+    t = median_call_seconds(lambda: iq.dense_prefill_attention(cache, q, p.q_start, bt[0], out=out))
     keys = sum(p.q_start + i + 1 for i in range(p.n_queries))
     tf = 4.0 * 128 * p.n_q_heads * keys / t / 1e12
     del cache
@@ -637,11 +636,11 @@ def write_traffic_record(root: str, workload: str = "gqa_decode_32k_32q4kv", cal
             raise SystemExit(f"expected one kernel, found {len(hits)}")
         return hits[0]
 
-    def split(k):  # decode_split_kernel<PACK8, waves, APPEND = false, record bits = 3>
+    def split(k):  # decode_split_kernel<PACK8, waves, APPEND = false, record bits = 3, BALANCED>
         if "decode_split_kernel<" not in k or "dense" in k:
             return False
         targs = [a.strip() for a in k.split("<")[1].split(">")[0].split(",")]
-        return len(targs) == 4 and targs[2] == "false" and targs[3] == "3"
+        return len(targs) == 5 and targs[2] == "false" and targs[3] == "3"
 
     merge = lambda k: "decode_merge_kernel<true>" in k
     copy = lambda k: "copy" in k.lower()
