@@ -40,16 +40,26 @@
 namespace iq {
 
 constexpr int kRowsPerTile = 128;  // rows = queries x group heads
-constexpr int kKStride = 136;   // halves per K^ row (128 + 8 pad)
-// halves per V^T row (64 + 8 pad: rows start 16-byte aligned and the 16 rows of
-// one fragment read cover the 64 banks once).  Within a row the tokens of each
-// 32-token half are in the matrix-core k order (see vt_col), so a lane's eight
-// P.V operands are one 16-byte read.
-constexpr int kVStride = 72;
-// column of token t (0..63) in a V^T row: half tp = t / 32 holds, for lane
-// group jq, tokens 4 jq .. +3 then 16 + 4 jq .. +3 at columns 32 tp + 8 jq ..
+// The unpacked f16 tiles are stored chunk-major: 16-byte chunk c of every row
+// forms a contiguous plane, so the 16 lanes of a matrix-core fragment read
+// (16 consecutive rows, one chunk) read 256 contiguous bytes, which the LDS
+// serves without bank conflicts (a padded row-major tile is served 2-way
+// conflicted on this GPU).
+//   K^:  plane c (coordinates 8c .. 8c+7) of the 64 tokens: byte 1024 c + 16 tok
+//   V^T: plane c (token columns 8c .. 8c+7) of the 128 coordinate rows:
+//        byte 2048 c + 16 row
+constexpr int kKTileBytes = 16 * kPage * 16;  // 16 planes x 64 tokens x 16 B
+constexpr int kVTileBytes = 8 * kD * 16;      // 8 planes x 128 rows x 16 B
+// Within a V^T row the tokens of each 32-token half are in the matrix-core k
+// order: column of token t (0..63): half tp = t / 32 holds, for lane group jq,
+// tokens 4 jq .. +3 then 16 + 4 jq .. +3 at columns 32 tp + 8 jq ..
 __host__ __device__ constexpr int vt_col(int t) {
   return 32 * (t >> 5) + 8 * ((t & 15) >> 2) + 4 * ((t & 31) >> 4) + (t & 3);
+}
+// byte offset of the 4-column (8-byte) run starting at column col (a multiple
+// of 4) of V^T row `row`
+__host__ __device__ constexpr int vt_at(int row, int col) {
+  return 2048 * (col >> 3) + 16 * row + 2 * (col & 7);
 }
 constexpr int kRawPage = 8192;  // raw code bytes of a page in LDS: 512 groups of 12 B at a 16 B stride
 constexpr int kRawSlot = kRawPage + 256;  // + the page's K and V norms
@@ -132,11 +142,15 @@ struct PfRole {
 
 // Raw loads of one page into a slot (each wave loads exactly the groups it
 // unpacks).  Part p of a raw slot: K bytes at 2048 p, V bytes at 2048 p + 1024
-// (64 lanes x 16 bytes each).  3-bit: the K quarter is the records of tokens
-// 16p..16p+15 (lane l: token 16p + l/4, group l%4 -- 768 contiguous bytes),
-// the V quarter chunk p of every V region (lane l: region l).  4-bit: bytes
-// 1024p.. of the 4,096-byte K and V blocks.  NORMS: the K norms (lanes 0-31)
-// and V norms (lanes 32-63).
+// (64 lanes x 16 bytes each, lane l at 16 l).  The lanes are assigned so that
+// the unpacked writes of 16 (or 32) consecutive lanes are contiguous:
+//   3-bit K quarter p: lane l = group l / 16 (coordinates 32 (l / 16) ..) of
+//     token 16 p + l % 16;
+//   3-bit V quarter p: lane l = chunk 2 (l / 32) + (l / 16) % 2 of V region
+//     16 p + l % 16;
+//   4-bit K quarter p: lane l = quarter l / 16 (16 bytes) of token 16 p + l % 16;
+//   4-bit V quarter p: lane l = dwords 4 (l / 16) .. + 3 of V region 16 p + l % 16.
+// NORMS: the K norms (lanes 0-31) and V norms (lanes 32-63).
 template <int BITS, class R>
 __device__ __forceinline__ void pf_issue(const PrefillArgs& a, int page_id, int g, int part, int lane,
                                          uint32_t slot) {
@@ -145,13 +159,16 @@ __device__ __forceinline__ void pf_issue(const PrefillArgs& a, int page_id, int 
   const uint32_t page = min((uint32_t)page_id, (uint32_t)a.num_pages - 1u);
   const size_t base = ((size_t)page * a.hkv + g) * kPage;
   const uint32_t dst = slot + 2048 * part;
+  const int row = 16 * part + (lane & 15);  // token (K) or V region of this lane
   if (BITS == 4) {
-    const size_t blk = base * kRec4;
-    if (R::k) pf_dma(a.k_codes + blk + 1024 * part + 16 * lane, dst, 16);
-    if (R::v) pf_dma(a.v_codes + blk + 1024 * part + 16 * lane, dst + 1024, 16);
+    if (R::k) pf_dma(a.k_codes + (base + row) * kRec4 + 16 * (lane >> 4), dst, 16);
+    if (R::v) pf_dma(a.v_codes + base * kRec4 + row * 64 + 16 * (lane >> 4), dst + 1024, 16);
   } else {
-    if (R::k) pf_dma(a.k_codes + base * kRec + 768 * part + 12 * lane, dst, 12);
-    if (R::v) pf_dma(a.v_codes + (base + lane) * kRec + 12 * part, dst + 1024, 12);
+    if (R::k) pf_dma(a.k_codes + (base + row) * kRec + 12 * (lane >> 4), dst, 12);
+    if (R::v) {
+      const int c = 2 * (lane >> 5) + ((lane >> 4) & 1);
+      pf_dma(a.v_codes + (base + row) * kRec + 12 * c, dst + 1024, 12);
+    }
   }
   if (R::norms) {
     const uint16_t* nb = (lane < 32 ? a.k_norms : a.v_norms) + base + 2 * (lane & 31);
@@ -159,70 +176,70 @@ __device__ __forceinline__ void pf_issue(const PrefillArgs& a, int page_id, int 
   }
 }
 
-// One K group (token tok, coordinates 32j..32j+31) into the f16 K^ buffer.
-__device__ __forceinline__ void pf_unpack_k(const u3& ck, int tok, int j, _Float16* sk) {
+// One K group (token tok, coordinates 32j..32j+31 = planes 4j .. 4j+3) into
+// the f16 K^ tile.
+__device__ __forceinline__ void pf_unpack_k(const u3& ck, int tok, int j, uint8_t* sk) {
   uint32_t z[8];
   group_to_selectors(ck.x, ck.y, ck.z, z);
-  u4* dst = reinterpret_cast<u4*>(sk + tok * kKStride + 32 * j);
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
     const u2 d0 = selector_to_f16(z[2 * kk]), d1 = selector_to_f16(z[2 * kk + 1]);
-    dst[kk] = u4{d0[0], d0[1], d1[0], d1[1]};
+    *reinterpret_cast<u4*>(sk + 1024 * (4 * j + kk) + 16 * tok) = u4{d0[0], d0[1], d1[0], d1[1]};
   }
 }
 // Chunk c of V region `region` = (n, q) = (region % 16, region / 16): tokens
-// 16c + 4q + r, selector m, into row 16m + n of the f16 V^T buffer (row 16m + n
+// 16c + 4q + r, selector m, into row 16m + n of the f16 V^T tile (row 16m + n
 // holds coordinate 32 (n / 4) + 4m + n % 4: accumulator order).
-__device__ __forceinline__ void pf_unpack_v(const u3& cv, int region, int c, _Float16* sv) {
+__device__ __forceinline__ void pf_unpack_v(const u3& cv, int region, int c, uint8_t* sv) {
   uint32_t z[8];
   group_to_selectors(cv.x, cv.y, cv.z, z);
   const int n = region & 15, q = region >> 4;
   const int col = vt_col(16 * c + 4 * q);  // the four tokens stay adjacent
 #pragma unroll
-  for (int m = 0; m < 8; ++m)
-    *reinterpret_cast<u2*>(sv + (16 * m + n) * kVStride + col) = selector_to_f16(z[m]);
+  for (int m = 0; m < 8; ++m) *reinterpret_cast<u2*>(sv + vt_at(16 * m + n, col)) = selector_to_f16(z[m]);
 }
 
 // 4-bit: quarter j of token tok's record (dword kk = coordinates 32j + 8kk
-// .. + 7) into the f16 K^ buffer.
-__device__ __forceinline__ void pf_unpack_k4(const u4& ck, int tok, int j, _Float16* sk,
+// .. + 7) into the f16 K^ tile.
+__device__ __forceinline__ void pf_unpack_k4(const u4& ck, int tok, int j, uint8_t* sk,
                                              const Levels4& lv) {
-  u4* dst = reinterpret_cast<u4*>(sk + tok * kKStride + 32 * j);
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) dst[kk] = __builtin_bit_cast(u4, dword4_to_h8(ck[kk], lv));
+  for (int kk = 0; kk < 4; ++kk)
+    *reinterpret_cast<u4*>(sk + 1024 * (4 * j + kk) + 16 * tok) = __builtin_bit_cast(u4, dword4_to_h8(ck[kk], lv));
 }
 // 4-bit: dwords 4p .. 4p+3 of V region `region` = n + 16 jq: dword (th, q)
 // holds tokens 32 th + 16 q + 4 jq + r of coordinate 32 (n / 4) + 4p + n % 4
-// (low nibbles) and that + 16 (high nibbles).  The V^T buffer is in
+// (low nibbles) and that + 16 (high nibbles).  The V^T tile is in
 // accumulator order, as for 3-bit pages: row 16m + n holds coordinate
 // 32 (n / 4) + 4m + n % 4, so the low nibbles go to row 16p + n and the high
-// ones to row 16 (p + 4) + n.
-__device__ __forceinline__ void pf_unpack_v4(const u4& cv, int region, int p, _Float16* sv,
+// ones to row 16 (p + 4) + n.  Lanes of odd p take the dwords in the order
+// 1 0 3 2, so that at every store the 32 lanes of a half-wave fill whole
+// 16-byte chunks.
+__device__ __forceinline__ void pf_unpack_v4(const u4& cv, int region, int p, uint8_t* sv,
                                              const Levels4& lv) {
   const int n = region & 15, jq = region >> 4;
 #pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    const int col = vt_col(32 * (d >> 1) + 16 * (d & 1) + 4 * jq);
-    const uint32_t w = cv[d];
-    *reinterpret_cast<u2*>(sv + (16 * p + n) * kVStride + col) = nibbles_to_f16(w & 0x0F0F0F0Fu, lv);
-    *reinterpret_cast<u2*>(sv + (16 * (p + 4) + n) * kVStride + col) =
-        nibbles_to_f16((w >> 4) & 0x0F0F0F0Fu, lv);
+  for (int i = 0; i < 4; ++i) {
+    const int d = i ^ (p & 1);
+    const int col = 32 * (d >> 1) + 8 * jq + 4 * (d & 1);  // vt_col(32 (d/2) + 16 (d%2) + 4 jq)
+    const uint32_t w = (p & 1) ? cv[i ^ 1] : cv[i];
+    *reinterpret_cast<u2*>(sv + vt_at(16 * p + n, col)) = nibbles_to_f16(w & 0x0F0F0F0Fu, lv);
+    *reinterpret_cast<u2*>(sv + vt_at(16 * (p + 4) + n, col)) = nibbles_to_f16((w >> 4) & 0x0F0F0F0Fu, lv);
   }
 }
 
-// Unpack this wave's part of a raw page into the f16 buffers.
+// Unpack this wave's part of a raw page into the f16 tiles.
 template <int BITS, class R>
-__device__ __forceinline__ void pf_unpack(const uint8_t* slot, int part, int lane, _Float16* sk,
-                                          _Float16* sv, uint16_t* snorm, const Levels4& lv) {
+__device__ __forceinline__ void pf_unpack(const uint8_t* slot, int part, int lane, uint8_t* sk,
+                                          uint8_t* sv, uint16_t* snorm, const Levels4& lv) {
   const uint8_t* raw = slot + 2048 * part + 16 * lane;
+  const int row = 16 * part + (lane & 15);
   if (BITS == 4) {
-    // 16-byte unit u of a block: K token u / 4, quarter u % 4; V region u / 4, dwords 4(u % 4)..
-    const int u = 64 * part + lane;
-    if (R::k) pf_unpack_k4(*reinterpret_cast<const u4*>(raw), u >> 2, u & 3, sk, lv);
-    if (R::v) pf_unpack_v4(*reinterpret_cast<const u4*>(raw + 1024), u >> 2, u & 3, sv, lv);
+    if (R::k) pf_unpack_k4(*reinterpret_cast<const u4*>(raw), row, lane >> 4, sk, lv);
+    if (R::v) pf_unpack_v4(*reinterpret_cast<const u4*>(raw + 1024), row, lane >> 4, sv, lv);
   } else {
-    if (R::k) pf_unpack_k(*reinterpret_cast<const u3*>(raw), 16 * part + (lane >> 2), lane & 3, sk);
-    if (R::v) pf_unpack_v(*reinterpret_cast<const u3*>(raw + 1024), lane, part, sv);
+    if (R::k) pf_unpack_k(*reinterpret_cast<const u3*>(raw), row, lane >> 4, sk);
+    if (R::v) pf_unpack_v(*reinterpret_cast<const u3*>(raw + 1024), row, 2 * (lane >> 5) + ((lane >> 4) & 1), sv);
   }
   if (R::norms)
     reinterpret_cast<uint32_t*>(snorm)[lane] = reinterpret_cast<const uint32_t*>(slot + kRawPage)[lane];
@@ -255,8 +272,8 @@ __global__ __launch_bounds__(64 * pf_waves<RB>(), 1) void prefill_kernel(Prefill
   // pages entirely at or before the smallest query position need no mask
   const int n_full = min(n_pages, (q_start + q0 + 1) / kPage);
 
-  __shared__ __attribute__((aligned(16))) _Float16 s_k[3][kPage * kKStride];  // 52,224 B
-  __shared__ __attribute__((aligned(16))) _Float16 s_v[3][kD * kVStride];     // 55,296 B
+  __shared__ __attribute__((aligned(16))) uint8_t s_k[3][kKTileBytes];  // 49,152 B
+  __shared__ __attribute__((aligned(16))) uint8_t s_v[3][kVTileBytes];  // 49,152 B
   __shared__ __attribute__((aligned(16))) uint8_t s_raw[kRawSlots][kRawSlot];  // 25,344 B
   __shared__ __attribute__((aligned(16))) uint16_t s_norm[3][2 * kPage];      // K | V norms
   __shared__ int s_pt[kPrefillMaxPages];                                       // 16,384 B
@@ -331,14 +348,14 @@ __global__ __launch_bounds__(64 * pf_waves<RB>(), 1) void prefill_kernel(Prefill
   // ---- S^T tiles [token block tb][row block cb] of the page in f16 buffer
   // `buf`: each K^ fragment feeds every row block (hi and lo parts of Q') ----
   auto scores = [&](int buf, f4 (&s)[4][RB]) {
-    const _Float16* sk = s_k[buf];
+    const uint8_t* sk = s_k[buf];
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
 #pragma unroll
       for (int cb = 0; cb < RB; ++cb) s[tb][cb] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        const h8 av = *reinterpret_cast<const h8*>(sk + (16 * tb + col) * kKStride + 32 * jq + 8 * kk);
+        const h8 av = *reinterpret_cast<const h8*>(sk + 1024 * (4 * jq + kk) + 16 * (16 * tb + col));
 #pragma unroll
         for (int cb = 0; cb < RB; ++cb) {
           s[tb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, qhi[cb][kk], s[tb][cb], 0, 0, 0);
@@ -477,13 +494,13 @@ __global__ __launch_bounds__(64 * pf_waves<RB>(), 1) void prefill_kernel(Prefill
       unpack(pg + 2);
 
       // ---- O'^T += V^T P~: each V^ fragment feeds both row blocks ----
-      const _Float16* svp = s_v[f];
+      const uint8_t* svp = s_v[f];
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
 #pragma unroll
         for (int tp = 0; tp < 2; ++tp) {
           // k index 8 jq + i: token 32 tp + 4 jq + i (i < 4) or 32 tp + 16 + 4 jq + i - 4
-          const h8 av = *reinterpret_cast<const h8*>(svp + (16 * m + col) * kVStride + 32 * tp + 8 * jq);
+          const h8 av = *reinterpret_cast<const h8*>(svp + 2048 * (4 * tp + jq) + 16 * (16 * m + col));
 #pragma unroll
           for (int cb = 0; cb < RB; ++cb)
             acc[cb][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pb[tp][cb], acc[cb][m], 0, 0, 0);
