@@ -22,9 +22,11 @@
 //     so no wave waits for another's loads);
 //   * unpacked pages -- K^ token-major, V^ as [coordinate][token], both
 //     alpha-scaled f16, and the fp16 norms -- sit in a ring of three LDS
-//     buffers: while page p's softmax and P.V products run, page p + 1's
-//     scores are already on the matrix cores (in a second register set) and
-//     page p + 2 is being unpacked;
+//     buffers, stored chunk-major (see below): while page p's softmax and
+//     P.V products run, page p + 1's scores are computed (into a second
+//     register set) and page p + 2 is unpacked; the two waves of a SIMD take
+//     these in opposite orders, so one's matrix-core products overlap the
+//     other's vector work;
 //   * only pages that reach past the smallest query position of the tile are
 //     masked.
 // The page ids of the whole causal range are staged in LDS once.
@@ -134,9 +136,15 @@ __device__ __forceinline__ float times_norm2(float x, const u2& n, int r) {
 // page's norms.  Four waves carry both quarters of their part; eight waves
 // split them, waves 0-3 the K quarters and waves 4-7 the V quarters, so that
 // every unpack runs on all 64 lanes.
-template <bool DO_K, bool DO_V, bool NORMS>
+// PRODUCTS_FIRST: the order of a page step.  true: the next page's scores,
+// this page's softmax, the unpack of the page after next, this page's P.V
+// products; false: softmax, scores, P.V, unpack.  Waves w and w + 4 share a
+// SIMD; the K waves (0-3) take the first order and the V waves (4-7) the
+// second, so that between two barriers one wave's matrix-core products run
+// while the other does vector work.
+template <bool DO_K, bool DO_V, bool NORMS, bool PRODUCTS_FIRST = true>
 struct PfRole {
-  static constexpr bool k = DO_K, v = DO_V, norms = NORMS;
+  static constexpr bool k = DO_K, v = DO_V, norms = NORMS, products_first = PRODUCTS_FIRST;
   static constexpr int loads = (DO_K ? 1 : 0) + (DO_V ? 1 : 0) + (NORMS ? 1 : 0);  // per page
 };
 
@@ -366,13 +374,14 @@ __global__ __launch_bounds__(64 * pf_waves<RB>(), 1) void prefill_kernel(Prefill
   };
 
   // Software pipeline over the pages.  Raw page p sits in raw slot p % 3 and
-  // is unpacked into f16 buffer p % 3.  Step pg: request raw page pg + 4,
-  // issue the scores of page pg + 1 (the matrix cores work on them while the
-  // vector ALU runs page pg's softmax), unpack page pg + 2 (while page pg's
-  // P.V products run), one barrier.  Every step issues the same loads -- past
-  // the last page it requests the last page again, and the steps past the
-  // end compute and unpack pages whose results are never used -- so the
-  // steady state holds no branch and every wait is a constant count.
+  // is unpacked into f16 buffer p % 3.  Step pg: request raw page pg + 4;
+  // compute the scores of page pg + 1, page pg's softmax and P.V products,
+  // and unpack page pg + 2, in the order of the wave's role (independent
+  // work, so the matrix cores and the vector ALU of a SIMD both stay busy);
+  // one barrier.  Every step issues the same loads -- past the last page it
+  // requests the last page again, and the steps past the end compute and
+  // unpack pages whose results are never used -- so the steady state holds
+  // no branch and every wait is a constant count.
   const int part = wave & 3;
   auto run = [&](auto role) {
     using R = decltype(role);
@@ -400,7 +409,7 @@ __global__ __launch_bounds__(64 * pf_waves<RB>(), 1) void prefill_kernel(Prefill
       constexpr bool MASKED = decltype(masked_tag)::value;
       const int f = pg % 3;
       issue(pg + 4);  // into the slot page pg + 1 left (read out before the last barrier)
-      scores((pg + 1) % 3, s_next);
+      if (R::products_first) scores((pg + 1) % 3, s_next);
 
       const uint16_t* nrm = s_norm[f];
       uint32_t vbits = 0;
@@ -486,12 +495,15 @@ __global__ __launch_bounds__(64 * pf_waves<RB>(), 1) void prefill_kernel(Prefill
         }
       }
       rho_e = rho_new;
+      if (!R::products_first) scores((pg + 1) % 3, s_next);
 
       // ---- unpack page pg + 2 into the buffer page pg - 1 used (every wave
       // has passed the barrier after its last read); loads still allowed in
       // flight: pages pg + 3 and pg + 4 ----
-      IQ_PF_WAIT_VM(2 * per_page);
-      unpack(pg + 2);
+      if (R::products_first) {
+        IQ_PF_WAIT_VM(2 * per_page);
+        unpack(pg + 2);
+      }
 
       // ---- O'^T += V^T P~: each V^ fragment feeds both row blocks ----
       const uint8_t* svp = s_v[f];
@@ -505,6 +517,10 @@ __global__ __launch_bounds__(64 * pf_waves<RB>(), 1) void prefill_kernel(Prefill
           for (int cb = 0; cb < RB; ++cb)
             acc[cb][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pb[tp][cb], acc[cb][m], 0, 0, 0);
         }
+      }
+      if (!R::products_first) {
+        IQ_PF_WAIT_VM(2 * per_page);
+        unpack(pg + 2);
       }
 
       __builtin_amdgcn_s_waitcnt(kPfWaitLgkm0);
@@ -537,7 +553,7 @@ __global__ __launch_bounds__(64 * pf_waves<RB>(), 1) void prefill_kernel(Prefill
   } else {
     if (wave == 0) run(PfRole<true, false, true>{});
     else if (wave < 4) run(PfRole<true, false, false>{});
-    else run(PfRole<false, true, false>{});
+    else run(PfRole<false, true, false, false>{});
   }
 
   // ---- epilogue: normalise, rotate back (B^T then H / sqrt(d)), store ----
