@@ -178,6 +178,9 @@ PREFILL4_CASES = [
     (700, 77, 2, 8, 4),
     (640, 1, 2, 4, None),
     (200, 70, 1, 128, 4),
+    # causal ranges of one to three pages (pipeline start and end)
+    (130, 130, 1, 2, None),
+    (10, 10, 2, 8, 4),
 ]
 
 

@@ -236,6 +236,11 @@ PREFILL_CASES = [
     (1024, 128, 1, 32),
     (640, 1, 2, 4),
     (200, 70, 1, 128),
+    # causal ranges of one to three pages: the page pipeline's start and its
+    # steps past the last page
+    (64, 64, 1, 1),
+    (130, 130, 1, 2),
+    (10, 10, 2, 8),
 ]
 
 
