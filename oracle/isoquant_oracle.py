@@ -201,7 +201,8 @@ def fp16_midpoint_near(n, rel_eps: float = NEAR_EPS) -> np.ndarray:
 
 
 # ----------------------------------------------------------------------------
-# Quantiser (north-star spec of [RQ]'s "3-bit scalar quantization"):
+# Quantiser.  [RQ] (abstract) names a 3-bit scalar quantisation after the
+# rotation and leaves its details open; they are fixed here as:
 #   n = ||x||_2 of the unrotated input (fp64),
 #   u = (T x) * sqrt(d) / n,
 #   code_i = #{ j : float32(u_i) >= THRESHOLDS_F32[j] }  (ties go up; R7),
