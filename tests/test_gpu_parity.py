@@ -106,6 +106,8 @@ DECODE_CASES = [
     ([1, 63, 64, 65, 700], 2, 4, "bf16", True),
     ([130, 1000, 2100], 4, 32, "bf16", True),
     ([640, 33], 2, 32, "f16", False),
+    # one sequence at the prefill staging limit (4,096 pages, 16 per split)
+    ([262144], 1, 8, "bf16", True),
 ]
 
 
@@ -241,6 +243,8 @@ PREFILL_CASES = [
     (64, 64, 1, 1),
     (130, 130, 1, 2),
     (10, 10, 2, 8),
+    # the largest causal range one call stages: 4,096 pages
+    (262144, 16, 1, 8),
 ]
 
 
