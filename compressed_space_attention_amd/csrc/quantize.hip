@@ -86,14 +86,21 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(
   wht128_quad(x, j);
   // SO(4) block by block (blocks 8j .. 8j + 7 of the quarter), each block's
   // four outputs turned into codes at once: sel[bb] holds the codes (3-bit)
-  // or nibbles (4-bit) of coordinates 32j + 4bb .. + 3, one per byte.  (The
-  // zero vector: every code 4, resp. nibble 0 = code 8.)
+  // or nibbles (4-bit) of coordinates 32j + 4bb .. + 3, one per byte.  The
+  // zero vector is coded through inv_n = 0: every u is then +-0, which codes
+  // as 4 (resp. nibble 0 = code 8), so no coordinate needs a branch.  The
+  // empty asm makes each block's rotation rows (LDS) depend on the previous
+  // block's codes: otherwise the compiler reads all 32 rows up front and holds
+  // 128 of them in registers (204 VGPRs instead of 62, a third of the waves).
   uint32_t sel[8];
   {
     const float inv_n = n > 0.f ? 1.0f / n : 0.f;
+    uint32_t prev = 0;
 #pragma unroll
     for (int bb = 0; bb < 8; ++bb) {
-      const f4* m = reinterpret_cast<const f4*>(s_rot + (8 * j + bb) * 16);
+      int off = (8 * j + bb) * 16;
+      asm volatile("" : "+v"(off) : "v"(prev));
+      const f4* m = reinterpret_cast<const f4*>(s_rot + off);
       uint32_t w = 0;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -101,11 +108,12 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(
         const float zr = row[0] * x[4 * bb] + row[1] * x[4 * bb + 1] + row[2] * x[4 * bb + 2] +
                          row[3] * x[4 * bb + 3];
         uint32_t c;
-        if constexpr (BITS == 3) c = n > 0.f ? code_of(zr * inv_n) : 4u;
-        else c = n > 0.f ? nibble_of(zr * inv_n, lv) : 0u;
+        if constexpr (BITS == 3) c = code_of(zr * inv_n);
+        else c = nibble_of(zr * inv_n, lv);
         w |= c << (8 * r);
       }
       sel[bb] = w;
+      prev = w;
     }
   }
 
