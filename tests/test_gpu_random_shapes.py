@@ -1,0 +1,81 @@
+"""Seeded random shapes through the C ABI against the oracle.
+
+The named cases pin chosen shapes; these draw their combinations from a seed
+instead: batch 1-5, sequence lengths 1-3,000, kv heads 1/2/4, query groups
+1-16 (decode; powers of two for prefill), fp32/bf16/f16 inputs, outlier key
+channels or not, 3- and 4-bit records.  Codes are compared with the oracle's
+quantiser (bit for bit outside the near-boundary exemption) and attention rows
+within the same relative tolerance as the fixed cases.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from compressed_space_attention_amd import synth
+from oracle import isoquant4_oracle as O4
+from oracle import isoquant_oracle as O
+from tests.gpu_cases import Scenario, code_parity, code_parity4, max_row_error, tol
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _draw(seed, prefill):
+    rng = np.random.default_rng(seed)
+    batch = 1 if prefill else int(rng.integers(1, 6))
+    lens = [int(x) for x in rng.integers(1, 3001, size=batch)]
+    hkv = int(rng.choice([1, 2, 4]))
+    group = int(rng.choice([1, 2, 4, 8, 16] if prefill else [1, 2, 3, 4, 6, 8, 12, 16]))
+    dtype = "bf16" if prefill else str(rng.choice(["f32", "bf16", "f16"]))
+    outliers = bool(rng.integers(0, 2))
+    bits = int(rng.choice([3, 4]))
+    return lens, hkv, group, dtype, outliers, bits
+
+
+def _codes(s):
+    ref, info = s.oracle_cache()
+    check = code_parity4 if s.bits == 4 else code_parity
+    return check(s.host_cache(), ref, info, s)
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_decode_random_shape(seed):
+    lens, hkv, group, dtype, outliers, bits = _draw(7000 + seed, prefill=False)
+    _say(f"decode random seed={seed} lens={lens} hkv={hkv} group={group} dtype={dtype} "
+         f"outliers={outliers} bits={bits}")
+    s = Scenario(7100 + seed, lens, hkv=hkv, dtype=dtype, outliers=outliers, bits=bits)
+    _say("  codes", _codes(s))
+    q = s.queries(7200 + seed, len(lens), hkv * group)
+    out = s.iq.decode_attention(s.cache, s.rot, q.cuda(), s.bt_dev, s.lens_dev, max(lens)).cpu().numpy()
+    ref = s.oracle_decode(s.host_cache(), q.double().numpy())
+    err = max_row_error(out, ref)
+    _say(f"  max row error {err:.3e}")
+    assert np.all(np.isfinite(out))
+    assert err <= tol()
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_prefill_random_shape(seed):
+    lens, hkv, group, dtype, outliers, bits = _draw(7300 + seed, prefill=True)
+    total = lens[0]
+    n_q = int(np.random.default_rng(7400 + seed).integers(1, min(total, 300) + 1))
+    _say(f"prefill random seed={seed} total={total} n_q={n_q} hkv={hkv} group={group} "
+         f"outliers={outliers} bits={bits}")
+    s = Scenario(7500 + seed, lens, hkv=hkv, dtype=dtype, outliers=outliers, bits=bits)
+    q = synth.to_dtype(synth.normal(7600 + seed, (n_q, hkv * group, 128)), "bf16")
+    q_start = total - n_q
+    out = s.iq.prefill_attention(s.cache, s.rot, q.cuda(), q_start, s.bt_dev[0]).cpu().numpy()
+    rows = np.unique(np.linspace(0, n_q - 1, min(n_q, 16)).astype(int))
+    fn = O4.prefill_attention4 if bits == 4 else O.prefill_attention
+    ref = fn(s.host_cache(), s.blocks, q.double().numpy(), q_start, s.block_table[0], rows=rows)
+    err = max_row_error(out[rows], ref)
+    _say(f"  max row error {err:.3e}")
+    assert np.all(np.isfinite(out))
+    assert err <= tol()
