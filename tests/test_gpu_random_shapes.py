@@ -3,10 +3,14 @@
 The named cases pin chosen shapes; these draw their combinations from a seed
 instead: batch 1-5, sequence lengths 1-3,000, kv heads 1/2/4, query groups
 1-16 (decode; powers of two for prefill), fp32/bf16/f16 inputs, outlier key
-channels or not, 3- and 4-bit records.  Codes are compared with the oracle's
-quantiser (bit for bit outside the near-boundary exemption) and attention rows
-within the same relative tolerance as the fixed cases.
+channels or not, 3- and 4-bit records, four or eight waves per decode
+workgroup.  Codes are compared with the oracle's quantiser (bit for bit outside
+the near-boundary exemption) and attention rows within the same relative
+tolerance as the fixed cases; a decode step (the token's append fused into
+attention) must leave the cache byte-identical to appending every token first.
 """
+
+import os
 
 import numpy as np
 import pytest
@@ -79,3 +83,36 @@ def test_prefill_random_shape(seed):
     _say(f"  max row error {err:.3e}")
     assert np.all(np.isfinite(out))
     assert err <= tol()
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_decode_step_random_shape(seed):
+    lens, hkv, group, dtype, outliers, bits = _draw(7700 + seed, prefill=False)
+    waves = int(np.random.default_rng(7800 + seed).choice([4, 8]))
+    _say(f"decode step random seed={seed} lens={lens} hkv={hkv} group={group} dtype={dtype} "
+         f"outliers={outliers} bits={bits} waves={waves}")
+    full = Scenario(7900 + seed, lens, hkv=hkv, dtype=dtype, outliers=outliers, bits=bits)
+    step = Scenario(7900 + seed, lens, hkv=hkv, dtype=dtype, outliers=outliers, bits=bits,
+                    kv_override=(full.k, full.v), hold_last=True)
+    q = step.queries(8000 + seed, len(lens), hkv * group).cuda()
+    old = os.environ.get("IQ_DECODE_WAVES")
+    os.environ["IQ_DECODE_WAVES"] = str(waves)
+    try:
+        out = step.iq.decode_step(step.cache, step.rot, q, step.k_last, step.v_last, step.bt_dev,
+                                  step.lens_dev, max(lens))
+        pair = full.iq.decode_attention(full.cache, full.rot, q, full.bt_dev, full.lens_dev, max(lens))
+        torch.cuda.synchronize()
+    finally:
+        if old is None:
+            os.environ.pop("IQ_DECODE_WAVES", None)
+        else:
+            os.environ["IQ_DECODE_WAVES"] = old
+    for a, b in zip(step.cache.to_host(), full.cache.to_host()):
+        assert np.array_equal(a, b)
+    o = out.cpu().numpy()
+    ref = step.oracle_decode(step.host_cache(), q.double().cpu().numpy())
+    err = max_row_error(o, ref)
+    _say(f"  max row error {err:.3e}")
+    assert np.all(np.isfinite(o))
+    assert err <= tol()
+    assert max_row_error(o, pair.cpu().numpy()) <= 0.5 * tol()
