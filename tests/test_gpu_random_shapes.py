@@ -116,3 +116,39 @@ def test_decode_step_random_shape(seed):
     assert np.all(np.isfinite(o))
     assert err <= tol()
     assert max_row_error(o, pair.cpu().numpy()) <= 0.5 * tol()
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_prefill_varlen_random_shape(seed):
+    rng = np.random.default_rng(8100 + seed)
+    batch = int(rng.integers(2, 6))
+    lens = [int(x) for x in rng.integers(1, 2501, size=batch)]
+    nq = [int(rng.integers(0, min(n, 200) + 1)) for n in lens]
+    if sum(nq) == 0:
+        nq[0] = 1
+    hkv = int(rng.choice([1, 2, 4]))
+    group = int(rng.choice([1, 2, 4, 8, 16]))
+    bits = int(rng.choice([3, 4]))
+    _say(f"prefill varlen random seed={seed} lens={lens} n_q={nq} hkv={hkv} group={group} bits={bits}")
+    s = Scenario(8200 + seed, lens, hkv=hkv, dtype="bf16", outliers=bool(rng.integers(0, 2)), bits=bits)
+    q = synth.to_dtype(synth.normal(8300 + seed, (sum(nq), hkv * group, 128)), "bf16")
+    cu = np.concatenate([[0], np.cumsum(nq)]).astype(np.int32)
+    starts = np.array([n - k for n, k in zip(lens, nq)], dtype=np.int32)
+    out = s.iq.prefill_attention_varlen(
+        s.cache, s.rot, q.cuda(), torch.from_numpy(cu).cuda(), torch.from_numpy(starts).cuda(), s.bt_dev,
+        max(nq), max(lens)).cpu().numpy()
+    host = s.host_cache()
+    fn = O4.prefill_attention4 if bits == 4 else O.prefill_attention
+    worst = 0.0
+    for b in range(batch):
+        if nq[b] == 0:
+            continue
+        rows = np.unique(np.linspace(0, nq[b] - 1, min(nq[b], 8)).astype(int))
+        ref = fn(host, s.blocks, q[cu[b]:cu[b + 1]].double().numpy(), int(starts[b]), s.block_table[b], rows=rows)
+        worst = max(worst, max_row_error(out[cu[b] + rows], ref))
+        one = s.iq.prefill_attention(s.cache, s.rot, q[cu[b]:cu[b + 1]].cuda(), int(starts[b]),
+                                     s.bt_dev[b]).cpu().numpy()
+        assert np.array_equal(one, out[cu[b]:cu[b + 1]])
+    _say(f"  max row error {worst:.3e}")
+    assert np.all(np.isfinite(out))
+    assert worst <= tol()
