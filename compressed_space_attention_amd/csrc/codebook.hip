@@ -1,8 +1,10 @@
 // Host-side quantiser codebooks of the record widths.
 //
-// 3 bits: the Gaussian Lloyd-Max levels the pages print ("TurboQuant and
-// RotorQuant ...", the 3-bit codebook), fixed in iq_device.h.
-// 4 bits (the family spans 3 and 4 bits): the 16-level Lloyd-Max quantiser of
+// 3 bits: the eight Gaussian Lloyd-Max levels the specification of this path
+// fixes (the pages name 3-bit scalar quantisation but print no levels),
+// held in iq_device.h.
+// 4 bits (FreeToken issue #141, Proposed Solution: the rotation-based KV
+// quantisers listed there span 3 and 4 bits): the 16-level Lloyd-Max quantiser of
 // N(0, 1), computed here once per process by Lloyd's iteration.  The density
 // is symmetric, so the iteration runs on the eight positive levels with the
 // middle threshold fixed at 0: thresholds = midpoints of adjacent levels,

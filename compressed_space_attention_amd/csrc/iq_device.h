@@ -29,9 +29,10 @@ struct __attribute__((aligned(4))) u3 {
 };
 
 // ---------------------------------------------------------------------------
-// 3-bit quantiser constants: the Gaussian Lloyd-Max levels the pages print
-// (positive half), and the decision thresholds = midpoints between adjacent
-// levels, as fp32 (the middle threshold is 0).
+// 3-bit quantiser constants: the Gaussian Lloyd-Max levels that the
+// specification of this path fixes (positive half; the pages name 3-bit
+// scalar quantisation but print no levels), and the decision thresholds =
+// midpoints between adjacent levels, as fp32 (the middle threshold is 0).
 // ---------------------------------------------------------------------------
 constexpr double kLevel3[4] = {0.2451, 0.7560, 1.3440, 2.1520};
 constexpr float kThr3[3] = {0.50055f, 1.05f, 1.748f};

@@ -87,9 +87,9 @@ enum {
  * of the record in slot 16 c + 4 q + r.  Norm arrays are slot-ordered for
  * both.  The struct is read during the call only.
  *
- * bits = 4 selects the 4-bit variant of the same pipeline (the pages' family
- * spans 3 and 4 bits; "TurboQuant and RotorQuant ...": 3-4 bit KV cache
- * compression): codes are the 16-level Gaussian Lloyd-Max quantiser's (see
+ * bits = 4 selects the 4-bit variant of the same pipeline (FreeToken issue
+ * #141, Proposed Solution: the rotation-based KV quantisers listed there span
+ * 3 and 4 bits): codes are the 16-level Gaussian Lloyd-Max quantiser's (see
  * iq_codebook), 64 bytes per record, k_codes/v_codes [num_pages][n_kv_heads][64][64].
  * A stored nibble is sign-magnitude: code c (0..15, ascending levels) is stored
  * as c - 8 for c >= 8 and 15 - c below.  Record: dword d (bytes 4d..4d+3)
@@ -119,8 +119,9 @@ int32_t iq_version(void);
 
 /*
  * The scalar quantiser of a record width, as the kernels apply it (host
- * only; no device is needed).  bits = 3: the Gaussian Lloyd-Max levels the
- * pages print ("TurboQuant and RotorQuant ...", the 3-bit codebook); bits = 4:
+ * only; no device is needed).  bits = 3: the eight Gaussian Lloyd-Max levels
+ * the specification of this path fixes (the pages name 3-bit scalar
+ * quantisation and print no levels); bits = 4:
  * the 16-level Gaussian Lloyd-Max quantiser, computed by Lloyd's iteration
  * (thresholds at the midpoints of adjacent levels, each level the mean of
  * N(0, 1) over its cell) once per process.

@@ -10,15 +10,18 @@ Sources (cited by page title and section):
   Compressed-Space Attention", abstract: Walsh-Hadamard transform, then
   block-diagonal SO(4) rotations, then low-bit scalar quantisation; attention
   runs on the packed tensors.
-* [TQ] "TurboQuant and RotorQuant ...: 3-4 bit KV cache compression" (the
-  pages' family spans 3 and 4 bits): the 4-bit member of the same pipeline.
+* [FT141] FreeToken issue #141 ("unified KV cache backend"), Proposed
+  Solution: the rotation-based KV quantisers it lists span 3 and 4 bits (the
+  TurboQuant line); this is the 4-bit member of the same pipeline.
 
 Readings (the pages fix the pipeline, not the 4-bit codebook or packing):
 
 * R4-1 Codebook: the 16-level Lloyd-Max quantiser of N(0, 1), computed here
   by Lloyd's iteration (decision thresholds at the midpoints of adjacent
   levels, each level the conditional mean of its cell).  The same iteration
-  with 8 levels reproduces the 3-bit codebook the pages print, which pins it.
+  with 8 levels reproduces, to their four digits, the 3-bit levels the
+  specification of this path fixes (the pages print no codebook), which pins
+  the iteration.
 * R4-2 Decision: code = #{j : float32(u) >= fp32 midpoint j} (ties go up),
   u = (T x) sqrt(d) / n as for 3 bits; the zero vector gets code 8.
 * R4-3 Stored nibble: sign-magnitude, nib = c - 8 for c >= 8 (levels >= 0)

@@ -1,6 +1,7 @@
 """The library's quantisers (host code, no GPU) against the oracle's.
 
-3 bits: the levels the pages print and the fp32 midpoints the oracle decides
+3 bits: the levels the specification of this path fixes and the fp32
+midpoints the oracle decides
 with.  4 bits: the library runs its own Lloyd iteration (positive half, by
 symmetry, from another start); it must land on the oracle's pinned codebook,
 with identical fp32 thresholds (the decisions are taken in fp32 on both
@@ -17,7 +18,7 @@ iq = pytest.importorskip("compressed_space_attention_amd.isoquant",
                          reason="libisoquant.so not built")
 
 
-def test_three_bit_codebook_is_the_printed_one():
+def test_three_bit_codebook_is_the_specified_one():
     levels, thr, alpha = iq.codebook(3)
     assert np.array_equal(levels, O.CENTROIDS)
     assert np.array_equal(thr, O.THRESHOLDS_F32)

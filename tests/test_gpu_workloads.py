@@ -50,6 +50,7 @@ class Built:
             ch = synth.outlier_channels(w.seed + 1, w.n_kv_heads)
             for h in range(w.n_kv_heads):
                 scale[h, torch.from_numpy(ch[h]).to(device)] = 10.0
+        self.k_scale, self.dt = scale, dt
         self.k = (synth.draw_normal_device(w.seed + 2, (total, w.n_kv_heads, 128), torch.float32, device)
                   * scale).to(dt)
         self.v = synth.draw_normal_device(w.seed + 3, (total, w.n_kv_heads, 128), dt, device)
@@ -141,6 +142,69 @@ def test_gqa_decode_32k_full(bits):
     cos = b.cosine_vs_uncompressed(0, range(0, w.n_q_heads, 4), out)
     _say(f"  {w.name}: max row error {err:.3e}, cosine min {min(cos):.4f} mean {np.mean(cos):.4f}")
     assert err <= tol()
+
+
+@pytest.mark.parametrize("bits", [3, 4])
+def test_gqa_decode_32k_step_full(bits):
+    """The benchmarked call itself: iq_decode_step at the 32K GQA shape (batch 1,
+    32 query / 4 kv heads, 32,767 cached tokens plus the current one), planned
+    as the benchmark plans it.  The step's cache equals quantise-append of the
+    token into a copy of the cache, byte for byte; the appended records match
+    the oracle's quantiser (codes bit for bit outside the 1e-6 boundary
+    exemption, norms outside fp16 midpoints); every query head's row is within
+    the tolerance of the oracle attending over the GPU-written cache, and
+    within half of it of decode attention on the pair's cache."""
+    w = workloads.GQA_DECODE_32K
+    L = w.context
+    b = Built(w, [L - 1], bits=bits)
+    hkv = w.n_kv_heads
+    k_new = (synth.draw_normal_device(w.seed + 12, (1, hkv, 128), torch.float32) * b.k_scale).to(b.dt)
+    v_new = synth.draw_normal_device(w.seed + 13, (1, hkv, 128), b.dt)
+    pair = iq.PagedCache(b.num_pages, hkv, zero=True, bits=bits)
+    for dst, src in zip((pair.k_codes, pair.k_norms, pair.v_codes, pair.v_norms),
+                        (b.cache.k_codes, b.cache.k_norms, b.cache.v_codes, b.cache.v_norms)):
+        dst.copy_(src)
+    lens_dev = torch.tensor([L], dtype=torch.int32, device="cuda")
+    _say(f"  {w.name} decode step, {bits}-bit records, {L} tokens")
+    out = iq.decode_step(b.cache, b.rot, b.q, k_new, v_new, b.bt_dev, lens_dev, L)
+    iq.quantize_append(pair, b.rot, k_new, v_new, torch.zeros(1, dtype=torch.int32, device="cuda"),
+                       torch.tensor([L - 1], dtype=torch.int32, device="cuda"), b.bt_dev)
+    out_pair = iq.decode_attention(pair, b.rot, b.q, b.bt_dev, lens_dev, L)
+    torch.cuda.synchronize()
+    for x, y in zip((b.cache.k_codes, b.cache.k_norms, b.cache.v_codes, b.cache.v_norms),
+                    (pair.k_codes, pair.k_norms, pair.v_codes, pair.v_norms)):
+        assert torch.equal(x, y), "the step's cache differs from quantise-append + the same cache"
+    host = b.host()
+    page, slot = int(b.bt[0, (L - 1) // 64]), (L - 1) % 64
+    near = mism = 0
+    for name, x in (("k", k_new), ("v", v_new)):
+        xs = x[0].double().cpu().numpy()
+        for h in range(hkv):
+            if bits == 4:
+                q = O4.quantize4(xs[h:h + 1], b.blocks[h])
+                gc = host.codes(name, np.array([page]), h, np.array([slot]))
+            else:
+                q = O.quantize(xs[h:h + 1], b.blocks[h])
+                gc = O.unpack_codes(host.records(name, np.array([page]), h, np.array([slot])))
+            bad = gc != q["codes"]
+            assert not np.any(bad & ~q["near"]), f"appended {name} head {h}: code mismatch off-boundary"
+            gn = getattr(host, name + "_norms")[page, h, slot]
+            assert gn == q["norm16"][0] or q["norm_near"][0], f"appended {name} head {h}: norm"
+            mism += int(bad.sum())
+            near += int(q["near"].sum())
+    _say(f"  appended token: {2 * hkv * 128} codes, mismatches {mism}, near-boundary {near}")
+    ref = (O4.decode_attention4 if bits == 4 else O.decode_attention)(
+        host, b.blocks, b.q.double().cpu().numpy(), b.bt, np.array([L]))
+    o = out.cpu().numpy()
+    err = max_row_error(o, ref)
+    err_pair = max_row_error(o, out_pair.cpu().numpy())
+    b.k, b.v, b.lens = torch.cat([b.k, k_new]), torch.cat([b.v, v_new]), np.array([L])
+    cos = b.cosine_vs_uncompressed(0, range(w.n_q_heads), o)
+    _say(f"  max row error {err:.3e} (all {w.n_q_heads} heads), vs append + decode {err_pair:.3e}, "
+         f"cosine vs uncompressed min {min(cos):.4f} mean {np.mean(cos):.4f}")
+    assert np.all(np.isfinite(o))
+    assert err <= tol()
+    assert err_pair <= 0.5 * tol()
 
 
 @pytest.mark.parametrize("bits", [3, 4])

@@ -1,5 +1,6 @@
 """Pins of the 4-bit oracle (oracle/isoquant4_oracle.py) against mathematics
-it does not share code with: the pages' printed 3-bit codebook, numerical
+it does not share code with: the 3-bit levels the specification of this path
+fixes (four digits each; the pages print no codebook), numerical
 integration of the Gaussian (scipy), brute force on tiny inputs, and a
 hand-worked packing example (tests/golden/pack4_worked_example.txt)."""
 
@@ -16,15 +17,15 @@ from oracle import isoquant_oracle as O
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "pack4_worked_example.txt")
 
 
-def test_lloyd_iteration_reproduces_printed_3bit_codebook():
-    """RotaryQuant's 3-bit Gaussian levels are printed to four digits: the
-    same iteration with 8 levels must land on them."""
+def test_lloyd_iteration_reproduces_specified_3bit_codebook():
+    """The 3-bit Gaussian Lloyd-Max levels of the specification are given to
+    four digits: the same iteration with 8 levels must land on them."""
     c8 = O4.lloyd_max_gaussian(8)
-    printed = np.array([-2.1520, -1.3440, -0.7560, -0.2451, 0.2451, 0.7560, 1.3440, 2.1520])
+    specified = np.array([-2.1520, -1.3440, -0.7560, -0.2451, 0.2451, 0.7560, 1.3440, 2.1520])
     # four significant digits each (2.152, 1.344, 0.7560, 0.2451): half a unit
     # of the fourth digit
-    half_ulp = 0.5 * 10.0 ** (np.floor(np.log10(np.abs(printed))) - 3)
-    assert np.all(np.abs(c8 - printed) <= half_ulp + 1e-12)
+    half_ulp = 0.5 * 10.0 ** (np.floor(np.log10(np.abs(specified))) - 3)
+    assert np.all(np.abs(c8 - specified) <= half_ulp + 1e-12)
     assert abs(O4.gaussian_mse(c8) - 0.034548) < 5e-7
 
 
