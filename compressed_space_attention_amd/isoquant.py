@@ -139,6 +139,52 @@ def _contig(t: torch.Tensor, name: str) -> torch.Tensor:
     return t
 
 
+def _device_of(t: torch.Tensor, name: str) -> torch.device:
+    """The GPU `t` lives on (the device every other operand must share)."""
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a tensor in GPU memory")
+    return t.device
+
+
+def _dev(t: torch.Tensor, name: str, device: torch.device, dtype: torch.dtype | None = None) -> int:
+    """Device pointer of a contiguous tensor on `device` (of `dtype` if given):
+    a host tensor would hand a host address to a kernel, and an index tensor
+    of another width would be misread."""
+    if not isinstance(t, torch.Tensor) or not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must be a tensor on {device}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return _contig(t, name).data_ptr()
+
+
+def _idx(t: torch.Tensor, name: str, device: torch.device) -> int:
+    return _dev(t, name, device, torch.int32)
+
+
+def _check_cache(cache, device: torch.device):
+    for name, t in cache.tensors():
+        _dev(t, f"cache.{name}", device)
+
+
+def _torch_stream(stream, device: torch.device):
+    if stream is None:
+        return None
+    if isinstance(stream, int):
+        return torch.cuda.ExternalStream(stream, device=device)
+    return stream
+
+
+def _alloc(shape, dtype, device: torch.device, stream, zero: bool = False) -> torch.Tensor:
+    """A buffer owned by the caching allocator on the stream the kernels run
+    on, so it is not handed out again while they may still use it."""
+    fn = torch.zeros if zero else torch.empty
+    s = _torch_stream(stream, device)
+    if s is None:
+        return fn(shape, dtype=dtype, device=device)
+    with torch.cuda.stream(s):
+        return fn(shape, dtype=dtype, device=device)
+
+
 def codebook(bits: int):
     """(levels float64[2^bits], thresholds float32[2^bits - 1], alpha) of the
     library's quantiser for 3- or 4-bit records (host only)."""
@@ -176,6 +222,10 @@ class PagedCache:
     def struct(self):
         return ctypes.byref(self._struct)
 
+    def tensors(self):
+        return (("k_codes", self.k_codes), ("k_norms", self.k_norms), ("v_codes", self.v_codes),
+                ("v_norms", self.v_norms))
+
     def nbytes(self) -> int:
         return sum(t.numel() * t.element_size() for t in
                    (self.k_codes, self.v_codes, self.k_norms, self.v_norms))
@@ -196,7 +246,10 @@ def rotation_init(quats, device="cuda", stream=None) -> torch.Tensor:
     hkv = q.shape[0]
     if q.shape != (hkv, 32, 2, 4):
         raise ValueError("quaternions must be [Hkv][32][2][4]")
-    rot = torch.empty(rotation_bytes(hkv), dtype=torch.uint8, device=device)
+    dev = torch.device(device)
+    if dev.type == "cuda" and dev.index is None:
+        dev = torch.device("cuda", torch.cuda.current_device())
+    rot = _alloc((rotation_bytes(hkv),), torch.uint8, dev, stream)
     _check("iq_rotation_init", lib.iq_rotation_init(q.ctypes.data, hkv, rot.data_ptr(), rot.numel(),
                                                     _stream(stream)))
     return rot
@@ -211,14 +264,38 @@ def quantize_append(cache: PagedCache, rot: torch.Tensor, k: torch.Tensor, v: to
     if k.shape[1] != cache.n_kv_heads:
         raise ValueError("kv head count differs from the cache")
     n = k.shape[0]
+    dev = _device_of(k, "k")
+    if seq_idx.numel() != n or pos.numel() != n:
+        raise ValueError("seq_idx and pos must hold one entry per token")
+    _check_cache(cache, dev)
     _check("iq_quantize_append", lib.iq_quantize_append(
-        cache.struct, rot.data_ptr(), _contig(k, "k").data_ptr(), _contig(v, "v").data_ptr(),
-        _dtype(k), n, _ptr(_contig(seq_idx, "seq_idx")), _ptr(_contig(pos, "pos")),
-        _ptr(_contig(block_table, "block_table")), block_table.shape[-1], _stream(stream)))
+        cache.struct, _dev(rot, "rot", dev), _dev(k, "k", dev), _dev(v, "v", dev), _dtype(k), n,
+        _idx(seq_idx, "seq_idx", dev), _idx(pos, "pos", dev), _idx(block_table, "block_table", dev),
+        block_table.shape[-1], _stream(stream)))
 
 
 def decode_workspace_bytes(batch: int, n_q_heads: int, n_kv_heads: int, max_seq_len: int) -> int:
     return int(lib.iq_decode_workspace_bytes(batch, n_q_heads, n_kv_heads, max_seq_len))
+
+
+def _decode_operands(cache, rot, q, block_table, seq_lens, max_seq_len, out, workspace, stream):
+    bsz, hq, d = q.shape
+    if d != HEAD_DIM:
+        raise ValueError("head dim must be 128")
+    dev = _device_of(q, "q")
+    _check_cache(cache, dev)
+    if block_table.dim() != 2 or block_table.shape[0] < bsz or seq_lens.numel() != bsz:
+        raise ValueError("block_table must be int32[B][max_pages] and seq_lens int32[B]")
+    if out is None:
+        out = _alloc((bsz, hq, HEAD_DIM), torch.float32, dev, stream)
+    elif out.dtype != torch.float32 or tuple(out.shape) != (bsz, hq, HEAD_DIM):
+        raise ValueError("out must be float32 [B][Hq][128]")
+    if workspace is None:
+        nbytes = decode_workspace_bytes(bsz, hq, cache.n_kv_heads, max_seq_len)
+        workspace = _alloc((max(nbytes, 16),), torch.uint8, dev, stream)
+    ptrs = (_dev(rot, "rot", dev), _dev(q, "q", dev), _idx(block_table, "block_table", dev),
+            _idx(seq_lens, "seq_lens", dev), _dev(out, "out", dev), _dev(workspace, "workspace", dev))
+    return dev, out, workspace, ptrs
 
 
 def decode_attention(cache: PagedCache, rot: torch.Tensor, q: torch.Tensor, block_table: torch.Tensor,
@@ -226,20 +303,12 @@ def decode_attention(cache: PagedCache, rot: torch.Tensor, q: torch.Tensor, bloc
                      out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
                      stream=None) -> torch.Tensor:
     """q: [B][Hq][128]; block_table int32[B][max_pages]; seq_lens int32[B] -> fp32 [B][Hq][128]."""
-    bsz, hq, d = q.shape
-    if d != HEAD_DIM:
-        raise ValueError("head dim must be 128")
-    if out is None:
-        out = torch.empty((bsz, hq, HEAD_DIM), dtype=torch.float32, device=q.device)
-    if workspace is None:
-        nbytes = decode_workspace_bytes(bsz, hq, cache.n_kv_heads, max_seq_len)
-        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    bsz, hq, _ = q.shape
+    dev, out, workspace, (p_rot, p_q, p_bt, p_len, p_out, p_ws) = _decode_operands(
+        cache, rot, q, block_table, seq_lens, max_seq_len, out, workspace, stream)
     _check("iq_decode_attention", lib.iq_decode_attention(
-        cache.struct, rot.data_ptr(), _contig(q, "q").data_ptr(), _dtype(q), bsz, hq,
-        _contig(block_table, "block_table").data_ptr(), block_table.shape[-1],
-        _contig(seq_lens, "seq_lens").data_ptr(), int(max_seq_len), float(softmax_scale),
-        out.data_ptr(), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-        _stream(stream)))
+        cache.struct, p_rot, p_q, _dtype(q), bsz, hq, p_bt, block_table.shape[-1], p_len, int(max_seq_len),
+        float(softmax_scale), p_out, p_ws, workspace.numel() * workspace.element_size(), _stream(stream)))
     return out
 
 
@@ -249,24 +318,16 @@ def decode_step(cache: PagedCache, rot: torch.Tensor, q: torch.Tensor, k_new: to
                 workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """Append each sequence's current token (k_new, v_new: [B][Hkv][128], at position
     seq_lens[b] - 1) and run decode attention over all seq_lens[b] tokens, in one call."""
-    bsz, hq, d = q.shape
-    if d != HEAD_DIM:
-        raise ValueError("head dim must be 128")
+    bsz, hq, _ = q.shape
     if (k_new.shape != v_new.shape or k_new.dtype != v_new.dtype
             or tuple(k_new.shape) != (bsz, cache.n_kv_heads, HEAD_DIM)):
         raise ValueError("k_new and v_new must both be [B][Hkv][128] of one dtype")
-    if out is None:
-        out = torch.empty((bsz, hq, HEAD_DIM), dtype=torch.float32, device=q.device)
-    if workspace is None:
-        nbytes = decode_workspace_bytes(bsz, hq, cache.n_kv_heads, max_seq_len)
-        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    dev, out, workspace, (p_rot, p_q, p_bt, p_len, p_out, p_ws) = _decode_operands(
+        cache, rot, q, block_table, seq_lens, max_seq_len, out, workspace, stream)
     _check("iq_decode_step", lib.iq_decode_step(
-        cache.struct, rot.data_ptr(), _contig(q, "q").data_ptr(), _dtype(q), bsz, hq,
-        _contig(k_new, "k_new").data_ptr(), _contig(v_new, "v_new").data_ptr(), _dtype(k_new),
-        _contig(block_table, "block_table").data_ptr(), block_table.shape[-1],
-        _contig(seq_lens, "seq_lens").data_ptr(), int(max_seq_len), float(softmax_scale),
-        out.data_ptr(), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-        _stream(stream)))
+        cache.struct, p_rot, p_q, _dtype(q), bsz, hq, _dev(k_new, "k_new", dev), _dev(v_new, "v_new", dev),
+        _dtype(k_new), p_bt, block_table.shape[-1], p_len, int(max_seq_len), float(softmax_scale),
+        p_out, p_ws, workspace.numel() * workspace.element_size(), _stream(stream)))
     return out
 
 
@@ -282,17 +343,21 @@ def prefill_attention(cache: PagedCache, rot: torch.Tensor, q: torch.Tensor, q_s
     n_q, hq, d = q.shape
     if d != HEAD_DIM:
         raise ValueError("head dim must be 128")
+    dev = _device_of(q, "q")
+    _check_cache(cache, dev)
     if out is None:
-        out = torch.empty((n_q, hq, HEAD_DIM), dtype=torch.float32, device=q.device)
+        out = _alloc((n_q, hq, HEAD_DIM), torch.float32, dev, stream)
+    elif out.dtype != torch.float32 or tuple(out.shape) != (n_q, hq, HEAD_DIM):
+        raise ValueError("out must be float32 [n_q][Hq][128]")
     need = prefill_workspace_bytes(max(n_q, 1), hq, cache.n_kv_heads, q_start)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_ptr = _ptr(workspace)
+        workspace = _alloc((need,), torch.uint8, dev, stream)
+    ws_ptr = None if workspace is None else _dev(workspace, "workspace", dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("iq_prefill_attention", lib.iq_prefill_attention(
-        cache.struct, rot.data_ptr(), _contig(q, "q").data_ptr(), _dtype(q), n_q, hq, int(q_start),
-        _contig(block_table, "block_table").data_ptr(), block_table.shape[-1], float(softmax_scale),
-        out.data_ptr(), ws_ptr, ws_bytes, _stream(stream)))
+        cache.struct, _dev(rot, "rot", dev), _dev(q, "q", dev), _dtype(q), n_q, hq, int(q_start),
+        _idx(block_table, "block_table", dev), block_table.shape[-1], float(softmax_scale),
+        _dev(out, "out", dev), ws_ptr, ws_bytes, _stream(stream)))
     return out
 
 
@@ -305,14 +370,20 @@ def prefill_attention_varlen(cache: PagedCache, rot: torch.Tensor, q: torch.Tens
     total_q, hq, d = q.shape
     if d != HEAD_DIM:
         raise ValueError("head dim must be 128")
+    dev = _device_of(q, "q")
+    _check_cache(cache, dev)
     bsz = cu_q.numel() - 1
+    if bsz < 1 or q_start.numel() != bsz or block_table.dim() != 2 or block_table.shape[0] < bsz:
+        raise ValueError("cu_q must be int32[B+1], q_start int32[B], block_table int32[B][max_pages]")
     if out is None:
-        out = torch.zeros((total_q, hq, HEAD_DIM), dtype=torch.float32, device=q.device)
+        out = _alloc((total_q, hq, HEAD_DIM), torch.float32, dev, stream, zero=True)
+    elif out.dtype != torch.float32 or tuple(out.shape) != (total_q, hq, HEAD_DIM):
+        raise ValueError("out must be float32 [total_q][Hq][128]")
     _check("iq_prefill_attention_varlen", lib.iq_prefill_attention_varlen(
-        cache.struct, rot.data_ptr(), _contig(q, "q").data_ptr(), _dtype(q), bsz, hq, total_q,
-        _contig(cu_q, "cu_q").data_ptr(), _contig(q_start, "q_start").data_ptr(), int(max_q_per_seq),
-        int(max_kv_len), _contig(block_table, "block_table").data_ptr(), block_table.shape[-1],
-        float(softmax_scale), out.data_ptr(), None, 0, _stream(stream)))
+        cache.struct, _dev(rot, "rot", dev), _dev(q, "q", dev), _dtype(q), bsz, hq, total_q,
+        _idx(cu_q, "cu_q", dev), _idx(q_start, "q_start", dev), int(max_q_per_seq),
+        int(max_kv_len), _idx(block_table, "block_table", dev), block_table.shape[-1],
+        float(softmax_scale), _dev(out, "out", dev), None, 0, _stream(stream)))
     return out
 
 
@@ -342,6 +413,9 @@ class DenseCache:
     def struct(self):
         return ctypes.byref(self._struct)
 
+    def tensors(self):
+        return (("k", self.k), ("v", self.v))
+
     def nbytes(self) -> int:
         return self.k.element_size() * (self.k.numel() + self.v.numel())
 
@@ -352,10 +426,14 @@ def dense_append(cache: DenseCache, k: torch.Tensor, v: torch.Tensor, seq_idx: t
         raise ValueError("k and v must both be [n_tokens][Hkv][128] of one dtype")
     if k.shape[1] != cache.n_kv_heads:
         raise ValueError("kv head count differs from the cache")
+    dev = _device_of(k, "k")
+    if seq_idx.numel() != k.shape[0] or pos.numel() != k.shape[0]:
+        raise ValueError("seq_idx and pos must hold one entry per token")
+    _check_cache(cache, dev)
     _check("iq_dense_append", lib.iq_dense_append(
-        cache.struct, _contig(k, "k").data_ptr(), _contig(v, "v").data_ptr(), _dtype(k), k.shape[0],
-        _ptr(_contig(seq_idx, "seq_idx")), _ptr(_contig(pos, "pos")),
-        _ptr(_contig(block_table, "block_table")), block_table.shape[-1], _stream(stream)))
+        cache.struct, _dev(k, "k", dev), _dev(v, "v", dev), _dtype(k), k.shape[0],
+        _idx(seq_idx, "seq_idx", dev), _idx(pos, "pos", dev), _idx(block_table, "block_table", dev),
+        block_table.shape[-1], _stream(stream)))
 
 
 def dense_decode_workspace_bytes(batch: int, n_q_heads: int, n_kv_heads: int, max_seq_len: int) -> int:
@@ -370,17 +448,22 @@ def dense_decode_attention(cache: DenseCache, q: torch.Tensor, block_table: torc
     bsz, hq, d = q.shape
     if d != HEAD_DIM:
         raise ValueError("head dim must be 128")
+    dev = _device_of(q, "q")
+    _check_cache(cache, dev)
+    if block_table.dim() != 2 or block_table.shape[0] < bsz or seq_lens.numel() != bsz:
+        raise ValueError("block_table must be int32[B][max_pages] and seq_lens int32[B]")
     if out is None:
-        out = torch.empty((bsz, hq, HEAD_DIM), dtype=torch.float32, device=q.device)
+        out = _alloc((bsz, hq, HEAD_DIM), torch.float32, dev, stream)
+    elif out.dtype != torch.float32 or tuple(out.shape) != (bsz, hq, HEAD_DIM):
+        raise ValueError("out must be float32 [B][Hq][128]")
     if workspace is None:
         nbytes = dense_decode_workspace_bytes(bsz, hq, cache.n_kv_heads, max_seq_len)
-        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+        workspace = _alloc((max(nbytes, 16),), torch.uint8, dev, stream)
     _check("iq_dense_decode_attention", lib.iq_dense_decode_attention(
-        cache.struct, _contig(q, "q").data_ptr(), _dtype(q), bsz, hq,
-        _contig(block_table, "block_table").data_ptr(), block_table.shape[-1],
-        _contig(seq_lens, "seq_lens").data_ptr(), int(max_seq_len), float(softmax_scale),
-        out.data_ptr(), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-        _stream(stream)))
+        cache.struct, _dev(q, "q", dev), _dtype(q), bsz, hq, _idx(block_table, "block_table", dev),
+        block_table.shape[-1], _idx(seq_lens, "seq_lens", dev), int(max_seq_len), float(softmax_scale),
+        _dev(out, "out", dev), _dev(workspace, "workspace", dev),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
     return out
 
 
@@ -392,12 +475,16 @@ def dense_prefill_attention(cache: DenseCache, q: torch.Tensor, q_start: int, bl
     n_q, hq, d = q.shape
     if d != HEAD_DIM:
         raise ValueError("head dim must be 128")
+    dev = _device_of(q, "q")
+    _check_cache(cache, dev)
     if out is None:
-        out = torch.empty((n_q, hq, HEAD_DIM), dtype=torch.float32, device=q.device)
+        out = _alloc((n_q, hq, HEAD_DIM), torch.float32, dev, stream)
+    elif out.dtype != torch.float32 or tuple(out.shape) != (n_q, hq, HEAD_DIM):
+        raise ValueError("out must be float32 [n_q][Hq][128]")
     _check("iq_dense_prefill_attention", lib.iq_dense_prefill_attention(
-        cache.struct, _contig(q, "q").data_ptr(), _dtype(q), n_q, hq, int(q_start),
-        _contig(block_table, "block_table").data_ptr(), block_table.shape[-1], float(softmax_scale),
-        out.data_ptr(), _stream(stream)))
+        cache.struct, _dev(q, "q", dev), _dtype(q), n_q, hq, int(q_start),
+        _idx(block_table, "block_table", dev), block_table.shape[-1], float(softmax_scale),
+        _dev(out, "out", dev), _stream(stream)))
     return out
 
 
@@ -407,6 +494,7 @@ def probe_sink_bytes() -> int:
 
 def probe_read(buf: torch.Tensor, sink: torch.Tensor, stream=None):
     """Stream `buf` (contiguous, size a multiple of 16 bytes) once on the GPU."""
+    dev = _device_of(buf, "buf")
     nbytes = buf.numel() * buf.element_size()
-    _check("iq_probe_read", lib.iq_probe_read(_contig(buf, "buf").data_ptr(), nbytes, sink.data_ptr(),
+    _check("iq_probe_read", lib.iq_probe_read(_dev(buf, "buf", dev), nbytes, _dev(sink, "sink", dev),
                                               sink.numel() * sink.element_size(), _stream(stream)))

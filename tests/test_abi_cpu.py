@@ -193,3 +193,27 @@ def test_prefill_varlen_validation():
     assert call(batch=0) == -1
     assert call(total_q=0, max_q=0) == 0     # no-op
     assert call(max_kv=300000, max_pages=5000) == -2   # beyond the staging limit
+
+
+def test_binding_refuses_host_tensors():
+    """The binding hands kernels device pointers only: a tensor in host memory
+    (here every tensor: this check runs without a GPU) is refused before any
+    call reaches the library."""
+    import torch
+    cache = iq.PagedCache(4, 2, device="cpu")
+    rot = torch.zeros(iq.rotation_bytes(2), dtype=torch.uint8)
+    q = torch.zeros((1, 4, 128), dtype=torch.bfloat16)
+    bt = torch.zeros((1, 4), dtype=torch.int32)
+    lens = torch.ones(1, dtype=torch.int32)
+    kv = torch.zeros((1, 2, 128), dtype=torch.bfloat16)
+    calls = [
+        lambda: iq.decode_attention(cache, rot, q, bt, lens, 64),
+        lambda: iq.decode_step(cache, rot, q, kv, kv, bt, lens, 64),
+        lambda: iq.quantize_append(cache, rot, kv, kv, torch.zeros(1, dtype=torch.int32),
+                                   torch.zeros(1, dtype=torch.int32), bt),
+        lambda: iq.prefill_attention(cache, rot, q, 0, bt[0]),
+        lambda: iq.probe_read(torch.zeros(16, dtype=torch.uint8), torch.zeros(16, dtype=torch.uint8)),
+    ]
+    for fn in calls:
+        with pytest.raises(ValueError, match="GPU memory"):
+            fn()
