@@ -151,8 +151,7 @@ def run_decode(args):
     layers = [DecodeLayer(iq, synth, w, i, block_table, num_pages, device, args.bits) for i in range(ring)]
     torch.cuda.synchronize()
     log(f"[bench] caches built in {time.time() - t0:.1f} s")
-    ws = torch.empty(max(16, iq.decode_workspace_bytes(w.batch, w.n_q_heads, w.n_kv_heads, max_len)),
-                     dtype=torch.uint8, device=device)
+    ws = iq.decode_workspace(w.batch, w.n_q_heads, w.n_kv_heads, max_len, device=device)
 
     def step(layer, mode="step"):
         """mode "step": the fused decode step (append + attention, one call);
@@ -415,8 +414,7 @@ def run_four_bit_aux(w, lens, bt_np, num_pages, t_decode3, t_step3, ring_bytes=1
         q = synth.draw_normal_device(seed * 19, (w.batch, w.n_q_heads, 128), torch.bfloat16, dev)
         out = torch.empty((w.batch, w.n_q_heads, 128), dtype=torch.float32, device=dev)
         layers.append((c, rot, kn, vn, q, out))
-    ws = torch.empty(max(16, iq.decode_workspace_bytes(w.batch, w.n_q_heads, w.n_kv_heads, max_len)),
-                     dtype=torch.uint8, device=dev)
+    ws = iq.decode_workspace(w.batch, w.n_q_heads, w.n_kv_heads, max_len, device=dev)
 
     def run(n, mode):
         for i in range(n):

@@ -63,6 +63,51 @@ iq_status launch_status(hipError_t e) { return e == hipSuccess ? IQ_OK : IQ_ERR_
 
 float resolve_scale(float s) { return (s > 0.f && isfinite(s)) ? s : 1.0f / sqrtf(128.0f); }
 
+// Decode options -> the planner's form; false for a field outside its values.
+bool decode_options(const iq_decode_options* o, iq::DecodeOptions* out) {
+  *out = iq::DecodeOptions{};
+  if (!o) return true;
+  if ((o->waves != 0 && o->waves != 4 && o->waves != 8) || o->pages_per_split < 0 || o->rounds < 0 ||
+      o->rounds > 64 || o->plan < IQ_PLAN_AUTO || o->plan > IQ_PLAN_BALANCED || o->merge < IQ_MERGE_AUTO ||
+      o->merge > IQ_MERGE_KERNEL)
+    return false;
+  out->waves = o->waves;
+  out->pages_per_split = o->pages_per_split;
+  out->rounds = o->rounds;
+  out->plan = o->plan == IQ_PLAN_HOST ? 1 : 0;
+  out->merge = o->merge == IQ_MERGE_FUSED ? 1 : o->merge == IQ_MERGE_KERNEL ? 2 : 0;
+  out->deterministic = o->deterministic != 0;
+  return true;
+}
+
+static_assert(IQ_DECODE_COUNTER_BYTES == iq::kWsCounterBytes, "counter region size");
+
+// Shared by iq_decode_attention(_ex) and iq_decode_step(_ex): k_new null for attention alone.
+iq_status decode_call(const iq_cache* cache, const void* rot_dev, const void* q_dev, int32_t q_dtype,
+                      int32_t batch, int32_t n_q_heads, const void* k_new_dev, const void* v_new_dev,
+                      int32_t kv_dtype, const int32_t* block_table_dev, int32_t max_pages_per_seq,
+                      const int32_t* seq_lens_dev, int32_t max_seq_len, float softmax_scale, float* out_dev,
+                      void* workspace_dev, size_t workspace_bytes, const iq_decode_options* options,
+                      hipStream_t stream) {
+  if (!cache_ok(cache) || !rot_dev || !q_dev || !dtype_ok(q_dtype) || batch < 1 || batch > 65535 ||
+      n_q_heads < 1 || !block_table_dev || max_pages_per_seq < 1 || !seq_lens_dev || max_seq_len < 0 ||
+      !out_dev || !workspace_dev)
+    return IQ_ERR_INVALID_ARG;
+  if (k_new_dev && (!v_new_dev || !dtype_ok(kv_dtype))) return IQ_ERR_INVALID_ARG;
+  iq::DecodeOptions opts;
+  if (!decode_options(options, &opts)) return IQ_ERR_INVALID_ARG;
+  if (n_q_heads % cache->n_kv_heads != 0) return IQ_ERR_INVALID_ARG;
+  if ((int64_t)max_seq_len > (int64_t)max_pages_per_seq * IQ_PAGE_TOKENS) return IQ_ERR_INVALID_ARG;
+  if (cache->n_kv_heads > 65535) return IQ_ERR_UNSUPPORTED;
+  if (n_q_heads / cache->n_kv_heads > IQ_MAX_GROUP) return IQ_ERR_UNSUPPORTED;
+  const iq::DecodePlan plan = iq::plan_decode(batch, cache->n_kv_heads, max_seq_len, device_cu_count(), opts);
+  if (workspace_bytes < iq::decode_workspace_bytes(batch, n_q_heads, plan)) return IQ_ERR_WORKSPACE;
+  return launch_status(iq::launch_decode(view(cache), reinterpret_cast<const float*>(rot_dev), q_dev,
+                                         q_dtype, batch, n_q_heads, block_table_dev, max_pages_per_seq,
+                                         seq_lens_dev, plan, resolve_scale(softmax_scale), out_dev,
+                                         workspace_dev, k_new_dev, v_new_dev, kv_dtype, stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -143,11 +188,39 @@ iq_status iq_quantize_append(const iq_cache* cache, const void* rot_dev, const v
                                                   block_table_dev, max_pages_per_seq, stream));
 }
 
+size_t iq_decode_workspace_bytes_ex(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                                    int32_t max_seq_len, const iq_decode_options* options) {
+  iq::DecodeOptions opts;
+  if (batch < 1 || n_q_heads < 1 || n_kv_heads < 1 || max_seq_len < 0 || !decode_options(options, &opts))
+    return 0;
+  const iq::DecodePlan plan = iq::plan_decode(batch, n_kv_heads, max_seq_len, device_cu_count(), opts);
+  return iq::decode_workspace_bytes(batch, n_q_heads, plan);
+}
+
+iq_status iq_decode_describe(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, int32_t max_seq_len,
+                             int32_t bits, int32_t step, const iq_decode_options* options,
+                             iq_decode_plan_info* info) {
+  iq::DecodeOptions opts;
+  if (!info || batch < 1 || batch > 65535 || n_q_heads < 1 || n_kv_heads < 1 || n_kv_heads > 65535 ||
+      max_seq_len < 0 || (bits != 0 && bits != 3 && bits != 4) || n_q_heads % n_kv_heads != 0 ||
+      !decode_options(options, &opts))
+    return IQ_ERR_INVALID_ARG;
+  if (n_q_heads / n_kv_heads > IQ_MAX_GROUP) return IQ_ERR_UNSUPPORTED;
+  const iq::DecodePlan plan = iq::plan_decode(batch, n_kv_heads, max_seq_len, device_cu_count(), opts);
+  const bool fused = iq::decode_fused_merge(plan, batch, n_kv_heads, n_q_heads, bits == 4 ? 4 : 3, step != 0);
+  info->waves = plan.waves;
+  info->splits = plan.splits;
+  info->pages_per_split = plan.pages_per_split;
+  info->balanced = plan.balanced;
+  info->fused_merge = fused ? 1 : 0;
+  info->workgroups = plan.balanced ? plan.grid_x
+                                   : plan.splits * n_kv_heads * batch + (fused ? batch * n_q_heads : 0);
+  return IQ_OK;
+}
+
 size_t iq_decode_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
                                  int32_t max_seq_len) {
-  if (batch < 1 || n_q_heads < 1 || n_kv_heads < 1 || max_seq_len < 0) return 0;
-  const iq::DecodePlan plan = iq::plan_decode(batch, n_kv_heads, max_seq_len, device_cu_count());
-  return iq::decode_workspace_bytes(batch, n_q_heads, plan);
+  return iq_decode_workspace_bytes_ex(batch, n_q_heads, n_kv_heads, max_seq_len, nullptr);
 }
 
 iq_status iq_decode_attention(const iq_cache* cache, const void* rot_dev, const void* q_dev,
@@ -156,20 +229,20 @@ iq_status iq_decode_attention(const iq_cache* cache, const void* rot_dev, const 
                               const int32_t* seq_lens_dev, int32_t max_seq_len, float softmax_scale,
                               float* out_dev, void* workspace_dev, size_t workspace_bytes,
                               hipStream_t stream) {
-  if (!cache_ok(cache) || !rot_dev || !q_dev || !dtype_ok(q_dtype) || batch < 1 || batch > 65535 ||
-      n_q_heads < 1 || !block_table_dev || max_pages_per_seq < 1 || !seq_lens_dev ||
-      max_seq_len < 0 || !out_dev || !workspace_dev)
-    return IQ_ERR_INVALID_ARG;
-  if (n_q_heads % cache->n_kv_heads != 0) return IQ_ERR_INVALID_ARG;
-  if ((int64_t)max_seq_len > (int64_t)max_pages_per_seq * IQ_PAGE_TOKENS) return IQ_ERR_INVALID_ARG;
-  if (cache->n_kv_heads > 65535) return IQ_ERR_UNSUPPORTED;
-  if (n_q_heads / cache->n_kv_heads > IQ_MAX_GROUP) return IQ_ERR_UNSUPPORTED;
-  const iq::DecodePlan plan = iq::plan_decode(batch, cache->n_kv_heads, max_seq_len, device_cu_count());
-  if (workspace_bytes < iq::decode_workspace_bytes(batch, n_q_heads, plan)) return IQ_ERR_WORKSPACE;
-  return launch_status(iq::launch_decode(view(cache), reinterpret_cast<const float*>(rot_dev), q_dev,
-                                         q_dtype, batch, n_q_heads, block_table_dev, max_pages_per_seq,
-                                         seq_lens_dev, plan, resolve_scale(softmax_scale), out_dev,
-                                         workspace_dev, nullptr, nullptr, 0, stream));
+  return decode_call(cache, rot_dev, q_dev, q_dtype, batch, n_q_heads, nullptr, nullptr, 0, block_table_dev,
+                     max_pages_per_seq, seq_lens_dev, max_seq_len, softmax_scale, out_dev, workspace_dev,
+                     workspace_bytes, nullptr, stream);
+}
+
+iq_status iq_decode_attention_ex(const iq_cache* cache, const void* rot_dev, const void* q_dev,
+                                 int32_t q_dtype, int32_t batch, int32_t n_q_heads,
+                                 const int32_t* block_table_dev, int32_t max_pages_per_seq,
+                                 const int32_t* seq_lens_dev, int32_t max_seq_len, float softmax_scale,
+                                 float* out_dev, void* workspace_dev, size_t workspace_bytes,
+                                 const iq_decode_options* options, hipStream_t stream) {
+  return decode_call(cache, rot_dev, q_dev, q_dtype, batch, n_q_heads, nullptr, nullptr, 0, block_table_dev,
+                     max_pages_per_seq, seq_lens_dev, max_seq_len, softmax_scale, out_dev, workspace_dev,
+                     workspace_bytes, options, stream);
 }
 
 iq_status iq_decode_step(const iq_cache* cache, const void* rot_dev, const void* q_dev,
@@ -178,20 +251,22 @@ iq_status iq_decode_step(const iq_cache* cache, const void* rot_dev, const void*
                          int32_t max_pages_per_seq, const int32_t* seq_lens_dev, int32_t max_seq_len,
                          float softmax_scale, float* out_dev, void* workspace_dev,
                          size_t workspace_bytes, hipStream_t stream) {
-  if (!cache_ok(cache) || !rot_dev || !q_dev || !dtype_ok(q_dtype) || !k_new_dev || !v_new_dev ||
-      !dtype_ok(kv_dtype) || batch < 1 || batch > 65535 || n_q_heads < 1 || !block_table_dev ||
-      max_pages_per_seq < 1 || !seq_lens_dev || max_seq_len < 0 || !out_dev || !workspace_dev)
-    return IQ_ERR_INVALID_ARG;
-  if (n_q_heads % cache->n_kv_heads != 0) return IQ_ERR_INVALID_ARG;
-  if ((int64_t)max_seq_len > (int64_t)max_pages_per_seq * IQ_PAGE_TOKENS) return IQ_ERR_INVALID_ARG;
-  if (cache->n_kv_heads > 65535) return IQ_ERR_UNSUPPORTED;
-  if (n_q_heads / cache->n_kv_heads > IQ_MAX_GROUP) return IQ_ERR_UNSUPPORTED;
-  const iq::DecodePlan plan = iq::plan_decode(batch, cache->n_kv_heads, max_seq_len, device_cu_count());
-  if (workspace_bytes < iq::decode_workspace_bytes(batch, n_q_heads, plan)) return IQ_ERR_WORKSPACE;
-  return launch_status(iq::launch_decode(view(cache), reinterpret_cast<const float*>(rot_dev), q_dev,
-                                         q_dtype, batch, n_q_heads, block_table_dev, max_pages_per_seq,
-                                         seq_lens_dev, plan, resolve_scale(softmax_scale), out_dev,
-                                         workspace_dev, k_new_dev, v_new_dev, kv_dtype, stream));
+  if (!k_new_dev) return IQ_ERR_INVALID_ARG;
+  return decode_call(cache, rot_dev, q_dev, q_dtype, batch, n_q_heads, k_new_dev, v_new_dev, kv_dtype,
+                     block_table_dev, max_pages_per_seq, seq_lens_dev, max_seq_len, softmax_scale, out_dev,
+                     workspace_dev, workspace_bytes, nullptr, stream);
+}
+
+iq_status iq_decode_step_ex(const iq_cache* cache, const void* rot_dev, const void* q_dev,
+                            int32_t q_dtype, int32_t batch, int32_t n_q_heads, const void* k_new_dev,
+                            const void* v_new_dev, int32_t kv_dtype, const int32_t* block_table_dev,
+                            int32_t max_pages_per_seq, const int32_t* seq_lens_dev, int32_t max_seq_len,
+                            float softmax_scale, float* out_dev, void* workspace_dev,
+                            size_t workspace_bytes, const iq_decode_options* options, hipStream_t stream) {
+  if (!k_new_dev) return IQ_ERR_INVALID_ARG;
+  return decode_call(cache, rot_dev, q_dev, q_dtype, batch, n_q_heads, k_new_dev, v_new_dev, kv_dtype,
+                     block_table_dev, max_pages_per_seq, seq_lens_dev, max_seq_len, softmax_scale, out_dev,
+                     workspace_dev, workspace_bytes, options, stream);
 }
 
 iq_status iq_dense_append(const iq_dense_cache* cache, const void* k_dev, const void* v_dev,
@@ -271,14 +346,16 @@ size_t iq_prefill_workspace_bytes(int32_t n_q, int32_t n_q_heads, int32_t n_kv_h
   return iq::prefill_workspace_bytes(n_q, n_q_heads, plan);
 }
 
-iq_status iq_prefill_attention(const iq_cache* cache, const void* rot_dev, const void* q_dev,
-                               int32_t q_dtype, int32_t n_q, int32_t n_q_heads, int32_t q_start_pos,
-                               const int32_t* block_table_dev, int32_t max_pages, float softmax_scale,
-                               float* out_dev, void* workspace_dev, size_t workspace_bytes,
-                               hipStream_t stream) {
+iq_status iq_prefill_attention_ex(const iq_cache* cache, const void* rot_dev, const void* q_dev,
+                                  int32_t q_dtype, int32_t n_q, int32_t n_q_heads, int32_t q_start_pos,
+                                  const int32_t* block_table_dev, int32_t max_pages, float softmax_scale,
+                                  float* out_dev, void* workspace_dev, size_t workspace_bytes,
+                                  const iq_prefill_options* options, hipStream_t stream) {
   if (!cache_ok(cache) || !rot_dev || !q_dev || !dtype_ok(q_dtype) || n_q < 0 || n_q_heads < 1 ||
       q_start_pos < 0 || !block_table_dev || max_pages < 1 || !out_dev)
     return IQ_ERR_INVALID_ARG;
+  const int waves = options ? options->waves : 0;
+  if (waves != 0 && waves != 4 && waves != 8) return IQ_ERR_INVALID_ARG;
   if (n_q_heads % cache->n_kv_heads != 0) return IQ_ERR_INVALID_ARG;
   if ((int64_t)q_start_pos + n_q > (int64_t)max_pages * IQ_PAGE_TOKENS) return IQ_ERR_INVALID_ARG;
   if (n_q == 0) return IQ_OK;
@@ -286,7 +363,8 @@ iq_status iq_prefill_attention(const iq_cache* cache, const void* rot_dev, const
   if (!pow2(group) || group > 128 || cache->n_kv_heads > 65535) return IQ_ERR_UNSUPPORTED;
   if ((int64_t)q_start_pos + n_q > (int64_t)iq::kPrefillMaxPages * IQ_PAGE_TOKENS)
     return IQ_ERR_UNSUPPORTED;
-  const iq::PrefillPlan plan = iq::plan_prefill(n_q, n_q_heads, cache->n_kv_heads, q_start_pos, device_cu_count());
+  iq::PrefillPlan plan = iq::plan_prefill(n_q, n_q_heads, cache->n_kv_heads, q_start_pos, device_cu_count());
+  if (waves == 4) plan.waves = 4;
   if (plan.row_tiles > 65535) return IQ_ERR_UNSUPPORTED;
   const size_t need = iq::prefill_workspace_bytes(n_q, n_q_heads, plan);
   if (need > 0 && (!workspace_dev || workspace_bytes < need)) return IQ_ERR_WORKSPACE;
@@ -294,6 +372,16 @@ iq_status iq_prefill_attention(const iq_cache* cache, const void* rot_dev, const
                                           q_dtype, n_q, n_q_heads, q_start_pos, block_table_dev, max_pages,
                                           plan, resolve_scale(softmax_scale), out_dev, workspace_dev,
                                           stream));
+}
+
+iq_status iq_prefill_attention(const iq_cache* cache, const void* rot_dev, const void* q_dev,
+                               int32_t q_dtype, int32_t n_q, int32_t n_q_heads, int32_t q_start_pos,
+                               const int32_t* block_table_dev, int32_t max_pages, float softmax_scale,
+                               float* out_dev, void* workspace_dev, size_t workspace_bytes,
+                               hipStream_t stream) {
+  return iq_prefill_attention_ex(cache, rot_dev, q_dev, q_dtype, n_q, n_q_heads, q_start_pos, block_table_dev,
+                                 max_pages, softmax_scale, out_dev, workspace_dev, workspace_bytes, nullptr,
+                                 stream);
 }
 
 iq_status iq_prefill_attention_varlen(const iq_cache* cache, const void* rot_dev, const void* q_dev,

@@ -37,6 +37,7 @@
 // stays inside the f16 range for any norm.
 #include <math.h>
 
+#include <atomic>
 #include <type_traits>
 
 #include "iq_device.h"
@@ -67,6 +68,17 @@ struct DecodeArgs {
   // and each sequence's split count, written for the merge.
   int plan_wgs, batch;
   int32_t* n_splits;
+  // Merge workgroups in the split launch (host plan, the whole grid resident
+  // at once): a flat grid of split_wgs split workgroups, then one merge
+  // workgroup per query head.  A split workgroup counts itself in
+  // arrive[b * hkv + g] once its partial rows are visible device-wide; the
+  // merge workgroups of (b, g) wait for every non-empty split, merge, and the
+  // last of them to finish counts itself in done[] and clears both counters.
+  // Null: a merge kernel follows the split launch.
+  uint32_t* arrive;
+  uint32_t* done;
+  int split_wgs;
+  int deterministic;  // each wave takes pages w, w + W, ... of its split (no claiming)
 };
 
 // DPP controls (gfx9): shifts and rotation inside rows of 16 lanes.
@@ -458,6 +470,223 @@ __device__ __forceinline__ void rotate_queries(int group, int q_dtype, const uin
   }
 }
 
+// A store performed at device scope (it completes at the point where every
+// XCD sees it, not in this XCD's L2): partial rows read by merge workgroups
+// that may run on another XCD.
+__device__ __forceinline__ void store_agent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---- merge of split partials (one query head, 256 threads) ----
+// Thread t keeps an online merge of coordinates 4*(t%32)..+3 over the splits
+// s = t/32 (mod 8), with all of its loads issued before any result is used;
+// the eight groups then combine through LDS, and the first wave normalises and
+// rotates back: o = (H / sqrt(d)) B^T o'.
+constexpr int kMergeChunk = 16;
+
+// The rows of SO(4) block (t % 64) / 2 of kv head g, which the first wave
+// applies transposed (every thread loads one, so the load needs no branch).
+__device__ __forceinline__ void merge_rot_block(const float* __restrict__ rot_all, int g, int tid,
+                                                f4 mt[4]) {
+  const f4* src = reinterpret_cast<const f4*>(rot_all + (size_t)g * kRotFloats + ((tid & 63) >> 1) * 16);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) mt[r] = src[r];
+}
+
+// Rows row0 .. row0 + count - 1 of (m, l) and acc[128] (count >= 1) -> the
+// 128 outputs of the head at `out`.  Must be called by all 256 threads.
+template <bool ROTATE>
+__device__ __forceinline__ void merge_head(const f4 mt[4], const float* __restrict__ ws_acc,
+                                           const float* __restrict__ ws_ml, size_t row0, int count,
+                                           float* __restrict__ out, int tid) {
+  const int quad = tid & 31, grp = tid >> 5;
+  __shared__ float s_mm[8], s_ml[8];
+  __shared__ f4 s_part[8][32];
+  const float2* ml = reinterpret_cast<const float2*>(ws_ml) + row0;
+  const f4* accp = reinterpret_cast<const f4*>(ws_acc + row0 * kD) + quad;
+  float m_t = -INFINITY, l_t = 0.f;
+  f4 acc_t = {0.f, 0.f, 0.f, 0.f};
+  // splits s0, s0 + 8, ..., s0 + 8 (kMergeChunk - 1): loads first, then an
+  // online merge into (m_t, l_t, acc_t)
+  auto merge_chunk = [&](int s0) {
+    float2 mv[kMergeChunk];
+    f4 av[kMergeChunk];
+#pragma unroll
+    for (int k = 0; k < kMergeChunk; ++k) {  // rows past the end repeat the last one
+      const int sp = min(s0 + 8 * k, count - 1);
+      mv[k] = ml[sp];
+      av[k] = accp[(size_t)sp * (kD / 4)];
+    }
+    __builtin_amdgcn_sched_barrier(0);  // every load above issues before any use
+#pragma unroll
+    for (int k = 0; k < kMergeChunk; ++k)
+      if (s0 + 8 * k >= count) mv[k].x = -INFINITY;  // ... with zero weight
+    float cm = m_t;
+#pragma unroll
+    for (int k = 0; k < kMergeChunk; ++k) cm = fmaxf(cm, mv[k].x);
+    // branch-free (a branch here would sink the loads behind it)
+    const float keep = (m_t == -INFINITY) ? 0.f : fast_exp2(m_t - cm);
+    acc_t *= keep;
+    l_t *= keep;
+#pragma unroll
+    for (int k = 0; k < kMergeChunk; ++k) {
+      // an empty row's accumulator is selected away, never multiplied
+      const bool live = mv[k].x > -INFINITY;
+      const float w = live ? fast_exp2(mv[k].x - cm) : 0.f;
+      const f4 c = w * av[k];
+      acc_t[0] += live ? c[0] : 0.f;
+      acc_t[1] += live ? c[1] : 0.f;
+      acc_t[2] += live ? c[2] : 0.f;
+      acc_t[3] += live ? c[3] : 0.f;
+      l_t += w * mv[k].y;
+    }
+    m_t = cm;
+  };
+  merge_chunk(grp);  // no loop before the first chunk: its loads follow the ones above
+  for (int s0 = grp + 8 * kMergeChunk; s0 < count; s0 += 8 * kMergeChunk) merge_chunk(s0);
+  s_part[grp][quad] = acc_t;
+  if (quad == 0) {
+    s_mm[grp] = m_t;
+    s_ml[grp] = l_t;
+  }
+  __syncthreads();
+  if (tid >= 64) return;
+  // lane l owns coordinates 2l, 2l+1
+  const int lane = tid;
+  float M = -INFINITY;
+#pragma unroll
+  for (int gq = 0; gq < 8; ++gq) M = fmaxf(M, s_mm[gq]);
+  float o0 = 0.f, o1 = 0.f, Ls = 0.f;
+  if (M > -INFINITY) {
+#pragma unroll
+    for (int gq = 0; gq < 8; ++gq) {
+      const float w = (s_mm[gq] == -INFINITY) ? 0.f : fast_exp2(s_mm[gq] - M);
+      const f4 v = s_part[gq][lane >> 1];
+      o0 += w * ((lane & 1) ? v[2] : v[0]);
+      o1 += w * ((lane & 1) ? v[3] : v[1]);
+      Ls += w * s_ml[gq];
+    }
+  }
+  const float inv = (Ls > 0.f) ? 1.0f / Ls : 0.f;  // an empty sequence gives zeros
+  o0 *= inv;
+  o1 *= inv;
+  if (!ROTATE) {
+    *reinterpret_cast<float2*>(out + 2 * lane) = make_float2(o0, o1);
+    return;
+  }
+  // B^T on block lane/2: this lane holds block coordinates c0 = 2*(lane&1), c0+1.
+  const float n0 = quad_xor1(o0), n1 = quad_xor1(o1);
+  const bool odd = lane & 1;
+  const float v0 = odd ? n0 : o0, v1 = odd ? n1 : o1, v2 = odd ? o0 : n0, v3 = odd ? o1 : n1;
+  const int c0 = odd ? 2 : 0;
+  float y0 = mt[0][c0] * v0 + mt[1][c0] * v1 + mt[2][c0] * v2 + mt[3][c0] * v3;
+  float y1 = mt[0][c0 + 1] * v0 + mt[1][c0 + 1] * v1 + mt[2][c0 + 1] * v2 + mt[3][c0 + 1] * v3;
+  // Walsh-Hadamard: coordinate distance 1 in-lane, 2..64 across lanes (lane
+  // distance 1..32): a butterfly keeps y + partner on the lower lane and
+  // partner - y on the upper one.
+  {
+    const float t0 = y0 + y1, t1 = y0 - y1;
+    y0 = t0;
+    y1 = t1;
+  }
+  {
+    const float sg = (lane & 1) ? -1.0f : 1.0f;
+    y0 = fmaf(sg, y0, quad_xor1(y0));
+    y1 = fmaf(sg, y1, quad_xor1(y1));
+  }
+  {
+    const float sg = (lane & 2) ? -1.0f : 1.0f;
+    y0 = fmaf(sg, y0, quad_xor2(y0));
+    y1 = fmaf(sg, y1, quad_xor2(y1));
+  }
+  {
+    const float sg = (lane & 4) ? -1.0f : 1.0f;
+    y0 = fmaf(sg, y0, lane_xor4(y0));
+    y1 = fmaf(sg, y1, lane_xor4(y1));
+  }
+  {
+    const float sg = (lane & 8) ? -1.0f : 1.0f;
+    y0 = fmaf(sg, y0, dpp_f<kRowRor8, 0xF>(y0, y0));
+    y1 = fmaf(sg, y1, dpp_f<kRowRor8, 0xF>(y1, y1));
+  }
+  {
+    // the swap pair (A, B): (own, partner) on the lower lanes, (partner, own)
+    // on the upper ones, so both results are A + (+-1) B
+    const float sg = (lane & 16) ? -1.0f : 1.0f;
+    const u2 p0 = pair_xor16(__builtin_bit_cast(uint32_t, y0));
+    const u2 p1 = pair_xor16(__builtin_bit_cast(uint32_t, y1));
+    y0 = fmaf(sg, __builtin_bit_cast(float, (uint32_t)p0[1]), __builtin_bit_cast(float, (uint32_t)p0[0]));
+    y1 = fmaf(sg, __builtin_bit_cast(float, (uint32_t)p1[1]), __builtin_bit_cast(float, (uint32_t)p1[0]));
+  }
+  {
+    const float sg = (lane & 32) ? -1.0f : 1.0f;
+    const u2 p0 = pair_xor32(__builtin_bit_cast(uint32_t, y0));
+    const u2 p1 = pair_xor32(__builtin_bit_cast(uint32_t, y1));
+    y0 = fmaf(sg, __builtin_bit_cast(float, (uint32_t)p0[1]), __builtin_bit_cast(float, (uint32_t)p0[0]));
+    y1 = fmaf(sg, __builtin_bit_cast(float, (uint32_t)p1[1]), __builtin_bit_cast(float, (uint32_t)p1[0]));
+  }
+  const float nrm = 0.08838834764831845f;  // 1/sqrt(128)
+  *reinterpret_cast<float2*>(out + 2 * lane) = make_float2(y0 * nrm, y1 * nrm);
+}
+
+// A merge workgroup of the split launch (four waves): query head hh of the
+// group of kv head g, sequence b.  The host enables this only when the whole
+// grid can be resident at once, so the split workgroups it waits for are
+// running or done; the wait is still bounded (2^20 polls, each a memory round
+// trip: about a second), and a wait that runs out writes NaN rows instead of
+// hanging.
+constexpr uint32_t kMergeSpinLimit = 1u << 20;
+__device__ __forceinline__ void merge_workgroup(const int32_t* __restrict__ seq_lens,
+                                            const float* __restrict__ rot_all, int max_pages,
+                                            int pages_per_split, int hq, int group, int splits,
+                                            const DecodeArgs& a, int mid) {
+  const int tid = threadIdx.x;
+  const int hh = mid % group, g = (mid / group) % a.hkv, b = mid / (group * a.hkv);
+  const int h = g * group + hh;
+  float* out = a.out + ((size_t)b * hq + h) * kD;
+  f4 mt[4];
+  merge_rot_block(rot_all, g, tid, mt);  // before the wait: it does not depend on the splits
+  const int L = seq_lens[b];
+  const int n_pages = min((L + kPage - 1) / kPage, max_pages);
+  const int n_used = (n_pages + pages_per_split - 1) / pages_per_split;  // the non-empty splits
+  uint32_t* arrive = a.arrive + (size_t)b * a.hkv + g;
+  __shared__ int s_timed_out;
+  if (tid == 0) {
+    uint32_t spins = 0;
+    int timed_out = 0;
+    while (__hip_atomic_load(arrive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (uint32_t)n_used) {
+      __builtin_amdgcn_s_sleep(2);
+      if (++spins == kMergeSpinLimit) {
+        timed_out = 1;
+        break;
+      }
+    }
+    // the split workgroups' partial rows, stored device-coherent before their
+    // arrival: drop any older copies of them from this CU's and XCD's caches
+    // (all waves of the workgroup share them)
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    s_timed_out = timed_out;
+  }
+  __syncthreads();
+  if (n_used == 0 || s_timed_out) {
+    // an empty sequence gives zeros; a wait that ran out gives NaN rows
+    if (tid < 32)
+      reinterpret_cast<f4*>(out)[tid] = s_timed_out ? f4{NAN, NAN, NAN, NAN} : f4{0.f, 0.f, 0.f, 0.f};
+  } else {
+    merge_head<true>(mt, a.ws_acc, a.ws_ml, ((size_t)b * hq + h) * splits, n_used, out, tid);
+  }
+  // the last merge workgroup of (b, g) clears the counters for the next call
+  // (every split has arrived and every merge workgroup has read the count)
+  if (tid == 0) {
+    uint32_t* done = a.done + (size_t)b * a.hkv + g;
+    const uint32_t old = __hip_atomic_fetch_add(done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (old + 1 == (uint32_t)group) {
+      __hip_atomic_store(arrive, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
 // APPEND (a decode step): the current token of each sequence, at position
 // L - 1, is quantised here instead of by a separate append: the wave that
 // processes the sequence's last page quantises the token's K and V rows,
@@ -472,7 +701,7 @@ __device__ __forceinline__ void rotate_queries(int group, int q_dtype, const uin
 // Without it the host plans from the longest length alone, and the splits of
 // short sequences idle while those of the longest run.
 template <bool PACK8, int kDecWaves, bool APPEND, int BITS, bool BALANCED>
-__global__ __launch_bounds__(64 * kDecWaves, 1) void decode_split_kernel(const int32_t* __restrict__ block_table,
+__global__ __launch_bounds__(64 * kDecWaves, kDecWaves == 4 ? 2 : 1) void decode_split_kernel(const int32_t* __restrict__ block_table,
                                                                       const int32_t* __restrict__ seq_lens,
                                                                       const uint8_t* __restrict__ q_bytes,
                                                                       const float* __restrict__ rot_all,
@@ -537,9 +766,21 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void decode_split_kernel(const i
     pages_per_split = __builtin_amdgcn_readfirstlane(max(1, (pb + nbb - 1) / nbb));
     if (tid == 0 && g == 0 && split == 0) a.n_splits[b] = nbb;
   } else {
-    split = blockIdx.x;
-    g = blockIdx.y;
-    b = blockIdx.z;
+    if (a.arrive) {  // flat grid: split workgroups, then merge workgroups
+      const int id = blockIdx.x;
+      if (id >= a.split_wgs) {
+        if constexpr (kDecWaves == 4)
+          merge_workgroup(seq_lens, rot_all, max_pages, pps_arg, hq, group, splits, a, id - a.split_wgs);
+        return;
+      }
+      split = id % splits;
+      g = (id / splits) % a.hkv;
+      b = id / (splits * a.hkv);
+    } else {
+      split = blockIdx.x;
+      g = blockIdx.y;
+      b = blockIdx.z;
+    }
     pages_per_split = pps_arg;
   }
   // wave-uniform: keeps the wave's page bookkeeping in scalar registers
@@ -561,7 +802,7 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void decode_split_kernel(const i
   __shared__ uint32_t s_q[32 * 64];  // Q' operands: [kstep*8 + dword][lane]
   __shared__ int s_pages[64 * kDecWaves];  // the split's page ids
   __shared__ float s_qinv[16];
-  __shared__ float s_m[kDecWaves][16], s_l[kDecWaves][16];
+  __shared__ float s_m[kDecWaves][16], s_l[kDecWaves][16], s_wt[kDecWaves][16];
   __shared__ int s_next;  // next unclaimed page of the split (waves claim pages as they go)
   __shared__ __attribute__((aligned(16))) uint8_t s_xraw[APPEND ? 1024 : 16];  // appended K | V rows
 
@@ -624,8 +865,9 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void decode_split_kernel(const i
   // (a length beyond the block table breaks the contract; never read past it)
   const int n_pages = min((L + kPage - 1) / kPage, max_pages);
   if (pg_begin >= n_pages) {  // uniform for the workgroup
-    // an empty split still leaves its mark: zero weight in the merge
-    if (tid < group) {
+    // an empty split still leaves its mark: zero weight in the merge kernel
+    // (merge workgroups read only the non-empty splits)
+    if (!a.arrive && tid < group) {
       const size_t row = ((size_t)b * hq + (size_t)g * group + tid) * splits + split;
       a.ws_ml[2 * row] = -INFINITY;
       a.ws_ml[2 * row + 1] = 0.f;
@@ -727,6 +969,7 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void decode_split_kernel(const i
   int seq0 = 0, seq1 = 1, issued = 2;
   int head = 0;
   bool pool_open = true;
+  int next_fixed = wave + 2 * kDecWaves;  // deterministic: the wave's next page of the pool
   while (head == 0 ? have0 : have1) {
     uint8_t* slot = s_ring[wave][head];
     const int seq_h = head == 0 ? seq0 : seq1;
@@ -743,9 +986,14 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void decode_split_kernel(const i
     // failed claim ends the stream)
     int claim = n_pool;
     if (pool_open) {
-      int c = 0;
-      if (lane == 0) c = atomicAdd(&s_next, 1);
-      claim = __builtin_amdgcn_readfirstlane(c);
+      if (a.deterministic) {
+        claim = next_fixed;
+        next_fixed += kDecWaves;
+      } else {
+        int c = 0;
+        if (lane == 0) c = atomicAdd(&s_next, 1);
+        claim = __builtin_amdgcn_readfirstlane(c);
+      }
     }
     const bool got = claim < n_pool;
     pool_open = got;
@@ -795,71 +1043,77 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void decode_split_kernel(const i
   if (PACK8) l_col += dpp_f<kRowRor8, 0xF>(l_col, l_col);
   l_col = sum_xor32(sum_xor16(l_col));
   const float fin = __builtin_amdgcn_ldexpf(a.out_factor, -st.rho_e);
-  // The wave's own two slots hold its accumulator now (all its loads have
-  // landed and its reads of them are done): values 0-15 in slot 0, 16-31 in
-  // slot 1.
-  static_assert(kSlotBytes >= 16 * 64 * 4, "a slot holds half an accumulator");
+  // The wave's own two slots (contiguous) hold its accumulator now (all its
+  // loads have landed and its reads of them are done), row-major [head]
+  // [coordinate] with rows of kAccStride floats: padded so that the f4
+  // writes of the 16 head columns fall on distinct banks.
+  constexpr int kAccStride = 132;
+  static_assert(2 * kSlotBytes >= 16 * kAccStride * 4, "two slots hold an accumulator");
   __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-  float* acc_lo = reinterpret_cast<float*>(s_ring[wave][0]);
-  float* acc_hi = reinterpret_cast<float*>(s_ring[wave][1]);
+  float* const acc_own = reinterpret_cast<float*>(s_ring[wave][0]);
 #pragma unroll
-  for (int k = 0; k < 32; ++k)
-    (k < 16 ? acc_lo : acc_hi)[(k & 15) * 64 + lane] = st.acc[k >> 2][k & 3] * fin;
+  for (int m = 0; m < 8; ++m)
+    *reinterpret_cast<f4*>(acc_own + col * kAccStride + 32 * jq + 4 * m) = st.acc[m] * fin;
   if (jq == 0) {
     s_m[wave][col] = st.m_run;
     s_l[wave][col] = l_col;
   }
   __syncthreads();
-  {
-    // this thread merges values V w .. V w + V - 1 of `lane` (coordinates
-    // 32 jq + k), V = 32 / waves
-    constexpr int V = 32 / kDecWaves;
+  // Per head: the largest wave maximum, each wave's weight relative to it,
+  // and the (m, l) of the partial row.
+  const size_t row0 = ((size_t)b * hq + (size_t)g * group) * splits + split;  // head h: + h * splits
+  if (tid < group) {
     float mw[kDecWaves], M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kDecWaves; ++w) {
-      mw[w] = s_m[w][col];
+      mw[w] = s_m[w][tid];
       M = fmaxf(M, mw[w]);
     }
-    float wt[kDecWaves], Ls = 0.f;
+    float Ls = 0.f;
 #pragma unroll
     for (int w = 0; w < kDecWaves; ++w) {
-      wt[w] = (mw[w] == -INFINITY) ? 0.f : fast_exp2(mw[w] - M);
-      Ls += wt[w] * s_l[w][col];
+      const float wt = (mw[w] == -INFINITY) ? 0.f : fast_exp2(mw[w] - M);
+      s_wt[w][tid] = wt;
+      Ls += wt * s_l[w][tid];
     }
-    if (col < group) {
-      const size_t row = ((size_t)b * hq + (size_t)g * group + col) * splits + split;
-#pragma unroll
-      for (int v4 = 0; v4 < V / 4; ++v4) {
-        f4 o;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int k = V * wave + 4 * v4 + r;  // value index; slot 0 holds 0-15, slot 1 16-31
-          float sum = 0.f;
-#pragma unroll
-          for (int w = 0; w < kDecWaves; ++w) {
-            const float* wacc = reinterpret_cast<const float*>(s_ring[w][k < 16 ? 0 : 1]);
-            sum += wt[w] * wacc[(k & 15) * 64 + lane];
-          }
-          o[r] = sum;
-        }
-        *reinterpret_cast<f4*>(a.ws_acc + row * kD + 32 * jq + V * wave + 4 * v4) = o;
-      }
-      if (jq == 0 && wave == 0) {
-        a.ws_ml[2 * row] = M;
-        a.ws_ml[2 * row + 1] = Ls;
-      }
+    float* dst = a.ws_ml + 2 * (row0 + (size_t)tid * splits);
+    if (a.arrive) {
+      store_agent(dst, M);
+      store_agent(dst + 1, Ls);
+    } else {
+      dst[0] = M;
+      dst[1] = Ls;
     }
+  }
+  __syncthreads();
+  // Value v = coordinate v % 128 of head v / 128: the 64 lanes of a wave
+  // write 64 consecutive coordinates of one row (256 contiguous bytes).
+  for (int v = tid; v < group * kD; v += 64 * kDecWaves) {
+    const int h = v >> 7, c = v & (kD - 1);
+    float sum = 0.f;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w)
+      sum += s_wt[w][h] * reinterpret_cast<const float*>(s_ring[w][0])[h * kAccStride + c];
+    float* dst = a.ws_acc + (row0 + (size_t)h * splits) * kD + c;
+    if (a.arrive) store_agent(dst, sum);
+    else *dst = sum;
+  }
+  if (a.arrive) {
+    // The partial rows were stored device-coherent: once every wave has them
+    // acknowledged, count the workgroup in.  (A release fence at device scope
+    // would also write back this XCD's L2, which here took several
+    // microseconds per wave.)
+    __builtin_amdgcn_s_waitcnt(wait_vm(0));
+    __syncthreads();
+    if (tid == 0)
+      __hip_atomic_fetch_add(&a.arrive[(size_t)b * a.hkv + g], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
 // One workgroup per (query head, sequence): merge the split partials,
-// normalise, and rotate back: o = (H / sqrt(d)) B^T o'.  Thread t keeps an
-// online merge of coordinates 4*(t%32)..+3 over the splits s = t/32 (mod 8),
-// with all of its loads issued before any result is used; the eight groups
-// then combine through LDS.
-// ROTATE = false: the partials are already in the original space (the
-// uncompressed baseline); the merge only normalises.
-constexpr int kMergeChunk = 16;
+// normalise, and rotate back (merge_head).  ROTATE = false: the partials are
+// already in the original space (the uncompressed baseline); the merge only
+// normalises.
 template <bool ROTATE>
 __global__ __launch_bounds__(256, 1) void decode_merge_kernel(const float* __restrict__ rot_all,
                                                            const float* __restrict__ ws_acc,
@@ -872,149 +1126,12 @@ __global__ __launch_bounds__(256, 1) void decode_merge_kernel(const float* __res
   // l = 0), so no length is needed here; zero-weight rows never touch the sums.
   // (A sequence's first merge chunk always exists: count >= 1.)
   const int hq = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  const int quad = tid & 31, grp = tid >> 5;
-  __shared__ float s_m[8], s_l[8];
-  __shared__ f4 s_part[8][32];
   const size_t row0 = ((size_t)b * hq_n + hq) * splits;
   // rows hold `splits` slots; a balanced plan used the first n_splits[b]
   const int count = n_splits ? n_splits[b] : splits;
-  const float2* ml = reinterpret_cast<const float2*>(ws_ml) + row0;
-  const f4* accp = reinterpret_cast<const f4*>(ws_acc + row0 * kD) + quad;
-
-  // this lane's rotation block (wave 0 applies B^T); every thread loads one
-  // so that no branch separates these loads from the others
   f4 mt[4];
-  if (ROTATE) {
-    const f4* src = reinterpret_cast<const f4*>(rot_all + (size_t)(hq / group) * kRotFloats +
-                                                 ((tid & 63) >> 1) * 16);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) mt[r] = src[r];
-  }
-  float m_t = -INFINITY, l_t = 0.f;
-  f4 acc_t = {0.f, 0.f, 0.f, 0.f};
-  // splits s0, s0 + 8, ..., s0 + 8 (kMergeChunk - 1): loads first, then an
-  // online merge into (m_t, l_t, acc_t)
-  auto merge_chunk = [&](int s0) {
-    float2 mv[kMergeChunk];
-    f4 av[kMergeChunk];
-#pragma unroll
-    for (int k = 0; k < kMergeChunk; ++k) {  // rows past the end repeat the last one
-      const int s = min(s0 + 8 * k, count - 1);
-      mv[k] = ml[s];
-      av[k] = accp[(size_t)s * (kD / 4)];
-    }
-    __builtin_amdgcn_sched_barrier(0);  // every load above issues before any use
-#pragma unroll
-    for (int k = 0; k < kMergeChunk; ++k)
-      if (s0 + 8 * k >= count) mv[k].x = -INFINITY;  // ... with zero weight
-    float cm = m_t;
-#pragma unroll
-    for (int k = 0; k < kMergeChunk; ++k) cm = fmaxf(cm, mv[k].x);
-    // branch-free (a branch here would sink the loads behind it)
-    const float keep = (m_t == -INFINITY) ? 0.f : fast_exp2(m_t - cm);
-    acc_t *= keep;
-    l_t *= keep;
-#pragma unroll
-    for (int k = 0; k < kMergeChunk; ++k) {
-      // an empty row's accumulator is selected away, never multiplied
-      const bool live = mv[k].x > -INFINITY;
-      const float w = live ? fast_exp2(mv[k].x - cm) : 0.f;
-      const f4 c = w * av[k];
-      acc_t[0] += live ? c[0] : 0.f;
-      acc_t[1] += live ? c[1] : 0.f;
-      acc_t[2] += live ? c[2] : 0.f;
-      acc_t[3] += live ? c[3] : 0.f;
-      l_t += w * mv[k].y;
-    }
-    m_t = cm;
-  };
-  merge_chunk(grp);  // no loop before the first chunk: its loads follow the ones above
-  for (int s0 = grp + 8 * kMergeChunk; s0 < count; s0 += 8 * kMergeChunk) merge_chunk(s0);
-  s_part[grp][quad] = acc_t;
-  if (quad == 0) {
-    s_m[grp] = m_t;
-    s_l[grp] = l_t;
-  }
-  __syncthreads();
-  if (tid >= 64) return;
-  // lane l owns coordinates 2l, 2l+1
-  const int lane = tid;
-  float M = -INFINITY;
-#pragma unroll
-  for (int gq = 0; gq < 8; ++gq) M = fmaxf(M, s_m[gq]);
-  float o0 = 0.f, o1 = 0.f, Ls = 0.f;
-  if (M > -INFINITY) {
-#pragma unroll
-    for (int gq = 0; gq < 8; ++gq) {
-      const float w = (s_m[gq] == -INFINITY) ? 0.f : fast_exp2(s_m[gq] - M);
-      const f4 v = s_part[gq][lane >> 1];
-      o0 += w * ((lane & 1) ? v[2] : v[0]);
-      o1 += w * ((lane & 1) ? v[3] : v[1]);
-      Ls += w * s_l[gq];
-    }
-  }
-  const float inv = (Ls > 0.f) ? 1.0f / Ls : 0.f;  // an empty sequence gives zeros
-  o0 *= inv;
-  o1 *= inv;
-  if (!ROTATE) {
-    float* out = out_all + ((size_t)b * hq_n + hq) * kD;
-    *reinterpret_cast<float2*>(out + 2 * lane) = make_float2(o0, o1);
-    return;
-  }
-  // B^T on block lane/2: this lane holds block coordinates c0 = 2*(lane&1), c0+1.
-  const float n0 = quad_xor1(o0), n1 = quad_xor1(o1);
-  const bool odd = lane & 1;
-  const float v0 = odd ? n0 : o0, v1 = odd ? n1 : o1, v2 = odd ? o0 : n0, v3 = odd ? o1 : n1;
-  const int c0 = odd ? 2 : 0;
-  float y0 = mt[0][c0] * v0 + mt[1][c0] * v1 + mt[2][c0] * v2 + mt[3][c0] * v3;
-  float y1 = mt[0][c0 + 1] * v0 + mt[1][c0 + 1] * v1 + mt[2][c0 + 1] * v2 + mt[3][c0 + 1] * v3;
-  // Walsh-Hadamard: coordinate distance 1 in-lane, 2..64 across lanes (lane
-  // distance 1..32): a butterfly keeps y + partner on the lower lane and
-  // partner - y on the upper one.
-  {
-    const float t0 = y0 + y1, t1 = y0 - y1;
-    y0 = t0;
-    y1 = t1;
-  }
-  {
-    const float s = (lane & 1) ? -1.0f : 1.0f;
-    y0 = fmaf(s, y0, quad_xor1(y0));
-    y1 = fmaf(s, y1, quad_xor1(y1));
-  }
-  {
-    const float s = (lane & 2) ? -1.0f : 1.0f;
-    y0 = fmaf(s, y0, quad_xor2(y0));
-    y1 = fmaf(s, y1, quad_xor2(y1));
-  }
-  {
-    const float s = (lane & 4) ? -1.0f : 1.0f;
-    y0 = fmaf(s, y0, lane_xor4(y0));
-    y1 = fmaf(s, y1, lane_xor4(y1));
-  }
-  {
-    const float s = (lane & 8) ? -1.0f : 1.0f;
-    y0 = fmaf(s, y0, dpp_f<kRowRor8, 0xF>(y0, y0));
-    y1 = fmaf(s, y1, dpp_f<kRowRor8, 0xF>(y1, y1));
-  }
-  {
-    // the swap pair (A, B): (own, partner) on the lower lanes, (partner, own)
-    // on the upper ones, so both results are A + (+-1) B
-    const float s = (lane & 16) ? -1.0f : 1.0f;
-    const u2 p0 = pair_xor16(__builtin_bit_cast(uint32_t, y0));
-    const u2 p1 = pair_xor16(__builtin_bit_cast(uint32_t, y1));
-    y0 = fmaf(s, __builtin_bit_cast(float, (uint32_t)p0[1]), __builtin_bit_cast(float, (uint32_t)p0[0]));
-    y1 = fmaf(s, __builtin_bit_cast(float, (uint32_t)p1[1]), __builtin_bit_cast(float, (uint32_t)p1[0]));
-  }
-  {
-    const float s = (lane & 32) ? -1.0f : 1.0f;
-    const u2 p0 = pair_xor32(__builtin_bit_cast(uint32_t, y0));
-    const u2 p1 = pair_xor32(__builtin_bit_cast(uint32_t, y1));
-    y0 = fmaf(s, __builtin_bit_cast(float, (uint32_t)p0[1]), __builtin_bit_cast(float, (uint32_t)p0[0]));
-    y1 = fmaf(s, __builtin_bit_cast(float, (uint32_t)p1[1]), __builtin_bit_cast(float, (uint32_t)p1[0]));
-  }
-  const float nrm = 0.08838834764831845f;  // 1/sqrt(128)
-  float* out = out_all + ((size_t)b * hq_n + hq) * kD;
-  *reinterpret_cast<float2*>(out + 2 * lane) = make_float2(y0 * nrm, y1 * nrm);
+  if (ROTATE) merge_rot_block(rot_all, hq / group, tid, mt);
+  merge_head<ROTATE>(mt, ws_acc, ws_ml, row0, count, out_all + ((size_t)b * hq_n + hq) * kD, tid);
 }
 
 // Split planning: one workgroup per CU.  Few pages per kv head (short or
@@ -1025,31 +1142,21 @@ __global__ __launch_bounds__(256, 1) void decode_merge_kernel(const float* __res
 // pages dynamically, so the waves of a CU finish together.  One workgroup
 // per CU also keeps two workgroups from competing for the same SIMDs (the
 // older would win the issue arbitration and the younger finish late).
-// Ragged batches may ask for more rounds of shorter splits
-// (IQ_DECODE_ROUNDS), which the hardware dispatcher balances; IQ_DECODE_WAVES
-// (4 or 8) overrides the waves per workgroup.
-DecodePlan plan_decode(int batch, int hkv, int max_seq_len, int num_cus) {
+// The caller may fix the waves, the pages per split of the host plan, the
+// workgroups per CU planned for (more rounds of shorter splits, which the
+// hardware dispatcher balances) and the plan kind.
+DecodePlan plan_decode(int batch, int hkv, int max_seq_len, int num_cus, const DecodeOptions& o) {
   const int max_pages = max(1, (max_seq_len + kPage - 1) / kPage);
   const long long units = (long long)max(1, batch) * max(1, hkv);
   const long long cus = max(1, num_cus);
   DecodePlan p{};
   p.waves = (units * max_pages <= cus * 4 * 2) ? 4 : 8;
-  if (const char* env = getenv("IQ_DECODE_WAVES")) {
-    const int v = atoi(env);
-    if (v == 4 || v == 8) p.waves = v;
-  }
-  long long rounds = 1;
-  if (const char* env = getenv("IQ_DECODE_ROUNDS")) {
-    const long long v = atoll(env);
-    if (v > 0) rounds = v;
-  }
+  if (o.waves == 4 || o.waves == 8) p.waves = o.waves;
+  const long long rounds = o.rounds > 0 ? o.rounds : 1;
   long long splits = (rounds * cus + units - 1) / units;
   if (splits > max_pages) splits = max_pages;
   long long pps = (max_pages + splits - 1) / splits;
-  if (const char* env = getenv("IQ_DECODE_PAGES_PER_SPLIT")) {
-    const long long v = atoll(env);
-    if (v > 0) pps = v;
-  }
+  if (o.pages_per_split > 0) pps = o.pages_per_split;
   const long long cap = 64LL * p.waves;  // page ids staged per split
   if (pps > cap) pps = cap;
   if (pps < 1) pps = 1;
@@ -1058,13 +1165,16 @@ DecodePlan plan_decode(int batch, int hkv, int max_seq_len, int num_cus) {
   p.balanced = 0;
   p.grid_x = p.splits;
   p.plan_wgs = 0;
+  p.merge = o.merge;
+  p.deterministic = o.deterministic ? 1 : 0;
+  p.cus = (int)cus;
   // Several sequences: the device balances the pages (their lengths are known
   // only there).  The plan's G workgroups hold at most `cap` pages each; rows
   // of the workspace get ceil(G / Hkv) slots, the most one sequence can take
   // (its pages are at most total / Hkv), and the grid G + B Hkv workgroups
   // (rounding up every sequence's count adds at most one per kv head).
   bool balanced = batch > 1 && batch <= 64;
-  if (const char* env = getenv("IQ_DECODE_BALANCED")) balanced = balanced && atoi(env) != 0;
+  if (o.plan == 1) balanced = false;
   if (balanced) {
     long long G = rounds * cus;
     const long long need = (units * max_pages + cap - 1) / cap;
@@ -1083,9 +1193,59 @@ DecodePlan plan_decode(int batch, int hkv, int max_seq_len, int num_cus) {
 
 size_t decode_workspace_bytes(int batch, int hq, const DecodePlan& plan) {
   const size_t rows = (size_t)batch * hq * plan.splits;
-  // + one split count per sequence for a balanced plan
-  return rows * kD * sizeof(float) + rows * 2 * sizeof(float) +
+  // counters, the partial rows, and one split count per sequence for a
+  // balanced plan
+  return kWsCounterBytes + rows * kD * sizeof(float) + rows * 2 * sizeof(float) +
          (plan.balanced ? (size_t)batch * sizeof(int32_t) : 0);
+}
+
+namespace {
+
+// Workgroups of one split-kernel instantiation that a CU holds at once (LDS,
+// registers and waves), from the runtime's occupancy calculator; cached.
+template <bool P8, int W, bool AP, int B, bool BAL>
+int split_blocks_per_cu() {
+  static std::atomic<int> cached{-1};
+  int n = cached.load(std::memory_order_relaxed);
+  if (n < 0) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_split_kernel<P8, W, AP, B, BAL>, 64 * W, 0) !=
+        hipSuccess)
+      n = 0;
+    cached.store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+// split_blocks_per_cu of the instantiation a call launches.
+int split_occupancy(bool pack8, int waves, bool append, int bits, bool balanced) {
+#define IQ_OCC_B(P8, W, AP, B) (balanced ? split_blocks_per_cu<P8, W, AP, B, true>() : split_blocks_per_cu<P8, W, AP, B, false>())
+#define IQ_OCC_W(P8, W, AP) (bits == 4 ? IQ_OCC_B(P8, W, AP, 4) : IQ_OCC_B(P8, W, AP, 3))
+#define IQ_OCC_A(P8, W) (append ? IQ_OCC_W(P8, W, true) : IQ_OCC_W(P8, W, false))
+#define IQ_OCC_P(W) (pack8 ? IQ_OCC_A(true, W) : IQ_OCC_A(false, W))
+  return waves == 4 ? IQ_OCC_P(4) : IQ_OCC_P(8);
+#undef IQ_OCC_P
+#undef IQ_OCC_A
+#undef IQ_OCC_W
+#undef IQ_OCC_B
+}
+
+}  // namespace
+
+// Merge workgroups join the split launch (host plan, four waves) when the
+// caller asks for it and the runtime's occupancy calculator says every
+// workgroup of the grid can be resident at once, so that a merge workgroup
+// never waits for a split workgroup that has no CU.  It is not the default:
+// the split workgroups then publish their partial rows with device-scope
+// stores (the merge workgroups may sit on another XCD, whose L2 does not see
+// this one's), and at the 32K single-sequence workload those stores took
+// longer to complete than the launch gap before a merge kernel.
+bool decode_fused_merge(const DecodePlan& plan, int batch, int hkv, int hq, int bits, bool append) {
+  if (plan.merge != 1 || plan.balanced || plan.waves != 4 || (long long)batch * hkv > kMaxCounterUnits)
+    return false;
+  const long long split_wgs = (long long)plan.splits * hkv * batch;
+  const long long merge_wgs = (long long)batch * hq;
+  const int bpc = split_occupancy(hq / hkv <= 8, 4, append, bits, false);
+  return bpc > 0 && split_wgs + merge_wgs <= (long long)bpc * plan.cus;
 }
 
 hipError_t launch_decode(const CacheView& c, const float* rot, const void* q, int q_dtype, int batch,
@@ -1115,18 +1275,37 @@ hipError_t launch_decode(const CacheView& c, const float* rot, const void* q, in
   a.score_factor = (float)((double)softmax_scale * log2e / (128.0 * alpha));
   a.out_factor = (float)(1.0 / (sqrt(128.0) * alpha));
   const size_t rows = (size_t)batch * hq * plan.splits;
-  a.ws_acc = reinterpret_cast<float*>(workspace);
+  uint32_t* counters = reinterpret_cast<uint32_t*>(workspace);
+  a.ws_acc = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + kWsCounterBytes);
   a.ws_ml = a.ws_acc + rows * kD;
   a.out = out;
   a.plan_wgs = plan.plan_wgs;
   a.batch = batch;
   a.n_splits = plan.balanced ? reinterpret_cast<int32_t*>(a.ws_ml + rows * 2) : nullptr;
+  a.deterministic = plan.deterministic;
+  a.arrive = nullptr;
+  a.done = nullptr;
+  a.split_wgs = 0;
   const uint8_t* qb = static_cast<const uint8_t*>(q);
-  const dim3 grid = plan.balanced ? dim3(plan.grid_x, 1, 1) : dim3(plan.splits, c.hkv, batch);
-#define IQ_SPLIT_K(P8, W, AP, B, BAL)                                                             \
-  hipLaunchKernelGGL((decode_split_kernel<P8, W, AP, B, BAL>), grid, dim3(64 * W), 0, stream,      \
-                     block_table, seq_lens, qb, rot, a.max_pages, a.pages_per_split, a.hq, a.group, \
-                     a.q_dtype, a.splits, a)
+  const bool append = k_new != nullptr;
+  const long long split_wgs = (long long)plan.splits * c.hkv * batch;
+  const long long merge_wgs = (long long)batch * hq;
+  hipError_t e = hipSuccess;
+  const bool fused = decode_fused_merge(plan, batch, c.hkv, hq, c.bits, append);
+  if (fused) {
+    a.arrive = counters;
+    a.done = counters + kMaxCounterUnits;
+    a.split_wgs = (int)split_wgs;
+  }
+  auto launch = [&](auto kernel, int waves) {
+    const dim3 grid = plan.balanced ? dim3(plan.grid_x, 1, 1)
+                      : fused       ? dim3((unsigned)(split_wgs + merge_wgs), 1, 1)
+                                    : dim3(plan.splits, c.hkv, batch);
+    hipLaunchKernelGGL(kernel, grid, dim3(64 * waves), 0, stream, block_table, seq_lens, qb, rot,
+                       a.max_pages, a.pages_per_split, a.hq, a.group, a.q_dtype, a.splits, a);
+    e = hipGetLastError();
+  };
+#define IQ_SPLIT_K(P8, W, AP, B, BAL) launch(decode_split_kernel<P8, W, AP, B, BAL>, W)
 #define IQ_SPLIT(P8, W, AP, B)                    \
   if (plan.balanced) IQ_SPLIT_K(P8, W, AP, B, true); \
   else IQ_SPLIT_K(P8, W, AP, B, false)
@@ -1136,7 +1315,6 @@ hipError_t launch_decode(const CacheView& c, const float* rot, const void* q, in
 #define IQ_SPLIT_W(P8, AP)              \
   if (plan.waves == 4) { IQ_SPLIT_B(P8, 4, AP); } \
   else { IQ_SPLIT_B(P8, 8, AP); }
-  const bool append = k_new != nullptr;
   if (a.group <= 8) {
     if (append) { IQ_SPLIT_W(true, true); }
     else { IQ_SPLIT_W(true, false); }
@@ -1148,8 +1326,7 @@ hipError_t launch_decode(const CacheView& c, const float* rot, const void* q, in
 #undef IQ_SPLIT_B
 #undef IQ_SPLIT
 #undef IQ_SPLIT_K
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || fused) return e;
   return launch_decode_merge(true, rot, a.ws_acc, a.ws_ml, plan.splits, batch, hq, a.group, a.n_splits,
                              out, stream);
 }

@@ -499,7 +499,8 @@ hipError_t launch_dense_decode(const DenseCacheView& c, const void* q, int batch
   a.score_factor = (float)((double)softmax_scale * 1.4426950408889634 * (fp8 ? (double)c.k_scale : 1.0));
   a.v_scale = fp8 ? c.v_scale : 1.0f;
   const size_t rows = (size_t)batch * hq * plan.splits;
-  a.ws_acc = reinterpret_cast<float*>(workspace);
+  // the partials follow the counter region every decode workspace starts with
+  a.ws_acc = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + kWsCounterBytes);
   a.ws_ml = a.ws_acc + rows * kD;
   const int group = hq / c.hkv;
   const dim3 grid(plan.splits, c.hkv, batch);

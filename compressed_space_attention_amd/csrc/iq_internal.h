@@ -45,6 +45,17 @@ hipError_t launch_quantize_append(const CacheView& c, const float* rot, const vo
                                   const int32_t* pos, const int32_t* block_table, int max_pages,
                                   hipStream_t stream);
 
+// Caller choices for one decode call (iq_decode_options in the C ABI); zero
+// fields leave the choice to the planner.
+struct DecodeOptions {
+  int waves;            // 0, 4 or 8 waves per workgroup
+  int pages_per_split;  // 0 or pages per split of the host plan
+  int rounds;           // 0 or workgroups per CU the plan is made for
+  int plan;             // 0 auto, 1 host plan, 2 device-balanced plan
+  int merge;            // 0 auto (a merge kernel), 1 merge workgroups in the split launch, 2 a merge kernel
+  int deterministic;    // nonzero: each wave takes a fixed share of its split's pages
+};
+
 struct DecodePlan {
   int splits;           // workgroups per (sequence, kv head); balanced: slots per workspace row
   int pages_per_split;
@@ -52,9 +63,21 @@ struct DecodePlan {
   int balanced;         // several sequences: the split plan is made on the device
   int grid_x;           // balanced: workgroups launched (the plan's plus spare ones)
   int plan_wgs;         // balanced: workgroups the pages are spread over
+  int merge;            // as DecodeOptions::merge (0: decided at launch)
+  int deterministic;
+  int cus;              // compute units planned for
 };
-DecodePlan plan_decode(int batch, int hkv, int max_seq_len, int num_cus);
+DecodePlan plan_decode(int batch, int hkv, int max_seq_len, int num_cus, const DecodeOptions& o);
 size_t decode_workspace_bytes(int batch, int hq, const DecodePlan& plan);
+// Whether a call with this plan merges in the split launch (else a merge kernel follows).
+bool decode_fused_merge(const DecodePlan& plan, int batch, int hkv, int hq, int bits, bool append);
+
+// Decode workspace: arrival counters first (a fixed region, so that any later
+// call finds them where the last one left them: zero), then the split
+// partials.  The counters must be zero before a buffer's first use; every
+// call leaves them zero.
+constexpr size_t kWsCounterBytes = 16384;
+constexpr int kMaxCounterUnits = (int)(kWsCounterBytes / 8);  // (sequence, kv head) pairs
 
 // k_new / v_new non-null: a decode step, which first appends each sequence's
 // token at position seq_lens[b] - 1 (rows [B][Hkv][128] of kv_dtype).
@@ -107,6 +130,7 @@ constexpr int kPrefillMaxPages = 4096;
 struct PrefillPlan {
   int row_tiles;        // workgroups per kv head along the query rows
   int kv_splits;        // workgroups along the key range
+  int waves;            // 8: eight waves of 16 rows; 4: four waves of 32 rows
 };
 PrefillPlan plan_prefill(int n_q, int hq, int hkv, int q_start, int num_cus);
 size_t prefill_workspace_bytes(int n_q, int hq, const PrefillPlan& plan);

@@ -595,6 +595,7 @@ PrefillPlan plan_prefill(int n_q, int hq, int hkv, int q_start, int num_cus) {
   const int qpt = kRowsPerTile / group;
   p.row_tiles = (n_q + qpt - 1) / qpt;
   p.kv_splits = 1;
+  p.waves = 8;
   return p;
 }
 
@@ -644,8 +645,7 @@ hipError_t launch_prefill_varlen(const CacheView& c, const float* rot, const voi
   a.score_factor = (float)((double)softmax_scale * log2e / (128.0 * alpha));
   a.out_factor = (float)(1.0 / (sqrt(128.0) * alpha));
   a.out = out;
-  int rb = 1;
-  if (const char* env = getenv("IQ_PREFILL_WAVES")) rb = atoi(env) == 4 ? 2 : 1;
+  const int rb = plan.waves == 4 ? 2 : 1;  // 16-row blocks per wave
   const dim3 grid(c.hkv, plan.row_tiles, batch);
 #define IQ_PREFILL(RB, B) \
   hipLaunchKernelGGL((prefill_kernel<RB, B>), grid, dim3(64 * pf_waves<RB>()), 0, stream, a)

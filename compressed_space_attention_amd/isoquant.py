@@ -47,6 +47,40 @@ class IqCacheStruct(ctypes.Structure):
 
 
 IQ_KV_BF16, IQ_KV_FP8_E4M3 = 0, 1
+IQ_PLAN_AUTO, IQ_PLAN_HOST, IQ_PLAN_BALANCED = 0, 1, 2
+IQ_MERGE_AUTO, IQ_MERGE_FUSED, IQ_MERGE_KERNEL = 0, 1, 2
+DECODE_COUNTER_BYTES = 16384
+
+
+class DecodeOptions(ctypes.Structure):
+    """iq_decode_options: zero fields leave the choice to the planner."""
+    _fields_ = [
+        ("waves", ctypes.c_int32),
+        ("pages_per_split", ctypes.c_int32),
+        ("rounds", ctypes.c_int32),
+        ("plan", ctypes.c_int32),
+        ("merge", ctypes.c_int32),
+        ("deterministic", ctypes.c_int32),
+    ]
+
+
+class DecodePlanInfo(ctypes.Structure):
+    _fields_ = [
+        ("waves", ctypes.c_int32),
+        ("splits", ctypes.c_int32),
+        ("pages_per_split", ctypes.c_int32),
+        ("balanced", ctypes.c_int32),
+        ("fused_merge", ctypes.c_int32),
+        ("workgroups", ctypes.c_int32),
+    ]
+
+
+class PrefillOptions(ctypes.Structure):
+    _fields_ = [("waves", ctypes.c_int32)]
+
+
+def _opts(options):
+    return None if options is None else ctypes.byref(options)
 
 
 class IqDenseCacheStruct(ctypes.Structure):
@@ -69,6 +103,8 @@ def _load():
     vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
     cp = ctypes.POINTER(IqCacheStruct)
     dp = ctypes.POINTER(IqDenseCacheStruct)
+    op = ctypes.POINTER(DecodeOptions)
+    pp = ctypes.POINTER(PrefillOptions)
     sigs = {
         "iq_status_string": (ctypes.c_char_p, [i32]),
         "iq_version": (i32, []),
@@ -77,9 +113,15 @@ def _load():
         "iq_rotation_init": (i32, [vp, i32, vp, sz, vp]),
         "iq_quantize_append": (i32, [cp, vp, vp, vp, i32, i32, vp, vp, vp, i32, vp]),
         "iq_decode_workspace_bytes": (sz, [i32, i32, i32, i32]),
+        "iq_decode_workspace_bytes_ex": (sz, [i32, i32, i32, i32, op]),
+        "iq_decode_describe": (i32, [i32, i32, i32, i32, i32, i32, op, ctypes.POINTER(DecodePlanInfo)]),
         "iq_decode_attention": (i32, [cp, vp, vp, i32, i32, i32, vp, i32, vp, i32, f32, vp, vp, sz, vp]),
+        "iq_decode_attention_ex": (i32, [cp, vp, vp, i32, i32, i32, vp, i32, vp, i32, f32, vp, vp, sz, op,
+                                         vp]),
         "iq_decode_step": (i32, [cp, vp, vp, i32, i32, i32, vp, vp, i32, vp, i32, vp, i32, f32, vp, vp,
                                  sz, vp]),
+        "iq_decode_step_ex": (i32, [cp, vp, vp, i32, i32, i32, vp, vp, i32, vp, i32, vp, i32, f32, vp, vp,
+                                    sz, op, vp]),
         "iq_dense_append": (i32, [dp, vp, vp, i32, i32, vp, vp, vp, i32, vp]),
         "iq_dense_decode_workspace_bytes": (sz, [i32, i32, i32, i32]),
         "iq_dense_decode_attention": (i32, [dp, vp, i32, i32, i32, vp, i32, vp, i32, f32, vp, vp, sz, vp]),
@@ -90,6 +132,7 @@ def _load():
         "iq_prefill_attention_varlen": (i32, [cp, vp, vp, i32, i32, i32, i32, vp, vp, i32, i32, vp, i32, f32,
                                               vp, vp, sz, vp]),
         "iq_prefill_attention": (i32, [cp, vp, vp, i32, i32, i32, i32, vp, i32, f32, vp, vp, sz, vp]),
+        "iq_prefill_attention_ex": (i32, [cp, vp, vp, i32, i32, i32, i32, vp, i32, f32, vp, vp, sz, pp, vp]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -101,7 +144,9 @@ def _load():
 lib = _load()
 EXPORTED = ("iq_status_string", "iq_version", "iq_codebook", "iq_rotation_bytes", "iq_rotation_init",
             "iq_quantize_append", "iq_decode_workspace_bytes", "iq_decode_attention",
-            "iq_decode_step", "iq_prefill_workspace_bytes", "iq_prefill_attention",
+            "iq_decode_step", "iq_decode_workspace_bytes_ex", "iq_decode_attention_ex", "iq_decode_step_ex",
+            "iq_decode_describe",
+            "iq_prefill_workspace_bytes", "iq_prefill_attention", "iq_prefill_attention_ex",
             "iq_prefill_attention_varlen",
             "iq_dense_append", "iq_dense_decode_workspace_bytes", "iq_dense_decode_attention",
             "iq_dense_prefill_attention",
@@ -274,11 +319,32 @@ def quantize_append(cache: PagedCache, rot: torch.Tensor, k: torch.Tensor, v: to
         block_table.shape[-1], _stream(stream)))
 
 
-def decode_workspace_bytes(batch: int, n_q_heads: int, n_kv_heads: int, max_seq_len: int) -> int:
-    return int(lib.iq_decode_workspace_bytes(batch, n_q_heads, n_kv_heads, max_seq_len))
+def decode_workspace_bytes(batch: int, n_q_heads: int, n_kv_heads: int, max_seq_len: int,
+                           options: DecodeOptions | None = None) -> int:
+    return int(lib.iq_decode_workspace_bytes_ex(batch, n_q_heads, n_kv_heads, max_seq_len, _opts(options)))
 
 
-def _decode_operands(cache, rot, q, block_table, seq_lens, max_seq_len, out, workspace, stream):
+def decode_describe(batch: int, n_q_heads: int, n_kv_heads: int, max_seq_len: int, bits: int = 3,
+                    step: bool = False, options: DecodeOptions | None = None) -> dict:
+    """The launch plan of a decode call with these arguments (iq_decode_describe)."""
+    info = DecodePlanInfo()
+    _check("iq_decode_describe", lib.iq_decode_describe(batch, n_q_heads, n_kv_heads, max_seq_len, bits,
+                                                        int(step), _opts(options), ctypes.byref(info)))
+    return {name: int(getattr(info, name)) for name, _ in DecodePlanInfo._fields_}
+
+
+def decode_workspace(batch: int, n_q_heads: int, n_kv_heads: int, max_seq_len: int,
+                     options: DecodeOptions | None = None, device="cuda", stream=None) -> torch.Tensor:
+    """A decode workspace ready for its first call: zero-filled (its leading
+    counters must start at zero; every call leaves them zero)."""
+    dev = torch.device(device)
+    if dev.type == "cuda" and dev.index is None:
+        dev = torch.device("cuda", torch.cuda.current_device())
+    nbytes = decode_workspace_bytes(batch, n_q_heads, n_kv_heads, max_seq_len, options)
+    return _alloc((max(nbytes, 16),), torch.uint8, dev, stream, zero=True)
+
+
+def _decode_operands(cache, rot, q, block_table, seq_lens, max_seq_len, out, workspace, stream, options):
     bsz, hq, d = q.shape
     if d != HEAD_DIM:
         raise ValueError("head dim must be 128")
@@ -291,8 +357,7 @@ def _decode_operands(cache, rot, q, block_table, seq_lens, max_seq_len, out, wor
     elif out.dtype != torch.float32 or tuple(out.shape) != (bsz, hq, HEAD_DIM):
         raise ValueError("out must be float32 [B][Hq][128]")
     if workspace is None:
-        nbytes = decode_workspace_bytes(bsz, hq, cache.n_kv_heads, max_seq_len)
-        workspace = _alloc((max(nbytes, 16),), torch.uint8, dev, stream)
+        workspace = decode_workspace(bsz, hq, cache.n_kv_heads, max_seq_len, options, dev, stream)
     ptrs = (_dev(rot, "rot", dev), _dev(q, "q", dev), _idx(block_table, "block_table", dev),
             _idx(seq_lens, "seq_lens", dev), _dev(out, "out", dev), _dev(workspace, "workspace", dev))
     return dev, out, workspace, ptrs
@@ -301,21 +366,24 @@ def _decode_operands(cache, rot, q, block_table, seq_lens, max_seq_len, out, wor
 def decode_attention(cache: PagedCache, rot: torch.Tensor, q: torch.Tensor, block_table: torch.Tensor,
                      seq_lens: torch.Tensor, max_seq_len: int, softmax_scale: float = 0.0,
                      out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
-                     stream=None) -> torch.Tensor:
-    """q: [B][Hq][128]; block_table int32[B][max_pages]; seq_lens int32[B] -> fp32 [B][Hq][128]."""
+                     stream=None, options: DecodeOptions | None = None) -> torch.Tensor:
+    """q: [B][Hq][128]; block_table int32[B][max_pages]; seq_lens int32[B] -> fp32 [B][Hq][128].
+    A workspace passed in must come from decode_workspace (or have zero counters)."""
     bsz, hq, _ = q.shape
     dev, out, workspace, (p_rot, p_q, p_bt, p_len, p_out, p_ws) = _decode_operands(
-        cache, rot, q, block_table, seq_lens, max_seq_len, out, workspace, stream)
-    _check("iq_decode_attention", lib.iq_decode_attention(
+        cache, rot, q, block_table, seq_lens, max_seq_len, out, workspace, stream, options)
+    _check("iq_decode_attention", lib.iq_decode_attention_ex(
         cache.struct, p_rot, p_q, _dtype(q), bsz, hq, p_bt, block_table.shape[-1], p_len, int(max_seq_len),
-        float(softmax_scale), p_out, p_ws, workspace.numel() * workspace.element_size(), _stream(stream)))
+        float(softmax_scale), p_out, p_ws, workspace.numel() * workspace.element_size(), _opts(options),
+        _stream(stream)))
     return out
 
 
 def decode_step(cache: PagedCache, rot: torch.Tensor, q: torch.Tensor, k_new: torch.Tensor,
                 v_new: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
                 softmax_scale: float = 0.0, out: torch.Tensor | None = None,
-                workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+                workspace: torch.Tensor | None = None, stream=None,
+                options: DecodeOptions | None = None) -> torch.Tensor:
     """Append each sequence's current token (k_new, v_new: [B][Hkv][128], at position
     seq_lens[b] - 1) and run decode attention over all seq_lens[b] tokens, in one call."""
     bsz, hq, _ = q.shape
@@ -323,11 +391,11 @@ def decode_step(cache: PagedCache, rot: torch.Tensor, q: torch.Tensor, k_new: to
             or tuple(k_new.shape) != (bsz, cache.n_kv_heads, HEAD_DIM)):
         raise ValueError("k_new and v_new must both be [B][Hkv][128] of one dtype")
     dev, out, workspace, (p_rot, p_q, p_bt, p_len, p_out, p_ws) = _decode_operands(
-        cache, rot, q, block_table, seq_lens, max_seq_len, out, workspace, stream)
-    _check("iq_decode_step", lib.iq_decode_step(
+        cache, rot, q, block_table, seq_lens, max_seq_len, out, workspace, stream, options)
+    _check("iq_decode_step", lib.iq_decode_step_ex(
         cache.struct, p_rot, p_q, _dtype(q), bsz, hq, _dev(k_new, "k_new", dev), _dev(v_new, "v_new", dev),
         _dtype(k_new), p_bt, block_table.shape[-1], p_len, int(max_seq_len), float(softmax_scale),
-        p_out, p_ws, workspace.numel() * workspace.element_size(), _stream(stream)))
+        p_out, p_ws, workspace.numel() * workspace.element_size(), _opts(options), _stream(stream)))
     return out
 
 
@@ -338,8 +406,9 @@ def prefill_workspace_bytes(n_q: int, n_q_heads: int, n_kv_heads: int, q_start: 
 def prefill_attention(cache: PagedCache, rot: torch.Tensor, q: torch.Tensor, q_start: int,
                       block_table: torch.Tensor, softmax_scale: float = 0.0,
                       out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
-                      stream=None) -> torch.Tensor:
-    """q: [n_q][Hq][128] at positions q_start..; block_table int32[max_pages] -> fp32 [n_q][Hq][128]."""
+                      stream=None, waves: int = 0) -> torch.Tensor:
+    """q: [n_q][Hq][128] at positions q_start..; block_table int32[max_pages] -> fp32 [n_q][Hq][128].
+    waves: 0 or 8 (eight waves of 16 rows) or 4 (four waves of 32 rows)."""
     n_q, hq, d = q.shape
     if d != HEAD_DIM:
         raise ValueError("head dim must be 128")
@@ -354,10 +423,11 @@ def prefill_attention(cache: PagedCache, rot: torch.Tensor, q: torch.Tensor, q_s
         workspace = _alloc((need,), torch.uint8, dev, stream)
     ws_ptr = None if workspace is None else _dev(workspace, "workspace", dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check("iq_prefill_attention", lib.iq_prefill_attention(
+    opts = PrefillOptions(int(waves))
+    _check("iq_prefill_attention", lib.iq_prefill_attention_ex(
         cache.struct, _dev(rot, "rot", dev), _dev(q, "q", dev), _dtype(q), n_q, hq, int(q_start),
         _idx(block_table, "block_table", dev), block_table.shape[-1], float(softmax_scale),
-        _dev(out, "out", dev), ws_ptr, ws_bytes, _stream(stream)))
+        _dev(out, "out", dev), ws_ptr, ws_bytes, ctypes.byref(opts), _stream(stream)))
     return out
 
 

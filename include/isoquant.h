@@ -190,14 +190,26 @@ iq_status iq_quantize_append(const iq_cache *cache, const void *rot_dev, const v
  * softmax_scale  : <= 0 selects 1/sqrt(128).
  * out_dev        : float[batch][n_q_heads][128], in the original (unrotated) space.
  *                  A sequence of length 0 gives zeros.
- * workspace_dev  : at least iq_decode_workspace_bytes(...) bytes, any contents;
- *                  holds the per-split partials (m, l, accumulator) between the
- *                  split and merge kernels of this call.
+ * workspace_dev  : at least iq_decode_workspace_bytes(...) bytes.  Its first
+ *                  IQ_DECODE_COUNTER_BYTES bytes are arrival counters and must
+ *                  be zero before the buffer's first decode call (zero a new
+ *                  buffer once); every call leaves them zero.  The rest holds
+ *                  the per-split partials (m, l, accumulator) of this call,
+ *                  any contents on entry.
  * Unsupported: n_q_heads / n_kv_heads > IQ_MAX_GROUP.
- * Determinism: inside a split, pages go to whichever wave asks first, so the
- * order of the f16 rounding of softmax weights can differ between runs (the
- * results agree to about 2^-11 of a weight, far inside the 1e-3 tolerance).
+ * Splits and their merge: the context of each (sequence, kv head) is split
+ * across workgroups; the partials are merged by a second kernel, or (on
+ * request, see iq_decode_options.merge) by merge workgroups of the same
+ * launch, which wait for the split workgroups of their (sequence, kv head)
+ * through the counters (only where the runtime's occupancy calculator says
+ * the whole grid is resident at once).
+ * Determinism: by default the waves of a workgroup take the pages of their
+ * split as they become free, so the order of the f16 rounding of softmax
+ * weights can differ between runs (the results agree to about 2^-11 of a
+ * weight, far inside the 1e-3 tolerance); iq_decode_options.deterministic
+ * fixes the order (bit-identical results for a fixed plan).
  */
+enum { IQ_DECODE_COUNTER_BYTES = 16384 };
 size_t iq_decode_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
                                  int32_t max_seq_len);
 iq_status iq_decode_attention(const iq_cache *cache, const void *rot_dev, const void *q_dev,
@@ -206,6 +218,48 @@ iq_status iq_decode_attention(const iq_cache *cache, const void *rot_dev, const 
                               const int32_t *seq_lens_dev, int32_t max_seq_len,
                               float softmax_scale, float *out_dev, void *workspace_dev,
                               size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Choices a caller may fix for one decode call (the _ex entry points below;
+ * the context split by length and CU count, FreeToken v0.2.0 release notes,
+ * Kernels #729).  A zero field leaves the choice to the planner; a null
+ * pointer means all zeros, which is what the plain entry points use.  The
+ * same options must be given to iq_decode_workspace_bytes_ex and to the call.
+ *   waves           : 0, 4 or 8 waves per workgroup.
+ *   pages_per_split : 0, or pages per split of the host plan (capped at 64 per wave).
+ *   rounds          : 0, or the workgroups per CU the plan is made for (more,
+ *                     shorter splits).
+ *   plan            : IQ_PLAN_AUTO (device-balanced for 2..64 sequences, else the
+ *                     host plan), IQ_PLAN_HOST (splits of equal page ranges
+ *                     planned from max_seq_len), IQ_PLAN_BALANCED (= AUTO).
+ *   merge           : IQ_MERGE_AUTO / IQ_MERGE_KERNEL: a merge kernel follows
+ *                     the split launch; IQ_MERGE_FUSED: merge workgroups join the
+ *                     split launch where allowed (host plan, four waves, the
+ *                     whole grid resident at once), else a merge kernel.
+ *   deterministic   : nonzero: wave w of a workgroup takes pages w, w + W, ...
+ *                     of its split in order: bit-identical results for a fixed
+ *                     plan, run after run.
+ * Errors: IQ_ERR_INVALID_ARG for a field outside these values.
+ */
+typedef enum { IQ_PLAN_AUTO = 0, IQ_PLAN_HOST = 1, IQ_PLAN_BALANCED = 2 } iq_decode_plan;
+typedef enum { IQ_MERGE_AUTO = 0, IQ_MERGE_FUSED = 1, IQ_MERGE_KERNEL = 2 } iq_decode_merge;
+typedef struct {
+  int32_t waves;
+  int32_t pages_per_split;
+  int32_t rounds;
+  int32_t plan;
+  int32_t merge;
+  int32_t deterministic;
+} iq_decode_options;
+size_t iq_decode_workspace_bytes_ex(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                                    int32_t max_seq_len, const iq_decode_options *options);
+iq_status iq_decode_attention_ex(const iq_cache *cache, const void *rot_dev, const void *q_dev,
+                                 int32_t q_dtype, int32_t batch, int32_t n_q_heads,
+                                 const int32_t *block_table_dev, int32_t max_pages_per_seq,
+                                 const int32_t *seq_lens_dev, int32_t max_seq_len,
+                                 float softmax_scale, float *out_dev, void *workspace_dev,
+                                 size_t workspace_bytes, const iq_decode_options *options,
+                                 hipStream_t stream);
 
 /*
  * Decode step = quantise-append of each sequence's current token followed by
@@ -230,6 +284,35 @@ iq_status iq_decode_step(const iq_cache *cache, const void *rot_dev, const void 
                          int32_t max_pages_per_seq, const int32_t *seq_lens_dev,
                          int32_t max_seq_len, float softmax_scale, float *out_dev,
                          void *workspace_dev, size_t workspace_bytes, hipStream_t stream);
+/*
+ * The launch plan a decode call with these arguments would use (host only;
+ * the merge choice asks the HIP runtime's occupancy calculator about the
+ * current device, so without a usable device fused_merge reads 0).  bits: 3
+ * or 4 (the cache's record width); step: nonzero for iq_decode_step(_ex).
+ * Writes *info; IQ_ERR_INVALID_ARG for arguments the call would refuse for
+ * the same reasons.
+ */
+typedef struct {
+  int32_t waves;            /* waves per workgroup                                   */
+  int32_t splits;           /* host plan: splits per (sequence, kv head); balanced:
+                               partial-row slots per query head                      */
+  int32_t pages_per_split;  /* host plan: pages per split; balanced: the cap         */
+  int32_t balanced;         /* 1: the split plan is made on the device from the lengths */
+  int32_t fused_merge;      /* 1: merge workgroups in the split launch; 0: a merge kernel */
+  int32_t workgroups;       /* workgroups of the split launch                        */
+} iq_decode_plan_info;
+iq_status iq_decode_describe(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, int32_t max_seq_len,
+                             int32_t bits, int32_t step, const iq_decode_options *options,
+                             iq_decode_plan_info *info);
+
+/* iq_decode_step with the options of iq_decode_attention_ex. */
+iq_status iq_decode_step_ex(const iq_cache *cache, const void *rot_dev, const void *q_dev,
+                            int32_t q_dtype, int32_t batch, int32_t n_q_heads, const void *k_new_dev,
+                            const void *v_new_dev, int32_t kv_dtype, const int32_t *block_table_dev,
+                            int32_t max_pages_per_seq, const int32_t *seq_lens_dev,
+                            int32_t max_seq_len, float softmax_scale, float *out_dev,
+                            void *workspace_dev, size_t workspace_bytes,
+                            const iq_decode_options *options, hipStream_t stream);
 
 /*
  * Chunked causal prefill attention of one sequence on the packed cache
@@ -252,6 +335,21 @@ iq_status iq_prefill_attention(const iq_cache *cache, const void *rot_dev, const
                                int32_t q_start_pos, const int32_t *block_table_dev,
                                int32_t max_pages, float softmax_scale, float *out_dev,
                                void *workspace_dev, size_t workspace_bytes, hipStream_t stream);
+/*
+ * iq_prefill_attention with a choice of workgroup shape (same results up to
+ * the order of the fp32 sums): waves 0 or 8 = eight waves of 16 query rows
+ * (the default), 4 = four waves of 32 rows.  A null pointer means 0.
+ * IQ_ERR_INVALID_ARG for another value.
+ */
+typedef struct {
+  int32_t waves;
+} iq_prefill_options;
+iq_status iq_prefill_attention_ex(const iq_cache *cache, const void *rot_dev, const void *q_dev,
+                                  int32_t q_dtype, int32_t n_q, int32_t n_q_heads,
+                                  int32_t q_start_pos, const int32_t *block_table_dev,
+                                  int32_t max_pages, float softmax_scale, float *out_dev,
+                                  void *workspace_dev, size_t workspace_bytes,
+                                  const iq_prefill_options *options, hipStream_t stream);
 
 /*
  * Batched variable-length chunked prefill: several sequences' query chunks in
@@ -322,7 +420,8 @@ iq_status iq_dense_append(const iq_dense_cache *cache, const void *k_dev, const 
 
 /* As iq_decode_attention over the bf16 or FP8 cache: out = softmax(scale q K^T) V
  * per query head over the stored values, fp32 [batch][n_q_heads][128].  q_dtype must be IQ_BF16
- * (IQ_ERR_UNSUPPORTED otherwise); group limit and workspace rules as there. */
+ * (IQ_ERR_UNSUPPORTED otherwise); group limit and workspace rules as there (its
+ * partials follow the counter region, which it leaves untouched). */
 size_t iq_dense_decode_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
                                        int32_t max_seq_len);
 iq_status iq_dense_decode_attention(const iq_dense_cache *cache, const void *q_dev,

@@ -217,3 +217,42 @@ def test_binding_refuses_host_tensors():
     for fn in calls:
         with pytest.raises(ValueError, match="GPU memory"):
             fn()
+
+
+def test_decode_options_validation():
+    """iq_decode_options: every field outside its values is refused on the host
+    (and the workspace query returns 0 for it); valid options plan a workspace
+    that starts with the counter region."""
+    c = _cache(hkv=4)
+    bad = [dict(waves=6), dict(waves=-4), dict(pages_per_split=-1), dict(rounds=-2), dict(rounds=65),
+           dict(plan=3), dict(plan=-1), dict(merge=3), dict(merge=-1)]
+    for kw in bad:
+        o = iq.DecodeOptions(**kw)
+        assert L.iq_decode_attention_ex(c, FAKE, FAKE, 1, 1, 32, FAKE, 16, FAKE, 1024, 0.0, FAKE, FAKE,
+                                        10 ** 9, ctypes.byref(o), None) == -1, kw
+        assert L.iq_decode_step_ex(c, FAKE, FAKE, 1, 1, 32, FAKE, FAKE, 1, FAKE, 16, FAKE, 1024, 0.0, FAKE,
+                                   FAKE, 10 ** 9, ctypes.byref(o), None) == -1, kw
+        assert iq.decode_workspace_bytes(1, 32, 4, 1024, o) == 0, kw
+    good = [iq.DecodeOptions(), iq.DecodeOptions(waves=8, pages_per_split=3, rounds=2, plan=1, merge=2,
+                                                 deterministic=1)]
+    for o in good:
+        n = iq.decode_workspace_bytes(2, 32, 4, 4096, o)
+        # counters + at least one partial row (m, l, 128 accumulators) per query head
+        assert n >= iq.DECODE_COUNTER_BYTES + 2 * 32 * 130 * 4
+        # a too-small workspace is the only failure left
+        assert L.iq_decode_attention_ex(c, FAKE, FAKE, 1, 2, 32, FAKE, 64, FAKE, 4096, 0.0, FAKE, FAKE,
+                                        n - 1, ctypes.byref(o), None) == -3
+    # a host plan of one-page splits needs one partial row per page and query head
+    o = iq.DecodeOptions(plan=1, pages_per_split=1)
+    assert iq.decode_workspace_bytes(2, 32, 4, 4096, o) == iq.DECODE_COUNTER_BYTES + 2 * 32 * 64 * 130 * 4
+
+
+def test_prefill_options_validation():
+    c = _cache(hkv=8)
+    for w in (1, 2, 16, -4):
+        o = iq.PrefillOptions(w)
+        assert L.iq_prefill_attention_ex(c, FAKE, FAKE, 1, 16, 64, 0, FAKE, 8, 0.0, FAKE, FAKE, 0,
+                                         ctypes.byref(o), None) == -1
+    o = iq.PrefillOptions(4)
+    assert L.iq_prefill_attention_ex(c, FAKE, FAKE, 1, 0, 64, 0, FAKE, 8, 0.0, FAKE, FAKE, 0,
+                                     ctypes.byref(o), None) == 0

@@ -8,7 +8,6 @@ rounding-midpoint exemption; attention max_rows max|gpu - oracle| / max|oracle|
 must write the records a separate append writes, byte for byte.
 """
 
-import os
 
 import numpy as np
 import pytest
@@ -30,18 +29,9 @@ def _say(*a):
 
 
 def _with_waves(waves, fn):
-    old = os.environ.get("IQ_DECODE_WAVES")
-    try:
-        if waves is None:
-            os.environ.pop("IQ_DECODE_WAVES", None)
-        else:
-            os.environ["IQ_DECODE_WAVES"] = str(waves)
-        return fn()
-    finally:
-        if old is None:
-            os.environ.pop("IQ_DECODE_WAVES", None)
-        else:
-            os.environ["IQ_DECODE_WAVES"] = old
+    """fn(options) with `waves` waves per decode workgroup (None: the planner's choice)."""
+    from compressed_space_attention_amd import isoquant as iq
+    return fn(iq.DecodeOptions(waves=waves or 0))
 
 
 SMALL_LENS = [1, 100, 700, 64]     # 6920 vectors: the 32-lanes-per-vector kernel
@@ -107,8 +97,8 @@ def test_decode4_matches_oracle_on_gpu_cache(case):
     _say(f"4-bit decode parity lens={lens} hkv={hkv} hq={hq} dtype={dtype} waves={waves}")
     s = Scenario(1100 + case, lens, hkv=hkv, dtype=dtype, outliers=outl, bits=4)
     q = s.queries(1200 + case, len(lens), hq)
-    out = _with_waves(waves, lambda: s.iq.decode_attention(s.cache, s.rot, q.cuda(), s.bt_dev,
-                                                             s.lens_dev, max(lens)))
+    out = _with_waves(waves, lambda o: s.iq.decode_attention(s.cache, s.rot, q.cuda(), s.bt_dev,
+                                                               s.lens_dev, max(lens), options=o))
     torch.cuda.synchronize()
     ref = s.oracle_decode(s.host_cache(), q.double().numpy())
     o = out.cpu().numpy()
@@ -135,10 +125,10 @@ def test_decode4_step_matches_append_then_decode(case):
     step = Scenario(1300 + case, lens, hkv=hkv, dtype=dtype, outliers=outl, bits=4,
                     kv_override=(full.k, full.v), hold_last=True)
     q = step.queries(1400 + case, len(lens), hq).cuda()
-    out = _with_waves(waves, lambda: step.iq.decode_step(
-        step.cache, step.rot, q, step.k_last, step.v_last, step.bt_dev, step.lens_dev, max(lens)))
-    pair = _with_waves(waves, lambda: full.iq.decode_attention(
-        full.cache, full.rot, q, full.bt_dev, full.lens_dev, max(lens)))
+    out = _with_waves(waves, lambda o: step.iq.decode_step(
+        step.cache, step.rot, q, step.k_last, step.v_last, step.bt_dev, step.lens_dev, max(lens), options=o))
+    pair = _with_waves(waves, lambda o: full.iq.decode_attention(
+        full.cache, full.rot, q, full.bt_dev, full.lens_dev, max(lens), options=o))
     torch.cuda.synchronize()
     for a, b in zip(step.cache.to_host(), full.cache.to_host()):
         assert np.array_equal(a, b)
@@ -184,21 +174,6 @@ PREFILL4_CASES = [
 ]
 
 
-def _with_prefill_waves(waves, fn):
-    old = os.environ.get("IQ_PREFILL_WAVES")
-    try:
-        if waves is None:
-            os.environ.pop("IQ_PREFILL_WAVES", None)
-        else:
-            os.environ["IQ_PREFILL_WAVES"] = str(waves)
-        return fn()
-    finally:
-        if old is None:
-            os.environ.pop("IQ_PREFILL_WAVES", None)
-        else:
-            os.environ["IQ_PREFILL_WAVES"] = old
-
-
 @pytest.mark.parametrize("case", range(len(PREFILL4_CASES)))
 def test_prefill4_matches_oracle(case):
     total, n_q, hkv, hq, waves = PREFILL4_CASES[case]
@@ -206,8 +181,7 @@ def test_prefill4_matches_oracle(case):
     s = Scenario(1500 + case, [total], hkv=hkv, dtype="bf16", bits=4)
     q = synth.to_dtype(synth.normal(1501 + case, (n_q, hq, 128)), "bf16")
     q_start = total - n_q
-    out = _with_prefill_waves(waves, lambda: s.iq.prefill_attention(
-        s.cache, s.rot, q.cuda(), q_start, s.bt_dev[0]).cpu().numpy())
+    out = s.iq.prefill_attention(s.cache, s.rot, q.cuda(), q_start, s.bt_dev[0], waves=waves or 0).cpu().numpy()
     rows = np.unique(np.linspace(0, n_q - 1, min(n_q, 24)).astype(int))
     ref = O4.prefill_attention4(s.host_cache(), s.blocks, q.double().numpy(), q_start, s.block_table[0],
                                 rows=rows)

@@ -24,8 +24,7 @@ def test_decode_step_stack_graph_replays():
               for i in range(3)]
     qs = [s.queries(1200 + i, len(lens), 16).cuda() for i, s in enumerate(layers)]
     iq = layers[0].iq
-    ws = torch.empty(iq.decode_workspace_bytes(len(lens), 16, 2, max(lens)), dtype=torch.uint8,
-                     device="cuda")
+    ws = iq.decode_workspace(len(lens), 16, 2, max(lens))
     outs = [torch.empty((len(lens), 16, 128), dtype=torch.float32, device="cuda") for _ in layers]
 
     def stack():

@@ -7,7 +7,6 @@ Attention outputs must satisfy max_rows max|gpu - oracle| / max|oracle| <= 1e-3,
 with the oracle attending over the GPU-written cache.
 """
 
-import os
 
 import numpy as np
 import pytest
@@ -151,22 +150,14 @@ def test_decode_split_plans_agree():
     s = Scenario(400, lens, hkv=2, dtype="bf16", outliers=True)
     q = s.queries(401, 2, 16).cuda()
     outs = []
-    saved = {k: os.environ.get(k) for k in ("IQ_DECODE_PAGES_PER_SPLIT", "IQ_DECODE_BALANCED")}
-    try:
-        os.environ["IQ_DECODE_BALANCED"] = "0"        # host plans from the longest length
-        for pps in ("1", "3", "16", "512"):
-            os.environ["IQ_DECODE_PAGES_PER_SPLIT"] = pps
-            outs.append(s.iq.decode_attention(s.cache, s.rot, q, s.bt_dev, s.lens_dev, 3000).cpu().numpy())
-        again = s.iq.decode_attention(s.cache, s.rot, q, s.bt_dev, s.lens_dev, 3000).cpu().numpy()
-        os.environ.pop("IQ_DECODE_PAGES_PER_SPLIT")
-        os.environ["IQ_DECODE_BALANCED"] = "1"        # the device-balanced plan
-        outs.append(s.iq.decode_attention(s.cache, s.rot, q, s.bt_dev, s.lens_dev, 3000).cpu().numpy())
-    finally:
-        for k, v in saved.items():
-            if v is None:
-                os.environ.pop(k, None)
-            else:
-                os.environ[k] = v
+    iq = s.iq
+    for pps in (1, 3, 16, 512):            # host plans from the longest length
+        opts = iq.DecodeOptions(plan=iq.IQ_PLAN_HOST, pages_per_split=pps)
+        outs.append(iq.decode_attention(s.cache, s.rot, q, s.bt_dev, s.lens_dev, 3000, options=opts)
+                    .cpu().numpy())
+    again = iq.decode_attention(s.cache, s.rot, q, s.bt_dev, s.lens_dev, 3000, options=opts).cpu().numpy()
+    # the device-balanced plan
+    outs.append(iq.decode_attention(s.cache, s.rot, q, s.bt_dev, s.lens_dev, 3000).cpu().numpy())
     ref = O.decode_attention(s.host_cache(), s.blocks, q.double().cpu().numpy(), s.block_table, lens)
     for o in outs + [again]:
         assert max_row_error(o, ref) <= tol()
@@ -192,20 +183,11 @@ def test_decode_balanced_plan(case):
     _say(f"balanced decode lens={lens[:8]}... B={len(lens)} hkv={hkv} hq={hq} waves={waves}")
     s = Scenario(450 + case, lens, hkv=hkv, dtype="bf16", outliers=True)
     q = s.queries(460 + case, len(lens), hq).cuda()
-    saved = {k: os.environ.get(k) for k in ("IQ_DECODE_BALANCED", "IQ_DECODE_WAVES")}
-    try:
-        if waves:
-            os.environ["IQ_DECODE_WAVES"] = str(waves)
-        os.environ["IQ_DECODE_BALANCED"] = "1"
-        bal = s.iq.decode_attention(s.cache, s.rot, q, s.bt_dev, s.lens_dev, max(lens)).cpu().numpy()
-        os.environ["IQ_DECODE_BALANCED"] = "0"
-        uni = s.iq.decode_attention(s.cache, s.rot, q, s.bt_dev, s.lens_dev, max(lens)).cpu().numpy()
-    finally:
-        for k, v in saved.items():
-            if v is None:
-                os.environ.pop(k, None)
-            else:
-                os.environ[k] = v
+    iq = s.iq
+    bal = iq.decode_attention(s.cache, s.rot, q, s.bt_dev, s.lens_dev, max(lens),
+                              options=iq.DecodeOptions(waves=waves or 0, plan=iq.IQ_PLAN_BALANCED)).cpu().numpy()
+    uni = iq.decode_attention(s.cache, s.rot, q, s.bt_dev, s.lens_dev, max(lens),
+                              options=iq.DecodeOptions(waves=waves or 0, plan=iq.IQ_PLAN_HOST)).cpu().numpy()
     ref = O.decode_attention(s.host_cache(), s.blocks, q.double().cpu().numpy(), s.block_table, lens)
     err = max_row_error(bal, ref)
     _say(f"  max row error {err:.3e}")

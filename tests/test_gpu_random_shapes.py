@@ -10,7 +10,6 @@ tolerance as the fixed cases; a decode step (the token's append fused into
 attention) must leave the cache byte-identical to appending every token first.
 """
 
-import os
 
 import numpy as np
 import pytest
@@ -95,18 +94,12 @@ def test_decode_step_random_shape(seed):
     step = Scenario(7900 + seed, lens, hkv=hkv, dtype=dtype, outliers=outliers, bits=bits,
                     kv_override=(full.k, full.v), hold_last=True)
     q = step.queries(8000 + seed, len(lens), hkv * group).cuda()
-    old = os.environ.get("IQ_DECODE_WAVES")
-    os.environ["IQ_DECODE_WAVES"] = str(waves)
-    try:
-        out = step.iq.decode_step(step.cache, step.rot, q, step.k_last, step.v_last, step.bt_dev,
-                                  step.lens_dev, max(lens))
-        pair = full.iq.decode_attention(full.cache, full.rot, q, full.bt_dev, full.lens_dev, max(lens))
-        torch.cuda.synchronize()
-    finally:
-        if old is None:
-            os.environ.pop("IQ_DECODE_WAVES", None)
-        else:
-            os.environ["IQ_DECODE_WAVES"] = old
+    opts = step.iq.DecodeOptions(waves=waves)
+    out = step.iq.decode_step(step.cache, step.rot, q, step.k_last, step.v_last, step.bt_dev,
+                              step.lens_dev, max(lens), options=opts)
+    pair = full.iq.decode_attention(full.cache, full.rot, q, full.bt_dev, full.lens_dev, max(lens),
+                                    options=opts)
+    torch.cuda.synchronize()
     for a, b in zip(step.cache.to_host(), full.cache.to_host()):
         assert np.array_equal(a, b)
     o = out.cpu().numpy()

@@ -9,8 +9,6 @@ must include the new token: max_rows max|gpu - oracle| / max|oracle| <= 1e-3,
 with the oracle attending over the cache holding every token.
 """
 
-import os
-
 import numpy as np
 import pytest
 import torch
@@ -39,21 +37,6 @@ STEP_CASES = [
 ]
 
 
-def _with_waves(waves, fn):
-    old = os.environ.get("IQ_DECODE_WAVES")
-    try:
-        if waves is None:
-            os.environ.pop("IQ_DECODE_WAVES", None)
-        else:
-            os.environ["IQ_DECODE_WAVES"] = str(waves)
-        return fn()
-    finally:
-        if old is None:
-            os.environ.pop("IQ_DECODE_WAVES", None)
-        else:
-            os.environ["IQ_DECODE_WAVES"] = old
-
-
 @pytest.mark.parametrize("case", range(len(STEP_CASES)))
 def test_decode_step_matches_append_then_decode(case):
     lens, hkv, hq, dtype, outl, waves = STEP_CASES[case]
@@ -62,10 +45,11 @@ def test_decode_step_matches_append_then_decode(case):
     step = Scenario(700 + case, lens, hkv=hkv, dtype=dtype, outliers=outl,
                     kv_override=(full.k, full.v), hold_last=True)
     q = step.queries(800 + case, len(lens), hq).cuda()
-    out = _with_waves(waves, lambda: step.iq.decode_step(
-        step.cache, step.rot, q, step.k_last, step.v_last, step.bt_dev, step.lens_dev, max(lens)))
-    pair = _with_waves(waves, lambda: full.iq.decode_attention(
-        full.cache, full.rot, q, full.bt_dev, full.lens_dev, max(lens)))
+    opts = step.iq.DecodeOptions(waves=waves or 0)
+    out = step.iq.decode_step(step.cache, step.rot, q, step.k_last, step.v_last, step.bt_dev, step.lens_dev,
+                              max(lens), options=opts)
+    pair = full.iq.decode_attention(full.cache, full.rot, q, full.bt_dev, full.lens_dev, max(lens),
+                                    options=opts)
     torch.cuda.synchronize()
     # the cache after the step is the cache after appending every token
     for a, b in zip(step.cache.to_host(), full.cache.to_host()):
