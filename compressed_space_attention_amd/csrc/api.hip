@@ -29,6 +29,24 @@ int device_cu_count() {
   return n;
 }
 
+// The no-allocation decode step's scratch: one array per GPU the library runs
+// on.  Host code never uses the array's name as an address (on the host it is
+// a stand-in, not device memory): it uses the address hipGetSymbolAddress
+// returns for the current device, kept per device.
+static __device__ __align__(256) uint8_t scratch[IQ_NOALLOC_SCRATCH_BYTES];
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+void* scratch_ptr() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  void* q = nullptr;
+  if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q) return nullptr;
+  g_scratch_ptr[dev].store(q, std::memory_order_release);  // the same address whoever stores it
+  return q;
+}
+
 bool cache_ok(const iq_cache* c) {
   return c && c->k_codes_dev && c->k_norms_dev && c->v_codes_dev && c->v_norms_dev &&
          c->num_pages > 0 && c->n_kv_heads > 0 && (c->bits == 0 || c->bits == 3 || c->bits == 4);
@@ -120,6 +138,7 @@ const char* iq_status_string(int32_t status) {
     case IQ_ERR_WORKSPACE: return "workspace too small";
     case IQ_ERR_LAUNCH: return "HIP copy or kernel launch failed";
     case IQ_ERR_DEVICE: return "no usable HIP device";
+    case IQ_ERR_SCRATCH: return "call needs more scratch than the library's static array holds";
     default: return "unknown status";
   }
 }
@@ -255,6 +274,32 @@ iq_status iq_decode_step(const iq_cache* cache, const void* rot_dev, const void*
   return decode_call(cache, rot_dev, q_dev, q_dtype, batch, n_q_heads, k_new_dev, v_new_dev, kv_dtype,
                      block_table_dev, max_pages_per_seq, seq_lens_dev, max_seq_len, softmax_scale, out_dev,
                      workspace_dev, workspace_bytes, nullptr, stream);
+}
+
+iq_status iq_decode_step_noalloc(const iq_cache* cache, const void* rot_dev, const void* q_dev,
+                                 int32_t q_dtype, int32_t batch, int32_t n_q_heads, const void* k_new_dev,
+                                 const void* v_new_dev, int32_t kv_dtype, const int32_t* block_table_dev,
+                                 int32_t max_pages_per_seq, const int32_t* seq_lens_dev, int32_t max_seq_len,
+                                 float softmax_scale, float* out_dev, hipStream_t stream) {
+  if (!cache_ok(cache) || !rot_dev || !q_dev || !dtype_ok(q_dtype) || !k_new_dev || !v_new_dev ||
+      !dtype_ok(kv_dtype) || batch < 1 || batch > 65535 || n_q_heads < 1 || !block_table_dev ||
+      max_pages_per_seq < 1 || !seq_lens_dev || max_seq_len < 0 || !out_dev)
+    return IQ_ERR_INVALID_ARG;
+  if (n_q_heads % cache->n_kv_heads != 0) return IQ_ERR_INVALID_ARG;
+  if ((int64_t)max_seq_len > (int64_t)max_pages_per_seq * IQ_PAGE_TOKENS) return IQ_ERR_INVALID_ARG;
+  if (cache->n_kv_heads > 65535) return IQ_ERR_UNSUPPORTED;
+  if (n_q_heads / cache->n_kv_heads > IQ_MAX_GROUP) return IQ_ERR_UNSUPPORTED;
+  iq::DecodeOptions opts{};
+  opts.merge = 2;  // the merge kernel: no counter in the array has to start at zero
+  const iq::DecodePlan plan = iq::plan_decode(batch, cache->n_kv_heads, max_seq_len, device_cu_count(), opts);
+  if (iq::decode_workspace_bytes(batch, n_q_heads, plan) > (size_t)IQ_NOALLOC_SCRATCH_BYTES)
+    return IQ_ERR_SCRATCH;
+  void* ws = scratch_ptr();
+  if (!ws) return IQ_ERR_DEVICE;
+  return launch_status(iq::launch_decode(view(cache), reinterpret_cast<const float*>(rot_dev), q_dev,
+                                         q_dtype, batch, n_q_heads, block_table_dev, max_pages_per_seq,
+                                         seq_lens_dev, plan, resolve_scale(softmax_scale), out_dev, ws,
+                                         k_new_dev, v_new_dev, kv_dtype, stream));
 }
 
 iq_status iq_decode_step_ex(const iq_cache* cache, const void* rot_dev, const void* q_dev,

@@ -122,6 +122,8 @@ def _load():
                                  sz, vp]),
         "iq_decode_step_ex": (i32, [cp, vp, vp, i32, i32, i32, vp, vp, i32, vp, i32, vp, i32, f32, vp, vp,
                                     sz, op, vp]),
+        "iq_decode_step_noalloc": (i32, [cp, vp, vp, i32, i32, i32, vp, vp, i32, vp, i32, vp, i32, f32, vp,
+                                         vp]),
         "iq_dense_append": (i32, [dp, vp, vp, i32, i32, vp, vp, vp, i32, vp]),
         "iq_dense_decode_workspace_bytes": (sz, [i32, i32, i32, i32]),
         "iq_dense_decode_attention": (i32, [dp, vp, i32, i32, i32, vp, i32, vp, i32, f32, vp, vp, sz, vp]),
@@ -145,7 +147,7 @@ lib = _load()
 EXPORTED = ("iq_status_string", "iq_version", "iq_codebook", "iq_rotation_bytes", "iq_rotation_init",
             "iq_quantize_append", "iq_decode_workspace_bytes", "iq_decode_attention",
             "iq_decode_step", "iq_decode_workspace_bytes_ex", "iq_decode_attention_ex", "iq_decode_step_ex",
-            "iq_decode_describe",
+            "iq_decode_describe", "iq_decode_step_noalloc",
             "iq_prefill_workspace_bytes", "iq_prefill_attention", "iq_prefill_attention_ex",
             "iq_prefill_attention_varlen",
             "iq_dense_append", "iq_dense_decode_workspace_bytes", "iq_dense_decode_attention",
@@ -396,6 +398,36 @@ def decode_step(cache: PagedCache, rot: torch.Tensor, q: torch.Tensor, k_new: to
         cache.struct, p_rot, p_q, _dtype(q), bsz, hq, _dev(k_new, "k_new", dev), _dev(v_new, "v_new", dev),
         _dtype(k_new), p_bt, block_table.shape[-1], p_len, int(max_seq_len), float(softmax_scale),
         p_out, p_ws, workspace.numel() * workspace.element_size(), _opts(options), _stream(stream)))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def decode_step_noalloc(cache: PagedCache, rot: torch.Tensor, q: torch.Tensor, k_new: torch.Tensor,
+                        v_new: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor,
+                        max_seq_len: int, out: torch.Tensor, softmax_scale: float = 0.0,
+                        stream=None) -> torch.Tensor:
+    """decode_step without a workspace: the library's static per-GPU scratch
+    holds the split partials, and `out` must be given, so the call allocates
+    nothing.  Calls that overlap on one GPU race (they share the scratch)."""
+    bsz, hq, d = q.shape
+    if d != HEAD_DIM:
+        raise ValueError("head dim must be 128")
+    if (k_new.shape != v_new.shape or k_new.dtype != v_new.dtype
+            or tuple(k_new.shape) != (bsz, cache.n_kv_heads, HEAD_DIM)):
+        raise ValueError("k_new and v_new must both be [B][Hkv][128] of one dtype")
+    dev = _device_of(q, "q")
+    _check_cache(cache, dev)
+    if block_table.dim() != 2 or block_table.shape[0] < bsz or seq_lens.numel() != bsz:
+        raise ValueError("block_table must be int32[B][max_pages] and seq_lens int32[B]")
+    if out.dtype != torch.float32 or tuple(out.shape) != (bsz, hq, HEAD_DIM):
+        raise ValueError("out must be float32 [B][Hq][128]")
+    _check("iq_decode_step_noalloc", lib.iq_decode_step_noalloc(
+        cache.struct, _dev(rot, "rot", dev), _dev(q, "q", dev), _dtype(q), bsz, hq,
+        _dev(k_new, "k_new", dev), _dev(v_new, "v_new", dev), _dtype(k_new),
+        _idx(block_table, "block_table", dev), block_table.shape[-1], _idx(seq_lens, "seq_lens", dev),
+        int(max_seq_len), float(softmax_scale), _dev(out, "out", dev), _stream(stream)))
     return out
 
 

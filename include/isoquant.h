@@ -53,7 +53,8 @@ typedef enum {
   IQ_ERR_UNSUPPORTED = -2,   /* valid but outside what the kernels handle     */
   IQ_ERR_WORKSPACE = -3,     /* workspace smaller than the *_workspace_bytes   */
   IQ_ERR_LAUNCH = -4,        /* HIP reported an error for a copy or launch     */
-  IQ_ERR_DEVICE = -5         /* no usable HIP device                           */
+  IQ_ERR_DEVICE = -5,        /* no usable HIP device                           */
+  IQ_ERR_SCRATCH = -6        /* the call needs more than the static scratch    */
 } iq_status;
 
 typedef enum { IQ_F32 = 0, IQ_BF16 = 1, IQ_F16 = 2 } iq_dtype;
@@ -304,6 +305,29 @@ typedef struct {
 iq_status iq_decode_describe(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, int32_t max_seq_len,
                              int32_t bits, int32_t step, const iq_decode_options *options,
                              iq_decode_plan_info *info);
+
+/*
+ * iq_decode_step for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * The same arguments and results as iq_decode_step without the workspace:
+ * the split partials live in a static device array of the library
+ * (IQ_NOALLOC_SCRATCH_BYTES per GPU, held until the process ends), located
+ * once per device on the first call made with that device current.  The call
+ * allocates and frees nothing.  Every call on a GPU shares that GPU's array,
+ * so calls that overlap on one GPU (other streams, other host threads) race;
+ * nothing in the array needs to start at zero (the merge always runs as a
+ * second kernel).  IQ_ERR_SCRATCH (nothing enqueued) when the call's plan
+ * needs more than the array holds (iq_decode_workspace_bytes of the same
+ * arguments > IQ_NOALLOC_SCRATCH_BYTES); IQ_ERR_DEVICE when the array cannot
+ * be located on the current device; other errors as iq_decode_step.
+ */
+enum { IQ_NOALLOC_SCRATCH_BYTES = 32 << 20 };
+iq_status iq_decode_step_noalloc(const iq_cache *cache, const void *rot_dev, const void *q_dev,
+                                 int32_t q_dtype, int32_t batch, int32_t n_q_heads,
+                                 const void *k_new_dev, const void *v_new_dev, int32_t kv_dtype,
+                                 const int32_t *block_table_dev, int32_t max_pages_per_seq,
+                                 const int32_t *seq_lens_dev, int32_t max_seq_len, float softmax_scale,
+                                 float *out_dev, hipStream_t stream);
 
 /* iq_decode_step with the options of iq_decode_attention_ex. */
 iq_status iq_decode_step_ex(const iq_cache *cache, const void *rot_dev, const void *q_dev,

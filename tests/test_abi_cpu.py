@@ -35,7 +35,8 @@ def test_header_declarations_are_exported_and_bound():
 def test_status_strings_and_sizes():
     for code, text in [(0, "ok"), (-1, "invalid argument"), (-2, "unsupported configuration"),
                        (-3, "workspace too small"), (-4, "HIP copy or kernel launch failed"),
-                       (-5, "no usable HIP device")]:
+                       (-5, "no usable HIP device"),
+                       (-6, "call needs more scratch than the library's static array holds")]:
         assert iq.status_string(code) == text
     assert iq.status_string(7) == "unknown status"
     assert L.iq_version() == 10000
@@ -256,3 +257,23 @@ def test_prefill_options_validation():
     o = iq.PrefillOptions(4)
     assert L.iq_prefill_attention_ex(c, FAKE, FAKE, 1, 0, 64, 0, FAKE, 8, 0.0, FAKE, FAKE, 0,
                                      ctypes.byref(o), None) == 0
+
+
+def _noalloc(c, batch=1, hq=32, max_len=1024, max_pages=16, out=FAKE, k_new=FAKE):
+    return L.iq_decode_step_noalloc(c, FAKE, FAKE, 1, batch, hq, k_new, FAKE, 1, FAKE, max_pages, FAKE,
+                                    max_len, 0.0, out, None)
+
+
+def test_decode_step_noalloc_validation():
+    """The no-allocation decode step refuses bad arguments, and calls whose plan
+    needs more than the static scratch, on the host before touching a device."""
+    c = _cache(hkv=4)
+    assert _noalloc(c, out=None) == -1
+    assert _noalloc(c, k_new=None) == -1
+    assert _noalloc(c, hq=30) == -1
+    assert _noalloc(c, max_len=2000, max_pages=16) == -1
+    assert _noalloc(c, hq=4 * 17) == -2
+    big = _cache(hkv=16)
+    need = iq.decode_workspace_bytes(64, 256, 16, 65536, iq.DecodeOptions(merge=iq.IQ_MERGE_KERNEL))
+    assert need > iq.NOALLOC_SCRATCH_BYTES
+    assert _noalloc(big, batch=64, hq=256, max_len=65536, max_pages=1024) == -6
