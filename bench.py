@@ -34,13 +34,16 @@ MFMA_F16_PEAK_TFLOPS = 2500.0    # MI355X dense f16 matrix peak, published
 METRIC = "packed-KV decode attention GB/s (% of HBM peak) + tokens/s at 32K ctx"
 REC_BYTES = 100                  # K + V records per (token, kv head): 2 x (48 + 2)
 REC_BYTES4 = 132                 # the same with 4-bit records: 2 x (64 + 2)
+FLUSH_BYTES = 2 << 30            # streamed before every timed region (> the 256 MB Infinity Cache)
 
 
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=160)
+    ap.add_argument("--warmup", type=int, default=160, help="minimum untimed warm-up steps")
+    ap.add_argument("--warmup-seconds", type=float, default=0.1,
+                    help="minimum wall time of untimed warm-up replays before each timed region")
     ap.add_argument("--workload", default="gqa_decode_32k_32q4kv")
     ap.add_argument("--bits", type=int, default=3, choices=(3, 4),
                     help="record width of the measured packed cache (3: the method's; 4: the 4-bit variant)")
@@ -87,12 +90,8 @@ class DecodeLayer:
                 scale[h, torch.from_numpy(outl[h]).to(device)] = 10.0
         seq_idx = torch.cat([torch.full((n,), b, dtype=torch.int32) for b, n in enumerate(n_prev)]).to(device)
         pos = torch.cat([torch.arange(n, dtype=torch.int32) for n in n_prev]).to(device)
-        chunk = 1 << 16
-        for s in range(0, total, chunk):
-            e = min(total, s + chunk)
-            k = (synth.draw_normal_device(seed * 7 + s, (e - s, w.n_kv_heads, 128), torch.float32, device)
-                 * scale).to(dt)
-            v = synth.draw_normal_device(seed * 11 + s, (e - s, w.n_kv_heads, 128), dt, device)
+        self.seed, self.scale, self.dt, self.n_prev, self.device = seed, scale, dt, n_prev, device
+        for s, e, k, v in self._chunks():
             iq.quantize_append(self.cache, self.rot, k, v, seq_idx[s:e], pos[s:e], block_table)
         # the current token of every sequence (position len-1) and the queries
         b = w.batch
@@ -103,6 +102,36 @@ class DecodeLayer:
         self.seq_new = torch.arange(b, dtype=torch.int32, device=device)
         self.pos_new = torch.tensor(n_prev, dtype=torch.int32, device=device)
         self.out = torch.empty((b, w.n_q_heads, 128), dtype=torch.float32, device=device)
+        self.w = w
+
+    def _chunks(self, chunk=1 << 16):
+        """The cached tokens' K and V rows (all sequences in order), as drawn."""
+        import torch
+        from compressed_space_attention_amd import synth
+        total, hkv = sum(self.n_prev), self.scale.shape[0]
+        for s in range(0, total, chunk):
+            e = min(total, s + chunk)
+            k = (synth.draw_normal_device(self.seed * 7 + s, (e - s, hkv, 128), torch.float32, self.device)
+                 * self.scale).to(self.dt)
+            v = synth.draw_normal_device(self.seed * 11 + s, (e - s, hkv, 128), self.dt, self.device)
+            yield s, e, k, v
+
+    def kv_host(self):
+        """Per sequence, float32 host copies of every K and V row the step's
+        attention covers (the cached tokens, then the current one), exactly
+        as the kernels received them."""
+        ks, vs = [], []
+        for _, _, k, v in self._chunks():
+            ks.append(k.float().cpu().numpy())
+            vs.append(v.float().cpu().numpy())
+        k_all, v_all = np.concatenate(ks), np.concatenate(vs)
+        kn, vn = self.k_new.float().cpu().numpy(), self.v_new.float().cpu().numpy()
+        kx, vx, at = [], [], 0
+        for b, n in enumerate(self.n_prev):
+            kx.append(np.concatenate([k_all[at:at + n], kn[b:b + 1]]))
+            vx.append(np.concatenate([v_all[at:at + n], vn[b:b + 1]]))
+            at += n
+        return kx, vx
 
 
 def measured_traffic(workload: str):
@@ -171,10 +200,16 @@ def run_decode(args):
         for i in range(n):
             step(layers[(start + i) % ring], mode)
 
-    # warmup (eager)
-    run_steps(args.warmup, 0)
+    # one untimed eager pass over the ring (every layer's new token appended,
+    # kernels loaded)
+    run_steps(ring, 0)
     run_steps(2, 0, "pair")
     torch.cuda.synchronize()
+    # a 2 GiB buffer streamed through the read probe right before each timed
+    # region: whatever layers the warm-up left in the 256 MB Infinity Cache
+    # are evicted, so the timed steps read their packed KV from HBM
+    flush_buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=device)
+    flush_sink = torch.empty(iq.probe_sink_bytes(), dtype=torch.uint8, device=device)
 
     def make_graph(n, mode):
         g = torch.cuda.CUDAGraph()
@@ -187,30 +222,38 @@ def run_decode(args):
         return g
 
     def timed(n_steps, mode):
-        """Time exactly n_steps steps; returns seconds measured by HIP events."""
+        """Seconds for exactly n_steps steps (HIP events on the launch stream):
+        whole rings of distinct layer caches, then the first n_steps % ring
+        layers, after a warm-up of at least args.warmup_seconds (and
+        args.warmup steps) of ring replays and a cache flush."""
         stream = torch.cuda.current_stream()
-        if args.no_graph:
-            torch.cuda.synchronize()
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            run_steps(n_steps, 0, mode)
-            b.record(stream)
-            torch.cuda.synchronize()
-            return a.elapsed_time(b) / 1e3
         full, rem = divmod(n_steps, ring)
-        g_full = make_graph(ring, mode) if full else None
-        g_rem = make_graph(rem, mode) if rem else None
-        if g_full:
-            g_full.replay()      # one untimed replay: the graph's first launch uploads it
-        if g_rem:
-            g_rem.replay()
-        torch.cuda.synchronize()
+        if args.no_graph:
+            warm = lambda: run_steps(ring, 0, mode)
+            timed_run = lambda: run_steps(n_steps, 0, mode)
+        else:
+            g_ring = make_graph(ring, mode)
+            g_rem = make_graph(rem, mode) if rem else None
+            warm = g_ring.replay
+
+            def timed_run():
+                for _ in range(full):
+                    g_ring.replay()
+                if g_rem:
+                    g_rem.replay()
+        t0, done = time.perf_counter(), 0
+        while True:
+            warm()
+            done += ring
+            torch.cuda.synchronize()
+            if done >= args.warmup and time.perf_counter() - t0 >= args.warmup_seconds:
+                break
+        if not args.no_graph and g_rem:
+            g_rem.replay()  # its first launch uploads the graph: not in the timed region
+        iq.probe_read(flush_buf, flush_sink)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
-        for _ in range(full):
-            g_full.replay()
-        if g_rem:
-            g_rem.replay()
+        timed_run()
         b.record(stream)
         torch.cuda.synchronize()
         return a.elapsed_time(b) / 1e3
@@ -222,6 +265,29 @@ def run_decode(args):
     dec_gbs = kv_bytes / t_decode / 1e9
     log(f"[bench] step {t_step * 1e6:.2f} us ({gbs:.0f} GB/s), decode call {t_decode * 1e6:.2f} us "
         f"({dec_gbs:.0f} GB/s), unfused append + decode {t_pair * 1e6:.2f} us")
+
+    # Quality of the benchmarked layer's step output: cosine against plain
+    # fp64 softmax attention over the uncompressed (bf16) K/V, per query head.
+    layer0 = layers[0]
+    run_steps(1, 0)
+    torch.cuda.synchronize()
+    kx, vx = layer0.kv_host()
+    out0 = layer0.out.double().cpu()
+    qh = layer0.q.double().cpu()
+    cos = []
+    for b in range(w.batch):
+        for h in range(w.n_q_heads):
+            g = h // w.group
+            k = torch.from_numpy(kx[b][:, g]).double()
+            v = torch.from_numpy(vx[b][:, g]).double()
+            ref = torch.softmax((k @ qh[b, h]) / math.sqrt(128), dim=0) @ v
+            cos.append(float(torch.nn.functional.cosine_similarity(out0[b, h], ref, dim=0)))
+    quality = {"cosine_vs_uncompressed_min": round(min(cos), 5),
+               "cosine_vs_uncompressed_mean": round(float(np.mean(cos)), 5),
+               "rows": len(cos),
+               "reference": "plain fp64 softmax attention over the layer's bf16 K/V (not quantised)"}
+    log(f"[bench] cosine vs uncompressed attention: min {quality['cosine_vs_uncompressed_min']}, "
+        f"mean {quality['cosine_vs_uncompressed_mean']} over {len(cos)} rows")
 
     result = {
         "metric": METRIC,
@@ -243,6 +309,8 @@ def run_decode(args):
             "workload": w.name, "batch": w.batch, "context": max_len, "n_q_heads": w.n_q_heads,
             "n_kv_heads": w.n_kv_heads, "head_dim": 128, "page_tokens": 64, "record_bits": args.bits,
             "packed_kv_bytes_per_step": kv_bytes, "layer_ring": ring,
+            "distinct_bytes_timed": min(args.steps, ring) * kv_bytes,
+            "flush_bytes_before_timed": FLUSH_BYTES, "warmup_seconds_min": args.warmup_seconds,
             "step": "one layer's decode step: quantise-append of the current token fused into "
                     "decode attention (iq_decode_step)",
         },
@@ -262,9 +330,9 @@ def run_decode(args):
             "step_us": round(t_step * 1e6, 3),
             "unfused_append_then_decode_us": round(t_pair * 1e6, 3),
             "tokens_per_s_per_layer": round(w.batch / t_step, 1),
+            "quality": quality,
         },
     }
-    layer0 = layers[0]
     if not args.no_aux:
         del layers
         torch.cuda.empty_cache()
@@ -558,52 +626,136 @@ def run_dense_prefill_aux(fmt="bf16"):
             "prefill_tflops": round(tf, 2), "prefill_frac_of_f16_peak": round(tf / MFMA_F16_PEAK_TFLOPS, 4)}
 
 
+# ---- CPU oracle baseline: independent (sequence, kv head) units in worker
+# processes (spawned: they import numpy and the oracle, never the GPU stack) ----
+_CPU_STATE = {}
+
+
+def _cpu_worker_init(path, meta):
+    """Load the layer's host cache (memory-mapped) and inputs; one BLAS thread."""
+    import threadpoolctl
+    threadpoolctl.threadpool_limits(1)
+    arrays = np.load(path, mmap_mode="r")
+    _CPU_STATE.clear()
+    _CPU_STATE.update({k: arrays[k] for k in arrays.files})
+    _CPU_STATE.update(meta)
+
+
+def _cpu_unit_step(unit):
+    """One (sequence b, kv head g) unit of a decode step, with the oracle as it
+    stands: quantise-append of the unit's new K/V row, then decode attention
+    of the group's query heads over the unit's tokens."""
+    from oracle import isoquant4_oracle as O4
+    from oracle import isoquant_oracle as O
+    b, g = unit
+    st = _CPU_STATE
+    four = st["bits"] == 4
+    names = ("k_codes", "k_norms", "v_codes", "v_norms")
+    # the unit's kv head as a one-head cache (a private copy: the append writes it)
+    sub = [np.array(st[n][:, g:g + 1]) for n in names]
+    cache = (O4.PagedCache4 if four else O.PagedCache).from_arrays(*sub)
+    blocks = st["blocks"][g:g + 1]
+    bt = st["block_table"][b:b + 1]
+    grp = st["group"]
+    append = O4.quantize_append4 if four else O.quantize_append
+    decode = O4.decode_attention4 if four else O.decode_attention
+    append(cache, blocks, st["k_new"][b:b + 1, g:g + 1], st["v_new"][b:b + 1, g:g + 1],
+           np.zeros(1, np.int32), st["pos_new"][b:b + 1], bt)
+    return decode(cache, blocks, st["q"][b:b + 1, g * grp:(g + 1) * grp], bt, st["lens"][b:b + 1])
+
+
 def cpu_baseline_decode(args, w, layer, bt_np, lens):
-    """The CPU oracle, as it stands, on a bounded sample of the same step:
-    quantise-append the current token, then decode over the layer's cache."""
+    """The CPU oracle, as it stands, on a bounded sample of the same step
+    (quantise-append the current token, then decode over the layer's cache):
+    the batch's independent (sequence, kv head) units spread over worker
+    processes (one core each), and the same units on one core; plus the
+    oracle's check of the benchmarked layer's codes (every record the GPU
+    wrote, re-quantised by the oracle)."""
+    import multiprocessing as mp
+    import tempfile
+
     import threadpoolctl
 
+    from compressed_space_attention_amd import synth
     from oracle import isoquant4_oracle as O4
     from oracle import isoquant_oracle as O
 
     four = layer.cache.bits == 4
-    host = (O4.PagedCache4 if four else O.PagedCache).from_arrays(*layer.cache.to_host())
-    append = O4.quantize_append4 if four else O.quantize_append
-    decode = O4.decode_attention4 if four else O.decode_attention
-    from compressed_space_attention_amd import synth
+    kc, kn, vc, vn = layer.cache.to_host()
     quats = synth.quaternions(w.seed * 1000 + layer.idx, w.n_kv_heads)
     blocks = O.rotation_matrices(quats)
-    q = layer.q.float().cpu().numpy().astype(np.float64)
-    k_new = layer.k_new.float().cpu().numpy().astype(np.float64)
-    v_new = layer.v_new.float().cpu().numpy().astype(np.float64)
-    pos_new = layer.pos_new.cpu().numpy()
-    seq_new = layer.seq_new.cpu().numpy()
-    kv_bytes = (REC_BYTES4 if four else REC_BYTES) * int(lens.sum()) * w.n_kv_heads
-    info = threadpoolctl.threadpool_info()
-    threads = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
-    def run(seconds):
-        steps, t0 = 0, time.perf_counter()
-        while True:
-            append(host, blocks, k_new, v_new, seq_new, pos_new, bt_np)
-            decode(host, blocks, q, bt_np, lens)
-            steps += 1
-            el = time.perf_counter() - t0
-            if el >= seconds or el * (steps + 1) / steps > 3 * seconds:
-                return steps, el
+    meta = {"bits": 4 if four else 3, "group": w.group}
+    arrays = {"k_codes": kc, "k_norms": kn, "v_codes": vc, "v_norms": vn, "blocks": blocks,
+              "block_table": bt_np, "lens": np.asarray(lens),
+              "q": layer.q.float().cpu().numpy().astype(np.float64),
+              "k_new": layer.k_new.float().cpu().numpy().astype(np.float64),
+              "v_new": layer.v_new.float().cpu().numpy().astype(np.float64),
+              "pos_new": layer.pos_new.cpu().numpy()}
+    kv_bytes = (REC_BYTES4 if four else REC_BYTES) * int(np.sum(lens)) * w.n_kv_heads
+    units = [(b, g) for b in range(w.batch) for g in range(w.n_kv_heads)]
+    procs = max(1, min(len(units), os.cpu_count() or 1, 16))
+    fd, path = tempfile.mkstemp(suffix=".npz", dir="/tmp")
+    os.close(fd)
+    try:
+        np.savez(path, **arrays)
 
-    steps, el = run(args.cpu_seconds)
-    with threadpoolctl.threadpool_limits(1):       # the same oracle on one core
-        steps1, el1 = run(args.cpu_seconds / 2)
+        def run(step_fn, seconds):
+            steps, t0 = 0, time.perf_counter()
+            while True:
+                step_fn()
+                steps += 1
+                el = time.perf_counter() - t0
+                if el >= seconds or el * (steps + 1) / steps > 3 * seconds:
+                    return steps, el
+
+        ctx = mp.get_context("spawn")
+        with ctx.Pool(procs, initializer=_cpu_worker_init, initargs=(path, meta)) as pool:
+            pool.map(_cpu_unit_step, units[:procs])          # workers started and warm
+            steps, el = run(lambda: pool.map(_cpu_unit_step, units, chunksize=1), args.cpu_seconds)
+        _cpu_worker_init(path, meta)                          # the same units on one core, here
+        with threadpoolctl.threadpool_limits(1):
+            steps1, el1 = run(lambda: [_cpu_unit_step(u) for u in units], args.cpu_seconds / 2)
+    finally:
+        _CPU_STATE.clear()
+        os.remove(path)
+
+    # the oracle's check of every record of the benchmarked layer (all tokens
+    # of every sequence, the appended one included)
+    host = (O4.PagedCache4 if four else O.PagedCache).from_arrays(kc, kn, vc, vn)
+    kx, vx = layer.kv_host()
+    codes = mism = near = off = norm_mism = norm_off = 0
+    for name, x in (("k", kx), ("v", vx)):
+        for h in range(w.n_kv_heads):
+            for b, n in enumerate(lens):
+                n = int(n)
+                page, slot = bt_np[b, np.arange(n) // 64], np.arange(n) % 64
+                qz = (O4.quantize4 if four else O.quantize)(x[b][:, h], blocks[h])
+                gc = host.codes(name, page, h, slot) if four else O.unpack_codes(host.records(name, page, h, slot))
+                bad = gc != qz["codes"]
+                codes += gc.size
+                mism += int(bad.sum())
+                near += int(qz["near"].sum())
+                off += int((bad & ~qz["near"]).sum())
+                nbad = getattr(host, name + "_norms")[page, h, slot] != qz["norm16"]
+                norm_mism += int(nbad.sum())
+                norm_off += int((nbad & ~qz["norm_near"]).sum())
     return {
         "value": round(kv_bytes * steps / el / 1e9, 5),
         "unit": "GB/s",
-        "cores": int(threads),
+        "cores": procs,
         "kind": "oracle",
-        "sample": f"{steps} {'4-bit ' if four else ''}oracle steps of one layer (append 1 token + decode over "
-                  f"{int(lens.max())} tokens, {w.n_q_heads}q/{w.n_kv_heads}kv) in {el:.1f} s; "
-                  f"host has {os.cpu_count()} logical CPUs",
+        "sample": f"{steps} oracle steps of one layer ({'4-bit ' if four else ''}append 1 token + decode over "
+                  f"{int(np.max(lens))} tokens, {w.n_q_heads}q/{w.n_kv_heads}kv) in {el:.1f} s, its "
+                  f"{len(units)} (sequence, kv head) units over {procs} worker processes (one BLAS thread "
+                  f"each); host has {os.cpu_count()} logical CPUs",
         "single_thread": {"value": round(kv_bytes * steps1 / el1 / 1e9, 5), "unit": "GB/s", "cores": 1,
                           "sample": f"{steps1} steps in {el1:.1f} s"},
+        "oracle_code_check": {"codes": codes, "mismatches": mism, "near_boundary": near,
+                              "mismatch_frac": mism / codes, "near_boundary_frac": near / codes,
+                              "mismatches_off_boundary": off, "norm_mismatches": norm_mism,
+                              "norm_mismatches_off_midpoint": norm_off,
+                              "records": "every K and V record of the benchmarked layer, re-quantised by "
+                                         "the oracle from the same bf16 inputs"},
     }
 
 
