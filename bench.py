@@ -578,6 +578,17 @@ def run_prefill_aux(bits=3):
     t_app = median_call_seconds(lambda: iq.quantize_append(cache, rot, k2, v2, s2, p2, bt), calls=30)
     t_pre = median_call_seconds(lambda: iq.prefill_attention(cache, rot, q, p.q_start, bt[0], out=out,
                                                              workspace=ws))
+    # the chunk's quantise-append and the prefill over it: one fused call
+    # against the two calls back to back
+    ws_pa = iq.prefill_append_workspace(p.n_queries, p.n_q_heads, p.n_kv_heads, p.q_start, dev)
+
+    def two_calls():
+        iq.quantize_append(cache, rot, k2, v2, s2, p2, bt)
+        iq.prefill_attention(cache, rot, q, p.q_start, bt[0], out=out, workspace=ws)
+
+    t_two = median_call_seconds(two_calls)
+    t_fused = median_call_seconds(lambda: iq.prefill_append(cache, rot, k2, v2, p.cached, q, p.q_start, bt[0],
+                                                            out=out, workspace=ws_pa))
     # algorithmic flops: 2 d for q.k and 2 d for p.v per (query head, key) pair
     keys = sum(p.q_start + i + 1 for i in range(p.n_queries))
     flops = 4.0 * 128 * p.n_q_heads * keys
@@ -594,6 +605,9 @@ def run_prefill_aux(bits=3):
         "prefill_tflops": round(tf, 2),
         "prefill_frac_of_f16_peak": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
         "prefill_mfma_tflops_issued": round(1.5 * tf, 2),  # q.k runs as two f16 products
+        "append_then_prefill_us": round(t_two * 1e6, 2),
+        "fused_append_prefill_us": round(t_fused * 1e6, 2),
+        "fused_append_prefill_launches": iq.prefill_append_launches(p.n_queries, p.n_q_heads, p.n_kv_heads, bits),
     }
 
 

@@ -429,6 +429,72 @@ iq_status iq_prefill_attention(const iq_cache* cache, const void* rot_dev, const
                                  stream);
 }
 
+size_t iq_prefill_append_workspace_bytes(int32_t n_q, int32_t n_q_heads, int32_t n_kv_heads,
+                                         int32_t q_start_pos) {
+  if (n_q < 0 || n_q_heads < 1 || n_kv_heads < 1 || q_start_pos < 0) return 0;
+  const size_t base = n_q > 0 ? iq_prefill_workspace_bytes(n_q, n_q_heads, n_kv_heads, q_start_pos) : 0;
+  return iq::kWsCounterBytes + base;
+}
+
+int32_t iq_prefill_append_launches(int32_t n_q, int32_t n_q_heads, int32_t n_kv_heads, int32_t bits) {
+  if (n_q < 1 || n_q_heads < 1 || n_kv_heads < 1 || n_q_heads % n_kv_heads != 0 || (bits != 3 && bits != 4))
+    return IQ_ERR_INVALID_ARG;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return IQ_ERR_DEVICE;
+  const int cus = device_cu_count();
+  const iq::PrefillPlan plan = iq::plan_prefill(n_q, n_q_heads, n_kv_heads, 0, cus);
+  return iq::prefill_append_fused(plan, n_kv_heads, bits, cus) ? 1 : 2;
+}
+
+iq_status iq_prefill_append(const iq_cache* cache, const void* rot_dev, const void* k_new_dev,
+                            const void* v_new_dev, int32_t kv_dtype, int32_t n_new, int32_t new_start,
+                            const void* q_dev, int32_t q_dtype, int32_t n_q, int32_t n_q_heads,
+                            int32_t q_start_pos, const int32_t* block_table_dev, int32_t max_pages,
+                            float softmax_scale, float* out_dev, void* workspace_dev,
+                            size_t workspace_bytes, hipStream_t stream) {
+  if (!cache_ok(cache) || !rot_dev || n_new < 0 || new_start < 0 || n_q < 0 || n_q_heads < 1 ||
+      q_start_pos < 0 || !block_table_dev || max_pages < 1 || !workspace_dev)
+    return IQ_ERR_INVALID_ARG;
+  if (n_new > 0 && (!k_new_dev || !v_new_dev || !dtype_ok(kv_dtype))) return IQ_ERR_INVALID_ARG;
+  if (n_q > 0 && (!q_dev || !dtype_ok(q_dtype) || !out_dev)) return IQ_ERR_INVALID_ARG;
+  if ((int64_t)new_start + n_new > (int64_t)max_pages * IQ_PAGE_TOKENS) return IQ_ERR_INVALID_ARG;
+  if (n_q_heads % cache->n_kv_heads != 0) return IQ_ERR_INVALID_ARG;
+  if ((int64_t)q_start_pos + n_q > (int64_t)max_pages * IQ_PAGE_TOKENS) return IQ_ERR_INVALID_ARG;
+  const int group = n_q_heads / cache->n_kv_heads;
+  if (n_q > 0) {
+    if (!pow2(group) || group > 128 || cache->n_kv_heads > 65535) return IQ_ERR_UNSUPPORTED;
+    if ((int64_t)q_start_pos + n_q > (int64_t)iq::kPrefillMaxPages * IQ_PAGE_TOKENS) return IQ_ERR_UNSUPPORTED;
+  }
+  if (workspace_bytes < iq_prefill_append_workspace_bytes(n_q, n_q_heads, cache->n_kv_heads, q_start_pos))
+    return IQ_ERR_WORKSPACE;
+  const iq::CacheView c = view(cache);
+  const float* rot = reinterpret_cast<const float*>(rot_dev);
+  if (n_q == 0)
+    return n_new == 0 ? IQ_OK
+                      : launch_status(iq::launch_quantize_append_range(c, rot, k_new_dev, v_new_dev, kv_dtype,
+                                                                       n_new, new_start, block_table_dev,
+                                                                       max_pages, stream));
+  const int cus = device_cu_count();
+  const iq::PrefillPlan plan = iq::plan_prefill(n_q, n_q_heads, cache->n_kv_heads, q_start_pos, cus);
+  if (plan.row_tiles > 65535) return IQ_ERR_UNSUPPORTED;
+  const float scale = resolve_scale(softmax_scale);
+  if (n_new > 0 && iq::prefill_append_fused(plan, cache->n_kv_heads, c.bits, cus)) {
+    const iq::PrefillAppend app{k_new_dev, v_new_dev, kv_dtype, n_new, new_start,
+                                reinterpret_cast<uint32_t*>(workspace_dev)};
+    return launch_status(iq::launch_prefill_args(c, rot, q_dev, q_dtype, 1, n_q, n_q_heads, nullptr,
+                                                 q_start_pos, nullptr, block_table_dev, max_pages, plan,
+                                                 scale, out_dev, &app, stream));
+  }
+  if (n_new > 0) {
+    const hipError_t e = iq::launch_quantize_append_range(c, rot, k_new_dev, v_new_dev, kv_dtype, n_new,
+                                                          new_start, block_table_dev, max_pages, stream);
+    if (e != hipSuccess) return IQ_ERR_LAUNCH;
+  }
+  return launch_status(iq::launch_prefill(c, rot, q_dev, q_dtype, n_q, n_q_heads, q_start_pos, block_table_dev,
+                                          max_pages, plan, scale, out_dev,
+                                          static_cast<uint8_t*>(workspace_dev) + iq::kWsCounterBytes, stream));
+}
+
 iq_status iq_prefill_attention_varlen(const iq_cache* cache, const void* rot_dev, const void* q_dev,
                                       int32_t q_dtype, int32_t batch, int32_t n_q_heads, int32_t total_q,
                                       const int32_t* cu_q_dev, const int32_t* q_start_dev,

@@ -169,6 +169,45 @@ __device__ __forceinline__ uint16_t float_to_half_sat(float x) {
   return b;
 }
 
+// load32 in two halves, so that a load can be issued well before its data is
+// needed: the raw 16-byte chunks (8 for fp32, 4 for the 16-bit types), then
+// their conversion.
+__device__ __forceinline__ void load32_raw(const void* base, size_t idx, int dtype, u4 r[8]) {
+  if (dtype == 0) {
+    const u4* p = reinterpret_cast<const u4*>(reinterpret_cast<const float*>(base) + idx);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = p[i];
+  } else {
+    const u4* p = reinterpret_cast<const u4*>(reinterpret_cast<const uint16_t*>(base) + idx);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = p[i];
+  }
+}
+__device__ __forceinline__ void raw_to_f32(const u4 r[8], int dtype, float x[32]) {
+  if (dtype == 0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) x[4 * i + k] = __builtin_bit_cast(float, r[i][k]);
+  } else if (dtype == 1) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        x[8 * i + 2 * k] = __builtin_bit_cast(float, r[i][k] << 16);
+        x[8 * i + 2 * k + 1] = __builtin_bit_cast(float, r[i][k] & 0xFFFF0000u);
+      }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        x[8 * i + 2 * k] = (float)__builtin_bit_cast(_Float16, (uint16_t)(r[i][k] & 0xFFFFu));
+        x[8 * i + 2 * k + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(r[i][k] >> 16));
+      }
+  }
+}
+
 __device__ __forceinline__ float load_as_float(const void* base, size_t idx, int dtype) {
   if (dtype == 0) return reinterpret_cast<const float*>(base)[idx];
   if (dtype == 1) {
@@ -552,6 +591,162 @@ __device__ __forceinline__ void so4_forward_quarter(const float* __restrict__ ro
       z[4 * bb + r] = row[0] * y[4 * bb] + row[1] * y[4 * bb + 1] + row[2] * y[4 * bb + 2] +
                       row[3] * y[4 * bb + 3];
     }
+  }
+}
+
+// One vector held by a quad of lanes (lane quarter j = coordinates 32j ..
+// 32j + 31 in x): its norm (returned) and codes.  sel[bb] holds the codes
+// (3-bit) or nibbles (4-bit) of coordinates 32j + 4bb .. + 3, one per byte;
+// s_rot is the kv head's rotation blocks in LDS.  The quantise-append kernel
+// and the fused append of the chunked prefill both code vectors through this
+// one function, so their records are byte-identical.
+template <int BITS>
+__device__ __forceinline__ float quad_codes(float x[32], int j, const float* s_rot, const Levels4& lv,
+                                            uint32_t sel[8]) {
+  float ss0 = 0.f, ss1 = 0.f, ss2 = 0.f, ss3 = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; i += 4) {
+    ss0 = fmaf(x[i], x[i], ss0);
+    ss1 = fmaf(x[i + 1], x[i + 1], ss1);
+    ss2 = fmaf(x[i + 2], x[i + 2], ss2);
+    ss3 = fmaf(x[i + 3], x[i + 3], ss3);
+  }
+  float ss = (ss0 + ss1) + (ss2 + ss3);
+  ss += quad_xor1(ss);
+  ss += quad_xor2(ss);
+  const float n = sqrtf(ss);
+
+  wht128_quad(x, j);
+  // SO(4) block by block (blocks 8j .. 8j + 7 of the quarter), each block's
+  // four outputs turned into codes at once: sel[bb] holds the codes (3-bit)
+  // or nibbles (4-bit) of coordinates 32j + 4bb .. + 3, one per byte.  The
+  // zero vector is coded through inv_n = 0: every u is then +-0, which codes
+  // as 4 (resp. nibble 0 = code 8), so no coordinate needs a branch.  The
+  // empty asm makes each block's rotation rows (LDS) depend on the previous
+  // block's codes: otherwise the compiler reads all 32 rows up front and holds
+  // 128 of them in registers (204 VGPRs instead of 62, a third of the waves).
+  {
+    const float inv_n = n > 0.f ? 1.0f / n : 0.f;
+    uint32_t prev = 0;
+#pragma unroll
+    for (int bb = 0; bb < 8; ++bb) {
+      int off = (8 * j + bb) * 16;
+      asm volatile("" : "+v"(off) : "v"(prev));
+      const f4* m = reinterpret_cast<const f4*>(s_rot + off);
+      uint32_t w = 0;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const f4 row = m[r];
+        const float zr = row[0] * x[4 * bb] + row[1] * x[4 * bb + 1] + row[2] * x[4 * bb + 2] +
+                         row[3] * x[4 * bb + 3];
+        uint32_t c;
+        if constexpr (BITS == 3) c = code_of(zr * inv_n);
+        else c = nibble_of(zr * inv_n, lv);
+        w |= c << (8 * r);
+      }
+      sel[bb] = w;
+      prev = w;
+    }
+  }
+
+  return n;
+}
+
+
+// Stores of the quantisers: plain ones, and device-scope ones (complete where
+// every XCD sees them, not in this XCD's L2) for records that workgroups of
+// the same launch on other XCDs read.  Vector stores only.
+struct PlainStore {
+  static __device__ __forceinline__ void b8(uint8_t* p, uint32_t v) { *p = (uint8_t)v; }
+  static __device__ __forceinline__ void b16(uint16_t* p, uint32_t v) { *p = (uint16_t)v; }
+  static __device__ __forceinline__ void b96(uint8_t* p, const u3& w) { *reinterpret_cast<u3*>(p) = w; }
+  static __device__ __forceinline__ void b128(uint8_t* p, const u4& w) { *reinterpret_cast<u4*>(p) = w; }
+};
+typedef uint32_t u3v __attribute__((ext_vector_type(3)));
+struct DeviceStore {
+  static __device__ __forceinline__ void b8(uint8_t* p, uint32_t v) {
+    asm volatile("global_store_byte %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
+  }
+  static __device__ __forceinline__ void b16(uint16_t* p, uint32_t v) {
+    asm volatile("global_store_short %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
+  }
+  static __device__ __forceinline__ void b96(uint8_t* p, const u3& w) {
+    const u3v v = {w.x, w.y, w.z};
+    asm volatile("global_store_dwordx3 %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
+  }
+  static __device__ __forceinline__ void b128(uint8_t* p, const u4& w) {
+    asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(p), "v"(w) : "memory");
+  }
+};
+
+// The record of quad_codes' vector in `slot` of a (page, kv head) block:
+// codes = the block's code bytes, norms = its 64 fp16 norms.  K records are
+// slot-ordered; V bytes go to the matrix-core order of the decode kernels
+// (see the cache layout in isoquant.h).  whole: the workgroup's 256 threads
+// (64 quads) hold the page's 64 slots in order, so the V block is assembled in
+// s_v (LDS) and written out as one contiguous run after a workgroup barrier
+// (every thread of the workgroup must call this then); otherwise each quad
+// stores its own bytes.  stored = false: nothing is written (the vector's
+// position or page lies outside the table or the cache).  t = the thread's
+// index in the workgroup.
+// UNIFORM_BARRIER: the barrier of a V record is taken whether or not the page
+// is whole (for callers whose workgroup halves code different blocks).
+template <int BITS, class S, bool UNIFORM_BARRIER = false>
+__device__ __forceinline__ void quad_store(bool is_v, bool stored, bool whole, int j, int slot,
+                                           const uint32_t sel[8], float n, uint8_t* codes,
+                                           uint16_t* norms, uint8_t* s_v, int t) {
+  constexpr int kRecB = BITS == 4 ? kRec4 : kRec;
+  if constexpr (BITS == 3) {
+    u3 w;
+    selectors_to_group(sel, w.x, w.y, w.z);
+    if (!is_v) {
+      if (stored) S::b96(codes + slot * kRec + 12 * j, w);
+    } else if (stored) {
+      // byte lane b of this group goes to region n = 4j + b (quad q of the
+      // slot), chunk c = slot / 16, byte lane r = slot % 4
+      const int c = slot >> 4, q = (slot >> 2) & 3, r = slot & 3;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int off = (4 * j + b + 16 * q) * kRec + 12 * c + r;
+        const uint32_t b0 = (w.x >> (8 * b)) & 0xFF, b1 = (w.y >> (8 * b)) & 0xFF, b2 = (w.z >> (8 * b)) & 0xFF;
+        if (whole) {
+          s_v[off] = (uint8_t)b0; s_v[off + 4] = (uint8_t)b1; s_v[off + 8] = (uint8_t)b2;
+        } else {
+          S::b8(codes + off, b0); S::b8(codes + off + 4, b1); S::b8(codes + off + 8, b2);
+        }
+      }
+    }
+  } else {
+    if (!is_v) {
+      // record dword 4j + kk: byte b = coordinate 32j + 8kk + b (low nibble,
+      // selector 2kk) and 32j + 8kk + 4 + b (high nibble, selector 2kk + 1)
+      u4 w;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) w[kk] = sel[2 * kk] | (sel[2 * kk + 1] << 4);
+      if (stored) S::b128(codes + slot * kRec4 + 16 * j, w);
+    } else if (stored) {
+      // coordinates 32j + 4p + b (selector p) and + 16 (selector p + 4) share
+      // byte slot % 4 of dword 4p + 2 th + q of region (4j + b) + 16 jq
+      // (slot = 32 th + 16 q + 4 jq + r)
+      const int th = slot >> 5, q = (slot >> 4) & 1, jq = (slot >> 2) & 3, r = slot & 3;
+      const int base = (4 * j + 16 * jq) * 64 + 4 * (2 * th + q) + r;
+#pragma unroll
+      for (int pp = 0; pp < 4; ++pp) {
+        const uint32_t v = sel[pp] | (sel[pp + 4] << 4);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int off = base + 64 * b + 16 * pp;
+          if (whole) s_v[off] = (uint8_t)(v >> (8 * b));
+          else S::b8(codes + off, (v >> (8 * b)) & 0xFF);
+        }
+      }
+    }
+  }
+  if (stored && j == 0) S::b16(norms + slot, float_to_half_sat(n));
+  if (is_v && (whole || UNIFORM_BARRIER)) {
+    __syncthreads();
+    constexpr int kChunks = kPage * kRecB / 16;
+    if (whole && t < kChunks) S::b128(codes + 16 * t, reinterpret_cast<const u4*>(s_v)[t]);
   }
 }
 

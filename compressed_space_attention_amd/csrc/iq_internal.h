@@ -142,6 +142,28 @@ hipError_t launch_prefill(const CacheView& c, const float* rot, const void* q, i
 // cu_q[b+1]-1 (device), its first at position q_starts[b] (device), its
 // block-table row block_table + b * max_pages; plan.row_tiles covers the
 // longest query count.
+// A chunk quantise-appended by the prefill launch itself: tokens new_start ..
+// new_start + n_new - 1 of the (one) sequence, rows [n_new][hkv][128] of
+// dtype; counters = the workspace's counter region (zero at rest).
+struct PrefillAppend {
+  const void* k;
+  const void* v;
+  int dtype, n_new, new_start;
+  uint32_t* counters;
+};
+// Whether the whole prefill grid can be resident at once (the fused append's
+// waits need it).
+bool prefill_append_fused(const PrefillPlan& plan, int hkv, int bits, int num_cus);
+hipError_t launch_prefill_args(const CacheView& c, const float* rot, const void* q, int q_dtype,
+                               int batch, int n_q, int hq, const int32_t* cu_q, int q_start,
+                               const int32_t* q_starts, const int32_t* block_table, int max_pages,
+                               const PrefillPlan& plan, float softmax_scale, float* out,
+                               const PrefillAppend* app, hipStream_t stream);
+// Quantise-append of tokens pos0 .. pos0 + n_tokens - 1 of one sequence
+// (block-table row block_table); the same records as launch_quantize_append.
+hipError_t launch_quantize_append_range(const CacheView& c, const float* rot, const void* k,
+                                        const void* v, int dtype, int n_tokens, int pos0,
+                                        const int32_t* block_table, int max_pages, hipStream_t stream);
 hipError_t launch_prefill_varlen(const CacheView& c, const float* rot, const void* q, int q_dtype,
                                  int batch, int n_q, int hq, const int32_t* cu_q, int q_start,
                                  const int32_t* q_starts, const int32_t* block_table, int max_pages,

@@ -36,6 +36,8 @@
 #include <math.h>
 #include <stdlib.h>
 
+#include <atomic>
+
 #include "iq_device.h"
 #include "iq_internal.h"
 
@@ -89,7 +91,140 @@ struct PrefillArgs {
   float out_factor;    // 1 / (sqrt(128) * alpha)
   float* out;
   Levels4 lv4;         // 4-bit records: thresholds and f16 level tables
+  // Fused quantise-append of the chunk (app_k null: none): tokens new_start ..
+  // new_start + n_new - 1 of this sequence, rows [n_new][hkv][128] of
+  // app_dtype, written into the cache by the workgroups of their kv head
+  // before they read it.  The row tiles of kv head g share its (64-token
+  // block, K|V) jobs; a workgroup adds the jobs it finished to app_arrive[g]
+  // once their records are visible device-wide, and waits for all of them
+  // before requesting the first page that holds appended tokens; the last
+  // workgroup of kv head g to finish clears app_arrive[g] and app_done[g].
+  const void* app_k;
+  const void* app_v;
+  int app_dtype, n_new, new_start, row_tiles;
+  uint8_t* k_codes_w;
+  uint16_t* k_norms_w;
+  uint8_t* v_codes_w;
+  uint16_t* v_norms_w;
+  uint32_t* app_arrive;
+  uint32_t* app_done;
 };
+
+// The wait for the appended pages is bounded (2^20 polls, each a memory round
+// trip: about a second); a wait that runs out leaves NaN rows.
+constexpr uint32_t kAppendSpinLimit = 1u << 20;
+
+// The fused append's share of this workgroup (kv head g, row tile `tile`):
+// K blocks first, then V blocks, 256 threads per block (a quad per token),
+// every workgroup thread in every pass; each pass's rows are requested while
+// the previous pass is coded.  lds: 2 KB for the head's rotation blocks + 4 KB
+// per 256 threads for assembling whole V pages.  Returns the jobs done; their
+// device-scope stores may still be in flight (the caller waits for them
+// before counting the jobs in).
+template <int BITS, int W>
+__device__ __forceinline__ int prefill_append(const PrefillArgs& a, const int32_t* btab, int g, int tile,
+                                              uint8_t* lds) {
+  constexpr int kRecB = BITS == 4 ? kRec4 : kRec;
+  constexpr int kPar = 64 * W / 256;  // blocks coded at once
+  const int tid = threadIdx.x, half = tid >> 8, t = tid & 255, tl = t >> 2, j = t & 3;
+  float* s_rot = reinterpret_cast<float*>(lds);
+  uint8_t* s_vb = lds + 2048 + 4096 * half;
+  if (tid < kRotFloats / 4)
+    reinterpret_cast<f4*>(s_rot)[tid] = reinterpret_cast<const f4*>(a.rot + (size_t)g * kRotFloats)[tid];
+  const int nb = (a.n_new + kPage - 1) / kPage;  // 64-token blocks of the chunk
+  const int stride = a.row_tiles * kPar;
+  const int per_kv = nb > tile * kPar ? (nb - tile * kPar + stride - 1) / stride : 0;  // passes per K | V
+  const int passes = 2 * per_kv;
+  // pass ps: K (ps < per_kv) or V, blocks b0 .. b0 + kPar - 1, this thread's block b0 + half
+  auto pass_block = [&](int ps, int& which) {
+    which = ps >= per_kv;
+    return tile * kPar + (ps - which * per_kv) * stride + half;
+  };
+  auto request = [&](int ps, u4 (&r)[8]) {
+    int which;
+    const int blk = pass_block(ps, which);
+    const int i = blk * kPage + tl;
+    const bool valid = blk < nb && i < a.n_new;
+    load32_raw(which ? a.app_v : a.app_k, ((size_t)(valid ? i : 0) * a.hkv + g) * kD + 32 * j, a.app_dtype, r);
+  };
+  u4 raw[8];
+  if (passes > 0) request(0, raw);
+  __syncthreads();  // the rotation blocks
+  for (int ps = 0; ps < passes; ++ps) {
+    float x[32];
+    raw_to_f32(raw, a.app_dtype, x);
+    if (ps + 1 < passes) request(ps + 1, raw);
+    int which;
+    const int blk = pass_block(ps, which);
+    const bool job = blk < nb;
+    const int i = blk * kPage + tl;  // token of the chunk
+    const bool valid = job && i < a.n_new;
+    const int p = a.new_start + i;
+    // a position outside the table or a page id outside the cache is skipped
+    const bool in_table = valid && (unsigned)p < (unsigned)a.max_pages * kPage;
+    const int page = in_table ? btab[p >> 6] : -1;
+    const bool stored = (unsigned)page < (unsigned)a.num_pages;
+    // a whole page: the block's 64 tokens fill one page (uniform per block)
+    const int p0 = a.new_start + blk * kPage;
+    const bool whole = job && (p0 & 63) == 0 && blk * kPage + kPage <= a.n_new &&
+                       (unsigned)p0 < (unsigned)a.max_pages * kPage &&
+                       (unsigned)btab[min(p0 >> 6, a.max_pages - 1)] < (unsigned)a.num_pages;
+    uint32_t sel[8];
+    const float n = quad_codes<BITS>(x, j, s_rot, a.lv4, sel);
+    const size_t pb = (size_t)(stored ? page : 0) * a.hkv + g;  // (page, kv head) block
+    quad_store<BITS, DeviceStore, true>(which, stored, whole, j, p & 63, sel, n,
+                                        (which ? a.v_codes_w : a.k_codes_w) + pb * (kPage * kRecB),
+                                        (which ? a.v_norms_w : a.k_norms_w) + pb * kPage, s_vb, t);
+    // the next pass assembles its V page in the same LDS bytes
+    if (which) __syncthreads();
+  }
+  int jobs = 0;
+  for (int b0 = tile * kPar; b0 < nb; b0 += stride) jobs += 2 * min(kPar, nb - b0);
+  return jobs;
+}
+
+// Count this workgroup's append jobs in once every thread's record stores
+// have completed (the stores are not tracked by the compiler: an explicit
+// wait on all counters, then a barrier).
+__device__ __forceinline__ void prefill_append_count(const PrefillArgs& a, int g, int jobs) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0 && jobs > 0) {
+    __hip_atomic_fetch_add(a.app_arrive + g, (uint32_t)jobs, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0);  // counted in before this workgroup can count itself done
+  }
+}
+
+// Wait (thread 0, bounded) until every job of kv head g's appended chunk is
+// visible, drop stale copies of the appended pages from this CU's and XCD's
+// caches, then let the workgroup on.  *s_fail = 1 when the wait ran out.
+__device__ __forceinline__ void prefill_wait_appended(const PrefillArgs& a, int g, int* s_fail) {
+  if (threadIdx.x == 0) {
+    const uint32_t target = 2u * (uint32_t)((a.n_new + kPage - 1) / kPage);
+    uint32_t spins = 0;
+    while (__hip_atomic_load(a.app_arrive + g, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+      __builtin_amdgcn_s_sleep(2);
+      if (++spins == kAppendSpinLimit) {
+        *s_fail = 1;
+        break;
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  }
+  __builtin_amdgcn_s_barrier();
+}
+
+// The last workgroup of kv head g to get here clears its counters for the
+// next call (every workgroup has added its jobs and passed its wait).
+__device__ __forceinline__ void prefill_append_finish(const PrefillArgs& a, int g) {
+  if (threadIdx.x == 0) {
+    const uint32_t old = __hip_atomic_fetch_add(a.app_done + g, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (old + 1 == (uint32_t)a.row_tiles) {
+      __hip_atomic_store(a.app_arrive + g, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(a.app_done + g, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
 
 // Direct-to-LDS loads, issued from inline asm so that the compiler does not
 // track them: it cannot tell which raw slot a load writes and would otherwise
@@ -253,7 +388,8 @@ __device__ __forceinline__ void pf_unpack(const uint8_t* slot, int part, int lan
     reinterpret_cast<uint32_t*>(snorm)[lane] = reinterpret_cast<const uint32_t*>(slot + kRawPage)[lane];
 }
 
-template <int RB, int BITS>
+// APP: the launch also quantise-appends a chunk (PrefillArgs::app_k).
+template <int RB, int BITS, bool APP>
 __global__ __launch_bounds__(64 * pf_waves<RB>(), 1) void prefill_kernel(PrefillArgs a) {
   constexpr int W = pf_waves<RB>();
   const int g = blockIdx.x, tile = blockIdx.y, b = blockIdx.z;
@@ -269,9 +405,31 @@ __global__ __launch_bounds__(64 * pf_waves<RB>(), 1) void prefill_kernel(Prefill
     q_start = a.q_starts[b];
     btab += (size_t)b * a.max_pages;
   }
+  __shared__ __attribute__((aligned(16))) uint8_t s_k[3][kKTileBytes];  // 49,152 B
+  __shared__ __attribute__((aligned(16))) uint8_t s_v[3][kVTileBytes];  // 49,152 B
+  __shared__ __attribute__((aligned(16))) uint8_t s_raw[kRawSlots][kRawSlot];  // 25,344 B
+  __shared__ __attribute__((aligned(16))) uint16_t s_norm[3][2 * kPage];      // K | V norms
+  __shared__ int s_pt[kPrefillMaxPages];                                       // 16,384 B
+  __shared__ int s_fail;
+
+  // ---- fused quantise-append: this workgroup's share of the chunk (the f16
+  // tile buffers are free yet); its jobs are counted in once the records are
+  // visible, after the query prologue below ----
+  int app_jobs = 0;
+  if constexpr (APP) {
+    if (tid == 0) s_fail = 0;
+    app_jobs = prefill_append<BITS, W>(a, btab, g, tile, s_k[0]);
+  }
+
   const int qpt = kRowsPerTile / a.group;  // queries per tile
   const int q0 = tile * qpt;
-  if (q0 >= n_q) return;  // a tile past this sequence's queries (uniform)
+  if (q0 >= n_q) {  // a tile past this sequence's queries (uniform)
+    if constexpr (APP) {
+      prefill_append_count(a, g, app_jobs);
+      prefill_append_finish(a, g);
+    }
+    return;
+  }
   const int q_last = min(n_q, q0 + qpt) - 1;
   const int kv_end = q_start + q_last + 1;
   // (a range beyond the table or the staging limit breaks the contract: never
@@ -279,12 +437,6 @@ __global__ __launch_bounds__(64 * pf_waves<RB>(), 1) void prefill_kernel(Prefill
   const int n_pages = min((kv_end + kPage - 1) / kPage, min(a.max_pages, kPrefillMaxPages));
   // pages entirely at or before the smallest query position need no mask
   const int n_full = min(n_pages, (q_start + q0 + 1) / kPage);
-
-  __shared__ __attribute__((aligned(16))) uint8_t s_k[3][kKTileBytes];  // 49,152 B
-  __shared__ __attribute__((aligned(16))) uint8_t s_v[3][kVTileBytes];  // 49,152 B
-  __shared__ __attribute__((aligned(16))) uint8_t s_raw[kRawSlots][kRawSlot];  // 25,344 B
-  __shared__ __attribute__((aligned(16))) uint16_t s_norm[3][2 * kPage];      // K | V norms
-  __shared__ int s_pt[kPrefillMaxPages];                                       // 16,384 B
 
   // ---- page ids of the causal range (wave w: a 1/W share of the entries) ----
   for (int i = 0; i < kPrefillMaxPages / (64 * W); ++i) {
@@ -338,6 +490,7 @@ __global__ __launch_bounds__(64 * pf_waves<RB>(), 1) void prefill_kernel(Prefill
   }
   __builtin_amdgcn_s_waitcnt(0);  // page-id loads landed (all counters)
   __syncthreads();
+  if constexpr (APP) prefill_append_count(a, g, app_jobs);
 
   const uint32_t raw_base = pf_lds_addr(&s_raw[0][0]);
   float m_run[RB], l_run[RB];
@@ -387,8 +540,18 @@ __global__ __launch_bounds__(64 * pf_waves<RB>(), 1) void prefill_kernel(Prefill
     using R = decltype(role);
     constexpr int per_page = R::loads;
     const int last = n_pages - 1;
+    // a fused append's pages are requested only once all of them are written
+    bool app_ready = !APP;
+    const int app_first = APP ? a.new_start / kPage : 0;
     auto issue = [&](int p) {
-      pf_issue<BITS, R>(a, s_pt[min(p, last)], g, part, lane, raw_base + (p % 3) * kRawSlot);
+      const int pp = min(p, last);
+      if constexpr (APP) {
+        if (!app_ready && pp >= app_first) {  // uniform: every wave issues the same pages
+          prefill_wait_appended(a, g, &s_fail);
+          app_ready = true;
+        }
+      }
+      pf_issue<BITS, R>(a, s_pt[pp], g, part, lane, raw_base + (p % 3) * kRawSlot);
     };
     auto unpack = [&](int p) {
       const int u = p % 3;
@@ -558,6 +721,7 @@ __global__ __launch_bounds__(64 * pf_waves<RB>(), 1) void prefill_kernel(Prefill
 
   // ---- epilogue: normalise, rotate back (B^T then H / sqrt(d)), store ----
   const float* rot = a.rot + (size_t)g * kRotFloats;
+  const bool failed = APP && s_fail;  // the appended pages never all arrived
 #pragma unroll
   for (int cb = 0; cb < RB; ++cb) {
     const float l = sum_xor32(sum_xor16(l_run[cb]));  // in units of the frame, as acc
@@ -579,12 +743,13 @@ __global__ __launch_bounds__(64 * pf_waves<RB>(), 1) void prefill_kernel(Prefill
       f4* dst = reinterpret_cast<f4*>(a.out +
                                       ((size_t)(row0 + qi_row[cb]) * a.hq + (size_t)g * a.group + head_row[cb]) * kD +
                                       32 * jq);
-      const float nrm = 0.08838834764831845f;  // 1/sqrt(128)
+      const float nrm = failed ? NAN : 0.08838834764831845f;  // 1/sqrt(128)
 #pragma unroll
       for (int i = 0; i < 8; ++i)
         dst[i] = f4{y[4 * i] * nrm, y[4 * i + 1] * nrm, y[4 * i + 2] * nrm, y[4 * i + 3] * nrm};
     }
   }
+  if constexpr (APP) prefill_append_finish(a, g);
 }
 
 PrefillPlan plan_prefill(int n_q, int hq, int hkv, int q_start, int num_cus) {
@@ -620,6 +785,40 @@ hipError_t launch_prefill_varlen(const CacheView& c, const float* rot, const voi
                                  const PrefillPlan& plan, float softmax_scale, float* out,
                                  void* workspace, hipStream_t stream) {
   (void)workspace;
+  return launch_prefill_args(c, rot, q, q_dtype, batch, n_q, hq, cu_q, q_start, q_starts, block_table,
+                             max_pages, plan, softmax_scale, out, nullptr, stream);
+}
+
+namespace {
+
+// Workgroups of one prefill instantiation that a CU holds at once; cached.
+template <int RB, int BITS>
+int prefill_blocks_per_cu() {
+  static std::atomic<int> cached{-1};
+  int n = cached.load(std::memory_order_relaxed);
+  if (n < 0) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, prefill_kernel<RB, BITS, true>, 64 * pf_waves<RB>(), 0) !=
+        hipSuccess)
+      return 0;  // not cached: asked again next time
+    cached.store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+}  // namespace
+
+bool prefill_append_fused(const PrefillPlan& plan, int hkv, int bits, int num_cus) {
+  if (hkv > kMaxCounterUnits) return false;
+  const int bpc = plan.waves == 4 ? (bits == 4 ? prefill_blocks_per_cu<2, 4>() : prefill_blocks_per_cu<2, 3>())
+                                  : (bits == 4 ? prefill_blocks_per_cu<1, 4>() : prefill_blocks_per_cu<1, 3>());
+  return bpc > 0 && (long long)hkv * plan.row_tiles <= (long long)bpc * num_cus;
+}
+
+hipError_t launch_prefill_args(const CacheView& c, const float* rot, const void* q, int q_dtype,
+                               int batch, int n_q, int hq, const int32_t* cu_q, int q_start,
+                               const int32_t* q_starts, const int32_t* block_table, int max_pages,
+                               const PrefillPlan& plan, float softmax_scale, float* out,
+                               const PrefillAppend* app, hipStream_t stream) {
   PrefillArgs a;
   a.k_codes = c.k_codes;
   a.k_norms = c.k_norms;
@@ -645,16 +844,41 @@ hipError_t launch_prefill_varlen(const CacheView& c, const float* rot, const voi
   a.score_factor = (float)((double)softmax_scale * log2e / (128.0 * alpha));
   a.out_factor = (float)(1.0 / (sqrt(128.0) * alpha));
   a.out = out;
+  a.app_k = a.app_v = nullptr;
+  a.app_arrive = a.app_done = nullptr;
+  a.k_codes_w = nullptr;
+  a.k_norms_w = nullptr;
+  a.v_codes_w = nullptr;
+  a.v_norms_w = nullptr;
+  a.app_dtype = a.n_new = a.new_start = 0;
+  a.row_tiles = plan.row_tiles;
+  if (app) {
+    a.app_k = app->k;
+    a.app_v = app->v;
+    a.app_dtype = app->dtype;
+    a.n_new = app->n_new;
+    a.new_start = app->new_start;
+    a.k_codes_w = c.k_codes;
+    a.k_norms_w = c.k_norms;
+    a.v_codes_w = c.v_codes;
+    a.v_norms_w = c.v_norms;
+    a.app_arrive = app->counters;
+    a.app_done = app->counters + kMaxCounterUnits;
+  }
   const int rb = plan.waves == 4 ? 2 : 1;  // 16-row blocks per wave
   const dim3 grid(c.hkv, plan.row_tiles, batch);
-#define IQ_PREFILL(RB, B) \
-  hipLaunchKernelGGL((prefill_kernel<RB, B>), grid, dim3(64 * pf_waves<RB>()), 0, stream, a)
-  if (rb == 2) {
-    if (four) IQ_PREFILL(2, 4);
-    else IQ_PREFILL(2, 3);
-  } else {
-    if (four) IQ_PREFILL(1, 4);
-    else IQ_PREFILL(1, 3);
+#define IQ_PREFILL(RB, B, APP) \
+  hipLaunchKernelGGL((prefill_kernel<RB, B, APP>), grid, dim3(64 * pf_waves<RB>()), 0, stream, a)
+  const int sel = (rb == 2 ? 4 : 0) + (four ? 2 : 0) + (app ? 1 : 0);
+  switch (sel) {
+    case 0: IQ_PREFILL(1, 3, false); break;
+    case 1: IQ_PREFILL(1, 3, true); break;
+    case 2: IQ_PREFILL(1, 4, false); break;
+    case 3: IQ_PREFILL(1, 4, true); break;
+    case 4: IQ_PREFILL(2, 3, false); break;
+    case 5: IQ_PREFILL(2, 3, true); break;
+    case 6: IQ_PREFILL(2, 4, false); break;
+    default: IQ_PREFILL(2, 4, true); break;
   }
 #undef IQ_PREFILL
   return hipGetLastError();

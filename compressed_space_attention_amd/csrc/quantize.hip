@@ -39,7 +39,7 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(
     const int32_t* __restrict__ pos, const int32_t* __restrict__ block_table, int n_tok,
     int hkv, int max_pages, const float* __restrict__ rot, int num_pages,
     uint8_t* __restrict__ k_codes, uint16_t* __restrict__ k_norms, uint8_t* __restrict__ v_codes,
-    uint16_t* __restrict__ v_norms, Levels4 lv) {
+    uint16_t* __restrict__ v_norms, Levels4 lv, int pos0) {
   constexpr int kRecB = BITS == 4 ? kRec4 : kRec;
   const int tl = threadIdx.x >> 2, j = threadIdx.x & 3;
   const int head = blockIdx.y, which = blockIdx.z;
@@ -53,9 +53,10 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(
 
   // The destination is looked up while the vector is transformed: position
   // and sequence first, then the page id, all before the arithmetic.
-  const int p = valid ? pos[tok] : -1;
-  const int si = valid ? seq_idx[tok] : -1;
-  const int p0 = pos[t0], s0 = seq_idx[t0];
+  // (seq_idx and pos null: one sequence, token i at position pos0 + i)
+  const int p = valid ? (pos ? pos[tok] : pos0 + tok) : -1;
+  const int si = valid ? (seq_idx ? seq_idx[tok] : 0) : -1;
+  const int p0 = pos ? pos[t0] : pos0 + t0, s0 = seq_idx ? seq_idx[t0] : 0;
   float x[32];
   const size_t vi = (size_t)(valid ? tok : t0) * hkv + head;
   load32(which ? v : k, vi * kD + 32 * j, DT, x);
@@ -70,106 +71,14 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(
   // workgroup); the barrier also publishes the rotation blocks
   const bool whole = __syncthreads_and(valid && si == s0 && p == p0 + tl && (p0 & 63) == 0 && stored);
 
-  float ss0 = 0.f, ss1 = 0.f, ss2 = 0.f, ss3 = 0.f;
-#pragma unroll
-  for (int i = 0; i < 32; i += 4) {
-    ss0 = fmaf(x[i], x[i], ss0);
-    ss1 = fmaf(x[i + 1], x[i + 1], ss1);
-    ss2 = fmaf(x[i + 2], x[i + 2], ss2);
-    ss3 = fmaf(x[i + 3], x[i + 3], ss3);
-  }
-  float ss = (ss0 + ss1) + (ss2 + ss3);
-  ss += quad_xor1(ss);
-  ss += quad_xor2(ss);
-  const float n = sqrtf(ss);
-
-  wht128_quad(x, j);
-  // SO(4) block by block (blocks 8j .. 8j + 7 of the quarter), each block's
-  // four outputs turned into codes at once: sel[bb] holds the codes (3-bit)
-  // or nibbles (4-bit) of coordinates 32j + 4bb .. + 3, one per byte.  The
-  // zero vector is coded through inv_n = 0: every u is then +-0, which codes
-  // as 4 (resp. nibble 0 = code 8), so no coordinate needs a branch.  The
-  // empty asm makes each block's rotation rows (LDS) depend on the previous
-  // block's codes: otherwise the compiler reads all 32 rows up front and holds
-  // 128 of them in registers (204 VGPRs instead of 62, a third of the waves).
   uint32_t sel[8];
-  {
-    const float inv_n = n > 0.f ? 1.0f / n : 0.f;
-    uint32_t prev = 0;
-#pragma unroll
-    for (int bb = 0; bb < 8; ++bb) {
-      int off = (8 * j + bb) * 16;
-      asm volatile("" : "+v"(off) : "v"(prev));
-      const f4* m = reinterpret_cast<const f4*>(s_rot + off);
-      uint32_t w = 0;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const f4 row = m[r];
-        const float zr = row[0] * x[4 * bb] + row[1] * x[4 * bb + 1] + row[2] * x[4 * bb + 2] +
-                         row[3] * x[4 * bb + 3];
-        uint32_t c;
-        if constexpr (BITS == 3) c = code_of(zr * inv_n);
-        else c = nibble_of(zr * inv_n, lv);
-        w |= c << (8 * r);
-      }
-      sel[bb] = w;
-      prev = w;
-    }
-  }
+  const float n = quad_codes<BITS>(x, j, s_rot, lv, sel);
 
   const int slot = p & 63;
-  const size_t rec = ((size_t)page * hkv + head) * kPage + slot;
-  uint8_t* blk = whole ? s_v : v_codes + ((size_t)page * hkv + head) * (kPage * kRecB);
-  if constexpr (BITS == 3) {
-    u3 w;
-    selectors_to_group(sel, w.x, w.y, w.z);
-    if (!which) {
-      if (stored) *reinterpret_cast<u3*>(k_codes + rec * kRec + 12 * j) = w;
-    } else if (stored) {
-      // V: byte lane b of this group goes to region n = 4j + b (quad q of the
-      // slot), chunk c = slot / 16, byte lane r = slot % 4 -- the order in
-      // which the decode matrix cores consume V (see the cache layout in
-      // isoquant.h).
-      const int c = slot >> 4, q = (slot >> 2) & 3, r = slot & 3;
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        uint8_t* dst = blk + (4 * j + b + 16 * q) * kRec + 12 * c + r;
-        dst[0] = (uint8_t)(w.x >> (8 * b));
-        dst[4] = (uint8_t)(w.y >> (8 * b));
-        dst[8] = (uint8_t)(w.z >> (8 * b));
-      }
-    }
-  } else {
-    if (!which) {
-      // record dword 4j + kk: byte b = coordinate 32j + 8kk + b (low nibble,
-      // selector 2kk) and 32j + 8kk + 4 + b (high nibble, selector 2kk + 1)
-      u4 w;
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) w[kk] = sel[2 * kk] | (sel[2 * kk + 1] << 4);
-      if (stored) *reinterpret_cast<u4*>(k_codes + rec * kRec4 + 16 * j) = w;
-    } else if (stored) {
-      // V: coordinates 32j + 4p + b (selector p) and + 16 (selector p + 4)
-      // share byte slot % 4 of dword 4p + 2 th + q of region (4j + b) + 16 jq
-      // (slot = 32 th + 16 q + 4 jq + r)
-      const int th = slot >> 5, q = (slot >> 4) & 1, jq = (slot >> 2) & 3, r = slot & 3;
-      uint8_t* dst = blk + (4 * j + 16 * jq) * 64 + 4 * (2 * th + q) + r;
-#pragma unroll
-      for (int pp = 0; pp < 4; ++pp) {
-        const uint32_t v = sel[pp] | (sel[pp + 4] << 4);
-#pragma unroll
-        for (int b = 0; b < 4; ++b) dst[64 * b + 16 * pp] = (uint8_t)(v >> (8 * b));
-      }
-    }
-  }
-  if (stored && j == 0) (which ? v_norms : k_norms)[rec] = float_to_half_sat(n);
-  if (which && whole) {
-    __syncthreads();
-    constexpr int kChunks = kPage * kRecB / 16;
-    if (threadIdx.x < kChunks) {
-      uint8_t* gblk = v_codes + ((size_t)page * hkv + head) * (kPage * kRecB);
-      reinterpret_cast<u4*>(gblk)[threadIdx.x] = reinterpret_cast<const u4*>(s_v)[threadIdx.x];
-    }
-  }
+  const size_t blk = (size_t)page * hkv + head;  // (page, kv head) block
+  quad_store<BITS, PlainStore>(which, stored, whole, j, slot, sel, n,
+                               (which ? v_codes : k_codes) + blk * (kPage * kRecB),
+                               (which ? v_norms : k_norms) + blk * kPage, s_v, threadIdx.x);
 }
 
 // Few vectors (a decode step appends one token per sequence): the latency
@@ -185,7 +94,7 @@ __global__ __launch_bounds__(256) void quantize_small_kernel(
     const int32_t* __restrict__ pos, const int32_t* __restrict__ block_table,
     const float* __restrict__ rot, int n_vec, int hkv, int max_pages, int num_pages,
     uint8_t* __restrict__ k_codes, uint16_t* __restrict__ k_norms, uint8_t* __restrict__ v_codes,
-    uint16_t* __restrict__ v_norms, Levels4 lv) {
+    uint16_t* __restrict__ v_norms, Levels4 lv, int pos0) {
   const int gv = blockIdx.x * 8 + (threadIdx.x >> 5);  // K vectors first, then V
   const int r = threadIdx.x & 31;
   if (gv >= 2 * n_vec) return;  // whole half-waves leave together
@@ -194,8 +103,8 @@ __global__ __launch_bounds__(256) void quantize_small_kernel(
   const int tok = vi / hkv;
   const int head = vi - tok * hkv;
 
-  const int p = pos[tok];
-  const int si = seq_idx[tok];
+  const int p = pos ? pos[tok] : pos0 + tok;
+  const int si = seq_idx ? seq_idx[tok] : 0;
   const f4* mrow = reinterpret_cast<const f4*>(rot + (size_t)head * kRotFloats + 16 * r);
   const f4 m0 = mrow[0], m1 = mrow[1], m2 = mrow[2], m3 = mrow[3];
   float x0, x1, x2, x3;
@@ -241,10 +150,11 @@ __global__ __launch_bounds__(256) void quantize_small_kernel(
   }
 }
 
-hipError_t launch_quantize_append(const CacheView& c, const float* rot, const void* k, const void* v,
-                                  int dtype, int n_tokens, const int32_t* seq_idx,
-                                  const int32_t* pos, const int32_t* block_table, int max_pages,
-                                  hipStream_t stream) {
+namespace {
+
+hipError_t launch_append(const CacheView& c, const float* rot, const void* k, const void* v, int dtype,
+                         int n_tokens, const int32_t* seq_idx, const int32_t* pos, int pos0,
+                         const int32_t* block_table, int max_pages, hipStream_t stream) {
   const Levels4 lv = c.bits == 4 ? codebook4().lv : Levels4{};
   const long long n_vec = (long long)n_tokens * c.hkv;
   if (2 * n_vec <= kSmallAppendVectors) {
@@ -252,7 +162,7 @@ hipError_t launch_quantize_append(const CacheView& c, const float* rot, const vo
 #define IQ_SMALL(DT, B)                                                                          \
   hipLaunchKernelGGL((quantize_small_kernel<DT, B>), dim3(blocks), dim3(256), 0, stream, k, v,   \
                      seq_idx, pos, block_table, rot, (int)n_vec, c.hkv, max_pages,               \
-                     c.num_pages, c.k_codes, c.k_norms, c.v_codes, c.v_norms, lv)
+                     c.num_pages, c.k_codes, c.k_norms, c.v_codes, c.v_norms, lv, pos0)
 #define IQ_SMALL_B(B)            \
   if (dtype == 0) IQ_SMALL(0, B); \
   else if (dtype == 1) IQ_SMALL(1, B); \
@@ -267,7 +177,7 @@ hipError_t launch_quantize_append(const CacheView& c, const float* rot, const vo
 #define IQ_QUADS(DT, B)                                                                           \
   hipLaunchKernelGGL((quantize_append_kernel<DT, B>), grid, dim3(256), 0, stream, k, v, seq_idx,   \
                      pos, block_table, n_tokens, c.hkv, max_pages, rot, c.num_pages, c.k_codes,     \
-                     c.k_norms, c.v_codes, c.v_norms, lv)
+                     c.k_norms, c.v_codes, c.v_norms, lv, pos0)
 #define IQ_QUADS_B(B)            \
   if (dtype == 0) IQ_QUADS(0, B); \
   else if (dtype == 1) IQ_QUADS(1, B); \
@@ -277,6 +187,21 @@ hipError_t launch_quantize_append(const CacheView& c, const float* rot, const vo
 #undef IQ_QUADS_B
 #undef IQ_QUADS
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quantize_append(const CacheView& c, const float* rot, const void* k, const void* v,
+                                  int dtype, int n_tokens, const int32_t* seq_idx,
+                                  const int32_t* pos, const int32_t* block_table, int max_pages,
+                                  hipStream_t stream) {
+  return launch_append(c, rot, k, v, dtype, n_tokens, seq_idx, pos, 0, block_table, max_pages, stream);
+}
+
+hipError_t launch_quantize_append_range(const CacheView& c, const float* rot, const void* k,
+                                        const void* v, int dtype, int n_tokens, int pos0,
+                                        const int32_t* block_table, int max_pages, hipStream_t stream) {
+  return launch_append(c, rot, k, v, dtype, n_tokens, nullptr, nullptr, pos0, block_table, max_pages, stream);
 }
 
 }  // namespace iq

@@ -135,6 +135,10 @@ def _load():
                                               vp, vp, sz, vp]),
         "iq_prefill_attention": (i32, [cp, vp, vp, i32, i32, i32, i32, vp, i32, f32, vp, vp, sz, vp]),
         "iq_prefill_attention_ex": (i32, [cp, vp, vp, i32, i32, i32, i32, vp, i32, f32, vp, vp, sz, pp, vp]),
+        "iq_prefill_append_workspace_bytes": (sz, [i32, i32, i32, i32]),
+        "iq_prefill_append_launches": (i32, [i32, i32, i32, i32]),
+        "iq_prefill_append": (i32, [cp, vp, vp, vp, i32, i32, i32, vp, i32, i32, i32, i32, vp, i32, f32, vp, vp,
+                                    sz, vp]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -149,6 +153,7 @@ EXPORTED = ("iq_status_string", "iq_version", "iq_codebook", "iq_rotation_bytes"
             "iq_decode_step", "iq_decode_workspace_bytes_ex", "iq_decode_attention_ex", "iq_decode_step_ex",
             "iq_decode_describe", "iq_decode_step_noalloc",
             "iq_prefill_workspace_bytes", "iq_prefill_attention", "iq_prefill_attention_ex",
+            "iq_prefill_append_workspace_bytes", "iq_prefill_append_launches", "iq_prefill_append",
             "iq_prefill_attention_varlen",
             "iq_dense_append", "iq_dense_decode_workspace_bytes", "iq_dense_decode_attention",
             "iq_dense_prefill_attention",
@@ -460,6 +465,55 @@ def prefill_attention(cache: PagedCache, rot: torch.Tensor, q: torch.Tensor, q_s
         cache.struct, _dev(rot, "rot", dev), _dev(q, "q", dev), _dtype(q), n_q, hq, int(q_start),
         _idx(block_table, "block_table", dev), block_table.shape[-1], float(softmax_scale),
         _dev(out, "out", dev), ws_ptr, ws_bytes, ctypes.byref(opts), _stream(stream)))
+    return out
+
+
+def prefill_append_workspace(n_q: int, n_q_heads: int, n_kv_heads: int, q_start: int, device="cuda",
+                             stream=None) -> torch.Tensor:
+    """A workspace for prefill_append, zero-filled (its counters start at zero)."""
+    dev = torch.device(device)
+    if dev.type == "cuda" and dev.index is None:
+        dev = torch.device("cuda", torch.cuda.current_device())
+    n = int(lib.iq_prefill_append_workspace_bytes(n_q, n_q_heads, n_kv_heads, q_start))
+    return _alloc((max(n, 16),), torch.uint8, dev, stream, zero=True)
+
+
+def prefill_append_launches(n_q: int, n_q_heads: int, n_kv_heads: int, bits: int = 3) -> int:
+    """Kernels a prefill_append call with a non-empty chunk and queries launches
+    on the current GPU: 1 (quantise-append fused into the prefill) or 2."""
+    n = int(lib.iq_prefill_append_launches(n_q, n_q_heads, n_kv_heads, bits))
+    if n < 0:
+        _check("iq_prefill_append_launches", n)
+    return n
+
+
+def prefill_append(cache: PagedCache, rot: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                   new_start: int, q: torch.Tensor, q_start: int, block_table: torch.Tensor,
+                   softmax_scale: float = 0.0, out: torch.Tensor | None = None,
+                   workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Quantise-append k_new / v_new ([n_new][Hkv][128], positions new_start..) of one
+    sequence and run the causal prefill of q ([n_q][Hq][128] at positions q_start..)
+    over the cache, in one call; block_table int32[max_pages] -> fp32 [n_q][Hq][128]."""
+    n_q, hq, d = q.shape
+    if d != HEAD_DIM:
+        raise ValueError("head dim must be 128")
+    if (k_new.shape != v_new.shape or k_new.dtype != v_new.dtype or k_new.dim() != 3
+            or k_new.shape[1] != cache.n_kv_heads or k_new.shape[2] != HEAD_DIM):
+        raise ValueError("k_new and v_new must both be [n_new][Hkv][128] of one dtype")
+    dev = _device_of(q, "q")
+    _check_cache(cache, dev)
+    if out is None:
+        out = _alloc((n_q, hq, HEAD_DIM), torch.float32, dev, stream)
+    elif out.dtype != torch.float32 or tuple(out.shape) != (n_q, hq, HEAD_DIM):
+        raise ValueError("out must be float32 [n_q][Hq][128]")
+    if workspace is None:
+        workspace = prefill_append_workspace(n_q, hq, cache.n_kv_heads, q_start, dev, stream)
+    _check("iq_prefill_append", lib.iq_prefill_append(
+        cache.struct, _dev(rot, "rot", dev), _dev(k_new, "k_new", dev), _dev(v_new, "v_new", dev),
+        _dtype(k_new), k_new.shape[0], int(new_start), _dev(q, "q", dev), _dtype(q), n_q, hq, int(q_start),
+        _idx(block_table, "block_table", dev), block_table.shape[-1], float(softmax_scale),
+        _dev(out, "out", dev), _dev(workspace, "workspace", dev),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
     return out
 
 

@@ -376,6 +376,44 @@ iq_status iq_prefill_attention_ex(const iq_cache *cache, const void *rot_dev, co
                                   const iq_prefill_options *options, hipStream_t stream);
 
 /*
+ * Quantise-append of a chunk fused with the chunked prefill over it
+ * ("RotaryQuant ...", abstract: quantiser and packed-tensor attention as one
+ * fused GPU pipeline; FreeToken v0.2.0 release notes, Kernels #632: extend
+ * attention, a prefill chunk attending the cache it extends).  The same
+ * records and the same attention as iq_quantize_append of the chunk's tokens
+ * (sequence 0 of the one-row block table, positions new_start .. new_start +
+ * n_new - 1) followed by iq_prefill_attention with the other arguments.
+ * When the runtime's occupancy calculator says the whole prefill grid is
+ * resident at once, one launch does both: the prefill workgroups of each kv
+ * head first quantise a share of the chunk's 64-token blocks, store the
+ * records device-coherent and count them in; a workgroup waits for the count
+ * only before it requests the first page holding appended tokens (the waits
+ * are bounded; a wait that runs out leaves NaN rows).  Otherwise the two
+ * kernels run one after the other.
+ *
+ * k_new_dev, v_new_dev : [n_new][n_kv_heads][128] of kv_dtype.
+ * workspace_dev        : at least iq_prefill_append_workspace_bytes(...) bytes;
+ *                        its first IQ_DECODE_COUNTER_BYTES bytes are counters that
+ *                        must be zero before the buffer's first use (every call
+ *                        leaves them zero).
+ * n_new = 0: the prefill alone; n_q = 0: the append alone.  Other arguments,
+ * limits and errors as iq_quantize_append and iq_prefill_attention;
+ * IQ_ERR_INVALID_ARG also when new_start + n_new exceeds the block table.
+ */
+size_t iq_prefill_append_workspace_bytes(int32_t n_q, int32_t n_q_heads, int32_t n_kv_heads,
+                                         int32_t q_start_pos);
+/* Kernels an iq_prefill_append call with n_new > 0 and n_q > 0 launches on the
+ * current device: 1 (fused) or 2; IQ_ERR_INVALID_ARG / IQ_ERR_DEVICE as a
+ * negative value. */
+int32_t iq_prefill_append_launches(int32_t n_q, int32_t n_q_heads, int32_t n_kv_heads, int32_t bits);
+iq_status iq_prefill_append(const iq_cache *cache, const void *rot_dev, const void *k_new_dev,
+                            const void *v_new_dev, int32_t kv_dtype, int32_t n_new, int32_t new_start,
+                            const void *q_dev, int32_t q_dtype, int32_t n_q, int32_t n_q_heads,
+                            int32_t q_start_pos, const int32_t *block_table_dev, int32_t max_pages,
+                            float softmax_scale, float *out_dev, void *workspace_dev,
+                            size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Batched variable-length chunked prefill: several sequences' query chunks in
  * one launch (the same attention as iq_prefill_attention for each sequence;
  * "RotaryQuant ...", abstract, and FreeToken issue #141, Proposed Solution).

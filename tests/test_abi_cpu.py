@@ -259,6 +259,32 @@ def test_prefill_options_validation():
                                      ctypes.byref(o), None) == 0
 
 
+def _pa(c, k=FAKE, n_new=64, new_start=0, q=FAKE, n_q=16, hq=64, q_start=0, max_pages=8, ws=FAKE,
+        ws_bytes=1 << 30, out=FAKE):
+    return L.iq_prefill_append(c, FAKE, k, FAKE, 1, n_new, new_start, q, 1, n_q, hq, q_start, FAKE, max_pages,
+                               0.0, out, ws, ws_bytes, None)
+
+
+def test_prefill_append_validation():
+    """The fused quantise-append + prefill refuses bad arguments on the host."""
+    c = _cache(hkv=8)
+    assert L.iq_prefill_append_workspace_bytes(16, 64, 8, 0) >= iq.DECODE_COUNTER_BYTES
+    assert L.iq_prefill_append_workspace_bytes(0, 64, 8, 0) == iq.DECODE_COUNTER_BYTES
+    assert L.iq_prefill_append_workspace_bytes(-1, 64, 8, 0) == 0
+    assert _pa(c, k=None) == -1                       # rows missing for a non-empty chunk
+    assert _pa(c, new_start=-1) == -1
+    assert _pa(c, new_start=8 * 64 - 63) == -1        # the chunk runs past the block table
+    assert _pa(c, q_start=8 * 64 - 15) == -1          # the queries run past it
+    assert _pa(c, hq=60) == -1                        # not a multiple of the kv heads
+    assert _pa(c, out=None) == -1
+    assert _pa(c, ws=None) == -1
+    assert _pa(c, ws_bytes=100) == -3                 # no room for the counters
+    assert _pa(c, hq=8 * 3) == -2                     # a group of 3
+    assert _pa(c, n_new=0, n_q=0, k=None, q=None, out=None) == 0   # nothing to do
+    assert L.iq_prefill_append_launches(16, 64, 8, 5) == -1
+    assert L.iq_prefill_append_launches(0, 64, 8, 3) == -1
+
+
 def _noalloc(c, batch=1, hq=32, max_len=1024, max_pages=16, out=FAKE, k_new=FAKE):
     return L.iq_decode_step_noalloc(c, FAKE, FAKE, 1, batch, hq, k_new, FAKE, 1, FAKE, max_pages, FAKE,
                                     max_len, 0.0, out, None)
