@@ -53,6 +53,8 @@ def parse():
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly (profiling runs)")
+    ap.add_argument("--deterministic", action="store_true",
+                    help="decode with the deterministic page order (iq_decode_options.deterministic)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (20 times): the known-size "
                          "reference that scales the HBM byte counters")
@@ -155,6 +157,100 @@ def measured_traffic(workload: str):
     return int(rec["traffic_bytes_per_call"])
 
 
+class Flush:
+    """A 2 GiB buffer streamed through the read probe right before each timed
+    region: whatever layers the warm-up left in the 256 MB Infinity Cache are
+    evicted, so the timed steps read their data from HBM."""
+
+    def __init__(self, device):
+        import torch
+        from compressed_space_attention_amd import isoquant as iq
+        self.iq = iq
+        self.buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=device)
+        self.sink = torch.empty(iq.probe_sink_bytes(), dtype=torch.uint8, device=device)
+
+    def __call__(self):
+        self.iq.probe_read(self.buf, self.sink)
+
+
+def ring_timer(args, ring, run_steps, flush):
+    """timed(n_steps, mode) -> seconds for exactly n_steps steps of a ring of
+    `ring` distinct layers (run_steps(n, start, mode) enqueues steps of layers
+    start, start + 1, ... mod ring), HIP events on the launch stream: whole
+    rings, then the first n_steps % ring layers, replayed from HIP graphs
+    (eager with --no-graph), after a warm-up of at least
+    args.warmup_seconds (and args.warmup steps) of ring replays, an untimed
+    first launch of the remainder graph and a cache flush."""
+    import torch
+
+    def make_graph(n, mode):
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                run_steps(n, 0, mode)
+        torch.cuda.current_stream().wait_stream(s)
+        return g
+
+    def timed(n_steps, mode):
+        stream = torch.cuda.current_stream()
+        full, rem = divmod(n_steps, ring)
+        if args.no_graph:
+            warm = lambda: run_steps(ring, 0, mode)
+            timed_run = lambda: run_steps(n_steps, 0, mode)
+            g_rem = None
+        else:
+            g_ring = make_graph(ring, mode)
+            g_rem = make_graph(rem, mode) if rem else None
+            warm = g_ring.replay
+
+            def timed_run():
+                for _ in range(full):
+                    g_ring.replay()
+                if g_rem:
+                    g_rem.replay()
+        t0, done = time.perf_counter(), 0
+        while True:
+            warm()
+            done += ring
+            torch.cuda.synchronize()
+            if done >= args.warmup and time.perf_counter() - t0 >= args.warmup_seconds:
+                break
+        if g_rem:
+            g_rem.replay()  # its first launch uploads the graph: not in the timed region
+        flush()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        timed_run()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / 1e3
+
+    return timed
+
+
+def layer_quality(layer, w):
+    """Cosine of a layer's step output against plain fp64 softmax attention
+    over its uncompressed (bf16) K/V, per query head: min and mean."""
+    import torch
+    kx, vx = layer.kv_host()
+    out0 = layer.out.double().cpu()
+    qh = layer.q.double().cpu()
+    cos = []
+    for b in range(w.batch):
+        for h in range(w.n_q_heads):
+            g = h // w.group
+            k = torch.from_numpy(kx[b][:, g]).double()
+            v = torch.from_numpy(vx[b][:, g]).double()
+            ref = torch.softmax((k @ qh[b, h]) / math.sqrt(128), dim=0) @ v
+            cos.append(float(torch.nn.functional.cosine_similarity(out0[b, h], ref, dim=0)))
+    return {"cosine_vs_uncompressed_min": round(min(cos), 5),
+            "cosine_vs_uncompressed_mean": round(float(np.mean(cos)), 5),
+            "rows": len(cos),
+            "reference": "plain fp64 softmax attention over the layer's bf16 K/V (not quantised)"}
+
+
 def run_decode(args):
     import torch
 
@@ -180,7 +276,8 @@ def run_decode(args):
     layers = [DecodeLayer(iq, synth, w, i, block_table, num_pages, device, args.bits) for i in range(ring)]
     torch.cuda.synchronize()
     log(f"[bench] caches built in {time.time() - t0:.1f} s")
-    ws = iq.decode_workspace(w.batch, w.n_q_heads, w.n_kv_heads, max_len, device=device)
+    opts = iq.DecodeOptions(deterministic=1) if args.deterministic else None
+    ws = iq.decode_workspace(w.batch, w.n_q_heads, w.n_kv_heads, max_len, device=device, options=opts)
 
     def step(layer, mode="step"):
         """mode "step": the fused decode step (append + attention, one call);
@@ -188,13 +285,13 @@ def run_decode(args):
         "decode": decode attention alone (the cache already holds the token)."""
         if mode == "step":
             iq.decode_step(layer.cache, layer.rot, layer.q, layer.k_new, layer.v_new, block_table,
-                           seq_lens, max_len, out=layer.out, workspace=ws)
+                           seq_lens, max_len, out=layer.out, workspace=ws, options=opts)
             return
         if mode == "pair":
             iq.quantize_append(layer.cache, layer.rot, layer.k_new, layer.v_new, layer.seq_new,
                                layer.pos_new, block_table)
         iq.decode_attention(layer.cache, layer.rot, layer.q, block_table, seq_lens, max_len,
-                            out=layer.out, workspace=ws)
+                            out=layer.out, workspace=ws, options=opts)
 
     def run_steps(n, start, mode="step"):
         for i in range(n):
@@ -205,58 +302,8 @@ def run_decode(args):
     run_steps(ring, 0)
     run_steps(2, 0, "pair")
     torch.cuda.synchronize()
-    # a 2 GiB buffer streamed through the read probe right before each timed
-    # region: whatever layers the warm-up left in the 256 MB Infinity Cache
-    # are evicted, so the timed steps read their packed KV from HBM
-    flush_buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=device)
-    flush_sink = torch.empty(iq.probe_sink_bytes(), dtype=torch.uint8, device=device)
-
-    def make_graph(n, mode):
-        g = torch.cuda.CUDAGraph()
-        s = torch.cuda.Stream()
-        s.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s):
-            with torch.cuda.graph(g, stream=s):
-                run_steps(n, 0, mode)
-        torch.cuda.current_stream().wait_stream(s)
-        return g
-
-    def timed(n_steps, mode):
-        """Seconds for exactly n_steps steps (HIP events on the launch stream):
-        whole rings of distinct layer caches, then the first n_steps % ring
-        layers, after a warm-up of at least args.warmup_seconds (and
-        args.warmup steps) of ring replays and a cache flush."""
-        stream = torch.cuda.current_stream()
-        full, rem = divmod(n_steps, ring)
-        if args.no_graph:
-            warm = lambda: run_steps(ring, 0, mode)
-            timed_run = lambda: run_steps(n_steps, 0, mode)
-        else:
-            g_ring = make_graph(ring, mode)
-            g_rem = make_graph(rem, mode) if rem else None
-            warm = g_ring.replay
-
-            def timed_run():
-                for _ in range(full):
-                    g_ring.replay()
-                if g_rem:
-                    g_rem.replay()
-        t0, done = time.perf_counter(), 0
-        while True:
-            warm()
-            done += ring
-            torch.cuda.synchronize()
-            if done >= args.warmup and time.perf_counter() - t0 >= args.warmup_seconds:
-                break
-        if not args.no_graph and g_rem:
-            g_rem.replay()  # its first launch uploads the graph: not in the timed region
-        iq.probe_read(flush_buf, flush_sink)
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        timed_run()
-        b.record(stream)
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / 1e3
+    flush = Flush(device)
+    timed = ring_timer(args, ring, run_steps, flush)
 
     t_step = timed(args.steps, "step") / args.steps
     t_decode = timed(args.steps, "decode") / args.steps
@@ -271,23 +318,9 @@ def run_decode(args):
     layer0 = layers[0]
     run_steps(1, 0)
     torch.cuda.synchronize()
-    kx, vx = layer0.kv_host()
-    out0 = layer0.out.double().cpu()
-    qh = layer0.q.double().cpu()
-    cos = []
-    for b in range(w.batch):
-        for h in range(w.n_q_heads):
-            g = h // w.group
-            k = torch.from_numpy(kx[b][:, g]).double()
-            v = torch.from_numpy(vx[b][:, g]).double()
-            ref = torch.softmax((k @ qh[b, h]) / math.sqrt(128), dim=0) @ v
-            cos.append(float(torch.nn.functional.cosine_similarity(out0[b, h], ref, dim=0)))
-    quality = {"cosine_vs_uncompressed_min": round(min(cos), 5),
-               "cosine_vs_uncompressed_mean": round(float(np.mean(cos)), 5),
-               "rows": len(cos),
-               "reference": "plain fp64 softmax attention over the layer's bf16 K/V (not quantised)"}
+    quality = layer_quality(layer0, w)
     log(f"[bench] cosine vs uncompressed attention: min {quality['cosine_vs_uncompressed_min']}, "
-        f"mean {quality['cosine_vs_uncompressed_mean']} over {len(cos)} rows")
+        f"mean {quality['cosine_vs_uncompressed_mean']} over {quality['rows']} rows")
 
     result = {
         "metric": METRIC,
@@ -311,6 +344,7 @@ def run_decode(args):
             "packed_kv_bytes_per_step": kv_bytes, "layer_ring": ring,
             "distinct_bytes_timed": min(args.steps, ring) * kv_bytes,
             "flush_bytes_before_timed": FLUSH_BYTES, "warmup_seconds_min": args.warmup_seconds,
+            "deterministic_page_order": bool(args.deterministic),
             "step": "one layer's decode step: quantise-append of the current token fused into "
                     "decode attention (iq_decode_step)",
         },
@@ -336,12 +370,13 @@ def run_decode(args):
     if not args.no_aux:
         del layers
         torch.cuda.empty_cache()
-        result["detail"]["dense_bf16_baseline"] = run_dense_aux(w, lens, bt_np, num_pages, t_decode)
+        result["detail"]["dense_bf16_baseline"] = run_dense_aux(args, w, lens, bt_np, num_pages, t_decode, flush)
         log(f"[bench] dense bf16 baseline: {result['detail']['dense_bf16_baseline']}")
-        result["detail"]["fp8_baseline"] = run_dense_aux(w, lens, bt_np, num_pages, t_decode, fmt="fp8")
+        result["detail"]["fp8_baseline"] = run_dense_aux(args, w, lens, bt_np, num_pages, t_decode, flush,
+                                                         fmt="fp8")
         log(f"[bench] fp8 baseline: {result['detail']['fp8_baseline']}")
         if args.bits == 3:
-            result["detail"]["four_bit"] = run_four_bit_aux(w, lens, bt_np, num_pages, t_decode, t_step)
+            result["detail"]["four_bit"] = run_four_bit_aux(args, w, bt_np, num_pages, t_decode, t_step, flush)
             log(f"[bench] 4-bit records: {result['detail']['four_bit']}")
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline_decode(args, w, layer0, bt_np, lens)
@@ -379,11 +414,10 @@ def probe_bandwidth(mib: int = 2048, iters: int = 20):
             "read_kernel": "probe_read_kernel (16-byte loads, 8 in flight per thread)"}
 
 
-def run_dense_aux(w, lens, bt_np, num_pages, t_packed, ring_bytes=1.0e9, steps=400, fmt="bf16"):
+def run_dense_aux(args, w, lens, bt_np, num_pages, t_packed, flush, ring_bytes=1.0e9, fmt="bf16"):
     """The uncompressed baseline on the same workload: a ring of bf16 (or FP8
-    E4M3, unit scales) layer caches (same paging), the decode call timed the
-    same way as the packed one (graph replay, HIP events on the launch
-    stream)."""
+    E4M3, unit scales) layer caches (same paging, the same K/V recipe as the
+    packed layers), the decode call timed like the packed one (ring_timer)."""
     import torch
 
     from compressed_space_attention_amd import isoquant as iq
@@ -399,47 +433,27 @@ def run_dense_aux(w, lens, bt_np, num_pages, t_packed, ring_bytes=1.0e9, steps=4
     caches, qs, outs = [], [], []
     seq_idx = torch.cat([torch.full((int(n),), b, dtype=torch.int32) for b, n in enumerate(lens)]).to(dev)
     pos = torch.cat([torch.arange(int(n), dtype=torch.int32) for n in lens]).to(dev)
-    total = int(lens.sum())
     for i in range(ring):
+        # the packed layer's draws (cached tokens, then the current one), appended uncompressed
+        src = DenseSource(synth, w, 500 + i, dev)
         c = iq.DenseCache(num_pages, w.n_kv_heads, device=dev, format=fmt)
-        seed = w.seed * 1000 + 500 + i
-        chunk = 1 << 16
-        for s0 in range(0, total, chunk):
-            e = min(total, s0 + chunk)
-            k = synth.draw_normal_device(seed * 7 + s0, (e - s0, w.n_kv_heads, 128), torch.bfloat16, dev)
-            v = synth.draw_normal_device(seed * 11 + s0, (e - s0, w.n_kv_heads, 128), torch.bfloat16, dev)
+        for s0, e, k, v in src.rows():
             iq.dense_append(c, k, v, seq_idx[s0:e], pos[s0:e], block_table)
         caches.append(c)
-        qs.append(synth.draw_normal_device(seed * 19, (w.batch, w.n_q_heads, 128), torch.bfloat16, dev))
+        qs.append(src.q)
         outs.append(torch.empty((w.batch, w.n_q_heads, 128), dtype=torch.float32, device=dev))
     ws = torch.empty(max(16, iq.dense_decode_workspace_bytes(w.batch, w.n_q_heads, w.n_kv_heads, max_len)),
                      dtype=torch.uint8, device=dev)
 
-    def run(n):
+    def run_steps(n, start, mode):
         for i in range(n):
-            j = i % ring
+            j = (start + i) % ring
             iq.dense_decode_attention(caches[j], qs[j], block_table, seq_lens, max_len, out=outs[j],
                                       workspace=ws)
 
-    run(ring)
+    run_steps(ring, 0, "decode")
     torch.cuda.synchronize()
-    reps = max(1, steps // ring)
-    g = torch.cuda.CUDAGraph()
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(s):
-        with torch.cuda.graph(g, stream=s):
-            run(ring)
-    torch.cuda.current_stream().wait_stream(s)
-    g.replay()
-    torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    for _ in range(reps):
-        g.replay()
-    b.record()
-    torch.cuda.synchronize()
-    t = a.elapsed_time(b) / 1e3 / (reps * ring)
+    t = ring_timer(args, ring, run_steps, flush)(args.steps, "decode") / args.steps
     del caches
     return {"kernel": f"dense_decode_split_kernel + decode_merge_kernel ({fmt} paged cache)",
             "decode_call_us": round(t * 1e6, 3), f"{fmt}_bytes_per_call": dense_bytes,
@@ -447,74 +461,88 @@ def run_dense_aux(w, lens, bt_np, num_pages, t_packed, ring_bytes=1.0e9, steps=4
             "packed_speedup": round(t / t_packed, 3)}
 
 
-def run_four_bit_aux(w, lens, bt_np, num_pages, t_decode3, t_step3, ring_bytes=1.0e9, steps=400):
-    """The 4-bit variant on the same workload: a ring of 4-bit layer caches
-    (same paging, same synthetic recipe), its decode step and decode call
-    timed like the 3-bit ones (graph replay, HIP events on the launch stream)."""
+class DenseSource:
+    """The K/V rows a packed DecodeLayer with the same index draws (every
+    sequence's cached tokens in order, each followed by its current token
+    where the packed layer's step appends it) and its queries."""
+
+    def __init__(self, synth, w, idx, device):
+        import torch
+        self.synth, self.w, self.device = synth, w, device
+        seed = w.seed * 1000 + idx
+        self.seed = seed
+        outl = synth.outlier_channels(seed + 1, w.n_kv_heads) if w.k_outliers else None
+        self.dt = {"bf16": torch.bfloat16, "f32": torch.float32}[w.dtype]
+        self.scale = torch.ones(w.n_kv_heads, 128, device=device)
+        if outl is not None:
+            for h in range(w.n_kv_heads):
+                self.scale[h, torch.from_numpy(outl[h]).to(device)] = 10.0
+        self.q = synth.draw_normal_device(seed * 19, (w.batch, w.n_q_heads, 128), self.dt, device)
+
+    def rows(self, chunk=1 << 16):
+        """(start, end, k, v) over the flat token order of sequences 0..B-1,
+        lens[b] tokens each: the cached rows as DecodeLayer draws them, the
+        last token of each sequence its current row."""
+        import torch
+        w, synth, dev, seed = self.w, self.synth, self.device, self.seed
+        lens = [int(n) for n in w.seq_lens()]
+        n_prev = [n - 1 for n in lens]
+        total_prev, hkv = sum(n_prev), w.n_kv_heads
+        k_new = (synth.draw_normal_device(seed * 13, (w.batch, hkv, 128), torch.float32, dev) * self.scale).to(self.dt)
+        v_new = synth.draw_normal_device(seed * 17, (w.batch, hkv, 128), self.dt, dev)
+        ks, vs = [], []
+        for s in range(0, total_prev, chunk):
+            e = min(total_prev, s + chunk)
+            ks.append((synth.draw_normal_device(seed * 7 + s, (e - s, hkv, 128), torch.float32, dev)
+                       * self.scale).to(self.dt))
+            vs.append(synth.draw_normal_device(seed * 11 + s, (e - s, hkv, 128), self.dt, dev))
+        k_prev, v_prev = torch.cat(ks), torch.cat(vs)
+        at, out_at = 0, 0
+        for b, n in enumerate(n_prev):
+            k = torch.cat([k_prev[at:at + n], k_new[b:b + 1]])
+            v = torch.cat([v_prev[at:at + n], v_new[b:b + 1]])
+            yield out_at, out_at + n + 1, k, v
+            at += n
+            out_at += n + 1
+
+
+def run_four_bit_aux(args, w, bt_np, num_pages, t_decode3, t_step3, flush, ring_bytes=1.0e9):
+    """The 4-bit variant on the same workload: a ring of 4-bit layers (the
+    same paging and synthetic recipe as the 3-bit ones), its decode step and
+    decode call timed like the 3-bit ones (ring_timer), and the quality of
+    its first layer's step output."""
     import torch
 
     from compressed_space_attention_amd import isoquant as iq
     from compressed_space_attention_amd import synth
     dev = "cuda"
     block_table = torch.from_numpy(bt_np).to(dev)
+    lens = w.seq_lens()
     seq_lens = torch.from_numpy(lens).to(dev)
     max_len = int(lens.max())
     kv_bytes = REC_BYTES4 * int(lens.sum()) * w.n_kv_heads
     layer_bytes = num_pages * w.n_kv_heads * 64 * REC_BYTES4
     ring = max(1, math.ceil(ring_bytes / layer_bytes))
-    n_prev = [int(n) - 1 for n in lens]
-    seq_idx = torch.cat([torch.full((n,), b, dtype=torch.int32) for b, n in enumerate(n_prev)]).to(dev)
-    pos = torch.cat([torch.arange(n, dtype=torch.int32) for n in n_prev]).to(dev)
-    total = sum(n_prev)
-    layers = []
-    for i in range(ring):
-        seed = w.seed * 1000 + 700 + i
-        rot = iq.rotation_init(synth.quaternions(seed, w.n_kv_heads), device=dev)
-        c = iq.PagedCache(num_pages, w.n_kv_heads, device=dev, bits=4)
-        chunk = 1 << 16
-        for s0 in range(0, total, chunk):
-            e = min(total, s0 + chunk)
-            k = synth.draw_normal_device(seed * 7 + s0, (e - s0, w.n_kv_heads, 128), torch.bfloat16, dev)
-            v = synth.draw_normal_device(seed * 11 + s0, (e - s0, w.n_kv_heads, 128), torch.bfloat16, dev)
-            iq.quantize_append(c, rot, k, v, seq_idx[s0:e], pos[s0:e], block_table)
-        kn = synth.draw_normal_device(seed * 13, (w.batch, w.n_kv_heads, 128), torch.bfloat16, dev)
-        vn = synth.draw_normal_device(seed * 17, (w.batch, w.n_kv_heads, 128), torch.bfloat16, dev)
-        q = synth.draw_normal_device(seed * 19, (w.batch, w.n_q_heads, 128), torch.bfloat16, dev)
-        out = torch.empty((w.batch, w.n_q_heads, 128), dtype=torch.float32, device=dev)
-        layers.append((c, rot, kn, vn, q, out))
+    layers = [DecodeLayer(iq, synth, w, i, block_table, num_pages, dev, bits=4) for i in range(ring)]
     ws = iq.decode_workspace(w.batch, w.n_q_heads, w.n_kv_heads, max_len, device=dev)
 
-    def run(n, mode):
+    def run_steps(n, start, mode):
         for i in range(n):
-            c, rot, kn, vn, q, out = layers[i % ring]
+            L = layers[(start + i) % ring]
             if mode == "step":
-                iq.decode_step(c, rot, q, kn, vn, block_table, seq_lens, max_len, out=out, workspace=ws)
+                iq.decode_step(L.cache, L.rot, L.q, L.k_new, L.v_new, block_table, seq_lens, max_len, out=L.out,
+                               workspace=ws)
             else:
-                iq.decode_attention(c, rot, q, block_table, seq_lens, max_len, out=out, workspace=ws)
+                iq.decode_attention(L.cache, L.rot, L.q, block_table, seq_lens, max_len, out=L.out, workspace=ws)
 
-    def timed(mode):
-        run(ring, mode)
-        torch.cuda.synchronize()
-        reps = max(1, steps // ring)
-        g = torch.cuda.CUDAGraph()
-        s = torch.cuda.Stream()
-        s.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s):
-            with torch.cuda.graph(g, stream=s):
-                run(ring, mode)
-        torch.cuda.current_stream().wait_stream(s)
-        g.replay()
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        for _ in range(reps):
-            g.replay()
-        b.record()
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / 1e3 / (reps * ring)
-
-    t_step = timed("step")
-    t_dec = timed("decode")
+    run_steps(ring, 0, "step")
+    torch.cuda.synchronize()
+    timed = ring_timer(args, ring, run_steps, flush)
+    t_step = timed(args.steps, "step") / args.steps
+    t_dec = timed(args.steps, "decode") / args.steps
+    run_steps(1, 0, "step")
+    torch.cuda.synchronize()
+    quality = layer_quality(layers[0], w)
     del layers
     torch.cuda.empty_cache()
     return {"kernel": "decode_split_kernel<..., 4-bit> + decode_merge_kernel",
@@ -523,7 +551,8 @@ def run_four_bit_aux(w, lens, bt_np, num_pages, t_decode3, t_step3, ring_bytes=1
             "decode_call_gbs": round(kv_bytes / t_dec / 1e9, 1),
             "decode_call_frac_of_hbm_peak": round(kv_bytes / t_dec / 1e9 / HBM_PEAK_GBS, 4),
             "time_vs_3bit_decode_call": round(t_dec / t_decode3, 3),
-            "time_vs_3bit_step": round(t_step / t_step3, 3)}
+            "time_vs_3bit_step": round(t_step / t_step3, 3),
+            "quality": quality}
 
 
 def median_call_seconds(fn, calls=10, reps=5, warm=20):
