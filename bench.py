@@ -55,6 +55,10 @@ def parse():
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly (profiling runs)")
     ap.add_argument("--deterministic", action="store_true",
                     help="decode with the deterministic page order (iq_decode_options.deterministic)")
+    ap.add_argument("--rounds", type=int, default=0,
+                    help="iq_decode_options.rounds: workgroups per CU the split plan is made for (0: planner)")
+    ap.add_argument("--waves", type=int, default=0, choices=(0, 4, 8),
+                    help="iq_decode_options.waves: waves per decode workgroup (0: planner)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (20 times): the known-size "
                          "reference that scales the HBM byte counters")
@@ -276,7 +280,7 @@ def run_decode(args):
     layers = [DecodeLayer(iq, synth, w, i, block_table, num_pages, device, args.bits) for i in range(ring)]
     torch.cuda.synchronize()
     log(f"[bench] caches built in {time.time() - t0:.1f} s")
-    opts = iq.DecodeOptions(deterministic=1) if args.deterministic else None
+    opts = iq.DecodeOptions(waves=args.waves, rounds=args.rounds, deterministic=int(args.deterministic))
     ws = iq.decode_workspace(w.batch, w.n_q_heads, w.n_kv_heads, max_len, device=device, options=opts)
 
     def step(layer, mode="step"):
@@ -345,6 +349,7 @@ def run_decode(args):
             "distinct_bytes_timed": min(args.steps, ring) * kv_bytes,
             "flush_bytes_before_timed": FLUSH_BYTES, "warmup_seconds_min": args.warmup_seconds,
             "deterministic_page_order": bool(args.deterministic),
+            "decode_plan": iq.decode_describe(w.batch, w.n_q_heads, w.n_kv_heads, max_len, args.bits, True, opts),
             "step": "one layer's decode step: quantise-append of the current token fused into "
                     "decode attention (iq_decode_step)",
         },

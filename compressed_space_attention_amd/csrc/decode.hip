@@ -1210,7 +1210,7 @@ int split_blocks_per_cu() {
   if (n < 0) {
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_split_kernel<P8, W, AP, B, BAL>, 64 * W, 0) !=
         hipSuccess)
-      n = 0;
+      return 0;  // not cached: asked again next time
     cached.store(n, std::memory_order_relaxed);
   }
   return n;
