@@ -234,12 +234,13 @@ def ring_timer(args, ring, run_steps, flush):
     return timed
 
 
-def layer_quality(layer, w):
-    """Cosine of a layer's step output against plain fp64 softmax attention
-    over its uncompressed (bf16) K/V, per query head: min and mean."""
+def layer_quality(layer, w, out=None):
+    """Cosine of a layer's step output (or of `out`, [B][Hq][128]) against
+    plain fp64 softmax attention over its uncompressed (bf16) K/V, per query
+    head: min and mean."""
     import torch
     kx, vx = layer.kv_host()
-    out0 = layer.out.double().cpu()
+    out0 = layer.out.double().cpu() if out is None else torch.as_tensor(np.asarray(out, dtype=np.float64))
     qh = layer.q.double().cpu()
     cos = []
     for b in range(w.batch):
@@ -760,12 +761,28 @@ def cpu_baseline_decode(args, w, layer, bt_np, lens):
         with ctx.Pool(procs, initializer=_cpu_worker_init, initargs=(path, meta)) as pool:
             pool.map(_cpu_unit_step, units[:procs])          # workers started and warm
             steps, el = run(lambda: pool.map(_cpu_unit_step, units, chunksize=1), args.cpu_seconds)
+            unit_out = pool.map(_cpu_unit_step, units, chunksize=1)
         _cpu_worker_init(path, meta)                          # the same units on one core, here
         with threadpoolctl.threadpool_limits(1):
             steps1, el1 = run(lambda: [_cpu_unit_step(u) for u in units], args.cpu_seconds / 2)
     finally:
         _CPU_STATE.clear()
         os.remove(path)
+
+    # the oracle's output of the benchmarked step against the GPU's, and its
+    # own quality against the uncompressed attention
+    grp = w.group
+    oracle_out = np.zeros((w.batch, w.n_q_heads, 128))
+    for (b, g), o in zip(units, unit_out):
+        oracle_out[b, g * grp:(g + 1) * grp] = np.asarray(o)[0]
+    gpu_out = layer.out.double().cpu().numpy()
+    row_err = [float(np.max(np.abs(gpu_out[b, h] - oracle_out[b, h])) / np.max(np.abs(oracle_out[b, h])))
+               for b in range(w.batch) for h in range(w.n_q_heads)]
+    oq = layer_quality(layer, w, oracle_out)
+    output_check = {"max_row_error_gpu_vs_oracle": float(f"{max(row_err):.3e}"), "tolerance": 1e-3,
+                    "oracle_cosine_vs_uncompressed_min": oq["cosine_vs_uncompressed_min"],
+                    "oracle_cosine_vs_uncompressed_mean": oq["cosine_vs_uncompressed_mean"],
+                    "rows": len(row_err)}
 
     # the oracle's check of every record of the benchmarked layer (all tokens
     # of every sequence, the appended one included)
@@ -798,6 +815,7 @@ def cpu_baseline_decode(args, w, layer, bt_np, lens):
                   f"each); host has {os.cpu_count()} logical CPUs",
         "single_thread": {"value": round(kv_bytes * steps1 / el1 / 1e9, 5), "unit": "GB/s", "cores": 1,
                           "sample": f"{steps1} steps in {el1:.1f} s"},
+        "oracle_output_check": output_check,
         "oracle_code_check": {"codes": codes, "mismatches": mism, "near_boundary": near,
                               "mismatch_frac": mism / codes, "near_boundary_frac": near / codes,
                               "mismatches_off_boundary": off, "norm_mismatches": norm_mism,
