@@ -59,6 +59,10 @@ def parse():
                     help="iq_decode_options.rounds: workgroups per CU the split plan is made for (0: planner)")
     ap.add_argument("--waves", type=int, default=0, choices=(0, 4, 8),
                     help="iq_decode_options.waves: waves per decode workgroup (0: planner)")
+    ap.add_argument("--plan", type=int, default=0, choices=(0, 1, 2),
+                    help="iq_decode_options.plan: 0 planner, 1 host plan, 2 device-balanced plan")
+    ap.add_argument("--merge", type=int, default=0, choices=(0, 1, 2),
+                    help="iq_decode_options.merge: 0 planner, 1 merge workgroups in the split launch, 2 merge kernel")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (20 times): the known-size "
                          "reference that scales the HBM byte counters")
@@ -281,7 +285,8 @@ def run_decode(args):
     layers = [DecodeLayer(iq, synth, w, i, block_table, num_pages, device, args.bits) for i in range(ring)]
     torch.cuda.synchronize()
     log(f"[bench] caches built in {time.time() - t0:.1f} s")
-    opts = iq.DecodeOptions(waves=args.waves, rounds=args.rounds, deterministic=int(args.deterministic))
+    opts = iq.DecodeOptions(waves=args.waves, rounds=args.rounds, plan=args.plan, merge=args.merge,
+                            deterministic=int(args.deterministic))
     ws = iq.decode_workspace(w.batch, w.n_q_heads, w.n_kv_heads, max_len, device=device, options=opts)
 
     def step(layer, mode="step"):

@@ -68,6 +68,17 @@ __host__ __device__ constexpr int vt_at(int row, int col) {
 constexpr int kRawPage = 8192;  // raw code bytes of a page in LDS: 512 groups of 12 B at a 16 B stride
 constexpr int kRawSlot = kRawPage + 256;  // + the page's K and V norms
 constexpr int kRawSlots = 3;
+// The prefill kernel's LDS block: norms of the three unpacked pages, the
+// wait flag, the raw page slots, the K^ and V^T tiles, the page ids.
+constexpr int kPfLdsNorm = 0;
+constexpr int kPfLdsFail = kPfLdsNorm + 3 * 2 * kPage * 2;
+constexpr int kPfLdsRaw = kPfLdsFail + 16;
+constexpr int kPfLdsK = kPfLdsRaw + kRawSlots * kRawSlot;
+constexpr int kPfLdsV = kPfLdsK + 3 * kKTileBytes;
+constexpr int kPfLdsPt = kPfLdsV + 3 * kVTileBytes;
+constexpr int kPfLdsBytes = kPfLdsPt + 4 * kPrefillMaxPages;
+static_assert(kPfLdsRaw % 16 == 0 && kPfLdsK % 16 == 0 && kPfLdsV % 16 == 0 && kPfLdsPt % 16 == 0,
+              "16-byte aligned LDS arrays");
 template <int RB> constexpr int pf_waves() { return 8 / RB; }
 
 struct PrefillArgs {
@@ -247,6 +258,19 @@ __device__ __forceinline__ void pf_dma(const void* g, uint32_t lds, int size) {
   else
     asm volatile("global_load_lds_dword %0, off" ::"v"(g), "{m0}"(m0) : "memory");
 }
+// LDS reads at a 32-bit LDS address.  A page step's read groups each take one
+// base address, computed once and kept opaque (so the compiler does not
+// re-associate it into a vector add per read), plus constant offsets that
+// the ds_read immediate field carries.
+typedef __attribute__((address_space(3))) const h8* pf_lds_h8p;
+typedef __attribute__((address_space(3))) const u2* pf_lds_u2p;
+__device__ __forceinline__ uint32_t pf_opaque(uint32_t a) {
+  asm volatile("" : "+v"(a));
+  return a;
+}
+__device__ __forceinline__ h8 pf_ld_h8(uint32_t addr) { return *(pf_lds_h8p)(uintptr_t)addr; }
+__device__ __forceinline__ u2 pf_ld_u2(uint32_t addr) { return *(pf_lds_u2p)(uintptr_t)addr; }
+
 // s_waitcnt vmcnt(n) (gfx9 encoding, other counters left alone)
 #define IQ_PF_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
 constexpr int kPfWaitLgkm0 = 0xF | (0x3 << 14) | (0x7 << 4);
@@ -321,34 +345,41 @@ __device__ __forceinline__ void pf_issue(const PrefillArgs& a, int page_id, int 
 
 // One K group (token tok, coordinates 32j..32j+31 = planes 4j .. 4j+3) into
 // the f16 K^ tile.
-__device__ __forceinline__ void pf_unpack_k(const u3& ck, int tok, int j, uint8_t* sk) {
+typedef __attribute__((address_space(3))) u4* pf_lds_u4w;
+typedef __attribute__((address_space(3))) u2* pf_lds_u2w;
+__device__ __forceinline__ void pf_st_u4(uint32_t addr, const u4& v) { *(pf_lds_u4w)(uintptr_t)addr = v; }
+__device__ __forceinline__ void pf_st_u2(uint32_t addr, const u2& v) { *(pf_lds_u2w)(uintptr_t)addr = v; }
+
+// kd = LDS address of the K^ tile + 1024 * 4j + 16 * tok (token tok, quarter j)
+__device__ __forceinline__ void pf_unpack_k(const u3& ck, uint32_t kd) {
   uint32_t z[8];
   group_to_selectors(ck.x, ck.y, ck.z, z);
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
     const u2 d0 = selector_to_f16(z[2 * kk]), d1 = selector_to_f16(z[2 * kk + 1]);
-    *reinterpret_cast<u4*>(sk + 1024 * (4 * j + kk) + 16 * tok) = u4{d0[0], d0[1], d1[0], d1[1]};
+    pf_st_u4(kd + 1024 * kk, u4{d0[0], d0[1], d1[0], d1[1]});
   }
 }
 // Chunk c of V region `region` = (n, q) = (region % 16, region / 16): tokens
 // 16c + 4q + r, selector m, into row 16m + n of the f16 V^T tile (row 16m + n
-// holds coordinate 32 (n / 4) + 4m + n % 4: accumulator order).
-__device__ __forceinline__ void pf_unpack_v(const u3& cv, int region, int c, uint8_t* sv) {
+// holds coordinate 32 (n / 4) + 4m + n % 4: accumulator order).  vd = LDS
+// address of the tile + vt_at(n, vt_col(16c + 4q)): row 16m + n is 256 m
+// further.
+__device__ __forceinline__ int pf_v_lane_offset(int region, int c) {
+  return vt_at(region & 15, vt_col(16 * c + 4 * (region >> 4)));  // the four tokens stay adjacent
+}
+__device__ __forceinline__ void pf_unpack_v(const u3& cv, uint32_t vd) {
   uint32_t z[8];
   group_to_selectors(cv.x, cv.y, cv.z, z);
-  const int n = region & 15, q = region >> 4;
-  const int col = vt_col(16 * c + 4 * q);  // the four tokens stay adjacent
 #pragma unroll
-  for (int m = 0; m < 8; ++m) *reinterpret_cast<u2*>(sv + vt_at(16 * m + n, col)) = selector_to_f16(z[m]);
+  for (int m = 0; m < 8; ++m) pf_st_u2(vd + 256 * m, selector_to_f16(z[m]));
 }
 
 // 4-bit: quarter j of token tok's record (dword kk = coordinates 32j + 8kk
-// .. + 7) into the f16 K^ tile.
-__device__ __forceinline__ void pf_unpack_k4(const u4& ck, int tok, int j, uint8_t* sk,
-                                             const Levels4& lv) {
+// .. + 7) into the f16 K^ tile; kd as for pf_unpack_k.
+__device__ __forceinline__ void pf_unpack_k4(const u4& ck, uint32_t kd, const Levels4& lv) {
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk)
-    *reinterpret_cast<u4*>(sk + 1024 * (4 * j + kk) + 16 * tok) = __builtin_bit_cast(u4, dword4_to_h8(ck[kk], lv));
+  for (int kk = 0; kk < 4; ++kk) pf_st_u4(kd + 1024 * kk, __builtin_bit_cast(u4, dword4_to_h8(ck[kk], lv)));
 }
 // 4-bit: dwords 4p .. 4p+3 of V region `region` = n + 16 jq: dword (th, q)
 // holds tokens 32 th + 16 q + 4 jq + r of coordinate 32 (n / 4) + 4p + n % 4
@@ -375,14 +406,22 @@ __device__ __forceinline__ void pf_unpack_v4(const u4& cv, int region, int p, ui
 template <int BITS, class R>
 __device__ __forceinline__ void pf_unpack(const uint8_t* slot, int part, int lane, uint8_t* sk,
                                           uint8_t* sv, uint16_t* snorm, const Levels4& lv) {
+  // one opaque base per store group; the per-store offsets are immediates
   const uint8_t* raw = slot + 2048 * part + 16 * lane;
   const int row = 16 * part + (lane & 15);
   if (BITS == 4) {
-    if (R::k) pf_unpack_k4(*reinterpret_cast<const u4*>(raw), row, lane >> 4, sk, lv);
-    if (R::v) pf_unpack_v4(*reinterpret_cast<const u4*>(raw + 1024), row, lane >> 4, sv, lv);
+    if (R::k)
+      pf_unpack_k4(*reinterpret_cast<const u4*>(raw),
+                   pf_opaque(pf_lds_addr(sk) + 1024 * 4 * (lane >> 4) + 16 * row), lv);
+    if (R::v)
+      pf_unpack_v4(*reinterpret_cast<const u4*>(raw + 1024), row, lane >> 4, sv, lv);
   } else {
-    if (R::k) pf_unpack_k(*reinterpret_cast<const u3*>(raw), row, lane >> 4, sk);
-    if (R::v) pf_unpack_v(*reinterpret_cast<const u3*>(raw + 1024), row, 2 * (lane >> 5) + ((lane >> 4) & 1), sv);
+    if (R::k)
+      pf_unpack_k(*reinterpret_cast<const u3*>(raw),
+                  pf_opaque(pf_lds_addr(sk) + 1024 * 4 * (lane >> 4) + 16 * row));
+    if (R::v)
+      pf_unpack_v(*reinterpret_cast<const u3*>(raw + 1024),
+                  pf_opaque(pf_lds_addr(sv) + pf_v_lane_offset(row, 2 * (lane >> 5) + ((lane >> 4) & 1))));
   }
   if (R::norms)
     reinterpret_cast<uint32_t*>(snorm)[lane] = reinterpret_cast<const uint32_t*>(slot + kRawPage)[lane];
@@ -405,12 +444,17 @@ __global__ __launch_bounds__(64 * pf_waves<RB>(), 1) void prefill_kernel(Prefill
     q_start = a.q_starts[b];
     btab += (size_t)b * a.max_pages;
   }
-  __shared__ __attribute__((aligned(16))) uint8_t s_k[3][kKTileBytes];  // 49,152 B
-  __shared__ __attribute__((aligned(16))) uint8_t s_v[3][kVTileBytes];  // 49,152 B
-  __shared__ __attribute__((aligned(16))) uint8_t s_raw[kRawSlots][kRawSlot];  // 25,344 B
-  __shared__ __attribute__((aligned(16))) uint16_t s_norm[3][2 * kPage];      // K | V norms
-  __shared__ int s_pt[kPrefillMaxPages];                                       // 16,384 B
-  __shared__ int s_fail;
+  // One LDS block carved by hand, the arrays read every page first: the
+  // norms sit within the 64 KiB that a ds_read's immediate offset reaches
+  // from one base register (the compiler's own placement put them last, past
+  // 136 KiB, and spent a vector add on every norm read).
+  __shared__ __attribute__((aligned(16))) uint8_t s_lds[kPfLdsBytes];
+  uint16_t (*s_norm)[2 * kPage] = reinterpret_cast<uint16_t (*)[2 * kPage]>(s_lds + kPfLdsNorm);  // K | V norms
+  int& s_fail = *reinterpret_cast<int*>(s_lds + kPfLdsFail);
+  uint8_t (*s_raw)[kRawSlot] = reinterpret_cast<uint8_t (*)[kRawSlot]>(s_lds + kPfLdsRaw);   // 25,344 B
+  uint8_t (*s_k)[kKTileBytes] = reinterpret_cast<uint8_t (*)[kKTileBytes]>(s_lds + kPfLdsK);  // 49,152 B
+  uint8_t (*s_v)[kVTileBytes] = reinterpret_cast<uint8_t (*)[kVTileBytes]>(s_lds + kPfLdsV);  // 49,152 B
+  int* s_pt = reinterpret_cast<int*>(s_lds + kPfLdsPt);                                       // 16,384 B
 
   // ---- fused quantise-append: this workgroup's share of the chunk (the f16
   // tile buffers are free yet); its jobs are counted in once the records are
@@ -509,14 +553,14 @@ __global__ __launch_bounds__(64 * pf_waves<RB>(), 1) void prefill_kernel(Prefill
   // ---- S^T tiles [token block tb][row block cb] of the page in f16 buffer
   // `buf`: each K^ fragment feeds every row block (hi and lo parts of Q') ----
   auto scores = [&](int buf, f4 (&s)[4][RB]) {
-    const uint8_t* sk = s_k[buf];
+    const uint32_t kb = pf_opaque(pf_lds_addr(s_k[buf]) + 1024 * 4 * jq + 16 * col);
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
 #pragma unroll
       for (int cb = 0; cb < RB; ++cb) s[tb][cb] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        const h8 av = *reinterpret_cast<const h8*>(sk + 1024 * (4 * jq + kk) + 16 * (16 * tb + col));
+        const h8 av = pf_ld_h8(kb + 1024 * kk + 256 * tb);
 #pragma unroll
         for (int cb = 0; cb < RB; ++cb) {
           s[tb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, qhi[cb][kk], s[tb][cb], 0, 0, 0);
@@ -574,11 +618,11 @@ __global__ __launch_bounds__(64 * pf_waves<RB>(), 1) void prefill_kernel(Prefill
       issue(pg + 4);  // into the slot page pg + 1 left (read out before the last barrier)
       if (R::products_first) scores((pg + 1) % 3, s_next);
 
-      const uint16_t* nrm = s_norm[f];
+      const uint32_t nb = pf_opaque(pf_lds_addr(s_norm[f]) + 8 * jq);  // norms of tokens 16 tb + 4 jq ..
       uint32_t vbits = 0;
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) {
-        const u2 vn = *reinterpret_cast<const u2*>(nrm + kPage + 16 * tb + 4 * jq);
+        const u2 vn = pf_ld_u2(nb + 2 * (kPage + 16 * tb));
         const us2 h0 = __builtin_bit_cast(us2, (uint32_t)vn[0]), h1 = __builtin_bit_cast(us2, (uint32_t)vn[1]);
         if (!MASKED) {
           const us2 m = __builtin_elementwise_max(h0, h1);
@@ -601,7 +645,7 @@ __global__ __launch_bounds__(64 * pf_waves<RB>(), 1) void prefill_kernel(Prefill
       u2 vnp[4];
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) {
-        vnp[tb] = *reinterpret_cast<const u2*>(nrm + kPage + 16 * tb + 4 * jq);
+        vnp[tb] = pf_ld_u2(nb + 2 * (kPage + 16 * tb));
         if (MASKED) {
           const int t0 = tok_base + 16 * tb;
           vnp[tb][0] &= (t0 < kv_end ? 0xFFFFu : 0u) | (t0 + 1 < kv_end ? 0xFFFF0000u : 0u);
@@ -620,7 +664,7 @@ __global__ __launch_bounds__(64 * pf_waves<RB>(), 1) void prefill_kernel(Prefill
         float mp = -INFINITY;
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) {
-          const u2 kn = *reinterpret_cast<const u2*>(nrm + 16 * tb + 4 * jq);
+          const u2 kn = pf_ld_u2(nb + 2 * 16 * tb);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const float v = times_norm2(s[tb][cb][r], kn, r);
@@ -669,13 +713,13 @@ __global__ __launch_bounds__(64 * pf_waves<RB>(), 1) void prefill_kernel(Prefill
       }
 
       // ---- O'^T += V^T P~: each V^ fragment feeds both row blocks ----
-      const uint8_t* svp = s_v[f];
+      const uint32_t vb = pf_opaque(pf_lds_addr(s_v[f]) + 2048 * jq + 16 * col);
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
 #pragma unroll
         for (int tp = 0; tp < 2; ++tp) {
           // k index 8 jq + i: token 32 tp + 4 jq + i (i < 4) or 32 tp + 16 + 4 jq + i - 4
-          const h8 av = *reinterpret_cast<const h8*>(svp + 2048 * (4 * tp + jq) + 16 * (16 * m + col));
+          const h8 av = pf_ld_h8(vb + 8192 * tp + 256 * m);
 #pragma unroll
           for (int cb = 0; cb < RB; ++cb)
             acc[cb][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pb[tp][cb], acc[cb][m], 0, 0, 0);
@@ -693,12 +737,18 @@ __global__ __launch_bounds__(64 * pf_waves<RB>(), 1) void prefill_kernel(Prefill
     f4 s_cur[4][RB], s_nxt[4][RB];
     scores(0, s_cur);
     int pg = 0;
-    for (; pg < n_full; ++pg) {
+    // two pages per iteration, the score sets trading places (no copies)
+    for (; pg + 1 < n_full; pg += 2) {
+      page_step(pg, s_cur, s_nxt, PfTag<false>{});
+      page_step(pg + 1, s_nxt, s_cur, PfTag<false>{});
+    }
+    if (pg < n_full) {
       page_step(pg, s_cur, s_nxt, PfTag<false>{});
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
         for (int cb = 0; cb < RB; ++cb) s_cur[tb][cb] = s_nxt[tb][cb];
+      ++pg;
     }
     for (; pg < n_pages; ++pg) {
       page_step(pg, s_cur, s_nxt, PfTag<true>{});
