@@ -388,8 +388,12 @@ iq_status iq_prefill_attention_ex(const iq_cache *cache, const void *rot_dev, co
  * head first quantise a share of the chunk's 64-token blocks, store the
  * records device-coherent and count them in; a workgroup waits for the count
  * only before it requests the first page holding appended tokens (the waits
- * are bounded; a wait that runs out leaves NaN rows).  Otherwise the two
- * kernels run one after the other.
+ * are bounded, about a second; a wait that runs out leaves NaN rows).  The
+ * waits need every workgroup of the launch to get a CU: work of other
+ * streams only delays that, but two such launches (or fused-merge decode
+ * launches) overlapping on one GPU can hold each other's CUs until the waits
+ * run out, so overlapping calls are the caller's to avoid.  Otherwise the
+ * two kernels run one after the other.
  *
  * k_new_dev, v_new_dev : [n_new][n_kv_heads][128] of kv_dtype.
  * workspace_dev        : at least iq_prefill_append_workspace_bytes(...) bytes;
