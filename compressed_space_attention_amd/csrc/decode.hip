@@ -918,7 +918,15 @@ __global__ __launch_bounds__(64 * kDecWaves, kDecWaves == 4 ? 2 : 1) void decode
 
   // the last wave brings the partial page now; it is used after its stream
   const bool tail_mine = has_tail && wave == kLastWave;
-  if (tail_mine)
+  // Where the wave's second prologue page is the tail page itself (pool page
+  // w + W would be the first past the pool), that slot already holds it,
+  // requested with the first pages: no second request, which would queue
+  // behind the whole split's page traffic.  Otherwise the tail goes to its
+  // own buffer now.
+  const bool tail_in_ring = tail_mine && wave + kDecWaves == n_pool;
+  uint8_t* const tail_buf = tail_in_ring ? s_ring[wave][1] : s_tail;
+  const bool tail_load = tail_mine && !tail_in_ring;
+  if (tail_load)
     issue_page<BITS>(a, (int)min((uint32_t)s_pages[n_pages - 1 - pg_begin], last_page), g, lane, s_tail);
   // ... and quantises the appended token (lanes 0-31 K, 32-63 V)
   float x_norm = 0.f;
@@ -951,6 +959,25 @@ __global__ __launch_bounds__(64 * kDecWaves, kDecWaves == 4 ? 2 : 1) void decode
     else
       x_rec.x = quantize_lanes32_4(x0, x1, x2, x3, m[0], m[1], m[2], m[3], r, lane >= 32, a.lv4, x_norm);
   }
+  // The record goes into the cache (skipped for a bad page id) once the
+  // wave's first page has landed: issued earlier, its stores would sit in
+  // front of that page in the wave's memory counter; issued then, they
+  // complete while the pages are processed.  This split's copy of the page
+  // in LDS is patched before use (the page load may have read the slot
+  // before or after these stores).
+  bool record_pending = append_here && wave == kLastWave;
+  auto store_record = [&]() {
+    const uint32_t id = (uint32_t)s_pages[n_pages - 1 - pg_begin];
+    if (id < (uint32_t)a.num_pages) {
+      const size_t blk = (size_t)id * a.hkv + g;
+      const bool is_v = lane >= 32;
+      uint8_t* codes = (is_v ? a.v_codes : a.k_codes) + blk * F::kBlockBytes;
+      uint16_t* norms = (is_v ? a.v_norms : a.k_norms) + blk * kPage;
+      if constexpr (BITS == 3) place_record(is_v, lane & 31, x_rec, x_norm, codes, norms, (L - 1) & 63);
+      else place_record4(is_v, lane & 31, x_rec.x, x_norm, codes, norms, (L - 1) & 63);
+    }
+    record_pending = false;
+  };
 
   PageState st;
   st.m_run = -INFINITY;
@@ -975,12 +1002,13 @@ __global__ __launch_bounds__(64 * kDecWaves, kDecWaves == 4 ? 2 : 1) void decode
     const int seq_h = head == 0 ? seq0 : seq1;
     // loads issued after this page's: the other slot (and the tail's, which
     // went out after the first pages)
-    const int after = issued - 1 - seq_h + ((tail_mine && seq_h < 2) ? 1 : 0);
+    const int after = issued - 1 - seq_h + ((tail_load && seq_h < 2) ? 1 : 0);
     if (after <= 0) __builtin_amdgcn_s_waitcnt(wait_vm(0));
     else if (after == 1) __builtin_amdgcn_s_waitcnt(wait_vm(kDmaPerPage));
     else __builtin_amdgcn_s_waitcnt(wait_vm(2 * kDmaPerPage));
     PageRegs<PACK8, BITS> cur;
     read_page<PACK8, BITS>(slot, lane, cur);
+    if (APPEND && record_pending) store_record();
     const int pg = head == 0 ? pg0 : pg1;
     // claim the next page and reuse this slot for it (claims only grow: a
     // failed claim ends the stream)
@@ -1012,31 +1040,25 @@ __global__ __launch_bounds__(64 * kDecWaves, kDecWaves == 4 ? 2 : 1) void decode
     // the other slot's page is older than the refill, if it holds one
     if (head == 0 ? have1 : have0) head ^= 1;
   }
+  if (APPEND && record_pending) store_record();  // the wave had no pool page
   if (tail_mine) {
     __builtin_amdgcn_s_waitcnt(wait_vm(0));
     if (append_here) {  // the appended record replaces slot L - 1 of the page copy
       const bool is_v = lane >= 32;
-      uint8_t* codes = s_tail + (is_v ? F::kBlockBytes : 0);
-      uint16_t* norms = reinterpret_cast<uint16_t*>(s_tail + 2 * F::kBlockBytes + (is_v ? 128 : 0));
+      uint8_t* codes = tail_buf + (is_v ? F::kBlockBytes : 0);
+      uint16_t* norms = reinterpret_cast<uint16_t*>(tail_buf + 2 * F::kBlockBytes + (is_v ? 128 : 0));
       if constexpr (BITS == 3) place_record(is_v, lane & 31, x_rec, x_norm, codes, norms, (L - 1) & 63);
       else place_record4(is_v, lane & 31, x_rec.x, x_norm, codes, norms, (L - 1) & 63);
     }
     PageRegs<PACK8, BITS> cur;
-    read_page<PACK8, BITS>(s_tail, lane, cur);
-    process_page<PACK8, true, BITS>(cur, st, (n_pages - 1) * kPage, L, lane, fac, qhi, qlo, a.lv4);
+    read_page<PACK8, BITS>(tail_buf, lane, cur);
+    // a full last page (a decode step that completes it) needs no mask
+    if (L == n_pages * kPage)
+      process_page<PACK8, false, BITS>(cur, st, (n_pages - 1) * kPage, L, lane, fac, qhi, qlo, a.lv4);
+    else
+      process_page<PACK8, true, BITS>(cur, st, (n_pages - 1) * kPage, L, lane, fac, qhi, qlo, a.lv4);
   }
   __builtin_amdgcn_s_waitcnt(wait_vm(0));  // a page requested but not used may still be landing
-  if (append_here && wave == kLastWave) {  // the record into the cache (skipped for a bad page id)
-    const uint32_t id = (uint32_t)s_pages[n_pages - 1 - pg_begin];
-    if (id < (uint32_t)a.num_pages) {
-      const size_t blk = (size_t)id * a.hkv + g;
-      const bool is_v = lane >= 32;
-      uint8_t* codes = (is_v ? a.v_codes : a.k_codes) + blk * F::kBlockBytes;
-      uint16_t* norms = (is_v ? a.v_norms : a.k_norms) + blk * kPage;
-      if constexpr (BITS == 3) place_record(is_v, lane & 31, x_rec, x_norm, codes, norms, (L - 1) & 63);
-      else place_record4(is_v, lane & 31, x_rec.x, x_norm, codes, norms, (L - 1) & 63);
-    }
-  }
 
   // ---- merge the eight waves ----
   float l_col = __builtin_amdgcn_ldexpf(st.l_run, -st.rho_e);

@@ -188,7 +188,7 @@ __device__ __forceinline__ void raw_to_f32(const u4 r[8], int dtype, float x[32]
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int k = 0; k < 4; ++k) x[4 * i + k] = __builtin_bit_cast(float, r[i][k]);
+      for (int k = 0; k < 4; ++k) x[4 * i + k] = __builtin_bit_cast(float, (uint32_t)r[i][k]);  // rvalue: see the note on bit casts
   } else if (dtype == 1) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -208,83 +208,11 @@ __device__ __forceinline__ void raw_to_f32(const u4 r[8], int dtype, float x[32]
   }
 }
 
-__device__ __forceinline__ float load_as_float(const void* base, size_t idx, int dtype) {
-  if (dtype == 0) return reinterpret_cast<const float*>(base)[idx];
-  if (dtype == 1) {
-    const uint32_t b = reinterpret_cast<const uint16_t*>(base)[idx];
-    return __builtin_bit_cast(float, b << 16);
-  }
-  return (float)reinterpret_cast<const _Float16*>(base)[idx];
-}
-
-// Load 32 consecutive elements (128-bit aligned) as fp32.  The dtype branch
-// is taken once, outside the element loops.
+// Load 32 consecutive elements (128-bit aligned) as fp32.
 __device__ __forceinline__ void load32(const void* base, size_t idx, int dtype, float x[32]) {
-  if (dtype == 0) {
-    const f4* p = reinterpret_cast<const f4*>(reinterpret_cast<const float*>(base) + idx);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const f4 v = p[i];
-      x[4 * i] = v[0]; x[4 * i + 1] = v[1]; x[4 * i + 2] = v[2]; x[4 * i + 3] = v[3];
-    }
-    return;
-  }
-  const u4* p = reinterpret_cast<const u4*>(reinterpret_cast<const uint16_t*>(base) + idx);
-  u4 v[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) v[i] = p[i];
-  if (dtype == 1) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        x[8 * i + 2 * k] = __builtin_bit_cast(float, v[i][k] << 16);
-        x[8 * i + 2 * k + 1] = __builtin_bit_cast(float, v[i][k] & 0xFFFF0000u);
-      }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        x[8 * i + 2 * k] = (float)__builtin_bit_cast(_Float16, (uint16_t)(v[i][k] & 0xFFFFu));
-        x[8 * i + 2 * k + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(v[i][k] >> 16));
-      }
-  }
-}
-
-// 32 consecutive elements starting at element `idx` of an LDS buffer, as
-// fp32 (each dtype converted in its own straight-line branch).
-__device__ __forceinline__ void lds_to_float32(const uint8_t* buf, int idx, int dtype, float x[32]) {
-  if (dtype == 0) {
-    const f4* p = reinterpret_cast<const f4*>(buf + 4 * idx);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const f4 v = p[i];
-      x[4 * i] = v[0]; x[4 * i + 1] = v[1]; x[4 * i + 2] = v[2]; x[4 * i + 3] = v[3];
-    }
-  } else if (dtype == 1) {
-    const u4* p = reinterpret_cast<const u4*>(buf + 2 * idx);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const u4 v = p[i];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        x[8 * i + 2 * k] = __builtin_bit_cast(float, v[k] << 16);
-        x[8 * i + 2 * k + 1] = __builtin_bit_cast(float, v[k] & 0xFFFF0000u);
-      }
-    }
-  } else {
-    const u4* p = reinterpret_cast<const u4*>(buf + 2 * idx);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const u4 v = p[i];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        x[8 * i + 2 * k] = (float)__builtin_bit_cast(_Float16, (uint16_t)(v[k] & 0xFFFFu));
-        x[8 * i + 2 * k + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(v[k] >> 16));
-      }
-    }
-  }
+  u4 r[8];
+  load32_raw(base, idx, dtype, r);
+  raw_to_f32(r, dtype, x);
 }
 
 // 2^x on the transcendental unit (v_exp_f32).  Results below 2^-126 flush to

@@ -33,7 +33,7 @@ def _say(*a):
     print(*a, flush=True)
 
 
-# (kv heads, query heads, record bits, chunks (new_start, n_new, q_start, n_q))
+# (kv heads, query heads, record bits, chunks (new_start, n_new, q_start, n_q)[, input dtype])
 SCHEDULES = {
     # extend attention over a first chunk, a ragged second chunk whose queries
     # are its last 50 positions, then a prefill-only and an append-only call
@@ -45,10 +45,14 @@ SCHEDULES = {
     # 8 kv heads x 64 row tiles: more workgroups than the GPU holds at once,
     # so the call runs the append and the prefill as two kernels
     "two_kernels": (8, 64, 3, [(0, 276, 0, 0), (276, 1024, 276, 1024)]),
+    # fp32 and fp16 K/V rows (the fused coding converts each input type)
+    "f32_rows": (2, 8, 3, [(0, 200, 0, 200), (200, 333, 500, 33)], "f32"),
+    "f16_rows_4bit": (2, 16, 4, [(0, 130, 0, 130), (130, 200, 300, 30)], "f16"),
 }
 
 
-def _run_schedule(seed, hkv, hq, bits, chunks, total, shared_prefix=0, oracle_codes=True, rows_per_chunk=8):
+def _run_schedule(seed, hkv, hq, bits, chunks, total, shared_prefix=0, oracle_codes=True, rows_per_chunk=8,
+                  dtype="bf16"):
     from compressed_space_attention_amd import isoquant as iq
     dev = "cuda"
     pages = -(-total // 64)
@@ -58,8 +62,8 @@ def _run_schedule(seed, hkv, hq, bits, chunks, total, shared_prefix=0, oracle_co
     blocks = O.rotation_matrices(quats)
     rot = iq.rotation_init(quats, device=dev)
     out_ch = synth.outlier_channels(seed + 2, hkv)
-    k = synth.kv_vectors(seed + 3, total, hkv, "bf16", out_ch)
-    v = synth.kv_vectors(seed + 4, total, hkv, "bf16", None)
+    k = synth.kv_vectors(seed + 3, total, hkv, dtype, out_ch)
+    v = synth.kv_vectors(seed + 4, total, hkv, dtype, None)
     kd, vd = k.to(dev), v.to(dev)
     ca = iq.PagedCache(num_pages, hkv, device=dev, zero=True, bits=bits)
     cb = iq.PagedCache(num_pages, hkv, device=dev, zero=True, bits=bits)
@@ -125,10 +129,11 @@ def _run_schedule(seed, hkv, hq, bits, chunks, total, shared_prefix=0, oracle_co
 
 @pytest.mark.parametrize("name", list(SCHEDULES))
 def test_prefill_append_matches_two_calls_and_oracle(name):
-    hkv, hq, bits, chunks = SCHEDULES[name]
+    hkv, hq, bits, chunks, *rest = SCHEDULES[name]
+    dtype = rest[0] if rest else "bf16"
     total = max(max(s0 + n, q0 + nq) for s0, n, q0, nq in chunks)
-    _say(f"prefill_append schedule {name}: hkv={hkv} hq={hq} bits={bits} total={total}")
-    _run_schedule(7100 + len(name), hkv, hq, bits, chunks, total)
+    _say(f"prefill_append schedule {name}: hkv={hkv} hq={hq} bits={bits} total={total} rows {dtype}")
+    _run_schedule(7100 + len(name), hkv, hq, bits, chunks, total, dtype=dtype)
 
 
 @pytest.mark.parametrize("bits", [3, 4])
