@@ -955,7 +955,7 @@ __global__ __launch_bounds__(64 * kDecWaves, kDecWaves == 4 ? 2 : 1) void decode
     }
     const f4* m = reinterpret_cast<const f4*>(s_rot + 16 * r);
     if constexpr (BITS == 3)
-      quantize_lanes32(x0, x1, x2, x3, m[0], m[1], m[2], m[3], r, x_norm, x_rec);
+      quantize_lanes32<true>(x0, x1, x2, x3, m[0], m[1], m[2], m[3], r, x_norm, x_rec);
     else
       x_rec.x = quantize_lanes32_4(x0, x1, x2, x3, m[0], m[1], m[2], m[3], r, lane >= 32, a.lv4, x_norm);
   }

@@ -136,7 +136,7 @@ __global__ __launch_bounds__(256) void quantize_small_kernel(
   float n;
   if constexpr (BITS == 3) {
     u3 w;
-    quantize_lanes32(x0, x1, x2, x3, m0, m1, m2, m3, r, n, w);
+    quantize_lanes32<false>(x0, x1, x2, x3, m0, m1, m2, m3, r, n, w);
     if ((unsigned)page >= (unsigned)num_pages) return;
     const size_t blk = (size_t)page * hkv + head;  // (page, kv head) block
     place_record(which, r, w, n, (which ? v_codes : k_codes) + blk * (kPage * kRec),

@@ -3,7 +3,8 @@
 // with plain threshold counting (the quantiser's definition: a code is the
 // number of thresholds u reaches, ties going up) on every float within 64 ulps
 // of every threshold, at the signed zeros and infinities, and on 2e7 normal
-// samples.  Exit status 0 when every decision agrees.
+// samples; and the placement of a selector's codes in a packed group.  Exit
+// status 0 when everything agrees.
 #include <math.h>
 #include <stdio.h>
 #include <string.h>
@@ -36,6 +37,31 @@ static float step(float x, int n) {
   return x;
 }
 
+// The two placements of a selector's fields in a group (shifts and masks, or
+// a switch) agree, and the fields of selectors 0..7 OR-ed together are the
+// group that selectors_to_group packs.
+static long check_fields(std::mt19937& rng) {
+  long bad = 0;
+  for (int it = 0; it < 200000; ++it) {
+    uint32_t z[8], a0 = 0, a1 = 0, a2 = 0;
+    for (int s = 0; s < 8; ++s) {
+      z[s] = 0;
+      for (int b = 0; b < 4; ++b) z[s] |= (uint32_t)(rng() & 7u) << (8 * b);
+      uint32_t p0, p1, p2, q0, q1, q2;
+      iq::selector_fields<true>(s, z[s], p0, p1, p2);
+      iq::selector_fields<false>(s, z[s], q0, q1, q2);
+      if (p0 != q0 || p1 != q1 || p2 != q2) ++bad;
+      a0 |= p0;
+      a1 |= p1;
+      a2 |= p2;
+    }
+    uint32_t g0, g1, g2;
+    iq::selectors_to_group(z, g0, g1, g2);
+    if (a0 != g0 || a1 != g1 || a2 != g2) ++bad;
+  }
+  return bad;
+}
+
 int main(int argc, char** argv) {
   // the 4-bit thresholds (fp32 midpoints of the 16-level Gaussian codebook)
   Levels4 lv{{0.25822166f, 0.5224037f, 0.79954976f, 1.0992858f, 1.4371388f, 1.8435318f, 2.4008033f}, 0, 0, 0, 0};
@@ -64,5 +90,7 @@ int main(int argc, char** argv) {
   std::normal_distribution<float> nd(0.f, 1.5f);
   for (long i = 0; i < samples; ++i) test(nd(rng));
   printf("%ld decisions, %ld disagree\n", n, bad);
-  return bad != 0;
+  const long bad_fields = check_fields(rng);
+  printf("selector fields: 200000 groups, %ld disagree\n", bad_fields);
+  return bad != 0 || bad_fields != 0;
 }
