@@ -959,13 +959,18 @@ __global__ __launch_bounds__(64 * kDecWaves, kDecWaves == 4 ? 2 : 1) void decode
     else
       x_rec.x = quantize_lanes32_4(x0, x1, x2, x3, m[0], m[1], m[2], m[3], r, lane >= 32, a.lv4, x_norm);
   }
-  // The record goes into the cache (skipped for a bad page id) once the
-  // wave's first page has landed: issued earlier, its stores would sit in
-  // front of that page in the wave's memory counter; issued then, they
-  // complete while the pages are processed.  This split's copy of the page
-  // in LDS is patched before use (the page load may have read the slot
+  // The record goes into the cache (skipped for a bad page id) before the
+  // wave's last pages are processed, so that the stores complete meanwhile
+  // (stores issued after the last page's processing would hold up the end of
+  // the workgroup).  The wave's memory counter completes in issue order, so
+  // the stores wait for the pages requested before them: with four waves
+  // (one or two pages each) they go out once the first page has landed; with
+  // eight (long streams, where code in the page loop costs registers and
+  // time on every page) right before the tail.  This split's copy of the
+  // page in LDS is patched before use (the page load may have read the slot
   // before or after these stores).
-  bool record_pending = append_here && wave == kLastWave;
+  constexpr bool kRecordInLoop = kDecWaves == 4;
+  bool record_pending = APPEND && kRecordInLoop && append_here && wave == kLastWave;
   auto store_record = [&]() {
     const uint32_t id = (uint32_t)s_pages[n_pages - 1 - pg_begin];
     if (id < (uint32_t)a.num_pages) {
@@ -1008,7 +1013,8 @@ __global__ __launch_bounds__(64 * kDecWaves, kDecWaves == 4 ? 2 : 1) void decode
     else __builtin_amdgcn_s_waitcnt(wait_vm(2 * kDmaPerPage));
     PageRegs<PACK8, BITS> cur;
     read_page<PACK8, BITS>(slot, lane, cur);
-    if (APPEND && record_pending) store_record();
+    if constexpr (APPEND && kRecordInLoop)
+      if (record_pending) store_record();
     const int pg = head == 0 ? pg0 : pg1;
     // claim the next page and reuse this slot for it (claims only grow: a
     // failed claim ends the stream)
@@ -1040,7 +1046,6 @@ __global__ __launch_bounds__(64 * kDecWaves, kDecWaves == 4 ? 2 : 1) void decode
     // the other slot's page is older than the refill, if it holds one
     if (head == 0 ? have1 : have0) head ^= 1;
   }
-  if (APPEND && record_pending) store_record();  // the wave had no pool page
   if (tail_mine) {
     __builtin_amdgcn_s_waitcnt(wait_vm(0));
     if (append_here) {  // the appended record replaces slot L - 1 of the page copy
@@ -1049,11 +1054,15 @@ __global__ __launch_bounds__(64 * kDecWaves, kDecWaves == 4 ? 2 : 1) void decode
       uint16_t* norms = reinterpret_cast<uint16_t*>(tail_buf + 2 * F::kBlockBytes + (is_v ? 128 : 0));
       if constexpr (BITS == 3) place_record(is_v, lane & 31, x_rec, x_norm, codes, norms, (L - 1) & 63);
       else place_record4(is_v, lane & 31, x_rec.x, x_norm, codes, norms, (L - 1) & 63);
+      if (!kRecordInLoop || record_pending) store_record();  // (four waves: no pool page)
     }
     PageRegs<PACK8, BITS> cur;
     read_page<PACK8, BITS>(tail_buf, lane, cur);
-    // a full last page (a decode step that completes it) needs no mask
-    if (L == n_pages * kPage)
+    // A full last page (a decode step that completes it) needs no mask; the
+    // unmasked instance is kept to four-wave workgroups (two pages per wave):
+    // beside the masked one it took the eight-wave step kernel from 146 to
+    // 210 registers and its page loop slower.
+    if (kDecWaves == 4 && L == n_pages * kPage)
       process_page<PACK8, false, BITS>(cur, st, (n_pages - 1) * kPage, L, lane, fac, qhi, qlo, a.lv4);
     else
       process_page<PACK8, true, BITS>(cur, st, (n_pages - 1) * kPage, L, lane, fac, qhi, qlo, a.lv4);
