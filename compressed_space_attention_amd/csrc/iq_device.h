@@ -37,15 +37,20 @@ struct __attribute__((aligned(4))) u3 {
 constexpr double kLevel3[4] = {0.2451, 0.7560, 1.3440, 2.1520};
 constexpr float kThr3[3] = {0.50055f, 1.05f, 1.748f};
 // code = number of the seven thresholds (-t3, -t2, -t1, 0, t1, t2, t3) that u
-// reaches, found by a binary search over them (three comparisons): code >= 4
-// iff u >= 0, then >= base + 2 iff u >= the threshold above base + 1, then
-// >= base + 1 likewise.
+// reaches (ties reach).  By symmetry it is 4 + m for u >= 0 with m = the
+// number of positive thresholds |u| reaches, and 3 - m' = m' ^ 3 for u < 0
+// with m' = the number |u| strictly exceeds; |u| > t is tested as a >= t with
+// a = the float one ulp below |u| (an integer decrement of the bits).  So one
+// magnitude count of three comparisons serves both signs and needs no
+// threshold selection.  u + 0 turns -0 into +0 (which codes 4, like +0).  A
+// NaN codes 3 or 4 (its vector's norm is NaN then).
 __host__ __device__ __forceinline__ uint32_t code_of(float u) {
-  const bool b2 = u >= 0.0f;
-  const bool b1 = u >= (b2 ? kThr3[1] : -kThr3[1]);
-  const float t0 = b2 ? (b1 ? kThr3[2] : kThr3[0]) : (b1 ? -kThr3[0] : -kThr3[2]);
-  const bool b0 = u >= t0;
-  return (b2 ? 4u : 0u) | (b1 ? 2u : 0u) | (b0 ? 1u : 0u);
+  const uint32_t b = __builtin_bit_cast(uint32_t, u + 0.0f);
+  const uint32_t neg = (uint32_t)((int32_t)b >> 31);  // all ones iff u < 0
+  const float a = fabsf(__builtin_bit_cast(float, b + neg));
+  const uint32_t m4 = 4u + (uint32_t)(a >= kThr3[0]) + (uint32_t)(a >= kThr3[1]) +
+                      (uint32_t)(a >= kThr3[2]);
+  return m4 ^ (neg & 7u);  // u < 0: 7 - (4 + m') = 3 - m'
 }
 
 // The matrix-core kernels consume the levels as f16 operands.  They carry
@@ -485,13 +490,62 @@ __device__ __forceinline__ void place_record4(bool is_v, int r, uint32_t w, floa
   if (r == 0) norms[slot] = float_to_half_sat(n);
 }
 
+// x[k] += s * (x[k] of the quad partner), k = 0..7, partner = lane ^ 1
+// (QUAD_PERM 0xB1) or lane ^ 2 (0x4E): one v_fmac_f32 with the partner's value
+// taken through DPP per element (the compiler keeps a separate DPP move for
+// this multiply-add form).  A VALU write followed by a DPP read of the same
+// register needs two wait states, which the compiler does not insert into
+// inline asm: hence the s_nop; within the block no element is read after the
+// block has written it.  Partner lanes outside EXEC read as 0 (bound_ctrl),
+// as with the DPP moves elsewhere.
+template <int QUAD_PERM>
+__device__ __forceinline__ void fmac_quad_xor8(float* x, float s) {
+  static_assert(QUAD_PERM == 0xB1 || QUAD_PERM == 0x4E, "quad exchange");
+  if constexpr (QUAD_PERM == 0xB1) {
+    asm("s_nop 1\n\t"
+        "v_fmac_f32_dpp %0, %0, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %1, %1, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %2, %2, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %3, %3, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %4, %4, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %5, %5, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %6, %6, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %7, %7, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1"
+        : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]),
+          "+v"(x[7])
+        : "v"(s));
+  } else {
+    asm("s_nop 1\n\t"
+        "v_fmac_f32_dpp %0, %0, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %1, %1, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %2, %2, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %3, %3, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %4, %4, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %5, %5, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %6, %6, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %7, %7, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1"
+        : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]),
+          "+v"(x[7])
+        : "v"(s));
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Unnormalised Walsh-Hadamard transform (Sylvester order) of a 128-vector held
 // by the four lanes of a quad, 32 consecutive coordinates each: lane quarter
 // j = lane % 4 holds coordinates 32j..32j+31.  Coordinate distances 1..16 are
 // in-register butterflies; 32 and 64 are DPP exchanges within the quad.
+//
+// Returns sigma = +-1 and leaves x = sigma * (H x) on the lane.  A cross-lane
+// butterfly step is x' = s x + p (p = the partner's value, s = -1 on the upper
+// lane of the pair); each lane computes t = x + s p instead, one fused
+// multiply-add with the partner's value taken through DPP, and carries the
+// factor: x' = s t exactly, since round-to-nearest is symmetric in sign.  The
+// partner two lanes away carries the same first factor s1, so the second step
+// leaves t' = t + s2 t_partner with x'' = s1 s2 t'.  Callers fold sigma = s1 s2
+// into a later scale factor.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void wht128_quad(float x[32], int j) {
+__device__ __forceinline__ float wht128_quad(float x[32], int j) {
 #pragma unroll
   for (int h = 1; h < 32; h <<= 1) {
 #pragma unroll
@@ -505,10 +559,11 @@ __device__ __forceinline__ void wht128_quad(float x[32], int j) {
   }
   const float s1 = (j & 1) ? -1.0f : 1.0f;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) x[i] = fmaf(s1, x[i], quad_xor1(x[i]));  // low: x + p, high: p - x
+  for (int i = 0; i < 32; i += 8) fmac_quad_xor8<0xB1>(x + i, s1);
   const float s2 = (j & 2) ? -1.0f : 1.0f;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) x[i] = fmaf(s2, x[i], quad_xor2(x[i]));
+  for (int i = 0; i < 32; i += 8) fmac_quad_xor8<0x4E>(x + i, s2);
+  return s1 * s2;
 }
 
 // The same transform with the quarters on lanes l, l^XOR_A (j^1) and
@@ -573,7 +628,9 @@ __device__ __forceinline__ float quad_codes(float x[32], int j, const float* s_r
   ss += quad_xor2(ss);
   const float n = sqrtf(ss);
 
-  wht128_quad(x, j);
+  // x = sigma * (H x): the rotated coordinates below carry sigma too, which
+  // inv_n takes back (an exact sign change)
+  const float sigma = wht128_quad(x, j);
   // SO(4) block by block (blocks 8j .. 8j + 7 of the quarter), each block's
   // four outputs turned into codes at once: sel[bb] holds the codes (3-bit)
   // or nibbles (4-bit) of coordinates 32j + 4bb .. + 3, one per byte.  The
@@ -583,7 +640,7 @@ __device__ __forceinline__ float quad_codes(float x[32], int j, const float* s_r
   // block's codes: otherwise the compiler reads all 32 rows up front and holds
   // 128 of them in registers (204 VGPRs instead of 62, a third of the waves).
   {
-    const float inv_n = n > 0.f ? 1.0f / n : 0.f;
+    const float inv_n = sigma * (n > 0.f ? 1.0f / n : 0.f);
     uint32_t prev = 0;
 #pragma unroll
     for (int bb = 0; bb < 8; ++bb) {

@@ -1,15 +1,19 @@
-// Host check of the kernels' quantiser decisions (no GPU): code_of (3-bit) and
-// nibble_of (4-bit) search the thresholds by bisection; here they are compared
-// with plain threshold counting (the quantiser's definition: a code is the
-// number of thresholds u reaches, ties going up) on every float within 64 ulps
-// of every threshold, at the signed zeros and infinities, and on 2e7 normal
-// samples; and the placement of a selector's codes in a packed group.  Exit
-// status 0 when everything agrees.
+// Host check of the kernels' quantiser decisions (no GPU): code_of (3-bit: a
+// magnitude count with a sign fix-up) and nibble_of (4-bit: bisection) are
+// compared with plain threshold counting (the quantiser's definition: a code
+// is the number of thresholds u reaches, ties going up) on every float within
+// 64 ulps of every threshold, at the signed zeros and infinities, on normal
+// samples, and (code_of, argument "all") on every float that is not a NaN;
+// and the placement of a selector's codes in a packed group.  Exit status 0
+// when everything agrees.
 #include <math.h>
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
+#include <atomic>
 #include <random>
+#include <thread>
 #include <vector>
 
 #include "../../compressed_space_attention_amd/csrc/iq_device.h"
@@ -90,6 +94,30 @@ int main(int argc, char** argv) {
   std::normal_distribution<float> nd(0.f, 1.5f);
   for (long i = 0; i < samples; ++i) test(nd(rng));
   printf("%ld decisions, %ld disagree\n", n, bad);
+  if (argc > 2 && strcmp(argv[2], "all") == 0) {
+    // every bit pattern but the NaNs, split over threads
+    std::atomic<long> bad_all{0}, n_all{0};
+    const unsigned nt = std::max(1u, std::min(16u, std::thread::hardware_concurrency()));
+    std::vector<std::thread> pool;
+    for (unsigned w = 0; w < nt; ++w)
+      pool.emplace_back([&, w] {
+        long b = 0, c = 0;
+        const uint64_t lo = (1ull << 32) * w / nt, hi = (1ull << 32) * (w + 1) / nt;
+        for (uint64_t i = lo; i < hi; ++i) {
+          float u;
+          const uint32_t bits = (uint32_t)i;
+          memcpy(&u, &bits, 4);
+          if (u != u) continue;
+          ++c;
+          b += iq::code_of(u) != count3(u);
+        }
+        bad_all += b;
+        n_all += c;
+      });
+    for (auto& t : pool) t.join();
+    printf("code_of on every non-NaN float: %ld values, %ld disagree\n", (long)n_all, (long)bad_all);
+    bad += bad_all;
+  }
   const long bad_fields = check_fields(rng);
   printf("selector fields: 200000 groups, %ld disagree\n", bad_fields);
   return bad != 0 || bad_fields != 0;
