@@ -494,10 +494,12 @@ __device__ __forceinline__ void place_record4(bool is_v, int r, uint32_t w, floa
 // (QUAD_PERM 0xB1) or lane ^ 2 (0x4E): one v_fmac_f32 with the partner's value
 // taken through DPP per element (the compiler keeps a separate DPP move for
 // this multiply-add form).  A VALU write followed by a DPP read of the same
-// register needs two wait states, which the compiler does not insert into
-// inline asm: hence the s_nop; within the block no element is read after the
-// block has written it.  Partner lanes outside EXEC read as 0 (bound_ctrl),
-// as with the DPP moves elsewhere.
+// register needs two wait states, which the compiler does not insert around
+// inline asm (it does not count the block's outputs as vector-ALU writes):
+// hence an s_nop before the block (for the writes that precede it) and one
+// after it (for a DPP read of its outputs that may follow); within the block
+// no element is read after the block has written it.  Partner lanes outside
+// EXEC read as 0 (bound_ctrl), as with the DPP moves elsewhere.
 template <int QUAD_PERM>
 __device__ __forceinline__ void fmac_quad_xor8(float* x, float s) {
   static_assert(QUAD_PERM == 0xB1 || QUAD_PERM == 0x4E, "quad exchange");
@@ -510,7 +512,8 @@ __device__ __forceinline__ void fmac_quad_xor8(float* x, float s) {
         "v_fmac_f32_dpp %4, %4, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
         "v_fmac_f32_dpp %5, %5, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
         "v_fmac_f32_dpp %6, %6, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
-        "v_fmac_f32_dpp %7, %7, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1"
+        "v_fmac_f32_dpp %7, %7, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "s_nop 1"
         : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]),
           "+v"(x[7])
         : "v"(s));
@@ -523,7 +526,8 @@ __device__ __forceinline__ void fmac_quad_xor8(float* x, float s) {
         "v_fmac_f32_dpp %4, %4, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
         "v_fmac_f32_dpp %5, %5, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
         "v_fmac_f32_dpp %6, %6, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
-        "v_fmac_f32_dpp %7, %7, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1"
+        "v_fmac_f32_dpp %7, %7, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "s_nop 1"
         : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]),
           "+v"(x[7])
         : "v"(s));
