@@ -15,7 +15,7 @@ HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 
 
 @pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not installed")
-def test_bisection_decisions_equal_threshold_counting(tmp_path):
+def test_decisions_equal_threshold_counting(tmp_path):
     exe = tmp_path / "decision_check"
     r = subprocess.run([HIPCC, "--offload-arch=gfx950", "-O2", "-std=c++17", SRC, "-o", str(exe)],
                        capture_output=True, text=True)

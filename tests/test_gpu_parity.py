@@ -54,28 +54,45 @@ def test_quantize_append_codes_and_norms(dtype, outliers, lens):
     assert st["mismatch"] < 1e-5 * st["codes"] + 1
 
 
-def test_quantize_special_vectors():
+def _special_vectors(k, at):
+    """Closed-form cases at tokens at .. at + 5 of k ([n][1][128] fp32)."""
+    k[at:at + 6] = 0.0                                     # at: zero vector -> all codes 4, norm 0
+    k[at + 1, 0, 0] = 3.0                                  # e_0 -> all codes 5
+    k[at + 2, 0] = torch.from_numpy(O.sylvester_hadamard()[:, 37] * 0.25)  # -> code 7 at 37, else 4
+    k[at + 3, 0] = 1e5                                     # norm 1.13e6 -> saturates at 65504
+    k[at + 4, 0, 5] = -2.0                                 # -e_5 -> u = -1 or +1 by Hadamard sign
+    k[at + 5] = torch.from_numpy(synth.normal(3, (1, 128)))
+
+
+@pytest.mark.parametrize("n", [6, 8300], ids=["lanes32", "quads"])
+def test_quantize_special_vectors(n):
     """Zero vectors, a huge norm (fp16 saturation), identity rotation with a
-    Hadamard column and a basis vector (closed-form codes)."""
-    n = 6
-    k = torch.zeros((n, 1, 128), dtype=torch.float32)
-    k[1, 0, 0] = 3.0                                  # e_0 -> all codes 5
-    k[2, 0] = torch.from_numpy(O.sylvester_hadamard()[:, 37] * 0.25)  # -> code 7 at 37, else 4
-    k[3, 0] = 1e5                                     # norm 1.13e6 -> saturates at 65504
-    k[4, 0, 5] = -2.0                                 # -e_5 -> u = -1 or +1 by Hadamard sign
-    k[5] = torch.from_numpy(synth.normal(3, (1, 128)))
+    Hadamard column and a basis vector (closed-form codes), through both append
+    kernels: 6 tokens take the 32-lanes-per-vector kernel; 8,300 tokens the
+    quad kernel, with the cases on its first (whole, LDS-assembled) page and on
+    its last, partial page."""
+    k = torch.from_numpy(synth.normal(29, (n, 1, 128))).float()
+    bases = [0] if n < 64 else [0, n - 10]
+    for at in bases:
+        _special_vectors(k, at)
     v = k.clone()
     s = Scenario(31, [n], hkv=1, dtype="f32", identity=True, kv_override=(k, v))
     ref, info = s.oracle_cache()
     code_parity(s.host_cache(), ref, info, s)
     g = s.host_cache()
-    codes = O.unpack_codes(g.k_codes[s.block_table[0, 0], 0, :n])
-    assert np.all(codes[0] == 4) and g.k_norms[s.block_table[0, 0], 0, 0] == 0
-    assert np.all(codes[1] == 5)
     want = np.full(128, 4)
     want[37] = 7
-    assert np.array_equal(codes[2], want)
-    assert g.k_norms[s.block_table[0, 0], 0, 3] == 0x7BFF
+    for at in bases:
+        page, slot = s.block_table[0, at // 64], at % 64
+        assert slot + 6 <= 64
+        # K records are slot-ordered (V records, in the matrix-core order, are
+        # checked against the oracle by code_parity above)
+        codes = O.unpack_codes(g.k_codes[page, 0, slot:slot + 6])
+        assert np.all(codes[0] == 4)
+        assert np.all(codes[1] == 5)
+        assert np.array_equal(codes[2], want)
+        for norms in (g.k_norms, g.v_norms):
+            assert norms[page, 0, slot] == 0 and norms[page, 0, slot + 3] == 0x7BFF
 
 
 @pytest.mark.parametrize("n_tok", [3, 5000], ids=["lanes32", "quads"])
