@@ -859,8 +859,13 @@ __global__ __launch_bounds__(64 * kDecWaves, kDecWaves == 4 ? 2 : 1) void decode
       }
     }
   }
+  // Four waves (one short pass over the chip): every wave's second page is
+  // requested only once the prologue loads have landed, so that the first
+  // pages of all waves stream in ahead of the second ones instead of beside
+  // them.
+  constexpr bool kLateSecond = kDecWaves == 4;
   issue_page<BITS>(a, (int)min(bt0, last_page), g, lane, s_ring[wave][0]);
-  issue_page<BITS>(a, (int)min(bt1, last_page), g, lane, s_ring[wave][1]);
+  if constexpr (!kLateSecond) issue_page<BITS>(a, (int)min(bt1, last_page), g, lane, s_ring[wave][1]);
 
   // (a length beyond the block table breaks the contract; never read past it)
   const int n_pages = min((L + kPage - 1) / kPage, max_pages);
@@ -886,11 +891,12 @@ __global__ __launch_bounds__(64 * kDecWaves, kDecWaves == 4 ? 2 : 1) void decode
   const int n_pool = (pg_end - pg_begin) - (has_tail ? 1 : 0);  // full pages to share
   if (tid == 0) s_next = 2 * kDecWaves;  // pool pages w and w + 8 are each wave's first two
 
-  // Everything but the two pages has landed once at most their loads are
-  // outstanding (loads complete in issue order).  (One straight-line wait:
+  // Everything but the two pages (four waves: the first page) has landed once
+  // at most their loads are outstanding (loads complete in issue order).  (One straight-line wait:
   // with waits on several paths the compiler would assume the worst and wait
   // for the pages before the LDS reads of the rotation below.)
-  __builtin_amdgcn_s_waitcnt(wait_vm(2 * kDmaPerPage));
+  __builtin_amdgcn_s_waitcnt(wait_vm((kLateSecond ? 1 : 2) * kDmaPerPage));
+  if constexpr (kLateSecond) issue_page<BITS>(a, (int)min(bt1, last_page), g, lane, s_ring[wave][1]);
 
   // Every wave rotates its query heads (rotate_queries: lane r of a half
   // wave holds coordinates 4r..4r+3).
