@@ -141,6 +141,11 @@ def test_prefill_validation():
     assert L.iq_prefill_attention(c4, FAKE, FAKE, 1, 0, 64, 0, FAKE, 8, 0.0, FAKE, FAKE, 0, None) == 0
     c5 = _cache(hkv=8, bits=5)
     assert L.iq_prefill_attention(c5, FAKE, FAKE, 1, 16, 64, 0, FAKE, 8, 0.0, FAKE, FAKE, 0, None) == -1
+    # the page-table staging limit: a causal range of 4,096 pages (262,144 tokens)
+    # at most; one token more is refused as unsupported, on either record width
+    for cc in (c, c4):
+        assert L.iq_prefill_attention(cc, FAKE, FAKE, 1, 32, 64, 262144 - 31, FAKE, 4097, 0.0, FAKE, FAKE, 0,
+                                      None) == -2
 
 
 def test_dense_and_probe_validation():

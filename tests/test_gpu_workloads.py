@@ -264,3 +264,25 @@ def test_chunked_prefill_full_shape_sampled_rows(bits):
     err = max_row_error(out[rows], ref)
     _say(f"  {p.name}: max row error {err:.3e} over rows {rows.tolist()}")
     assert err <= tol()
+
+
+def test_prefill4_at_the_staging_limit():
+    """4-bit records over a causal range of exactly the prefill's page-table
+    staging limit (4,096 pages, 262,144 tokens; the 3-bit case is one of the
+    prefill cases in tests/test_gpu_parity.py): the last 32 positions attend
+    over the whole cache; sampled rows against the oracle.  One token more is
+    refused on the host (tests/test_abi_cpu.py)."""
+    bits = 4
+    total, n_q = 4096 * 64, 32
+    w = workloads.DecodeWorkload("prefill_staging_limit", 1, 2, 1, "bf16", False, True, 977, context=total)
+    b = Built(w, [total], bits=bits)
+    q_start = total - n_q
+    q = synth.draw_normal_device(978, (n_q, 2, 128), torch.bfloat16)
+    out = iq.prefill_attention(b.cache, b.rot, q, q_start, b.bt_dev[0]).cpu().numpy()
+    rows = np.array([0, 1, 15, 30, 31])            # queries; the last one sees every token
+    ref = O4.prefill_attention4(b.host(), b.blocks, q.double().cpu().numpy(), q_start, b.bt[0], rows=rows)
+    err = max_row_error(out[rows], ref)
+    _say(f"  staging limit (4-bit): max row error {err:.3e}")
+    assert np.all(np.isfinite(out))
+    assert err <= tol()
+
