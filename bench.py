@@ -18,6 +18,7 @@ CPU oracle timed on a bounded sample on the host.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import math
 import os
@@ -45,6 +46,9 @@ def parse():
     ap.add_argument("--warmup-seconds", type=float, default=0.1,
                     help="minimum wall time of untimed warm-up replays before each timed region")
     ap.add_argument("--workload", default="gqa_decode_32k_32q4kv")
+    ap.add_argument("--context", type=int, default=0,
+                    help="a fixed-context decode workload at another context length (same shapes and "
+                         "seeds; the workload is reported as NAME@CONTEXT): a context sweep")
     ap.add_argument("--bits", type=int, default=3, choices=(3, 4),
                     help="record width of the measured packed cache (3: the method's; 4: the 4-bit variant)")
     ap.add_argument("--ring-bytes", type=float, default=1.0e9,
@@ -267,6 +271,10 @@ def run_decode(args):
     from compressed_space_attention_amd import synth, workloads
 
     w = workloads.DECODE_WORKLOADS[args.workload]
+    if args.context:
+        if w.ragged or args.context < 1:
+            raise SystemExit("--context needs a fixed-context workload and a positive length")
+        w = dataclasses.replace(w, name=f"{w.name}@{args.context}", context=args.context)
     device = "cuda"
     torch.cuda.set_device(0)
     lens = w.seq_lens()
