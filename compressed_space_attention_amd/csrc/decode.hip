@@ -997,6 +997,36 @@ __global__ __launch_bounds__(64 * kDecWaves, kDecWaves == 4 ? 2 : 1) void decode
 #pragma unroll
   for (int m = 0; m < 8; ++m) st.acc[m] = f4{0.f, 0.f, 0.f, 0.f};
 
+  // The tail page: the appended record replaces slot L - 1 of its copy, then
+  // it is processed (masked; a full last page of a four-wave step unmasked).
+  // Eight waves (long streams) take it first, so that the waves' page claims
+  // spread its cost over the workgroup; four waves (one or two pages each),
+  // last.
+  auto run_tail = [&]() {
+    __builtin_amdgcn_s_waitcnt(wait_vm(0));
+    if (append_here) {
+      const bool is_v = lane >= 32;
+      uint8_t* codes = tail_buf + (is_v ? F::kBlockBytes : 0);
+      uint16_t* norms = reinterpret_cast<uint16_t*>(tail_buf + 2 * F::kBlockBytes + (is_v ? 128 : 0));
+      if constexpr (BITS == 3) place_record(is_v, lane & 31, x_rec, x_norm, codes, norms, (L - 1) & 63);
+      else place_record4(is_v, lane & 31, x_rec.x, x_norm, codes, norms, (L - 1) & 63);
+      if (!kRecordInLoop || record_pending) store_record();  // (four waves: no pool page)
+    }
+    PageRegs<PACK8, BITS> cur;
+    read_page<PACK8, BITS>(tail_buf, lane, cur);
+    // A full last page (a decode step that completes it) needs no mask; the
+    // unmasked instance is kept to four-wave workgroups (two pages per wave):
+    // beside the masked one it took the eight-wave step kernel from 146 to
+    // 210 registers and its page loop slower.
+    if (kDecWaves == 4 && L == n_pages * kPage)
+      process_page<PACK8, false, BITS>(cur, st, (n_pages - 1) * kPage, L, lane, fac, qhi, qlo, a.lv4);
+    else
+      process_page<PACK8, true, BITS>(cur, st, (n_pages - 1) * kPage, L, lane, fac, qhi, qlo, a.lv4);
+  };
+  constexpr bool kTailFirst = kDecWaves == 8;
+  if constexpr (kTailFirst)
+    if (tail_mine) run_tail();
+
   // ---- the wave's stream of full pages ----
   // Slots 0 and 1 start with pool pages w and w + W; each processed slot is
   // refilled with the next unclaimed pool page (an LDS counter), so the waves
@@ -1052,27 +1082,8 @@ __global__ __launch_bounds__(64 * kDecWaves, kDecWaves == 4 ? 2 : 1) void decode
     // the other slot's page is older than the refill, if it holds one
     if (head == 0 ? have1 : have0) head ^= 1;
   }
-  if (tail_mine) {
-    __builtin_amdgcn_s_waitcnt(wait_vm(0));
-    if (append_here) {  // the appended record replaces slot L - 1 of the page copy
-      const bool is_v = lane >= 32;
-      uint8_t* codes = tail_buf + (is_v ? F::kBlockBytes : 0);
-      uint16_t* norms = reinterpret_cast<uint16_t*>(tail_buf + 2 * F::kBlockBytes + (is_v ? 128 : 0));
-      if constexpr (BITS == 3) place_record(is_v, lane & 31, x_rec, x_norm, codes, norms, (L - 1) & 63);
-      else place_record4(is_v, lane & 31, x_rec.x, x_norm, codes, norms, (L - 1) & 63);
-      if (!kRecordInLoop || record_pending) store_record();  // (four waves: no pool page)
-    }
-    PageRegs<PACK8, BITS> cur;
-    read_page<PACK8, BITS>(tail_buf, lane, cur);
-    // A full last page (a decode step that completes it) needs no mask; the
-    // unmasked instance is kept to four-wave workgroups (two pages per wave):
-    // beside the masked one it took the eight-wave step kernel from 146 to
-    // 210 registers and its page loop slower.
-    if (kDecWaves == 4 && L == n_pages * kPage)
-      process_page<PACK8, false, BITS>(cur, st, (n_pages - 1) * kPage, L, lane, fac, qhi, qlo, a.lv4);
-    else
-      process_page<PACK8, true, BITS>(cur, st, (n_pages - 1) * kPage, L, lane, fac, qhi, qlo, a.lv4);
-  }
+  if constexpr (!kTailFirst)
+    if (tail_mine) run_tail();
   __builtin_amdgcn_s_waitcnt(wait_vm(0));  // a page requested but not used may still be landing
 
   // ---- merge the eight waves ----
