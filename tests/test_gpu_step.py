@@ -69,6 +69,53 @@ def test_decode_step_matches_append_then_decode(case):
             assert np.all(o[b] == 0)
 
 
+# Host plan, four waves, eight pages per split (three splits at 1,536 tokens):
+# the step's last wave loads its pages w + 4 and w in that order.  Lengths
+# whose last split has exactly eight pages put the sequence's last page in that
+# wave's first slot, processed first (full: 1,536; partial: 1,526); the others
+# end in splits of six, four, two and one pages (last page in its own buffer,
+# the wave's stream starting from its second slot or absent).
+SWAP_LENS = [1536, 1526, 1408, 1275, 577, 64, 1]
+
+
+@pytest.mark.parametrize("bits,hkv,hq,det", [(3, 4, 32, 0), (3, 2, 32, 1), (4, 4, 32, 0), (4, 4, 16, 1)])
+def test_decode_step_four_wave_eight_page_splits(bits, hkv, hq, det):
+    lens = SWAP_LENS
+    _say(f"decode step, 4 waves x 8-page splits, bits={bits} hkv={hkv} hq={hq} det={det} lens={lens}")
+    from compressed_space_attention_amd import isoquant as iq
+    opts = iq.DecodeOptions(waves=4, pages_per_split=8, plan=iq.IQ_PLAN_HOST, deterministic=det)
+    info = iq.decode_describe(len(lens), hq, hkv, max(lens), bits, True, opts)
+    assert (info["waves"], info["pages_per_split"], info["splits"], info["balanced"]) == (4, 8, 3, 0)
+    seed = 770 + 10 * bits + hkv + det
+    full = Scenario(seed, lens, hkv=hkv, dtype="bf16", outliers=True, bits=bits)
+    step = Scenario(seed, lens, hkv=hkv, dtype="bf16", outliers=True, bits=bits,
+                    kv_override=(full.k, full.v), hold_last=True)
+    q = step.queries(seed + 1, len(lens), hq).cuda()
+    outs = [step.iq.decode_step(step.cache, step.rot, q, step.k_last, step.v_last, step.bt_dev,
+                                step.lens_dev, max(lens), options=opts)]
+    pair = full.iq.decode_attention(full.cache, full.rot, q, full.bt_dev, full.lens_dev, max(lens),
+                                    options=opts)
+    torch.cuda.synchronize()
+    for a, b in zip(step.cache.to_host(), full.cache.to_host()):
+        assert np.array_equal(a, b)
+    ref = step.oracle_decode(step.host_cache(), q.double().cpu().numpy())
+    # a second step over the same cache rewrites the same records
+    outs.append(step.iq.decode_step(step.cache, step.rot, q, step.k_last, step.v_last, step.bt_dev,
+                                    step.lens_dev, max(lens), options=opts))
+    torch.cuda.synchronize()
+    for a, b in zip(step.cache.to_host(), full.cache.to_host()):
+        assert np.array_equal(a, b)
+    for out in outs:
+        o = out.cpu().numpy()
+        err = max_row_error(o, ref)
+        _say(f"  max row error {err:.3e}")
+        assert np.all(np.isfinite(o))
+        assert err <= tol()
+        assert max_row_error(o, pair.cpu().numpy()) <= 0.5 * tol()
+    if det:
+        assert torch.equal(outs[0], outs[1])
+
+
 def test_decode_step_single_token_is_its_value():
     """Context 1: the output of every head is the dequantised new value row."""
     s = Scenario(760, [1, 1], hkv=2, dtype="bf16", hold_last=True)
