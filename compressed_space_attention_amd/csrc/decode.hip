@@ -25,9 +25,11 @@
 //   O'^T[dim][head] += V^T[dim][token] . P~^T[token][head]   (16x16x32); the V
 //       pages are stored so that lane l's 48-byte region is exactly its V
 //       operand for the page, so no transpose is needed.
-// With G <= 8 two 16-token score tiles share one set of registers (columns
-// 0-7 and 8-15), which halves the softmax work; the shared layout is also the
-// B operand of the PV product after one row shift.
+// With G <= 8 the score MFMA's columns 8-15 carry the low part of Q' (one
+// MFMA per k-step instead of two), and two 16-token score tiles then share
+// one set of registers (columns 0-7 and 8-15, each the sum of a column and
+// its partner eight lanes round), which halves the softmax work; the shared
+// layout is also the B operand of the PV product after one row shift.
 // 4-bit records (BITS = 4) use the same tiles: a record dword is eight
 // coordinates of the score operand, and a V region dword eight tokens' nibbles
 // of one coordinate pair (c, c + 16), i.e. accumulator tiles m and m + 4.
@@ -248,7 +250,8 @@ __device__ __forceinline__ void process_page(const PageRegs<PACK8, BITS>& cur, P
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[kk], qhi[kk], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[kk], qlo[kk], acc, 0, 0, 0);
+      // (PACK8: qhi carries both parts, columns 0-7 high and 8-15 low)
+      if (!PACK8) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[kk], qlo[kk], acc, 0, 0, 0);
     }
     s[rb] = acc;
   }
@@ -262,8 +265,18 @@ __device__ __forceinline__ void process_page(const PageRegs<PACK8, BITS>& cur, P
     const int tok = tok0 + 16 * tile_block<PACK8>(t, col) + 4 * jq;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      // with PACK8, columns 8-15 take the scores of the odd token block
-      const float raw = PACK8 ? dpp_f<kRowShr8, 0xC>(s[2 * t][r], s[2 * t + 1][r]) : s[t][r];
+      // With PACK8 column c < 8 of a tile holds head c's high-part score and
+      // column c + 8 its low part; the packed layout takes the even token
+      // block in columns 0-7 and the odd one in 8-15, each the sum of its two
+      // parts (the partner column is 8 lanes round the row).
+      float raw;
+      if (PACK8) {
+        const float x = dpp_f<kRowRor8, 0x3>(s[2 * t + 1][r], s[2 * t][r]);
+        const float y = dpp_f<kRowRor8, 0xC>(s[2 * t][r], s[2 * t + 1][r]);
+        raw = x + y;
+      } else {
+        raw = s[t][r];
+      }
       const float v = times_norm(raw, cur.kn[t], r);
       sc[t][r] = (!MASKED || tok + r < L) ? v : -INFINITY;
       mp = fmaxf(mp, sc[t][r]);
@@ -907,14 +920,22 @@ __global__ __launch_bounds__(64 * kDecWaves, kDecWaves == 4 ? 2 : 1) void decode
   __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
   __builtin_amdgcn_s_barrier();
 
+  // With PACK8 (G <= 8) score columns 8-15 would multiply padding: they take
+  // the low part of heads 0-7 instead (qhi of lane col >= 8 = low part of
+  // head col - 8), so one MFMA per k-step yields both parts and qlo is unused.
   h8 qhi[4], qlo[4];
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
     u4 dh, dl;
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-      dh[d] = s_q[(kk * 8 + d) * 64 + lane];
-      dl[d] = s_q[(kk * 8 + 4 + d) * 64 + lane];
+      if (PACK8) {
+        dh[d] = s_q[(kk * 8 + (col < 8 ? 0 : 4) + d) * 64 + (col < 8 ? lane : lane - 8)];
+        dl[d] = 0u;
+      } else {
+        dh[d] = s_q[(kk * 8 + d) * 64 + lane];
+        dl[d] = s_q[(kk * 8 + 4 + d) * 64 + lane];
+      }
     }
     qhi[kk] = __builtin_bit_cast(h8, dh);
     qlo[kk] = __builtin_bit_cast(h8, dl);
