@@ -268,12 +268,15 @@ __device__ __forceinline__ void process_page(const PageRegs<PACK8, BITS>& cur, P
       // With PACK8 column c < 8 of a tile holds head c's high-part score and
       // column c + 8 its low part; the packed layout takes the even token
       // block in columns 0-7 and the odd one in 8-15, each the sum of its two
-      // parts (the partner column is 8 lanes round the row).
+      // parts: the even tile plus itself shifted down eight lanes, the odd
+      // one plus itself shifted up (each add takes its shift as a DPP
+      // operand), and a per-lane select.
       float raw;
       if (PACK8) {
-        const float x = dpp_f<kRowRor8, 0x3>(s[2 * t + 1][r], s[2 * t][r]);
-        const float y = dpp_f<kRowRor8, 0xC>(s[2 * t][r], s[2 * t + 1][r]);
-        raw = x + y;
+        const float e = s[2 * t][r], o = s[2 * t + 1][r];
+        const float pe = e + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, e), kRowShl8, 0xF, 0xF, true));
+        const float po = o + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, o), kRowShr8, 0xF, 0xF, true));
+        raw = col < 8 ? pe : po;
       } else {
         raw = s[t][r];
       }
@@ -334,8 +337,11 @@ __device__ __forceinline__ void process_page(const PageRegs<PACK8, BITS>& cur, P
     if (PACK8) {
       w[0] = pw[th][0];
       w[1] = pw[th][1];
-      w[2] = dpp_u<kRowShl8, 0x3>(pw[th][0], pw[th][0]);
-      w[3] = dpp_u<kRowShl8, 0x3>(pw[th][1], pw[th][1]);
+      // the odd block's weights (columns 8-15 of the score tile) move down
+      // eight lanes; the product's columns 8-15 are never read (G <= 8),
+      // so their lanes take zeros and no copy of the old value is needed
+      w[2] = (uint32_t)__builtin_amdgcn_mov_dpp((int)pw[th][0], kRowShl8, 0xF, 0xF, true);
+      w[3] = (uint32_t)__builtin_amdgcn_mov_dpp((int)pw[th][1], kRowShl8, 0xF, 0xF, true);
     } else {
       w[0] = pw[2 * th][0];
       w[1] = pw[2 * th][1];
