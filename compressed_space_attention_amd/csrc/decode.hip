@@ -144,6 +144,18 @@ __device__ __forceinline__ uint32_t lds_base(void* lds) {
 __device__ __forceinline__ void lds_dma16(const void* g, void* lds) {
   asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds_base(lds)) : "memory");
 }
+// N consecutive KiB from one address and one M0: the instruction's immediate
+// offset moves the global and the LDS address alike, so the loads of a block
+// need no address arithmetic each.
+template <int N>
+__device__ __forceinline__ void lds_dma16_kib(const void* g, void* lds) {
+  static_assert(N >= 1 && N <= 4, "offsets stay within the 12-bit immediate");
+  const uint32_t m0 = lds_base(lds);
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(m0) : "memory");
+  if constexpr (N > 1) asm volatile("global_load_lds_dwordx4 %0, off offset:1024" ::"v"(g), "{m0}"(m0) : "memory");
+  if constexpr (N > 2) asm volatile("global_load_lds_dwordx4 %0, off offset:2048" ::"v"(g), "{m0}"(m0) : "memory");
+  if constexpr (N > 3) asm volatile("global_load_lds_dwordx4 %0, off offset:3072" ::"v"(g), "{m0}"(m0) : "memory");
+}
 __device__ __forceinline__ void lds_dma4(const void* g, void* lds) {
   asm volatile("global_load_lds_dword %0, off" ::"v"(g), "{m0}"(lds_base(lds)) : "memory");
 }
@@ -161,11 +173,8 @@ __device__ __forceinline__ void issue_page(const DecodeArgs& a, int page, int g,
   const size_t base = ((size_t)page * a.hkv + g) * kPage;  // record index of slot 0
   const uint8_t* kb = a.k_codes + base * F::kRecBytes + 16 * lane;
   const uint8_t* vb = a.v_codes + base * F::kRecBytes + 16 * lane;
-#pragma unroll
-  for (int i = 0; i < F::kBlockBytes / 1024; ++i) lds_dma16(kb + 1024 * i, slot + 1024 * i);
-#pragma unroll
-  for (int i = 0; i < F::kBlockBytes / 1024; ++i)
-    lds_dma16(vb + 1024 * i, slot + F::kBlockBytes + 1024 * i);
+  lds_dma16_kib<F::kBlockBytes / 1024>(kb, slot);
+  lds_dma16_kib<F::kBlockBytes / 1024>(vb, slot + F::kBlockBytes);
   // lanes 0-31 bring the K norms (two per lane), lanes 32-63 the V norms
   const uint16_t* nb = (lane < 32 ? a.k_norms : a.v_norms) + base + 2 * (lane & 31);
   lds_dma4(nb, slot + 2 * F::kBlockBytes);
@@ -217,8 +226,19 @@ __device__ __forceinline__ int frame_exp(uint32_t max_bits, int current) {
 
 template <bool PACK8>
 __device__ __forceinline__ float column_max(float v) {
-  if (PACK8) v = fmaxf(v, dpp_f<kRowRor8, 0xF>(v, v));
-  return max_xor32(max_xor16(v));
+  // The column's values are scores or -inf, never NaN: a plain v_max_f32
+  // (fmaxf would first quiet every operand that arrives through a lane
+  // exchange, two extra instructions per step).
+  auto vmax = [](float a, float b) {
+    float r;
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+  };
+  if (PACK8) v = vmax(v, dpp_f<kRowRor8, 0xF>(v, v));
+  u2 p = pair_xor16(__builtin_bit_cast(uint32_t, v));
+  v = vmax(__builtin_bit_cast(float, (uint32_t)p[0]), __builtin_bit_cast(float, (uint32_t)p[1]));
+  p = pair_xor32(__builtin_bit_cast(uint32_t, v));
+  return vmax(__builtin_bit_cast(float, (uint32_t)p[0]), __builtin_bit_cast(float, (uint32_t)p[1]));
 }
 
 // One page for one wave: scores on the matrix cores, online-softmax update,
@@ -858,8 +878,7 @@ __global__ __launch_bounds__(64 * kDecWaves, kDecWaves == 4 ? 2 : 1) void decode
   const int n_pass = (group + kHeadsPerPass - 1) / kHeadsPerPass;
   {
     const uint8_t* rg = reinterpret_cast<const uint8_t*>(rot_all + (size_t)g * kRotFloats) + 16 * lane;
-    lds_dma16(rg, s_rot);
-    lds_dma16(rg + 1024, reinterpret_cast<uint8_t*>(s_rot) + 1024);
+    lds_dma16_kib<2>(rg, s_rot);
     const size_t row_bytes = (size_t)kD * esize;
     const uint8_t* qg = q_bytes + ((size_t)b * hq + (size_t)g * group) * row_bytes;
     for (int p = 0; p < n_pass; ++p) {
