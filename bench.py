@@ -871,7 +871,7 @@ def write_traffic_record(root: str, workload: str = "gqa_decode_32k_32q4kv", cal
         targs = [a.strip() for a in k.split("<")[1].split(">")[0].split(",")]
         return len(targs) == 5 and targs[2] == "false" and targs[3] == "3"
 
-    merge = lambda k: "decode_merge_kernel<true>" in k
+    merge = lambda k: "decode_merge_kernel<true" in k  # decode_merge_kernel<true, chunk>
     copy = lambda k: "copy" in k.lower()
     fetch, write = medians("pmc_FETCH_SIZE"), medians("pmc_WRITE_SIZE")
     cf, cw = medians("cal_FETCH_SIZE"), medians("cal_WRITE_SIZE")

@@ -521,6 +521,9 @@ __device__ __forceinline__ void store_agent(float* p, float v) {
 // s = t/32 (mod 8), with all of its loads issued before any result is used;
 // the eight groups then combine through LDS, and the first wave normalises and
 // rotates back: o = (H / sqrt(d)) B^T o'.
+// The chunk (slots per thread whose loads go out together) is sized to the
+// plan's slots, so that one chunk covers them and no load or exponential is
+// spent on padding slots (4, 8 or 16 for up to 32, 64 or more slots).
 constexpr int kMergeChunk = 16;
 
 // The rows of SO(4) block (t % 64) / 2 of kv head g, which the first wave
@@ -534,7 +537,7 @@ __device__ __forceinline__ void merge_rot_block(const float* __restrict__ rot_al
 
 // Rows row0 .. row0 + count - 1 of (m, l) and acc[128] (count >= 1) -> the
 // 128 outputs of the head at `out`.  Must be called by all 256 threads.
-template <bool ROTATE>
+template <bool ROTATE, int CHUNK = kMergeChunk>
 __device__ __forceinline__ void merge_head(const f4 mt[4], const float* __restrict__ ws_acc,
                                            const float* __restrict__ ws_ml, size_t row0, int count,
                                            float* __restrict__ out, int tid) {
@@ -545,30 +548,30 @@ __device__ __forceinline__ void merge_head(const f4 mt[4], const float* __restri
   const f4* accp = reinterpret_cast<const f4*>(ws_acc + row0 * kD) + quad;
   float m_t = -INFINITY, l_t = 0.f;
   f4 acc_t = {0.f, 0.f, 0.f, 0.f};
-  // splits s0, s0 + 8, ..., s0 + 8 (kMergeChunk - 1): loads first, then an
+  // splits s0, s0 + 8, ..., s0 + 8 (CHUNK - 1): loads first, then an
   // online merge into (m_t, l_t, acc_t)
   auto merge_chunk = [&](int s0) {
-    float2 mv[kMergeChunk];
-    f4 av[kMergeChunk];
+    float2 mv[CHUNK];
+    f4 av[CHUNK];
 #pragma unroll
-    for (int k = 0; k < kMergeChunk; ++k) {  // rows past the end repeat the last one
+    for (int k = 0; k < CHUNK; ++k) {  // rows past the end repeat the last one
       const int sp = min(s0 + 8 * k, count - 1);
       mv[k] = ml[sp];
       av[k] = accp[(size_t)sp * (kD / 4)];
     }
     __builtin_amdgcn_sched_barrier(0);  // every load above issues before any use
 #pragma unroll
-    for (int k = 0; k < kMergeChunk; ++k)
+    for (int k = 0; k < CHUNK; ++k)
       if (s0 + 8 * k >= count) mv[k].x = -INFINITY;  // ... with zero weight
     float cm = m_t;
 #pragma unroll
-    for (int k = 0; k < kMergeChunk; ++k) cm = fmaxf(cm, mv[k].x);
+    for (int k = 0; k < CHUNK; ++k) cm = fmaxf(cm, mv[k].x);
     // branch-free (a branch here would sink the loads behind it)
     const float keep = (m_t == -INFINITY) ? 0.f : fast_exp2(m_t - cm);
     acc_t *= keep;
     l_t *= keep;
 #pragma unroll
-    for (int k = 0; k < kMergeChunk; ++k) {
+    for (int k = 0; k < CHUNK; ++k) {
       // an empty row's accumulator is selected away, never multiplied
       const bool live = mv[k].x > -INFINITY;
       const float w = live ? fast_exp2(mv[k].x - cm) : 0.f;
@@ -582,7 +585,7 @@ __device__ __forceinline__ void merge_head(const f4 mt[4], const float* __restri
     m_t = cm;
   };
   merge_chunk(grp);  // no loop before the first chunk: its loads follow the ones above
-  for (int s0 = grp + 8 * kMergeChunk; s0 < count; s0 += 8 * kMergeChunk) merge_chunk(s0);
+  for (int s0 = grp + 8 * CHUNK; s0 < count; s0 += 8 * CHUNK) merge_chunk(s0);
   s_part[grp][quad] = acc_t;
   if (quad == 0) {
     s_mm[grp] = m_t;
@@ -1208,7 +1211,7 @@ __global__ __launch_bounds__(64 * kDecWaves, kDecWaves == 4 ? 2 : 1) void decode
 // normalise, and rotate back (merge_head).  ROTATE = false: the partials are
 // already in the original space (the uncompressed baseline); the merge only
 // normalises.
-template <bool ROTATE>
+template <bool ROTATE, int CHUNK>
 __global__ __launch_bounds__(256, 1) void decode_merge_kernel(const float* __restrict__ rot_all,
                                                            const float* __restrict__ ws_acc,
                                                            const float* __restrict__ ws_ml,
@@ -1225,7 +1228,7 @@ __global__ __launch_bounds__(256, 1) void decode_merge_kernel(const float* __res
   const int count = n_splits ? n_splits[b] : splits;
   f4 mt[4];
   if (ROTATE) merge_rot_block(rot_all, hq / group, tid, mt);
-  merge_head<ROTATE>(mt, ws_acc, ws_ml, row0, count, out_all + ((size_t)b * hq_n + hq) * kD, tid);
+  merge_head<ROTATE, CHUNK>(mt, ws_acc, ws_ml, row0, count, out_all + ((size_t)b * hq_n + hq) * kD, tid);
 }
 
 // Split planning: one workgroup per CU.  Few pages per kv head (short or
@@ -1429,12 +1432,18 @@ hipError_t launch_decode(const CacheView& c, const float* rot, const void* q, in
 hipError_t launch_decode_merge(bool rotate, const float* rot, const float* ws_acc, const float* ws_ml,
                                int splits, int batch, int hq, int group, const int32_t* n_splits,
                                float* out, hipStream_t stream) {
-  if (rotate)
-    hipLaunchKernelGGL(decode_merge_kernel<true>, dim3(hq, batch), dim3(256), 0, stream, rot, ws_acc,
-                       ws_ml, splits, hq, group, n_splits, out);
-  else
-    hipLaunchKernelGGL(decode_merge_kernel<false>, dim3(hq, batch), dim3(256), 0, stream, rot,
-                       ws_acc, ws_ml, splits, hq, group, n_splits, out);
+#define IQ_MERGE(R, C)                                                                         \
+  hipLaunchKernelGGL((decode_merge_kernel<R, C>), dim3(hq, batch), dim3(256), 0, stream, rot, ws_acc, \
+                     ws_ml, splits, hq, group, n_splits, out)
+  // eight thread groups: one chunk of C slots each covers 8 C slots
+  if (splits <= 32) {
+    if (rotate) IQ_MERGE(true, 4); else IQ_MERGE(false, 4);
+  } else if (splits <= 64) {
+    if (rotate) IQ_MERGE(true, 8); else IQ_MERGE(false, 8);
+  } else {
+    if (rotate) IQ_MERGE(true, 16); else IQ_MERGE(false, 16);
+  }
+#undef IQ_MERGE
   return hipGetLastError();
 }
 
