@@ -1156,55 +1156,76 @@ __global__ __launch_bounds__(64 * kDecWaves, kDecWaves == 4 ? 2 : 1) void decode
     s_l[wave][col] = l_col;
   }
   __syncthreads();
-  // Per head: the largest wave maximum, each wave's weight relative to it,
-  // and the (m, l) of the partial row.
   const size_t row0 = ((size_t)b * hq + (size_t)g * group) * splits + split;  // head h: + h * splits
-  if (tid < group) {
+  // Head h's wave weights 2^(m_w - M), M the largest wave maximum; returns M.
+  auto wave_weights = [&](int h, float (&wt)[kDecWaves]) {
     float mw[kDecWaves], M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kDecWaves; ++w) {
-      mw[w] = s_m[w][tid];
+      mw[w] = s_m[w][h];
       M = fmaxf(M, mw[w]);
     }
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) wt[w] = (mw[w] == -INFINITY) ? 0.f : fast_exp2(mw[w] - M);
+    return M;
+  };
+  if (!a.arrive) {
+    // Each head's 32 threads compute its weights themselves (no second
+    // barrier) and sum the waves' accumulators over four coordinates each:
+    // one 512-byte row per head, and the (m, l) pair from its first thread.
+    for (int h = tid >> 5; h < group; h += 2 * kDecWaves) {
+      float wt[kDecWaves];
+      const float M = wave_weights(h, wt);
+      const int c = 4 * (tid & 31);
+      f4 sum = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int w = 0; w < kDecWaves; ++w)
+        sum += wt[w] * *reinterpret_cast<const f4*>(reinterpret_cast<const float*>(s_ring[w][0]) +
+                                                   h * kAccStride + c);
+      *reinterpret_cast<f4*>(a.ws_acc + (row0 + (size_t)h * splits) * kD + c) = sum;
+      if ((tid & 31) == 0) {
+        float Ls = 0.f;
+#pragma unroll
+        for (int w = 0; w < kDecWaves; ++w) Ls += wt[w] * s_l[w][h];
+        float* dst = a.ws_ml + 2 * (row0 + (size_t)h * splits);
+        dst[0] = M;
+        dst[1] = Ls;
+      }
+    }
+    return;
+  }
+  // Merged in the same launch: the weights through LDS, and the rows as
+  // device-coherent dword stores, 64 consecutive coordinates of one row per
+  // wave instruction (whole lines).
+  if (tid < group) {
+    float wt[kDecWaves];
+    const float M = wave_weights(tid, wt);
     float Ls = 0.f;
 #pragma unroll
     for (int w = 0; w < kDecWaves; ++w) {
-      const float wt = (mw[w] == -INFINITY) ? 0.f : fast_exp2(mw[w] - M);
-      s_wt[w][tid] = wt;
-      Ls += wt * s_l[w][tid];
+      s_wt[w][tid] = wt[w];
+      Ls += wt[w] * s_l[w][tid];
     }
     float* dst = a.ws_ml + 2 * (row0 + (size_t)tid * splits);
-    if (a.arrive) {
-      store_agent(dst, M);
-      store_agent(dst + 1, Ls);
-    } else {
-      dst[0] = M;
-      dst[1] = Ls;
-    }
+    store_agent(dst, M);
+    store_agent(dst + 1, Ls);
   }
   __syncthreads();
-  // Value v = coordinate v % 128 of head v / 128: the 64 lanes of a wave
-  // write 64 consecutive coordinates of one row (256 contiguous bytes).
   for (int v = tid; v < group * kD; v += 64 * kDecWaves) {
     const int h = v >> 7, c = v & (kD - 1);
     float sum = 0.f;
 #pragma unroll
     for (int w = 0; w < kDecWaves; ++w)
       sum += s_wt[w][h] * reinterpret_cast<const float*>(s_ring[w][0])[h * kAccStride + c];
-    float* dst = a.ws_acc + (row0 + (size_t)h * splits) * kD + c;
-    if (a.arrive) store_agent(dst, sum);
-    else *dst = sum;
+    store_agent(a.ws_acc + (row0 + (size_t)h * splits) * kD + c, sum);
   }
-  if (a.arrive) {
-    // The partial rows were stored device-coherent: once every wave has them
-    // acknowledged, count the workgroup in.  (A release fence at device scope
-    // would also write back this XCD's L2, which here took several
-    // microseconds per wave.)
-    __builtin_amdgcn_s_waitcnt(wait_vm(0));
-    __syncthreads();
-    if (tid == 0)
-      __hip_atomic_fetch_add(&a.arrive[(size_t)b * a.hkv + g], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
+  // Once every wave has its device-coherent stores acknowledged, count the
+  // workgroup in.  (A release fence at device scope would also write back this
+  // XCD's L2, which here took several microseconds per wave.)
+  __builtin_amdgcn_s_waitcnt(wait_vm(0));
+  __syncthreads();
+  if (tid == 0)
+    __hip_atomic_fetch_add(&a.arrive[(size_t)b * a.hkv + g], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // One workgroup per (query head, sequence): merge the split partials,
