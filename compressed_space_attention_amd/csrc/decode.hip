@@ -1047,7 +1047,7 @@ __global__ __launch_bounds__(64 * kDecWaves, kDecWaves == 4 ? 2 : 1) void decode
   for (int m = 0; m < 8; ++m) st.acc[m] = f4{0.f, 0.f, 0.f, 0.f};
 
   // The tail page: the appended record replaces slot L - 1 of its copy, then
-  // it is processed (masked; a full last page of a four-wave step unmasked).
+  // it is processed (masked).
   // Eight waves (long streams) take it first, so that the waves' page claims
   // spread its cost over the workgroup; four waves (one or two pages each),
   // last.
@@ -1063,14 +1063,11 @@ __global__ __launch_bounds__(64 * kDecWaves, kDecWaves == 4 ? 2 : 1) void decode
     }
     PageRegs<PACK8, BITS> cur;
     read_page<PACK8, BITS>(tail_buf, lane, cur);
-    // A full last page (a decode step that completes it) needs no mask; the
-    // unmasked instance is kept to four-wave workgroups (two pages per wave):
-    // beside the masked one it took the eight-wave step kernel from 146 to
-    // 210 registers and its page loop slower.
-    if (kDecWaves == 4 && L == n_pages * kPage)
-      process_page<PACK8, false, BITS>(cur, st, (n_pages - 1) * kPage, L, lane, fac, qhi, qlo, a.lv4);
-    else
-      process_page<PACK8, true, BITS>(cur, st, (n_pages - 1) * kPage, L, lane, fac, qhi, qlo, a.lv4);
+    // Masked, also where the step completes the page (the mask then keeps
+    // every token): a second, unmasked instance beside the loop's took the
+    // four-wave step kernel from 156 to 219 registers (and an earlier
+    // eight-wave one from 146 to 210) and measured no faster.
+    process_page<PACK8, true, BITS>(cur, st, (n_pages - 1) * kPage, L, lane, fac, qhi, qlo, a.lv4);
   };
   constexpr bool kTailFirst = kDecWaves == 8;
   if constexpr (kTailFirst)
