@@ -7,6 +7,8 @@ deterministic option) both give bit-identical outputs, run after run; both are
 within the tolerance of the oracle; and the arrival counters at the head of the
 workspace are zero again after every call, so a workspace can be reused by
 calls of any shape.  Graph replays of fused-merge steps match the eager runs.
+The merge kernel's three chunk sizes (slots each thread loads at once, chosen
+from the plan's slot count) each match the oracle.
 """
 
 import numpy as np
@@ -147,3 +149,35 @@ def test_fused_merge_step_graph_replays():
         for o, e in zip(outs, eager):
             assert torch.equal(o, e), f"replay {rep} differs"
         assert int(torch.count_nonzero(ws[:iq.DECODE_COUNTER_BYTES])) == 0
+
+
+CHUNK_CASES = [
+    # (lens, hkv, hq, slots range): the merge kernel's chunk is 4 slots per
+    # thread up to 32 slots, 8 up to 64 and 16 beyond; every regime and a
+    # balanced plan whose sequences use fewer slots than the rows hold
+    ([4096], 8, 16, (1, 32)),
+    ([4096], 4, 32, (33, 64)),
+    ([8192], 1, 8, (65, 256)),
+    ([8192, 3000, 64], 1, 8, (65, 256)),
+]
+
+
+@pytest.mark.parametrize("case", range(len(CHUNK_CASES)))
+def test_merge_chunk_regimes_match_oracle(case):
+    lens, hkv, hq, (lo, hi) = CHUNK_CASES[case]
+    _say(f"merge chunk regime lens={lens} hkv={hkv} hq={hq}")
+    info = iq.decode_describe(len(lens), hq, hkv, max(lens), 3, False)
+    _say(f"  plan {info}")
+    assert lo <= info["splits"] <= hi
+    s = Scenario(2300 + case, lens, hkv=hkv, dtype="bf16", outliers=True)
+    q = s.queries(2400 + case, len(lens), hq).cuda()
+    ws = torch.zeros(iq.decode_workspace_bytes(len(lens), hq, hkv, max(lens)), dtype=torch.uint8, device="cuda")
+    det = iq.DecodeOptions(deterministic=1)
+    a = iq.decode_attention(s.cache, s.rot, q, s.bt_dev, s.lens_dev, max(lens), workspace=ws, options=det)
+    b = iq.decode_attention(s.cache, s.rot, q, s.bt_dev, s.lens_dev, max(lens), workspace=ws, options=det)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b), "deterministic runs differ"
+    ref = s.oracle_decode(s.host_cache(), q.double().cpu().numpy())
+    err = max_row_error(a.cpu().numpy(), ref)
+    _say(f"  max row error {err:.3e}")
+    assert err <= tol()
